@@ -1,0 +1,265 @@
+/*
+ * kvq.h - quantized KV-cache attention decode for AMD MI355X (gfx950).
+ *
+ * A plain C ABI: pointers (host or device, as stated per argument), sizes,
+ * and a HIP stream passed as `void*` (a hipStream_t; NULL = the default
+ * stream).  No allocation happens inside the library: every buffer is owned
+ * by the caller.  Work is enqueued on the given stream and the call returns
+ * without synchronizing.  Arguments are validated before anything is
+ * launched; a rejected call launches nothing and returns a nonzero status
+ * with a message retrievable by kvq_last_error() (thread-local).  Faults in
+ * device memory named by the caller surface at the caller's next
+ * synchronization, not here.
+ *
+ * Method sources (cited by page title and section):
+ *  - NVFP4 KV cache: Model-Optimizer PR #714 "KV cache quantization for
+ *    MLAAttention in vLLM fakequant", Testing section (quantizer dump:
+ *    E2M1 "(2, 1) bit" elements, blocks of 16 along the last dim, dynamic
+ *    E4M3 "scale_bits (4, 3)" block scales, per-tensor amax from a
+ *    MaxCalibrator; only the latent kv_c quantizer of QuantMLAAttention is
+ *    enabled, the query quantizer is disabled).
+ *  - FP8 KV cache: compressed-tensors PR #436 (llm-compressor attention /
+ *    KV-cache quantization), kv_cache_scheme JSON: 8-bit float, tensor
+ *    strategy, symmetric, min-max observer, static.
+ *  - Split-KV decode and combine: Model-Optimizer PR #1832 "Add quant+sparse
+ *    attention for vLLM serving", Testing section (split-KV description and
+ *    the auto split count chosen from the compute-unit count and
+ *    batch x heads).
+ *  - FP8 probabilities and FP8 output: vLLM PR #15734 "[Quantization][FP8]
+ *    Add support for FP8 models with input_scale for output projection and QK
+ *    quantization", items 1 and 2.
+ *  - A missing KV scale served as 1: Model-Optimizer PR #673 "Fix KV cache
+ *    quantization bugs", comments.
+ *
+ * Numeric conventions (readings where the pages are silent):
+ *  - NVFP4: s_t = fp32(amax / 2688) (1 if amax == 0); block scale
+ *    s_hat = E4M3(bamax / (6 s_t)); code = E2M1(x / (s_hat s_t)).  Every
+ *    rounding decision is the exact real-number one (round to nearest, ties
+ *    to the even code, saturating, sign of zero kept); a block whose scale
+ *    rounds to 0 stores scale byte 0 and code bytes 0.
+ *  - FP8: scale = fp32(amax / 448) (1 if amax == 0); code = E4M3(x / scale),
+ *    same rounding rules.  E4M3 is the FN variant (max 448, NaN = 0x7F/0xFF).
+ *  - Packed NVFP4 rows: element 2j in the low nibble of byte j; scale byte k
+ *    is the E4M3 bits of block k (elements 16k..16k+15).
+ *  - GQA head mapping: query head h reads kv head h / (Hq / Hkv).
+ *  - Partials: part_o[b][h][j][0..Dv) = normalized output of split j,
+ *    part_lse[b][h][j] = natural-log log-sum-exp of the scaled scores of
+ *    split j (-inf for an empty split).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define KVQ_OK 0
+#define KVQ_ERR_ARG 1         /* null pointer, bad size, inconsistent shape   */
+#define KVQ_ERR_UNSUPPORTED 2 /* valid but not implemented (dtype, D, G ...)  */
+#define KVQ_ERR_ALIGN 3       /* a plane base or stride breaks the alignment  */
+#define KVQ_ERR_WORKSPACE 4   /* workspace too small                          */
+#define KVQ_ERR_HIP 5         /* a HIP runtime call or launch failed          */
+
+/* ---- element types ------------------------------------------------------ */
+#define KVQ_F32 0
+#define KVQ_BF16 1
+#define KVQ_F16 2
+#define KVQ_FP8E4M3 3
+#define KVQ_NVFP4 4
+
+/* ---- cache layouts ------------------------------------------------------ */
+#define KVQ_LAYOUT_GQA 0 /* K and V planes per (request, kv head, token)      */
+#define KVQ_LAYOUT_MLA 1 /* one latent plane per (request, token) + bf16 rope */
+
+/*
+ * Row addressing.  A tensor of rows of `d` contiguous elements is addressed
+ * by three indices (i0, i1, i2) with extents n0, n1, n2: row (i0, i1, i2)
+ * starts at base + i0*s0 + i1*s1 + i2*s2.  For unquantized tensors (x, out)
+ * the strides count elements of the tensor's dtype; for packed planes they
+ * count rows of the plane (a plane row is d/2 code bytes or d/16 scale
+ * bytes for NVFP4, d bytes for FP8), so one kvq_rows describes the code and
+ * the scale plane together.
+ */
+typedef struct {
+  int64_t n0, n1, n2;
+  int64_t s0, s1, s2;
+} kvq_rows;
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int32_t kvq_version(void);
+
+/*
+ * kvq_amax - per-tensor max |x| (max calibration; Model-Optimizer PR #714,
+ * Testing section, MaxCalibrator; compressed-tensors PR #436 min-max
+ * observer).
+ *   x        device, dtype x_dtype (KVQ_F32 or KVQ_BF16), rows per x_rows.
+ *   d        elements per row (> 0).
+ *   kv_lens  device int32[n0] or NULL: rows with i2 >= kv_lens[i0] are
+ *            skipped (padding of a ragged cache).
+ *   amax_out device float[1].  If accumulate == 0 it is overwritten with the
+ *            result; if accumulate != 0 the result is max-merged into the
+ *            value already there (which must be >= 0).
+ * The result is exact (an element of x).  NaN inputs are not supported.
+ */
+int kvq_amax(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const int32_t* kv_lens,
+             float* amax_out, int32_t accumulate, void* stream);
+
+/*
+ * kvq_pack_nvfp4 - quantize rows to NVFP4 (Model-Optimizer PR #714, Testing
+ * section quantizer dump).
+ *   x            device, KVQ_F32 or KVQ_BF16, rows per x_rows, d elements each.
+ *   d            multiple of 16, <= 1024.
+ *   amax         device float[1]: the calibrated per-tensor amax (>= 0).
+ *   codes        device uint8 plane, rows of d/2 bytes.
+ *   scales       device uint8 plane, rows of d/16 bytes.
+ *   dst_rows     the destination plane: n0, n1 equal to x_rows', n2 (the
+ *                plane's length along i2) >= x_rows.n2; strides in plane rows.
+ *   dst_pos      device int32[n0] or NULL: row (i0, i1, i2) of x is stored at
+ *                plane row (i0, i1, i2 + dst_pos[i0]) (append of new tokens);
+ *                rows that would land outside [0, dst_rows.n2) are skipped.
+ *   tensor_scale_out  device float[1] or NULL: receives s_t.
+ * Deterministic and bit-exact with the exact-real definition above.
+ */
+int kvq_pack_nvfp4(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax,
+                   uint8_t* codes, uint8_t* scales, kvq_rows dst_rows, const int32_t* dst_pos,
+                   float* tensor_scale_out, void* stream);
+
+/*
+ * kvq_pack_fp8 - quantize rows to per-tensor FP8 E4M3 (compressed-tensors
+ * PR #436 kv_cache_scheme).  Arguments as kvq_pack_nvfp4; codes rows are d
+ * bytes (d > 0, d % 4 == 0, <= 4096); scale_out (device float[1] or NULL)
+ * receives the scale amax/448 (1 if amax == 0).
+ */
+int kvq_pack_fp8(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax,
+                 uint8_t* codes, kvq_rows dst_rows, const int32_t* dst_pos, float* scale_out,
+                 void* stream);
+
+/*
+ * kvq_unpack_nvfp4 - dequantize NVFP4 rows to float32: out = fp32(E2M1(c) *
+ * s_hat * s_t) (one rounding; e * s_hat is exact).  Test / inspection path.
+ *   codes, scales  device planes per src_rows; tensor_scale device float[1];
+ *   out            device float32 rows per out_rows (extents == src_rows').
+ */
+int kvq_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, kvq_rows src_rows, int32_t d,
+                     const float* tensor_scale, float* out, kvq_rows out_rows, void* stream);
+
+/* kvq_unpack_fp8 - out = fp32(E4M3(c) * scale); as kvq_unpack_nvfp4. */
+int kvq_unpack_fp8(const uint8_t* codes, kvq_rows src_rows, int32_t d, const float* scale, float* out,
+                   kvq_rows out_rows, void* stream);
+
+/*
+ * Decode arguments (one query token per request).
+ *
+ * GQA / MHA (layout KVQ_LAYOUT_GQA): q [B][Hq][D]; K and V planes indexed by
+ * (request b, kv head, token t) with row strides kv_sb, kv_sh, kv_st (in
+ * plane rows, shared by the code and scale planes of K and V); D == Dv;
+ * Hq % Hkv == 0.
+ *
+ * MLA (layout KVQ_LAYOUT_MLA): q = absorbed latent query q_c [B][Hq][D]
+ * (D = Dv = latent rank), q_rope = q_r [B][Hq][Drope] (bf16); k_codes /
+ * k_scales = the NVFP4 latent plane c, used as keys and as values (v_* are
+ * ignored); k_rope = bf16 rope keys [.. Drope] addressed with the same row
+ * strides (in rows of Drope elements); Hkv must be 1; kv_sh is ignored.
+ *
+ * Scores are softmax_scale * (q . K_t) with K_t dequantized (and, for MLA,
+ * + q_r . k_rope_t); tokens t >= min(kv_lens[b], max_kv_len) are masked.
+ */
+typedef struct {
+  int32_t kv_format;   /* KVQ_NVFP4 or KVQ_FP8E4M3 (MLA: KVQ_NVFP4)       */
+  int32_t layout;      /* KVQ_LAYOUT_GQA or KVQ_LAYOUT_MLA                 */
+  int32_t B, Hq, Hkv;  /* batch, query heads, kv heads                     */
+  int32_t D, Dv, Drope;
+  int32_t max_kv_len;  /* upper bound on kv_lens and rows allocated per request */
+  const void* q;       /* device, q_dtype, [B][Hq][D] with element strides: */
+  int32_t q_dtype;     /* KVQ_BF16 or KVQ_F32                              */
+  int64_t q_sb, q_sh;  /*   q + b*q_sb + h*q_sh                            */
+  const void* q_rope;  /* MLA: device bf16 [B][Hq][Drope], element strides */
+  int64_t qr_sb, qr_sh;
+  const uint8_t* k_codes;   /* device plane (NVFP4: d/2 B rows; FP8: d B rows) */
+  const uint8_t* k_scales;  /* device NVFP4 scale plane (d/16 B rows); NULL for FP8 */
+  const float* k_scale;     /* device float[1]: s_t (NVFP4) or scale (FP8)  */
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  const float* v_scale;
+  const void* k_rope;       /* MLA: device bf16 rope-key rows              */
+  int64_t kv_sb, kv_sh, kv_st;
+  const int32_t* kv_lens;   /* device int32[B]                             */
+  float softmax_scale;
+  int32_t num_splits;       /* >= 1 explicit; <= 0: kvq_auto_num_splits    */
+  int32_t quantize_p;       /* 1: FP8 probabilities (vLLM PR #15734 item 2) */
+  float prob_scale;         /* P~ = E4M3(P / prob_scale) * prob_scale      */
+  float* part_o;            /* device float32 [B][Hq][s][Dv] (split stride s) */
+  float* part_lse;          /* device float32 [B][Hq][s]                   */
+  int32_t part_capacity;    /* the partial buffers hold at least this many
+                               splits; s must not exceed it                */
+  float* p_scratch;         /* quantize_p only: device float32 buffer of
+                               kvq_fp8p_scratch_floats(...) floats; else NULL */
+} kvq_decode_args;
+
+/*
+ * attn_decode_splitkv - split-KV flash decode over the packed cache
+ * (Model-Optimizer PR #1832, Testing section): each work-group takes one
+ * contiguous chunk of one (request, kv head), dequantizes in registers,
+ * computes the scores, keeps an online softmax (running max and
+ * denominator) and accumulates P.V; it writes per-split partials.
+ * Chunking: c = ceil(L_b / s) rounded up to the kernel tile; split j covers
+ * [j c, min((j+1) c, L_b)).
+ * With quantize_p = 1 (GQA only) the partials are written so that
+ * attn_decode_combine returns sum_t P~_t V_t (normalized P quantized to E4M3
+ * with prob_scale, not renormalized; vLLM PR #15734 item 2); this mode
+ * needs p_scratch (kvq_fp8p_scratch_floats).
+ *   splits_used  host int32* or NULL: receives the split count s used.
+ */
+int attn_decode_splitkv(const kvq_decode_args* args, int32_t* splits_used, void* stream);
+
+/*
+ * attn_decode_combine - merge the s partials (Model-Optimizer PR #1832,
+ * Testing section: "a small combine kernel merges the s partials"):
+ * LSE = log sum_j exp(lse_j), o = sum_j exp(lse_j - LSE) o_j; empty splits
+ * (lse_j = -inf) are skipped; a request with no tokens gives o = 0, lse =
+ * -inf.
+ *   out        device [B][Hq][Dv], out_dtype KVQ_F32, KVQ_BF16 (RNE) or
+ *              KVQ_FP8E4M3 (code = E4M3(o / out_scale), saturating; vLLM
+ *              PR #15734 item 1).
+ *   out_scale  device float[1], required for KVQ_FP8E4M3, else ignored.
+ *   lse_out    device float[B][Hq] or NULL.
+ */
+int attn_decode_combine(const float* part_o, const float* part_lse, int32_t B, int32_t Hq, int32_t Dv,
+                        int32_t num_splits, void* out, int32_t out_dtype, const float* out_scale,
+                        float* lse_out, void* stream);
+
+/*
+ * kvq_auto_num_splits - split count when the caller passes num_splits <= 0
+ * (Model-Optimizer PR #1832, Testing section: the built-in heuristic picks s
+ * from the compute-unit count and batch x heads).  Host-only, pure integer
+ * arithmetic, no device access.
+ *   num_cus           compute units of the device (256 on MI355X).
+ *   programs_per_req  kv heads per request (1 for MLA).
+ *   max_kv_len        longest kv length in the batch.
+ *   Dv, Hq            value width and query heads (partial-traffic bound).
+ *   s_out             host int32*: receives s in [1, 64].
+ */
+int kvq_auto_num_splits(int32_t num_cus, int32_t B, int32_t programs_per_req, int32_t max_kv_len,
+                        int32_t Dv, int32_t Hq, int32_t* s_out);
+
+/* Compute units of the current HIP device (host call; needs a GPU). */
+int kvq_device_cu_count(int32_t* num_cus_out);
+
+/*
+ * kvq_fp8p_scratch_floats - float32 elements of p_scratch needed by the
+ * FP8-probability path (quantize_p = 1): the spilled scores B*Hq*max_kv_len
+ * followed by per-split and per-head statistics.  Host-only.
+ */
+size_t kvq_fp8p_scratch_floats(int32_t B, int32_t Hq, int32_t s, int32_t max_kv_len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,243 @@
+"""Quantized KV-cache attention decode for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``include/kvq.h`` (libkvq.so): each
+function here has the C entry point's name, takes torch tensors, and only
+marshals pointers, strides and the current HIP stream.  Every step of the
+path runs in the HIP kernels; nothing is computed here.
+
+Packed planes are plain uint8 tensors:
+  NVFP4: codes [..., D/2] (element 2j in the low nibble of byte j),
+         scales [..., D/16] (E4M3 bits), tensor scale float32 [1]
+  FP8:   codes [..., D] (E4M3 bits), scale float32 [1]
+"""
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (KVQ_BF16, KVQ_F16, KVQ_F32, KVQ_FP8E4M3, KVQ_LAYOUT_GQA, KVQ_LAYOUT_MLA, KVQ_NVFP4, KvqError,
+                   KvqDecodeArgs, KvqRows, check)
+
+__all__ = [
+    "kvq_amax", "kvq_pack_nvfp4", "kvq_pack_fp8", "kvq_unpack_nvfp4", "kvq_unpack_fp8",
+    "attn_decode_splitkv", "attn_decode_combine", "kvq_auto_num_splits", "kvq_device_cu_count",
+    "kvq_fp8p_scratch_floats", "kvq_last_error", "kvq_version", "NVFP4Plane", "FP8Plane", "KvqError",
+    "KVQ_F32", "KVQ_BF16", "KVQ_F16", "KVQ_FP8E4M3", "KVQ_NVFP4", "KVQ_LAYOUT_GQA", "KVQ_LAYOUT_MLA",
+]
+
+_DT = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16, torch.float16: KVQ_F16}
+
+
+@dataclass
+class NVFP4Plane:
+    """An NVFP4-packed tensor: codes [..., D/2], scales [..., D/16], s_t [1]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: torch.Tensor
+
+    @property
+    def d(self):
+        return self.codes.shape[-1] * 2
+
+
+@dataclass
+class FP8Plane:
+    """A per-tensor FP8 E4M3 tensor: codes [..., D], scale [1]."""
+    codes: torch.Tensor
+    scale: torch.Tensor
+
+    @property
+    def d(self):
+        return self.codes.shape[-1]
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _rows(t: torch.Tensor, row_elems: int = None) -> KvqRows:
+    """Rows of the last dim of t (up to 3 leading dims).  With row_elems set
+    (packed planes) the strides are converted to plane rows."""
+    if t.dim() < 1 or t.dim() > 4:
+        raise ValueError("tensors must have 1 to 4 dims")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("the last dim must be contiguous")
+    lead = list(t.shape[:-1])
+    strides = list(t.stride()[:-1])
+    while len(lead) < 3:
+        lead.insert(0, 1)
+        strides.insert(0, 0)
+    if row_elems is not None:
+        for s in strides:
+            if s % row_elems:
+                raise ValueError("packed plane strides must be whole rows")
+        strides = [s // row_elems for s in strides]
+    return KvqRows(*lead, *strides)
+
+
+def kvq_last_error() -> str:
+    return _lib.lib().kvq_last_error().decode()
+
+
+def kvq_version() -> int:
+    return _lib.lib().kvq_version()
+
+
+def kvq_amax(x: torch.Tensor, kv_lens: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+             accumulate: bool = False, stream=None) -> torch.Tensor:
+    """Per-tensor max |x| over rows [..., d]; rows with i2 >= kv_lens[i0]
+    skipped.  Returns a float32 [1] device tensor."""
+    if out is None:
+        out = torch.zeros(1, dtype=torch.float32, device=x.device)
+    check(_lib.lib().kvq_amax(_ptr(x), _DT[x.dtype], _rows(x), x.shape[-1], _ptr(kv_lens), _ptr(out),
+                              int(accumulate), _stream(stream)))
+    return out
+
+
+def kvq_pack_nvfp4(x: torch.Tensor, amax: torch.Tensor, out: Optional[NVFP4Plane] = None,
+                   dst_pos: Optional[torch.Tensor] = None, stream=None) -> NVFP4Plane:
+    """Pack rows of x ([..., D], D % 16 == 0) to NVFP4.  With ``out`` given,
+    x's rows go to out's rows (offset by dst_pos[i0] along i2 if given)."""
+    d = x.shape[-1]
+    if out is None:
+        shp = tuple(x.shape[:-1])
+        out = NVFP4Plane(torch.empty(shp + (d // 2,), dtype=torch.uint8, device=x.device),
+                         torch.empty(shp + (d // 16,), dtype=torch.uint8, device=x.device),
+                         torch.empty(1, dtype=torch.float32, device=x.device))
+    dst = _rows(out.codes, d // 2)
+    sdst = _rows(out.scales, d // 16)
+    if (dst.s0, dst.s1, dst.s2) != (sdst.s0, sdst.s1, sdst.s2):
+        raise ValueError("code and scale planes must share their row layout")
+    xr = _rows(x)
+    check(_lib.lib().kvq_pack_nvfp4(_ptr(x), _DT[x.dtype], xr, d, _ptr(amax), _ptr(out.codes), _ptr(out.scales),
+                                    dst, _ptr(dst_pos), _ptr(out.tensor_scale), _stream(stream)))
+    return out
+
+
+def kvq_pack_fp8(x: torch.Tensor, amax: torch.Tensor, out: Optional[FP8Plane] = None,
+                 dst_pos: Optional[torch.Tensor] = None, stream=None) -> FP8Plane:
+    """Pack rows of x ([..., D]) to per-tensor FP8 E4M3."""
+    d = x.shape[-1]
+    if out is None:
+        out = FP8Plane(torch.empty(tuple(x.shape), dtype=torch.uint8, device=x.device),
+                       torch.empty(1, dtype=torch.float32, device=x.device))
+    dst = _rows(out.codes, d)
+    xr = _rows(x)
+    check(_lib.lib().kvq_pack_fp8(_ptr(x), _DT[x.dtype], xr, d, _ptr(amax), _ptr(out.codes), dst, _ptr(dst_pos),
+                                  _ptr(out.scale), _stream(stream)))
+    return out
+
+
+def kvq_unpack_nvfp4(p: NVFP4Plane, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    d = p.d
+    if out is None:
+        out = torch.empty(tuple(p.codes.shape[:-1]) + (d,), dtype=torch.float32, device=p.codes.device)
+    check(_lib.lib().kvq_unpack_nvfp4(_ptr(p.codes), _ptr(p.scales), _rows(p.codes, d // 2), d,
+                                      _ptr(p.tensor_scale), _ptr(out), _rows(out), _stream(stream)))
+    return out
+
+
+def kvq_unpack_fp8(p: FP8Plane, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    d = p.d
+    if out is None:
+        out = torch.empty(tuple(p.codes.shape), dtype=torch.float32, device=p.codes.device)
+    check(_lib.lib().kvq_unpack_fp8(_ptr(p.codes), _rows(p.codes, d), d, _ptr(p.scale), _ptr(out), _rows(out),
+                                    _stream(stream)))
+    return out
+
+
+def kvq_auto_num_splits(num_cus: int, B: int, programs_per_req: int, max_kv_len: int, Dv: int, Hq: int) -> int:
+    s = ctypes.c_int32(0)
+    check(_lib.lib().kvq_auto_num_splits(num_cus, B, programs_per_req, max_kv_len, Dv, Hq, ctypes.byref(s)))
+    return s.value
+
+
+def kvq_device_cu_count() -> int:
+    n = ctypes.c_int32(0)
+    check(_lib.lib().kvq_device_cu_count(ctypes.byref(n)))
+    return n.value
+
+
+def kvq_fp8p_scratch_floats(B: int, Hq: int, s: int, max_kv_len: int) -> int:
+    return _lib.lib().kvq_fp8p_scratch_floats(B, Hq, s, max_kv_len)
+
+
+def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_splits=0, part_o, part_lse,
+                     q_rope=None, k_rope=None, quantize_p=False, prob_scale=1.0 / 448.0,
+                     p_scratch=None) -> KvqDecodeArgs:
+    """Fill the C decode-argument struct from tensors (no device work).
+
+    GQA: q [B, Hq, D]; k, v NVFP4Plane / FP8Plane with codes [B, Hkv, Lmax, .].
+    MLA: q = q_c [B, H, Dc]; k = NVFP4Plane of the latent [B, Lmax, .];
+    v = None; q_rope [B, H, Dr] and k_rope [B, Lmax, Dr] bf16.
+    """
+    a = KvqDecodeArgs()
+    mla = v is None
+    fmt = KVQ_NVFP4 if isinstance(k, NVFP4Plane) else KVQ_FP8E4M3
+    B, Hq, D = q.shape
+    a.kv_format, a.layout = fmt, (KVQ_LAYOUT_MLA if mla else KVQ_LAYOUT_GQA)
+    a.B, a.Hq, a.D, a.Dv = B, Hq, D, D
+    row_elems = D // 2 if fmt == KVQ_NVFP4 else D
+    if mla:
+        a.Hkv, a.Drope = 1, (q_rope.shape[-1] if q_rope is not None else 0)
+        kr = _rows(k.codes, row_elems)  # [B, Lmax, .] -> n0=1, n1=B, n2=Lmax
+        a.kv_sb, a.kv_sh, a.kv_st = kr.s1, 0, kr.s2
+        if k_rope is not None:
+            rr = _rows(k_rope, k_rope.shape[-1])
+            if (rr.s1, rr.s2) != (kr.s1, kr.s2):
+                raise ValueError("k_rope must share the latent plane's row layout")
+        a.q_rope, a.k_rope = _ptr(q_rope), _ptr(k_rope)
+        if q_rope is not None:
+            a.qr_sb, a.qr_sh = q_rope.stride(0), q_rope.stride(1)
+    else:
+        a.Hkv = k.codes.shape[1]
+        kr = _rows(k.codes, row_elems)
+        vr = _rows(v.codes, row_elems)
+        if (kr.s0, kr.s1, kr.s2) != (vr.s0, vr.s1, vr.s2):
+            raise ValueError("K and V planes must share their row layout")
+        a.kv_sb, a.kv_sh, a.kv_st = kr.s0, kr.s1, kr.s2
+        a.Drope = 0
+    a.max_kv_len = int(max_kv_len)
+    a.q, a.q_dtype, a.q_sb, a.q_sh = _ptr(q), _DT[q.dtype], q.stride(0), q.stride(1)
+    if fmt == KVQ_NVFP4:
+        a.k_codes, a.k_scales, a.k_scale = _ptr(k.codes), _ptr(k.scales), _ptr(k.tensor_scale)
+        if not mla:
+            a.v_codes, a.v_scales, a.v_scale = _ptr(v.codes), _ptr(v.scales), _ptr(v.tensor_scale)
+        else:
+            a.v_scale = _ptr(k.tensor_scale)
+    else:
+        a.k_codes, a.k_scale = _ptr(k.codes), _ptr(k.scale)
+        a.v_codes, a.v_scale = _ptr(v.codes), _ptr(v.scale)
+    a.kv_lens = _ptr(kv_lens)
+    a.softmax_scale = float(softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(D))
+    a.num_splits = int(num_splits)
+    a.quantize_p, a.prob_scale = int(bool(quantize_p)), float(prob_scale)
+    a.part_o, a.part_lse = _ptr(part_o), _ptr(part_lse)
+    a.part_capacity = part_o.numel() // (B * Hq * D) if part_o is not None else 0
+    a.p_scratch = _ptr(p_scratch)
+    return a
+
+
+def attn_decode_splitkv(args: KvqDecodeArgs, stream=None) -> int:
+    """Launch the split-KV decode for prepared args; returns the split count."""
+    s = ctypes.c_int32(0)
+    check(_lib.lib().attn_decode_splitkv(ctypes.byref(args), ctypes.byref(s), _stream(stream)))
+    return s.value
+
+
+def attn_decode_combine(part_o, part_lse, B, Hq, Dv, num_splits, out, out_scale=None, lse_out=None,
+                        stream=None):
+    """Merge partials into out ([B, Hq, Dv] float32, bfloat16 or uint8 = FP8 codes)."""
+    odt = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16, torch.uint8: KVQ_FP8E4M3}[out.dtype]
+    check(_lib.lib().attn_decode_combine(_ptr(part_o), _ptr(part_lse), B, Hq, Dv, num_splits, _ptr(out), odt,
+                                         _ptr(out_scale), _ptr(lse_out), _stream(stream)))
+    return out

@@ -1,0 +1,100 @@
+"""ctypes view of libkvq.so: structs and function prototypes of include/kvq.h.
+
+Loading fails loudly when the library has not been built; there is no
+fallback path of any kind.
+"""
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "kvq.h")
+
+KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = range(6)
+KVQ_F32, KVQ_BF16, KVQ_F16, KVQ_FP8E4M3, KVQ_NVFP4 = range(5)
+KVQ_LAYOUT_GQA, KVQ_LAYOUT_MLA = 0, 1
+
+
+class KvqRows(ctypes.Structure):
+    _fields_ = [("n0", ctypes.c_int64), ("n1", ctypes.c_int64), ("n2", ctypes.c_int64),
+                ("s0", ctypes.c_int64), ("s1", ctypes.c_int64), ("s2", ctypes.c_int64)]
+
+
+class KvqDecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("kv_format", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("Dv", ctypes.c_int32), ("Drope", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("q_dtype", ctypes.c_int32),
+        ("q_sb", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("q_rope", ctypes.c_void_p), ("qr_sb", ctypes.c_int64), ("qr_sh", ctypes.c_int64),
+        ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("k_rope", ctypes.c_void_p),
+        ("kv_sb", ctypes.c_int64), ("kv_sh", ctypes.c_int64), ("kv_st", ctypes.c_int64),
+        ("kv_lens", ctypes.c_void_p),
+        ("softmax_scale", ctypes.c_float),
+        ("num_splits", ctypes.c_int32),
+        ("quantize_p", ctypes.c_int32), ("prob_scale", ctypes.c_float),
+        ("part_o", ctypes.c_void_p), ("part_lse", ctypes.c_void_p),
+        ("part_capacity", ctypes.c_int32),
+        ("p_scratch", ctypes.c_void_p),
+    ]
+
+
+_VP, _I32, _I64, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+_PROTOS = {
+    "kvq_last_error": (ctypes.c_char_p, []),
+    "kvq_version": (_I32, []),
+    "kvq_amax": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, _I32, _VP]),
+    "kvq_pack_nvfp4": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, _VP, KvqRows, _VP, _VP, _VP]),
+    "kvq_pack_fp8": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, KvqRows, _VP, _VP, _VP]),
+    "kvq_unpack_nvfp4": (ctypes.c_int, [_VP, _VP, KvqRows, _I32, _VP, _VP, KvqRows, _VP]),
+    "kvq_unpack_fp8": (ctypes.c_int, [_VP, KvqRows, _I32, _VP, _VP, KvqRows, _VP]),
+    "attn_decode_splitkv": (ctypes.c_int, [ctypes.POINTER(KvqDecodeArgs), ctypes.POINTER(_I32), _VP]),
+    "attn_decode_combine": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _I32, _VP, _VP, _VP]),
+    "kvq_auto_num_splits": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_I32)]),
+    "kvq_device_cu_count": (ctypes.c_int, [ctypes.POINTER(_I32)]),
+    "kvq_fp8p_scratch_floats": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
+}
+
+_lib = None
+
+
+def header_functions():
+    """Names of the functions include/kvq.h declares."""
+    with open(HEADER) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def lib():
+    """The loaded library (raises if libkvq.so has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m quantized_kv_cache_nvfp4_amd.build` "
+                "(or __graft_entry__.build()); there is no non-HIP fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _PROTOS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class KvqError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"kvq error {code}: {msg}")
+        self.code = code
+
+
+def check(rc):
+    if rc != KVQ_OK:
+        raise KvqError(rc, lib().kvq_last_error().decode())
+    return rc

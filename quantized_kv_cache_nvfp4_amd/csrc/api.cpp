@@ -1,0 +1,262 @@
+// C-ABI entry points: argument validation, split planning and dispatch to the
+// HIP kernels.  Every check runs on the host before anything is launched, so
+// a rejected call leaves the stream untouched.  No allocation, no host sync.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return KVQ_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_rows(const kvq_rows& r, const char* name) {
+  if (r.n0 < 0 || r.n1 < 0 || r.n2 < 0) return fail(KVQ_ERR_ARG, "%s: negative extent", name);
+  if (r.n0 > (1LL << 31) || r.n1 > (1LL << 31) || r.n2 > (1LL << 31))
+    return fail(KVQ_ERR_ARG, "%s: extent too large", name);
+  return KVQ_OK;
+}
+
+bool same_extents(const kvq_rows& a, const kvq_rows& b) { return a.n0 == b.n0 && a.n1 == b.n1 && a.n2 == b.n2; }
+
+// destination plane of a pack: same n0, n1 as the source, at least as long along i2
+bool fits_dst(const kvq_rows& x, const kvq_rows& d) { return x.n0 == d.n0 && x.n1 == d.n1 && d.n2 >= x.n2; }
+
+int64_t n_rows(const kvq_rows& r) { return r.n0 * r.n1 * r.n2; }
+
+int check_float_input(const void* x, int32_t dt, const char* name) {
+  if (x == nullptr) return fail(KVQ_ERR_ARG, "%s is null", name);
+  if (dt != KVQ_F32 && dt != KVQ_BF16) return fail(KVQ_ERR_UNSUPPORTED, "%s: dtype %d not supported (F32, BF16)", name, dt);
+  if (!aligned(x, dt == KVQ_F32 ? 4 : 2)) return fail(KVQ_ERR_ALIGN, "%s is not element-aligned", name);
+  return KVQ_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+int32_t kvq_version(void) { return 100; }  // 0.1.0
+
+int kvq_amax(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const int32_t* kv_lens, float* amax_out,
+             int32_t accumulate, void* stream) {
+  int rc;
+  if ((rc = check_float_input(x, x_dtype, "x")) != KVQ_OK) return rc;
+  if ((rc = check_rows(x_rows, "x_rows")) != KVQ_OK) return rc;
+  if (d <= 0) return fail(KVQ_ERR_ARG, "d must be > 0 (got %d)", d);
+  if (amax_out == nullptr) return fail(KVQ_ERR_ARG, "amax_out is null");
+  if (!aligned(amax_out, 4)) return fail(KVQ_ERR_ALIGN, "amax_out is not 4-byte aligned");
+  return hip_status(kvq::launch_amax(x, x_dtype, kvq::to_rows(x_rows), d, kv_lens, amax_out, accumulate != 0,
+                                     as_stream(stream)),
+                    "kvq_amax launch");
+}
+
+int kvq_pack_nvfp4(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax, uint8_t* codes,
+                   uint8_t* scales, kvq_rows dst_rows, const int32_t* dst_pos, float* tensor_scale_out,
+                   void* stream) {
+  int rc;
+  if ((rc = check_float_input(x, x_dtype, "x")) != KVQ_OK) return rc;
+  if ((rc = check_rows(x_rows, "x_rows")) != KVQ_OK) return rc;
+  if ((rc = check_rows(dst_rows, "dst_rows")) != KVQ_OK) return rc;
+  if (d <= 0 || d % 16 != 0 || d > 1024) return fail(KVQ_ERR_ARG, "d must be a positive multiple of 16, <= 1024 (got %d)", d);
+  if (amax == nullptr || codes == nullptr || scales == nullptr)
+    return fail(KVQ_ERR_ARG, "amax, codes and scales must be non-null");
+  if (!fits_dst(x_rows, dst_rows)) return fail(KVQ_ERR_ARG, "dst_rows must match x_rows in n0, n1 and be at least as long in n2");
+  if (!aligned(codes, 8)) return fail(KVQ_ERR_ALIGN, "codes plane must be 8-byte aligned");
+  if (n_rows(x_rows) == 0) return ok();
+  return hip_status(kvq::launch_pack_nvfp4(x, x_dtype, kvq::to_rows(x_rows), d, amax, codes, scales,
+                                           kvq::to_rows(dst_rows), dst_pos, tensor_scale_out, as_stream(stream)),
+                    "kvq_pack_nvfp4 launch");
+}
+
+int kvq_pack_fp8(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax, uint8_t* codes,
+                 kvq_rows dst_rows, const int32_t* dst_pos, float* scale_out, void* stream) {
+  int rc;
+  if ((rc = check_float_input(x, x_dtype, "x")) != KVQ_OK) return rc;
+  if ((rc = check_rows(x_rows, "x_rows")) != KVQ_OK) return rc;
+  if ((rc = check_rows(dst_rows, "dst_rows")) != KVQ_OK) return rc;
+  if (d <= 0 || d % 4 != 0 || d > 4096) return fail(KVQ_ERR_ARG, "d must be a positive multiple of 4, <= 4096 (got %d)", d);
+  if (amax == nullptr || codes == nullptr) return fail(KVQ_ERR_ARG, "amax and codes must be non-null");
+  if (!fits_dst(x_rows, dst_rows)) return fail(KVQ_ERR_ARG, "dst_rows must match x_rows in n0, n1 and be at least as long in n2");
+  if (!aligned(codes, 4)) return fail(KVQ_ERR_ALIGN, "codes plane must be 4-byte aligned");
+  if (n_rows(x_rows) == 0) return ok();
+  return hip_status(kvq::launch_pack_fp8(x, x_dtype, kvq::to_rows(x_rows), d, amax, codes, kvq::to_rows(dst_rows),
+                                         dst_pos, scale_out, as_stream(stream)),
+                    "kvq_pack_fp8 launch");
+}
+
+int kvq_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, kvq_rows src_rows, int32_t d,
+                     const float* tensor_scale, float* out, kvq_rows out_rows, void* stream) {
+  int rc;
+  if ((rc = check_rows(src_rows, "src_rows")) != KVQ_OK) return rc;
+  if ((rc = check_rows(out_rows, "out_rows")) != KVQ_OK) return rc;
+  if (d <= 0 || d % 16 != 0 || d > 1024) return fail(KVQ_ERR_ARG, "d must be a positive multiple of 16, <= 1024 (got %d)", d);
+  if (codes == nullptr || scales == nullptr || tensor_scale == nullptr || out == nullptr)
+    return fail(KVQ_ERR_ARG, "codes, scales, tensor_scale and out must be non-null");
+  if (!same_extents(src_rows, out_rows)) return fail(KVQ_ERR_ARG, "out_rows extents differ from src_rows extents");
+  if (!aligned(codes, 8) || !aligned(out, 4)) return fail(KVQ_ERR_ALIGN, "codes must be 8-byte, out 4-byte aligned");
+  if (n_rows(src_rows) == 0) return ok();
+  return hip_status(kvq::launch_unpack_nvfp4(codes, scales, kvq::to_rows(src_rows), d, tensor_scale, out,
+                                             kvq::to_rows(out_rows), as_stream(stream)),
+                    "kvq_unpack_nvfp4 launch");
+}
+
+int kvq_unpack_fp8(const uint8_t* codes, kvq_rows src_rows, int32_t d, const float* scale, float* out,
+                   kvq_rows out_rows, void* stream) {
+  int rc;
+  if ((rc = check_rows(src_rows, "src_rows")) != KVQ_OK) return rc;
+  if ((rc = check_rows(out_rows, "out_rows")) != KVQ_OK) return rc;
+  if (d <= 0 || d > 4096) return fail(KVQ_ERR_ARG, "d must be in [1, 4096] (got %d)", d);
+  if (codes == nullptr || scale == nullptr || out == nullptr)
+    return fail(KVQ_ERR_ARG, "codes, scale and out must be non-null");
+  if (!same_extents(src_rows, out_rows)) return fail(KVQ_ERR_ARG, "out_rows extents differ from src_rows extents");
+  if (!aligned(out, 4)) return fail(KVQ_ERR_ALIGN, "out must be 4-byte aligned");
+  if (n_rows(src_rows) == 0) return ok();
+  return hip_status(kvq::launch_unpack_fp8(codes, kvq::to_rows(src_rows), d, scale, out, kvq::to_rows(out_rows),
+                                           as_stream(stream)),
+                    "kvq_unpack_fp8 launch");
+}
+
+// ------------------------------------------------------------ split planning
+int kvq_auto_num_splits(int32_t num_cus, int32_t B, int32_t programs_per_req, int32_t max_kv_len, int32_t Dv,
+                        int32_t Hq, int32_t* s_out) {
+  if (s_out == nullptr) return fail(KVQ_ERR_ARG, "s_out is null");
+  if (num_cus <= 0 || B <= 0 || programs_per_req <= 0 || Dv <= 0 || Hq <= 0 || max_kv_len < 0)
+    return fail(KVQ_ERR_ARG, "kvq_auto_num_splits: non-positive argument");
+  // 1) enough work-groups to give every compute unit two of them
+  const int64_t base = static_cast<int64_t>(B) * programs_per_req;
+  int64_t s = (2LL * num_cus + base - 1) / base;
+  // 2) no split shorter than 256 tokens
+  const int64_t by_len = (static_cast<int64_t>(max_kv_len) + 255) / 256;
+  if (s > by_len) s = by_len;
+  // 3) the partials (written and read once: 8 bytes per element) stay under
+  //    a sixth of the packed KV bytes (about 9/8 * Dv bytes per token and
+  //    program for NVFP4 K and V)
+  const double kv_bytes = static_cast<double>(base) * max_kv_len * (9.0 * Dv / 8.0);
+  const double per_split = static_cast<double>(B) * Hq * (Dv + 1) * 8.0;
+  const int64_t by_traffic = static_cast<int64_t>(kv_bytes / (6.0 * per_split));
+  if (s > by_traffic) s = by_traffic;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  *s_out = static_cast<int32_t>(s);
+  return ok();
+}
+
+int kvq_device_cu_count(int32_t* num_cus_out) {
+  if (num_cus_out == nullptr) return fail(KVQ_ERR_ARG, "num_cus_out is null");
+  int dev = 0, n = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_device_cu_count: %s", hipGetErrorString(e));
+  *num_cus_out = n;
+  return ok();
+}
+
+size_t kvq_fp8p_scratch_floats(int32_t B, int32_t Hq, int32_t s, int32_t max_kv_len) {
+  if (B <= 0 || Hq <= 0 || s <= 0 || max_kv_len < 0) return 0;
+  // spilled scores, per-split (max, sum) and per-head (max, sum)
+  return static_cast<size_t>(B) * Hq * (static_cast<size_t>(max_kv_len) + 2 * s + 2);
+}
+
+int attn_decode_splitkv(const kvq_decode_args* a, int32_t* splits_used, void* stream) {
+  if (a == nullptr) return fail(KVQ_ERR_ARG, "args is null");
+  if (a->kv_format != KVQ_NVFP4 && a->kv_format != KVQ_FP8E4M3)
+    return fail(KVQ_ERR_UNSUPPORTED, "kv_format %d not supported (NVFP4, FP8E4M3)", a->kv_format);
+  if (a->layout != KVQ_LAYOUT_GQA && a->layout != KVQ_LAYOUT_MLA)
+    return fail(KVQ_ERR_ARG, "layout %d unknown", a->layout);
+  if (a->B <= 0 || a->Hq <= 0 || a->Hkv <= 0) return fail(KVQ_ERR_ARG, "B, Hq and Hkv must be positive");
+  if (a->Hq % a->Hkv != 0) return fail(KVQ_ERR_ARG, "Hq (%d) must be a multiple of Hkv (%d)", a->Hq, a->Hkv);
+  if (a->max_kv_len < 0) return fail(KVQ_ERR_ARG, "max_kv_len must be >= 0");
+  if (a->q == nullptr || a->k_codes == nullptr || a->k_scale == nullptr || a->kv_lens == nullptr ||
+      a->part_o == nullptr || a->part_lse == nullptr)
+    return fail(KVQ_ERR_ARG, "q, k_codes, k_scale, kv_lens, part_o and part_lse must be non-null");
+  if (a->kv_format == KVQ_NVFP4 && a->k_scales == nullptr) return fail(KVQ_ERR_ARG, "NVFP4 needs k_scales");
+  if (a->q_dtype != KVQ_BF16 && a->q_dtype != KVQ_F32) return fail(KVQ_ERR_UNSUPPORTED, "q_dtype must be BF16 or F32");
+  if (!(a->softmax_scale > 0.0f) || a->softmax_scale != a->softmax_scale)
+    return fail(KVQ_ERR_ARG, "softmax_scale must be a positive finite number");
+  if (!aligned(a->k_codes, 16)) return fail(KVQ_ERR_ALIGN, "k_codes must be 16-byte aligned");
+  if (a->k_scales != nullptr && !aligned(a->k_scales, 4)) return fail(KVQ_ERR_ALIGN, "k_scales must be 4-byte aligned");
+  if (!aligned(a->part_o, 4) || !aligned(a->part_lse, 4)) return fail(KVQ_ERR_ALIGN, "partials must be 4-byte aligned");
+  if (a->q_dtype == KVQ_F32 ? !aligned(a->q, 4) : !aligned(a->q, 2)) return fail(KVQ_ERR_ALIGN, "q misaligned");
+
+  int32_t s = a->num_splits;
+  if (s <= 0) {
+    int32_t cus = 0;
+    int rc = kvq_device_cu_count(&cus);
+    if (rc != KVQ_OK) return rc;
+    const int ppr = a->layout == KVQ_LAYOUT_MLA ? 1 : a->Hkv;
+    rc = kvq_auto_num_splits(cus, a->B, ppr, a->max_kv_len, a->Dv, a->Hq, &s);
+    if (rc != KVQ_OK) return rc;
+  }
+  if (s > 64) return fail(KVQ_ERR_ARG, "num_splits %d exceeds 64", s);
+  if (s > a->part_capacity) return fail(KVQ_ERR_WORKSPACE, "num_splits %d exceeds part_capacity %d", s, a->part_capacity);
+  if (a->quantize_p) {
+    if (a->layout != KVQ_LAYOUT_GQA) return fail(KVQ_ERR_UNSUPPORTED, "quantize_p is implemented for the GQA layout only");
+    return fail(KVQ_ERR_UNSUPPORTED, "quantize_p is not implemented yet");
+  }
+
+  kvq::DecodePlan plan{s, 0};
+  if (a->layout == KVQ_LAYOUT_GQA) {
+    if (a->v_codes == nullptr || a->v_scale == nullptr) return fail(KVQ_ERR_ARG, "GQA needs v_codes and v_scale");
+    if (a->kv_format == KVQ_NVFP4 && a->v_scales == nullptr) return fail(KVQ_ERR_ARG, "NVFP4 needs v_scales");
+    if (!aligned(a->v_codes, 16)) return fail(KVQ_ERR_ALIGN, "v_codes must be 16-byte aligned");
+    if (a->v_scales != nullptr && !aligned(a->v_scales, 4)) return fail(KVQ_ERR_ALIGN, "v_scales must be 4-byte aligned");
+    if (a->Dv != a->D) return fail(KVQ_ERR_ARG, "GQA layout needs Dv == D");
+    const int G = a->Hq / a->Hkv;
+    if (!kvq::gqa_supported(a->kv_format, G, a->D, a->q_dtype))
+      return fail(KVQ_ERR_UNSUPPORTED, "GQA decode: G=%d, D=%d not supported (G in 1,2,4,8,16; D in 64,128)", G, a->D);
+    if (splits_used) *splits_used = s;
+    return hip_status(kvq::launch_decode_gqa(*a, plan, as_stream(stream)), "attn_decode_splitkv launch");
+  }
+  if (a->kv_format != KVQ_NVFP4) return fail(KVQ_ERR_UNSUPPORTED, "MLA layout supports NVFP4 only");
+  if (a->Hkv != 1) return fail(KVQ_ERR_ARG, "MLA layout needs Hkv == 1");
+  return fail(KVQ_ERR_UNSUPPORTED, "MLA decode is not implemented yet");
+}
+
+int attn_decode_combine(const float* part_o, const float* part_lse, int32_t B, int32_t Hq, int32_t Dv,
+                        int32_t num_splits, void* out, int32_t out_dtype, const float* out_scale, float* lse_out,
+                        void* stream) {
+  if (part_o == nullptr || part_lse == nullptr || out == nullptr)
+    return fail(KVQ_ERR_ARG, "part_o, part_lse and out must be non-null");
+  if (B <= 0 || Hq <= 0 || Dv <= 0) return fail(KVQ_ERR_ARG, "B, Hq and Dv must be positive");
+  if (num_splits <= 0 || num_splits > 64) return fail(KVQ_ERR_ARG, "num_splits must be in [1, 64] (got %d)", num_splits);
+  if (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16 && out_dtype != KVQ_FP8E4M3)
+    return fail(KVQ_ERR_UNSUPPORTED, "out_dtype %d not supported (F32, BF16, FP8E4M3)", out_dtype);
+  if (out_dtype == KVQ_FP8E4M3 && out_scale == nullptr) return fail(KVQ_ERR_ARG, "FP8 output needs out_scale");
+  if (!aligned(out, out_dtype == KVQ_F32 ? 4 : (out_dtype == KVQ_BF16 ? 2 : 1)))
+    return fail(KVQ_ERR_ALIGN, "out misaligned");
+  return hip_status(kvq::launch_combine(part_o, part_lse, B, Hq, Dv, num_splits, out, out_dtype, out_scale, lse_out,
+                                        as_stream(stream)),
+                    "attn_decode_combine launch");
+}
+
+}  // extern "C"

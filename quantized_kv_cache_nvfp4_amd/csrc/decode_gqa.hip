@@ -1,0 +1,467 @@
+// Split-KV flash decode over an NVFP4 or FP8 E4M3 KV cache, GQA / MHA layout,
+// for gfx950 (wave64, MFMA 16x16x32 f16).
+//
+// Method: Model-Optimizer PR #1832 "Add quant+sparse attention for vLLM
+// serving", Testing section: the KV sequence of one (request, head) is cut
+// into s contiguous chunks; each program keeps a running max and denominator
+// of the softmax over its chunk and accumulates the probability-weighted V,
+// and a combine step merges the s partials.  Cache formats: Model-Optimizer
+// PR #714 Testing section (NVFP4: E2M1 codes, E4M3 scale per 16 elements
+// along head_dim, per-tensor fp32 scale) and compressed-tensors PR #436
+// kv_cache_scheme (per-tensor FP8 E4M3).
+//
+// Design for CDNA4 (not a translation of the pages' Triton kernel):
+//  * one work-group = 4 waves = one chunk of one (request, kv head); the
+//    waves take interleaved tiles of the chunk and are merged through LDS.
+//  * dequantization happens in registers: E2M1 -> f16 with the hardware
+//    convert (exact), times the E4M3 block scale (an exact f16 product:
+//    at most 5 significant bits, inside f16's normal range); the per-tensor
+//    scale is applied in fp32 after the contraction.
+//  * Q.K^T and P.V run on MFMA 16x16x32 f16.  The query group is narrow
+//    (G = Hq/Hkv query heads share a kv head), so the 16 MFMA columns are
+//    filled with (sub-tile, head) pairs: sub-tile u of 16 tokens only
+//    meets the Q columns of its own row group (block-diagonal B operand), so
+//    one 16x16 score tile holds 16*16/G tokens x G heads with no padding.
+//    Each of the 16 rows keeps its own online-softmax state; rows of the same
+//    head are merged at the end of the chunk.
+//  * Q.K^T contracts over head_dim, and the order of that contraction is
+//    free: lane group g owns a contiguous quarter of head_dim, so each lane
+//    reads its K codes with one 128-bit load per token.  P.V contracts over
+//    tokens, and V is stored token-major, so each lane loads a short run of
+//    head_dim for 4 tokens and transposes 2x2 blocks of f16 in registers
+//    (v_perm_b32) into the token-contiguous MFMA operand; the output
+//    columns are permuted the same way and un-permuted on the final store.
+//  * fp32 queries are split into f16 hi + lo parts and, when asked, P is
+//    split the same way (two MFMAs each) for the fp32-accuracy path.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ inline uint32_t as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ inline f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+
+// E2M1 pair (byte SEL of w) -> f16x2, exact (scale argument 1.0)
+template <int SEL>
+__device__ inline f16x2 fp4x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+// E4M3 pair (16-bit half HI of w) -> f16x2, exact
+template <bool HI>
+__device__ inline f16x2 fp8x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+__device__ inline f16x8 cat4(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
+  f16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ inline f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ inline T ldg(const T* p) { return *p; }
+
+// ------------------------------------------------------------------ traits
+template <int KVF, int D>
+struct Geo {
+  static constexpr bool kFp4 = (KVF == KVQ_NVFP4);
+  static constexpr int kRowBytes = kFp4 ? D / 2 : D;   // code bytes per token row
+  static constexpr int kScaleBytes = D / 16;            // NVFP4 scale bytes per row
+  static constexpr int kQkJ = D / 32;                   // QK MFMAs per sub-tile
+  static constexpr int kPvJ = D / 16;                   // PV MFMAs (output column blocks)
+  static constexpr int kQkElems = D / 4;                // head_dim elements per lane (QK)
+  static constexpr int kPvElems = D / 16;               // head_dim elements per lane (PV)
+  static constexpr int kKWords = kFp4 ? D / 32 : D / 16;  // K code dwords per lane per token
+  static constexpr int kVBytes = kFp4 ? kPvElems / 2 : kPvElems;  // V code bytes per lane per token
+};
+
+// dequantized K operand of QK MFMA j for this lane (8 consecutive elements)
+template <int KVF, int D>
+__device__ inline f16x8 k_operand(const uint32_t* kw, uint32_t ks, int j) {
+  if constexpr (KVF == KVQ_NVFP4) {
+    const uint32_t w = kw[j];
+    f16x2 s2;
+    if constexpr (D == 128) {
+      const f16x2 s = fp8x2<false>(ks);  // (scale of block 2g, scale of block 2g+1)
+      const _Float16 sv = (j < 2) ? s[0] : s[1];
+      s2 = f16x2{sv, sv};
+    } else {
+      const f16x2 s = fp8x2<false>(ks);
+      s2 = f16x2{s[0], s[0]};
+    }
+    return cat4(fp4x2<0>(w) * s2, fp4x2<1>(w) * s2, fp4x2<2>(w) * s2, fp4x2<3>(w) * s2);
+  } else {
+    const uint32_t w0 = kw[2 * j], w1 = kw[2 * j + 1];
+    return cat4(fp8x2<false>(w0), fp8x2<true>(w0), fp8x2<false>(w1), fp8x2<true>(w1));
+  }
+}
+
+// V elements of one token for this lane as f16 pairs (d0,d1),(d2,d3),...
+template <int KVF, int D>
+__device__ inline void v_pairs(uint32_t vw0, uint32_t vw1, uint32_t vs, f16x2* out) {
+  using Gm = Geo<KVF, D>;
+  if constexpr (KVF == KVQ_NVFP4) {
+    const f16x2 s = fp8x2<false>(vs);
+    const f16x2 s2 = f16x2{s[0], s[0]};
+    out[0] = fp4x2<0>(vw0) * s2;
+    out[1] = fp4x2<1>(vw0) * s2;
+    if constexpr (Gm::kPvElems == 8) {
+      out[2] = fp4x2<2>(vw0) * s2;
+      out[3] = fp4x2<3>(vw0) * s2;
+    }
+  } else {
+    out[0] = fp8x2<false>(vw0);
+    out[1] = fp8x2<true>(vw0);
+    if constexpr (Gm::kPvElems == 8) {
+      out[2] = fp8x2<false>(vw1);
+      out[3] = fp8x2<true>(vw1);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ kernel
+// Template: KVF cache format, G query heads per kv head, D head_dim,
+// QF32 fp32 queries (hi/lo split), PSPLIT 2 = P carried as f16 hi + lo.
+template <int KVF, int G, int D, bool QF32, int PSPLIT>
+__global__ void __launch_bounds__(kThreads) k_decode_gqa(kvq_decode_args a, int num_splits) {
+  using Gm = Geo<KVF, D>;
+  constexpr int NSUB = 16 / G;                  // row groups in the 16 MFMA columns
+  constexpr int NT = NSUB < 2 ? 2 : NSUB;       // sub-tiles (16 tokens) per tile
+  constexpr int NACC = NT / NSUB;               // score accumulators per tile
+  constexpr int TT = 16 * NT;                   // tokens per tile
+  constexpr int NQ = QF32 ? 2 : 1;
+
+  __shared__ float lds_o[kWaves][16][D];
+  __shared__ float lds_m[kWaves][16];
+  __shared__ float lds_l[kWaves][16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane & 15;   // MFMA column / row-within-16 of this lane
+  const int g = lane >> 4;   // lane group (k-slice of the MFMA operands)
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+
+  int L = a.kv_lens[b];
+  L = L < a.max_kv_len ? L : a.max_kv_len;
+  L = L > 0 ? L : 0;
+  int chunk = (L + num_splits - 1) / num_splits;
+  chunk = (chunk + TT - 1) / TT * TT;
+  const int cs = split * chunk;
+  const int ce = (cs + chunk < L) ? cs + chunk : L;
+
+  const int hq0 = kvh * G;
+  float* part_o = a.part_o;
+  float* part_lse = a.part_lse;
+
+  if (cs >= ce) {  // empty split
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+      const int h = idx / D, d = idx % D;
+      const int64_t po = (static_cast<int64_t>(b) * a.Hq + hq0 + h) * num_splits + split;
+      part_o[po * D + d] = 0.0f;
+      if (d == 0) part_lse[po] = -INFINITY;
+    }
+    return;
+  }
+
+  // ---- query operand: lane (g, c) holds Q[h = c % G][g*QKE + 8j + e]
+  const int my_h = c % G;
+  const int my_sub = c / G;
+  f16x8 qop[NQ][Gm::kQkJ];
+  {
+    const int64_t qb = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(hq0 + my_h) * a.q_sh;
+#pragma unroll
+    for (int j = 0; j < Gm::kQkJ; ++j) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = g * Gm::kQkElems + 8 * j + e;
+        float x;
+        if constexpr (QF32) x = static_cast<const float*>(a.q)[qb + d];
+        else x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[qb + d]) << 16);
+        const _Float16 hi = static_cast<_Float16>(x);
+        qop[0][j][e] = hi;
+        if constexpr (QF32) qop[1][j][e] = static_cast<_Float16>(x - static_cast<float>(hi));
+      }
+    }
+  }
+
+  const float kscale = *a.k_scale;
+  const float vscale = *a.v_scale;
+  const float qk_scale = a.softmax_scale * kscale * kLog2e;
+
+  const int64_t head_row = static_cast<int64_t>(b) * a.kv_sb + static_cast<int64_t>(kvh) * a.kv_sh;
+  const uint8_t* kc = a.k_codes;
+  const uint8_t* vc = a.v_codes;
+  const uint8_t* ksc = a.k_scales;
+  const uint8_t* vsc = a.v_scales;
+
+  float m_run = -INFINITY;  // running max of row c (log2 domain)
+  float l_run = 0.0f;       // this lane's share of row c's denominator
+  f32x4 acc_o[Gm::kPvJ];
+#pragma unroll
+  for (int j = 0; j < Gm::kPvJ; ++j) acc_o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int ntiles = (ce - cs + TT - 1) / TT;
+  const f16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+
+  for (int tile = wave; tile < ntiles; tile += kWaves) {
+    const int tb = cs + tile * TT;
+
+    // ---------------- scores: S[token][(sub, h)] via block-diagonal MFMA
+    f32x4 acc_s[NACC];
+#pragma unroll
+    for (int x = 0; x < NACC; ++x) acc_s[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      int t = tb + 16 * u + c;
+      t = t < ce ? t : ce - 1;
+      const int64_t row = head_row + static_cast<int64_t>(t) * a.kv_st;
+      uint32_t kw[Gm::kKWords];
+      const uint8_t* kp = kc + row * Gm::kRowBytes + g * (Gm::kKWords * 4);
+      if constexpr (Gm::kKWords == 8) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(kp);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(kp + 16);
+        kw[0] = x0.x; kw[1] = x0.y; kw[2] = x0.z; kw[3] = x0.w;
+        kw[4] = x1.x; kw[5] = x1.y; kw[6] = x1.z; kw[7] = x1.w;
+      } else if constexpr (Gm::kKWords == 4) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(kp);
+        kw[0] = x0.x; kw[1] = x0.y; kw[2] = x0.z; kw[3] = x0.w;
+      } else {
+        const uint2 x0 = *reinterpret_cast<const uint2*>(kp);
+        kw[0] = x0.x; kw[1] = x0.y;
+      }
+      uint32_t ks = 0;
+      if constexpr (KVF == KVQ_NVFP4) {
+        const uint8_t* sp = ksc + row * Gm::kScaleBytes;
+        if constexpr (D == 128) ks = *reinterpret_cast<const uint16_t*>(sp + 2 * g);
+        else ks = sp[g];
+      }
+      const bool mine = (my_sub == (u % NSUB));
+#pragma unroll
+      for (int j = 0; j < Gm::kQkJ; ++j) {
+        const f16x8 kop = k_operand<KVF, D>(kw, ks, j);
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) {
+          const f16x8 qm = mine ? qop[qq][j] : zero8;
+          acc_s[u / NSUB] = mfma(kop, qm, acc_s[u / NSUB]);
+        }
+      }
+    }
+
+    // ---------------- online softmax per row c (this lane: 4*NACC tokens)
+    float sc[NACC][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < NACC; ++x) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tb + 16 * (x * NSUB + my_sub) + 4 * g + i;
+        const float v = (t < ce) ? acc_s[x][i] * qk_scale : -INFINITY;
+        sc[x][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    if (__any(m_new > m_run)) {
+      const float fac = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+      l_run *= fac;
+      float fr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fr[i] = __shfl(fac, 4 * g + i);
+#pragma unroll
+      for (int j = 0; j < Gm::kPvJ; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_o[j][i] *= fr[i];
+      }
+      m_run = m_new;
+    }
+    f16x2 p_hi[NACC][2], p_lo[NACC][2];
+#pragma unroll
+    for (int x = 0; x < NACC; ++x) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = (sc[x][i] == -INFINITY) ? 0.0f : exp2f(sc[x][i] - m_run);
+        l_run += p[i];
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const _Float16 h0 = static_cast<_Float16>(p[2 * k]);
+        const _Float16 h1 = static_cast<_Float16>(p[2 * k + 1]);
+        p_hi[x][k] = f16x2{h0, h1};
+        if constexpr (PSPLIT == 2)
+          p_lo[x][k] = f16x2{static_cast<_Float16>(p[2 * k] - static_cast<float>(h0)),
+                             static_cast<_Float16>(p[2 * k + 1] - static_cast<float>(h1))};
+      }
+    }
+
+    // ---------------- P.V over sub-tile pairs (u0, u1) = (2q, 2q+1)
+#pragma unroll
+    for (int q = 0; q < NT / 2; ++q) {
+      const int u0 = 2 * q, u1 = 2 * q + 1;
+      // A operand: k = 8g + e; e < 4 -> sub-tile u0 token 4g+e; e >= 4 -> u1
+      const bool own0 = (my_sub == (u0 % NSUB));
+      const bool own1 = (my_sub == (u1 % NSUB));
+      const f16x2 z2 = {0, 0};
+      f16x8 pa[PSPLIT];
+      {
+        const f16x2 a0 = own0 ? p_hi[u0 / NSUB][0] : z2, a1 = own0 ? p_hi[u0 / NSUB][1] : z2;
+        const f16x2 b0 = own1 ? p_hi[u1 / NSUB][0] : z2, b1 = own1 ? p_hi[u1 / NSUB][1] : z2;
+        pa[0] = cat4(a0, a1, b0, b1);
+        if constexpr (PSPLIT == 2) {
+          const f16x2 c0 = own0 ? p_lo[u0 / NSUB][0] : z2, c1 = own0 ? p_lo[u0 / NSUB][1] : z2;
+          const f16x2 d0 = own1 ? p_lo[u1 / NSUB][0] : z2, d1 = own1 ? p_lo[u1 / NSUB][1] : z2;
+          pa[1] = cat4(c0, c1, d0, d1);
+        }
+      }
+      // V: tokens 4g..4g+3 of u0 and u1, head_dim run [c*PVE, (c+1)*PVE)
+      f16x2 vt[8][Gm::kPvElems / 2];  // [token 0..7][pair]
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const int u = tt < 4 ? u0 : u1;
+        int t = tb + 16 * u + 4 * g + (tt & 3);
+        t = t < ce ? t : ce - 1;
+        const int64_t row = head_row + static_cast<int64_t>(t) * a.kv_st;
+        const uint8_t* vp = vc + row * Gm::kRowBytes + c * Gm::kVBytes;
+        uint32_t w0 = 0, w1 = 0, vs = 0;
+        if constexpr (Gm::kVBytes == 8) {
+          const uint2 x = *reinterpret_cast<const uint2*>(vp);
+          w0 = x.x; w1 = x.y;
+        } else if constexpr (Gm::kVBytes == 4) {
+          w0 = *reinterpret_cast<const uint32_t*>(vp);
+        } else {
+          w0 = *reinterpret_cast<const uint16_t*>(vp);
+        }
+        if constexpr (KVF == KVQ_NVFP4) vs = vsc[row * Gm::kScaleBytes + (c * Gm::kPvElems) / 16];
+        v_pairs<KVF, D>(w0, w1, vs, vt[tt]);
+      }
+#pragma unroll
+      for (int k = 0; k < Gm::kPvElems / 2; ++k) {
+        // output columns j = 2k (low halves) and 2k+1 (high halves)
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+          const uint32_t x0 = as_u32(vt[2 * pr][k]), x1 = as_u32(vt[2 * pr + 1][k]);
+          lo[pr] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+          hi[pr] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+        }
+        const f16x8 blo = cat4(as_h2(lo[0]), as_h2(lo[1]), as_h2(lo[2]), as_h2(lo[3]));
+        const f16x8 bhi = cat4(as_h2(hi[0]), as_h2(hi[1]), as_h2(hi[2]), as_h2(hi[3]));
+#pragma unroll
+        for (int ps = 0; ps < PSPLIT; ++ps) {
+          acc_o[2 * k] = mfma(pa[ps], blo, acc_o[2 * k]);
+          acc_o[2 * k + 1] = mfma(pa[ps], bhi, acc_o[2 * k + 1]);
+        }
+      }
+    }
+  }
+
+  // ---------------- per-wave state -> LDS
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (g == 0) {
+    lds_m[wave][c] = m_run;
+    lds_l[wave][c] = l_tot;
+  }
+#pragma unroll
+  for (int j = 0; j < Gm::kPvJ; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_o[wave][4 * g + i][c * Gm::kPvElems + j] = acc_o[j][i];
+  }
+  __syncthreads();
+
+  // ---------------- merge rows (wave, sub) of each head, write the partial
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int h = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) M = fmaxf(M, lds_m[w][s * G + h]);
+    float num = 0.0f, den = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          const float mv = lds_m[w][s * G + h];
+          if (mv == -INFINITY) continue;
+          const float f = exp2f(mv - M);
+          num += f * lds_o[w][s * G + h][d];
+          den += f * lds_l[w][s * G + h];
+        }
+    }
+    const int64_t po = (static_cast<int64_t>(b) * a.Hq + hq0 + h) * num_splits + split;
+    part_o[po * D + d] = den > 0.0f ? (num / den) * vscale : 0.0f;
+    if (d == 0) part_lse[po] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int KVF, int G, int D, bool QF32, int PSPLIT>
+hipError_t launch_t(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
+  dim3 grid(p.s, a.Hkv, a.B);
+  hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT>), grid, dim3(kThreads), 0, st, a, p.s);
+  return hipGetLastError();
+}
+
+template <int KVF, int G, int D>
+hipError_t launch_q(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
+  // fp32 queries select the fp32-accuracy path (hi/lo split of Q and P)
+  if (a.q_dtype == KVQ_F32) return launch_t<KVF, G, D, true, 2>(a, p, st);
+  return launch_t<KVF, G, D, false, 2>(a, p, st);
+}
+
+template <int KVF, int D>
+hipError_t launch_g(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_q<KVF, 1, D>(a, p, st);
+    case 2: return launch_q<KVF, 2, D>(a, p, st);
+    case 4: return launch_q<KVF, 4, D>(a, p, st);
+    case 8: return launch_q<KVF, 8, D>(a, p, st);
+    case 16: return launch_q<KVF, 16, D>(a, p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int gqa_tile_tokens(int G) {
+  const int nsub = 16 / G;
+  return 16 * (nsub < 2 ? 2 : nsub);
+}
+
+bool gqa_supported(int kv_format, int G, int D, int q_dtype) {
+  if (kv_format != KVQ_NVFP4 && kv_format != KVQ_FP8E4M3) return false;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return false;
+  if (D != 64 && D != 128) return false;
+  return q_dtype == KVQ_BF16 || q_dtype == KVQ_F32;
+}
+
+hipError_t launch_decode_gqa(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
+  if (a.kv_format == KVQ_NVFP4) {
+    return a.D == 128 ? launch_g<KVQ_NVFP4, 128>(a, p, st) : launch_g<KVQ_NVFP4, 64>(a, p, st);
+  }
+  return a.D == 128 ? launch_g<KVQ_FP8E4M3, 128>(a, p, st) : launch_g<KVQ_FP8E4M3, 64>(a, p, st);
+}
+
+}  // namespace kvq

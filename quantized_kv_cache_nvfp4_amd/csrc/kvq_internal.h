@@ -1,0 +1,48 @@
+// Internal declarations shared by the C-ABI layer (api.cpp) and the HIP
+// kernel files.  Not part of the public interface (that is include/kvq.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+struct Rows {
+  int64_t n0, n1, n2;
+  int64_t s0, s1, s2;
+};
+
+inline Rows to_rows(const kvq_rows& r) { return Rows{r.n0, r.n1, r.n2, r.s0, r.s1, r.s2}; }
+
+// ---- quantization kernels (quant_kernels.hip) ----
+hipError_t launch_amax(const void* x, int x_dtype, Rows rows, int d, const int32_t* kv_lens, float* amax_out,
+                       bool accumulate, hipStream_t st);
+hipError_t launch_pack_nvfp4(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes,
+                             uint8_t* scales, Rows dr, const int32_t* dst_pos, float* ts_out, hipStream_t st);
+hipError_t launch_pack_fp8(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes, Rows dr,
+                           const int32_t* dst_pos, float* scale_out, hipStream_t st);
+hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, Rows sr, int d, const float* ts,
+                               float* out, Rows orow, hipStream_t st);
+hipError_t launch_unpack_fp8(const uint8_t* codes, Rows sr, int d, const float* scale, float* out, Rows orow,
+                             hipStream_t st);
+
+// ---- decode (decode_gqa.hip, decode_mla.hip, combine.hip) ----
+struct DecodePlan {
+  int s;           // number of splits
+  int chunk;       // tokens per split (multiple of the kernel tile)
+};
+
+hipError_t launch_decode_gqa(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st);
+hipError_t launch_decode_mla(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st);
+hipError_t launch_decode_fp8p(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st);
+hipError_t launch_combine(const float* part_o, const float* part_lse, int B, int Hq, int Dv, int s, void* out,
+                          int out_dtype, const float* out_scale, float* lse_out, hipStream_t st);
+
+// tile (tokens) of the GQA kernel for a query-group width G and of the MLA kernel
+int gqa_tile_tokens(int G);
+int mla_tile_tokens();
+// is (format, G, D, q dtype) implemented by the GQA kernel
+bool gqa_supported(int kv_format, int G, int D, int q_dtype);
+
+}  // namespace kvq

@@ -1,0 +1,285 @@
+// Max calibration, NVFP4 / FP8 E4M3 packing and unpacking for gfx950.
+//
+// Formats: Model-Optimizer PR #714 "KV cache quantization for MLAAttention in
+// vLLM fakequant", Testing section (E2M1 elements in blocks of 16 along the
+// last dim, dynamic E4M3 block scale, per-tensor amax from a max
+// calibrator); compressed-tensors PR #436 kv_cache_scheme (per-tensor
+// symmetric static FP8 E4M3 from a min-max observer).
+//
+// Every rounding decision is the exact real-number decision.  The inputs have
+// at most 24 significant bits and every decision threshold (an E2M1 midpoint
+// times s_hat * s_t, or an E4M3 midpoint times 6 * s_t or times the FP8
+// scale) at most 32, so two that differ do so by at least 2^-32 relative;
+// a correctly rounded float64 quotient (error 2^-53) therefore lands on the
+// same side of every threshold as the real quotient, and exactly on it when
+// the real quotient is a tie.  Rounding is then done by power-of-two scaling
+// and rint (round half to even) on that float64 quotient.  A float32
+// quotient would not be exact here.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline float load_elem(const void* base, int dt, int64_t idx) {
+  if (dt == KVQ_F32) return static_cast<const float*>(base)[idx];
+  uint32_t bits = static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16;
+  return __uint_as_float(bits);
+}
+
+// unravel a flat row index into the (i0, i1, i2) of `r`
+__device__ inline void unravel(int64_t row, const Rows& r, int64_t& i0, int64_t& i1, int64_t& i2) {
+  i2 = row % r.n2;
+  int64_t t = row / r.n2;
+  i1 = t % r.n1;
+  i0 = t / r.n1;
+}
+
+__device__ inline int64_t row_off(const Rows& r, int64_t i0, int64_t i1, int64_t i2) {
+  return i0 * r.s0 + i1 * r.s1 + i2 * r.s2;
+}
+
+// ---------------------------------------------------------------- codecs
+// E4M3 (FN) code of the round-to-nearest-even of a non-negative double q,
+// saturating at 448.
+__device__ inline uint32_t e4m3_rne_code(double q) {
+  if (!(q < 448.0)) return 0x7E;
+  int ex;
+  (void)frexp(q, &ex);             // q = f * 2^ex, f in [0.5, 1)
+  int e = ex - 1;                  // floor(log2 q)
+  if (e < -6) e = -6;              // subnormal binade shares 2^-6's quantum
+  double n = rint(ldexp(q, 3 - e));  // exact scaling, round half to even
+  int ni = static_cast<int>(n);
+  if (ni == 0) return 0;
+  if (ni == 16) { e += 1; ni = 8; }
+  if (ni < 8) return static_cast<uint32_t>(ni);  // subnormal (e == -6)
+  return static_cast<uint32_t>(((e + 7) << 3) | (ni - 8));
+}
+
+// E2M1 code (0..7) of the round-to-nearest-even of a non-negative double r,
+// saturating at 6.
+__device__ inline uint32_t e2m1_rne_code(double r) {
+  if (!(r < 6.0)) return 7;
+  int ex;
+  (void)frexp(r, &ex);
+  int e = ex - 1;
+  if (e < 0) e = 0;
+  int ni = static_cast<int>(rint(ldexp(r, 1 - e)));
+  if (ni == 4) { e += 1; ni = 2; }
+  if (ni < 2) return static_cast<uint32_t>(ni);  // 0 or 0.5
+  return static_cast<uint32_t>(((e + 1) << 1) | (ni - 2));
+}
+
+__device__ inline double e4m3_value(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  double mag = (e == 0) ? ldexp(static_cast<double>(m), -9) : ldexp(static_cast<double>(8 + m), static_cast<int>(e) - 10);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+__device__ inline float e2m1_value(uint32_t c) {
+  uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  float mag = (e == 0) ? 0.5f * static_cast<float>(m) : ldexpf(1.0f + 0.5f * static_cast<float>(m), static_cast<int>(e) - 1);
+  return (c & 8u) ? -mag : mag;
+}
+
+__device__ inline float nvfp4_tensor_scale(float amax) {
+  return amax > 0.0f ? static_cast<float>(static_cast<double>(amax) / 2688.0) : 1.0f;
+}
+
+__device__ inline float fp8_tensor_scale(float amax) {
+  return amax > 0.0f ? static_cast<float>(static_cast<double>(amax) / 448.0) : 1.0f;
+}
+
+// ---------------------------------------------------------------- amax
+__global__ void k_zero_scalar(float* p) { *p = 0.0f; }
+
+__global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, int dt, Rows r, int d,
+                                                   const int32_t* __restrict__ kv_lens, float* __restrict__ out) {
+  const int64_t n_rows = r.n0 * r.n1 * r.n2;
+  const int64_t total = n_rows * d;
+  float m = 0.0f;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * kThreads) {
+    int64_t row = i / d;
+    int col = static_cast<int>(i - row * d);
+    int64_t i0, i1, i2;
+    unravel(row, r, i0, i1, i2);
+    if (kv_lens != nullptr && i2 >= kv_lens[i0]) continue;
+    m = fmaxf(m, fabsf(load_elem(x, dt, row_off(r, i0, i1, i2) + col)));
+  }
+  // wave64 reduction, then one atomic per wave (non-negative floats order as
+  // their bit patterns, so an unsigned max on the bits is a float max)
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+}
+
+// ---------------------------------------------------------------- NVFP4 pack
+// one thread per 16-element block: 16 exact decisions, 8 code bytes, 1 scale byte
+__global__ void __launch_bounds__(kThreads) k_pack_nvfp4(const void* __restrict__ x, int dt, Rows xr, int d,
+                                                         const float* __restrict__ amax, uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales, Rows dr,
+                                                         const int32_t* __restrict__ dst_pos, float* ts_out) {
+  const float s_t = nvfp4_tensor_scale(*amax);
+  const int nb = d / 16;
+  const int64_t total = xr.n0 * xr.n1 * xr.n2 * nb;
+  int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
+  if (gid == 0 && ts_out != nullptr) *ts_out = s_t;
+  for (; gid < total; gid += static_cast<int64_t>(gridDim.x) * kThreads) {
+    int64_t row = gid / nb;
+    int blk = static_cast<int>(gid - row * nb);
+    int64_t i0, i1, i2;
+    unravel(row, xr, i0, i1, i2);
+    const int64_t xo = row_off(xr, i0, i1, i2) + blk * 16;
+    float v[16];
+    float bamax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      v[i] = load_elem(x, dt, xo + i);
+      bamax = fmaxf(bamax, fabsf(v[i]));
+    }
+    const int64_t di2 = i2 + (dst_pos != nullptr ? dst_pos[i0] : 0);
+    if (di2 < 0 || di2 >= dr.n2) continue;  // outside the destination plane
+    const int64_t drow = row_off(dr, i0, i1, di2);
+    const uint32_t sc = e4m3_rne_code(static_cast<double>(bamax) / (6.0 * static_cast<double>(s_t)));
+    uint32_t lo = 0, hi = 0;
+    if (sc != 0) {
+      const double denom = e4m3_value(sc) * static_cast<double>(s_t);  // exact
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint32_t c = e2m1_rne_code(fabs(static_cast<double>(v[i])) / denom);
+        c |= (__float_as_uint(v[i]) >> 28) & 8u;  // sign of x, zero included
+        if (i < 8) lo |= c << (4 * i);
+        else hi |= c << (4 * (i - 8));
+      }
+    }
+    uint2* cp = reinterpret_cast<uint2*>(codes + drow * (d / 2) + blk * 8);
+    *cp = make_uint2(lo, hi);
+    scales[drow * nb + blk] = static_cast<uint8_t>(sc);
+  }
+}
+
+// ---------------------------------------------------------------- FP8 pack
+// one thread per 4 elements (one 32-bit code word)
+__global__ void __launch_bounds__(kThreads) k_pack_fp8(const void* __restrict__ x, int dt, Rows xr, int d,
+                                                       const float* __restrict__ amax, uint8_t* __restrict__ codes,
+                                                       Rows dr, const int32_t* __restrict__ dst_pos, float* sc_out) {
+  const float scale = fp8_tensor_scale(*amax);
+  const double dscale = static_cast<double>(scale);
+  const int nw = d / 4;
+  const int64_t total = xr.n0 * xr.n1 * xr.n2 * nw;
+  int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
+  if (gid == 0 && sc_out != nullptr) *sc_out = scale;
+  for (; gid < total; gid += static_cast<int64_t>(gridDim.x) * kThreads) {
+    int64_t row = gid / nw;
+    int w = static_cast<int>(gid - row * nw);
+    int64_t i0, i1, i2;
+    unravel(row, xr, i0, i1, i2);
+    const int64_t xo = row_off(xr, i0, i1, i2) + w * 4;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = load_elem(x, dt, xo + i);
+      uint32_t c = e4m3_rne_code(fabs(static_cast<double>(v)) / dscale);
+      c |= (__float_as_uint(v) >> 24) & 0x80u;
+      word |= c << (8 * i);
+    }
+    const int64_t di2 = i2 + (dst_pos != nullptr ? dst_pos[i0] : 0);
+    if (di2 < 0 || di2 >= dr.n2) continue;  // outside the destination plane
+    *reinterpret_cast<uint32_t*>(codes + row_off(dr, i0, i1, di2) * d + w * 4) = word;
+  }
+}
+
+// ---------------------------------------------------------------- unpack
+__global__ void __launch_bounds__(kThreads) k_unpack_nvfp4(const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales, Rows sr, int d,
+                                                           const float* __restrict__ ts, float* __restrict__ out,
+                                                           Rows orow) {
+  const float s_t = *ts;
+  const int nb = d / 16;
+  const int64_t total = sr.n0 * sr.n1 * sr.n2 * nb;
+  for (int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; gid < total;
+       gid += static_cast<int64_t>(gridDim.x) * kThreads) {
+    int64_t row = gid / nb;
+    int blk = static_cast<int>(gid - row * nb);
+    int64_t i0, i1, i2;
+    unravel(row, sr, i0, i1, i2);
+    const int64_t srow = row_off(sr, i0, i1, i2);
+    const uint2 cw = *reinterpret_cast<const uint2*>(codes + srow * (d / 2) + blk * 8);
+    const float s_hat = static_cast<float>(e4m3_value(scales[srow * nb + blk]));
+    float* o = out + row_off(orow, i0, i1, i2) + blk * 16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t c = ((i < 8 ? cw.x : cw.y) >> (4 * (i & 7))) & 15u;
+      o[i] = (e2m1_value(c) * s_hat) * s_t;  // e * s_hat exact in fp32, one rounding
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) k_unpack_fp8(const uint8_t* __restrict__ codes, Rows sr, int d,
+                                                         const float* __restrict__ scale, float* __restrict__ out,
+                                                         Rows orow) {
+  const float sc = *scale;
+  const int64_t total = sr.n0 * sr.n1 * sr.n2 * d;
+  for (int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; gid < total;
+       gid += static_cast<int64_t>(gridDim.x) * kThreads) {
+    int64_t row = gid / d;
+    int col = static_cast<int>(gid - row * d);
+    int64_t i0, i1, i2;
+    unravel(row, sr, i0, i1, i2);
+    uint32_t c = codes[row_off(sr, i0, i1, i2) * d + col];
+    out[row_off(orow, i0, i1, i2) + col] = static_cast<float>(e4m3_value(c)) * sc;
+  }
+}
+
+int grid_for(int64_t items) {
+  int64_t g = (items + kThreads - 1) / kThreads;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;  // grid-stride loops cover the rest
+  return static_cast<int>(g);
+}
+
+}  // namespace
+
+hipError_t launch_amax(const void* x, int x_dtype, Rows rows, int d, const int32_t* kv_lens, float* amax_out,
+                       bool accumulate, hipStream_t st) {
+  if (!accumulate) hipLaunchKernelGGL(k_zero_scalar, dim3(1), dim3(1), 0, st, amax_out);
+  const int64_t items = rows.n0 * rows.n1 * rows.n2 * d;
+  if (items > 0) hipLaunchKernelGGL(k_amax, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, rows, d, kv_lens, amax_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_nvfp4(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes,
+                             uint8_t* scales, Rows dr, const int32_t* dst_pos, float* ts_out, hipStream_t st) {
+  const int64_t items = xr.n0 * xr.n1 * xr.n2 * (d / 16);
+  hipLaunchKernelGGL(k_pack_nvfp4, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes, scales,
+                     dr, dst_pos, ts_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_fp8(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes, Rows dr,
+                           const int32_t* dst_pos, float* scale_out, hipStream_t st) {
+  const int64_t items = xr.n0 * xr.n1 * xr.n2 * (d / 4);
+  hipLaunchKernelGGL(k_pack_fp8, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes, dr,
+                     dst_pos, scale_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, Rows sr, int d, const float* ts,
+                               float* out, Rows orow, hipStream_t st) {
+  const int64_t items = sr.n0 * sr.n1 * sr.n2 * (d / 16);
+  hipLaunchKernelGGL(k_unpack_nvfp4, dim3(grid_for(items)), dim3(kThreads), 0, st, codes, scales, sr, d, ts, out, orow);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_fp8(const uint8_t* codes, Rows sr, int d, const float* scale, float* out, Rows orow,
+                             hipStream_t st) {
+  const int64_t items = sr.n0 * sr.n1 * sr.n2 * d;
+  hipLaunchKernelGGL(k_unpack_fp8, dim3(grid_for(items)), dim3(kThreads), 0, st, codes, sr, d, scale, out, orow);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,125 @@
+"""Shared plumbing for the GPU parity tests: run the HIP path through the C ABI
+and the oracle on the same seeded inputs.  The oracle side never sees a value
+produced by the HIP path."""
+import functools
+import math
+
+import numpy as np
+import torch
+
+import kvq_synth
+from oracle import attention as OA
+from oracle import formats as OF
+from oracle import quant as OQ
+
+DEV = "cuda:0"
+
+
+def K():
+    import quantized_kv_cache_nvfp4_amd as mod
+    return mod
+
+
+def announce(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------- oracle side
+@functools.lru_cache(maxsize=8)
+def oracle_gqa(cfg_key):
+    """Oracle packing + dequantization of a GQA config (cached per session)."""
+    inp = make_inputs(cfg_key)
+    fmt = cfg_key[0]
+    announce(f"  oracle pack {cfg_key}")
+    kf, vf = kvq_synth.f64(inp.k), kvq_synth.f64(inp.v)
+    ka, va = OQ.amax(kf, inp.kv_lens), OQ.amax(vf, inp.kv_lens)
+    if fmt == "nvfp4":
+        kc, ks, kst = OQ.nvfp4_pack(kf, ka)
+        vc, vs, vst = OQ.nvfp4_pack(vf, va)
+        khat, vhat = OQ.nvfp4_unpack(kc, ks, kst), OQ.nvfp4_unpack(vc, vs, vst)
+        packed = dict(kc=kc, ks=ks, kst=kst, vc=vc, vs=vs, vst=vst, ka=ka, va=va)
+    else:
+        kc, kst = OQ.fp8_pack(kf, ka)
+        vc, vst = OQ.fp8_pack(vf, va)
+        khat, vhat = OQ.fp8_unpack(kc, kst), OQ.fp8_unpack(vc, vst)
+        packed = dict(kc=kc, kst=kst, vc=vc, vst=vst, ka=ka, va=va)
+    q64 = kvq_synth.f64(inp.q)
+    announce(f"  oracle attention {cfg_key}")
+    o, lse = OA.decode_gqa(q64, khat, vhat, inp.kv_lens, inp.softmax_scale)
+    return packed, o, lse, khat, vhat
+
+
+_INPUT_CACHE = {}
+
+
+def make_inputs(cfg_key):
+    """cfg_key: (fmt, name, *params)."""
+    if cfg_key in _INPUT_CACHE:
+        return _INPUT_CACHE[cfg_key]
+    fmt, name, *p = cfg_key
+    if name == "tiny":
+        inp = kvq_synth.tiny()
+    elif name == "gqa":
+        inp = kvq_synth.gqa(p[0])
+    elif name == "mha":
+        inp = kvq_synth.mha(p[0], B=p[1], H=p[2])
+    elif name == "fp8":
+        inp = kvq_synth.fp8_ragged(B=p[0])
+    elif name == "custom":
+        B, Hq, Hkv, D, lens, dt = p
+        inp = kvq_synth.gqa_inputs(B, Hq, Hkv, D, None, kv_lens=list(lens), config="gqa", salt=7,
+                                   dtype=torch.float32 if dt == "f32" else torch.bfloat16, outliers=False)
+    else:
+        raise KeyError(name)
+    _INPUT_CACHE[cfg_key] = inp
+    return inp
+
+
+# ---------------------------------------------------------------- GPU side
+def gpu_pack(inp, fmt):
+    k_ = K()
+    k, v = inp.k.to(DEV), inp.v.to(DEV)
+    lens = torch.from_numpy(inp.kv_lens).to(DEV)
+    ka, va = k_.kvq_amax(k, lens), k_.kvq_amax(v, lens)
+    if fmt == "nvfp4":
+        return k_.kvq_pack_nvfp4(k, ka), k_.kvq_pack_nvfp4(v, va), ka, va, lens
+    return k_.kvq_pack_fp8(k, ka), k_.kvq_pack_fp8(v, va), ka, va, lens
+
+
+def gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.bfloat16, out_scale=None, with_lse=False):
+    k_ = K()
+    B, Hq, D = inp.B, inp.Hq, inp.D
+    cap = 64
+    part_o = torch.empty(B * Hq * cap * D, dtype=torch.float32, device=DEV)
+    part_lse = torch.empty(B * Hq * cap, dtype=torch.float32, device=DEV)
+    q = inp.q.to(DEV)
+    args = k_.make_decode_args(q, kp, vp, lens, max_kv_len=inp.Lmax, softmax_scale=inp.softmax_scale,
+                               num_splits=s, part_o=part_o, part_lse=part_lse)
+    used = k_.attn_decode_splitkv(args)
+    out = torch.empty(B, Hq, D, dtype=out_dtype, device=DEV)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV) if with_lse else None
+    k_.attn_decode_combine(part_o, part_lse, B, Hq, D, used, out, out_scale=out_scale, lse_out=lse)
+    torch.cuda.synchronize()
+    return out, used, lse
+
+
+# ---------------------------------------------------------------- metrics
+def err_report(got, ref):
+    """The pages' three columns: max abs error, max rel error, cosine."""
+    g = np.asarray(got, np.float64).ravel()
+    r = np.asarray(ref, np.float64).ravel()
+    ae = np.abs(g - r)
+    rel = ae / np.maximum(np.abs(r), 1e-30)
+    cos = float(g @ r / max(np.linalg.norm(g) * np.linalg.norm(r), 1e-300))
+    return float(ae.max()), float(rel.max()), cos
+
+
+def assert_bf16_output(got_bf16, ref, label=""):
+    """Per element |o - o_ref| <= max(2e-3, 1 bf16 ulp(o_ref)) and cosine >= 0.9999."""
+    g = got_bf16.float().cpu().double().numpy()
+    tol = np.maximum(2e-3, OF.bf16_ulp(ref))
+    bad = np.abs(g - ref) > tol
+    mae, mre, cos = err_report(g, ref)
+    assert not bad.any(), f"{label}: {bad.sum()} elements out of tolerance; max abs {mae:.3g}"
+    assert cos >= 0.9999, f"{label}: cosine {cos}"
+    return mae, mre, cos

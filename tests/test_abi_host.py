@@ -1,0 +1,155 @@
+"""Host-side tests of the C ABI: the library loads and exports every function
+include/kvq.h declares, the pure-host planning functions, and the argument
+validation (every rejected call returns before any HIP call, so these run
+without a GPU)."""
+import ctypes
+import math
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from quantized_kv_cache_nvfp4_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _lib.lib()
+
+
+@pytest.fixture(scope="module")
+def K():
+    import quantized_kv_cache_nvfp4_amd as K
+    return K
+
+
+def test_exports_every_declared_symbol(L):
+    from quantized_kv_cache_nvfp4_amd import _lib
+    names = _lib.header_functions()
+    assert {"kvq_pack_nvfp4", "kvq_pack_fp8", "attn_decode_splitkv", "attn_decode_combine",
+            "kvq_auto_num_splits"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libkvq.so does not export {n}"
+    assert L.kvq_version() >= 100
+
+
+def test_auto_split_worked_values(K):
+    # 256 CUs (MI355X): GQA 4:1, B=2, 8 kv heads, 32K -> 32 splits
+    assert K.kvq_auto_num_splits(256, 2, 8, 32768, 128, 32) == 32
+    # short context caps at ceil(L / 256)
+    assert K.kvq_auto_num_splits(256, 2, 8, 1024, 128, 32) == 4
+    # MHA B=1 H=32 32K: 2*256/32 = 16
+    assert K.kvq_auto_num_splits(256, 1, 32, 32768, 128, 32) == 16
+    # large batch: already 512 programs -> 1
+    assert K.kvq_auto_num_splits(256, 64, 8, 4096, 128, 32) == 1
+    # MLA: one program per request, partial traffic bound
+    s = K.kvq_auto_num_splits(256, 32, 1, 8192, 512, 16)
+    assert 1 <= s <= 16
+    assert K.kvq_auto_num_splits(256, 1, 1, 0, 128, 1) == 1
+
+
+def test_auto_split_properties(K):
+    for cus in (80, 256, 304):
+        for B in (1, 2, 8, 64):
+            for P in (1, 8, 32):
+                for Lm in (1, 100, 1000, 32768, 1 << 20):
+                    s = K.kvq_auto_num_splits(cus, B, P, Lm, 128, P * 4)
+                    assert 1 <= s <= 64
+                    assert s <= max(1, math.ceil(Lm / 256))
+
+
+def test_auto_split_rejects_bad_args(K):
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_auto_num_splits(0, 1, 1, 10, 128, 1)
+    assert e.value.code == 1
+
+
+def test_fp8p_scratch_size(K):
+    assert K.kvq_fp8p_scratch_floats(2, 4, 3, 100) == 2 * 4 * (100 + 6 + 2)
+    assert K.kvq_fp8p_scratch_floats(0, 4, 3, 100) == 0
+
+
+def _rows(n0, n1, n2, s0, s1, s2):
+    from quantized_kv_cache_nvfp4_amd._lib import KvqRows
+    return KvqRows(n0, n1, n2, s0, s1, s2)
+
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: every call below is rejected
+FAKE_ODD = ctypes.c_void_p(0x10001)
+
+
+def test_pack_validation(L, K):
+    r = _rows(1, 1, 4, 0, 0, 24)
+    rc = L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r, 24, FAKE, FAKE, FAKE, r, None, None, None)
+    assert rc == 1 and "multiple of 16" in K.kvq_last_error()
+    r16 = _rows(1, 1, 4, 0, 0, 16)
+    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r16, 16, None, FAKE, FAKE, r16, None, None, None) == 1
+    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_F16, r16, 16, FAKE, FAKE, FAKE, r16, None, None, None) == 2
+    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE_ODD, FAKE, r16, None, None, None) == 3
+    rdiff = _rows(1, 2, 5, 0, 0, 1)
+    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE, FAKE, rdiff, None, None, None) == 1
+    assert L.kvq_pack_fp8(FAKE, K.KVQ_BF16, r16, 6, FAKE, FAKE, r16, None, None, None) == 1
+    assert L.kvq_pack_fp8(FAKE, K.KVQ_F32, _rows(-1, 1, 1, 0, 0, 0), 16, FAKE, FAKE, r16, None, None, None) == 1
+    assert L.kvq_amax(None, K.KVQ_F32, r16, 16, None, FAKE, 0, None) == 1
+    assert L.kvq_amax(FAKE, K.KVQ_F32, r16, 0, None, FAKE, 0, None) == 1
+    assert L.kvq_unpack_nvfp4(FAKE, FAKE, r16, 20, FAKE, FAKE, r16, None) == 1
+    assert L.kvq_unpack_fp8(FAKE, r16, 16, None, FAKE, r16, None) == 1
+
+
+def _good_args(K):
+    a = K.KvqDecodeArgs()
+    a.kv_format, a.layout = K.KVQ_NVFP4, K.KVQ_LAYOUT_GQA
+    a.B, a.Hq, a.Hkv, a.D, a.Dv = 2, 32, 8, 128, 128
+    a.max_kv_len = 1024
+    a.q, a.q_dtype = FAKE, K.KVQ_BF16
+    a.k_codes = a.k_scales = a.k_scale = FAKE
+    a.v_codes = a.v_scales = a.v_scale = FAKE
+    a.kv_lens = FAKE
+    a.softmax_scale = 0.088
+    a.num_splits = 4
+    a.part_o = a.part_lse = FAKE
+    a.part_capacity = 4
+    return a
+
+
+def _decode_rc(L, a):
+    s = ctypes.c_int32(0)
+    return L.attn_decode_splitkv(ctypes.byref(a), ctypes.byref(s), None)
+
+
+def test_decode_validation(L, K):
+    a = _good_args(K); a.Hq = 30
+    assert _decode_rc(L, a) == 1                     # Hq % Hkv
+    a = _good_args(K); a.Hq, a.Hkv = 24, 8
+    assert _decode_rc(L, a) == 2                     # G = 3 unsupported
+    a = _good_args(K); a.D = a.Dv = 96
+    assert _decode_rc(L, a) == 2                     # D = 96 unsupported
+    a = _good_args(K); a.num_splits = 8
+    assert _decode_rc(L, a) == 4                     # exceeds part_capacity
+    a = _good_args(K); a.num_splits = 65; a.part_capacity = 100
+    assert _decode_rc(L, a) == 1
+    a = _good_args(K); a.k_codes = FAKE_ODD
+    assert _decode_rc(L, a) == 3
+    a = _good_args(K); a.kv_format = 7
+    assert _decode_rc(L, a) == 2
+    a = _good_args(K); a.softmax_scale = float("nan")
+    assert _decode_rc(L, a) == 1
+    a = _good_args(K); a.kv_lens = None
+    assert _decode_rc(L, a) == 1
+    a = _good_args(K); a.layout = K.KVQ_LAYOUT_MLA; a.Hkv = 2; a.Hq = 16
+    assert _decode_rc(L, a) == 1                     # MLA needs Hkv == 1
+    a = _good_args(K); a.k_scales = None
+    assert _decode_rc(L, a) == 1
+    assert L.attn_decode_splitkv(None, None, None) == 1
+
+
+def test_combine_validation(L, K):
+    assert L.attn_decode_combine(FAKE, FAKE, 2, 4, 128, 0, FAKE, K.KVQ_F32, None, None, None) == 1
+    assert L.attn_decode_combine(FAKE, FAKE, 2, 4, 128, 65, FAKE, K.KVQ_F32, None, None, None) == 1
+    assert L.attn_decode_combine(FAKE, FAKE, 2, 4, 128, 2, FAKE, K.KVQ_NVFP4, None, None, None) == 2
+    assert L.attn_decode_combine(FAKE, FAKE, 2, 4, 128, 2, FAKE, K.KVQ_FP8E4M3, None, None, None) == 1
+    assert L.attn_decode_combine(None, FAKE, 2, 4, 128, 2, FAKE, K.KVQ_F32, None, None, None) == 1
+    assert L.attn_decode_combine(FAKE, FAKE, 2, 4, 128, 2, FAKE_ODD, K.KVQ_BF16, None, None, None) == 3

@@ -1,0 +1,184 @@
+"""GPU parity: amax, NVFP4 / FP8 pack and unpack are bit-exact against the
+oracle (the pages fix the formats; every decision is exact-real on both
+sides)."""
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth
+from oracle import formats as OF
+from oracle import quant as OQ
+
+from gpu_helpers import DEV, K, announce
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg", [("tiny",), ("gqa", 1024), ("mha", 1024)], ids=str)
+def test_amax_and_nvfp4_pack_bit_exact(cfg):
+    announce(f"pack nvfp4 {cfg}")
+    inp = kvq_synth.tiny() if cfg[0] == "tiny" else (kvq_synth.gqa(cfg[1]) if cfg[0] == "gqa" else kvq_synth.mha(cfg[1]))
+    for x in (inp.k, inp.v):
+        xd = x.to(DEV)
+        amax = K().kvq_amax(xd)
+        xf = kvq_synth.f64(x)
+        ref_amax = OQ.amax(xf)
+        assert float(amax.item()) == ref_amax
+        p = K().kvq_pack_nvfp4(xd, amax)
+        c, s, st = OQ.nvfp4_pack(xf, ref_amax)
+        torch.cuda.synchronize()
+        assert float(p.tensor_scale.item()) == st
+        assert np.array_equal(_np(p.scales), s)
+        assert np.array_equal(_np(p.codes), c)
+        # unpack: fp32(e * s_hat * s_t), one rounding
+        u = K().kvq_unpack_nvfp4(p)
+        assert np.array_equal(_np(u).astype(np.float64), OF.fp32_round(OQ.nvfp4_unpack(c, s, st)))
+
+
+def test_amax_masks_ragged_padding():
+    announce("amax ragged")
+    inp = kvq_synth.fp8_ragged(B=8, lo=100, hi=700)
+    lens = torch.from_numpy(inp.kv_lens).to(DEV)
+    xd = inp.k.to(DEV)
+    xd[:, :, -1, 0] = 1e4     # padding beyond every length (max len < 700 = Lmax) ... unless a request has len 700
+    got = float(K().kvq_amax(xd, lens).item())
+    ref = OQ.amax(kvq_synth.f64(xd.cpu()), inp.kv_lens)
+    assert got == ref
+    # accumulate = max-merge into an existing value
+    out = torch.full((1,), 1e6, dtype=torch.float32, device=DEV)
+    K().kvq_amax(xd, lens, out=out, accumulate=True)
+    assert float(out.item()) == 1e6
+
+
+def _adversarial_rows():
+    """Rows that sit on every E2M1 / E4M3 decision boundary, plus zeros, -0,
+    subnormal block scales and saturation; one 2688-scaled anchor fixes s_t."""
+    rows = []
+    s_t = 1.0
+    for s_hat in [1.0, 0.875, 2.0 ** -7, 3 * 2.0 ** -9, 2.0 ** -9, 448.0, 13 * 2.0 ** -8, 1.5]:
+        d = s_hat * s_t
+        for mid in [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]:
+            for x in [mid * d, np.nextafter(np.float32(mid * d), np.float32(0)),
+                      np.nextafter(np.float32(mid * d), np.float32(1e9))]:
+                r = np.zeros(16, np.float32)
+                r[0] = 6 * d
+                r[1] = x
+                r[2] = -x
+                r[3] = -0.0
+                rows.append(r)
+    # block-scale boundaries: bamax / 6 exactly at and around E4M3 midpoints
+    pos = OF.e4m3_decode(np.arange(0x7F))
+    for a, b in zip(pos[:-1], pos[1:]):
+        m = np.float32((a + b) / 2 * 6)
+        for x in (m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1e9))):
+            r = np.zeros(16, np.float32)
+            r[5] = x
+            r[6] = x / 3
+            rows.append(r)
+    z = np.zeros(16, np.float32); z[7] = -0.0
+    rows.append(z)
+    big = np.zeros(16, np.float32); big[0] = 2688.0; big[1] = -2000.0; big[2] = 2e-6
+    rows.append(big)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_nvfp4_pack_adversarial(dt):
+    announce(f"pack nvfp4 adversarial {dt}")
+    x = torch.from_numpy(_adversarial_rows()).to(dt)
+    x = x.reshape(-1, 64) if x.shape[0] % 4 == 0 else x
+    xf = kvq_synth.f64(x)
+    amax_val = np.float32(2688.0)
+    amax = torch.tensor([amax_val], device=DEV)
+    p = K().kvq_pack_nvfp4(x.to(DEV), amax)
+    c, s, st = OQ.nvfp4_pack(xf, amax_val)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(p.scales), s)
+    assert np.array_equal(_np(p.codes), c)
+
+
+def test_nvfp4_golden_blocks_on_gpu():
+    announce("pack nvfp4 golden")
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_blocks.txt")
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        head, xs, sc, codes = [p.strip() for p in line.split("|")]
+        amax = float(head.split("amax=")[1])
+        x = torch.tensor([[float(v) for v in xs.split()]], dtype=torch.float32, device=DEV)
+        p = K().kvq_pack_nvfp4(x, torch.tensor([amax], device=DEV))
+        torch.cuda.synchronize()
+        assert int(p.scales[0, 0].item()) == int(sc, 16), head
+        assert [int(b) for b in _np(p.codes[0])] == [int(v, 16) for v in codes.split()], head
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_fp8_pack_bit_exact(dt):
+    announce(f"pack fp8 {dt}")
+    inp = kvq_synth.fp8_ragged(B=4, lo=64, hi=300)
+    x = inp.k.to(dt)
+    extra = torch.from_numpy(np.concatenate([
+        np.ldexp(np.arange(1, 300, dtype=np.float64), -12), [1.0625, 1.1875, 2 ** -10, 3 * 2 ** -10, -0.0, 464.0, 470.0]
+    ]).astype(np.float32)).to(dt)
+    x.view(-1)[:extra.numel()] = extra
+    xd = x.to(DEV)
+    amax = K().kvq_amax(xd)
+    p = K().kvq_pack_fp8(xd, amax)
+    xf = kvq_synth.f64(x)
+    c, sc = OQ.fp8_pack(xf, OQ.amax(xf))
+    torch.cuda.synchronize()
+    assert float(p.scale.item()) == sc
+    assert np.array_equal(_np(p.codes), c)
+    u = K().kvq_unpack_fp8(p)
+    assert np.array_equal(_np(u).astype(np.float64), OF.fp32_round(OQ.fp8_unpack(c, sc)))
+
+
+def test_append_with_dst_pos():
+    announce("pack append dst_pos")
+    B, H, Lmax, D = 3, 2, 40, 128
+    cache = K().NVFP4Plane(torch.zeros(B, H, Lmax, D // 2, dtype=torch.uint8, device=DEV),
+                           torch.zeros(B, H, Lmax, D // 16, dtype=torch.uint8, device=DEV),
+                           torch.zeros(1, device=DEV))
+    new = torch.randn(B, H, 1, D, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    pos = torch.tensor([5, 0, 39], dtype=torch.int32, device=DEV)
+    amax = torch.tensor([20.0], device=DEV)
+    K().kvq_pack_nvfp4(new.to(DEV), amax, out=cache, dst_pos=pos)
+    c, s, st = OQ.nvfp4_pack(kvq_synth.f64(new), 20.0)
+    torch.cuda.synchronize()
+    cc, cs = _np(cache.codes), _np(cache.scales)
+    for b, p in enumerate([5, 0, 39]):
+        assert np.array_equal(cc[b, :, p], c[b, :, 0])
+        assert np.array_equal(cs[b, :, p], s[b, :, 0])
+        mask = np.ones(Lmax, bool); mask[p] = False
+        assert not cc[b, :, mask].any()
+
+
+def test_full_size_gqa32k_sampled_rows():
+    """The bench workload's cache (B=2, Hkv=8, 32K, D=128 with outliers):
+    codes and scales of sampled rows (plus the amax row) bit-exact."""
+    announce("pack nvfp4 gqa-32k sampled")
+    inp = kvq_synth.gqa(32768)
+    for x in (inp.k, inp.v):
+        xd = x.to(DEV)
+        amax = K().kvq_amax(xd)
+        p = K().kvq_pack_nvfp4(xd, amax)
+        flat = x.reshape(-1, 128)
+        rng = np.random.default_rng(0)
+        rows = rng.choice(flat.shape[0], 4096, replace=False)
+        am_row = int(torch.argmax(flat.float().abs().max(dim=1).values))
+        rows = np.unique(np.append(rows, am_row))
+        xf = kvq_synth.f64(flat[torch.from_numpy(rows)])
+        ref_amax = float(np.float32(amax.item()))
+        assert ref_amax == OQ.amax(kvq_synth.f64(flat[am_row:am_row + 1]))
+        c, s, st = OQ.nvfp4_pack(xf, ref_amax)
+        torch.cuda.synchronize()
+        gc = _np(p.codes.reshape(-1, 64))[rows]
+        gs = _np(p.scales.reshape(-1, 8))[rows]
+        assert np.array_equal(gs, s)
+        assert np.array_equal(gc, c)
