@@ -1,0 +1,249 @@
+"""Benchmark: NVFP4-KV split-KV decode step on one MI355X.
+
+Workload: GQA 4:1 decode, B=2, Hq=32, Hkv=8, head_dim=128, kv_len=32768
+(the split-KV accuracy table shape of Model-Optimizer PR #1832), K/V ~ N(0,1)
+with 4 outlier channels x20 per kv head, bf16, packed to NVFP4; bf16 output;
+softmax scale 1/sqrt(128).
+
+One step = the decode-time hot path on one batch: quantize-on-append of the
+new token's K and V rows into the NVFP4 cache (kvq_pack_nvfp4 with the
+calibrated amax), split-KV decode over the whole cache and the combine of the
+partials, here through attn_decode (both in one launch; the two-launch
+attn_decode_splitkv + attn_decode_combine path is timed beside it).  Calibration (kvq_amax) and the bulk
+packing of the cache run once before the timed region.
+
+The 256 MB Infinity Cache would hold one 75.5 MB cache, so every step reads a
+different copy from a rotation of >= 1 GiB of identical caches (as successive
+layers would).  Steps are captured in a HIP graph and replayed; the timed
+region is bracketed by synchronizations.
+
+Prints one JSON line (see the keys below).  ``--gpus N`` with N > 1 exits:
+this build runs on one GPU.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/decode step + achieved HBM GB/s, NVFP4-KV split-KV decode B=2 GQA4:1 32K"
+HBM_PEAK_GBPS = 8000.0
+B, HQ, HKV, D, L = 2, 32, 8, 128, 32768
+BYTES_PER_TOKEN_HEAD = 2 * (D // 2 + D // 16)   # K and V: codes + E4M3 scales = 144 B
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--splits", type=int, default=0, help="<= 0: auto")
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, reps):
+    """The oracle, untouched, timed on this host: per step it dequantizes the
+    packed cache and runs exact fp64 attention for all 2 x 32 heads, plus
+    packs the new token.  Sample: `reps` full steps (each over the full 32K
+    cache); the oracle's one-off packing of the cache is not timed."""
+    import numpy as np
+    import kvq_synth
+    from oracle import attention as OA
+    from oracle import quant as OQ
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
+    except Exception:
+        threads = 1
+    log("oracle: packing the cache once (untimed)")
+    kf, vf = kvq_synth.f64(inp.k), kvq_synth.f64(inp.v)
+    ka, va = OQ.amax(kf), OQ.amax(vf)
+    kc, ks, kst = OQ.nvfp4_pack(kf, ka)
+    vc, vs, vst = OQ.nvfp4_pack(vf, va)
+    q = kvq_synth.f64(inp.q)
+    new = kf[:, :, -1:, :]
+    times = []
+    for r in range(reps):
+        log(f"oracle step {r + 1}/{reps}")
+        t0 = time.perf_counter()
+        OQ.nvfp4_pack(new, ka)
+        OQ.nvfp4_pack(new, va)
+        khat, vhat = OQ.nvfp4_unpack(kc, ks, kst), OQ.nvfp4_unpack(vc, vs, vst)
+        OA.decode_gqa(q, khat, vhat, inp.kv_lens, inp.softmax_scale)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": t * 1e6, "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full steps (B=2, 32 heads, 32K tokens): fp64 dequantize + exact attention + "
+                      f"pack of the new token; median {t:.2f} s/step; numpy elementwise single-threaded, "
+                      f"BLAS threads {threads}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import kvq_synth
+    import quantized_kv_cache_nvfp4_amd as K
+
+    K._lib.lib()  # fails loudly if libkvq.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating inputs")
+    inp = kvq_synth.gqa(L)
+    kv_lens = torch.from_numpy(inp.kv_lens).to(dev)
+    q = inp.q.to(dev)
+    k = inp.k.to(dev)
+    v = inp.v.to(dev)
+    # calibration + bulk pack (untimed)
+    k_amax, v_amax = K.kvq_amax(k, kv_lens), K.kvq_amax(v, kv_lens)
+    # K planes row-major; V planes in the TOKEN4 layout (four consecutive
+    # tokens interleaved per 8-element chunk: one 16-byte load per lane)
+    kp0 = K.kvq_pack_nvfp4(k, k_amax)
+    vp0 = K.kvq_pack_nvfp4(v, v_amax, layout=K.KVQ_PLANE_TOKEN4)
+    new_k = k[:, :, L - 1:L, :].contiguous()
+    new_v = v[:, :, L - 1:L, :].contiguous()
+    del k, v
+    pos = torch.full((B,), L - 1, dtype=torch.int32, device=dev)
+
+    per_copy = sum(t.numel() for t in (kp0.codes, kp0.scales, vp0.codes, vp0.scales))
+    assert per_copy == B * HKV * L * BYTES_PER_TOKEN_HEAD
+    n_copies = max(2, math.ceil(args.rotate_gib * (1 << 30) / per_copy))
+    log(f"rotation: {n_copies} cache copies x {per_copy / 1e6:.1f} MB")
+    copies = [(kp0, vp0)]
+    for _ in range(n_copies - 1):
+        copies.append((K.NVFP4Plane(kp0.codes.clone(), kp0.scales.clone(), kp0.tensor_scale.clone(), kp0.layout),
+                       K.NVFP4Plane(vp0.codes.clone(), vp0.scales.clone(), vp0.tensor_scale.clone(), vp0.layout)))
+
+    cus = K.kvq_device_cu_count()
+    s = args.splits if args.splits > 0 else K.kvq_auto_num_splits(cus, B, HKV, L, D, HQ)
+    part_o = torch.empty(B * HQ * s * D, dtype=torch.float32, device=dev)
+    part_lse = torch.empty(B * HQ * s, dtype=torch.float32, device=dev)
+    out = torch.empty(B, HQ, D, dtype=torch.bfloat16, device=dev)
+    counters = torch.zeros(B * HKV, dtype=torch.int32, device=dev)
+    dargs = [K.make_decode_args(q, kc, vc, kv_lens, max_kv_len=L, softmax_scale=inp.softmax_scale,
+                                num_splits=s, part_o=part_o, part_lse=part_lse) for kc, vc in copies]
+
+    def step(i, with_append=True, fused=True):
+        kc, vc = copies[i]
+        if with_append:
+            K.kvq_pack_nvfp4(new_k, k_amax, out=kc, dst_pos=pos)
+            K.kvq_pack_nvfp4(new_v, v_amax, out=vc, dst_pos=pos)
+        if fused:
+            K.attn_decode(dargs[i], out, counters=counters)
+        else:
+            used = K.attn_decode_splitkv(dargs[i])
+            K.attn_decode_combine(part_o, part_lse, B, HQ, D, used, out)
+
+    # warm-up (eager), then capture one graph over all copies
+    for i in range(max(args.warmup, n_copies)):
+        step(i % n_copies)
+    torch.cuda.synchronize()
+
+    def capture(with_append, fused=True):
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            step(0, with_append, fused)  # eager once on the capture stream
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(n_copies):
+                step(i, with_append, fused)
+        torch.cuda.synchronize()
+        return g
+
+    g_full = capture(True)
+    g_dec = capture(False)
+    g_two = capture(False, fused=False)
+    reps = max(1, math.ceil(args.steps / n_copies))
+    steps = reps * n_copies
+
+    def timed(g):
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per step
+
+    log(f"timing {steps} steps (graph of {n_copies} steps x {reps})")
+    ms_full = timed(g_full)
+    ms_dec = timed(g_dec)
+    ms_two = timed(g_two)
+
+    # per-launch duration of the split-KV kernel: HIP events around each
+    # launch on the launch stream, queued behind a spin kernel so that the
+    # GPU runs them back to back
+    n_ev = 4 * n_copies
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(20_000_000)
+    for j in range(n_ev):
+        evs[j][0].record()
+        K.attn_decode_splitkv(dargs[j % n_copies])
+        evs[j][1].record()
+    torch.cuda.synchronize()
+    k_ms = [a.elapsed_time(b) for a, b in evs]
+    kernel_us = float(np.mean(k_ms)) * 1e3
+    kernel_med_us = float(np.median(k_ms)) * 1e3
+
+    # correctness spot check of the last output against nothing but itself:
+    # the parity tests cover accuracy; here only finiteness is asserted
+    assert torch.isfinite(out.float()).all()
+
+    algo_bytes = B * HKV * L * BYTES_PER_TOKEN_HEAD
+    achieved = algo_bytes / (kernel_us * 1e-6) / 1e9
+    step_us = ms_full * 1e3
+    res = {
+        "metric": METRIC,
+        "value": round(step_us, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_full, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA, fp32 accumulate (NVFP4 KV)",
+        "data": "synthetic",
+        "config": {"workload": "NVFP4-KV split-KV decode, GQA 4:1", "B": B, "Hq": HQ, "Hkv": HKV,
+                   "head_dim": D, "kv_len": L, "splits": s, "out_dtype": "bf16",
+                   "v_layout": "token4", "rotation_copies": n_copies},
+        "hbm_gbps_step": round(algo_bytes / (step_us * 1e-6) / 1e9, 1),
+        "decode_only_us": round(ms_dec * 1e3, 3),
+        "hbm_gbps_decode_only": round(algo_bytes / (ms_dec * 1e-3) / 1e9, 1),
+        "two_launch_decode_us": round(ms_two * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "k_decode_gqa<NVFP4,G=4,D=128>", "kernel_us_mean": round(kernel_us, 3),
+                     "kernel_us_median": round(kernel_med_us, 3), "algorithmic_bytes": algo_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_reps)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -71,6 +71,25 @@ extern "C" {
 #define KVQ_FP8E4M3 3
 #define KVQ_NVFP4 4
 
+/* ---- packed plane layouts ----------------------------------------------- */
+/*
+ * KVQ_PLANE_ROWS: row r of a plane occupies bytes [r*R, (r+1)*R), R = the
+ *   plane's row bytes.
+ * KVQ_PLANE_TOKEN4: rows are taken in groups of four consecutive tokens
+ *   (i2 = 4q .. 4q+3), which share 4*R bytes starting at the address the
+ *   group's first row has in KVQ_PLANE_ROWS.  Inside a group each row is cut
+ *   into chunks of W bytes -- the codes of 8 elements (W = 4 for NVFP4 codes,
+ *   8 for FP8 codes) or one 16-element block's scale (W = 1 for NVFP4
+ *   scales) -- and chunk k of token 4q+j is stored at byte k*4*W + j*W of the
+ *   group.  One 16-byte load then yields 8 elements of 4 consecutive tokens,
+ *   which is the operand a wave64 lane feeds to the P.V matrix multiply; the
+ *   decode kernel reads V planes in this layout with a quarter of the load
+ *   instructions of the row layout.  Requires the token stride s2 == 1 and
+ *   s0, s1 and the plane length along i2 to be multiples of 4.
+ */
+#define KVQ_PLANE_ROWS 0
+#define KVQ_PLANE_TOKEN4 1
+
 /* ---- cache layouts ------------------------------------------------------ */
 #define KVQ_LAYOUT_GQA 0 /* K and V planes per (request, kv head, token)      */
 #define KVQ_LAYOUT_MLA 1 /* one latent plane per (request, token) + bf16 rope */
@@ -94,6 +113,9 @@ const char* kvq_last_error(void);
 
 /* Library version as 10000*major + 100*minor + patch. */
 int32_t kvq_version(void);
+
+/* sizeof(kvq_decode_args) as compiled into the library (binding check). */
+size_t kvq_decode_args_size(void);
 
 /*
  * kvq_amax - per-tensor max |x| (max calibration; Model-Optimizer PR #714,
@@ -121,6 +143,7 @@ int kvq_amax(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const i
  *   scales       device uint8 plane, rows of d/16 bytes.
  *   dst_rows     the destination plane: n0, n1 equal to x_rows', n2 (the
  *                plane's length along i2) >= x_rows.n2; strides in plane rows.
+ *   dst_layout   KVQ_PLANE_ROWS or KVQ_PLANE_TOKEN4 (both planes).
  *   dst_pos      device int32[n0] or NULL: row (i0, i1, i2) of x is stored at
  *                plane row (i0, i1, i2 + dst_pos[i0]) (append of new tokens);
  *                rows that would land outside [0, dst_rows.n2) are skipped.
@@ -128,31 +151,33 @@ int kvq_amax(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const i
  * Deterministic and bit-exact with the exact-real definition above.
  */
 int kvq_pack_nvfp4(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax,
-                   uint8_t* codes, uint8_t* scales, kvq_rows dst_rows, const int32_t* dst_pos,
-                   float* tensor_scale_out, void* stream);
+                   uint8_t* codes, uint8_t* scales, kvq_rows dst_rows, int32_t dst_layout,
+                   const int32_t* dst_pos, float* tensor_scale_out, void* stream);
 
 /*
  * kvq_pack_fp8 - quantize rows to per-tensor FP8 E4M3 (compressed-tensors
  * PR #436 kv_cache_scheme).  Arguments as kvq_pack_nvfp4; codes rows are d
- * bytes (d > 0, d % 4 == 0, <= 4096); scale_out (device float[1] or NULL)
- * receives the scale amax/448 (1 if amax == 0).
+ * bytes (d > 0, d % 4 == 0, <= 4096; d % 8 == 0 for KVQ_PLANE_TOKEN4);
+ * scale_out (device float[1] or NULL) receives the scale amax/448 (1 if
+ * amax == 0).
  */
 int kvq_pack_fp8(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax,
-                 uint8_t* codes, kvq_rows dst_rows, const int32_t* dst_pos, float* scale_out,
-                 void* stream);
+                 uint8_t* codes, kvq_rows dst_rows, int32_t dst_layout, const int32_t* dst_pos,
+                 float* scale_out, void* stream);
 
 /*
  * kvq_unpack_nvfp4 - dequantize NVFP4 rows to float32: out = fp32(E2M1(c) *
  * s_hat * s_t) (one rounding; e * s_hat is exact).  Test / inspection path.
- *   codes, scales  device planes per src_rows; tensor_scale device float[1];
+ *   codes, scales  device planes per src_rows and src_layout (KVQ_PLANE_*);
+ *                  tensor_scale device float[1];
  *   out            device float32 rows per out_rows (extents == src_rows').
  */
-int kvq_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, kvq_rows src_rows, int32_t d,
-                     const float* tensor_scale, float* out, kvq_rows out_rows, void* stream);
+int kvq_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, kvq_rows src_rows, int32_t src_layout,
+                     int32_t d, const float* tensor_scale, float* out, kvq_rows out_rows, void* stream);
 
 /* kvq_unpack_fp8 - out = fp32(E4M3(c) * scale); as kvq_unpack_nvfp4. */
-int kvq_unpack_fp8(const uint8_t* codes, kvq_rows src_rows, int32_t d, const float* scale, float* out,
-                   kvq_rows out_rows, void* stream);
+int kvq_unpack_fp8(const uint8_t* codes, kvq_rows src_rows, int32_t src_layout, int32_t d, const float* scale,
+                   float* out, kvq_rows out_rows, void* stream);
 
 /*
  * Decode arguments (one query token per request).
@@ -188,6 +213,10 @@ typedef struct {
   const uint8_t* v_codes;
   const uint8_t* v_scales;
   const float* v_scale;
+  int32_t v_layout;         /* KVQ_PLANE_ROWS or KVQ_PLANE_TOKEN4 (D = 128,
+                               kv_st = 1, kv_sb and kv_sh multiples of 4,
+                               the V planes at least roundup(max_kv_len, 4)
+                               tokens long); K planes are always ROWS     */
   const void* k_rope;       /* MLA: device bf16 rope-key rows              */
   int64_t kv_sb, kv_sh, kv_st;
   const int32_t* kv_lens;   /* device int32[B]                             */
@@ -234,6 +263,21 @@ int attn_decode_splitkv(const kvq_decode_args* args, int32_t* splits_used, void*
 int attn_decode_combine(const float* part_o, const float* part_lse, int32_t B, int32_t Hq, int32_t Dv,
                         int32_t num_splits, void* out, int32_t out_dtype, const float* out_scale,
                         float* lse_out, void* stream);
+
+/*
+ * attn_decode - attn_decode_splitkv and attn_decode_combine in one launch:
+ * the last work-group to finish a (request, kv head) merges its s partials
+ * and writes the output (with s == 1 the output is written directly and no
+ * partials or counters are touched).  Same results as the two-call path.
+ *   out, out_dtype, out_scale, lse_out  as attn_decode_combine.
+ *   counters  device int32[B * Hkv]: all zero before the first call; every
+ *             completed call leaves them zero.  Calls sharing a counters
+ *             buffer or partial buffers must not overlap (same stream is
+ *             fine).  Unused (may be NULL) when s == 1.
+ *   splits_used  host int32* or NULL: receives s.
+ */
+int attn_decode(const kvq_decode_args* args, void* out, int32_t out_dtype, const float* out_scale, float* lse_out,
+                int32_t* counters, int32_t* splits_used, void* stream);
 
 /*
  * kvq_auto_num_splits - split count when the caller passes num_splits <= 0

@@ -18,14 +18,15 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (KVQ_BF16, KVQ_F16, KVQ_F32, KVQ_FP8E4M3, KVQ_LAYOUT_GQA, KVQ_LAYOUT_MLA, KVQ_NVFP4, KvqError,
-                   KvqDecodeArgs, KvqRows, check)
+from ._lib import (KVQ_BF16, KVQ_F16, KVQ_F32, KVQ_FP8E4M3, KVQ_LAYOUT_GQA, KVQ_LAYOUT_MLA, KVQ_NVFP4,
+                   KVQ_PLANE_ROWS, KVQ_PLANE_TOKEN4, KvqError, KvqDecodeArgs, KvqRows, check)
 
 __all__ = [
     "kvq_amax", "kvq_pack_nvfp4", "kvq_pack_fp8", "kvq_unpack_nvfp4", "kvq_unpack_fp8",
-    "attn_decode_splitkv", "attn_decode_combine", "kvq_auto_num_splits", "kvq_device_cu_count",
+    "attn_decode_splitkv", "attn_decode_combine", "attn_decode", "kvq_auto_num_splits", "kvq_device_cu_count",
     "kvq_fp8p_scratch_floats", "kvq_last_error", "kvq_version", "NVFP4Plane", "FP8Plane", "KvqError",
     "KVQ_F32", "KVQ_BF16", "KVQ_F16", "KVQ_FP8E4M3", "KVQ_NVFP4", "KVQ_LAYOUT_GQA", "KVQ_LAYOUT_MLA",
+    "KVQ_PLANE_ROWS", "KVQ_PLANE_TOKEN4", "make_decode_args",
 ]
 
 _DT = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16, torch.float16: KVQ_F16}
@@ -33,10 +34,13 @@ _DT = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16, torch.float16: KVQ_F16}
 
 @dataclass
 class NVFP4Plane:
-    """An NVFP4-packed tensor: codes [..., D/2], scales [..., D/16], s_t [1]."""
+    """An NVFP4-packed tensor: codes [..., D/2], scales [..., D/16], s_t [1];
+    layout KVQ_PLANE_ROWS or KVQ_PLANE_TOKEN4 (byte order inside groups of 4
+    tokens; the tensor shapes are the same)."""
     codes: torch.Tensor
     scales: torch.Tensor
     tensor_scale: torch.Tensor
+    layout: int = KVQ_PLANE_ROWS
 
     @property
     def d(self):
@@ -45,9 +49,10 @@ class NVFP4Plane:
 
 @dataclass
 class FP8Plane:
-    """A per-tensor FP8 E4M3 tensor: codes [..., D], scale [1]."""
+    """A per-tensor FP8 E4M3 tensor: codes [..., D], scale [1], layout."""
     codes: torch.Tensor
     scale: torch.Tensor
+    layout: int = KVQ_PLANE_ROWS
 
     @property
     def d(self):
@@ -104,36 +109,38 @@ def kvq_amax(x: torch.Tensor, kv_lens: Optional[torch.Tensor] = None, out: Optio
 
 
 def kvq_pack_nvfp4(x: torch.Tensor, amax: torch.Tensor, out: Optional[NVFP4Plane] = None,
-                   dst_pos: Optional[torch.Tensor] = None, stream=None) -> NVFP4Plane:
+                   dst_pos: Optional[torch.Tensor] = None, layout: int = KVQ_PLANE_ROWS,
+                   stream=None) -> NVFP4Plane:
     """Pack rows of x ([..., D], D % 16 == 0) to NVFP4.  With ``out`` given,
-    x's rows go to out's rows (offset by dst_pos[i0] along i2 if given)."""
+    x's rows go to out's rows (offset by dst_pos[i0] along i2 if given) in
+    out's layout."""
     d = x.shape[-1]
     if out is None:
         shp = tuple(x.shape[:-1])
         out = NVFP4Plane(torch.empty(shp + (d // 2,), dtype=torch.uint8, device=x.device),
                          torch.empty(shp + (d // 16,), dtype=torch.uint8, device=x.device),
-                         torch.empty(1, dtype=torch.float32, device=x.device))
+                         torch.empty(1, dtype=torch.float32, device=x.device), layout)
     dst = _rows(out.codes, d // 2)
     sdst = _rows(out.scales, d // 16)
     if (dst.s0, dst.s1, dst.s2) != (sdst.s0, sdst.s1, sdst.s2):
         raise ValueError("code and scale planes must share their row layout")
     xr = _rows(x)
     check(_lib.lib().kvq_pack_nvfp4(_ptr(x), _DT[x.dtype], xr, d, _ptr(amax), _ptr(out.codes), _ptr(out.scales),
-                                    dst, _ptr(dst_pos), _ptr(out.tensor_scale), _stream(stream)))
+                                    dst, out.layout, _ptr(dst_pos), _ptr(out.tensor_scale), _stream(stream)))
     return out
 
 
 def kvq_pack_fp8(x: torch.Tensor, amax: torch.Tensor, out: Optional[FP8Plane] = None,
-                 dst_pos: Optional[torch.Tensor] = None, stream=None) -> FP8Plane:
+                 dst_pos: Optional[torch.Tensor] = None, layout: int = KVQ_PLANE_ROWS, stream=None) -> FP8Plane:
     """Pack rows of x ([..., D]) to per-tensor FP8 E4M3."""
     d = x.shape[-1]
     if out is None:
         out = FP8Plane(torch.empty(tuple(x.shape), dtype=torch.uint8, device=x.device),
-                       torch.empty(1, dtype=torch.float32, device=x.device))
+                       torch.empty(1, dtype=torch.float32, device=x.device), layout)
     dst = _rows(out.codes, d)
     xr = _rows(x)
-    check(_lib.lib().kvq_pack_fp8(_ptr(x), _DT[x.dtype], xr, d, _ptr(amax), _ptr(out.codes), dst, _ptr(dst_pos),
-                                  _ptr(out.scale), _stream(stream)))
+    check(_lib.lib().kvq_pack_fp8(_ptr(x), _DT[x.dtype], xr, d, _ptr(amax), _ptr(out.codes), dst, out.layout,
+                                  _ptr(dst_pos), _ptr(out.scale), _stream(stream)))
     return out
 
 
@@ -141,7 +148,7 @@ def kvq_unpack_nvfp4(p: NVFP4Plane, out: Optional[torch.Tensor] = None, stream=N
     d = p.d
     if out is None:
         out = torch.empty(tuple(p.codes.shape[:-1]) + (d,), dtype=torch.float32, device=p.codes.device)
-    check(_lib.lib().kvq_unpack_nvfp4(_ptr(p.codes), _ptr(p.scales), _rows(p.codes, d // 2), d,
+    check(_lib.lib().kvq_unpack_nvfp4(_ptr(p.codes), _ptr(p.scales), _rows(p.codes, d // 2), p.layout, d,
                                       _ptr(p.tensor_scale), _ptr(out), _rows(out), _stream(stream)))
     return out
 
@@ -150,7 +157,7 @@ def kvq_unpack_fp8(p: FP8Plane, out: Optional[torch.Tensor] = None, stream=None)
     d = p.d
     if out is None:
         out = torch.empty(tuple(p.codes.shape), dtype=torch.float32, device=p.codes.device)
-    check(_lib.lib().kvq_unpack_fp8(_ptr(p.codes), _rows(p.codes, d), d, _ptr(p.scale), _ptr(out), _rows(out),
+    check(_lib.lib().kvq_unpack_fp8(_ptr(p.codes), _rows(p.codes, d), p.layout, d, _ptr(p.scale), _ptr(out), _rows(out),
                                     _stream(stream)))
     return out
 
@@ -203,9 +210,12 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
         kr = _rows(k.codes, row_elems)
         vr = _rows(v.codes, row_elems)
         if (kr.s0, kr.s1, kr.s2) != (vr.s0, vr.s1, vr.s2):
-            raise ValueError("K and V planes must share their row layout")
+            raise ValueError("K and V planes must share their row strides")
+        if k.layout != KVQ_PLANE_ROWS:
+            raise ValueError("K planes are read in the row layout")
         a.kv_sb, a.kv_sh, a.kv_st = kr.s0, kr.s1, kr.s2
         a.Drope = 0
+        a.v_layout = v.layout
     a.max_kv_len = int(max_kv_len)
     a.q, a.q_dtype, a.q_sb, a.q_sh = _ptr(q), _DT[q.dtype], q.stride(0), q.stride(1)
     if fmt == KVQ_NVFP4:
@@ -241,3 +251,14 @@ def attn_decode_combine(part_o, part_lse, B, Hq, Dv, num_splits, out, out_scale=
     check(_lib.lib().attn_decode_combine(_ptr(part_o), _ptr(part_lse), B, Hq, Dv, num_splits, _ptr(out), odt,
                                          _ptr(out_scale), _ptr(lse_out), _stream(stream)))
     return out
+
+
+def attn_decode(args: KvqDecodeArgs, out, out_scale=None, lse_out=None, counters=None, stream=None) -> int:
+    """Split-KV decode and combine in one launch (the last work-group of each
+    (request, kv head) merges the partials).  counters: int32 [B * Hkv],
+    zero before the first call, left zero by every call.  Returns s."""
+    odt = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16, torch.uint8: KVQ_FP8E4M3}[out.dtype]
+    s = ctypes.c_int32(0)
+    check(_lib.lib().attn_decode(ctypes.byref(args), _ptr(out), odt, _ptr(out_scale), _ptr(lse_out), _ptr(counters),
+                                 ctypes.byref(s), _stream(stream)))
+    return s.value

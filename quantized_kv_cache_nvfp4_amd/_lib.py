@@ -14,6 +14,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "kvq.h")
 KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = range(6)
 KVQ_F32, KVQ_BF16, KVQ_F16, KVQ_FP8E4M3, KVQ_NVFP4 = range(5)
 KVQ_LAYOUT_GQA, KVQ_LAYOUT_MLA = 0, 1
+KVQ_PLANE_ROWS, KVQ_PLANE_TOKEN4 = 0, 1
 
 
 class KvqRows(ctypes.Structure):
@@ -32,6 +33,7 @@ class KvqDecodeArgs(ctypes.Structure):
         ("q_rope", ctypes.c_void_p), ("qr_sb", ctypes.c_int64), ("qr_sh", ctypes.c_int64),
         ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
         ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("v_layout", ctypes.c_int32),
         ("k_rope", ctypes.c_void_p),
         ("kv_sb", ctypes.c_int64), ("kv_sh", ctypes.c_int64), ("kv_st", ctypes.c_int64),
         ("kv_lens", ctypes.c_void_p),
@@ -48,13 +50,15 @@ _VP, _I32, _I64, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.
 _PROTOS = {
     "kvq_last_error": (ctypes.c_char_p, []),
     "kvq_version": (_I32, []),
+    "kvq_decode_args_size": (ctypes.c_size_t, []),
     "kvq_amax": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, _I32, _VP]),
-    "kvq_pack_nvfp4": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, _VP, KvqRows, _VP, _VP, _VP]),
-    "kvq_pack_fp8": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, KvqRows, _VP, _VP, _VP]),
-    "kvq_unpack_nvfp4": (ctypes.c_int, [_VP, _VP, KvqRows, _I32, _VP, _VP, KvqRows, _VP]),
-    "kvq_unpack_fp8": (ctypes.c_int, [_VP, KvqRows, _I32, _VP, _VP, KvqRows, _VP]),
+    "kvq_pack_nvfp4": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, _VP, KvqRows, _I32, _VP, _VP, _VP]),
+    "kvq_pack_fp8": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, KvqRows, _I32, _VP, _VP, _VP]),
+    "kvq_unpack_nvfp4": (ctypes.c_int, [_VP, _VP, KvqRows, _I32, _I32, _VP, _VP, KvqRows, _VP]),
+    "kvq_unpack_fp8": (ctypes.c_int, [_VP, KvqRows, _I32, _I32, _VP, _VP, KvqRows, _VP]),
     "attn_decode_splitkv": (ctypes.c_int, [ctypes.POINTER(KvqDecodeArgs), ctypes.POINTER(_I32), _VP]),
     "attn_decode_combine": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _I32, _VP, _VP, _VP]),
+    "attn_decode": (ctypes.c_int, [ctypes.POINTER(KvqDecodeArgs), _VP, _I32, _VP, _VP, _VP, ctypes.POINTER(_I32), _VP]),
     "kvq_auto_num_splits": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_I32)]),
     "kvq_device_cu_count": (ctypes.c_int, [ctypes.POINTER(_I32)]),
     "kvq_fp8p_scratch_floats": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
@@ -84,6 +88,8 @@ def lib():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
+        if L.kvq_decode_args_size() != ctypes.sizeof(KvqDecodeArgs):
+            raise RuntimeError("libkvq.so and this binding disagree on kvq_decode_args; rebuild the library")
         _lib = L
     return _lib
 

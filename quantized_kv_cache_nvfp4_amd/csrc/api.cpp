@@ -59,6 +59,17 @@ int check_float_input(const void* x, int32_t dt, const char* name) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// TOKEN4 planes: groups of four consecutive tokens (s2 == 1, s0, s1 and the
+// plane length along i2 multiples of 4)
+int check_layout(int32_t layout, const kvq_rows& r, const char* name) {
+  if (layout == KVQ_PLANE_ROWS) return KVQ_OK;
+  if (layout != KVQ_PLANE_TOKEN4) return fail(KVQ_ERR_ARG, "%s: unknown plane layout %d", name, layout);
+  if (r.n2 > 1 && r.s2 != 1) return fail(KVQ_ERR_ALIGN, "%s: TOKEN4 layout needs token stride 1", name);
+  if ((r.n0 > 1 && r.s0 % 4 != 0) || (r.n1 > 1 && r.s1 % 4 != 0) || r.n2 % 4 != 0)
+    return fail(KVQ_ERR_ALIGN, "%s: TOKEN4 layout needs s0, s1 and the plane length to be multiples of 4", name);
+  return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -66,6 +77,8 @@ extern "C" {
 const char* kvq_last_error(void) { return g_err.c_str(); }
 
 int32_t kvq_version(void) { return 100; }  // 0.1.0
+
+size_t kvq_decode_args_size(void) { return sizeof(kvq_decode_args); }
 
 int kvq_amax(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const int32_t* kv_lens, float* amax_out,
              int32_t accumulate, void* stream) {
@@ -81,8 +94,8 @@ int kvq_amax(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const i
 }
 
 int kvq_pack_nvfp4(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax, uint8_t* codes,
-                   uint8_t* scales, kvq_rows dst_rows, const int32_t* dst_pos, float* tensor_scale_out,
-                   void* stream) {
+                   uint8_t* scales, kvq_rows dst_rows, int32_t dst_layout, const int32_t* dst_pos,
+                   float* tensor_scale_out, void* stream) {
   int rc;
   if ((rc = check_float_input(x, x_dtype, "x")) != KVQ_OK) return rc;
   if ((rc = check_rows(x_rows, "x_rows")) != KVQ_OK) return rc;
@@ -92,14 +105,16 @@ int kvq_pack_nvfp4(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, c
     return fail(KVQ_ERR_ARG, "amax, codes and scales must be non-null");
   if (!fits_dst(x_rows, dst_rows)) return fail(KVQ_ERR_ARG, "dst_rows must match x_rows in n0, n1 and be at least as long in n2");
   if (!aligned(codes, 8)) return fail(KVQ_ERR_ALIGN, "codes plane must be 8-byte aligned");
+  if ((rc = check_layout(dst_layout, dst_rows, "dst_rows")) != KVQ_OK) return rc;
   if (n_rows(x_rows) == 0) return ok();
   return hip_status(kvq::launch_pack_nvfp4(x, x_dtype, kvq::to_rows(x_rows), d, amax, codes, scales,
-                                           kvq::to_rows(dst_rows), dst_pos, tensor_scale_out, as_stream(stream)),
+                                           kvq::to_rows(dst_rows), dst_layout, dst_pos, tensor_scale_out,
+                                           as_stream(stream)),
                     "kvq_pack_nvfp4 launch");
 }
 
 int kvq_pack_fp8(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax, uint8_t* codes,
-                 kvq_rows dst_rows, const int32_t* dst_pos, float* scale_out, void* stream) {
+                 kvq_rows dst_rows, int32_t dst_layout, const int32_t* dst_pos, float* scale_out, void* stream) {
   int rc;
   if ((rc = check_float_input(x, x_dtype, "x")) != KVQ_OK) return rc;
   if ((rc = check_rows(x_rows, "x_rows")) != KVQ_OK) return rc;
@@ -108,13 +123,15 @@ int kvq_pack_fp8(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, con
   if (amax == nullptr || codes == nullptr) return fail(KVQ_ERR_ARG, "amax and codes must be non-null");
   if (!fits_dst(x_rows, dst_rows)) return fail(KVQ_ERR_ARG, "dst_rows must match x_rows in n0, n1 and be at least as long in n2");
   if (!aligned(codes, 4)) return fail(KVQ_ERR_ALIGN, "codes plane must be 4-byte aligned");
+  if ((rc = check_layout(dst_layout, dst_rows, "dst_rows")) != KVQ_OK) return rc;
+  if (dst_layout == KVQ_PLANE_TOKEN4 && d % 8 != 0) return fail(KVQ_ERR_ARG, "TOKEN4 FP8 planes need d % 8 == 0");
   if (n_rows(x_rows) == 0) return ok();
   return hip_status(kvq::launch_pack_fp8(x, x_dtype, kvq::to_rows(x_rows), d, amax, codes, kvq::to_rows(dst_rows),
-                                         dst_pos, scale_out, as_stream(stream)),
+                                         dst_layout, dst_pos, scale_out, as_stream(stream)),
                     "kvq_pack_fp8 launch");
 }
 
-int kvq_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, kvq_rows src_rows, int32_t d,
+int kvq_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, kvq_rows src_rows, int32_t src_layout, int32_t d,
                      const float* tensor_scale, float* out, kvq_rows out_rows, void* stream) {
   int rc;
   if ((rc = check_rows(src_rows, "src_rows")) != KVQ_OK) return rc;
@@ -124,14 +141,15 @@ int kvq_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, kvq_rows src_r
     return fail(KVQ_ERR_ARG, "codes, scales, tensor_scale and out must be non-null");
   if (!same_extents(src_rows, out_rows)) return fail(KVQ_ERR_ARG, "out_rows extents differ from src_rows extents");
   if (!aligned(codes, 8) || !aligned(out, 4)) return fail(KVQ_ERR_ALIGN, "codes must be 8-byte, out 4-byte aligned");
+  if ((rc = check_layout(src_layout, src_rows, "src_rows")) != KVQ_OK) return rc;
   if (n_rows(src_rows) == 0) return ok();
-  return hip_status(kvq::launch_unpack_nvfp4(codes, scales, kvq::to_rows(src_rows), d, tensor_scale, out,
+  return hip_status(kvq::launch_unpack_nvfp4(codes, scales, kvq::to_rows(src_rows), src_layout, d, tensor_scale, out,
                                              kvq::to_rows(out_rows), as_stream(stream)),
                     "kvq_unpack_nvfp4 launch");
 }
 
-int kvq_unpack_fp8(const uint8_t* codes, kvq_rows src_rows, int32_t d, const float* scale, float* out,
-                   kvq_rows out_rows, void* stream) {
+int kvq_unpack_fp8(const uint8_t* codes, kvq_rows src_rows, int32_t src_layout, int32_t d, const float* scale,
+                   float* out, kvq_rows out_rows, void* stream) {
   int rc;
   if ((rc = check_rows(src_rows, "src_rows")) != KVQ_OK) return rc;
   if ((rc = check_rows(out_rows, "out_rows")) != KVQ_OK) return rc;
@@ -140,8 +158,10 @@ int kvq_unpack_fp8(const uint8_t* codes, kvq_rows src_rows, int32_t d, const flo
     return fail(KVQ_ERR_ARG, "codes, scale and out must be non-null");
   if (!same_extents(src_rows, out_rows)) return fail(KVQ_ERR_ARG, "out_rows extents differ from src_rows extents");
   if (!aligned(out, 4)) return fail(KVQ_ERR_ALIGN, "out must be 4-byte aligned");
+  if ((rc = check_layout(src_layout, src_rows, "src_rows")) != KVQ_OK) return rc;
+  if (src_layout == KVQ_PLANE_TOKEN4 && d % 8 != 0) return fail(KVQ_ERR_ARG, "TOKEN4 FP8 planes need d % 8 == 0");
   if (n_rows(src_rows) == 0) return ok();
-  return hip_status(kvq::launch_unpack_fp8(codes, kvq::to_rows(src_rows), d, scale, out, kvq::to_rows(out_rows),
+  return hip_status(kvq::launch_unpack_fp8(codes, kvq::to_rows(src_rows), src_layout, d, scale, out, kvq::to_rows(out_rows),
                                            as_stream(stream)),
                     "kvq_unpack_fp8 launch");
 }
@@ -187,26 +207,37 @@ size_t kvq_fp8p_scratch_floats(int32_t B, int32_t Hq, int32_t s, int32_t max_kv_
   return static_cast<size_t>(B) * Hq * (static_cast<size_t>(max_kv_len) + 2 * s + 2);
 }
 
-int attn_decode_splitkv(const kvq_decode_args* a, int32_t* splits_used, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates decode arguments and resolves the split count.  need_partials:
+// whether part_o / part_lse are written (false only for the fused path with
+// s == 1).
+int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
   if (a == nullptr) return fail(KVQ_ERR_ARG, "args is null");
   if (a->kv_format != KVQ_NVFP4 && a->kv_format != KVQ_FP8E4M3)
     return fail(KVQ_ERR_UNSUPPORTED, "kv_format %d not supported (NVFP4, FP8E4M3)", a->kv_format);
   if (a->layout != KVQ_LAYOUT_GQA && a->layout != KVQ_LAYOUT_MLA)
     return fail(KVQ_ERR_ARG, "layout %d unknown", a->layout);
   if (a->B <= 0 || a->Hq <= 0 || a->Hkv <= 0) return fail(KVQ_ERR_ARG, "B, Hq and Hkv must be positive");
+  if (a->B > 65535 || a->Hkv > 65535) return fail(KVQ_ERR_ARG, "B and Hkv must be <= 65535");
   if (a->Hq % a->Hkv != 0) return fail(KVQ_ERR_ARG, "Hq (%d) must be a multiple of Hkv (%d)", a->Hq, a->Hkv);
   if (a->max_kv_len < 0) return fail(KVQ_ERR_ARG, "max_kv_len must be >= 0");
-  if (a->q == nullptr || a->k_codes == nullptr || a->k_scale == nullptr || a->kv_lens == nullptr ||
-      a->part_o == nullptr || a->part_lse == nullptr)
-    return fail(KVQ_ERR_ARG, "q, k_codes, k_scale, kv_lens, part_o and part_lse must be non-null");
+  if (a->q == nullptr || a->k_codes == nullptr || a->k_scale == nullptr || a->kv_lens == nullptr)
+    return fail(KVQ_ERR_ARG, "q, k_codes, k_scale and kv_lens must be non-null");
   if (a->kv_format == KVQ_NVFP4 && a->k_scales == nullptr) return fail(KVQ_ERR_ARG, "NVFP4 needs k_scales");
   if (a->q_dtype != KVQ_BF16 && a->q_dtype != KVQ_F32) return fail(KVQ_ERR_UNSUPPORTED, "q_dtype must be BF16 or F32");
-  if (!(a->softmax_scale > 0.0f) || a->softmax_scale != a->softmax_scale)
+  if (!(a->softmax_scale > 0.0f) || a->softmax_scale != a->softmax_scale || a->softmax_scale > 3.0e38f)
     return fail(KVQ_ERR_ARG, "softmax_scale must be a positive finite number");
   if (!aligned(a->k_codes, 16)) return fail(KVQ_ERR_ALIGN, "k_codes must be 16-byte aligned");
   if (a->k_scales != nullptr && !aligned(a->k_scales, 4)) return fail(KVQ_ERR_ALIGN, "k_scales must be 4-byte aligned");
-  if (!aligned(a->part_o, 4) || !aligned(a->part_lse, 4)) return fail(KVQ_ERR_ALIGN, "partials must be 4-byte aligned");
   if (a->q_dtype == KVQ_F32 ? !aligned(a->q, 4) : !aligned(a->q, 2)) return fail(KVQ_ERR_ALIGN, "q misaligned");
+  if (a->kv_st < 0 || a->kv_sb < 0 || a->kv_sh < 0) return fail(KVQ_ERR_ARG, "cache strides must be >= 0");
+  // token offsets inside one (request, kv head) are computed in 32 bits
+  const int64_t row_bytes = a->kv_format == KVQ_NVFP4 ? a->D / 2 : a->D;
+  if (static_cast<int64_t>(a->max_kv_len) * a->kv_st * row_bytes >= (int64_t(1) << 31))
+    return fail(KVQ_ERR_ARG, "max_kv_len * kv_st * row bytes must stay below 2^31");
 
   int32_t s = a->num_splits;
   if (s <= 0) {
@@ -218,28 +249,77 @@ int attn_decode_splitkv(const kvq_decode_args* a, int32_t* splits_used, void* st
     if (rc != KVQ_OK) return rc;
   }
   if (s > 64) return fail(KVQ_ERR_ARG, "num_splits %d exceeds 64", s);
-  if (s > a->part_capacity) return fail(KVQ_ERR_WORKSPACE, "num_splits %d exceeds part_capacity %d", s, a->part_capacity);
+  const bool need_partials = !(fused && s == 1);
+  if (need_partials) {
+    if (a->part_o == nullptr || a->part_lse == nullptr) return fail(KVQ_ERR_ARG, "part_o and part_lse must be non-null");
+    if (!aligned(a->part_o, 4) || !aligned(a->part_lse, 4)) return fail(KVQ_ERR_ALIGN, "partials must be 4-byte aligned");
+    if (s > a->part_capacity)
+      return fail(KVQ_ERR_WORKSPACE, "num_splits %d exceeds part_capacity %d", s, a->part_capacity);
+  }
   if (a->quantize_p) {
     if (a->layout != KVQ_LAYOUT_GQA) return fail(KVQ_ERR_UNSUPPORTED, "quantize_p is implemented for the GQA layout only");
     return fail(KVQ_ERR_UNSUPPORTED, "quantize_p is not implemented yet");
   }
-
-  kvq::DecodePlan plan{s, 0};
   if (a->layout == KVQ_LAYOUT_GQA) {
     if (a->v_codes == nullptr || a->v_scale == nullptr) return fail(KVQ_ERR_ARG, "GQA needs v_codes and v_scale");
     if (a->kv_format == KVQ_NVFP4 && a->v_scales == nullptr) return fail(KVQ_ERR_ARG, "NVFP4 needs v_scales");
     if (!aligned(a->v_codes, 16)) return fail(KVQ_ERR_ALIGN, "v_codes must be 16-byte aligned");
     if (a->v_scales != nullptr && !aligned(a->v_scales, 4)) return fail(KVQ_ERR_ALIGN, "v_scales must be 4-byte aligned");
     if (a->Dv != a->D) return fail(KVQ_ERR_ARG, "GQA layout needs Dv == D");
+    if (a->v_layout != KVQ_PLANE_ROWS && a->v_layout != KVQ_PLANE_TOKEN4)
+      return fail(KVQ_ERR_ARG, "v_layout %d unknown", a->v_layout);
+    if (a->v_layout == KVQ_PLANE_TOKEN4) {
+      if (a->D != 128) return fail(KVQ_ERR_UNSUPPORTED, "TOKEN4 V planes are decoded for D == 128 only");
+      if (a->kv_st != 1 || a->kv_sb % 4 != 0 || a->kv_sh % 4 != 0)
+        return fail(KVQ_ERR_ALIGN, "TOKEN4 V planes need kv_st == 1 and kv_sb, kv_sh multiples of 4");
+    }
     const int G = a->Hq / a->Hkv;
     if (!kvq::gqa_supported(a->kv_format, G, a->D, a->q_dtype))
       return fail(KVQ_ERR_UNSUPPORTED, "GQA decode: G=%d, D=%d not supported (G in 1,2,4,8,16; D in 64,128)", G, a->D);
-    if (splits_used) *splits_used = s;
-    return hip_status(kvq::launch_decode_gqa(*a, plan, as_stream(stream)), "attn_decode_splitkv launch");
+  } else {
+    if (a->kv_format != KVQ_NVFP4) return fail(KVQ_ERR_UNSUPPORTED, "MLA layout supports NVFP4 only");
+    if (a->Hkv != 1) return fail(KVQ_ERR_ARG, "MLA layout needs Hkv == 1");
+    return fail(KVQ_ERR_UNSUPPORTED, "MLA decode is not implemented yet");
   }
-  if (a->kv_format != KVQ_NVFP4) return fail(KVQ_ERR_UNSUPPORTED, "MLA layout supports NVFP4 only");
-  if (a->Hkv != 1) return fail(KVQ_ERR_ARG, "MLA layout needs Hkv == 1");
-  return fail(KVQ_ERR_UNSUPPORTED, "MLA decode is not implemented yet");
+  *s_out = s;
+  return KVQ_OK;
+}
+
+int check_out(void* out, int32_t out_dtype, const float* out_scale) {
+  if (out == nullptr) return fail(KVQ_ERR_ARG, "out must be non-null");
+  if (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16 && out_dtype != KVQ_FP8E4M3)
+    return fail(KVQ_ERR_UNSUPPORTED, "out_dtype %d not supported (F32, BF16, FP8E4M3)", out_dtype);
+  if (out_dtype == KVQ_FP8E4M3 && out_scale == nullptr) return fail(KVQ_ERR_ARG, "FP8 output needs out_scale");
+  if (!aligned(out, out_dtype == KVQ_F32 ? 4 : (out_dtype == KVQ_BF16 ? 2 : 1)))
+    return fail(KVQ_ERR_ALIGN, "out misaligned");
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_splitkv(const kvq_decode_args* a, int32_t* splits_used, void* stream) {
+  int32_t s = 0;
+  int rc = validate_decode(a, &s, false);
+  if (rc != KVQ_OK) return rc;
+  if (splits_used) *splits_used = s;
+  kvq::DecodePlan plan{s, 0};
+  return hip_status(kvq::launch_decode_gqa(*a, plan, as_stream(stream)), "attn_decode_splitkv launch");
+}
+
+int attn_decode(const kvq_decode_args* a, void* out, int32_t out_dtype, const float* out_scale, float* lse_out,
+                int32_t* counters, int32_t* splits_used, void* stream) {
+  int32_t s = 0;
+  int rc = validate_decode(a, &s, true);
+  if (rc != KVQ_OK) return rc;
+  if ((rc = check_out(out, out_dtype, out_scale)) != KVQ_OK) return rc;
+  if (s > 1 && counters == nullptr) return fail(KVQ_ERR_ARG, "counters must be non-null when num_splits > 1");
+  if (splits_used) *splits_used = s;
+  kvq::DecodePlan plan{s, 0};
+  return hip_status(kvq::launch_decode_gqa_fused(*a, plan, out, out_dtype, out_scale, lse_out, counters,
+                                                 as_stream(stream)),
+                    "attn_decode launch");
 }
 
 int attn_decode_combine(const float* part_o, const float* part_lse, int32_t B, int32_t Hq, int32_t Dv,
@@ -249,11 +329,8 @@ int attn_decode_combine(const float* part_o, const float* part_lse, int32_t B, i
     return fail(KVQ_ERR_ARG, "part_o, part_lse and out must be non-null");
   if (B <= 0 || Hq <= 0 || Dv <= 0) return fail(KVQ_ERR_ARG, "B, Hq and Dv must be positive");
   if (num_splits <= 0 || num_splits > 64) return fail(KVQ_ERR_ARG, "num_splits must be in [1, 64] (got %d)", num_splits);
-  if (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16 && out_dtype != KVQ_FP8E4M3)
-    return fail(KVQ_ERR_UNSUPPORTED, "out_dtype %d not supported (F32, BF16, FP8E4M3)", out_dtype);
-  if (out_dtype == KVQ_FP8E4M3 && out_scale == nullptr) return fail(KVQ_ERR_ARG, "FP8 output needs out_scale");
-  if (!aligned(out, out_dtype == KVQ_F32 ? 4 : (out_dtype == KVQ_BF16 ? 2 : 1)))
-    return fail(KVQ_ERR_ALIGN, "out misaligned");
+  int rc = check_out(out, out_dtype, out_scale);
+  if (rc != KVQ_OK) return rc;
   return hip_status(kvq::launch_combine(part_o, part_lse, B, Hq, Dv, num_splits, out, out_dtype, out_scale, lse_out,
                                         as_stream(stream)),
                     "attn_decode_combine launch");

@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "combine_impl.h"
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -136,21 +137,53 @@ __device__ inline void v_pairs(uint32_t vw0, uint32_t vw1, uint32_t vs, f16x2* o
   }
 }
 
+// ------------------------------------------------------------------ tiles
+// Registers holding one tile's packed K (codes + block scales) and V, as
+// loaded from HBM.  K and V are separate so that the next tile's K can be in
+// flight during this tile's Q.K^T and its V during this tile's P.V.
+template <int KVF, int D, int NT>
+struct KTile {
+  using Gm = Geo<KVF, D>;
+  uint32_t k[NT][Gm::kKWords];
+  uint32_t ks[NT];
+};
+template <int KVF, int D, int NT>
+struct VTile {
+  using Gm = Geo<KVF, D>;
+  static constexpr int kVW = (Gm::kVBytes + 3) / 4;  // V code dwords per token
+  uint32_t v[NT][4][kVW];
+  uint32_t vs[NT][4];
+};
+
+// Output of the fused path (split + combine in one launch).
+struct FusedOut {
+  void* out;              // [B][Hq][Dv], out_dtype
+  int out_dtype;
+  const float* out_scale; // FP8 output scale
+  float* lse_out;         // [B][Hq] or null
+  int* counters;          // [B][Hkv], zero on entry, left zero
+};
+
 // ------------------------------------------------------------------ kernel
 // Template: KVF cache format, G query heads per kv head, D head_dim,
-// QF32 fp32 queries (hi/lo split), PSPLIT 2 = P carried as f16 hi + lo.
-template <int KVF, int G, int D, bool QF32, int PSPLIT>
-__global__ void __launch_bounds__(kThreads) k_decode_gqa(kvq_decode_args a, int num_splits) {
+// QF32 fp32 queries (hi/lo split), PSPLIT 2 = P carried as f16 hi + lo,
+// FUSED: the last work-group of each (request, kv head) merges the partials
+// and writes the final output (one launch per decode step).
+template <int KVF, int G, int D, bool QF32, int PSPLIT, bool FUSED, int VL>
+__global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, int num_splits, FusedOut fo) {
   using Gm = Geo<KVF, D>;
   constexpr int NSUB = 16 / G;                  // row groups in the 16 MFMA columns
   constexpr int NT = NSUB < 2 ? 2 : NSUB;       // sub-tiles (16 tokens) per tile
   constexpr int NACC = NT / NSUB;               // score accumulators per tile
   constexpr int TT = 16 * NT;                   // tokens per tile
   constexpr int NQ = QF32 ? 2 : 1;
+  using KT = KTile<KVF, D, NT>;
+  using VT = VTile<KVF, D, NT>;
 
   __shared__ float lds_o[kWaves][16][D];
   __shared__ float lds_m[kWaves][16];
   __shared__ float lds_l[kWaves][16];
+  __shared__ int lds_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -169,49 +202,12 @@ __global__ void __launch_bounds__(kThreads) k_decode_gqa(kvq_decode_args a, int 
   const int ce = (cs + chunk < L) ? cs + chunk : L;
 
   const int hq0 = kvh * G;
-  float* part_o = a.part_o;
-  float* part_lse = a.part_lse;
-
-  if (cs >= ce) {  // empty split
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-      const int h = idx / D, d = idx % D;
-      const int64_t po = (static_cast<int64_t>(b) * a.Hq + hq0 + h) * num_splits + split;
-      part_o[po * D + d] = 0.0f;
-      if (d == 0) part_lse[po] = -INFINITY;
-    }
-    return;
-  }
-
-  // ---- query operand: lane (g, c) holds Q[h = c % G][g*QKE + 8j + e]
   const int my_h = c % G;
   const int my_sub = c / G;
-  f16x8 qop[NQ][Gm::kQkJ];
-  {
-    const int64_t qb = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(hq0 + my_h) * a.q_sh;
-#pragma unroll
-    for (int j = 0; j < Gm::kQkJ; ++j) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = g * Gm::kQkElems + 8 * j + e;
-        float x;
-        if constexpr (QF32) x = static_cast<const float*>(a.q)[qb + d];
-        else x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[qb + d]) << 16);
-        const _Float16 hi = static_cast<_Float16>(x);
-        qop[0][j][e] = hi;
-        if constexpr (QF32) qop[1][j][e] = static_cast<_Float16>(x - static_cast<float>(hi));
-      }
-    }
-  }
 
   const float kscale = *a.k_scale;
   const float vscale = *a.v_scale;
   const float qk_scale = a.softmax_scale * kscale * kLog2e;
-
-  const int64_t head_row = static_cast<int64_t>(b) * a.kv_sb + static_cast<int64_t>(kvh) * a.kv_sh;
-  const uint8_t* kc = a.k_codes;
-  const uint8_t* vc = a.v_codes;
-  const uint8_t* ksc = a.k_scales;
-  const uint8_t* vsc = a.v_scales;
 
   float m_run = -INFINITY;  // running max of row c (log2 domain)
   float l_run = 0.0f;       // this lane's share of row c's denominator
@@ -219,159 +215,368 @@ __global__ void __launch_bounds__(kThreads) k_decode_gqa(kvq_decode_args a, int 
 #pragma unroll
   for (int j = 0; j < Gm::kPvJ; ++j) acc_o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ntiles = (ce - cs + TT - 1) / TT;
-  const f16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int ntiles = cs < ce ? (ce - cs + TT - 1) / TT : 0;
 
-  for (int tile = wave; tile < ntiles; tile += kWaves) {
-    const int tb = cs + tile * TT;
+  if (wave < ntiles) {
+    // ---- query operand: lane (g, c) holds Q[h = c % G][g*QKE + 8j + e]
+    f16x8 qop[NQ][Gm::kQkJ];
+    {
+      const int64_t qb = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(hq0 + my_h) * a.q_sh;
+#pragma unroll
+      for (int j = 0; j < Gm::kQkJ; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = g * Gm::kQkElems + 8 * j + e;
+          float x;
+          if constexpr (QF32) x = static_cast<const float*>(a.q)[qb + d];
+          else x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[qb + d]) << 16);
+          const _Float16 hi = static_cast<_Float16>(x);
+          qop[0][j][e] = hi;
+          if constexpr (QF32) qop[1][j][e] = static_cast<_Float16>(x - static_cast<float>(hi));
+        }
+      }
+    }
 
-    // ---------------- scores: S[token][(sub, h)] via block-diagonal MFMA
-    f32x4 acc_s[NACC];
-#pragma unroll
-    for (int x = 0; x < NACC; ++x) acc_s[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      int t = tb + 16 * u + c;
-      t = t < ce ? t : ce - 1;
-      const int64_t row = head_row + static_cast<int64_t>(t) * a.kv_st;
-      uint32_t kw[Gm::kKWords];
-      const uint8_t* kp = kc + row * Gm::kRowBytes + g * (Gm::kKWords * 4);
+    // per-(request, kv head) plane bases; token offsets below fit in 32 bits
+    const int64_t head_row = static_cast<int64_t>(b) * a.kv_sb + static_cast<int64_t>(kvh) * a.kv_sh;
+    const uint8_t* kc = a.k_codes + head_row * Gm::kRowBytes;
+    const uint8_t* vc = a.v_codes + head_row * Gm::kRowBytes;
+    const uint8_t* ksc = (KVF == KVQ_NVFP4) ? a.k_scales + head_row * Gm::kScaleBytes : nullptr;
+    const uint8_t* vsc = (KVF == KVQ_NVFP4) ? a.v_scales + head_row * Gm::kScaleBytes : nullptr;
+    const int st = static_cast<int>(a.kv_st);
+
+    // Loads of one tile.  A full tile with unit token stride uses one
+    // per-lane base address and immediate offsets (no per-load arithmetic);
+    // the last, partial tile (or a strided cache) clamps every token to the
+    // chunk so that no row past kv_len is touched.
+    const bool unit_stride = (st == 1);
+    // per-lane byte offsets inside a tile (unit token stride)
+    const uint32_t lk = static_cast<uint32_t>(c * Gm::kRowBytes + g * (Gm::kKWords * 4));
+    const uint32_t lks = static_cast<uint32_t>(c * Gm::kScaleBytes + (D == 128 ? 2 * g : g));
+    const uint32_t lv = static_cast<uint32_t>(4 * g * Gm::kRowBytes + c * Gm::kVBytes);
+    const uint32_t lvs = static_cast<uint32_t>(4 * g * Gm::kScaleBytes + (c * Gm::kPvElems) / 16);
+
+    auto load_k = [&](KT& R, int u, const uint8_t* kp, const uint8_t* sp) {
       if constexpr (Gm::kKWords == 8) {
         const uint4 x0 = *reinterpret_cast<const uint4*>(kp);
         const uint4 x1 = *reinterpret_cast<const uint4*>(kp + 16);
-        kw[0] = x0.x; kw[1] = x0.y; kw[2] = x0.z; kw[3] = x0.w;
-        kw[4] = x1.x; kw[5] = x1.y; kw[6] = x1.z; kw[7] = x1.w;
+        R.k[u][0] = x0.x; R.k[u][1] = x0.y; R.k[u][2] = x0.z; R.k[u][3] = x0.w;
+        R.k[u][4] = x1.x; R.k[u][5] = x1.y; R.k[u][6] = x1.z; R.k[u][7] = x1.w;
       } else if constexpr (Gm::kKWords == 4) {
         const uint4 x0 = *reinterpret_cast<const uint4*>(kp);
-        kw[0] = x0.x; kw[1] = x0.y; kw[2] = x0.z; kw[3] = x0.w;
+        R.k[u][0] = x0.x; R.k[u][1] = x0.y; R.k[u][2] = x0.z; R.k[u][3] = x0.w;
       } else {
         const uint2 x0 = *reinterpret_cast<const uint2*>(kp);
-        kw[0] = x0.x; kw[1] = x0.y;
+        R.k[u][0] = x0.x; R.k[u][1] = x0.y;
       }
-      uint32_t ks = 0;
       if constexpr (KVF == KVQ_NVFP4) {
-        const uint8_t* sp = ksc + row * Gm::kScaleBytes;
-        if constexpr (D == 128) ks = *reinterpret_cast<const uint16_t*>(sp + 2 * g);
-        else ks = sp[g];
+        if constexpr (D == 128) R.ks[u] = *reinterpret_cast<const uint16_t*>(sp);
+        else R.ks[u] = *sp;
       }
-      const bool mine = (my_sub == (u % NSUB));
+    };
+    auto load_v = [&](VT& R, int u, int i, const uint8_t* vp, const uint8_t* sp) {
+      if constexpr (Gm::kVBytes == 8) {
+        const uint2 x = *reinterpret_cast<const uint2*>(vp);
+        R.v[u][i][0] = x.x; R.v[u][i][1] = x.y;
+      } else if constexpr (Gm::kVBytes == 4) {
+        R.v[u][i][0] = *reinterpret_cast<const uint32_t*>(vp);
+      } else {
+        R.v[u][i][0] = *reinterpret_cast<const uint16_t*>(vp);
+      }
+      if constexpr (KVF == KVQ_NVFP4) R.vs[u][i] = *sp;
+    };
+    // Loads of one tile.  A full tile with unit token stride uses one
+    // uniform tile base, one per-lane offset and immediate offsets (no
+    // per-load address arithmetic); the last, partial tile (or a strided
+    // cache) clamps every token to the chunk so that no row past kv_len is
+    // read.
+    auto load_ktile = [&](KT& R, int tile) {
+      const int tb = cs + tile * TT;
+      if (unit_stride && tb + TT <= ce) {
+        const uint8_t* kt = kc + static_cast<size_t>(tb) * Gm::kRowBytes + lk;
+        const uint8_t* kst = (KVF == KVQ_NVFP4) ? ksc + static_cast<size_t>(tb) * Gm::kScaleBytes + lks : nullptr;
 #pragma unroll
-      for (int j = 0; j < Gm::kQkJ; ++j) {
-        const f16x8 kop = k_operand<KVF, D>(kw, ks, j);
+        for (int u = 0; u < NT; ++u) load_k(R, u, kt + 16 * u * Gm::kRowBytes, kst + 16 * u * Gm::kScaleBytes);
+      } else {
 #pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) {
-          const f16x8 qm = mine ? qop[qq][j] : zero8;
-          acc_s[u / NSUB] = mfma(kop, qm, acc_s[u / NSUB]);
+        for (int u = 0; u < NT; ++u) {
+          int t = tb + 16 * u + c;
+          t = t < ce ? t : ce - 1;
+          const int r = t * st;
+          load_k(R, u, kc + r * Gm::kRowBytes + g * (Gm::kKWords * 4),
+                 (KVF == KVQ_NVFP4) ? ksc + r * Gm::kScaleBytes + (D == 128 ? 2 * g : g) : nullptr);
         }
       }
-    }
+    };
+    auto load_vtile = [&](VT& R, int tile) {
+      const int tb = cs + tile * TT;
+      if constexpr (VL == KVQ_PLANE_TOKEN4) {
+        // group q = 4 consecutive tokens; this lane's 8-element chunk c of
+        // the 4 tokens is one contiguous run of 4 * kVBytes bytes
+        constexpr int GB = 4 * Gm::kRowBytes;      // bytes per 4-token group (codes)
+        constexpr int GS = 4 * Gm::kScaleBytes;    // bytes per 4-token group (scales)
+        const bool full = tb + TT <= ce;
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          int q = (tb + 16 * u) / 4 + g;
+          int nvalid = 4;
+          if (!full) {
+            nvalid = ce - 4 * q;
+            if (nvalid <= 0) q = (ce - 1) / 4;       // keep the load inside the chunk
+          }
+          const uint8_t* vp = vc + static_cast<size_t>(q) * GB + c * (4 * Gm::kVBytes);
+          if constexpr (Gm::kVBytes == 8) {
+            const uint4 x0 = *reinterpret_cast<const uint4*>(vp);
+            const uint4 x1 = *reinterpret_cast<const uint4*>(vp + 16);
+            R.v[u][0][0] = x0.x; R.v[u][0][1] = x0.y; R.v[u][1][0] = x0.z; R.v[u][1][1] = x0.w;
+            R.v[u][2][0] = x1.x; R.v[u][2][1] = x1.y; R.v[u][3][0] = x1.z; R.v[u][3][1] = x1.w;
+          } else {
+            const uint4 x0 = *reinterpret_cast<const uint4*>(vp);
+            R.v[u][0][0] = x0.x; R.v[u][1][0] = x0.y; R.v[u][2][0] = x0.z; R.v[u][3][0] = x0.w;
+          }
+          if constexpr (KVF == KVQ_NVFP4)
+            R.vs[u][0] = *reinterpret_cast<const uint32_t*>(vsc + static_cast<size_t>(q) * GS + (c * Gm::kPvElems / 16) * 4);
+          if (!full) {
+            // tokens past the chunk end: zero codes and scales (their
+            // probabilities are zero; never multiply 0 by unread bytes)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (i >= nvalid) {
+#pragma unroll
+                for (int w = 0; w < VT::kVW; ++w) R.v[u][i][w] = 0u;
+                if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] &= ~(0xFFu << (8 * i));
+              }
+            }
+          }
+        }
+      } else if (unit_stride && tb + TT <= ce) {
+        const uint8_t* vt_ = vc + static_cast<size_t>(tb) * Gm::kRowBytes + lv;
+        const uint8_t* vst = (KVF == KVQ_NVFP4) ? vsc + static_cast<size_t>(tb) * Gm::kScaleBytes + lvs : nullptr;
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            load_v(R, u, i, vt_ + (16 * u + i) * Gm::kRowBytes, vst + (16 * u + i) * Gm::kScaleBytes);
+      } else {
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            int tv = tb + 16 * u + 4 * g + i;
+            tv = tv < ce ? tv : ce - 1;
+            const int rv = tv * st;
+            load_v(R, u, i, vc + rv * Gm::kRowBytes + c * Gm::kVBytes,
+                   (KVF == KVQ_NVFP4) ? vsc + rv * Gm::kScaleBytes + (c * Gm::kPvElems) / 16 : nullptr);
+          }
+        }
+      }
+    };
 
-    // ---------------- online softmax per row c (this lane: 4*NACC tokens)
-    float sc[NACC][4];
-    float tmax = -INFINITY;
+    auto qk_tile = [&](const KT& R, int tile, f16x2 (&p_hi)[NACC][2], f16x2 (&p_lo)[NACC][2]) {
+      const int tb = cs + tile * TT;
+      // ---------------- scores.  Every sub-tile u is multiplied by the full
+      // (unmasked) query operand into its own accumulator; lane column c
+      // then keeps the sub-tile of its row group (u % NSUB == c / G): the
+      // block-diagonal selection costs one select per score instead of a
+      // masked operand per MFMA.
+      f32x4 acc_u[NT];
 #pragma unroll
-    for (int x = 0; x < NACC; ++x) {
+      for (int u = 0; u < NT; ++u) {
+        acc_u[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = tb + 16 * (x * NSUB + my_sub) + 4 * g + i;
-        const float v = (t < ce) ? acc_s[x][i] * qk_scale : -INFINITY;
-        sc[x][i] = v;
-        tmax = fmaxf(tmax, v);
+        for (int j = 0; j < Gm::kQkJ; ++j) {
+          const f16x8 kop = k_operand<KVF, D>(R.k[u], R.ks[u], j);
+#pragma unroll
+          for (int qq = 0; qq < NQ; ++qq) acc_u[u] = mfma(kop, qop[qq][j], acc_u[u]);
+        }
       }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    if (__any(m_new > m_run)) {
-      const float fac = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
-      l_run *= fac;
-      float fr[4];
+      f32x4 acc_s[NACC];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fr[i] = __shfl(fac, 4 * g + i);
+      for (int x = 0; x < NACC; ++x) {
+        acc_s[x] = acc_u[x * NSUB];
 #pragma unroll
-      for (int j = 0; j < Gm::kPvJ; ++j) {
+        for (int r = 1; r < NSUB; ++r) {
+          const bool pick = (my_sub == r);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc_o[j][i] *= fr[i];
+          for (int i = 0; i < 4; ++i) acc_s[x][i] = pick ? acc_u[x * NSUB + r][i] : acc_s[x][i];
+        }
       }
-      m_run = m_new;
-    }
+      // ---------------- online softmax per row c (this lane: 4*NACC tokens)
+      const bool full_tile = (tb + TT <= ce);
+      float sc[NACC][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int x = 0; x < NACC; ++x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tb + 16 * (x * NSUB + my_sub) + 4 * g + i;
+          const float v = (full_tile || t < ce) ? acc_s[x][i] * qk_scale : -INFINITY;
+          sc[x][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      if (__any(m_new > m_run)) {
+        const float fac = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+        l_run *= fac;
+        float fr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fr[i] = __shfl(fac, 4 * g + i);
+#pragma unroll
+        for (int j = 0; j < Gm::kPvJ; ++j) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc_o[j][i] *= fr[i];
+        }
+        m_run = m_new;
+      }
+#pragma unroll
+      for (int x = 0; x < NACC; ++x) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = (sc[x][i] == -INFINITY) ? 0.0f : exp2f(sc[x][i] - m_run);
+          l_run += p[i];
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const _Float16 h0 = static_cast<_Float16>(p[2 * k]);
+          const _Float16 h1 = static_cast<_Float16>(p[2 * k + 1]);
+          p_hi[x][k] = f16x2{h0, h1};
+          if constexpr (PSPLIT == 2)
+            p_lo[x][k] = f16x2{static_cast<_Float16>(p[2 * k] - static_cast<float>(h0)),
+                               static_cast<_Float16>(p[2 * k + 1] - static_cast<float>(h1))};
+        }
+      }
+    };
+
+    auto pv_tile = [&](const VT& R, const f16x2 (&p_hi)[NACC][2], const f16x2 (&p_lo)[NACC][2]) {
+      // ---------------- P.V over sub-tile pairs (u0, u1) = (2q, 2q+1)
+#pragma unroll
+      for (int q = 0; q < NT / 2; ++q) {
+        const int u0 = 2 * q, u1 = 2 * q + 1;
+        // A operand: k = 8g + e; e < 4 -> sub-tile u0 token 4g+e; e >= 4 -> u1
+        const bool own0 = (my_sub == (u0 % NSUB));
+        const bool own1 = (my_sub == (u1 % NSUB));
+        const f16x2 z2 = {0, 0};
+        f16x8 pa[PSPLIT];
+        {
+          const f16x2 a0 = own0 ? p_hi[u0 / NSUB][0] : z2, a1 = own0 ? p_hi[u0 / NSUB][1] : z2;
+          const f16x2 b0 = own1 ? p_hi[u1 / NSUB][0] : z2, b1 = own1 ? p_hi[u1 / NSUB][1] : z2;
+          pa[0] = cat4(a0, a1, b0, b1);
+          if constexpr (PSPLIT == 2) {
+            const f16x2 c0 = own0 ? p_lo[u0 / NSUB][0] : z2, c1 = own0 ? p_lo[u0 / NSUB][1] : z2;
+            const f16x2 d0 = own1 ? p_lo[u1 / NSUB][0] : z2, d1 = own1 ? p_lo[u1 / NSUB][1] : z2;
+            pa[1] = cat4(c0, c1, d0, d1);
+          }
+        }
+        // V: tokens 4g..4g+3 of u0 and u1, head_dim run [c*PVE, (c+1)*PVE).
+        // For each pair of head_dim elements k: convert the pair of every
+        // token, then transpose 2x2 blocks (tokens x elements) so that each
+        // register holds two tokens of one element, then scale by the two
+        // tokens' block scales.
+        uint32_t w[8];
+        f16x2 s2[4];
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) w[tt] = R.v[tt < 4 ? u0 : u1][tt & 3][0];
+        if constexpr (KVF == KVQ_NVFP4) {
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            const int ua = pr < 2 ? u0 : u1;
+            if constexpr (VL == KVQ_PLANE_TOKEN4) {
+              // the 4 tokens' scale bytes arrive in one dword
+              s2[pr] = (pr & 1) ? fp8x2<true>(R.vs[ua][0]) : fp8x2<false>(R.vs[ua][0]);
+            } else {
+              const uint32_t sb =
+                  __builtin_amdgcn_perm(R.vs[ua][2 * (pr & 1) + 1], R.vs[ua][2 * (pr & 1)], 0x0c0c0400u);
+              s2[pr] = fp8x2<false>(sb);  // (scale of token 2pr, scale of token 2pr+1)
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < Gm::kPvElems / 2; ++k) {
+          f16x2 x[8];
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt) {
+            if constexpr (KVF == KVQ_NVFP4) {
+              switch (k) {
+                case 0: x[tt] = fp4x2<0>(w[tt]); break;
+                case 1: x[tt] = fp4x2<1>(w[tt]); break;
+                case 2: x[tt] = fp4x2<2>(w[tt]); break;
+                default: x[tt] = fp4x2<3>(w[tt]); break;
+              }
+            } else {
+              const uint32_t ww = (k < 2) ? w[tt] : R.v[tt < 4 ? u0 : u1][tt & 3][VT::kVW - 1];
+              x[tt] = (k & 1) ? fp8x2<true>(ww) : fp8x2<false>(ww);
+            }
+          }
+          // output columns j = 2k (low halves) and 2k+1 (high halves)
+          uint32_t lo[4], hi[4];
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            const uint32_t x0 = as_u32(x[2 * pr]), x1 = as_u32(x[2 * pr + 1]);
+            lo[pr] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+            hi[pr] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+          }
+          f16x2 lo2[4], hi2[4];
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            lo2[pr] = as_h2(lo[pr]);
+            hi2[pr] = as_h2(hi[pr]);
+            if constexpr (KVF == KVQ_NVFP4) {
+              lo2[pr] = lo2[pr] * s2[pr];
+              hi2[pr] = hi2[pr] * s2[pr];
+            }
+          }
+          const f16x8 blo = cat4(lo2[0], lo2[1], lo2[2], lo2[3]);
+          const f16x8 bhi = cat4(hi2[0], hi2[1], hi2[2], hi2[3]);
+#pragma unroll
+          for (int ps = 0; ps < PSPLIT; ++ps) {
+            acc_o[2 * k] = mfma(pa[ps], blo, acc_o[2 * k]);
+            acc_o[2 * k + 1] = mfma(pa[ps], bhi, acc_o[2 * k + 1]);
+          }
+        }
+      }
+    };
+
+    // software pipeline: the next tile's K is loaded while this tile's
+    // scores are computed, and its V while this tile's P.V runs, so every
+    // load has a full tile of compute to hide behind.  (Narrow query groups
+    // have 8-16 sub-tiles per tile and use one register set.)
     f16x2 p_hi[NACC][2], p_lo[NACC][2];
-#pragma unroll
-    for (int x = 0; x < NACC; ++x) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = (sc[x][i] == -INFINITY) ? 0.0f : exp2f(sc[x][i] - m_run);
-        l_run += p[i];
+    if constexpr (NT <= 4) {
+      KT KA, KB;
+      VT VA, VB;
+      int tile = wave;
+      load_ktile(KA, tile);
+      load_vtile(VA, tile);
+      while (true) {
+        int nxt = tile + kWaves;
+        const bool more = nxt < ntiles;
+        if (more) load_ktile(KB, nxt);
+        qk_tile(KA, tile, p_hi, p_lo);
+        if (more) load_vtile(VB, nxt);
+        pv_tile(VA, p_hi, p_lo);
+        if (!more) break;
+        tile = nxt;
+        nxt = tile + kWaves;
+        const bool more2 = nxt < ntiles;
+        if (more2) load_ktile(KA, nxt);
+        qk_tile(KB, tile, p_hi, p_lo);
+        if (more2) load_vtile(VA, nxt);
+        pv_tile(VB, p_hi, p_lo);
+        if (!more2) break;
+        tile = nxt;
       }
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const _Float16 h0 = static_cast<_Float16>(p[2 * k]);
-        const _Float16 h1 = static_cast<_Float16>(p[2 * k + 1]);
-        p_hi[x][k] = f16x2{h0, h1};
-        if constexpr (PSPLIT == 2)
-          p_lo[x][k] = f16x2{static_cast<_Float16>(p[2 * k] - static_cast<float>(h0)),
-                             static_cast<_Float16>(p[2 * k + 1] - static_cast<float>(h1))};
-      }
-    }
-
-    // ---------------- P.V over sub-tile pairs (u0, u1) = (2q, 2q+1)
-#pragma unroll
-    for (int q = 0; q < NT / 2; ++q) {
-      const int u0 = 2 * q, u1 = 2 * q + 1;
-      // A operand: k = 8g + e; e < 4 -> sub-tile u0 token 4g+e; e >= 4 -> u1
-      const bool own0 = (my_sub == (u0 % NSUB));
-      const bool own1 = (my_sub == (u1 % NSUB));
-      const f16x2 z2 = {0, 0};
-      f16x8 pa[PSPLIT];
-      {
-        const f16x2 a0 = own0 ? p_hi[u0 / NSUB][0] : z2, a1 = own0 ? p_hi[u0 / NSUB][1] : z2;
-        const f16x2 b0 = own1 ? p_hi[u1 / NSUB][0] : z2, b1 = own1 ? p_hi[u1 / NSUB][1] : z2;
-        pa[0] = cat4(a0, a1, b0, b1);
-        if constexpr (PSPLIT == 2) {
-          const f16x2 c0 = own0 ? p_lo[u0 / NSUB][0] : z2, c1 = own0 ? p_lo[u0 / NSUB][1] : z2;
-          const f16x2 d0 = own1 ? p_lo[u1 / NSUB][0] : z2, d1 = own1 ? p_lo[u1 / NSUB][1] : z2;
-          pa[1] = cat4(c0, c1, d0, d1);
-        }
-      }
-      // V: tokens 4g..4g+3 of u0 and u1, head_dim run [c*PVE, (c+1)*PVE)
-      f16x2 vt[8][Gm::kPvElems / 2];  // [token 0..7][pair]
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int u = tt < 4 ? u0 : u1;
-        int t = tb + 16 * u + 4 * g + (tt & 3);
-        t = t < ce ? t : ce - 1;
-        const int64_t row = head_row + static_cast<int64_t>(t) * a.kv_st;
-        const uint8_t* vp = vc + row * Gm::kRowBytes + c * Gm::kVBytes;
-        uint32_t w0 = 0, w1 = 0, vs = 0;
-        if constexpr (Gm::kVBytes == 8) {
-          const uint2 x = *reinterpret_cast<const uint2*>(vp);
-          w0 = x.x; w1 = x.y;
-        } else if constexpr (Gm::kVBytes == 4) {
-          w0 = *reinterpret_cast<const uint32_t*>(vp);
-        } else {
-          w0 = *reinterpret_cast<const uint16_t*>(vp);
-        }
-        if constexpr (KVF == KVQ_NVFP4) vs = vsc[row * Gm::kScaleBytes + (c * Gm::kPvElems) / 16];
-        v_pairs<KVF, D>(w0, w1, vs, vt[tt]);
-      }
-#pragma unroll
-      for (int k = 0; k < Gm::kPvElems / 2; ++k) {
-        // output columns j = 2k (low halves) and 2k+1 (high halves)
-        uint32_t lo[4], hi[4];
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const uint32_t x0 = as_u32(vt[2 * pr][k]), x1 = as_u32(vt[2 * pr + 1][k]);
-          lo[pr] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-          hi[pr] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-        }
-        const f16x8 blo = cat4(as_h2(lo[0]), as_h2(lo[1]), as_h2(lo[2]), as_h2(lo[3]));
-        const f16x8 bhi = cat4(as_h2(hi[0]), as_h2(hi[1]), as_h2(hi[2]), as_h2(hi[3]));
-#pragma unroll
-        for (int ps = 0; ps < PSPLIT; ++ps) {
-          acc_o[2 * k] = mfma(pa[ps], blo, acc_o[2 * k]);
-          acc_o[2 * k + 1] = mfma(pa[ps], bhi, acc_o[2 * k + 1]);
-        }
+    } else {
+      KT KA;
+      VT VA;
+      for (int tile = wave; tile < ntiles; tile += kWaves) {
+        load_ktile(KA, tile);
+        load_vtile(VA, tile);
+        qk_tile(KA, tile, p_hi, p_lo);
+        pv_tile(VA, p_hi, p_lo);
       }
     }
   }
@@ -390,7 +595,8 @@ __global__ void __launch_bounds__(kThreads) k_decode_gqa(kvq_decode_args a, int 
   }
   __syncthreads();
 
-  // ---------------- merge rows (wave, sub) of each head, write the partial
+  // ---------------- merge rows (wave, sub) of each head
+  const bool direct = FUSED && num_splits == 1;   // no partials needed
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
@@ -405,42 +611,100 @@ __global__ void __launch_bounds__(kThreads) k_decode_gqa(kvq_decode_args a, int 
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
           const float mv = lds_m[w][s * G + h];
-          if (mv == -INFINITY) continue;
-          const float f = exp2f(mv - M);
+          const float f = (mv == -INFINITY) ? 0.0f : exp2f(mv - M);
           num += f * lds_o[w][s * G + h][d];
           den += f * lds_l[w][s * G + h];
         }
     }
-    const int64_t po = (static_cast<int64_t>(b) * a.Hq + hq0 + h) * num_splits + split;
-    part_o[po * D + d] = den > 0.0f ? (num / den) * vscale : 0.0f;
-    if (d == 0) part_lse[po] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    const float o = den > 0.0f ? (num / den) * vscale : 0.0f;
+    const float lse = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + h;
+    if (direct) {
+      store_out(fo.out, fo.out_dtype, bh * D + d, o, fo.out_dtype == KVQ_FP8E4M3 ? *fo.out_scale : 1.0f);
+      if (d == 0 && fo.lse_out != nullptr) fo.lse_out[bh] = lse;
+    } else {
+      const int64_t po = bh * num_splits + split;
+      a.part_o[po * D + d] = o;
+      if (d == 0) a.part_lse[po] = lse;
+    }
+  }
+  if constexpr (!FUSED) return;
+  if (direct) return;
+
+  // ---------------- fused combine: the last work-group of (b, kv head) to
+  // finish merges the num_splits partials of its G heads
+  __threadfence();   // partials visible device-wide before the count
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int* ctr = fo.counters + static_cast<int64_t>(b) * a.Hkv + kvh;
+    const int prev = atomicAdd(ctr, 1);
+    const int last = (prev == num_splits - 1);
+    if (last) *ctr = 0;   // reset for the next call
+    lds_last = last;
+  }
+  __syncthreads();
+  if (!lds_last) return;
+  __threadfence();   // acquire: see every other work-group's partials
+  const float osc = (fo.out_dtype == KVQ_FP8E4M3) ? *fo.out_scale : 1.0f;
+  // lds_o is free now: stage the split weights there
+  float* w_s = &lds_o[0][0][0];            // [G][num_splits] weights
+  float* inv_s = &lds_o[1][0][0];          // [G] 1/sum, [G] merged lse
+  for (int idx = threadIdx.x; idx < G; idx += kThreads) {
+    const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + idx;
+    split_weights(a.part_lse + bh * num_splits, num_splits, w_s + idx * num_splits, inv_s[idx], inv_s[G + idx]);
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int h = idx / D, d = idx % D;
+    const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + h;
+    const float o = combine_column(a.part_o + bh * num_splits * D + d, D, w_s + h * num_splits, num_splits, inv_s[h]);
+    store_out(fo.out, fo.out_dtype, bh * D + d, o, osc);
+    if (d == 0 && fo.lse_out != nullptr) fo.lse_out[bh] = inv_s[G + h];
   }
 }
 
-template <int KVF, int G, int D, bool QF32, int PSPLIT>
-hipError_t launch_t(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
+template <int KVF, int G, int D, bool QF32, int PSPLIT, int VL>
+hipError_t launch_v(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
   dim3 grid(p.s, a.Hkv, a.B);
-  hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT>), grid, dim3(kThreads), 0, st, a, p.s);
+  if (fo != nullptr)
+    hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, true, VL>), grid, dim3(kThreads), 0, st, a, p.s, *fo);
+  else
+    hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, false, VL>), grid, dim3(kThreads), 0, st, a, p.s,
+                       FusedOut{});
   return hipGetLastError();
 }
 
+template <int KVF, int G, int D, bool QF32, int PSPLIT>
+hipError_t launch_t(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
+  if constexpr (D == 128) {
+    if (a.v_layout == KVQ_PLANE_TOKEN4) return launch_v<KVF, G, D, QF32, PSPLIT, KVQ_PLANE_TOKEN4>(a, p, fo, st);
+  }
+  return launch_v<KVF, G, D, QF32, PSPLIT, KVQ_PLANE_ROWS>(a, p, fo, st);
+}
+
 template <int KVF, int G, int D>
-hipError_t launch_q(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
+hipError_t launch_q(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
   // fp32 queries select the fp32-accuracy path (hi/lo split of Q and P)
-  if (a.q_dtype == KVQ_F32) return launch_t<KVF, G, D, true, 2>(a, p, st);
-  return launch_t<KVF, G, D, false, 2>(a, p, st);
+  if (a.q_dtype == KVQ_F32) return launch_t<KVF, G, D, true, 2>(a, p, fo, st);
+  return launch_t<KVF, G, D, false, 1>(a, p, fo, st);
 }
 
 template <int KVF, int D>
-hipError_t launch_g(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
+hipError_t launch_g(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_q<KVF, 1, D>(a, p, st);
-    case 2: return launch_q<KVF, 2, D>(a, p, st);
-    case 4: return launch_q<KVF, 4, D>(a, p, st);
-    case 8: return launch_q<KVF, 8, D>(a, p, st);
-    case 16: return launch_q<KVF, 16, D>(a, p, st);
+    case 1: return launch_q<KVF, 1, D>(a, p, fo, st);
+    case 2: return launch_q<KVF, 2, D>(a, p, fo, st);
+    case 4: return launch_q<KVF, 4, D>(a, p, fo, st);
+    case 8: return launch_q<KVF, 8, D>(a, p, fo, st);
+    case 16: return launch_q<KVF, 16, D>(a, p, fo, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t dispatch(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
+  if (a.kv_format == KVQ_NVFP4)
+    return a.D == 128 ? launch_g<KVQ_NVFP4, 128>(a, p, fo, st) : launch_g<KVQ_NVFP4, 64>(a, p, fo, st);
+  return a.D == 128 ? launch_g<KVQ_FP8E4M3, 128>(a, p, fo, st) : launch_g<KVQ_FP8E4M3, 64>(a, p, fo, st);
 }
 
 }  // namespace
@@ -458,10 +722,13 @@ bool gqa_supported(int kv_format, int G, int D, int q_dtype) {
 }
 
 hipError_t launch_decode_gqa(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
-  if (a.kv_format == KVQ_NVFP4) {
-    return a.D == 128 ? launch_g<KVQ_NVFP4, 128>(a, p, st) : launch_g<KVQ_NVFP4, 64>(a, p, st);
-  }
-  return a.D == 128 ? launch_g<KVQ_FP8E4M3, 128>(a, p, st) : launch_g<KVQ_FP8E4M3, 64>(a, p, st);
+  return dispatch(a, p, nullptr, st);
+}
+
+hipError_t launch_decode_gqa_fused(const kvq_decode_args& a, const DecodePlan& p, void* out, int out_dtype,
+                                   const float* out_scale, float* lse_out, int* counters, hipStream_t st) {
+  FusedOut fo{out, out_dtype, out_scale, lse_out, counters};
+  return dispatch(a, p, &fo, st);
 }
 
 }  // namespace kvq

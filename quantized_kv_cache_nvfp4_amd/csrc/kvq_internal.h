@@ -19,12 +19,13 @@ inline Rows to_rows(const kvq_rows& r) { return Rows{r.n0, r.n1, r.n2, r.s0, r.s
 hipError_t launch_amax(const void* x, int x_dtype, Rows rows, int d, const int32_t* kv_lens, float* amax_out,
                        bool accumulate, hipStream_t st);
 hipError_t launch_pack_nvfp4(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes,
-                             uint8_t* scales, Rows dr, const int32_t* dst_pos, float* ts_out, hipStream_t st);
+                             uint8_t* scales, Rows dr, int layout, const int32_t* dst_pos, float* ts_out,
+                             hipStream_t st);
 hipError_t launch_pack_fp8(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes, Rows dr,
-                           const int32_t* dst_pos, float* scale_out, hipStream_t st);
-hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, Rows sr, int d, const float* ts,
+                           int layout, const int32_t* dst_pos, float* scale_out, hipStream_t st);
+hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, Rows sr, int layout, int d, const float* ts,
                                float* out, Rows orow, hipStream_t st);
-hipError_t launch_unpack_fp8(const uint8_t* codes, Rows sr, int d, const float* scale, float* out, Rows orow,
+hipError_t launch_unpack_fp8(const uint8_t* codes, Rows sr, int layout, int d, const float* scale, float* out, Rows orow,
                              hipStream_t st);
 
 // ---- decode (decode_gqa.hip, decode_mla.hip, combine.hip) ----
@@ -34,6 +35,8 @@ struct DecodePlan {
 };
 
 hipError_t launch_decode_gqa(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st);
+hipError_t launch_decode_gqa_fused(const kvq_decode_args& a, const DecodePlan& p, void* out, int out_dtype,
+                                   const float* out_scale, float* lse_out, int* counters, hipStream_t st);
 hipError_t launch_decode_mla(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st);
 hipError_t launch_decode_fp8p(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st);
 hipError_t launch_combine(const float* part_o, const float* part_lse, int B, int Hq, int Dv, int s, void* out,

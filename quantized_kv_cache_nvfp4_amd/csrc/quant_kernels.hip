@@ -43,6 +43,18 @@ __device__ inline int64_t row_off(const Rows& r, int64_t i0, int64_t i1, int64_t
   return i0 * r.s0 + i1 * r.s1 + i2 * r.s2;
 }
 
+// Byte offset of chunk k (W bytes) of plane row (i0, i1, i2), rows of R
+// bytes, in the ROWS or TOKEN4 layout (TOKEN4: four consecutive tokens
+// share 4R bytes, chunk k of token 4q+j at k*4W + j*W; s2 == 1).
+__device__ inline int64_t plane_off(const Rows& r, int layout, int64_t i0, int64_t i1, int64_t i2, int R, int W,
+                                    int k) {
+  if (layout == KVQ_PLANE_TOKEN4) {
+    const int64_t grp = i0 * r.s0 + i1 * r.s1 + (i2 & ~int64_t(3));
+    return grp * R + static_cast<int64_t>(k) * 4 * W + (i2 & 3) * W;
+  }
+  return row_off(r, i0, i1, i2) * R + static_cast<int64_t>(k) * W;
+}
+
 // ---------------------------------------------------------------- codecs
 // E4M3 (FN) code of the round-to-nearest-even of a non-negative double q,
 // saturating at 448.
@@ -121,7 +133,7 @@ __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, i
 // one thread per 16-element block: 16 exact decisions, 8 code bytes, 1 scale byte
 __global__ void __launch_bounds__(kThreads) k_pack_nvfp4(const void* __restrict__ x, int dt, Rows xr, int d,
                                                          const float* __restrict__ amax, uint8_t* __restrict__ codes,
-                                                         uint8_t* __restrict__ scales, Rows dr,
+                                                         uint8_t* __restrict__ scales, Rows dr, int layout,
                                                          const int32_t* __restrict__ dst_pos, float* ts_out) {
   const float s_t = nvfp4_tensor_scale(*amax);
   const int nb = d / 16;
@@ -143,7 +155,6 @@ __global__ void __launch_bounds__(kThreads) k_pack_nvfp4(const void* __restrict_
     }
     const int64_t di2 = i2 + (dst_pos != nullptr ? dst_pos[i0] : 0);
     if (di2 < 0 || di2 >= dr.n2) continue;  // outside the destination plane
-    const int64_t drow = row_off(dr, i0, i1, di2);
     const uint32_t sc = e4m3_rne_code(static_cast<double>(bamax) / (6.0 * static_cast<double>(s_t)));
     uint32_t lo = 0, hi = 0;
     if (sc != 0) {
@@ -156,9 +167,13 @@ __global__ void __launch_bounds__(kThreads) k_pack_nvfp4(const void* __restrict_
         else hi |= c << (4 * (i - 8));
       }
     }
-    uint2* cp = reinterpret_cast<uint2*>(codes + drow * (d / 2) + blk * 8);
-    *cp = make_uint2(lo, hi);
-    scales[drow * nb + blk] = static_cast<uint8_t>(sc);
+    if (layout == KVQ_PLANE_TOKEN4) {  // two 8-element chunks of 4 bytes
+      *reinterpret_cast<uint32_t*>(codes + plane_off(dr, layout, i0, i1, di2, d / 2, 4, 2 * blk)) = lo;
+      *reinterpret_cast<uint32_t*>(codes + plane_off(dr, layout, i0, i1, di2, d / 2, 4, 2 * blk + 1)) = hi;
+    } else {
+      *reinterpret_cast<uint2*>(codes + plane_off(dr, layout, i0, i1, di2, d / 2, 8, blk)) = make_uint2(lo, hi);
+    }
+    scales[plane_off(dr, layout, i0, i1, di2, nb, 1, blk)] = static_cast<uint8_t>(sc);
   }
 }
 
@@ -166,7 +181,8 @@ __global__ void __launch_bounds__(kThreads) k_pack_nvfp4(const void* __restrict_
 // one thread per 4 elements (one 32-bit code word)
 __global__ void __launch_bounds__(kThreads) k_pack_fp8(const void* __restrict__ x, int dt, Rows xr, int d,
                                                        const float* __restrict__ amax, uint8_t* __restrict__ codes,
-                                                       Rows dr, const int32_t* __restrict__ dst_pos, float* sc_out) {
+                                                       Rows dr, int layout, const int32_t* __restrict__ dst_pos,
+                                                       float* sc_out) {
   const float scale = fp8_tensor_scale(*amax);
   const double dscale = static_cast<double>(scale);
   const int nw = d / 4;
@@ -189,13 +205,14 @@ __global__ void __launch_bounds__(kThreads) k_pack_fp8(const void* __restrict__ 
     }
     const int64_t di2 = i2 + (dst_pos != nullptr ? dst_pos[i0] : 0);
     if (di2 < 0 || di2 >= dr.n2) continue;  // outside the destination plane
-    *reinterpret_cast<uint32_t*>(codes + row_off(dr, i0, i1, di2) * d + w * 4) = word;
+    // a 4-byte word is half of an 8-element chunk (W = 8)
+    *reinterpret_cast<uint32_t*>(codes + plane_off(dr, layout, i0, i1, di2, d, 8, w >> 1) + (w & 1) * 4) = word;
   }
 }
 
 // ---------------------------------------------------------------- unpack
 __global__ void __launch_bounds__(kThreads) k_unpack_nvfp4(const uint8_t* __restrict__ codes,
-                                                           const uint8_t* __restrict__ scales, Rows sr, int d,
+                                                           const uint8_t* __restrict__ scales, Rows sr, int layout, int d,
                                                            const float* __restrict__ ts, float* __restrict__ out,
                                                            Rows orow) {
   const float s_t = *ts;
@@ -207,9 +224,14 @@ __global__ void __launch_bounds__(kThreads) k_unpack_nvfp4(const uint8_t* __rest
     int blk = static_cast<int>(gid - row * nb);
     int64_t i0, i1, i2;
     unravel(row, sr, i0, i1, i2);
-    const int64_t srow = row_off(sr, i0, i1, i2);
-    const uint2 cw = *reinterpret_cast<const uint2*>(codes + srow * (d / 2) + blk * 8);
-    const float s_hat = static_cast<float>(e4m3_value(scales[srow * nb + blk]));
+    uint2 cw;
+    if (layout == KVQ_PLANE_TOKEN4) {
+      cw.x = *reinterpret_cast<const uint32_t*>(codes + plane_off(sr, layout, i0, i1, i2, d / 2, 4, 2 * blk));
+      cw.y = *reinterpret_cast<const uint32_t*>(codes + plane_off(sr, layout, i0, i1, i2, d / 2, 4, 2 * blk + 1));
+    } else {
+      cw = *reinterpret_cast<const uint2*>(codes + plane_off(sr, layout, i0, i1, i2, d / 2, 8, blk));
+    }
+    const float s_hat = static_cast<float>(e4m3_value(scales[plane_off(sr, layout, i0, i1, i2, nb, 1, blk)]));
     float* o = out + row_off(orow, i0, i1, i2) + blk * 16;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -219,7 +241,7 @@ __global__ void __launch_bounds__(kThreads) k_unpack_nvfp4(const uint8_t* __rest
   }
 }
 
-__global__ void __launch_bounds__(kThreads) k_unpack_fp8(const uint8_t* __restrict__ codes, Rows sr, int d,
+__global__ void __launch_bounds__(kThreads) k_unpack_fp8(const uint8_t* __restrict__ codes, Rows sr, int layout, int d,
                                                          const float* __restrict__ scale, float* __restrict__ out,
                                                          Rows orow) {
   const float sc = *scale;
@@ -230,7 +252,7 @@ __global__ void __launch_bounds__(kThreads) k_unpack_fp8(const uint8_t* __restri
     int col = static_cast<int>(gid - row * d);
     int64_t i0, i1, i2;
     unravel(row, sr, i0, i1, i2);
-    uint32_t c = codes[row_off(sr, i0, i1, i2) * d + col];
+    uint32_t c = codes[plane_off(sr, layout, i0, i1, i2, d, 8, col >> 3) + (col & 7)];
     out[row_off(orow, i0, i1, i2) + col] = static_cast<float>(e4m3_value(c)) * sc;
   }
 }
@@ -253,32 +275,34 @@ hipError_t launch_amax(const void* x, int x_dtype, Rows rows, int d, const int32
 }
 
 hipError_t launch_pack_nvfp4(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes,
-                             uint8_t* scales, Rows dr, const int32_t* dst_pos, float* ts_out, hipStream_t st) {
+                             uint8_t* scales, Rows dr, int layout, const int32_t* dst_pos, float* ts_out,
+                             hipStream_t st) {
   const int64_t items = xr.n0 * xr.n1 * xr.n2 * (d / 16);
   hipLaunchKernelGGL(k_pack_nvfp4, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes, scales,
-                     dr, dst_pos, ts_out);
+                     dr, layout, dst_pos, ts_out);
   return hipGetLastError();
 }
 
 hipError_t launch_pack_fp8(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes, Rows dr,
-                           const int32_t* dst_pos, float* scale_out, hipStream_t st) {
+                           int layout, const int32_t* dst_pos, float* scale_out, hipStream_t st) {
   const int64_t items = xr.n0 * xr.n1 * xr.n2 * (d / 4);
   hipLaunchKernelGGL(k_pack_fp8, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes, dr,
-                     dst_pos, scale_out);
+                     layout, dst_pos, scale_out);
   return hipGetLastError();
 }
 
-hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, Rows sr, int d, const float* ts,
+hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, Rows sr, int layout, int d, const float* ts,
                                float* out, Rows orow, hipStream_t st) {
   const int64_t items = sr.n0 * sr.n1 * sr.n2 * (d / 16);
-  hipLaunchKernelGGL(k_unpack_nvfp4, dim3(grid_for(items)), dim3(kThreads), 0, st, codes, scales, sr, d, ts, out, orow);
+  hipLaunchKernelGGL(k_unpack_nvfp4, dim3(grid_for(items)), dim3(kThreads), 0, st, codes, scales, sr, layout, d, ts, out,
+                     orow);
   return hipGetLastError();
 }
 
-hipError_t launch_unpack_fp8(const uint8_t* codes, Rows sr, int d, const float* scale, float* out, Rows orow,
+hipError_t launch_unpack_fp8(const uint8_t* codes, Rows sr, int layout, int d, const float* scale, float* out, Rows orow,
                              hipStream_t st) {
   const int64_t items = sr.n0 * sr.n1 * sr.n2 * d;
-  hipLaunchKernelGGL(k_unpack_fp8, dim3(grid_for(items)), dim3(kThreads), 0, st, codes, sr, d, scale, out, orow);
+  hipLaunchKernelGGL(k_unpack_fp8, dim3(grid_for(items)), dim3(kThreads), 0, st, codes, sr, layout, d, scale, out, orow);
   return hipGetLastError();
 }
 

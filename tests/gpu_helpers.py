@@ -49,6 +49,29 @@ def oracle_gqa(cfg_key):
     return packed, o, lse, khat, vhat
 
 
+@functools.lru_cache(maxsize=8)
+def oracle_pv_abs(cfg_key):
+    """sum_t P_t |V_t| per output element (the oracle's attention with |V|):
+    the scale of the error that rounding P to f16 can cause."""
+    inp = make_inputs(cfg_key)
+    _, _, _, khat, vhat = oracle_gqa(cfg_key)
+    o, _ = OA.decode_gqa(kvq_synth.f64(inp.q), khat, np.abs(vhat), inp.kv_lens, inp.softmax_scale)
+    return o
+
+
+def fp32_bound(cfg_key, ref):
+    """Per-element bound on |o_gpu - o_ref| for fp32 output.  Scores are
+    exact f16 products summed in fp32; P goes to the P.V MFMA as f16 (one
+    rounding, <= 2^-11 relative) on the bf16-query path, or as f16 hi + lo
+    (<= 2^-22) on the fp32-query path; the rest is fp32 rounding, covered by
+    1e-5 (1 + |o|)."""
+    inp = make_inputs(cfg_key)
+    base = 1e-5 * (1.0 + np.abs(ref))
+    if inp.q.dtype == torch.float32:
+        return base
+    return base + 2.0 ** -11 * oracle_pv_abs(cfg_key)
+
+
 _INPUT_CACHE = {}
 
 
@@ -76,17 +99,52 @@ def make_inputs(cfg_key):
 
 
 # ---------------------------------------------------------------- GPU side
-def gpu_pack(inp, fmt):
+def to_token4(rows, W):
+    """Byte order of the TOKEN4 plane layout, built from row-major bytes
+    [..., L, R] (L % 4 == 0): inside each group of 4 tokens, chunk k (W
+    bytes) of token j goes to byte k*4W + j*W.  Pure index permutation."""
+    a = np.asarray(rows)
+    L, R = a.shape[-2], a.shape[-1]
+    g = a.reshape(a.shape[:-2] + (L // 4, 4, R // W, W))
+    g = np.swapaxes(g, -3, -2)                       # [.., q, k, j, W]
+    return g.reshape(a.shape)
+
+
+def empty_plane(fmt, shape_lead, D, layout, fill=0xFF):
+    """A V plane of shape [..., L, .] pre-filled with `fill` bytes (0xFF:
+    NaN E4M3 scales) so that reading padding rows would be caught."""
+    k_ = K()
+    if fmt == "nvfp4":
+        return k_.NVFP4Plane(torch.full(shape_lead + (D // 2,), fill, dtype=torch.uint8, device=DEV),
+                             torch.full(shape_lead + (D // 16,), fill, dtype=torch.uint8, device=DEV),
+                             torch.empty(1, dtype=torch.float32, device=DEV), layout)
+    return k_.FP8Plane(torch.full(shape_lead + (D,), fill, dtype=torch.uint8, device=DEV),
+                       torch.empty(1, dtype=torch.float32, device=DEV), layout)
+
+
+def gpu_pack(inp, fmt, v_layout=0):
+    """K in the row layout; V in v_layout (TOKEN4 planes are padded to a
+    multiple of 4 tokens and the padding holds 0xFF bytes)."""
     k_ = K()
     k, v = inp.k.to(DEV), inp.v.to(DEV)
     lens = torch.from_numpy(inp.kv_lens).to(DEV)
     ka, va = k_.kvq_amax(k, lens), k_.kvq_amax(v, lens)
-    if fmt == "nvfp4":
-        return k_.kvq_pack_nvfp4(k, ka), k_.kvq_pack_nvfp4(v, va), ka, va, lens
-    return k_.kvq_pack_fp8(k, ka), k_.kvq_pack_fp8(v, va), ka, va, lens
+    pack = k_.kvq_pack_nvfp4 if fmt == "nvfp4" else k_.kvq_pack_fp8
+    if v_layout == k_.KVQ_PLANE_ROWS:
+        kp = pack(k, ka)
+        vp = pack(v, va)
+    else:
+        # both planes padded to a multiple of 4 tokens (shared strides)
+        B, H, L, D = v.shape
+        Lp = (L + 3) // 4 * 4
+        kp = empty_plane(fmt, (B, H, Lp), D, k_.KVQ_PLANE_ROWS)
+        pack(k, ka, out=kp)
+        vp = empty_plane(fmt, (B, H, Lp), D, v_layout)
+        pack(v, va, out=vp)
+    return kp, vp, ka, va, lens
 
 
-def gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.bfloat16, out_scale=None, with_lse=False):
+def gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.bfloat16, out_scale=None, with_lse=False, fused=False):
     k_ = K()
     B, Hq, D = inp.B, inp.Hq, inp.D
     cap = 64
@@ -95,10 +153,16 @@ def gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.bfloat16, out_scale=None, w
     q = inp.q.to(DEV)
     args = k_.make_decode_args(q, kp, vp, lens, max_kv_len=inp.Lmax, softmax_scale=inp.softmax_scale,
                                num_splits=s, part_o=part_o, part_lse=part_lse)
-    used = k_.attn_decode_splitkv(args)
     out = torch.empty(B, Hq, D, dtype=out_dtype, device=DEV)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV) if with_lse else None
-    k_.attn_decode_combine(part_o, part_lse, B, Hq, D, used, out, out_scale=out_scale, lse_out=lse)
+    if fused:
+        counters = torch.zeros(B * inp.Hkv, dtype=torch.int32, device=DEV)
+        used = k_.attn_decode(args, out, out_scale=out_scale, lse_out=lse, counters=counters)
+        torch.cuda.synchronize()
+        assert int(counters.abs().sum().item()) == 0, "fused decode must leave its counters at zero"
+    else:
+        used = k_.attn_decode_splitkv(args)
+        k_.attn_decode_combine(part_o, part_lse, B, Hq, D, used, out, out_scale=out_scale, lse_out=lse)
     torch.cuda.synchronize()
     return out, used, lse
 

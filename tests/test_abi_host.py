@@ -26,6 +26,11 @@ def K():
     return K
 
 
+def test_struct_size_matches_binding(L):
+    from quantized_kv_cache_nvfp4_amd import _lib
+    assert L.kvq_decode_args_size() == ctypes.sizeof(_lib.KvqDecodeArgs)
+
+
 def test_exports_every_declared_symbol(L):
     from quantized_kv_cache_nvfp4_amd import _lib
     names = _lib.header_functions()
@@ -83,20 +88,28 @@ FAKE_ODD = ctypes.c_void_p(0x10001)
 
 def test_pack_validation(L, K):
     r = _rows(1, 1, 4, 0, 0, 24)
-    rc = L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r, 24, FAKE, FAKE, FAKE, r, None, None, None)
+    R, T4 = K.KVQ_PLANE_ROWS, K.KVQ_PLANE_TOKEN4
+    rc = L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r, 24, FAKE, FAKE, FAKE, r, R, None, None, None)
     assert rc == 1 and "multiple of 16" in K.kvq_last_error()
     r16 = _rows(1, 1, 4, 0, 0, 16)
-    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r16, 16, None, FAKE, FAKE, r16, None, None, None) == 1
-    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_F16, r16, 16, FAKE, FAKE, FAKE, r16, None, None, None) == 2
-    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE_ODD, FAKE, r16, None, None, None) == 3
+    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r16, 16, None, FAKE, FAKE, r16, R, None, None, None) == 1
+    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_F16, r16, 16, FAKE, FAKE, FAKE, r16, R, None, None, None) == 2
+    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE_ODD, FAKE, r16, R, None, None, None) == 3
     rdiff = _rows(1, 2, 5, 0, 0, 1)
-    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE, FAKE, rdiff, None, None, None) == 1
-    assert L.kvq_pack_fp8(FAKE, K.KVQ_BF16, r16, 6, FAKE, FAKE, r16, None, None, None) == 1
-    assert L.kvq_pack_fp8(FAKE, K.KVQ_F32, _rows(-1, 1, 1, 0, 0, 0), 16, FAKE, FAKE, r16, None, None, None) == 1
+    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE, FAKE, rdiff, R, None, None, None) == 1
+    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE, FAKE, r16, 9, None, None, None) == 1
+    # TOKEN4: token stride must be 1 and lengths / strides multiples of 4
+    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE, FAKE, r16, T4, None, None, None) == 3
+    r_t4 = _rows(2, 3, 8, 24, 8, 1)
+    r_t4_bad = _rows(2, 3, 6, 18, 6, 1)
+    assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r_t4_bad, 16, FAKE, FAKE, FAKE, r_t4_bad, T4, None, None, None) == 3
+    assert L.kvq_pack_fp8(FAKE, K.KVQ_BF16, r_t4, 12, FAKE, FAKE, r_t4, T4, None, None, None) == 1
+    assert L.kvq_pack_fp8(FAKE, K.KVQ_BF16, r16, 6, FAKE, FAKE, r16, R, None, None, None) == 1
+    assert L.kvq_pack_fp8(FAKE, K.KVQ_F32, _rows(-1, 1, 1, 0, 0, 0), 16, FAKE, FAKE, r16, R, None, None, None) == 1
     assert L.kvq_amax(None, K.KVQ_F32, r16, 16, None, FAKE, 0, None) == 1
     assert L.kvq_amax(FAKE, K.KVQ_F32, r16, 0, None, FAKE, 0, None) == 1
-    assert L.kvq_unpack_nvfp4(FAKE, FAKE, r16, 20, FAKE, FAKE, r16, None) == 1
-    assert L.kvq_unpack_fp8(FAKE, r16, 16, None, FAKE, r16, None) == 1
+    assert L.kvq_unpack_nvfp4(FAKE, FAKE, r16, R, 20, FAKE, FAKE, r16, None) == 1
+    assert L.kvq_unpack_fp8(FAKE, r16, R, 16, None, FAKE, r16, None) == 1
 
 
 def _good_args(K):
@@ -108,6 +121,7 @@ def _good_args(K):
     a.k_codes = a.k_scales = a.k_scale = FAKE
     a.v_codes = a.v_scales = a.v_scale = FAKE
     a.kv_lens = FAKE
+    a.kv_sb, a.kv_sh, a.kv_st = 8 * 1024, 1024, 1
     a.softmax_scale = 0.088
     a.num_splits = 4
     a.part_o = a.part_lse = FAKE
@@ -142,6 +156,12 @@ def test_decode_validation(L, K):
     a = _good_args(K); a.layout = K.KVQ_LAYOUT_MLA; a.Hkv = 2; a.Hq = 16
     assert _decode_rc(L, a) == 1                     # MLA needs Hkv == 1
     a = _good_args(K); a.k_scales = None
+    assert _decode_rc(L, a) == 1
+    a = _good_args(K); a.v_layout = K.KVQ_PLANE_TOKEN4; a.D = a.Dv = 64
+    assert _decode_rc(L, a) == 2                     # TOKEN4 V needs D = 128
+    a = _good_args(K); a.v_layout = K.KVQ_PLANE_TOKEN4; a.kv_st = 2
+    assert _decode_rc(L, a) == 3
+    a = _good_args(K); a.v_layout = 5
     assert _decode_rc(L, a) == 1
     assert L.attn_decode_splitkv(None, None, None) == 1
 

@@ -9,7 +9,7 @@ import kvq_synth
 from oracle import formats as OF
 from oracle import quant as OQ
 
-from gpu_helpers import DEV, K, announce
+from gpu_helpers import DEV, K, announce, empty_plane, to_token4
 
 pytestmark = pytest.mark.gpu
 
@@ -182,3 +182,40 @@ def test_full_size_gqa32k_sampled_rows():
         gs = _np(p.scales.reshape(-1, 8))[rows]
         assert np.array_equal(gs, s)
         assert np.array_equal(gc, c)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_token4_layout_pack_unpack(fmt):
+    """TOKEN4 planes hold exactly the oracle's bytes in the interleaved order;
+    padding rows are left untouched; unpack reads the layout back."""
+    announce(f"pack {fmt} token4")
+    inp = kvq_synth.gqa_inputs(2, 8, 2, 128, None, kv_lens=[37, 61], config="gqa", salt=11, outliers=True)
+    x = inp.v
+    B, H, L, D = x.shape
+    Lp = (L + 3) // 4 * 4
+    xd = x.to(DEV)
+    amax = K().kvq_amax(xd)
+    plane = empty_plane(fmt, (B, H, Lp), D, K().KVQ_PLANE_TOKEN4, fill=0xAB)
+    xf = kvq_synth.f64(x)
+    if fmt == "nvfp4":
+        K().kvq_pack_nvfp4(xd, amax, out=plane)
+        c, sc, st = OQ.nvfp4_pack(xf, float(amax.item()))
+        pad = np.full((B, H, Lp - L), 0xAB, np.uint8)
+        c_full = np.concatenate([c, np.broadcast_to(pad[..., None], (B, H, Lp - L, D // 2))], axis=2)
+        s_full = np.concatenate([sc, np.broadcast_to(pad[..., None], (B, H, Lp - L, D // 16))], axis=2)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(plane.codes), to_token4(c_full, 4))
+        assert np.array_equal(_np(plane.scales), to_token4(s_full, 1))
+        u = K().kvq_unpack_nvfp4(plane)
+        ref = OF.fp32_round(OQ.nvfp4_unpack(c, sc, st))
+    else:
+        K().kvq_pack_fp8(xd, amax, out=plane)
+        c, sc = OQ.fp8_pack(xf, float(amax.item()))
+        pad = np.full((B, H, Lp - L, D), 0xAB, np.uint8)
+        c_full = np.concatenate([c, pad], axis=2)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(plane.codes), to_token4(c_full, 8))
+        u = K().kvq_unpack_fp8(plane)
+        ref = OF.fp32_round(OQ.fp8_unpack(c, sc))
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(u)[:, :, :L].astype(np.float64), ref)
