@@ -111,8 +111,8 @@ def main():
     v = inp.v.to(dev)
     # calibration + bulk pack (untimed)
     k_amax, v_amax = K.kvq_amax(k, kv_lens), K.kvq_amax(v, kv_lens)
-    # K planes row-major; V planes in the TOKEN4 layout (four consecutive
-    # tokens interleaved per 8-element chunk: one 16-byte load per lane)
+    # K planes row-major; V planes in the TOKEN4 layout (per group of four
+    # tokens, element-major with the four tokens' codes side by side)
     kp0 = K.kvq_pack_nvfp4(k, k_amax)
     vp0 = K.kvq_pack_nvfp4(v, v_amax, layout=K.KVQ_PLANE_TOKEN4)
     new_k = k[:, :, L - 1:L, :].contiguous()

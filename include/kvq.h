@@ -76,16 +76,17 @@ extern "C" {
  * KVQ_PLANE_ROWS: row r of a plane occupies bytes [r*R, (r+1)*R), R = the
  *   plane's row bytes.
  * KVQ_PLANE_TOKEN4: rows are taken in groups of four consecutive tokens
- *   (i2 = 4q .. 4q+3), which share 4*R bytes starting at the address the
- *   group's first row has in KVQ_PLANE_ROWS.  Inside a group each row is cut
- *   into chunks of W bytes -- the codes of 8 elements (W = 4 for NVFP4 codes,
- *   8 for FP8 codes) or one 16-element block's scale (W = 1 for NVFP4
- *   scales) -- and chunk k of token 4q+j is stored at byte k*4*W + j*W of the
- *   group.  One 16-byte load then yields 8 elements of 4 consecutive tokens,
- *   which is the operand a wave64 lane feeds to the P.V matrix multiply; the
- *   decode kernel reads V planes in this layout with a quarter of the load
- *   instructions of the row layout.  Requires the token stride s2 == 1 and
- *   s0, s1 and the plane length along i2 to be multiples of 4.
+ *   (i2 = 4q .. 4q+3), which share the 4*R bytes starting at the address
+ *   the group's first row has in KVQ_PLANE_ROWS.  Inside a group the
+ *   elements are stored in order and, for each element, the codes of the
+ *   four tokens in token order: NVFP4 element x of token 4q+j is nibble
+ *   (j & 1) (low nibble first) of byte 2x + (j >> 1); FP8 element x of token
+ *   4q+j is byte 4x + j; the NVFP4 scale of block b of token 4q+j is byte
+ *   4b + j.  One byte then holds one element of two consecutive tokens, so
+ *   the hardware FP4 -> f16 convert yields the token-contiguous pair a
+ *   wave64 lane feeds to the P.V matrix multiply, and one 16-byte load gives
+ *   a lane 8 elements of 4 tokens.  Requires the token stride s2 == 1 and s0,
+ *   s1 and the plane length along i2 to be multiples of 4.
  */
 #define KVQ_PLANE_ROWS 0
 #define KVQ_PLANE_TOKEN4 1
@@ -157,9 +158,8 @@ int kvq_pack_nvfp4(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, c
 /*
  * kvq_pack_fp8 - quantize rows to per-tensor FP8 E4M3 (compressed-tensors
  * PR #436 kv_cache_scheme).  Arguments as kvq_pack_nvfp4; codes rows are d
- * bytes (d > 0, d % 4 == 0, <= 4096; d % 8 == 0 for KVQ_PLANE_TOKEN4);
- * scale_out (device float[1] or NULL) receives the scale amax/448 (1 if
- * amax == 0).
+ * bytes (d > 0, d % 4 == 0, <= 4096); scale_out (device float[1] or NULL)
+ * receives the scale amax/448 (1 if amax == 0).
  */
 int kvq_pack_fp8(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax,
                  uint8_t* codes, kvq_rows dst_rows, int32_t dst_layout, const int32_t* dst_pos,

@@ -124,7 +124,6 @@ int kvq_pack_fp8(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, con
   if (!fits_dst(x_rows, dst_rows)) return fail(KVQ_ERR_ARG, "dst_rows must match x_rows in n0, n1 and be at least as long in n2");
   if (!aligned(codes, 4)) return fail(KVQ_ERR_ALIGN, "codes plane must be 4-byte aligned");
   if ((rc = check_layout(dst_layout, dst_rows, "dst_rows")) != KVQ_OK) return rc;
-  if (dst_layout == KVQ_PLANE_TOKEN4 && d % 8 != 0) return fail(KVQ_ERR_ARG, "TOKEN4 FP8 planes need d % 8 == 0");
   if (n_rows(x_rows) == 0) return ok();
   return hip_status(kvq::launch_pack_fp8(x, x_dtype, kvq::to_rows(x_rows), d, amax, codes, kvq::to_rows(dst_rows),
                                          dst_layout, dst_pos, scale_out, as_stream(stream)),
@@ -159,7 +158,7 @@ int kvq_unpack_fp8(const uint8_t* codes, kvq_rows src_rows, int32_t src_layout, 
   if (!same_extents(src_rows, out_rows)) return fail(KVQ_ERR_ARG, "out_rows extents differ from src_rows extents");
   if (!aligned(out, 4)) return fail(KVQ_ERR_ALIGN, "out must be 4-byte aligned");
   if ((rc = check_layout(src_layout, src_rows, "src_rows")) != KVQ_OK) return rc;
-  if (src_layout == KVQ_PLANE_TOKEN4 && d % 8 != 0) return fail(KVQ_ERR_ARG, "TOKEN4 FP8 planes need d % 8 == 0");
+  if (src_layout == KVQ_PLANE_TOKEN4 && d % 4 != 0) return fail(KVQ_ERR_ARG, "TOKEN4 FP8 planes need d % 4 == 0");
   if (n_rows(src_rows) == 0) return ok();
   return hip_status(kvq::launch_unpack_fp8(codes, kvq::to_rows(src_rows), src_layout, d, scale, out, kvq::to_rows(out_rows),
                                            as_stream(stream)),

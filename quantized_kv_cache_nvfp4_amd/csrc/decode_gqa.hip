@@ -65,6 +65,16 @@ __device__ inline f16x2 fp8x2(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
 }
 
+// fp4x2 with a byte select that is a constant after unrolling
+__device__ inline f16x2 fp4x2_sel(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return fp4x2<0>(w);
+    case 1: return fp4x2<1>(w);
+    case 2: return fp4x2<2>(w);
+    default: return fp4x2<3>(w);
+  }
+}
+
 __device__ inline f16x8 cat4(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
   f16x8 r;
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
@@ -151,8 +161,9 @@ template <int KVF, int D, int NT>
 struct VTile {
   using Gm = Geo<KVF, D>;
   static constexpr int kVW = (Gm::kVBytes + 3) / 4;  // V code dwords per token
-  uint32_t v[NT][4][kVW];
+  uint32_t v[NT][4][kVW];   // row layout: [sub-tile][token][dword]
   uint32_t vs[NT][4];
+  uint32_t t4[NT][8];       // TOKEN4 layout: [sub-tile][dword of the lane's 16 / 32 bytes]
 };
 
 // Output of the fused path (split + combine in one launch).
@@ -311,42 +322,54 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
     auto load_vtile = [&](VT& R, int tile) {
       const int tb = cs + tile * TT;
       if constexpr (VL == KVQ_PLANE_TOKEN4) {
-        // group q = 4 consecutive tokens; this lane's 8-element chunk c of
-        // the 4 tokens is one contiguous run of 4 * kVBytes bytes
+        // Group q = 4 consecutive tokens, stored element-major: for this
+        // lane's elements [8c, 8c+8) the 4 tokens' codes are one contiguous
+        // run (16 bytes NVFP4, 32 bytes FP8), and block c/2's 4 scale bytes
+        // one dword.  Lane group g takes group 4u+g of sub-tile u.
         constexpr int GB = 4 * Gm::kRowBytes;      // bytes per 4-token group (codes)
         constexpr int GS = 4 * Gm::kScaleBytes;    // bytes per 4-token group (scales)
-        const bool full = tb + TT <= ce;
+        constexpr int CB = 4 * Gm::kVBytes;        // bytes of one lane's chunk in a group
+        if (tb + TT <= ce) {
+          const uint8_t* vp = vc + static_cast<size_t>(tb / 4 + g) * GB + c * CB;
+          const uint8_t* sp = (KVF == KVQ_NVFP4) ? vsc + static_cast<size_t>(tb / 4 + g) * GS + (c / 2) * 4 : nullptr;
 #pragma unroll
-        for (int u = 0; u < NT; ++u) {
-          int q = (tb + 16 * u) / 4 + g;
-          int nvalid = 4;
-          if (!full) {
-            nvalid = ce - 4 * q;
+          for (int u = 0; u < NT; ++u) {
+            const uint4 x0 = *reinterpret_cast<const uint4*>(vp + u * 4 * GB);
+            R.t4[u][0] = x0.x; R.t4[u][1] = x0.y; R.t4[u][2] = x0.z; R.t4[u][3] = x0.w;
+            if constexpr (CB == 32) {
+              const uint4 x1 = *reinterpret_cast<const uint4*>(vp + u * 4 * GB + 16);
+              R.t4[u][4] = x1.x; R.t4[u][5] = x1.y; R.t4[u][6] = x1.z; R.t4[u][7] = x1.w;
+            }
+            if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] = *reinterpret_cast<const uint32_t*>(sp + u * 4 * GS);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < NT; ++u) {
+            int q = (tb + 16 * u) / 4 + g;
+            const int nvalid = ce - 4 * q;
             if (nvalid <= 0) q = (ce - 1) / 4;       // keep the load inside the chunk
-          }
-          const uint8_t* vp = vc + static_cast<size_t>(q) * GB + c * (4 * Gm::kVBytes);
-          if constexpr (Gm::kVBytes == 8) {
+            const uint8_t* vp = vc + static_cast<size_t>(q) * GB + c * CB;
             const uint4 x0 = *reinterpret_cast<const uint4*>(vp);
-            const uint4 x1 = *reinterpret_cast<const uint4*>(vp + 16);
-            R.v[u][0][0] = x0.x; R.v[u][0][1] = x0.y; R.v[u][1][0] = x0.z; R.v[u][1][1] = x0.w;
-            R.v[u][2][0] = x1.x; R.v[u][2][1] = x1.y; R.v[u][3][0] = x1.z; R.v[u][3][1] = x1.w;
-          } else {
-            const uint4 x0 = *reinterpret_cast<const uint4*>(vp);
-            R.v[u][0][0] = x0.x; R.v[u][1][0] = x0.y; R.v[u][2][0] = x0.z; R.v[u][3][0] = x0.w;
-          }
-          if constexpr (KVF == KVQ_NVFP4)
-            R.vs[u][0] = *reinterpret_cast<const uint32_t*>(vsc + static_cast<size_t>(q) * GS + (c * Gm::kPvElems / 16) * 4);
-          if (!full) {
-            // tokens past the chunk end: zero codes and scales (their
-            // probabilities are zero; never multiply 0 by unread bytes)
+            R.t4[u][0] = x0.x; R.t4[u][1] = x0.y; R.t4[u][2] = x0.z; R.t4[u][3] = x0.w;
+            if constexpr (CB == 32) {
+              const uint4 x1 = *reinterpret_cast<const uint4*>(vp + 16);
+              R.t4[u][4] = x1.x; R.t4[u][5] = x1.y; R.t4[u][6] = x1.z; R.t4[u][7] = x1.w;
+            }
+            if constexpr (KVF == KVQ_NVFP4)
+              R.vs[u][0] = *reinterpret_cast<const uint32_t*>(vsc + static_cast<size_t>(q) * GS + (c / 2) * 4);
+            // tokens past the chunk end: zero their codes and scales (their
+            // probabilities are zero; 0 must never meet unread bytes)
+            uint32_t keep = 0xFFFFFFFFu, keep_s = 0xFFFFFFFFu;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (i >= nvalid) {
-#pragma unroll
-                for (int w = 0; w < VT::kVW; ++w) R.v[u][i][w] = 0u;
-                if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] &= ~(0xFFu << (8 * i));
+            for (int j = 0; j < 4; ++j) {
+              if (j >= nvalid) {
+                keep_s &= ~(0xFFu << (8 * j));
+                keep &= (KVF == KVQ_NVFP4) ? ~(0x000F000Fu << (4 * j)) : ~(0xFFu << (8 * j));
               }
             }
+#pragma unroll
+            for (int w = 0; w < CB / 4; ++w) R.t4[u][w] &= keep;
+            if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] &= keep_s;
           }
         }
       } else if (unit_stride && tb + TT <= ce) {
@@ -471,70 +494,102 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
             pa[1] = cat4(c0, c1, d0, d1);
           }
         }
-        // V: tokens 4g..4g+3 of u0 and u1, head_dim run [c*PVE, (c+1)*PVE).
-        // For each pair of head_dim elements k: convert the pair of every
-        // token, then transpose 2x2 blocks (tokens x elements) so that each
-        // register holds two tokens of one element, then scale by the two
-        // tokens' block scales.
-        uint32_t w[8];
-        f16x2 s2[4];
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) w[tt] = R.v[tt < 4 ? u0 : u1][tt & 3][0];
-        if constexpr (KVF == KVQ_NVFP4) {
-#pragma unroll
-          for (int pr = 0; pr < 4; ++pr) {
-            const int ua = pr < 2 ? u0 : u1;
-            if constexpr (VL == KVQ_PLANE_TOKEN4) {
-              // the 4 tokens' scale bytes arrive in one dword
-              s2[pr] = (pr & 1) ? fp8x2<true>(R.vs[ua][0]) : fp8x2<false>(R.vs[ua][0]);
-            } else {
-              const uint32_t sb =
-                  __builtin_amdgcn_perm(R.vs[ua][2 * (pr & 1) + 1], R.vs[ua][2 * (pr & 1)], 0x0c0c0400u);
-              s2[pr] = fp8x2<false>(sb);  // (scale of token 2pr, scale of token 2pr+1)
-            }
+        if constexpr (VL == KVQ_PLANE_TOKEN4) {
+          // element-major groups: one convert yields element j of two tokens
+          // (already the token-contiguous operand); block scales per token pair
+          f16x2 s2[4];
+          if constexpr (KVF == KVQ_NVFP4) {
+            s2[0] = fp8x2<false>(R.vs[u0][0]);  // (token 0, token 1) of u0
+            s2[1] = fp8x2<true>(R.vs[u0][0]);   // (token 2, token 3)
+            s2[2] = fp8x2<false>(R.vs[u1][0]);
+            s2[3] = fp8x2<true>(R.vs[u1][0]);
           }
-        }
 #pragma unroll
-        for (int k = 0; k < Gm::kPvElems / 2; ++k) {
-          f16x2 x[8];
-#pragma unroll
-          for (int tt = 0; tt < 8; ++tt) {
+          for (int j = 0; j < Gm::kPvElems; ++j) {
+            f16x2 x0, x1, x2, x3;
             if constexpr (KVF == KVQ_NVFP4) {
-              switch (k) {
-                case 0: x[tt] = fp4x2<0>(w[tt]); break;
-                case 1: x[tt] = fp4x2<1>(w[tt]); break;
-                case 2: x[tt] = fp4x2<2>(w[tt]); break;
-                default: x[tt] = fp4x2<3>(w[tt]); break;
+              const uint32_t w0 = R.t4[u0][j >> 1], w1 = R.t4[u1][j >> 1];
+              const int sel = 2 * (j & 1);
+              x0 = fp4x2_sel(w0, sel) * s2[0];
+              x1 = fp4x2_sel(w0, sel + 1) * s2[1];
+              x2 = fp4x2_sel(w1, sel) * s2[2];
+              x3 = fp4x2_sel(w1, sel + 1) * s2[3];
+            } else {
+              x0 = fp8x2<false>(R.t4[u0][j]);
+              x1 = fp8x2<true>(R.t4[u0][j]);
+              x2 = fp8x2<false>(R.t4[u1][j]);
+              x3 = fp8x2<true>(R.t4[u1][j]);
+            }
+            const f16x8 bv = cat4(x0, x1, x2, x3);
+#pragma unroll
+            for (int ps = 0; ps < PSPLIT; ++ps) acc_o[j] = mfma(pa[ps], bv, acc_o[j]);
+          }
+        } else {
+          // V: tokens 4g..4g+3 of u0 and u1, head_dim run [c*PVE, (c+1)*PVE).
+          // For each pair of head_dim elements k: convert the pair of every
+          // token, then transpose 2x2 blocks (tokens x elements) so that each
+          // register holds two tokens of one element, then scale by the two
+          // tokens' block scales.
+          uint32_t w[8];
+          f16x2 s2[4];
+  #pragma unroll
+          for (int tt = 0; tt < 8; ++tt) w[tt] = R.v[tt < 4 ? u0 : u1][tt & 3][0];
+          if constexpr (KVF == KVQ_NVFP4) {
+  #pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+              const int ua = pr < 2 ? u0 : u1;
+              if constexpr (VL == KVQ_PLANE_TOKEN4) {
+                // the 4 tokens' scale bytes arrive in one dword
+                s2[pr] = (pr & 1) ? fp8x2<true>(R.vs[ua][0]) : fp8x2<false>(R.vs[ua][0]);
+              } else {
+                const uint32_t sb =
+                    __builtin_amdgcn_perm(R.vs[ua][2 * (pr & 1) + 1], R.vs[ua][2 * (pr & 1)], 0x0c0c0400u);
+                s2[pr] = fp8x2<false>(sb);  // (scale of token 2pr, scale of token 2pr+1)
               }
-            } else {
-              const uint32_t ww = (k < 2) ? w[tt] : R.v[tt < 4 ? u0 : u1][tt & 3][VT::kVW - 1];
-              x[tt] = (k & 1) ? fp8x2<true>(ww) : fp8x2<false>(ww);
             }
           }
-          // output columns j = 2k (low halves) and 2k+1 (high halves)
-          uint32_t lo[4], hi[4];
-#pragma unroll
-          for (int pr = 0; pr < 4; ++pr) {
-            const uint32_t x0 = as_u32(x[2 * pr]), x1 = as_u32(x[2 * pr + 1]);
-            lo[pr] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-            hi[pr] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-          }
-          f16x2 lo2[4], hi2[4];
-#pragma unroll
-          for (int pr = 0; pr < 4; ++pr) {
-            lo2[pr] = as_h2(lo[pr]);
-            hi2[pr] = as_h2(hi[pr]);
-            if constexpr (KVF == KVQ_NVFP4) {
-              lo2[pr] = lo2[pr] * s2[pr];
-              hi2[pr] = hi2[pr] * s2[pr];
+  #pragma unroll
+          for (int k = 0; k < Gm::kPvElems / 2; ++k) {
+            f16x2 x[8];
+  #pragma unroll
+            for (int tt = 0; tt < 8; ++tt) {
+              if constexpr (KVF == KVQ_NVFP4) {
+                switch (k) {
+                  case 0: x[tt] = fp4x2<0>(w[tt]); break;
+                  case 1: x[tt] = fp4x2<1>(w[tt]); break;
+                  case 2: x[tt] = fp4x2<2>(w[tt]); break;
+                  default: x[tt] = fp4x2<3>(w[tt]); break;
+                }
+              } else {
+                const uint32_t ww = (k < 2) ? w[tt] : R.v[tt < 4 ? u0 : u1][tt & 3][VT::kVW - 1];
+                x[tt] = (k & 1) ? fp8x2<true>(ww) : fp8x2<false>(ww);
+              }
             }
-          }
-          const f16x8 blo = cat4(lo2[0], lo2[1], lo2[2], lo2[3]);
-          const f16x8 bhi = cat4(hi2[0], hi2[1], hi2[2], hi2[3]);
-#pragma unroll
-          for (int ps = 0; ps < PSPLIT; ++ps) {
-            acc_o[2 * k] = mfma(pa[ps], blo, acc_o[2 * k]);
-            acc_o[2 * k + 1] = mfma(pa[ps], bhi, acc_o[2 * k + 1]);
+            // output columns j = 2k (low halves) and 2k+1 (high halves)
+            uint32_t lo[4], hi[4];
+  #pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+              const uint32_t x0 = as_u32(x[2 * pr]), x1 = as_u32(x[2 * pr + 1]);
+              lo[pr] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+              hi[pr] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+            }
+            f16x2 lo2[4], hi2[4];
+  #pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+              lo2[pr] = as_h2(lo[pr]);
+              hi2[pr] = as_h2(hi[pr]);
+              if constexpr (KVF == KVQ_NVFP4) {
+                lo2[pr] = lo2[pr] * s2[pr];
+                hi2[pr] = hi2[pr] * s2[pr];
+              }
+            }
+            const f16x8 blo = cat4(lo2[0], lo2[1], lo2[2], lo2[3]);
+            const f16x8 bhi = cat4(hi2[0], hi2[1], hi2[2], hi2[3]);
+  #pragma unroll
+            for (int ps = 0; ps < PSPLIT; ++ps) {
+              acc_o[2 * k] = mfma(pa[ps], blo, acc_o[2 * k]);
+              acc_o[2 * k + 1] = mfma(pa[ps], bhi, acc_o[2 * k + 1]);
+            }
           }
         }
       }

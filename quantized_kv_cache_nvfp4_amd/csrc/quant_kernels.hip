@@ -43,16 +43,14 @@ __device__ inline int64_t row_off(const Rows& r, int64_t i0, int64_t i1, int64_t
   return i0 * r.s0 + i1 * r.s1 + i2 * r.s2;
 }
 
-// Byte offset of chunk k (W bytes) of plane row (i0, i1, i2), rows of R
-// bytes, in the ROWS or TOKEN4 layout (TOKEN4: four consecutive tokens
-// share 4R bytes, chunk k of token 4q+j at k*4W + j*W; s2 == 1).
-__device__ inline int64_t plane_off(const Rows& r, int layout, int64_t i0, int64_t i1, int64_t i2, int R, int W,
-                                    int k) {
-  if (layout == KVQ_PLANE_TOKEN4) {
-    const int64_t grp = i0 * r.s0 + i1 * r.s1 + (i2 & ~int64_t(3));
-    return grp * R + static_cast<int64_t>(k) * 4 * W + (i2 & 3) * W;
-  }
-  return row_off(r, i0, i1, i2) * R + static_cast<int64_t>(k) * W;
+// TOKEN4 plane layout: four consecutive tokens (4q .. 4q+3) share the 4R
+// bytes that start at the group's first row; inside, elements are stored in
+// order and, for each element, the codes of the four tokens in token order:
+// NVFP4 element x of token j is nibble (j & 1) of byte 2x + (j >> 1), FP8
+// element x of token j is byte 4x + j, NVFP4 block b's scale of token j is
+// byte 4b + j.  (Requires token stride 1 and 4-aligned groups.)
+__device__ inline int64_t group_row(const Rows& r, int64_t i0, int64_t i1, int64_t t0) {
+  return i0 * r.s0 + i1 * r.s1 + t0;  // row index of the group's first token
 }
 
 // ---------------------------------------------------------------- codecs
@@ -106,6 +104,30 @@ __device__ inline float fp8_tensor_scale(float amax) {
   return amax > 0.0f ? static_cast<float>(static_cast<double>(amax) / 448.0) : 1.0f;
 }
 
+// NVFP4 encoding of one 16-element block with tensor scale s_t: returns the
+// E4M3 scale code and writes the 16 E2M1 codes (sign in bit 3); a block whose
+// scale rounds to 0 gets all-zero codes.
+__device__ inline uint32_t encode_nvfp4_block(const float* v, float s_t, uint32_t* c) {
+  float bamax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bamax = fmaxf(bamax, fabsf(v[i]));
+  const uint32_t sc = e4m3_rne_code(static_cast<double>(bamax) / (6.0 * static_cast<double>(s_t)));
+  if (sc == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = 0;
+    return 0;
+  }
+  const double denom = e4m3_value(sc) * static_cast<double>(s_t);  // exact
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    c[i] = e2m1_rne_code(fabs(static_cast<double>(v[i])) / denom) | ((__float_as_uint(v[i]) >> 28) & 8u);
+  return sc;
+}
+
+__device__ inline uint32_t encode_fp8(float v, double dscale) {
+  return e4m3_rne_code(fabs(static_cast<double>(v)) / dscale) | ((__float_as_uint(v) >> 24) & 0x80u);
+}
+
 // ---------------------------------------------------------------- amax
 __global__ void k_zero_scalar(float* p) { *p = 0.0f; }
 
@@ -130,10 +152,10 @@ __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, i
 }
 
 // ---------------------------------------------------------------- NVFP4 pack
-// one thread per 16-element block: 16 exact decisions, 8 code bytes, 1 scale byte
+// ROWS layout: one thread per 16-element block -> 8 code bytes, 1 scale byte
 __global__ void __launch_bounds__(kThreads) k_pack_nvfp4(const void* __restrict__ x, int dt, Rows xr, int d,
                                                          const float* __restrict__ amax, uint8_t* __restrict__ codes,
-                                                         uint8_t* __restrict__ scales, Rows dr, int layout,
+                                                         uint8_t* __restrict__ scales, Rows dr,
                                                          const int32_t* __restrict__ dst_pos, float* ts_out) {
   const float s_t = nvfp4_tensor_scale(*amax);
   const int nb = d / 16;
@@ -145,44 +167,107 @@ __global__ void __launch_bounds__(kThreads) k_pack_nvfp4(const void* __restrict_
     int blk = static_cast<int>(gid - row * nb);
     int64_t i0, i1, i2;
     unravel(row, xr, i0, i1, i2);
-    const int64_t xo = row_off(xr, i0, i1, i2) + blk * 16;
-    float v[16];
-    float bamax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      v[i] = load_elem(x, dt, xo + i);
-      bamax = fmaxf(bamax, fabsf(v[i]));
-    }
     const int64_t di2 = i2 + (dst_pos != nullptr ? dst_pos[i0] : 0);
     if (di2 < 0 || di2 >= dr.n2) continue;  // outside the destination plane
-    const uint32_t sc = e4m3_rne_code(static_cast<double>(bamax) / (6.0 * static_cast<double>(s_t)));
+    const int64_t xo = row_off(xr, i0, i1, i2) + blk * 16;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = load_elem(x, dt, xo + i);
+    uint32_t c[16];
+    const uint32_t sc = encode_nvfp4_block(v, s_t, c);
     uint32_t lo = 0, hi = 0;
-    if (sc != 0) {
-      const double denom = e4m3_value(sc) * static_cast<double>(s_t);  // exact
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo |= c[i] << (4 * i);
+      hi |= c[8 + i] << (4 * i);
+    }
+    const int64_t drow = row_off(dr, i0, i1, di2);
+    *reinterpret_cast<uint2*>(codes + drow * (d / 2) + blk * 8) = make_uint2(lo, hi);
+    scales[drow * nb + blk] = static_cast<uint8_t>(sc);
+  }
+}
+
+// Group slots per (i0, i1) that a pack into a TOKEN4 plane visits: rows
+// [pos, pos + n2) touch at most n2/4 + 2 groups.
+__device__ inline int64_t t4_slots(int64_t n2) { return n2 / 4 + 2; }
+
+// For group slot gl of (i0, i1): first destination token t0 and, per token
+// j, the source row (or -1).  Returns false if the slot has no source row.
+__device__ inline bool t4_group(const Rows& xr, const Rows& dr, const int32_t* dst_pos, int64_t i0, int64_t gl,
+                                int64_t& t0, int64_t (&src)[4]) {
+  const int64_t pos = dst_pos != nullptr ? dst_pos[i0] : 0;
+  const int64_t q = (pos >= 0 ? pos / 4 : -((-pos + 3) / 4)) + gl;  // floor(pos / 4) + gl
+  t0 = 4 * q;
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t = t0 + j;
+    const int64_t r = t - pos;
+    const bool ok = t >= 0 && t < dr.n2 && r >= 0 && r < xr.n2;
+    src[j] = ok ? r : -1;
+    any |= ok;
+  }
+  return any;
+}
+
+// TOKEN4 layout: one thread per (4-token group, 16-element block): 32 code
+// bytes (two 16-byte stores) and one 4-byte scale word; tokens of the group
+// that this call does not write keep their bytes.
+__global__ void __launch_bounds__(kThreads) k_pack_nvfp4_t4(const void* __restrict__ x, int dt, Rows xr, int d,
+                                                            const float* __restrict__ amax,
+                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                            Rows dr, const int32_t* __restrict__ dst_pos,
+                                                            float* ts_out) {
+  const float s_t = nvfp4_tensor_scale(*amax);
+  const int nb = d / 16;
+  const int64_t slots = t4_slots(xr.n2);
+  const int64_t total = xr.n0 * xr.n1 * slots * nb;
+  int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
+  if (gid == 0 && ts_out != nullptr) *ts_out = s_t;
+  for (; gid < total; gid += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int blk = static_cast<int>(gid % nb);
+    int64_t rest = gid / nb;
+    const int64_t gl = rest % slots;
+    rest /= slots;
+    const int64_t i1 = rest % xr.n1, i0 = rest / xr.n1;
+    int64_t t0, src[4];
+    if (!t4_group(xr, dr, dst_pos, i0, gl, t0, src)) continue;
+    const int64_t grow = group_row(dr, i0, i1, t0);
+    uint4* cp = reinterpret_cast<uint4*>(codes + grow * (d / 2) + blk * 32);
+    uint32_t* sp = reinterpret_cast<uint32_t*>(scales + grow * nb + blk * 4);
+    const bool partial = src[0] < 0 || src[1] < 0 || src[2] < 0 || src[3] < 0;
+    uint4 w0 = partial ? cp[0] : make_uint4(0, 0, 0, 0);
+    uint4 w1 = partial ? cp[1] : make_uint4(0, 0, 0, 0);
+    uint32_t sw = partial ? *sp : 0u;
+    uint32_t* wd[8] = {&w0.x, &w0.y, &w0.z, &w0.w, &w1.x, &w1.y, &w1.z, &w1.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (src[j] < 0) continue;
+      const int64_t xo = row_off(xr, i0, i1, src[j]) + blk * 16;
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = load_elem(x, dt, xo + i);
+      uint32_t c[16];
+      const uint32_t sc = encode_nvfp4_block(v, s_t, c);
+      sw = (sw & ~(0xFFu << (8 * j))) | (sc << (8 * j));
+      // element i: byte 2i + (j >> 1), nibble j & 1 -> dword i / 2, bit 16 (i & 1) + 8 (j >> 1) + 4 (j & 1)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        uint32_t c = e2m1_rne_code(fabs(static_cast<double>(v[i])) / denom);
-        c |= (__float_as_uint(v[i]) >> 28) & 8u;  // sign of x, zero included
-        if (i < 8) lo |= c << (4 * i);
-        else hi |= c << (4 * (i - 8));
+        const int sh = 16 * (i & 1) + 8 * (j >> 1) + 4 * (j & 1);
+        *wd[i >> 1] = (*wd[i >> 1] & ~(0xFu << sh)) | (c[i] << sh);
       }
     }
-    if (layout == KVQ_PLANE_TOKEN4) {  // two 8-element chunks of 4 bytes
-      *reinterpret_cast<uint32_t*>(codes + plane_off(dr, layout, i0, i1, di2, d / 2, 4, 2 * blk)) = lo;
-      *reinterpret_cast<uint32_t*>(codes + plane_off(dr, layout, i0, i1, di2, d / 2, 4, 2 * blk + 1)) = hi;
-    } else {
-      *reinterpret_cast<uint2*>(codes + plane_off(dr, layout, i0, i1, di2, d / 2, 8, blk)) = make_uint2(lo, hi);
-    }
-    scales[plane_off(dr, layout, i0, i1, di2, nb, 1, blk)] = static_cast<uint8_t>(sc);
+    cp[0] = w0;
+    cp[1] = w1;
+    *sp = sw;
   }
 }
 
 // ---------------------------------------------------------------- FP8 pack
-// one thread per 4 elements (one 32-bit code word)
+// ROWS layout: one thread per 4 elements (one 32-bit code word)
 __global__ void __launch_bounds__(kThreads) k_pack_fp8(const void* __restrict__ x, int dt, Rows xr, int d,
                                                        const float* __restrict__ amax, uint8_t* __restrict__ codes,
-                                                       Rows dr, int layout, const int32_t* __restrict__ dst_pos,
-                                                       float* sc_out) {
+                                                       Rows dr, const int32_t* __restrict__ dst_pos, float* sc_out) {
   const float scale = fp8_tensor_scale(*amax);
   const double dscale = static_cast<double>(scale);
   const int nw = d / 4;
@@ -194,19 +279,49 @@ __global__ void __launch_bounds__(kThreads) k_pack_fp8(const void* __restrict__ 
     int w = static_cast<int>(gid - row * nw);
     int64_t i0, i1, i2;
     unravel(row, xr, i0, i1, i2);
+    const int64_t di2 = i2 + (dst_pos != nullptr ? dst_pos[i0] : 0);
+    if (di2 < 0 || di2 >= dr.n2) continue;  // outside the destination plane
     const int64_t xo = row_off(xr, i0, i1, i2) + w * 4;
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = load_elem(x, dt, xo + i);
-      uint32_t c = e4m3_rne_code(fabs(static_cast<double>(v)) / dscale);
-      c |= (__float_as_uint(v) >> 24) & 0x80u;
-      word |= c << (8 * i);
+    for (int i = 0; i < 4; ++i) word |= encode_fp8(load_elem(x, dt, xo + i), dscale) << (8 * i);
+    *reinterpret_cast<uint32_t*>(codes + row_off(dr, i0, i1, di2) * d + w * 4) = word;
+  }
+}
+
+// TOKEN4 layout: one thread per (4-token group, 4 elements): 16 code bytes
+__global__ void __launch_bounds__(kThreads) k_pack_fp8_t4(const void* __restrict__ x, int dt, Rows xr, int d,
+                                                          const float* __restrict__ amax, uint8_t* __restrict__ codes,
+                                                          Rows dr, const int32_t* __restrict__ dst_pos,
+                                                          float* sc_out) {
+  const float scale = fp8_tensor_scale(*amax);
+  const double dscale = static_cast<double>(scale);
+  const int nw = d / 4;
+  const int64_t slots = t4_slots(xr.n2);
+  const int64_t total = xr.n0 * xr.n1 * slots * nw;
+  int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
+  if (gid == 0 && sc_out != nullptr) *sc_out = scale;
+  for (; gid < total; gid += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int w = static_cast<int>(gid % nw);
+    int64_t rest = gid / nw;
+    const int64_t gl = rest % slots;
+    rest /= slots;
+    const int64_t i1 = rest % xr.n1, i0 = rest / xr.n1;
+    int64_t t0, src[4];
+    if (!t4_group(xr, dr, dst_pos, i0, gl, t0, src)) continue;
+    uint4* cp = reinterpret_cast<uint4*>(codes + group_row(dr, i0, i1, t0) * d + w * 16);
+    const bool partial = src[0] < 0 || src[1] < 0 || src[2] < 0 || src[3] < 0;
+    uint4 wv = partial ? *cp : make_uint4(0, 0, 0, 0);
+    uint32_t* wd[4] = {&wv.x, &wv.y, &wv.z, &wv.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (src[j] < 0) continue;
+      const int64_t xo = row_off(xr, i0, i1, src[j]) + w * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // element 4w + i of token j: byte 4 (4w + i) + j
+        *wd[i] = (*wd[i] & ~(0xFFu << (8 * j))) | (encode_fp8(load_elem(x, dt, xo + i), dscale) << (8 * j));
     }
-    const int64_t di2 = i2 + (dst_pos != nullptr ? dst_pos[i0] : 0);
-    if (di2 < 0 || di2 >= dr.n2) continue;  // outside the destination plane
-    // a 4-byte word is half of an 8-element chunk (W = 8)
-    *reinterpret_cast<uint32_t*>(codes + plane_off(dr, layout, i0, i1, di2, d, 8, w >> 1) + (w & 1) * 4) = word;
+    *cp = wv;
   }
 }
 
@@ -224,20 +339,26 @@ __global__ void __launch_bounds__(kThreads) k_unpack_nvfp4(const uint8_t* __rest
     int blk = static_cast<int>(gid - row * nb);
     int64_t i0, i1, i2;
     unravel(row, sr, i0, i1, i2);
-    uint2 cw;
+    uint32_t c[16];
+    uint32_t sc;
     if (layout == KVQ_PLANE_TOKEN4) {
-      cw.x = *reinterpret_cast<const uint32_t*>(codes + plane_off(sr, layout, i0, i1, i2, d / 2, 4, 2 * blk));
-      cw.y = *reinterpret_cast<const uint32_t*>(codes + plane_off(sr, layout, i0, i1, i2, d / 2, 4, 2 * blk + 1));
+      const int64_t grow = group_row(sr, i0, i1, i2 & ~int64_t(3));
+      const int j = static_cast<int>(i2 & 3);
+      const uint8_t* cb = codes + grow * (d / 2) + blk * 32;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = (cb[2 * i + (j >> 1)] >> (4 * (j & 1))) & 15u;
+      sc = scales[grow * nb + blk * 4 + j];
     } else {
-      cw = *reinterpret_cast<const uint2*>(codes + plane_off(sr, layout, i0, i1, i2, d / 2, 8, blk));
+      const int64_t r = row_off(sr, i0, i1, i2);
+      const uint2 cw = *reinterpret_cast<const uint2*>(codes + r * (d / 2) + blk * 8);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = ((i < 8 ? cw.x : cw.y) >> (4 * (i & 7))) & 15u;
+      sc = scales[r * nb + blk];
     }
-    const float s_hat = static_cast<float>(e4m3_value(scales[plane_off(sr, layout, i0, i1, i2, nb, 1, blk)]));
+    const float s_hat = static_cast<float>(e4m3_value(sc));
     float* o = out + row_off(orow, i0, i1, i2) + blk * 16;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t c = ((i < 8 ? cw.x : cw.y) >> (4 * (i & 7))) & 15u;
-      o[i] = (e2m1_value(c) * s_hat) * s_t;  // e * s_hat exact in fp32, one rounding
-    }
+    for (int i = 0; i < 16; ++i) o[i] = (e2m1_value(c[i]) * s_hat) * s_t;  // e * s_hat exact in fp32, one rounding
   }
 }
 
@@ -252,7 +373,11 @@ __global__ void __launch_bounds__(kThreads) k_unpack_fp8(const uint8_t* __restri
     int col = static_cast<int>(gid - row * d);
     int64_t i0, i1, i2;
     unravel(row, sr, i0, i1, i2);
-    uint32_t c = codes[plane_off(sr, layout, i0, i1, i2, d, 8, col >> 3) + (col & 7)];
+    uint32_t c;
+    if (layout == KVQ_PLANE_TOKEN4)
+      c = codes[group_row(sr, i0, i1, i2 & ~int64_t(3)) * d + 4 * col + (i2 & 3)];
+    else
+      c = codes[row_off(sr, i0, i1, i2) * d + col];
     out[row_off(orow, i0, i1, i2) + col] = static_cast<float>(e4m3_value(c)) * sc;
   }
 }
@@ -277,17 +402,29 @@ hipError_t launch_amax(const void* x, int x_dtype, Rows rows, int d, const int32
 hipError_t launch_pack_nvfp4(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes,
                              uint8_t* scales, Rows dr, int layout, const int32_t* dst_pos, float* ts_out,
                              hipStream_t st) {
-  const int64_t items = xr.n0 * xr.n1 * xr.n2 * (d / 16);
-  hipLaunchKernelGGL(k_pack_nvfp4, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes, scales,
-                     dr, layout, dst_pos, ts_out);
+  if (layout == KVQ_PLANE_TOKEN4) {
+    const int64_t items = xr.n0 * xr.n1 * (xr.n2 / 4 + 2) * (d / 16);
+    hipLaunchKernelGGL(k_pack_nvfp4_t4, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes,
+                       scales, dr, dst_pos, ts_out);
+  } else {
+    const int64_t items = xr.n0 * xr.n1 * xr.n2 * (d / 16);
+    hipLaunchKernelGGL(k_pack_nvfp4, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes,
+                       scales, dr, dst_pos, ts_out);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_pack_fp8(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes, Rows dr,
                            int layout, const int32_t* dst_pos, float* scale_out, hipStream_t st) {
-  const int64_t items = xr.n0 * xr.n1 * xr.n2 * (d / 4);
-  hipLaunchKernelGGL(k_pack_fp8, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes, dr,
-                     layout, dst_pos, scale_out);
+  if (layout == KVQ_PLANE_TOKEN4) {
+    const int64_t items = xr.n0 * xr.n1 * (xr.n2 / 4 + 2) * (d / 4);
+    hipLaunchKernelGGL(k_pack_fp8_t4, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes, dr,
+                       dst_pos, scale_out);
+  } else {
+    const int64_t items = xr.n0 * xr.n1 * xr.n2 * (d / 4);
+    hipLaunchKernelGGL(k_pack_fp8, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes, dr,
+                       dst_pos, scale_out);
+  }
   return hipGetLastError();
 }
 

@@ -99,15 +99,26 @@ def make_inputs(cfg_key):
 
 
 # ---------------------------------------------------------------- GPU side
-def to_token4(rows, W):
-    """Byte order of the TOKEN4 plane layout, built from row-major bytes
-    [..., L, R] (L % 4 == 0): inside each group of 4 tokens, chunk k (W
-    bytes) of token j goes to byte k*4W + j*W.  Pure index permutation."""
-    a = np.asarray(rows)
-    L, R = a.shape[-2], a.shape[-1]
-    g = a.reshape(a.shape[:-2] + (L // 4, 4, R // W, W))
-    g = np.swapaxes(g, -3, -2)                       # [.., q, k, j, W]
-    return g.reshape(a.shape)
+def to_token4(codes, fmt):
+    """Byte image of a TOKEN4 plane built from the oracle's per-element codes
+    (pure index permutation, no arithmetic).  codes: [..., L, n] with one
+    code per element (E2M1 nibble values 0..15 for "nvfp4", E4M3 bytes for
+    "fp8" and for "scales", L % 4 == 0).  Inside each group of 4 tokens the
+    elements go in order and, per element, the 4 tokens in token order; two
+    NVFP4 nibbles share a byte, low nibble first."""
+    a = np.asarray(codes, dtype=np.uint8)
+    L, n = a.shape[-2], a.shape[-1]
+    g = a.reshape(a.shape[:-2] + (L // 4, 4, n))
+    g = np.swapaxes(g, -2, -1)                           # [.., q, element, token]
+    if fmt == "nvfp4":
+        g = (g[..., 0::2] | (g[..., 1::2] << 4)).astype(np.uint8)   # [.., q, element, 2]
+    return g.reshape(a.shape[:-2] + (L, -1))
+
+
+def nibbles(packed):
+    """Row-major NVFP4 code bytes [..., n/2] -> per-element nibbles [..., n]."""
+    p = np.asarray(packed, np.uint8)
+    return np.stack([p & 0xF, p >> 4], -1).reshape(p.shape[:-1] + (-1,))
 
 
 def empty_plane(fmt, shape_lead, D, layout, fill=0xFF):

@@ -103,7 +103,7 @@ def test_pack_validation(L, K):
     r_t4 = _rows(2, 3, 8, 24, 8, 1)
     r_t4_bad = _rows(2, 3, 6, 18, 6, 1)
     assert L.kvq_pack_nvfp4(FAKE, K.KVQ_BF16, r_t4_bad, 16, FAKE, FAKE, FAKE, r_t4_bad, T4, None, None, None) == 3
-    assert L.kvq_pack_fp8(FAKE, K.KVQ_BF16, r_t4, 12, FAKE, FAKE, r_t4, T4, None, None, None) == 1
+    assert L.kvq_pack_fp8(FAKE, K.KVQ_BF16, r_t4, 10, FAKE, FAKE, r_t4, T4, None, None, None) == 1
     assert L.kvq_pack_fp8(FAKE, K.KVQ_BF16, r16, 6, FAKE, FAKE, r16, R, None, None, None) == 1
     assert L.kvq_pack_fp8(FAKE, K.KVQ_F32, _rows(-1, 1, 1, 0, 0, 0), 16, FAKE, FAKE, r16, R, None, None, None) == 1
     assert L.kvq_amax(None, K.KVQ_F32, r16, 16, None, FAKE, 0, None) == 1

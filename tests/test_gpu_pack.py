@@ -9,7 +9,7 @@ import kvq_synth
 from oracle import formats as OF
 from oracle import quant as OQ
 
-from gpu_helpers import DEV, K, announce, empty_plane, to_token4
+from gpu_helpers import DEV, K, announce, empty_plane, nibbles, to_token4
 
 pytestmark = pytest.mark.gpu
 
@@ -186,8 +186,9 @@ def test_full_size_gqa32k_sampled_rows():
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
 def test_token4_layout_pack_unpack(fmt):
-    """TOKEN4 planes hold exactly the oracle's bytes in the interleaved order;
-    padding rows are left untouched; unpack reads the layout back."""
+    """TOKEN4 planes hold exactly the oracle's codes in the element-major
+    interleaved order; padding rows keep their bytes; unpack reads the
+    layout back; an append into a partly filled group keeps the neighbours."""
     announce(f"pack {fmt} token4")
     inp = kvq_synth.gqa_inputs(2, 8, 2, 128, None, kv_lens=[37, 61], config="gqa", salt=11, outliers=True)
     x = inp.v
@@ -197,25 +198,49 @@ def test_token4_layout_pack_unpack(fmt):
     amax = K().kvq_amax(xd)
     plane = empty_plane(fmt, (B, H, Lp), D, K().KVQ_PLANE_TOKEN4, fill=0xAB)
     xf = kvq_synth.f64(x)
+    pad_c = np.full((B, H, Lp - L, D), 0xAB, np.uint8)  # FP8 padding bytes
     if fmt == "nvfp4":
         K().kvq_pack_nvfp4(xd, amax, out=plane)
         c, sc, st = OQ.nvfp4_pack(xf, float(amax.item()))
-        pad = np.full((B, H, Lp - L), 0xAB, np.uint8)
-        c_full = np.concatenate([c, np.broadcast_to(pad[..., None], (B, H, Lp - L, D // 2))], axis=2)
-        s_full = np.concatenate([sc, np.broadcast_to(pad[..., None], (B, H, Lp - L, D // 16))], axis=2)
+        # untouched 0xAB bytes read as nibble 0xB for even tokens of a group
+        # (low nibble) and 0xA for odd ones
+        pad_n = np.where((np.arange(L, Lp) % 2 == 0)[:, None], 0xB, 0xA).astype(np.uint8)
+        pad_n = np.broadcast_to(pad_n, (B, H, Lp - L, D))
+        c_full = np.concatenate([nibbles(c), pad_n], axis=2)
+        s_full = np.concatenate([sc, np.full((B, H, Lp - L, D // 16), 0xAB, np.uint8)], axis=2)
         torch.cuda.synchronize()
-        assert np.array_equal(_np(plane.codes), to_token4(c_full, 4))
-        assert np.array_equal(_np(plane.scales), to_token4(s_full, 1))
+        assert np.array_equal(_np(plane.scales), to_token4(s_full, "scales"))
+        assert np.array_equal(_np(plane.codes), to_token4(c_full, "nvfp4"))
         u = K().kvq_unpack_nvfp4(plane)
         ref = OF.fp32_round(OQ.nvfp4_unpack(c, sc, st))
     else:
         K().kvq_pack_fp8(xd, amax, out=plane)
         c, sc = OQ.fp8_pack(xf, float(amax.item()))
-        pad = np.full((B, H, Lp - L, D), 0xAB, np.uint8)
-        c_full = np.concatenate([c, pad], axis=2)
+        c_full = np.concatenate([c, pad_c], axis=2)
         torch.cuda.synchronize()
-        assert np.array_equal(_np(plane.codes), to_token4(c_full, 8))
+        assert np.array_equal(_np(plane.codes), to_token4(c_full, "fp8"))
         u = K().kvq_unpack_fp8(plane)
         ref = OF.fp32_round(OQ.fp8_unpack(c, sc))
     torch.cuda.synchronize()
     assert np.array_equal(_np(u)[:, :, :L].astype(np.float64), ref)
+    # append one token per request into the last, partly filled group: the
+    # other tokens of that group must keep their bytes
+    before = _np(u).copy()
+    new = torch.randn(B, H, 1, D, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    pos = torch.tensor([L, L - 2], dtype=torch.int32, device=DEV)
+    if fmt == "nvfp4":
+        K().kvq_pack_nvfp4(new.to(DEV), amax, out=plane, dst_pos=pos)
+        nc, ns, _ = OQ.nvfp4_pack(kvq_synth.f64(new), float(amax.item()))
+        nref = OF.fp32_round(OQ.nvfp4_unpack(nc, ns, st))
+        u2 = K().kvq_unpack_nvfp4(plane)
+    else:
+        K().kvq_pack_fp8(new.to(DEV), amax, out=plane, dst_pos=pos)
+        nc, _ = OQ.fp8_pack(kvq_synth.f64(new), float(amax.item()))
+        nref = OF.fp32_round(OQ.fp8_unpack(nc, sc))
+        u2 = K().kvq_unpack_fp8(plane)
+    torch.cuda.synchronize()
+    u2 = _np(u2)
+    for b_, p_ in enumerate([L, L - 2]):
+        assert np.array_equal(u2[b_, :, p_].astype(np.float64), nref[b_, :, 0])
+        keep = [t for t in range(L) if t != p_]
+        assert np.array_equal(u2[b_][:, keep], before[b_][:, keep])
