@@ -86,8 +86,32 @@ __device__ inline f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-template <typename T>
-__device__ inline T ldg(const T* p) { return *p; }
+// ------------------------------------------------------------------ loads
+// Raw buffer loads: base and size live in a (uniform) buffer resource, the
+// lane supplies a byte offset; offsets at or past the size read as zero.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcFlags = 0x00020000;   // gfx9 raw buffer: 32-bit data format, no swizzle
+
+__device__ inline Rsrc make_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes > 0 ? bytes : 0, kRsrcFlags);
+}
+__device__ inline u32x4 ld128(Rsrc r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline u32x2 ld64(Rsrc r, int off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ inline uint32_t ld32(Rsrc r, int off) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline uint32_t ld16(Rsrc r, int off) {
+  return static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+__device__ inline uint32_t ld8(Rsrc r, int off) {
+  return static_cast<uint8_t>(__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0));
+}
 
 // ------------------------------------------------------------------ traits
 template <int KVF, int D>
@@ -197,7 +221,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
   __shared__ int lds_last;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int c = lane & 15;   // MFMA column / row-within-16 of this lane
   const int g = lane >> 4;   // lane group (k-slice of the MFMA operands)
   const int split = blockIdx.x;
@@ -248,117 +272,117 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
       }
     }
 
-    // per-(request, kv head) plane bases; token offsets below fit in 32 bits
+    // per-(request, kv head) plane bases
     const int64_t head_row = static_cast<int64_t>(b) * a.kv_sb + static_cast<int64_t>(kvh) * a.kv_sh;
     const uint8_t* kc = a.k_codes + head_row * Gm::kRowBytes;
     const uint8_t* vc = a.v_codes + head_row * Gm::kRowBytes;
-    const uint8_t* ksc = (KVF == KVQ_NVFP4) ? a.k_scales + head_row * Gm::kScaleBytes : nullptr;
-    const uint8_t* vsc = (KVF == KVQ_NVFP4) ? a.v_scales + head_row * Gm::kScaleBytes : nullptr;
-    const int st = static_cast<int>(a.kv_st);
+    const uint8_t* ksc = (KVF == KVQ_NVFP4) ? a.k_scales + head_row * Gm::kScaleBytes : kc;
+    const uint8_t* vsc = (KVF == KVQ_NVFP4) ? a.v_scales + head_row * Gm::kScaleBytes : vc;
+    // token stride in rows (always 1 with a TOKEN4 V plane, K and V share it)
+    const int st = (VL == KVQ_PLANE_TOKEN4) ? 1 : static_cast<int>(a.kv_st);
+    constexpr int RB = Gm::kRowBytes;
+    constexpr int SB = Gm::kScaleBytes;
 
-    // Loads of one tile.  A full tile with unit token stride uses one
-    // per-lane base address and immediate offsets (no per-load arithmetic);
-    // the last, partial tile (or a strided cache) clamps every token to the
-    // chunk so that no row past kv_len is touched.
-    const bool unit_stride = (st == 1);
-    // per-lane byte offsets inside a tile (unit token stride)
-    const uint32_t lk = static_cast<uint32_t>(c * Gm::kRowBytes + g * (Gm::kKWords * 4));
-    const uint32_t lks = static_cast<uint32_t>(c * Gm::kScaleBytes + (D == 128 ? 2 * g : g));
-    const uint32_t lv = static_cast<uint32_t>(4 * g * Gm::kRowBytes + c * Gm::kVBytes);
-    const uint32_t lvs = static_cast<uint32_t>(4 * g * Gm::kScaleBytes + (c * Gm::kPvElems) / 16);
+    // Every load goes through a buffer resource whose base is the tile's
+    // first token and whose size ends at the chunk end ce: lanes whose token
+    // is at or past ce read zeros (hardware range check, nothing is
+    // fetched), and the prefetch past a wave's last tile touches no memory.
+    // Lane offsets are fixed for the whole chunk, so the loop does no
+    // address arithmetic.  (All byte offsets stay below 2^31.)
+    const int lk = c * st * RB + g * (Gm::kKWords * 4);          // K codes: token c, quarter g
+    const int lks = c * st * SB + (D == 128 ? 2 * g : g);          // K scales of that quarter
+    const int lv = 4 * g * st * RB + c * Gm::kVBytes;              // V codes (row layout)
+    const int lvs = 4 * g * st * SB + (c * Gm::kPvElems) / 16;     // V scales (row layout)
+    constexpr int GB = 4 * RB;                // TOKEN4: bytes per 4-token group (codes)
+    constexpr int GS = 4 * SB;                //         bytes per 4-token group (scales)
+    constexpr int CB = 4 * Gm::kVBytes;       //         this lane's run inside a group
+    const int lvt = g * GB + c * CB;
+    const int lvts = g * GS + (c / 2) * 4;
 
-    auto load_k = [&](KT& R, int u, const uint8_t* kp, const uint8_t* sp) {
-      if constexpr (Gm::kKWords == 8) {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(kp);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(kp + 16);
-        R.k[u][0] = x0.x; R.k[u][1] = x0.y; R.k[u][2] = x0.z; R.k[u][3] = x0.w;
-        R.k[u][4] = x1.x; R.k[u][5] = x1.y; R.k[u][6] = x1.z; R.k[u][7] = x1.w;
-      } else if constexpr (Gm::kKWords == 4) {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(kp);
-        R.k[u][0] = x0.x; R.k[u][1] = x0.y; R.k[u][2] = x0.z; R.k[u][3] = x0.w;
-      } else {
-        const uint2 x0 = *reinterpret_cast<const uint2*>(kp);
-        R.k[u][0] = x0.x; R.k[u][1] = x0.y;
-      }
-      if constexpr (KVF == KVQ_NVFP4) {
-        if constexpr (D == 128) R.ks[u] = *reinterpret_cast<const uint16_t*>(sp);
-        else R.ks[u] = *sp;
-      }
-    };
-    auto load_v = [&](VT& R, int u, int i, const uint8_t* vp, const uint8_t* sp) {
-      if constexpr (Gm::kVBytes == 8) {
-        const uint2 x = *reinterpret_cast<const uint2*>(vp);
-        R.v[u][i][0] = x.x; R.v[u][i][1] = x.y;
-      } else if constexpr (Gm::kVBytes == 4) {
-        R.v[u][i][0] = *reinterpret_cast<const uint32_t*>(vp);
-      } else {
-        R.v[u][i][0] = *reinterpret_cast<const uint16_t*>(vp);
-      }
-      if constexpr (KVF == KVQ_NVFP4) R.vs[u][i] = *sp;
-    };
-    // Loads of one tile.  A full tile with unit token stride uses one
-    // uniform tile base, one per-lane offset and immediate offsets (no
-    // per-load address arithmetic); the last, partial tile (or a strided
-    // cache) clamps every token to the chunk so that no row past kv_len is
-    // read.
     auto load_ktile = [&](KT& R, int tile) {
       const int tb = cs + tile * TT;
-      if (unit_stride && tb + TT <= ce) {
-        const uint8_t* kt = kc + static_cast<size_t>(tb) * Gm::kRowBytes + lk;
-        const uint8_t* kst = (KVF == KVQ_NVFP4) ? ksc + static_cast<size_t>(tb) * Gm::kScaleBytes + lks : nullptr;
+      const int nv = ce - tb;
+      const int64_t base = static_cast<int64_t>(tb) * st;
+      const Rsrc rk = make_rsrc(kc + base * RB, nv * st * RB);
+      const Rsrc rks = make_rsrc(ksc + base * SB, nv * st * SB);
 #pragma unroll
-        for (int u = 0; u < NT; ++u) load_k(R, u, kt + 16 * u * Gm::kRowBytes, kst + 16 * u * Gm::kScaleBytes);
-      } else {
+      for (int u = 0; u < NT; ++u) {
+        const int o = lk + u * 16 * st * RB;
+        if constexpr (Gm::kKWords == 8) {
+          const u32x4 x0 = ld128(rk, o), x1 = ld128(rk, o + 16);
 #pragma unroll
-        for (int u = 0; u < NT; ++u) {
-          int t = tb + 16 * u + c;
-          t = t < ce ? t : ce - 1;
-          const int r = t * st;
-          load_k(R, u, kc + r * Gm::kRowBytes + g * (Gm::kKWords * 4),
-                 (KVF == KVQ_NVFP4) ? ksc + r * Gm::kScaleBytes + (D == 128 ? 2 * g : g) : nullptr);
+          for (int w = 0; w < 4; ++w) { R.k[u][w] = x0[w]; R.k[u][4 + w] = x1[w]; }
+        } else if constexpr (Gm::kKWords == 4) {
+          const u32x4 x0 = ld128(rk, o);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) R.k[u][w] = x0[w];
+        } else {
+          const u32x2 x0 = ld64(rk, o);
+          R.k[u][0] = x0[0]; R.k[u][1] = x0[1];
+        }
+        if constexpr (KVF == KVQ_NVFP4) {
+          const int os = lks + u * 16 * st * SB;
+          R.ks[u] = (D == 128) ? ld16(rks, os) : ld8(rks, os);
         }
       }
     };
     auto load_vtile = [&](VT& R, int tile) {
       const int tb = cs + tile * TT;
+      const int nv = ce - tb;
       if constexpr (VL == KVQ_PLANE_TOKEN4) {
-        // Group q = 4 consecutive tokens, stored element-major: for this
-        // lane's elements [8c, 8c+8) the 4 tokens' codes are one contiguous
-        // run (16 bytes NVFP4, 32 bytes FP8), and block c/2's 4 scale bytes
-        // one dword.  Lane group g takes group 4u+g of sub-tile u.
-        constexpr int GB = 4 * Gm::kRowBytes;      // bytes per 4-token group (codes)
-        constexpr int GS = 4 * Gm::kScaleBytes;    // bytes per 4-token group (scales)
-        constexpr int CB = 4 * Gm::kVBytes;        // bytes of one lane's chunk in a group
-        if (tb + TT <= ce) {
-          const uint8_t* vp = vc + static_cast<size_t>(tb / 4 + g) * GB + c * CB;
-          const uint8_t* sp = (KVF == KVQ_NVFP4) ? vsc + static_cast<size_t>(tb / 4 + g) * GS + (c / 2) * 4 : nullptr;
+        // Group 4u+g of the tile (lane group g): for this lane's elements
+        // [8c, 8c+8) the 4 tokens' codes are one contiguous run (16 bytes
+        // NVFP4, 32 bytes FP8) and block c/2's 4 scale bytes one dword.  A
+        // group that straddles ce is read whole; pv_tile clears its tokens
+        // past ce.
+        const int ng = nv > 0 ? (nv + 3) / 4 : 0;
+        const Rsrc rv = make_rsrc(vc + static_cast<int64_t>(tb) * RB, ng * GB);
+        const Rsrc rvs = make_rsrc(vsc + static_cast<int64_t>(tb) * SB, ng * GS);
 #pragma unroll
-          for (int u = 0; u < NT; ++u) {
-            const uint4 x0 = *reinterpret_cast<const uint4*>(vp + u * 4 * GB);
-            R.t4[u][0] = x0.x; R.t4[u][1] = x0.y; R.t4[u][2] = x0.z; R.t4[u][3] = x0.w;
-            if constexpr (CB == 32) {
-              const uint4 x1 = *reinterpret_cast<const uint4*>(vp + u * 4 * GB + 16);
-              R.t4[u][4] = x1.x; R.t4[u][5] = x1.y; R.t4[u][6] = x1.z; R.t4[u][7] = x1.w;
-            }
-            if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] = *reinterpret_cast<const uint32_t*>(sp + u * 4 * GS);
+        for (int u = 0; u < NT; ++u) {
+          const int o = lvt + u * 4 * GB;
+          const u32x4 x0 = ld128(rv, o);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) R.t4[u][w] = x0[w];
+          if constexpr (CB == 32) {
+            const u32x4 x1 = ld128(rv, o + 16);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) R.t4[u][4 + w] = x1[w];
           }
-        } else {
+          if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] = ld32(rvs, lvts + u * 4 * GS);
+        }
+      } else {
+        const int64_t base = static_cast<int64_t>(tb) * st;
+        const Rsrc rv = make_rsrc(vc + base * RB, nv * st * RB);
+        const Rsrc rvs = make_rsrc(vsc + base * SB, nv * st * SB);
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int o = lv + (16 * u + i) * st * RB;
+            if constexpr (Gm::kVBytes == 8) {
+              const u32x2 x = ld64(rv, o);
+              R.v[u][i][0] = x[0]; R.v[u][i][1] = x[1];
+            } else if constexpr (Gm::kVBytes == 4) {
+              R.v[u][i][0] = ld32(rv, o);
+            } else {
+              R.v[u][i][0] = ld16(rv, o);
+            }
+            if constexpr (KVF == KVQ_NVFP4) R.vs[u][i] = ld8(rvs, lvs + (16 * u + i) * st * SB);
+          }
+        }
+      }
+    };
+    // TOKEN4: clear the codes and scales of tokens at or past ce inside the
+    // group that straddles it (their probabilities are zero, and zero must
+    // never meet bytes that were never written)
+    auto mask_vtile = [&](VT& R, int tile) {
+      if constexpr (VL == KVQ_PLANE_TOKEN4) {
+        const int tb = cs + tile * TT;
+        if (tb + TT > ce) {
 #pragma unroll
           for (int u = 0; u < NT; ++u) {
-            int q = (tb + 16 * u) / 4 + g;
-            const int nvalid = ce - 4 * q;
-            if (nvalid <= 0) q = (ce - 1) / 4;       // keep the load inside the chunk
-            const uint8_t* vp = vc + static_cast<size_t>(q) * GB + c * CB;
-            const uint4 x0 = *reinterpret_cast<const uint4*>(vp);
-            R.t4[u][0] = x0.x; R.t4[u][1] = x0.y; R.t4[u][2] = x0.z; R.t4[u][3] = x0.w;
-            if constexpr (CB == 32) {
-              const uint4 x1 = *reinterpret_cast<const uint4*>(vp + 16);
-              R.t4[u][4] = x1.x; R.t4[u][5] = x1.y; R.t4[u][6] = x1.z; R.t4[u][7] = x1.w;
-            }
-            if constexpr (KVF == KVQ_NVFP4)
-              R.vs[u][0] = *reinterpret_cast<const uint32_t*>(vsc + static_cast<size_t>(q) * GS + (c / 2) * 4);
-            // tokens past the chunk end: zero their codes and scales (their
-            // probabilities are zero; 0 must never meet unread bytes)
+            const int nvalid = ce - (tb + 16 * u + 4 * g);
             uint32_t keep = 0xFFFFFFFFu, keep_s = 0xFFFFFFFFu;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -369,27 +393,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
             }
 #pragma unroll
             for (int w = 0; w < CB / 4; ++w) R.t4[u][w] &= keep;
-            if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] &= keep_s;
-          }
-        }
-      } else if (unit_stride && tb + TT <= ce) {
-        const uint8_t* vt_ = vc + static_cast<size_t>(tb) * Gm::kRowBytes + lv;
-        const uint8_t* vst = (KVF == KVQ_NVFP4) ? vsc + static_cast<size_t>(tb) * Gm::kScaleBytes + lvs : nullptr;
-#pragma unroll
-        for (int u = 0; u < NT; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            load_v(R, u, i, vt_ + (16 * u + i) * Gm::kRowBytes, vst + (16 * u + i) * Gm::kScaleBytes);
-      } else {
-#pragma unroll
-        for (int u = 0; u < NT; ++u) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            int tv = tb + 16 * u + 4 * g + i;
-            tv = tv < ce ? tv : ce - 1;
-            const int rv = tv * st;
-            load_v(R, u, i, vc + rv * Gm::kRowBytes + c * Gm::kVBytes,
-                   (KVF == KVQ_NVFP4) ? vsc + rv * Gm::kScaleBytes + (c * Gm::kPvElems) / 16 : nullptr);
+            R.vs[u][0] &= keep_s;
           }
         }
       }
@@ -601,28 +605,33 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
     // have 8-16 sub-tiles per tile and use one register set.)
     f16x2 p_hi[NACC][2], p_lo[NACC][2];
     if constexpr (NT <= 4) {
+      // loads past the wave's last tile are empty (size-0 resources)
       KT KA, KB;
       VT VA, VB;
+      // (scheduling barriers keep each prefetch ahead of the compute that
+      // follows it, so a full tile of work hides every load)
       int tile = wave;
       load_ktile(KA, tile);
       load_vtile(VA, tile);
       while (true) {
-        int nxt = tile + kWaves;
-        const bool more = nxt < ntiles;
-        if (more) load_ktile(KB, nxt);
+        load_ktile(KB, tile + kWaves);
+        __builtin_amdgcn_sched_barrier(0);
         qk_tile(KA, tile, p_hi, p_lo);
-        if (more) load_vtile(VB, nxt);
+        load_vtile(VB, tile + kWaves);
+        __builtin_amdgcn_sched_barrier(0);
+        mask_vtile(VA, tile);
         pv_tile(VA, p_hi, p_lo);
-        if (!more) break;
-        tile = nxt;
-        nxt = tile + kWaves;
-        const bool more2 = nxt < ntiles;
-        if (more2) load_ktile(KA, nxt);
+        tile += kWaves;
+        if (tile >= ntiles) break;
+        load_ktile(KA, tile + kWaves);
+        __builtin_amdgcn_sched_barrier(0);
         qk_tile(KB, tile, p_hi, p_lo);
-        if (more2) load_vtile(VA, nxt);
+        load_vtile(VA, tile + kWaves);
+        __builtin_amdgcn_sched_barrier(0);
+        mask_vtile(VB, tile);
         pv_tile(VB, p_hi, p_lo);
-        if (!more2) break;
-        tile = nxt;
+        tile += kWaves;
+        if (tile >= ntiles) break;
       }
     } else {
       KT KA;
@@ -631,6 +640,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
         load_ktile(KA, tile);
         load_vtile(VA, tile);
         qk_tile(KA, tile, p_hi, p_lo);
+        mask_vtile(VA, tile);
         pv_tile(VA, p_hi, p_lo);
       }
     }
