@@ -166,6 +166,34 @@ int kvq_pack_fp8(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, con
                  float* scale_out, void* stream);
 
 /*
+ * Batched packing: several planes (for instance the K and the V rows of the
+ * new tokens of one decode step) quantized in ONE launch.  Each job carries
+ * exactly the arguments of one kvq_pack_nvfp4 / kvq_pack_fp8 call (scales
+ * is ignored for FP8; scale_out receives the tensor scale or is NULL) and is
+ * validated as that call would be; the destinations of different jobs must
+ * not overlap.  jobs is a host array of 1..KVQ_MAX_PACK_JOBS entries, read
+ * before the call returns.  Errors: as the single-plane calls, plus
+ * KVQ_ERR_ARG for n_jobs outside [1, KVQ_MAX_PACK_JOBS].
+ */
+#define KVQ_MAX_PACK_JOBS 8
+typedef struct {
+  const void* x;
+  int32_t x_dtype;
+  kvq_rows x_rows;
+  int32_t d;
+  const float* amax;
+  uint8_t* codes;
+  uint8_t* scales;
+  kvq_rows dst_rows;
+  int32_t dst_layout;
+  const int32_t* dst_pos;
+  float* scale_out;
+} kvq_pack_job;
+
+int kvq_pack_nvfp4_batch(const kvq_pack_job* jobs, int32_t n_jobs, void* stream);
+int kvq_pack_fp8_batch(const kvq_pack_job* jobs, int32_t n_jobs, void* stream);
+
+/*
  * kvq_unpack_nvfp4 - dequantize NVFP4 rows to float32: out = fp32(E2M1(c) *
  * s_hat * s_t) (one rounding; e * s_hat is exact).  Test / inspection path.
  *   codes, scales  device planes per src_rows and src_layout (KVQ_PLANE_*);

@@ -144,6 +144,33 @@ def kvq_pack_fp8(x: torch.Tensor, amax: torch.Tensor, out: Optional[FP8Plane] = 
     return out
 
 
+def kvq_pack_batch(jobs, stream=None):
+    """Pack several planes in one launch.  jobs: sequence of
+    (x, amax, plane, dst_pos) with plane an NVFP4Plane (all of them) or an
+    FP8Plane (all of them) already allocated; dst_pos may be None.  Typical
+    use: the K and V rows of the new tokens of a decode step."""
+    if not 1 <= len(jobs) <= _lib.KVQ_MAX_PACK_JOBS:
+        raise ValueError(f"1..{_lib.KVQ_MAX_PACK_JOBS} jobs per call")
+    fp4 = isinstance(jobs[0][2], NVFP4Plane)
+    arr = (_lib.KvqPackJob * len(jobs))()
+    for i, (x, amax, plane, dst_pos) in enumerate(jobs):
+        if isinstance(plane, NVFP4Plane) != fp4:
+            raise ValueError("all jobs of a batch must have the same format")
+        d = x.shape[-1]
+        if fp4:
+            dst = _rows(plane.codes, d // 2)
+            sdst = _rows(plane.scales, d // 16)
+            if (dst.s0, dst.s1, dst.s2) != (sdst.s0, sdst.s1, sdst.s2):
+                raise ValueError("code and scale planes must share their row layout")
+            scales, sout = _ptr(plane.scales), _ptr(plane.tensor_scale)
+        else:
+            dst, scales, sout = _rows(plane.codes, d), ctypes.c_void_p(0), _ptr(plane.scale)
+        arr[i] = _lib.KvqPackJob(_ptr(x), _DT[x.dtype], _rows(x), d, _ptr(amax), _ptr(plane.codes), scales, dst,
+                                 plane.layout, _ptr(dst_pos), sout)
+    fn = _lib.lib().kvq_pack_nvfp4_batch if fp4 else _lib.lib().kvq_pack_fp8_batch
+    check(fn(arr, len(jobs), _stream(stream)))
+
+
 def kvq_unpack_nvfp4(p: NVFP4Plane, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     d = p.d
     if out is None:

@@ -22,6 +22,16 @@ class KvqRows(ctypes.Structure):
                 ("s0", ctypes.c_int64), ("s1", ctypes.c_int64), ("s2", ctypes.c_int64)]
 
 
+class KvqPackJob(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int32), ("x_rows", KvqRows), ("d", ctypes.c_int32),
+                ("amax", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("dst_rows", KvqRows), ("dst_layout", ctypes.c_int32), ("dst_pos", ctypes.c_void_p),
+                ("scale_out", ctypes.c_void_p)]
+
+
+KVQ_MAX_PACK_JOBS = 8
+
+
 class KvqDecodeArgs(ctypes.Structure):
     _fields_ = [
         ("kv_format", ctypes.c_int32), ("layout", ctypes.c_int32),
@@ -54,6 +64,8 @@ _PROTOS = {
     "kvq_amax": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, _I32, _VP]),
     "kvq_pack_nvfp4": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, _VP, KvqRows, _I32, _VP, _VP, _VP]),
     "kvq_pack_fp8": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, KvqRows, _I32, _VP, _VP, _VP]),
+    "kvq_pack_nvfp4_batch": (ctypes.c_int, [ctypes.POINTER(KvqPackJob), _I32, _VP]),
+    "kvq_pack_fp8_batch": (ctypes.c_int, [ctypes.POINTER(KvqPackJob), _I32, _VP]),
     "kvq_unpack_nvfp4": (ctypes.c_int, [_VP, _VP, KvqRows, _I32, _I32, _VP, _VP, KvqRows, _VP]),
     "kvq_unpack_fp8": (ctypes.c_int, [_VP, KvqRows, _I32, _I32, _VP, _VP, KvqRows, _VP]),
     "attn_decode_splitkv": (ctypes.c_int, [ctypes.POINTER(KvqDecodeArgs), ctypes.POINTER(_I32), _VP]),

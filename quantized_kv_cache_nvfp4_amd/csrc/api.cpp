@@ -70,6 +70,46 @@ int check_layout(int32_t layout, const kvq_rows& r, const char* name) {
   return KVQ_OK;
 }
 
+// Validation of one pack job (the rules of kvq_pack_nvfp4 / kvq_pack_fp8).
+int check_pack_job(const kvq_pack_job& j, bool fp4) {
+  int rc;
+  if ((rc = check_float_input(j.x, j.x_dtype, "x")) != KVQ_OK) return rc;
+  if ((rc = check_rows(j.x_rows, "x_rows")) != KVQ_OK) return rc;
+  if ((rc = check_rows(j.dst_rows, "dst_rows")) != KVQ_OK) return rc;
+  if (fp4) {
+    if (j.d <= 0 || j.d % 16 != 0 || j.d > 1024)
+      return fail(KVQ_ERR_ARG, "d must be a positive multiple of 16, <= 1024 (got %d)", j.d);
+    if (j.amax == nullptr || j.codes == nullptr || j.scales == nullptr)
+      return fail(KVQ_ERR_ARG, "amax, codes and scales must be non-null");
+  } else {
+    if (j.d <= 0 || j.d % 4 != 0 || j.d > 4096)
+      return fail(KVQ_ERR_ARG, "d must be a positive multiple of 4, <= 4096 (got %d)", j.d);
+    if (j.amax == nullptr || j.codes == nullptr) return fail(KVQ_ERR_ARG, "amax and codes must be non-null");
+  }
+  if (!fits_dst(j.x_rows, j.dst_rows))
+    return fail(KVQ_ERR_ARG, "dst_rows must match x_rows in n0, n1 and be at least as long in n2");
+  if (!aligned(j.codes, fp4 ? 8 : 4)) return fail(KVQ_ERR_ALIGN, "codes plane must be %d-byte aligned", fp4 ? 8 : 4);
+  return check_layout(j.dst_layout, j.dst_rows, "dst_rows");
+}
+
+int pack_batch(const kvq_pack_job* jobs, int32_t n_jobs, bool fp4, const char* what, void* stream) {
+  if (jobs == nullptr || n_jobs < 1 || n_jobs > KVQ_MAX_PACK_JOBS)
+    return fail(KVQ_ERR_ARG, "%s: n_jobs must be in [1, %d] with a non-null jobs array", what, KVQ_MAX_PACK_JOBS);
+  kvq::PackJobs P{};
+  P.n = 0;
+  for (int i = 0; i < n_jobs; ++i) {
+    const kvq_pack_job& j = jobs[i];
+    int rc = check_pack_job(j, fp4);
+    if (rc != KVQ_OK) return rc;
+    if (n_rows(j.x_rows) == 0) continue;
+    P.j[P.n++] = kvq::PackJob{j.x, j.x_dtype, kvq::to_rows(j.x_rows), j.d, j.amax, j.codes, j.scales,
+                              kvq::to_rows(j.dst_rows), j.dst_layout, j.dst_pos, j.scale_out};
+  }
+  if (P.n == 0) return ok();
+  const hipError_t e = fp4 ? kvq::launch_pack_nvfp4(P, as_stream(stream)) : kvq::launch_pack_fp8(P, as_stream(stream));
+  return hip_status(e, what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,38 +136,22 @@ int kvq_amax(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const i
 int kvq_pack_nvfp4(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax, uint8_t* codes,
                    uint8_t* scales, kvq_rows dst_rows, int32_t dst_layout, const int32_t* dst_pos,
                    float* tensor_scale_out, void* stream) {
-  int rc;
-  if ((rc = check_float_input(x, x_dtype, "x")) != KVQ_OK) return rc;
-  if ((rc = check_rows(x_rows, "x_rows")) != KVQ_OK) return rc;
-  if ((rc = check_rows(dst_rows, "dst_rows")) != KVQ_OK) return rc;
-  if (d <= 0 || d % 16 != 0 || d > 1024) return fail(KVQ_ERR_ARG, "d must be a positive multiple of 16, <= 1024 (got %d)", d);
-  if (amax == nullptr || codes == nullptr || scales == nullptr)
-    return fail(KVQ_ERR_ARG, "amax, codes and scales must be non-null");
-  if (!fits_dst(x_rows, dst_rows)) return fail(KVQ_ERR_ARG, "dst_rows must match x_rows in n0, n1 and be at least as long in n2");
-  if (!aligned(codes, 8)) return fail(KVQ_ERR_ALIGN, "codes plane must be 8-byte aligned");
-  if ((rc = check_layout(dst_layout, dst_rows, "dst_rows")) != KVQ_OK) return rc;
-  if (n_rows(x_rows) == 0) return ok();
-  return hip_status(kvq::launch_pack_nvfp4(x, x_dtype, kvq::to_rows(x_rows), d, amax, codes, scales,
-                                           kvq::to_rows(dst_rows), dst_layout, dst_pos, tensor_scale_out,
-                                           as_stream(stream)),
-                    "kvq_pack_nvfp4 launch");
+  const kvq_pack_job j{x, x_dtype, x_rows, d, amax, codes, scales, dst_rows, dst_layout, dst_pos, tensor_scale_out};
+  return pack_batch(&j, 1, true, "kvq_pack_nvfp4", stream);
 }
 
 int kvq_pack_fp8(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax, uint8_t* codes,
                  kvq_rows dst_rows, int32_t dst_layout, const int32_t* dst_pos, float* scale_out, void* stream) {
-  int rc;
-  if ((rc = check_float_input(x, x_dtype, "x")) != KVQ_OK) return rc;
-  if ((rc = check_rows(x_rows, "x_rows")) != KVQ_OK) return rc;
-  if ((rc = check_rows(dst_rows, "dst_rows")) != KVQ_OK) return rc;
-  if (d <= 0 || d % 4 != 0 || d > 4096) return fail(KVQ_ERR_ARG, "d must be a positive multiple of 4, <= 4096 (got %d)", d);
-  if (amax == nullptr || codes == nullptr) return fail(KVQ_ERR_ARG, "amax and codes must be non-null");
-  if (!fits_dst(x_rows, dst_rows)) return fail(KVQ_ERR_ARG, "dst_rows must match x_rows in n0, n1 and be at least as long in n2");
-  if (!aligned(codes, 4)) return fail(KVQ_ERR_ALIGN, "codes plane must be 4-byte aligned");
-  if ((rc = check_layout(dst_layout, dst_rows, "dst_rows")) != KVQ_OK) return rc;
-  if (n_rows(x_rows) == 0) return ok();
-  return hip_status(kvq::launch_pack_fp8(x, x_dtype, kvq::to_rows(x_rows), d, amax, codes, kvq::to_rows(dst_rows),
-                                         dst_layout, dst_pos, scale_out, as_stream(stream)),
-                    "kvq_pack_fp8 launch");
+  const kvq_pack_job j{x, x_dtype, x_rows, d, amax, codes, nullptr, dst_rows, dst_layout, dst_pos, scale_out};
+  return pack_batch(&j, 1, false, "kvq_pack_fp8", stream);
+}
+
+int kvq_pack_nvfp4_batch(const kvq_pack_job* jobs, int32_t n_jobs, void* stream) {
+  return pack_batch(jobs, n_jobs, true, "kvq_pack_nvfp4_batch", stream);
+}
+
+int kvq_pack_fp8_batch(const kvq_pack_job* jobs, int32_t n_jobs, void* stream) {
+  return pack_batch(jobs, n_jobs, false, "kvq_pack_fp8_batch", stream);
 }
 
 int kvq_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, kvq_rows src_rows, int32_t src_layout, int32_t d,

@@ -17,32 +17,26 @@
 namespace kvq {
 namespace {
 
-constexpr int kThreads = 128;
+constexpr int kThreads = 256;   // 4 waves: one (request, head) per wave
 
-// grid: (B*Hq); block: 128 threads over Dv.  One thread computes the split
-// weights into LDS; every thread then merges its columns.
+// grid: ceil(B*Hq / 4); one wave per (request, head)
 __global__ void __launch_bounds__(kThreads) k_combine(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-                                                      int Dv, int s, void* __restrict__ out, int out_dtype,
+                                                      int nbh, int Dv, int s, void* __restrict__ out, int out_dtype,
                                                       const float* __restrict__ out_scale, float* __restrict__ lse_out) {
-  __shared__ float w_s[64];
-  __shared__ float stat[2];
-  const int64_t bh = blockIdx.x;
-  if (threadIdx.x == 0) split_weights(part_lse + bh * s, s, w_s, stat[0], stat[1]);
-  __syncthreads();
+  const int64_t bh = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (bh >= nbh) return;   // whole waves leave together
   const float osc = (out_dtype == KVQ_FP8E4M3) ? *out_scale : 1.0f;
-  for (int d = threadIdx.x; d < Dv; d += kThreads) {
-    const float o = combine_column(part_o + bh * s * Dv + d, Dv, w_s, s, stat[0]);
-    store_out(out, out_dtype, bh * Dv + d, o, osc);
-  }
-  if (threadIdx.x == 0 && lse_out != nullptr) lse_out[bh] = stat[1];
+  combine_head<false>(part_lse + bh * s, part_o + bh * s * Dv, s, Dv, out, out_dtype, bh * Dv, osc,
+                      lse_out != nullptr ? lse_out + bh : nullptr);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const float* part_o, const float* part_lse, int B, int Hq, int Dv, int s, void* out,
                           int out_dtype, const float* out_scale, float* lse_out, hipStream_t st) {
-  hipLaunchKernelGGL(k_combine, dim3(B * Hq), dim3(kThreads), 0, st, part_o, part_lse, Dv, s, out, out_dtype, out_scale,
-                     lse_out);
+  const int nbh = B * Hq;
+  hipLaunchKernelGGL(k_combine, dim3((nbh + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads), 0, st, part_o, part_lse,
+                     nbh, Dv, s, out, out_dtype, out_scale, lse_out);
   return hipGetLastError();
 }
 

@@ -11,34 +11,12 @@
 
 namespace kvq {
 
-// w[j] = exp(lse_j - M); returns 1/sum in inv and the merged LSE in lse_m.
-__device__ inline void split_weights(const float* lse, int s, float* w, float& inv, float& lse_m) {
-  float M = -INFINITY;
-  for (int j = 0; j < s; ++j) M = fmaxf(M, lse[j]);
-  float sum = 0.0f;
-  for (int j = 0; j < s; ++j) {
-    const float lj = lse[j];
-    const float wj = (M == -INFINITY || lj == -INFINITY) ? 0.0f : __expf(lj - M);
-    w[j] = wj;
-    sum += wj;
-  }
-  inv = sum > 0.0f ? 1.0f / sum : 0.0f;
-  lse_m = sum > 0.0f ? M + __logf(sum) : -INFINITY;
-}
-
-// sum_j w[j] * po[j * stride] with four independent accumulators (so the
-// loads are in flight together), times inv.
-__device__ inline float combine_column(const float* po, int64_t stride, const float* w, int s, float inv) {
-  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-  int j = 0;
-  for (; j + 4 <= s; j += 4) {
-    a0 += w[j] * po[(j + 0) * stride];
-    a1 += w[j + 1] * po[(j + 1) * stride];
-    a2 += w[j + 2] * po[(j + 2) * stride];
-    a3 += w[j + 3] * po[(j + 3) * stride];
-  }
-  for (; j < s; ++j) a0 += w[j] * po[j * stride];
-  return ((a0 + a1) + (a2 + a3)) * inv;
+// Loads of partials: COHERENT reads at device scope (past this XCD's L2),
+// for partials that other work-groups of the same launch have just written.
+template <bool COHERENT>
+__device__ inline float ld_part(const float* p) {
+  if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
 }
 
 __device__ inline uint16_t f32_to_bf16_rne(float x) {
@@ -59,6 +37,72 @@ __device__ inline void store_out(void* out, int dt, int64_t idx, float o, float 
   if (dt == KVQ_F32) static_cast<float*>(out)[idx] = o;
   else if (dt == KVQ_BF16) static_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(o);
   else static_cast<uint8_t*>(out)[idx] = f32_to_e4m3_sat(o / osc);
+}
+
+// Wave-wide split weights (s <= 64): lane j < s returns w_j = exp(lse_j - M)
+// (0 for the other lanes); every lane receives 1/sum_j w_j in inv and the
+// merged LSE in lse_m.  Must be called by a whole wave.
+template <bool COHERENT>
+__device__ inline float wave_split_weight(const float* lse, int s, float& inv, float& lse_m) {
+  const int lane = threadIdx.x & 63;
+  const float lj = lane < s ? ld_part<COHERENT>(lse + lane) : -INFINITY;
+  float M = lj;
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
+  const float wj = (M == -INFINITY || lj == -INFINITY) ? 0.0f : __expf(lj - M);
+  float sum = wj;
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) sum += __shfl_xor(sum, x);
+  inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+  lse_m = sum > 0.0f ? M + __logf(sum) : -INFINITY;
+  return wj;
+}
+
+// Merge of one (request, head) by one wave: po = its partials [s][Dv],
+// out element i of the head = out[oidx + i].  The partial loads of the
+// lane's columns (lane, lane + 64) for all s splits are issued before the
+// weights are computed, so the merge costs one memory round trip per 128
+// columns (64 when s > 32).  Splits j >= s read split s - 1 and get weight 0 (lane j's
+// weight), which leaves every sum unchanged, so N (16, 32 or 64) does not
+// change the result.  Four accumulators (j mod 4).  (For N = 64 one column
+// per pass.)
+template <bool COHERENT, int N>
+__device__ inline void combine_head_n(const float* lse, const float* po, int s, int Dv, void* out, int dt,
+                                      int64_t oidx, float osc, float* lse_out) {
+  constexpr int C = N <= 32 ? 2 : 1;   // columns per lane per pass (at most 64 loads in flight)
+  const int lane = threadIdx.x & 63;
+  float inv = 0.0f, lse_m = -INFINITY, w = 0.0f;
+  for (int d0 = 0; d0 < Dv; d0 += 64 * C) {
+    float v[C][N];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int d = d0 + lane + 64 * c;
+      if (d < Dv) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) v[c][j] = ld_part<COHERENT>(po + static_cast<int64_t>(j < s ? j : s - 1) * Dv + d);
+      }
+    }
+    if (d0 == 0) w = wave_split_weight<COHERENT>(lse, s, inv, lse_m);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int d = d0 + lane + 64 * c;
+      if (d < Dv) {
+        float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < N; ++j) a[j & 3] += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j)) * v[c][j];
+        store_out(out, dt, oidx + d, ((a[0] + a[1]) + (a[2] + a[3])) * inv, osc);
+      }
+    }
+  }
+  if (lane == 0 && lse_out != nullptr) *lse_out = lse_m;
+}
+
+template <bool COHERENT>
+__device__ inline void combine_head(const float* lse, const float* po, int s, int Dv, void* out, int dt, int64_t oidx,
+                                    float osc, float* lse_out) {
+  if (s <= 16) combine_head_n<COHERENT, 16>(lse, po, s, Dv, out, dt, oidx, osc, lse_out);
+  else if (s <= 32) combine_head_n<COHERENT, 32>(lse, po, s, Dv, out, dt, oidx, osc, lse_out);
+  else combine_head_n<COHERENT, 64>(lse, po, s, Dv, out, dt, oidx, osc, lse_out);
 }
 
 }  // namespace kvq

@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "combine_impl.h"
 #include "kvq_internal.h"
 
@@ -204,12 +206,21 @@ struct FusedOut {
 // QF32 fp32 queries (hi/lo split), PSPLIT 2 = P carried as f16 hi + lo,
 // FUSED: the last work-group of each (request, kv head) merges the partials
 // and writes the final output (one launch per decode step).
+// Work-groups per CU the register allocation is sized for: 4 (16 waves per
+// CU) where the tile state fits in 128 VGPRs, fewer for the wide-tile
+// (G <= 2) and fp32-query variants.
+template <int KVF, int G, bool QF32, int VL>
+constexpr int decode_min_blocks() {
+  return (16 / G > 4) ? 2 : ((QF32 || KVF != KVQ_NVFP4) ? 2 : 2);
+}
+
 template <int KVF, int G, int D, bool QF32, int PSPLIT, bool FUSED, int VL>
-__global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, int num_splits, FusedOut fo) {
+__global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>())) k_decode_gqa(kvq_decode_args a, int num_splits, FusedOut fo) {
   using Gm = Geo<KVF, D>;
   constexpr int NSUB = 16 / G;                  // row groups in the 16 MFMA columns
   constexpr int NT = NSUB < 2 ? 2 : NSUB;       // sub-tiles (16 tokens) per tile
   constexpr int NACC = NT / NSUB;               // score accumulators per tile
+  constexpr int NG = NT <= 4 ? 4 : 1;           // tiles per softmax group
   constexpr int TT = 16 * NT;                   // tokens per tile
   constexpr int NQ = QF32 ? 2 : 1;
   using KT = KTile<KVF, D, NT>;
@@ -218,6 +229,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
   __shared__ float lds_o[kWaves][16][D];
   __shared__ float lds_m[kWaves][16];
   __shared__ float lds_l[kWaves][16];
+  __shared__ float lds_w[kWaves][16];   // merge weights
+  __shared__ float lds_lse[16];         // merged lse per head
   __shared__ int lds_last;
 
   const int lane = threadIdx.x & 63;
@@ -256,19 +269,37 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
     // ---- query operand: lane (g, c) holds Q[h = c % G][g*QKE + 8j + e]
     f16x8 qop[NQ][Gm::kQkJ];
     {
-      const int64_t qb = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(hq0 + my_h) * a.q_sh;
+      // 16-byte vector loads (q rows and strides are 16-byte aligned)
+      const int64_t qb = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(hq0 + my_h) * a.q_sh +
+                         g * Gm::kQkElems;
 #pragma unroll
       for (int j = 0; j < Gm::kQkJ; ++j) {
+        float x[8];
+        if constexpr (QF32) {
+          const float* qp = static_cast<const float*>(a.q) + qb + 8 * j;
+          const float4 x0 = *reinterpret_cast<const float4*>(qp);
+          const float4 x1 = *reinterpret_cast<const float4*>(qp + 4);
+          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+          x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+        } else {
+          const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qb + 8 * j);
+          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = g * Gm::kQkElems + 8 * j + e;
-          float x;
-          if constexpr (QF32) x = static_cast<const float*>(a.q)[qb + d];
-          else x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[qb + d]) << 16);
-          const _Float16 hi = static_cast<_Float16>(x);
-          qop[0][j][e] = hi;
-          if constexpr (QF32) qop[1][j][e] = static_cast<_Float16>(x - static_cast<float>(hi));
+          for (int k = 0; k < 4; ++k) {   // bf16 pair -> two fp32 (exact)
+            x[2 * k] = __uint_as_float(ws[k] << 16);
+            x[2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
+          }
         }
+        f16x2 hi[4], lo[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          hi[k] = f16x2{static_cast<_Float16>(x[2 * k]), static_cast<_Float16>(x[2 * k + 1])};
+          if constexpr (QF32)
+            lo[k] = f16x2{static_cast<_Float16>(x[2 * k] - static_cast<float>(hi[k][0])),
+                          static_cast<_Float16>(x[2 * k + 1] - static_cast<float>(hi[k][1]))};
+        }
+        qop[0][j] = cat4(hi[0], hi[1], hi[2], hi[3]);
+        if constexpr (QF32) qop[1][j] = cat4(lo[0], lo[1], lo[2], lo[3]);
       }
     }
 
@@ -299,15 +330,20 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
     const int lvt = g * GB + c * CB;
     const int lvts = g * GS + (c / 2) * 4;
 
+    // (the lane offsets are re-materialized per call, so that the constant
+    // parts fold into the loads' immediate offsets instead of occupying
+    // loop-invariant registers)
+    auto opaque = [](int x) { asm volatile("" : "+v"(x)); return x; };
     auto load_ktile = [&](KT& R, int tile) {
       const int tb = cs + tile * TT;
+      const int lk_ = opaque(lk), lks_ = opaque(lks);
       const int nv = ce - tb;
       const int64_t base = static_cast<int64_t>(tb) * st;
       const Rsrc rk = make_rsrc(kc + base * RB, nv * st * RB);
       const Rsrc rks = make_rsrc(ksc + base * SB, nv * st * SB);
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
-        const int o = lk + u * 16 * st * RB;
+        const int o = lk_ + u * 16 * st * RB;
         if constexpr (Gm::kKWords == 8) {
           const u32x4 x0 = ld128(rk, o), x1 = ld128(rk, o + 16);
 #pragma unroll
@@ -321,13 +357,14 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
           R.k[u][0] = x0[0]; R.k[u][1] = x0[1];
         }
         if constexpr (KVF == KVQ_NVFP4) {
-          const int os = lks + u * 16 * st * SB;
+          const int os = lks_ + u * 16 * st * SB;
           R.ks[u] = (D == 128) ? ld16(rks, os) : ld8(rks, os);
         }
       }
     };
     auto load_vtile = [&](VT& R, int tile) {
       const int tb = cs + tile * TT;
+      const int lvt_ = opaque(lvt), lvts_ = opaque(lvts), lv_ = opaque(lv), lvs_ = opaque(lvs);
       const int nv = ce - tb;
       if constexpr (VL == KVQ_PLANE_TOKEN4) {
         // Group 4u+g of the tile (lane group g): for this lane's elements
@@ -340,7 +377,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
         const Rsrc rvs = make_rsrc(vsc + static_cast<int64_t>(tb) * SB, ng * GS);
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
-          const int o = lvt + u * 4 * GB;
+          const int o = lvt_ + u * 4 * GB;
           const u32x4 x0 = ld128(rv, o);
 #pragma unroll
           for (int w = 0; w < 4; ++w) R.t4[u][w] = x0[w];
@@ -349,7 +386,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
 #pragma unroll
             for (int w = 0; w < 4; ++w) R.t4[u][4 + w] = x1[w];
           }
-          if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] = ld32(rvs, lvts + u * 4 * GS);
+          if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] = ld32(rvs, lvts_ + u * 4 * GS);
         }
       } else {
         const int64_t base = static_cast<int64_t>(tb) * st;
@@ -359,7 +396,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
         for (int u = 0; u < NT; ++u) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int o = lv + (16 * u + i) * st * RB;
+            const int o = lv_ + (16 * u + i) * st * RB;
             if constexpr (Gm::kVBytes == 8) {
               const u32x2 x = ld64(rv, o);
               R.v[u][i][0] = x[0]; R.v[u][i][1] = x[1];
@@ -368,7 +405,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
             } else {
               R.v[u][i][0] = ld16(rv, o);
             }
-            if constexpr (KVF == KVQ_NVFP4) R.vs[u][i] = ld8(rvs, lvs + (16 * u + i) * st * SB);
+            if constexpr (KVF == KVQ_NVFP4) R.vs[u][i] = ld8(rvs, lvs_ + (16 * u + i) * st * SB);
           }
         }
       }
@@ -399,13 +436,14 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
       }
     };
 
-    auto qk_tile = [&](const KT& R, int tile, f16x2 (&p_hi)[NACC][2], f16x2 (&p_lo)[NACC][2]) {
+    // Scores of one tile for this lane's row c (log2 domain; tokens past ce
+    // are -inf).  Every sub-tile u is multiplied by the full (unmasked)
+    // query operand into its own accumulator; lane column c then keeps the
+    // sub-tile of its row group (u % NSUB == c / G): the block-diagonal
+    // selection costs one select per score instead of a masked operand per
+    // MFMA.
+    auto qk_scores = [&](const KT& R, int tile, float (&sc)[NACC][4]) {
       const int tb = cs + tile * TT;
-      // ---------------- scores.  Every sub-tile u is multiplied by the full
-      // (unmasked) query operand into its own accumulator; lane column c
-      // then keeps the sub-tile of its row group (u % NSUB == c / G): the
-      // block-diagonal selection costs one select per score instead of a
-      // masked operand per MFMA.
       f32x4 acc_u[NT];
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
@@ -417,36 +455,48 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
           for (int qq = 0; qq < NQ; ++qq) acc_u[u] = mfma(kop, qop[qq][j], acc_u[u]);
         }
       }
-      f32x4 acc_s[NACC];
 #pragma unroll
       for (int x = 0; x < NACC; ++x) {
-        acc_s[x] = acc_u[x * NSUB];
+        f32x4 acc_s = acc_u[x * NSUB];
 #pragma unroll
         for (int r = 1; r < NSUB; ++r) {
           const bool pick = (my_sub == r);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc_s[x][i] = pick ? acc_u[x * NSUB + r][i] : acc_s[x][i];
+          for (int i = 0; i < 4; ++i) acc_s[i] = pick ? acc_u[x * NSUB + r][i] : acc_s[i];
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[x][i] = acc_s[i] * qk_scale;
       }
-      // ---------------- online softmax per row c (this lane: 4*NACC tokens)
-      const bool full_tile = (tb + TT <= ce);
-      float sc[NACC][4];
+      if (tb + TT > ce) {   // the chunk's last, partial tile (uniform branch)
+#pragma unroll
+        for (int x = 0; x < NACC; ++x)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tb + 16 * (x * NSUB + my_sub) + 4 * g + i >= ce) sc[x][i] = -INFINITY;
+      }
+    };
+
+    // Online softmax over a group of n tiles at once: one row maximum, at
+    // most one rescale of the accumulators per group, then the
+    // probabilities of every tile of the group (f16, hi + lo parts when
+    // PSPLIT == 2).  The reference is the running maximum itself, so the
+    // dominant probability of a peaked row is exactly 1 in f16.
+    auto softmax_group = [&](const float (&sc)[NG][NACC][4], int n, f16x2 (&ph)[NG][NACC][2],
+                             f16x2 (&pl)[NG][NACC][2]) {
       float tmax = -INFINITY;
 #pragma unroll
-      for (int x = 0; x < NACC; ++x) {
+      for (int t = 0; t < NG; ++t)
+        if (t < n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = tb + 16 * (x * NSUB + my_sub) + 4 * g + i;
-          const float v = (full_tile || t < ce) ? acc_s[x][i] * qk_scale : -INFINITY;
-          sc[x][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      }
+          for (int x = 0; x < NACC; ++x)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[t][x][i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      if (__any(m_new > m_run)) {
-        const float fac = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+      const bool bump = tmax > m_run;
+      if (__any(bump)) {
+        const float m_new = bump ? tmax : m_run;
+        const float fac = bump ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;   // 0 when m_run = -inf
         l_run *= fac;
         float fr[4];
 #pragma unroll
@@ -458,22 +508,28 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
         }
         m_run = m_new;
       }
+      const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;  // rows with no valid token yet
 #pragma unroll
-      for (int x = 0; x < NACC; ++x) {
-        float p[4];
+      for (int t = 0; t < NG; ++t) {
+        if (t < n) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = (sc[x][i] == -INFINITY) ? 0.0f : exp2f(sc[x][i] - m_run);
-          l_run += p[i];
-        }
+          for (int x = 0; x < NACC; ++x) {
+            float p[4];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const _Float16 h0 = static_cast<_Float16>(p[2 * k]);
-          const _Float16 h1 = static_cast<_Float16>(p[2 * k + 1]);
-          p_hi[x][k] = f16x2{h0, h1};
-          if constexpr (PSPLIT == 2)
-            p_lo[x][k] = f16x2{static_cast<_Float16>(p[2 * k] - static_cast<float>(h0)),
-                               static_cast<_Float16>(p[2 * k + 1] - static_cast<float>(h1))};
+            for (int i = 0; i < 4; ++i) {
+              p[i] = __builtin_amdgcn_exp2f(sc[t][x][i] - m_ref);   // masked scores: exp2(-inf) = 0
+              l_run += p[i];
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              const _Float16 h0 = static_cast<_Float16>(p[2 * k]);
+              const _Float16 h1 = static_cast<_Float16>(p[2 * k + 1]);
+              ph[t][x][k] = f16x2{h0, h1};
+              if constexpr (PSPLIT == 2)
+                pl[t][x][k] = f16x2{static_cast<_Float16>(p[2 * k] - static_cast<float>(h0)),
+                                    static_cast<_Float16>(p[2 * k + 1] - static_cast<float>(h1))};
+            }
+          }
         }
       }
     };
@@ -603,45 +659,59 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
     // scores are computed, and its V while this tile's P.V runs, so every
     // load has a full tile of compute to hide behind.  (Narrow query groups
     // have 8-16 sub-tiles per tile and use one register set.)
-    f16x2 p_hi[NACC][2], p_lo[NACC][2];
-    if constexpr (NT <= 4) {
-      // loads past the wave's last tile are empty (size-0 resources)
-      KT KA, KB;
-      VT VA, VB;
-      // (scheduling barriers keep each prefetch ahead of the compute that
-      // follows it, so a full tile of work hides every load)
-      int tile = wave;
-      load_ktile(KA, tile);
-      load_vtile(VA, tile);
-      while (true) {
-        load_ktile(KB, tile + kWaves);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_tile(KA, tile, p_hi, p_lo);
-        load_vtile(VB, tile + kWaves);
-        __builtin_amdgcn_sched_barrier(0);
-        mask_vtile(VA, tile);
-        pv_tile(VA, p_hi, p_lo);
-        tile += kWaves;
-        if (tile >= ntiles) break;
-        load_ktile(KA, tile + kWaves);
-        __builtin_amdgcn_sched_barrier(0);
-        qk_tile(KB, tile, p_hi, p_lo);
-        load_vtile(VA, tile + kWaves);
-        __builtin_amdgcn_sched_barrier(0);
-        mask_vtile(VB, tile);
-        pv_tile(VB, p_hi, p_lo);
-        tile += kWaves;
-        if (tile >= ntiles) break;
+    // Tile loop.  The wave's tiles (wave, wave + 4, ...) are taken in groups
+    // of NG: phase 1 computes the scores of every tile of the group, one
+    // softmax step handles the whole group, phase 2 runs P.V.  Operands
+    // stream through two register sets per kind (K in phase 1, V in phase
+    // 2): the load of the next operand is issued before the current one is
+    // used, so every load has one tile of compute to hide behind, and the
+    // K and V sets are never live at the same time except at the phase
+    // boundaries.  Loads past the wave's last tile are empty.
+    const int nw = (ntiles - wave + kWaves - 1) / kWaves;   // this wave's tiles
+    auto tile_of = [&](int k) { return wave + k * kWaves; };
+    KT KA, KB;
+    VT VA, VB;
+    auto group = [&](int k0, int n, auto full) {
+      constexpr bool kFull = decltype(full)::value;
+      float sc[NG][NACC][4];
+      f16x2 ph[NG][NACC][2], pl[NG][NACC][2];
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        if (kFull || i < n) {
+          if (kFull ? (i + 1 < NG) : (i + 1 < n)) load_ktile((i & 1) ? KA : KB, tile_of(k0 + i + 1));
+          else load_vtile(VA, tile_of(k0));
+          __builtin_amdgcn_sched_barrier(0);
+          qk_scores((i & 1) ? KB : KA, tile_of(k0 + i), sc[i]);
+        }
       }
+      softmax_group(sc, kFull ? NG : n, ph, pl);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        if (kFull || i < n) {
+          if (kFull ? (i + 1 < NG) : (i + 1 < n)) load_vtile((i & 1) ? VA : VB, tile_of(k0 + i + 1));
+          else load_ktile(KA, tile_of(k0 + NG));   // first tile of the next group
+          __builtin_amdgcn_sched_barrier(0);
+          mask_vtile((i & 1) ? VB : VA, tile_of(k0 + i));
+          pv_tile((i & 1) ? VB : VA, ph[i], pl[i]);
+        }
+      }
+    };
+    if constexpr (NG > 1) {
+      load_ktile(KA, tile_of(0));
+      int k0 = 0;
+      for (; k0 + NG <= nw; k0 += NG) group(k0, NG, std::integral_constant<bool, true>{});
+      if (k0 < nw) group(k0, nw - k0, std::integral_constant<bool, false>{});
     } else {
-      KT KA;
-      VT VA;
-      for (int tile = wave; tile < ntiles; tile += kWaves) {
-        load_ktile(KA, tile);
-        load_vtile(VA, tile);
-        qk_tile(KA, tile, p_hi, p_lo);
-        mask_vtile(VA, tile);
-        pv_tile(VA, p_hi, p_lo);
+      // wide tiles (8-16 sub-tiles): one register set, no cross-tile prefetch
+      for (int k = 0; k < nw; ++k) {
+        float sc[1][NACC][4];
+        f16x2 ph[1][NACC][2], pl[1][NACC][2];
+        load_ktile(KA, tile_of(k));
+        load_vtile(VA, tile_of(k));
+        qk_scores(KA, tile_of(k), sc[0]);
+        softmax_group(sc, 1, ph, pl);
+        mask_vtile(VA, tile_of(k));
+        pv_tile(VA, ph[0], pl[0]);
       }
     }
   }
@@ -660,71 +730,77 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_gqa(kvq_decode_args a, i
   }
   __syncthreads();
 
-  // ---------------- merge rows (wave, sub) of each head
+  // ---------------- merge rows (wave, sub) of each head.  Wave 0 turns
+  // the 64 (wave, row) maxima into merge weights, one lane per row: row r
+  // of wave w belongs to head r % G, so the lanes of one head are those
+  // with equal lane % G, and butterfly shuffles over the other lane bits
+  // give the head's maximum and merged denominator.  The weights include
+  // the division by that denominator.
+  if (wave == 0) {
+    const int w = lane >> 4, r = lane & 15;
+    const float mv = lds_m[w][r];
+    float M = mv;
+#pragma unroll
+    for (int x = G; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
+    const float f = (mv == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+    float den = f * lds_l[w][r];
+#pragma unroll
+    for (int x = G; x < 64; x <<= 1) den += __shfl_xor(den, x);
+    lds_w[w][r] = den > 0.0f ? f / den : 0.0f;
+    if (lane < G) lds_lse[lane] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
   const bool direct = FUSED && num_splits == 1;   // no partials needed
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, d = idx % D;
-    float M = -INFINITY;
+    float num = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) M = fmaxf(M, lds_m[w][s * G + h]);
-    float num = 0.0f, den = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          const float mv = lds_m[w][s * G + h];
-          const float f = (mv == -INFINITY) ? 0.0f : exp2f(mv - M);
-          num += f * lds_o[w][s * G + h][d];
-          den += f * lds_l[w][s * G + h];
-        }
-    }
-    const float o = den > 0.0f ? (num / den) * vscale : 0.0f;
-    const float lse = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+      for (int s = 0; s < NSUB; ++s) num += lds_w[w][s * G + h] * lds_o[w][s * G + h][d];
+    const float o = num * vscale;
+    const float lse = lds_lse[h];
     const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + h;
     if (direct) {
       store_out(fo.out, fo.out_dtype, bh * D + d, o, fo.out_dtype == KVQ_FP8E4M3 ? *fo.out_scale : 1.0f);
       if (d == 0 && fo.lse_out != nullptr) fo.lse_out[bh] = lse;
     } else {
       const int64_t po = bh * num_splits + split;
-      a.part_o[po * D + d] = o;
-      if (d == 0) a.part_lse[po] = lse;
+      if constexpr (FUSED) {   // device-scope stores: read back by another work-group
+        __hip_atomic_store(a.part_o + po * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) __hip_atomic_store(a.part_lse + po, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        a.part_o[po * D + d] = o;
+        if (d == 0) a.part_lse[po] = lse;
+      }
     }
   }
   if constexpr (!FUSED) return;
   if (direct) return;
 
   // ---------------- fused combine: the last work-group of (b, kv head) to
-  // finish merges the num_splits partials of its G heads
-  __threadfence();   // partials visible device-wide before the count
+  // finish merges the num_splits partials of its G heads.  The partials
+  // were stored at device scope; waiting for those stores to complete
+  // before the counter increment orders them before it (no cache
+  // write-back fence is needed), and the last work-group reads them at
+  // device scope.
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
     int* ctr = fo.counters + static_cast<int64_t>(b) * a.Hkv + kvh;
-    const int prev = atomicAdd(ctr, 1);
+    const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = (prev == num_splits - 1);
-    if (last) *ctr = 0;   // reset for the next call
+    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
     lds_last = last;
   }
   __syncthreads();
   if (!lds_last) return;
-  __threadfence();   // acquire: see every other work-group's partials
   const float osc = (fo.out_dtype == KVQ_FP8E4M3) ? *fo.out_scale : 1.0f;
-  // lds_o is free now: stage the split weights there
-  float* w_s = &lds_o[0][0][0];            // [G][num_splits] weights
-  float* inv_s = &lds_o[1][0][0];          // [G] 1/sum, [G] merged lse
-  for (int idx = threadIdx.x; idx < G; idx += kThreads) {
-    const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + idx;
-    split_weights(a.part_lse + bh * num_splits, num_splits, w_s + idx * num_splits, inv_s[idx], inv_s[G + idx]);
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int h = idx / D, d = idx % D;
+  // one head per wave (the routine of the standalone combine kernel)
+  for (int h = wave; h < G; h += kWaves) {
     const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + h;
-    const float o = combine_column(a.part_o + bh * num_splits * D + d, D, w_s + h * num_splits, num_splits, inv_s[h]);
-    store_out(fo.out, fo.out_dtype, bh * D + d, o, osc);
-    if (d == 0 && fo.lse_out != nullptr) fo.lse_out[bh] = inv_s[G + h];
+    combine_head<true>(a.part_lse + bh * num_splits, a.part_o + bh * num_splits * D, num_splits, D, fo.out,
+                       fo.out_dtype, bh * D, osc, fo.lse_out != nullptr ? fo.lse_out + bh : nullptr);
   }
 }
 

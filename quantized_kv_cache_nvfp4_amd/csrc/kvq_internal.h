@@ -15,14 +15,34 @@ struct Rows {
 
 inline Rows to_rows(const kvq_rows& r) { return Rows{r.n0, r.n1, r.n2, r.s0, r.s1, r.s2}; }
 
+// One plane pack: source rows x (dt, xr, d) quantized with the calibrated
+// amax into the destination plane (codes, NVFP4 scales, dr, layout) at
+// rows + dst_pos[i0]; sout receives the tensor scale (or is null).
+struct PackJob {
+  const void* x;
+  int dt;
+  Rows xr;
+  int d;
+  const float* amax;
+  uint8_t* codes;
+  uint8_t* scales;
+  Rows dr;
+  int layout;
+  const int32_t* dst_pos;
+  float* sout;
+};
+constexpr int kMaxPackJobs = KVQ_MAX_PACK_JOBS;
+struct PackJobs {
+  PackJob j[kMaxPackJobs];
+  int n;
+};
+
 // ---- quantization kernels (quant_kernels.hip) ----
 hipError_t launch_amax(const void* x, int x_dtype, Rows rows, int d, const int32_t* kv_lens, float* amax_out,
                        bool accumulate, hipStream_t st);
-hipError_t launch_pack_nvfp4(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes,
-                             uint8_t* scales, Rows dr, int layout, const int32_t* dst_pos, float* ts_out,
-                             hipStream_t st);
-hipError_t launch_pack_fp8(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes, Rows dr,
-                           int layout, const int32_t* dst_pos, float* scale_out, hipStream_t st);
+// every job of one call in one launch (blockIdx.y = job)
+hipError_t launch_pack_nvfp4(const PackJobs& jobs, hipStream_t st);
+hipError_t launch_pack_fp8(const PackJobs& jobs, hipStream_t st);
 hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, Rows sr, int layout, int d, const float* ts,
                                float* out, Rows orow, hipStream_t st);
 hipError_t launch_unpack_fp8(const uint8_t* codes, Rows sr, int layout, int d, const float* scale, float* out, Rows orow,

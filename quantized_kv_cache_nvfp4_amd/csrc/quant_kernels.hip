@@ -153,26 +153,22 @@ __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, i
 
 // ---------------------------------------------------------------- NVFP4 pack
 // ROWS layout: one thread per 16-element block -> 8 code bytes, 1 scale byte
-__global__ void __launch_bounds__(kThreads) k_pack_nvfp4(const void* __restrict__ x, int dt, Rows xr, int d,
-                                                         const float* __restrict__ amax, uint8_t* __restrict__ codes,
-                                                         uint8_t* __restrict__ scales, Rows dr,
-                                                         const int32_t* __restrict__ dst_pos, float* ts_out) {
-  const float s_t = nvfp4_tensor_scale(*amax);
+__device__ inline void pack_nvfp4_rows(const PackJob& J, float s_t, int64_t gid, int64_t stride) {
+  const int d = J.d;
   const int nb = d / 16;
+  const Rows xr = J.xr, dr = J.dr;
   const int64_t total = xr.n0 * xr.n1 * xr.n2 * nb;
-  int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
-  if (gid == 0 && ts_out != nullptr) *ts_out = s_t;
-  for (; gid < total; gid += static_cast<int64_t>(gridDim.x) * kThreads) {
+  for (; gid < total; gid += stride) {
     int64_t row = gid / nb;
     int blk = static_cast<int>(gid - row * nb);
     int64_t i0, i1, i2;
     unravel(row, xr, i0, i1, i2);
-    const int64_t di2 = i2 + (dst_pos != nullptr ? dst_pos[i0] : 0);
+    const int64_t di2 = i2 + (J.dst_pos != nullptr ? J.dst_pos[i0] : 0);
     if (di2 < 0 || di2 >= dr.n2) continue;  // outside the destination plane
     const int64_t xo = row_off(xr, i0, i1, i2) + blk * 16;
     float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = load_elem(x, dt, xo + i);
+    for (int i = 0; i < 16; ++i) v[i] = load_elem(J.x, J.dt, xo + i);
     uint32_t c[16];
     const uint32_t sc = encode_nvfp4_block(v, s_t, c);
     uint32_t lo = 0, hi = 0;
@@ -182,8 +178,8 @@ __global__ void __launch_bounds__(kThreads) k_pack_nvfp4(const void* __restrict_
       hi |= c[8 + i] << (4 * i);
     }
     const int64_t drow = row_off(dr, i0, i1, di2);
-    *reinterpret_cast<uint2*>(codes + drow * (d / 2) + blk * 8) = make_uint2(lo, hi);
-    scales[drow * nb + blk] = static_cast<uint8_t>(sc);
+    *reinterpret_cast<uint2*>(J.codes + drow * (d / 2) + blk * 8) = make_uint2(lo, hi);
+    J.scales[drow * nb + blk] = static_cast<uint8_t>(sc);
   }
 }
 
@@ -213,28 +209,23 @@ __device__ inline bool t4_group(const Rows& xr, const Rows& dr, const int32_t* d
 // TOKEN4 layout: one thread per (4-token group, 16-element block): 32 code
 // bytes (two 16-byte stores) and one 4-byte scale word; tokens of the group
 // that this call does not write keep their bytes.
-__global__ void __launch_bounds__(kThreads) k_pack_nvfp4_t4(const void* __restrict__ x, int dt, Rows xr, int d,
-                                                            const float* __restrict__ amax,
-                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                            Rows dr, const int32_t* __restrict__ dst_pos,
-                                                            float* ts_out) {
-  const float s_t = nvfp4_tensor_scale(*amax);
+__device__ inline void pack_nvfp4_t4(const PackJob& J, float s_t, int64_t gid, int64_t stride) {
+  const int d = J.d;
   const int nb = d / 16;
+  const Rows xr = J.xr, dr = J.dr;
   const int64_t slots = t4_slots(xr.n2);
   const int64_t total = xr.n0 * xr.n1 * slots * nb;
-  int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
-  if (gid == 0 && ts_out != nullptr) *ts_out = s_t;
-  for (; gid < total; gid += static_cast<int64_t>(gridDim.x) * kThreads) {
+  for (; gid < total; gid += stride) {
     const int blk = static_cast<int>(gid % nb);
     int64_t rest = gid / nb;
     const int64_t gl = rest % slots;
     rest /= slots;
     const int64_t i1 = rest % xr.n1, i0 = rest / xr.n1;
     int64_t t0, src[4];
-    if (!t4_group(xr, dr, dst_pos, i0, gl, t0, src)) continue;
+    if (!t4_group(xr, dr, J.dst_pos, i0, gl, t0, src)) continue;
     const int64_t grow = group_row(dr, i0, i1, t0);
-    uint4* cp = reinterpret_cast<uint4*>(codes + grow * (d / 2) + blk * 32);
-    uint32_t* sp = reinterpret_cast<uint32_t*>(scales + grow * nb + blk * 4);
+    uint4* cp = reinterpret_cast<uint4*>(J.codes + grow * (d / 2) + blk * 32);
+    uint32_t* sp = reinterpret_cast<uint32_t*>(J.scales + grow * nb + blk * 4);
     const bool partial = src[0] < 0 || src[1] < 0 || src[2] < 0 || src[3] < 0;
     uint4 w0 = partial ? cp[0] : make_uint4(0, 0, 0, 0);
     uint4 w1 = partial ? cp[1] : make_uint4(0, 0, 0, 0);
@@ -246,7 +237,7 @@ __global__ void __launch_bounds__(kThreads) k_pack_nvfp4_t4(const void* __restri
       const int64_t xo = row_off(xr, i0, i1, src[j]) + blk * 16;
       float v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = load_elem(x, dt, xo + i);
+      for (int i = 0; i < 16; ++i) v[i] = load_elem(J.x, J.dt, xo + i);
       uint32_t c[16];
       const uint32_t sc = encode_nvfp4_block(v, s_t, c);
       sw = (sw & ~(0xFFu << (8 * j))) | (sc << (8 * j));
@@ -263,53 +254,54 @@ __global__ void __launch_bounds__(kThreads) k_pack_nvfp4_t4(const void* __restri
   }
 }
 
+__global__ void __launch_bounds__(kThreads) k_pack_nvfp4(PackJobs P) {
+  const PackJob& J = P.j[blockIdx.y];
+  const float s_t = nvfp4_tensor_scale(*J.amax);
+  const int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
+  if (gid == 0 && J.sout != nullptr) *J.sout = s_t;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  if (J.layout == KVQ_PLANE_TOKEN4) pack_nvfp4_t4(J, s_t, gid, stride);
+  else pack_nvfp4_rows(J, s_t, gid, stride);
+}
+
 // ---------------------------------------------------------------- FP8 pack
 // ROWS layout: one thread per 4 elements (one 32-bit code word)
-__global__ void __launch_bounds__(kThreads) k_pack_fp8(const void* __restrict__ x, int dt, Rows xr, int d,
-                                                       const float* __restrict__ amax, uint8_t* __restrict__ codes,
-                                                       Rows dr, const int32_t* __restrict__ dst_pos, float* sc_out) {
-  const float scale = fp8_tensor_scale(*amax);
-  const double dscale = static_cast<double>(scale);
+__device__ inline void pack_fp8_rows(const PackJob& J, double dscale, int64_t gid, int64_t stride) {
+  const int d = J.d;
   const int nw = d / 4;
+  const Rows xr = J.xr, dr = J.dr;
   const int64_t total = xr.n0 * xr.n1 * xr.n2 * nw;
-  int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
-  if (gid == 0 && sc_out != nullptr) *sc_out = scale;
-  for (; gid < total; gid += static_cast<int64_t>(gridDim.x) * kThreads) {
+  for (; gid < total; gid += stride) {
     int64_t row = gid / nw;
     int w = static_cast<int>(gid - row * nw);
     int64_t i0, i1, i2;
     unravel(row, xr, i0, i1, i2);
-    const int64_t di2 = i2 + (dst_pos != nullptr ? dst_pos[i0] : 0);
+    const int64_t di2 = i2 + (J.dst_pos != nullptr ? J.dst_pos[i0] : 0);
     if (di2 < 0 || di2 >= dr.n2) continue;  // outside the destination plane
     const int64_t xo = row_off(xr, i0, i1, i2) + w * 4;
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) word |= encode_fp8(load_elem(x, dt, xo + i), dscale) << (8 * i);
-    *reinterpret_cast<uint32_t*>(codes + row_off(dr, i0, i1, di2) * d + w * 4) = word;
+    for (int i = 0; i < 4; ++i) word |= encode_fp8(load_elem(J.x, J.dt, xo + i), dscale) << (8 * i);
+    *reinterpret_cast<uint32_t*>(J.codes + row_off(dr, i0, i1, di2) * d + w * 4) = word;
   }
 }
 
 // TOKEN4 layout: one thread per (4-token group, 4 elements): 16 code bytes
-__global__ void __launch_bounds__(kThreads) k_pack_fp8_t4(const void* __restrict__ x, int dt, Rows xr, int d,
-                                                          const float* __restrict__ amax, uint8_t* __restrict__ codes,
-                                                          Rows dr, const int32_t* __restrict__ dst_pos,
-                                                          float* sc_out) {
-  const float scale = fp8_tensor_scale(*amax);
-  const double dscale = static_cast<double>(scale);
+__device__ inline void pack_fp8_t4(const PackJob& J, double dscale, int64_t gid, int64_t stride) {
+  const int d = J.d;
   const int nw = d / 4;
+  const Rows xr = J.xr, dr = J.dr;
   const int64_t slots = t4_slots(xr.n2);
   const int64_t total = xr.n0 * xr.n1 * slots * nw;
-  int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
-  if (gid == 0 && sc_out != nullptr) *sc_out = scale;
-  for (; gid < total; gid += static_cast<int64_t>(gridDim.x) * kThreads) {
+  for (; gid < total; gid += stride) {
     const int w = static_cast<int>(gid % nw);
     int64_t rest = gid / nw;
     const int64_t gl = rest % slots;
     rest /= slots;
     const int64_t i1 = rest % xr.n1, i0 = rest / xr.n1;
     int64_t t0, src[4];
-    if (!t4_group(xr, dr, dst_pos, i0, gl, t0, src)) continue;
-    uint4* cp = reinterpret_cast<uint4*>(codes + group_row(dr, i0, i1, t0) * d + w * 16);
+    if (!t4_group(xr, dr, J.dst_pos, i0, gl, t0, src)) continue;
+    uint4* cp = reinterpret_cast<uint4*>(J.codes + group_row(dr, i0, i1, t0) * d + w * 16);
     const bool partial = src[0] < 0 || src[1] < 0 || src[2] < 0 || src[3] < 0;
     uint4 wv = partial ? *cp : make_uint4(0, 0, 0, 0);
     uint32_t* wd[4] = {&wv.x, &wv.y, &wv.z, &wv.w};
@@ -319,10 +311,20 @@ __global__ void __launch_bounds__(kThreads) k_pack_fp8_t4(const void* __restrict
       const int64_t xo = row_off(xr, i0, i1, src[j]) + w * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i)  // element 4w + i of token j: byte 4 (4w + i) + j
-        *wd[i] = (*wd[i] & ~(0xFFu << (8 * j))) | (encode_fp8(load_elem(x, dt, xo + i), dscale) << (8 * j));
+        *wd[i] = (*wd[i] & ~(0xFFu << (8 * j))) | (encode_fp8(load_elem(J.x, J.dt, xo + i), dscale) << (8 * j));
     }
     *cp = wv;
   }
+}
+
+__global__ void __launch_bounds__(kThreads) k_pack_fp8(PackJobs P) {
+  const PackJob& J = P.j[blockIdx.y];
+  const float scale = fp8_tensor_scale(*J.amax);
+  const int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
+  if (gid == 0 && J.sout != nullptr) *J.sout = scale;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  if (J.layout == KVQ_PLANE_TOKEN4) pack_fp8_t4(J, static_cast<double>(scale), gid, stride);
+  else pack_fp8_rows(J, static_cast<double>(scale), gid, stride);
 }
 
 // ---------------------------------------------------------------- unpack
@@ -399,34 +401,28 @@ hipError_t launch_amax(const void* x, int x_dtype, Rows rows, int d, const int32
   return hipGetLastError();
 }
 
-hipError_t launch_pack_nvfp4(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes,
-                             uint8_t* scales, Rows dr, int layout, const int32_t* dst_pos, float* ts_out,
-                             hipStream_t st) {
-  if (layout == KVQ_PLANE_TOKEN4) {
-    const int64_t items = xr.n0 * xr.n1 * (xr.n2 / 4 + 2) * (d / 16);
-    hipLaunchKernelGGL(k_pack_nvfp4_t4, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes,
-                       scales, dr, dst_pos, ts_out);
-  } else {
-    const int64_t items = xr.n0 * xr.n1 * xr.n2 * (d / 16);
-    hipLaunchKernelGGL(k_pack_nvfp4, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes,
-                       scales, dr, dst_pos, ts_out);
+// work items of one job: one per (row, 16-block) / (row, 4 elements), or
+// per (4-token group slot, ...) for TOKEN4 destinations
+static int64_t pack_items(const PackJob& J, bool fp4) {
+  const int64_t per = fp4 ? J.d / 16 : J.d / 4;
+  const int64_t rows = J.layout == KVQ_PLANE_TOKEN4 ? J.xr.n0 * J.xr.n1 * (J.xr.n2 / 4 + 2) : J.xr.n0 * J.xr.n1 * J.xr.n2;
+  return rows * per;
+}
+
+static hipError_t launch_pack(const PackJobs& P, bool fp4, hipStream_t st) {
+  int64_t items = 0;
+  for (int i = 0; i < P.n; ++i) {
+    const int64_t n = pack_items(P.j[i], fp4);
+    items = n > items ? n : items;
   }
+  const dim3 grid(grid_for(items), P.n);
+  if (fp4) hipLaunchKernelGGL(k_pack_nvfp4, grid, dim3(kThreads), 0, st, P);
+  else hipLaunchKernelGGL(k_pack_fp8, grid, dim3(kThreads), 0, st, P);
   return hipGetLastError();
 }
 
-hipError_t launch_pack_fp8(const void* x, int x_dtype, Rows xr, int d, const float* amax, uint8_t* codes, Rows dr,
-                           int layout, const int32_t* dst_pos, float* scale_out, hipStream_t st) {
-  if (layout == KVQ_PLANE_TOKEN4) {
-    const int64_t items = xr.n0 * xr.n1 * (xr.n2 / 4 + 2) * (d / 4);
-    hipLaunchKernelGGL(k_pack_fp8_t4, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes, dr,
-                       dst_pos, scale_out);
-  } else {
-    const int64_t items = xr.n0 * xr.n1 * xr.n2 * (d / 4);
-    hipLaunchKernelGGL(k_pack_fp8, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, xr, d, amax, codes, dr,
-                       dst_pos, scale_out);
-  }
-  return hipGetLastError();
-}
+hipError_t launch_pack_nvfp4(const PackJobs& P, hipStream_t st) { return launch_pack(P, true, st); }
+hipError_t launch_pack_fp8(const PackJobs& P, hipStream_t st) { return launch_pack(P, false, st); }
 
 hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, Rows sr, int layout, int d, const float* ts,
                                float* out, Rows orow, hipStream_t st) {

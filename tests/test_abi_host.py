@@ -173,3 +173,27 @@ def test_combine_validation(L, K):
     assert L.attn_decode_combine(FAKE, FAKE, 2, 4, 128, 2, FAKE, K.KVQ_FP8E4M3, None, None, None) == 1
     assert L.attn_decode_combine(None, FAKE, 2, 4, 128, 2, FAKE, K.KVQ_F32, None, None, None) == 1
     assert L.attn_decode_combine(FAKE, FAKE, 2, 4, 128, 2, FAKE_ODD, K.KVQ_BF16, None, None, None) == 3
+
+
+def test_pack_batch_validation(L, K):
+    from quantized_kv_cache_nvfp4_amd import _lib
+    R = K.KVQ_PLANE_ROWS
+    r16 = _rows(1, 1, 4, 0, 0, 16)
+    good = _lib.KvqPackJob(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE, FAKE, r16, R, None, None)
+    arr = (_lib.KvqPackJob * 9)(*([good] * 9))
+    assert L.kvq_pack_nvfp4_batch(arr, 0, None) == 1
+    assert L.kvq_pack_nvfp4_batch(arr, 9, None) == 1
+    assert L.kvq_pack_nvfp4_batch(None, 1, None) == 1
+    assert L.kvq_pack_fp8_batch(arr, 0, None) == 1
+    # a bad job anywhere in the batch is reported with the single-call code
+    bad = _lib.KvqPackJob(FAKE, K.KVQ_BF16, r16, 24, FAKE, FAKE, FAKE, r16, R, None, None)
+    arr2 = (_lib.KvqPackJob * 2)(good, bad)
+    assert L.kvq_pack_nvfp4_batch(arr2, 2, None) == 1 and "multiple of 16" in K.kvq_last_error()
+    odd = _lib.KvqPackJob(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE_ODD, FAKE, r16, R, None, None)
+    arr3 = (_lib.KvqPackJob * 2)(good, odd)
+    assert L.kvq_pack_nvfp4_batch(arr3, 2, None) == 3
+    # empty jobs are skipped without a launch
+    r0 = _rows(1, 1, 0, 0, 0, 16)
+    empty = _lib.KvqPackJob(FAKE, K.KVQ_BF16, r0, 16, FAKE, FAKE, FAKE, r16, R, None, None)
+    arr4 = (_lib.KvqPackJob * 2)(empty, empty)
+    assert L.kvq_pack_nvfp4_batch(arr4, 2, None) == 0

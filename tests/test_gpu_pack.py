@@ -244,3 +244,47 @@ def test_token4_layout_pack_unpack(fmt):
         assert np.array_equal(u2[b_, :, p_].astype(np.float64), nref[b_, :, 0])
         keep = [t for t in range(L) if t != p_]
         assert np.array_equal(u2[b_][:, keep], before[b_][:, keep])
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_pack_batch_matches_single_calls(fmt):
+    """One batched launch (K rows into a ROWS plane, V rows into a TOKEN4
+    plane, with per-request positions) writes the same bytes as two
+    single-plane calls, and those bytes are the oracle's."""
+    announce(f"pack batch {fmt}")
+    inp = kvq_synth.gqa_inputs(2, 8, 2, 128, None, kv_lens=[30, 45], config="gqa", salt=13, outliers=True)
+    B, H, L, D = inp.k.shape
+    Lp = (L + 3) // 4 * 4
+    k, v = inp.k.to(DEV), inp.v.to(DEV)
+    ka, va = K().kvq_amax(k), K().kvq_amax(v)
+    pos = torch.tensor([3, 0], dtype=torch.int32, device=DEV)
+    Lt = Lp + 4
+    pack = K().kvq_pack_nvfp4 if fmt == "nvfp4" else K().kvq_pack_fp8
+    a_k = empty_plane(fmt, (B, H, Lt), D, K().KVQ_PLANE_ROWS, fill=0x5A)
+    a_v = empty_plane(fmt, (B, H, Lt), D, K().KVQ_PLANE_TOKEN4, fill=0x5A)
+    b_k = empty_plane(fmt, (B, H, Lt), D, K().KVQ_PLANE_ROWS, fill=0x5A)
+    b_v = empty_plane(fmt, (B, H, Lt), D, K().KVQ_PLANE_TOKEN4, fill=0x5A)
+    pack(k, ka, out=a_k, dst_pos=pos)
+    pack(v, va, out=a_v, dst_pos=pos)
+    K().kvq_pack_batch([(k, ka, b_k, pos), (v, va, b_v, pos)])
+    torch.cuda.synchronize()
+    for a_, b_ in ((a_k, b_k), (a_v, b_v)):
+        assert torch.equal(a_.codes, b_.codes)
+        if fmt == "nvfp4":
+            assert torch.equal(a_.scales, b_.scales)
+            assert torch.equal(a_.tensor_scale, b_.tensor_scale)
+        else:
+            assert torch.equal(a_.scale, b_.scale)
+    # and the K plane holds the oracle's codes at rows pos[b] + t
+    kf = kvq_synth.f64(inp.k)
+    if fmt == "nvfp4":
+        c, sc, _ = OQ.nvfp4_pack(kf, float(ka.item()))
+        got_c, got_s = _np(b_k.codes), _np(b_k.scales)
+        for b_, p_ in enumerate([3, 0]):
+            assert np.array_equal(got_c[b_, :, p_:p_ + L], c[b_])
+            assert np.array_equal(got_s[b_, :, p_:p_ + L], sc[b_])
+    else:
+        c, _ = OQ.fp8_pack(kf, float(ka.item()))
+        got_c = _np(b_k.codes)
+        for b_, p_ in enumerate([3, 0]):
+            assert np.array_equal(got_c[b_, :, p_:p_ + L], c[b_])
