@@ -13,6 +13,8 @@
 // Design for CDNA4 (not a translation of the pages' Triton kernel):
 //  * one work-group = 4 waves = one chunk of one (request, kv head); the
 //    waves take interleaved tiles of the chunk and are merged through LDS.
+//  * loads go through buffer resources sized to the chunk: tokens past its
+//    end read zeros in hardware, no per-lane clamping or address math.
 //  * dequantization happens in registers: E2M1 -> f16 with the hardware
 //    convert (exact), times the E4M3 block scale (an exact f16 product:
 //    at most 5 significant bits, inside f16's normal range); the per-tensor
@@ -27,12 +29,14 @@
 //  * Q.K^T contracts over head_dim, and the order of that contraction is
 //    free: lane group g owns a contiguous quarter of head_dim, so each lane
 //    reads its K codes with one 128-bit load per token.  P.V contracts over
-//    tokens, and V is stored token-major, so each lane loads a short run of
-//    head_dim for 4 tokens and transposes 2x2 blocks of f16 in registers
-//    (v_perm_b32) into the token-contiguous MFMA operand; the output
-//    columns are permuted the same way and un-permuted on the final store.
-//  * fp32 queries are split into f16 hi + lo parts and, when asked, P is
-//    split the same way (two MFMAs each) for the fp32-accuracy path.
+//    tokens: with the TOKEN4 V layout one byte holds one element of two
+//    consecutive tokens, so the hardware convert yields the token-contiguous
+//    MFMA operand directly; with row-major V, 2x2 blocks of f16 are
+//    transposed in registers (v_perm_b32).
+//  * the softmax works on groups of 4 tiles: one row maximum and at most
+//    one rescale of the accumulators per group.
+//  * fp32 queries are split into f16 hi + lo parts and P is split the same
+//    way (two MFMAs each) for the fp32-accuracy path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
