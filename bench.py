@@ -49,11 +49,50 @@ def parse():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of the cache's size (counter calibration under rocprofv3)")
     return ap.parse_args()
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_gqa_nvfp4_b2_hq32_hkv8_d128_kv32k_traffic.txt")
+DECODE_SRC = os.path.join(ROOT, "quantized_kv_cache_nvfp4_amd", "csrc", "decode_gqa.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the split kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size),
+    or None when the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE).read().splitlines() if ":" in line)
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != src:
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe():
+    """A plain device-to-device copy of the cache's size (75,497,472 B read
+    and written per launch), 20 launches: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = B * HKV * L * BYTES_PER_TOKEN_HEAD
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 20}), flush=True)
 
 
 def cpu_baseline(inp, reps):
@@ -95,6 +134,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
     import numpy as np
     import torch
     import kvq_synth
@@ -231,7 +273,7 @@ def main():
         "hbm_gbps_step": round(algo_bytes / (step_us * 1e-6) / 1e9, 1),
         "step_us": {k: round(v * 1e3, 3) for k, v in ms.items()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                      "kernel": "k_decode_gqa<NVFP4,G=4,D=128> (split kernel, partials)",
                      "kernel_us_mean": round(kernel_us, 3), "algorithmic_bytes": algo_bytes},
     }
