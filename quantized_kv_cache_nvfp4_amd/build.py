@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "quant_kernels.hip", "decode_gqa.hip", "combine.hip"]
+SOURCES = ["api.cpp", "quant_kernels.hip", "decode_gqa.hip", "decode_mla.hip", "combine.hip"]
 
 ARCH = "gfx950"
 

@@ -302,7 +302,18 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
   } else {
     if (a->kv_format != KVQ_NVFP4) return fail(KVQ_ERR_UNSUPPORTED, "MLA layout supports NVFP4 only");
     if (a->Hkv != 1) return fail(KVQ_ERR_ARG, "MLA layout needs Hkv == 1");
-    return fail(KVQ_ERR_UNSUPPORTED, "MLA decode is not implemented yet");
+    if (a->k_scales == nullptr || a->q_rope == nullptr || a->k_rope == nullptr)
+      return fail(KVQ_ERR_ARG, "MLA needs k_scales, q_rope and k_rope");
+    if (!kvq::mla_supported(*a))
+      return fail(KVQ_ERR_UNSUPPORTED,
+                  "MLA decode: implemented for Hq = 16, D = Dv = 512, Drope = 64, bf16 queries (got Hq=%d D=%d Dv=%d "
+                  "Drope=%d)", a->Hq, a->D, a->Dv, a->Drope);
+    if (!aligned(a->q, 16) || a->q_sh % 8 != 0 || a->q_sb % 8 != 0 || !aligned(a->q_rope, 16) ||
+        a->qr_sh % 8 != 0 || a->qr_sb % 8 != 0)
+      return fail(KVQ_ERR_ALIGN, "MLA queries must be 16-byte aligned with strides multiple of 8 elements");
+    if (!aligned(a->k_scales, 8) || !aligned(a->k_rope, 16))
+      return fail(KVQ_ERR_ALIGN, "MLA k_scales must be 8-byte and k_rope 16-byte aligned");
+    if (a->kv_st < 1) return fail(KVQ_ERR_ARG, "MLA cache token stride must be >= 1");
   }
   *s_out = s;
   return KVQ_OK;
@@ -328,6 +339,8 @@ int attn_decode_splitkv(const kvq_decode_args* a, int32_t* splits_used, void* st
   if (rc != KVQ_OK) return rc;
   if (splits_used) *splits_used = s;
   kvq::DecodePlan plan{s, 0};
+  if (a->layout == KVQ_LAYOUT_MLA)
+    return hip_status(kvq::launch_decode_mla(*a, plan, as_stream(stream)), "attn_decode_splitkv launch");
   return hip_status(kvq::launch_decode_gqa(*a, plan, as_stream(stream)), "attn_decode_splitkv launch");
 }
 
@@ -337,6 +350,17 @@ int attn_decode(const kvq_decode_args* a, void* out, int32_t out_dtype, const fl
   int rc = validate_decode(a, &s, true);
   if (rc != KVQ_OK) return rc;
   if ((rc = check_out(out, out_dtype, out_scale)) != KVQ_OK) return rc;
+  if (a->layout == KVQ_LAYOUT_MLA) {
+    // MLA: split kernel + combine kernel (two launches on the stream)
+    if (a->part_o == nullptr || a->part_lse == nullptr) return fail(KVQ_ERR_ARG, "MLA needs part_o and part_lse");
+    if (splits_used) *splits_used = s;
+    kvq::DecodePlan plan{s, 0};
+    hipError_t e = kvq::launch_decode_mla(*a, plan, as_stream(stream));
+    if (e == hipSuccess)
+      e = kvq::launch_combine(a->part_o, a->part_lse, a->B, a->Hq, a->Dv, s, out, out_dtype, out_scale, lse_out,
+                              as_stream(stream));
+    return hip_status(e, "attn_decode launch");
+  }
   if (s > 1 && counters == nullptr) return fail(KVQ_ERR_ARG, "counters must be non-null when num_splits > 1");
   if (splits_used) *splits_used = s;
   kvq::DecodePlan plan{s, 0};

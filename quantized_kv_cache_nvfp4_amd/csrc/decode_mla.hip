@@ -1,0 +1,244 @@
+// Split-KV flash decode over a DeepSeek-style MLA latent cache (NVFP4
+// latent c + bf16 rope key) for gfx950.
+//
+// Method: Model-Optimizer PR #714 (KV-cache quantization for MLAAttention in
+// vLLM fake-quant), "What does this PR do?" and "Testing": MLA attention
+// caches one latent row c per token (kv_lora_rank 512) plus a rope key; only
+// the latent is quantized (NVFP4, blocks of 16); the absorbed query gives
+// score = softmax_scale * (q_c . c_hat + q_r . k_r) and output = P . c_hat.
+// The split-KV scheme is that of Model-Optimizer PR #1832 "Add quant+sparse
+// attention for vLLM serving", Testing section.
+//
+// Design for CDNA4:
+//  * one work-group = 4 waves = one chunk of one request; all 16 query
+//    heads share every latent row, so they are the 16 MFMA rows and no
+//    query-group packing is needed.
+//  * tiles of 32 tokens.  Scores: wave w covers token half (w & 1) of the
+//    tile over latent half (w >> 1) (256 dims) and rope half (32 dims): 8
+//    MFMA 16x16x32 f16 steps over the dequantized latent plus one bf16 step
+//    over the rope; the two latent halves' partial scores meet in LDS.  The
+//    dequantized latent rows (f16) are staged in LDS.
+//  * P.V: wave w owns output columns 128w .. 128w+127 for all 32 tokens;
+//    its A operand (latent, token-contiguous per column) comes from the
+//    staged rows through the LDS transpose read ds_read_b64_tr_b16, so the
+//    latent is dequantized once and used by both contractions, and its B
+//    operand (P) is already in the right lanes (the token order of the P.V
+//    contraction is chosen to match the score layout).
+//  * every wave computes the softmax of the whole tile (8 scores per lane),
+//    so the four waves share one reference maximum and one denominator.
+//  * loads use buffer resources sized to the chunk (tokens past its end read
+//    zeros), as in the GQA kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "decode_common.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+using namespace dec;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kW = 4;                      // waves per work-group
+constexpr int kThreads = 64 * kW;
+constexpr int kT = 32;                     // tokens per tile
+constexpr int kH = 16;                     // query heads (MFMA rows)
+constexpr int kD = 512;                    // latent rank
+constexpr int kDr = 64;                    // rope dims
+constexpr int kRow = kD / 2;               // latent code bytes per token
+constexpr int kSRow = kD / 16;             // latent scale bytes per token
+constexpr int kPitch = kD * 2 + 32;        // staged f16 row pitch in LDS (bytes; +32 spreads banks)
+
+__device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(kThreads, 4) k_decode_mla(kvq_decode_args a, int num_splits) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_c[kT * kPitch];   // staged latent rows (f16)
+  __shared__ __attribute__((aligned(16))) f32x4 lds_s[kW][64];          // partial scores per wave / lane
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15;   // MFMA row / column index of this lane
+  const int g = lane >> 4;   // lane group (k-slice of the MFMA operands)
+  const int th = wave & 1;   // token half of the tile this wave scores
+  const int dh = wave >> 1;  // latent / rope half this wave scores
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+
+  int L = a.kv_lens[b];
+  L = L < a.max_kv_len ? L : a.max_kv_len;
+  L = L > 0 ? L : 0;
+  int chunk = (L + num_splits - 1) / num_splits;
+  chunk = (chunk + kT - 1) / kT * kT;
+  const int cs = split * chunk;
+  const int ce = (cs + chunk < L) ? cs + chunk : L;
+  const int ntiles = cs < ce ? (ce - cs + kT - 1) / kT : 0;
+
+  const float s_t = *a.k_scale;
+  const float sc_lat = a.softmax_scale * s_t * kLog2e;   // latent scores carry the tensor scale
+  const float sc_rope = a.softmax_scale * kLog2e;
+
+  // ---- query operands, lane (g, c) = head c:
+  //   latent MFMA j (0..7): dims 256 dh + 64 g + 8 j + e; rope: 32 dh + 8 g + e
+  f16x8 qop[8];
+  bf16x8 qr;
+  {
+    const uint16_t* qc = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * a.q_sb +
+                         static_cast<int64_t>(c) * a.q_sh + 256 * dh + 64 * g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qc + 8 * j);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      f16x2 h[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)   // bf16 pair -> fp32 (exact) -> f16 (exact in f16's normal range)
+        h[k] = f16x2{static_cast<_Float16>(__uint_as_float(ws[k] << 16)),
+                     static_cast<_Float16>(__uint_as_float(ws[k] & 0xFFFF0000u))};
+      qop[j] = cat4(h[0], h[1], h[2], h[3]);
+    }
+    const uint16_t* qrp = static_cast<const uint16_t*>(a.q_rope) + static_cast<int64_t>(b) * a.qr_sb +
+                          static_cast<int64_t>(c) * a.qr_sh + 32 * dh + 8 * g;
+    qr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrp));
+  }
+
+  // per-request plane bases (rows of the latent, scale and rope planes)
+  const int64_t row0 = static_cast<int64_t>(b) * a.kv_sb;
+  const int st = static_cast<int>(a.kv_st);
+  const uint8_t* cc = a.k_codes + row0 * kRow;
+  const uint8_t* csc = a.k_scales + row0 * kSRow;
+  const uint8_t* cr = static_cast<const uint8_t*>(a.k_rope) + row0 * (kDr * 2);
+
+  float m_run = -INFINITY;   // running max of head c (log2 domain), the same in every wave
+  float l_run = 0.0f;        // this lane's share of head c's denominator (its 8 tokens per tile)
+  f32x4 acc_o[8];            // O^T rows d = 128*wave + 16*jj + 4g + i, column head c
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) acc_o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int tb = cs + tile * kT;
+    const int t0 = tb + 16 * th;          // first token this wave scores
+    const int nv = ce - t0;               // its valid tokens (may be <= 0)
+    // ---- loads: token c; latent bytes [128 dh + 32 g, +32), scale bytes [16 dh + 4 g, +4),
+    //      rope bytes [64 dh + 16 g, +16)
+    const Rsrc rc_ = make_rsrc(cc + static_cast<int64_t>(t0) * st * kRow, nv * st * kRow);
+    const Rsrc rs_ = make_rsrc(csc + static_cast<int64_t>(t0) * st * kSRow, nv * st * kSRow);
+    const Rsrc rr_ = make_rsrc(cr + static_cast<int64_t>(t0) * st * (kDr * 2), nv * st * (kDr * 2));
+    const u32x4 cw0 = ld128(rc_, c * st * kRow + 128 * dh + 32 * g);
+    const u32x4 cw1 = ld128(rc_, c * st * kRow + 128 * dh + 32 * g + 16);
+    const uint32_t sw = ld32(rs_, c * st * kSRow + 16 * dh + 4 * g);
+    const u32x4 rw = ld128(rr_, c * st * (kDr * 2) + 64 * dh + 16 * g);
+
+    // ---- partial scores S^T[token][head] over this wave's halves; stage the f16 rows
+    f32x4 acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
+    uint8_t* stage = lds_c + (16 * th + c) * kPitch + 512 * dh + 128 * g;   // token row, dims 256 dh + 64 g ..
+    const f16x2 sp0 = fp8x2<false>(sw), sp1 = fp8x2<true>(sw);             // scales of the lane's 4 blocks
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = (j < 4) ? cw0[j] : cw1[j - 4];
+      const _Float16 sv = (j < 4) ? ((j < 2) ? sp0[0] : sp0[1]) : ((j < 6) ? sp1[0] : sp1[1]);   // block j/2
+      const f16x2 s2 = {sv, sv};
+      const f16x8 kop = cat4(fp4x2<0>(w) * s2, fp4x2<1>(w) * s2, fp4x2<2>(w) * s2, fp4x2<3>(w) * s2);
+      acc_l = mfma(kop, qop[j], acc_l);
+      *reinterpret_cast<f16x8*>(stage + 16 * j) = kop;
+    }
+    acc_r = mfma_bf16(__builtin_bit_cast(bf16x8, rw), qr, acc_r);
+    f32x4 ps;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ps[i] = acc_l[i] * sc_lat + acc_r[i] * sc_rope;
+    lds_s[wave][lane] = ps;
+    __syncthreads();   // staged rows and partial scores visible
+
+    // ---- the whole tile's scores for this lane: tokens 4g+i of half 0 (x = 0) and half 1 (x = 1)
+    float sc[2][4];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const f32x4 p0 = lds_s[x][lane], p1 = lds_s[2 + x][lane];   // latent halves 0 and 1
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[x][i] = p0[i] + p1[i];
+    }
+    if (tb + kT > ce) {   // the chunk's last tile (uniform branch)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tb + 16 * x + 4 * g + i >= ce) sc[x][i] = -INFINITY;
+    }
+    float tm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    tm = fmaxf(tm, __shfl_xor(tm, 16));
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    if (__any(tm > m_run)) {   // the same decision for column c in every wave
+      const bool bump = tm > m_run;
+      const float fac = bump ? __builtin_amdgcn_exp2f(m_run - tm) : 1.0f;   // 0 when m_run = -inf
+      l_run *= fac;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_o[jj][i] *= fac;
+      m_run = bump ? tm : m_run;
+    }
+    const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
+    // B operand of P.V (k = 8g + e): e < 4 -> token 4g+e of half 0, e >= 4 -> token 4g+e-4 of half 1
+    f16x2 ph[4];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float p0 = __builtin_amdgcn_exp2f(sc[x][2 * k] - m_ref);   // masked: exp2(-inf) = 0
+        const float p1 = __builtin_amdgcn_exp2f(sc[x][2 * k + 1] - m_ref);
+        l_run += p0 + p1;
+        ph[2 * x + k] = f16x2{static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
+      }
+    const f16x8 pb = cat4(ph[0], ph[1], ph[2], ph[3]);
+
+    // ---- P.V for this wave's 128 output columns over the 32 tokens.  A =
+    // latent^T rows d, k = the tokens above: two transposed reads of 4
+    // token rows; lane m of the 16-lane group points at row r + m/4, columns
+    // d0 + 4(m%4) .. +3, and receives column d0 + m of the 4 rows.
+    const int rlo = 4 * g + (c >> 2), rhi = 16 + 4 * g + (c >> 2);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int col = 2 * (128 * wave + 16 * jj + 4 * (c & 3));
+      const f16x4 lo = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(lds_c + rlo * kPitch + col)));
+      const f16x4 hi = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(lds_c + rhi * kPitch + col)));
+      const f16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc_o[jj] = mfma(av, pb, acc_o[jj]);
+    }
+    __syncthreads();   // the tile's LDS may be overwritten
+  }
+
+  // ---- partials: o = acc * s_t / l, lse = (m + log2 l) ln 2 (l is the same in every wave)
+  float lt = l_run + __shfl_xor(l_run, 16);
+  lt += __shfl_xor(lt, 32);
+  const float f = lt > 0.0f ? s_t / lt : 0.0f;
+  const int64_t po = (static_cast<int64_t>(b) * a.Hq + c) * num_splits + split;
+  float* op = a.part_o + po * kD + 128 * wave + 4 * g;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj)
+    *reinterpret_cast<float4*>(op + 16 * jj) =
+        make_float4(acc_o[jj][0] * f, acc_o[jj][1] * f, acc_o[jj][2] * f, acc_o[jj][3] * f);
+  if (wave == 0 && g == 0) a.part_lse[po] = lt > 0.0f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+int mla_tile_tokens() { return kT; }
+
+bool mla_supported(const kvq_decode_args& a) {
+  return a.kv_format == KVQ_NVFP4 && a.Hq == kH && a.Hkv == 1 && a.D == kD && a.Dv == kD && a.Drope == kDr &&
+         a.q_dtype == KVQ_BF16;
+}
+
+hipError_t launch_decode_mla(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_decode_mla, dim3(p.s, a.B), dim3(kThreads), 0, st, a, p.s);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -67,5 +67,7 @@ int gqa_tile_tokens(int G);
 int mla_tile_tokens();
 // is (format, G, D, q dtype) implemented by the GQA kernel
 bool gqa_supported(int kv_format, int G, int D, int q_dtype);
+// is the MLA configuration implemented (NVFP4 latent 512 + rope 64, 16 heads, bf16 queries)
+bool mla_supported(const kvq_decode_args& a);
 
 }  // namespace kvq

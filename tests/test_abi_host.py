@@ -197,3 +197,37 @@ def test_pack_batch_validation(L, K):
     empty = _lib.KvqPackJob(FAKE, K.KVQ_BF16, r0, 16, FAKE, FAKE, FAKE, r16, R, None, None)
     arr4 = (_lib.KvqPackJob * 2)(empty, empty)
     assert L.kvq_pack_nvfp4_batch(arr4, 2, None) == 0
+
+
+def _mla_args(K):
+    a = K.KvqDecodeArgs()
+    a.kv_format, a.layout = K.KVQ_NVFP4, K.KVQ_LAYOUT_MLA
+    a.B, a.Hq, a.Hkv, a.D, a.Dv, a.Drope = 2, 16, 1, 512, 512, 64
+    a.max_kv_len = 1024
+    a.q, a.q_dtype, a.q_sb, a.q_sh = FAKE, K.KVQ_BF16, 16 * 512, 512
+    a.q_rope, a.qr_sb, a.qr_sh = FAKE, 16 * 64, 64
+    a.k_codes = a.k_scales = a.k_scale = a.k_rope = FAKE
+    a.kv_lens = FAKE
+    a.kv_sb, a.kv_sh, a.kv_st = 1024, 0, 1
+    a.softmax_scale = 0.072
+    a.num_splits = 4
+    a.part_o = a.part_lse = FAKE
+    a.part_capacity = 4
+    return a
+
+
+def test_mla_validation(L, K):
+    a = _mla_args(K); a.Hq = 8
+    assert _decode_rc(L, a) == 2                     # 16 heads only
+    a = _mla_args(K); a.Drope = 32
+    assert _decode_rc(L, a) == 2
+    a = _mla_args(K); a.q_dtype = K.KVQ_F32
+    assert _decode_rc(L, a) == 2
+    a = _mla_args(K); a.kv_format = K.KVQ_FP8E4M3
+    assert _decode_rc(L, a) == 2
+    a = _mla_args(K); a.k_rope = None
+    assert _decode_rc(L, a) == 1
+    a = _mla_args(K); a.q_sh = 500
+    assert _decode_rc(L, a) == 3
+    a = _mla_args(K); a.kv_st = 0
+    assert _decode_rc(L, a) == 1

@@ -1,0 +1,130 @@
+"""GPU parity of the MLA latent-cache decode (NVFP4 latent 512 + bf16 rope 64,
+16 heads) against the fp64 oracle.
+
+The latent is packed on the GPU (bit-exact with the oracle, asserted here
+too), the oracle dequantizes its own packing and runs exact MLA attention.
+Gates: bf16 output per element |o - o_ref| <= max(2e-3, 1 bf16 ulp) and
+cosine >= 0.9999; fp32 output per element <= 1e-5 (1 + |o|) +
+2^-11 * sum_t P_t |c_hat_t| (P enters the P.V contraction as one f16 value;
+scores and products are exact f16 / bf16 products summed in fp32).
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth
+from oracle import attention as OA
+from oracle import quant as OQ
+
+from gpu_helpers import DEV, K, announce, assert_bf16_output
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+@functools.lru_cache(maxsize=8)
+def _case(B, lens, salt):
+    inp = kvq_synth.mla(L=max(lens), B=B, salt=salt, kv_lens=list(lens))
+    cf = kvq_synth.f64(inp.c)
+    amax = OQ.amax(cf[:, None], inp.kv_lens)   # latent viewed as [B, 1, L, 512]
+    codes, scales, st = OQ.nvfp4_pack(cf, amax)
+    chat = OQ.nvfp4_unpack(codes, scales, st)
+    q_c, q_r, k_r = kvq_synth.f64(inp.q_c), kvq_synth.f64(inp.q_r), kvq_synth.f64(inp.k_r)
+    o, lse = OA.decode_mla(q_c, q_r, chat, k_r, inp.kv_lens, inp.softmax_scale)
+    o_abs, _ = OA.decode_mla(q_c, q_r, np.abs(chat), k_r, inp.kv_lens, inp.softmax_scale)
+    return inp, (codes, scales, st, amax), o, lse, o_abs
+
+
+def _gpu(inp, s, out_dtype, fused=False):
+    k_ = K()
+    c = inp.c.to(DEV)
+    lens = torch.from_numpy(inp.kv_lens).to(DEV)
+    amax = k_.kvq_amax(c.unsqueeze(1), lens)
+    plane = k_.kvq_pack_nvfp4(c, amax)                      # codes [B, Lmax, 256], scales [B, Lmax, 32]
+    q_c, q_r, k_r = inp.q_c.to(DEV), inp.q_r.to(DEV), inp.k_r.to(DEV)
+    B, H, D = q_c.shape
+    cap = 64
+    part_o = torch.empty(B * H * cap * D, dtype=torch.float32, device=DEV)
+    part_lse = torch.empty(B * H * cap, dtype=torch.float32, device=DEV)
+    args = k_.make_decode_args(q_c, plane, None, lens, max_kv_len=int(inp.c.shape[1]),
+                               softmax_scale=inp.softmax_scale, num_splits=s, part_o=part_o, part_lse=part_lse,
+                               q_rope=q_r, k_rope=k_r)
+    out = torch.empty(B, H, D, dtype=out_dtype, device=DEV)
+    lse = torch.empty(B, H, dtype=torch.float32, device=DEV)
+    if fused:
+        used = k_.attn_decode(args, out, lse_out=lse)
+    else:
+        used = k_.attn_decode_splitkv(args)
+        k_.attn_decode_combine(part_o, part_lse, B, H, D, used, out, lse_out=lse)
+    torch.cuda.synchronize()
+    return plane, amax, out, lse, used
+
+
+def _check_fp32(out, o_ref, o_abs, label):
+    g = _np(out).astype(np.float64)
+    bound = 1e-5 * (1.0 + np.abs(o_ref)) + 2.0 ** -11 * o_abs
+    bad = np.abs(g - o_ref) > bound
+    assert not bad.any(), f"{label}: {bad.sum()} outputs off; max abs {np.abs(g - o_ref).max():.3g}"
+
+
+MLA_CASES = [
+    (2, (300, 77), 1), (2, (300, 77), 3), (3, (1000, 64, 65), 0), (2, (513, 1), 8), (4, (2048, 2000, 1500, 129), 4),
+]
+
+
+@pytest.mark.parametrize("B,lens,s", MLA_CASES, ids=lambda v: str(v))
+def test_mla_decode(B, lens, s):
+    announce(f"mla B={B} lens={lens} s={s}")
+    inp, (codes, scales, st, amax), o_ref, lse_ref, o_abs = _case(B, lens, 1)
+    plane, amax_g, out32, lse, used = _gpu(inp, s, torch.float32)
+    # the latent plane is the oracle's, byte for byte
+    assert float(amax_g.item()) == amax
+    L = max(lens)
+    assert np.array_equal(_np(plane.codes)[:, :L], codes)
+    assert np.array_equal(_np(plane.scales)[:, :L], scales)
+    _check_fp32(out32, o_ref, o_abs, f"mla s={used}")
+    lse_g = _np(lse).astype(np.float64)
+    assert np.allclose(lse_g, lse_ref, rtol=0, atol=1e-4)
+    _, _, outb, _, _ = _gpu(inp, s, torch.bfloat16)
+    assert_bf16_output(outb, o_ref, f"mla bf16 s={used}")
+
+
+def test_mla_fused_entry_matches_two_launch():
+    inp, _, o_ref, _, o_abs = _case(2, (700, 450), 2)
+    _, _, a32, alse, _ = _gpu(inp, 5, torch.float32)
+    _, _, b32, blse, _ = _gpu(inp, 5, torch.float32, fused=True)
+    assert torch.equal(a32, b32) and torch.equal(alse, blse)
+    _check_fp32(b32, o_ref, o_abs, "mla fused")
+
+
+def test_mla_empty_request():
+    """kv_len 0 gives output 0 and lse -inf; its neighbour is unaffected."""
+    inp, _, o_ref, lse_ref, o_abs = _case(2, (0, 200), 3)
+    _, _, out, lse, _ = _gpu(inp, 4, torch.float32)
+    o = _np(out)
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(_np(lse)[0]))
+    _check_fp32(out[1:], o_ref[1:], o_abs[1:], "mla neighbour of empty")
+
+
+def test_mla_full_config_sampled():
+    """DeepSeek-V2 per-rank shape, B = 32, kv 8192, auto splits: the GPU output
+    of 3 requests checked against the oracle run on those requests alone."""
+    announce("mla full config")
+    inp = kvq_synth.mla()   # B=32, L=8192
+    plane, amax_g, out, _, used = _gpu(inp, 0, torch.bfloat16)
+    assert used >= 1
+    cf = kvq_synth.f64(inp.c)
+    amax = OQ.amax(cf[:, None], inp.kv_lens)
+    assert float(amax_g.item()) == amax
+    for b in (0, 17, 31):
+        codes, scales, st = OQ.nvfp4_pack(cf[b:b + 1], amax)
+        assert np.array_equal(_np(plane.codes)[b:b + 1], codes)
+        chat = OQ.nvfp4_unpack(codes, scales, st)
+        o, _ = OA.decode_mla(kvq_synth.f64(inp.q_c[b:b + 1]), kvq_synth.f64(inp.q_r[b:b + 1]), chat,
+                             kvq_synth.f64(inp.k_r[b:b + 1]), inp.kv_lens[b:b + 1], inp.softmax_scale)
+        assert_bf16_output(out[b:b + 1], o, f"mla full b={b}")
