@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--workload", choices=["gqa32k", "mla"], default="gqa32k",
+                    help="gqa32k: the metric's configuration (default); mla: DeepSeek-V2 per-rank MLA, "
+                         "B=32, 16 heads, NVFP4 latent 512 + bf16 rope 64, kv 8192")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of the cache's size (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -128,6 +131,112 @@ def cpu_baseline(inp, reps):
                       f"attention; median {t:.2f} s/step; numpy elementwise single-threaded, BLAS threads {threads}"}
 
 
+def graph_timer(torch, n_copies, steps_wanted):
+    """Capture fn(i) for every cache copy i into one HIP graph and time its
+    replays with HIP events on the replay stream (ms per captured step)."""
+    reps = max(1, math.ceil(steps_wanted / n_copies))
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(n_copies):
+                fn(i)
+        torch.cuda.synchronize()
+        return g
+
+    def timed(g):
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * n_copies)
+
+    return capture, timed, reps * n_copies
+
+
+MLA_B, MLA_H, MLA_DC, MLA_DR, MLA_L = 32, 16, 512, 64, 8192
+MLA_BYTES_PER_TOKEN = MLA_DC // 2 + MLA_DC // 16 + 2 * MLA_DR   # 256 + 32 + 128 = 416
+
+
+def run_mla(args):
+    """MLA latent-cache decode: one step = attn_decode_splitkv + combine
+    over a rotation of >= 1 GiB of cache copies (109 MB each)."""
+    import numpy as np
+    import torch
+    import kvq_synth
+    import quantized_kv_cache_nvfp4_amd as K
+
+    K._lib.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating MLA inputs")
+    inp = kvq_synth.mla(L=MLA_L, B=MLA_B, H=MLA_H, Dc=MLA_DC, Dr=MLA_DR)
+    lens = torch.from_numpy(inp.kv_lens).to(dev)
+    c = inp.c.to(dev)
+    amax = K.kvq_amax(c.unsqueeze(1), lens)
+    plane0 = K.kvq_pack_nvfp4(c, amax)
+    kr0 = inp.k_r.to(dev)
+    del c
+    q_c, q_r = inp.q_c.to(dev), inp.q_r.to(dev)
+    per_copy = plane0.codes.numel() + plane0.scales.numel() + kr0.numel() * 2
+    assert per_copy == MLA_B * MLA_L * MLA_BYTES_PER_TOKEN
+    n_copies = max(2, math.ceil(args.rotate_gib * (1 << 30) / per_copy))
+    log(f"rotation: {n_copies} cache copies x {per_copy / 1e6:.1f} MB")
+    copies = [(plane0, kr0)] + [(K.NVFP4Plane(plane0.codes.clone(), plane0.scales.clone(),
+                                              plane0.tensor_scale.clone(), plane0.layout), kr0.clone())
+                                for _ in range(n_copies - 1)]
+    s = args.splits if args.splits > 0 else K.kvq_auto_num_splits(K.kvq_device_cu_count(), MLA_B, 1, MLA_L,
+                                                                   MLA_DC, MLA_H)
+    part_o = torch.empty(MLA_B * MLA_H * s * MLA_DC, dtype=torch.float32, device=dev)
+    part_lse = torch.empty(MLA_B * MLA_H * s, dtype=torch.float32, device=dev)
+    out = torch.empty(MLA_B, MLA_H, MLA_DC, dtype=torch.bfloat16, device=dev)
+    dargs = [K.make_decode_args(q_c, pl, None, lens, max_kv_len=MLA_L, softmax_scale=inp.softmax_scale,
+                                num_splits=s, part_o=part_o, part_lse=part_lse, q_rope=q_r, k_rope=kr)
+             for pl, kr in copies]
+
+    def step(i):
+        used = K.attn_decode_splitkv(dargs[i])
+        K.attn_decode_combine(part_o, part_lse, MLA_B, MLA_H, MLA_DC, used, out)
+
+    for i in range(max(args.warmup, n_copies)):
+        step(i % n_copies)
+    torch.cuda.synchronize()
+    capture, timed, steps = graph_timer(torch, n_copies, args.steps)
+    ms_step = timed(capture(step))
+    ms_split = timed(capture(lambda i: K.attn_decode_splitkv(dargs[i])))
+    assert torch.isfinite(out.float()).all()
+    algo = MLA_B * MLA_L * MLA_BYTES_PER_TOKEN
+    kernel_us = ms_split * 1e3
+    achieved = algo / (kernel_us * 1e-6) / 1e9
+    res = {
+        "metric": "us/decode step + achieved HBM GB/s, NVFP4-latent MLA split-KV decode B=32 H=16 8K",
+        "value": round(ms_step * 1e3, 3), "unit": "us/step", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16/bf16 MFMA, fp32 accumulate (NVFP4 latent)", "data": "synthetic",
+        "config": {"workload": "MLA latent-cache decode (DeepSeek-V2 per-rank shape)", "B": MLA_B, "heads": MLA_H,
+                   "latent": MLA_DC, "rope": MLA_DR, "kv_len": MLA_L, "splits": s, "out_dtype": "bf16",
+                   "rotation_copies": n_copies},
+        "hbm_gbps_step": round(algo / (ms_step * 1e-3) / 1e9, 1),
+        "step_us": {"decode_two_launch": round(ms_step * 1e3, 3), "split_kernel": round(kernel_us, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "k_decode_mla (split kernel, partials)", "kernel_us_mean": round(kernel_us, 3),
+                     "algorithmic_bytes": algo},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -136,6 +245,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.workload == "mla":
+        run_mla(args)
         return
     import numpy as np
     import torch
