@@ -119,19 +119,33 @@ __global__ void __launch_bounds__(kThreads, 4) k_decode_mla(kvq_decode_args a, i
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc_o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int tb = cs + tile * kT;
-    const int t0 = tb + 16 * th;          // first token this wave scores
-    const int nv = ce - t0;               // its valid tokens (may be <= 0)
-    // ---- loads: token c; latent bytes [128 dh + 32 g, +32), scale bytes [16 dh + 4 g, +4),
-    //      rope bytes [64 dh + 16 g, +16)
+  // loads of one tile: token c; latent bytes [128 dh + 32 g, +32), scale
+  // bytes [16 dh + 4 g, +4), rope bytes [64 dh + 16 g, +16).  Tokens at or
+  // past the chunk end read zeros; a tile past the chunk reads nothing.
+  struct Raw {
+    u32x4 cw0, cw1, rw;
+    uint32_t sw;
+  };
+  auto load_tile = [&](Raw& R, int tile) {
+    const int t0 = cs + tile * kT + 16 * th;
+    const int nv = ce - t0;
     const Rsrc rc_ = make_rsrc(cc + static_cast<int64_t>(t0) * st * kRow, nv * st * kRow);
     const Rsrc rs_ = make_rsrc(csc + static_cast<int64_t>(t0) * st * kSRow, nv * st * kSRow);
     const Rsrc rr_ = make_rsrc(cr + static_cast<int64_t>(t0) * st * (kDr * 2), nv * st * (kDr * 2));
-    const u32x4 cw0 = ld128(rc_, c * st * kRow + 128 * dh + 32 * g);
-    const u32x4 cw1 = ld128(rc_, c * st * kRow + 128 * dh + 32 * g + 16);
-    const uint32_t sw = ld32(rs_, c * st * kSRow + 16 * dh + 4 * g);
-    const u32x4 rw = ld128(rr_, c * st * (kDr * 2) + 64 * dh + 16 * g);
+    R.cw0 = ld128(rc_, c * st * kRow + 128 * dh + 32 * g);
+    R.cw1 = ld128(rc_, c * st * kRow + 128 * dh + 32 * g + 16);
+    R.sw = ld32(rs_, c * st * kSRow + 16 * dh + 4 * g);
+    R.rw = ld128(rr_, c * st * (kDr * 2) + 64 * dh + 16 * g);
+  };
+  Raw cur, nxt;
+  if (ntiles > 0) load_tile(cur, 0);
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int tb = cs + tile * kT;
+    load_tile(nxt, tile + 1);   // the next tile's data is in flight during this one
+    __builtin_amdgcn_sched_barrier(0);
+    const u32x4 cw0 = cur.cw0, cw1 = cur.cw1, rw = cur.rw;
+    const uint32_t sw = cur.sw;
 
     // ---- partial scores S^T[token][head] over this wave's halves; stage the f16 rows
     f32x4 acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
@@ -212,6 +226,7 @@ __global__ void __launch_bounds__(kThreads, 4) k_decode_mla(kvq_decode_args a, i
       acc_o[jj] = mfma(av, pb, acc_o[jj]);
     }
     __syncthreads();   // the tile's LDS may be overwritten
+    cur = nxt;
   }
 
   // ---- partials: o = acc * s_t / l, lse = (m + log2 l) ln 2 (l is the same in every wave)
