@@ -17,17 +17,22 @@
 namespace kvq {
 namespace {
 
-constexpr int kThreads = 256;   // 4 waves: one (request, head) per wave
+constexpr int kThreads = 256;   // 4 waves, each merging one column slice of one (request, head)
+constexpr int kSlice = 128;     // columns per wave: wide heads (the 512-wide MLA latent) spread over several waves
 
-// grid: ceil(B*Hq / 4); one wave per (request, head)
+// grid: ceil(B*Hq*nsl / 4), nsl = ceil(Dv / kSlice); wave -> (request, head) bh, slice sl
 __global__ void __launch_bounds__(kThreads) k_combine(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-                                                      int nbh, int Dv, int s, void* __restrict__ out, int out_dtype,
-                                                      const float* __restrict__ out_scale, float* __restrict__ lse_out) {
-  const int64_t bh = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
-  if (bh >= nbh) return;   // whole waves leave together
+                                                      int nbh, int nsl, int Dv, int s, void* __restrict__ out,
+                                                      int out_dtype, const float* __restrict__ out_scale,
+                                                      float* __restrict__ lse_out) {
+  const int64_t wv = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (wv >= static_cast<int64_t>(nbh) * nsl) return;   // whole waves leave together
+  const int64_t bh = wv / nsl;
+  const int sl = static_cast<int>(wv - bh * nsl);
+  const int d_lo = sl * kSlice, d_hi = d_lo + kSlice < Dv ? d_lo + kSlice : Dv;
   const float osc = (out_dtype == KVQ_FP8E4M3) ? *out_scale : 1.0f;
-  combine_head<false>(part_lse + bh * s, part_o + bh * s * Dv, s, Dv, out, out_dtype, bh * Dv, osc,
-                      lse_out != nullptr ? lse_out + bh : nullptr);
+  combine_head<false>(part_lse + bh * s, part_o + bh * s * Dv, s, Dv, d_lo, d_hi, out, out_dtype, bh * Dv, osc,
+                      (lse_out != nullptr && sl == 0) ? lse_out + bh : nullptr);
 }
 
 }  // namespace
@@ -35,8 +40,10 @@ __global__ void __launch_bounds__(kThreads) k_combine(const float* __restrict__ 
 hipError_t launch_combine(const float* part_o, const float* part_lse, int B, int Hq, int Dv, int s, void* out,
                           int out_dtype, const float* out_scale, float* lse_out, hipStream_t st) {
   const int nbh = B * Hq;
-  hipLaunchKernelGGL(k_combine, dim3((nbh + kThreads / 64 - 1) / (kThreads / 64)), dim3(kThreads), 0, st, part_o, part_lse,
-                     nbh, Dv, s, out, out_dtype, out_scale, lse_out);
+  const int nsl = (Dv + kSlice - 1) / kSlice;
+  const int64_t waves = static_cast<int64_t>(nbh) * nsl;
+  hipLaunchKernelGGL(k_combine, dim3(static_cast<unsigned>((waves + kThreads / 64 - 1) / (kThreads / 64))), dim3(kThreads),
+                     0, st, part_o, part_lse, nbh, nsl, Dv, s, out, out_dtype, out_scale, lse_out);
   return hipGetLastError();
 }
 

@@ -58,8 +58,9 @@ __device__ inline float wave_split_weight(const float* lse, int s, float& inv, f
   return wj;
 }
 
-// Merge of one (request, head) by one wave: po = its partials [s][Dv],
-// out element i of the head = out[oidx + i].  The partial loads of the
+// Merge of columns [d_lo, d_hi) of one (request, head) by one wave: po = its
+// partials [s][Dv], out element i of the head = out[oidx + i]; lse_out (may
+// be null) receives the merged LSE.  The partial loads of the
 // lane's columns (lane, lane + 64) for all s splits are issued before the
 // weights are computed, so the merge costs one memory round trip per 128
 // columns (64 when s > 32).  Splits j >= s read split s - 1 and get weight 0 (lane j's
@@ -67,26 +68,26 @@ __device__ inline float wave_split_weight(const float* lse, int s, float& inv, f
 // change the result.  Four accumulators (j mod 4).  (For N = 64 one column
 // per pass.)
 template <bool COHERENT, int N>
-__device__ inline void combine_head_n(const float* lse, const float* po, int s, int Dv, void* out, int dt,
-                                      int64_t oidx, float osc, float* lse_out) {
+__device__ inline void combine_head_n(const float* lse, const float* po, int s, int Dv, int d_lo, int d_hi, void* out,
+                                      int dt, int64_t oidx, float osc, float* lse_out) {
   constexpr int C = N <= 32 ? 2 : 1;   // columns per lane per pass (at most 64 loads in flight)
   const int lane = threadIdx.x & 63;
   float inv = 0.0f, lse_m = -INFINITY, w = 0.0f;
-  for (int d0 = 0; d0 < Dv; d0 += 64 * C) {
+  for (int d0 = d_lo; d0 < d_hi; d0 += 64 * C) {
     float v[C][N];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int d = d0 + lane + 64 * c;
-      if (d < Dv) {
+      if (d < d_hi) {
 #pragma unroll
         for (int j = 0; j < N; ++j) v[c][j] = ld_part<COHERENT>(po + static_cast<int64_t>(j < s ? j : s - 1) * Dv + d);
       }
     }
-    if (d0 == 0) w = wave_split_weight<COHERENT>(lse, s, inv, lse_m);
+    if (d0 == d_lo) w = wave_split_weight<COHERENT>(lse, s, inv, lse_m);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int d = d0 + lane + 64 * c;
-      if (d < Dv) {
+      if (d < d_hi) {
         float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int j = 0; j < N; ++j) a[j & 3] += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j)) * v[c][j];
@@ -98,11 +99,11 @@ __device__ inline void combine_head_n(const float* lse, const float* po, int s, 
 }
 
 template <bool COHERENT>
-__device__ inline void combine_head(const float* lse, const float* po, int s, int Dv, void* out, int dt, int64_t oidx,
-                                    float osc, float* lse_out) {
-  if (s <= 16) combine_head_n<COHERENT, 16>(lse, po, s, Dv, out, dt, oidx, osc, lse_out);
-  else if (s <= 32) combine_head_n<COHERENT, 32>(lse, po, s, Dv, out, dt, oidx, osc, lse_out);
-  else combine_head_n<COHERENT, 64>(lse, po, s, Dv, out, dt, oidx, osc, lse_out);
+__device__ inline void combine_head(const float* lse, const float* po, int s, int Dv, int d_lo, int d_hi, void* out,
+                                    int dt, int64_t oidx, float osc, float* lse_out) {
+  if (s <= 16) combine_head_n<COHERENT, 16>(lse, po, s, Dv, d_lo, d_hi, out, dt, oidx, osc, lse_out);
+  else if (s <= 32) combine_head_n<COHERENT, 32>(lse, po, s, Dv, d_lo, d_hi, out, dt, oidx, osc, lse_out);
+  else combine_head_n<COHERENT, 64>(lse, po, s, Dv, d_lo, d_hi, out, dt, oidx, osc, lse_out);
 }
 
 }  // namespace kvq

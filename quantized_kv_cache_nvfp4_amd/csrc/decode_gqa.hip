@@ -738,7 +738,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   // one head per wave (the routine of the standalone combine kernel)
   for (int h = wave; h < G; h += kWaves) {
     const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + h;
-    combine_head<true>(a.part_lse + bh * num_splits, a.part_o + bh * num_splits * D, num_splits, D, fo.out,
+    combine_head<true>(a.part_lse + bh * num_splits, a.part_o + bh * num_splits * D, num_splits, D, 0, D, fo.out,
                        fo.out_dtype, bh * D, osc, fo.lse_out != nullptr ? fo.lse_out + bh : nullptr);
   }
 }

@@ -34,6 +34,10 @@
 #include "decode_common.h"
 #include "kvq_internal.h"
 
+#ifndef KVQ_MLA_AHEAD
+#define KVQ_MLA_AHEAD 1
+#endif
+
 namespace kvq {
 namespace {
 
@@ -52,12 +56,13 @@ constexpr int kDr = 64;                    // rope dims
 constexpr int kRow = kD / 2;               // latent code bytes per token
 constexpr int kSRow = kD / 16;             // latent scale bytes per token
 constexpr int kPitch = kD * 2 + 32;        // staged f16 row pitch in LDS (bytes; +32 spreads banks)
+constexpr int kAhead = KVQ_MLA_AHEAD;      // tiles loaded ahead of the one being computed
 
 __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ void __launch_bounds__(kThreads, 4) k_decode_mla(kvq_decode_args a, int num_splits) {
+__global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, int num_splits) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_c[kT * kPitch];   // staged latent rows (f16)
   __shared__ __attribute__((aligned(16))) f32x4 lds_s[kW][64];          // partial scores per wave / lane
 
@@ -67,6 +72,11 @@ __global__ void __launch_bounds__(kThreads, 4) k_decode_mla(kvq_decode_args a, i
   const int g = lane >> 4;   // lane group (k-slice of the MFMA operands)
   const int th = wave & 1;   // token half of the tile this wave scores
   const int dh = wave >> 1;  // latent / rope half this wave scores
+  // LDS bank spreading of the staged rows: chunk k (16 bytes) of row r sits at
+  // k ^ swz(r), swz(r) = bit 2 of r xor bit 3 of r, which makes both the
+  // row-wise 16-byte stores and the transposed 8-byte reads conflict-free.
+  const int swz_w = ((c >> 2) ^ (c >> 3)) & 1;   // rows 16 th + c (stores)
+  const int swz_r = (g ^ (g >> 1)) & 1;          // rows 4 g + m/4 and 16 + 4 g + m/4 (transposed reads)
   const int split = blockIdx.x;
   const int b = blockIdx.y;
 
@@ -137,19 +147,17 @@ __global__ void __launch_bounds__(kThreads, 4) k_decode_mla(kvq_decode_args a, i
     R.sw = ld32(rs_, c * st * kSRow + 16 * dh + 4 * g);
     R.rw = ld128(rr_, c * st * (kDr * 2) + 64 * dh + 16 * g);
   };
-  Raw cur, nxt;
-  if (ntiles > 0) load_tile(cur, 0);
-
-  for (int tile = 0; tile < ntiles; ++tile) {
+  auto process = [&](const Raw& cur, int tile) {
     const int tb = cs + tile * kT;
-    load_tile(nxt, tile + 1);   // the next tile's data is in flight during this one
-    __builtin_amdgcn_sched_barrier(0);
     const u32x4 cw0 = cur.cw0, cw1 = cur.cw1, rw = cur.rw;
     const uint32_t sw = cur.sw;
 
     // ---- partial scores S^T[token][head] over this wave's halves; stage the f16 rows
     f32x4 acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
-    uint8_t* stage = lds_c + (16 * th + c) * kPitch + 512 * dh + 128 * g;   // token row, dims 256 dh + 64 g ..
+    // token row 16 th + c, dims 256 dh + 64 g ..; 16-byte chunk k of the row is stored at k ^ swz(row)
+    uint8_t* stage = lds_c + (16 * th + c) * kPitch + 512 * dh + 128 * g;
+    uint8_t* const stage_even = stage + 16 * swz_w;   // chunks with even k move by +16 bytes when swz = 1
+    uint8_t* const stage_odd = stage - 16 * swz_w;    // odd k by -16
     const f16x2 sp0 = fp8x2<false>(sw), sp1 = fp8x2<true>(sw);             // scales of the lane's 4 blocks
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -158,7 +166,7 @@ __global__ void __launch_bounds__(kThreads, 4) k_decode_mla(kvq_decode_args a, i
       const f16x2 s2 = {sv, sv};
       const f16x8 kop = cat4(fp4x2<0>(w) * s2, fp4x2<1>(w) * s2, fp4x2<2>(w) * s2, fp4x2<3>(w) * s2);
       acc_l = mfma(kop, qop[j], acc_l);
-      *reinterpret_cast<f16x8*>(stage + 16 * j) = kop;
+      *reinterpret_cast<f16x8*>(((j & 1) ? stage_odd : stage_even) + 16 * j) = kop;
     }
     acc_r = mfma_bf16(__builtin_bit_cast(bf16x8, rw), qr, acc_r);
     f32x4 ps;
@@ -214,10 +222,10 @@ __global__ void __launch_bounds__(kThreads, 4) k_decode_mla(kvq_decode_args a, i
     // latent^T rows d, k = the tokens above: two transposed reads of 4
     // token rows; lane m of the 16-lane group points at row r + m/4, columns
     // d0 + 4(m%4) .. +3, and receives column d0 + m of the 4 rows.
-    const int rlo = 4 * g + (c >> 2), rhi = 16 + 4 * g + (c >> 2);
+    const int rlo = 4 * g + (c >> 2), rhi = 16 + 4 * g + (c >> 2);   // both have swz = swz_r
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      const int col = 2 * (128 * wave + 16 * jj + 4 * (c & 3));
+      const int col = 256 * wave + 32 * jj + 16 * (((c >> 1) & 1) ^ swz_r) + 8 * (c & 1);
       const f16x4 lo = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)(lds_c + rlo * kPitch + col)));
       const f16x4 hi = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -226,7 +234,25 @@ __global__ void __launch_bounds__(kThreads, 4) k_decode_mla(kvq_decode_args a, i
       acc_o[jj] = mfma(av, pb, acc_o[jj]);
     }
     __syncthreads();   // the tile's LDS may be overwritten
-    cur = nxt;
+  };
+
+  // kAhead tiles are in flight while one computes: buffer (tile mod
+  // kAhead+1) holds tile's data; the loop is unrolled over the buffers so
+  // that each has fixed registers.  Tiles past the chunk load nothing.
+  Raw buf[kAhead + 1];
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {
+    load_tile(buf[k], k);
+    __builtin_amdgcn_sched_barrier(0);   // issue order = tile order, so a wait for one tile spares the later ones
+  }
+  for (int t0 = 0; t0 < ntiles; t0 += kAhead + 1) {
+#pragma unroll
+    for (int u = 0; u <= kAhead; ++u) {
+      if (t0 + u >= ntiles) break;
+      load_tile(buf[(u + kAhead) % (kAhead + 1)], t0 + u + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+      process(buf[u], t0 + u);
+    }
   }
 
   // ---- partials: o = acc * s_t / l, lse = (m + log2 l) ln 2 (l is the same in every wave)
