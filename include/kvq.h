@@ -268,10 +268,18 @@ typedef struct {
  * denominator) and accumulates P.V; it writes per-split partials.
  * Chunking: c = ceil(L_b / s) rounded up to the kernel tile; split j covers
  * [j c, min((j+1) c, L_b)).
- * With quantize_p = 1 (GQA only) the partials are written so that
- * attn_decode_combine returns sum_t P~_t V_t (normalized P quantized to E4M3
- * with prob_scale, not renormalized; vLLM PR #15734 item 2); this mode
- * needs p_scratch (kvq_fp8p_scratch_floats).
+ * With quantize_p = 1 (GQA only; vLLM PR #15734 "[Quantization][FP8] Add
+ * support for FP8 models with input_scale for output projection and QK
+ * quantization", item 2) the probabilities are the normalized softmax over
+ * the whole sequence, P_t = exp(sigma_t - LSE), quantized as
+ * P~_t = E4M3(P_t / prob_scale) * prob_scale (round to nearest even,
+ * saturating), and attn_decode_combine then returns sum_t P~_t V_t (not
+ * renormalized) and the exact LSE.  Two launches: pass 1 reads K, spills
+ * the scores to p_scratch and writes each split's lse to part_lse; pass 2
+ * reads V and the spilled scores and writes part_o as
+ * sum_{t in j} P~_t V_t / exp(lse_j - LSE).  p_scratch: device float32,
+ * kvq_fp8p_scratch_floats(...) elements, 16-byte aligned; prob_scale > 0.
+ * The scratch and the partials must not be shared by overlapping calls.
  *   splits_used  host int32* or NULL: receives the split count s used.
  */
 int attn_decode_splitkv(const kvq_decode_args* args, int32_t* splits_used, void* stream);
@@ -297,6 +305,8 @@ int attn_decode_combine(const float* part_o, const float* part_lse, int32_t B, i
  * the last work-group to finish a (request, kv head) merges its s partials
  * and writes the output (with s == 1 the output is written directly and no
  * partials or counters are touched).  Same results as the two-call path.
+ * MLA and quantize_p = 1 run as the split launch(es) followed by the
+ * combine launch (counters unused).
  *   out, out_dtype, out_scale, lse_out  as attn_decode_combine.
  *   counters  device int32[B * Hkv]: all zero before the first call; every
  *             completed call leaves them zero.  Calls sharing a counters
@@ -326,8 +336,9 @@ int kvq_device_cu_count(int32_t* num_cus_out);
 
 /*
  * kvq_fp8p_scratch_floats - float32 elements of p_scratch needed by the
- * FP8-probability path (quantize_p = 1): the spilled scores B*Hq*max_kv_len
- * followed by per-split and per-head statistics.  Host-only.
+ * FP8-probability path (quantize_p = 1): the spilled scores, one row of
+ * roundup(max_kv_len, 4) floats per (request, query head); s is accepted for
+ * interface stability and does not change the size.  Host-only.
  */
 size_t kvq_fp8p_scratch_floats(int32_t B, int32_t Hq, int32_t s, int32_t max_kv_len);
 

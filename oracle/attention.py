@@ -144,26 +144,38 @@ def combine(o_part, lse_part):
     return o, lse
 
 
+def gqa_probs(q, k, kv_lens, softmax_scale):
+    """Normalized softmax probabilities of GQA decode: P [B, Hq, Lmax] with
+    P[b, h, t] = softmax_t(alpha * q_h . K_{floor(h/G), t}) for t < kv_len,
+    0 past it (float64)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    B, Hq, _ = q.shape
+    G = Hq // k.shape[1]
+    P = np.zeros((B, Hq, k.shape[2]))
+    for b in range(B):
+        L = int(kv_lens[b])
+        for h in range(Hq):
+            if L:
+                P[b, h, :L], _ = _softmax_stats(softmax_scale * (k[b, h // G, :L] @ q[b, h]))
+    return P
+
+
 def decode_gqa_fp8p(q, k, v, kv_lens, softmax_scale, prob_scale):
     """GQA decode with the normalized probabilities quantized to E4M3:
     P~ = E4M3(P / prob_scale) * prob_scale, o = sum_t P~_t V_t (not
     renormalized).  Returns o [B, Hq, Dv]."""
-    q = np.asarray(q, np.float64)
-    k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
-    B, Hq, _ = q.shape
-    G = Hq // k.shape[1]
+    P = gqa_probs(q, k, kv_lens, softmax_scale)
+    B, Hq, _ = P.shape
+    G = Hq // v.shape[1]
     o = np.zeros((B, Hq, v.shape[-1]))
     for b in range(B):
         L = int(kv_lens[b])
         for h in range(Hq):
-            if not L:
-                continue
-            kvh = h // G
-            s = softmax_scale * (k[b, kvh, :L] @ q[b, h])
-            p, _ = _softmax_stats(s)
-            pq = F.e4m3_round(p / prob_scale) * prob_scale
-            o[b, h] = pq @ v[b, kvh, :L]
+            if L:
+                pq = F.e4m3_round(P[b, h, :L] / prob_scale) * prob_scale
+                o[b, h] = pq @ v[b, h // G, :L]
     return o
 
 

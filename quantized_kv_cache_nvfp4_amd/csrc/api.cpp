@@ -226,8 +226,8 @@ int kvq_device_cu_count(int32_t* num_cus_out) {
 
 size_t kvq_fp8p_scratch_floats(int32_t B, int32_t Hq, int32_t s, int32_t max_kv_len) {
   if (B <= 0 || Hq <= 0 || s <= 0 || max_kv_len < 0) return 0;
-  // spilled scores, per-split (max, sum) and per-head (max, sum)
-  return static_cast<size_t>(B) * Hq * (static_cast<size_t>(max_kv_len) + 2 * s + 2);
+  // the spilled scores: one row of roundup(max_kv_len, 4) floats per (request, head)
+  return static_cast<size_t>(B) * Hq * ((static_cast<size_t>(max_kv_len) + 3) / 4 * 4);
 }
 
 }  // extern "C"
@@ -272,7 +272,8 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
     if (rc != KVQ_OK) return rc;
   }
   if (s > 64) return fail(KVQ_ERR_ARG, "num_splits %d exceeds 64", s);
-  const bool need_partials = !(fused && s == 1);
+  // the FP8-probability passes always go through the partials
+  const bool need_partials = a->quantize_p || !(fused && s == 1);
   if (need_partials) {
     if (a->part_o == nullptr || a->part_lse == nullptr) return fail(KVQ_ERR_ARG, "part_o and part_lse must be non-null");
     if (!aligned(a->part_o, 4) || !aligned(a->part_lse, 4)) return fail(KVQ_ERR_ALIGN, "partials must be 4-byte aligned");
@@ -281,7 +282,10 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
   }
   if (a->quantize_p) {
     if (a->layout != KVQ_LAYOUT_GQA) return fail(KVQ_ERR_UNSUPPORTED, "quantize_p is implemented for the GQA layout only");
-    return fail(KVQ_ERR_UNSUPPORTED, "quantize_p is not implemented yet");
+    if (!(a->prob_scale > 0.0f) || a->prob_scale > 3.0e38f)
+      return fail(KVQ_ERR_ARG, "prob_scale must be a positive finite number");
+    if (a->p_scratch == nullptr) return fail(KVQ_ERR_ARG, "quantize_p needs p_scratch (kvq_fp8p_scratch_floats)");
+    if (!aligned(a->p_scratch, 16)) return fail(KVQ_ERR_ALIGN, "p_scratch must be 16-byte aligned");
   }
   if (a->layout == KVQ_LAYOUT_GQA) {
     if (a->v_codes == nullptr || a->v_scale == nullptr) return fail(KVQ_ERR_ARG, "GQA needs v_codes and v_scale");
@@ -341,6 +345,8 @@ int attn_decode_splitkv(const kvq_decode_args* a, int32_t* splits_used, void* st
   kvq::DecodePlan plan{s, 0};
   if (a->layout == KVQ_LAYOUT_MLA)
     return hip_status(kvq::launch_decode_mla(*a, plan, as_stream(stream)), "attn_decode_splitkv launch");
+  if (a->quantize_p)
+    return hip_status(kvq::launch_decode_fp8p(*a, plan, as_stream(stream)), "attn_decode_splitkv launch");
   return hip_status(kvq::launch_decode_gqa(*a, plan, as_stream(stream)), "attn_decode_splitkv launch");
 }
 
@@ -350,12 +356,13 @@ int attn_decode(const kvq_decode_args* a, void* out, int32_t out_dtype, const fl
   int rc = validate_decode(a, &s, true);
   if (rc != KVQ_OK) return rc;
   if ((rc = check_out(out, out_dtype, out_scale)) != KVQ_OK) return rc;
-  if (a->layout == KVQ_LAYOUT_MLA) {
-    // MLA: split kernel + combine kernel (two launches on the stream)
-    if (a->part_o == nullptr || a->part_lse == nullptr) return fail(KVQ_ERR_ARG, "MLA needs part_o and part_lse");
+  if (a->layout == KVQ_LAYOUT_MLA || a->quantize_p) {
+    // MLA and FP8 probabilities: split kernel(s) + combine kernel on the stream
+    if (a->part_o == nullptr || a->part_lse == nullptr) return fail(KVQ_ERR_ARG, "part_o and part_lse must be non-null");
     if (splits_used) *splits_used = s;
     kvq::DecodePlan plan{s, 0};
-    hipError_t e = kvq::launch_decode_mla(*a, plan, as_stream(stream));
+    hipError_t e = a->quantize_p ? kvq::launch_decode_fp8p(*a, plan, as_stream(stream))
+                                 : kvq::launch_decode_mla(*a, plan, as_stream(stream));
     if (e == hipSuccess)
       e = kvq::launch_combine(a->part_o, a->part_lse, a->B, a->Hq, a->Dv, s, out, out_dtype, out_scale, lse_out,
                               as_stream(stream));

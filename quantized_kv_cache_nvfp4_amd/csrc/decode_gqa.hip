@@ -37,6 +37,21 @@
 //    one rescale of the accumulators per group.
 //  * fp32 queries are split into f16 hi + lo parts and P is split the same
 //    way (two MFMAs each) for the fp32-accuracy path.
+//  * FP8 probabilities (vLLM PR #15734 "[Quantization][FP8] Add support for
+//    FP8 models with input_scale for output projection and QK
+//    quantization", item 2: softmax(QK^T) quantized to FP8 with a
+//    probability scale inside the attention loop), read as the normalized
+//    probabilities P = softmax over the whole sequence, so the quantized
+//    P~ = E4M3(P / prob_scale) * prob_scale do not depend on the split or
+//    the tile order.  P needs the global max and denominator, hence two
+//    passes over the same chunking: pass 1 (PM = 1) computes the scores
+//    from K only, spills them (fp32, log2 units) and writes each split's
+//    log-sum-exp to the partial lse array; pass 2 (PM = 2) reads the
+//    spilled scores of its chunk and the s split lse values of its heads,
+//    forms P, quantizes it and accumulates P~ . V from V only.  Its partial
+//    is o_j = sum_t P~_t V_t / w_j with w_j = exp(lse_j - LSE) the split's
+//    share of the softmax mass, so that the ordinary combine (weights w_j)
+//    returns sum_t P~_t V_t, not renormalized.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -153,8 +168,10 @@ constexpr int decode_min_blocks() {
   return (16 / G > 4) ? 2 : ((QF32 || KVF != KVQ_NVFP4) ? 2 : 2);
 }
 
-template <int KVF, int G, int D, bool QF32, int PSPLIT, bool FUSED, int VL>
+// PM: 0 attention, 1 FP8-P pass 1 (scores), 2 FP8-P pass 2 (quantized P . V).
+template <int KVF, int G, int D, bool QF32, int PSPLIT, bool FUSED, int VL, int PM>
 __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>())) k_decode_gqa(kvq_decode_args a, int num_splits, FusedOut fo) {
+  static_assert(PM == 0 || (!FUSED && PSPLIT == 1), "the FP8-P passes write partials only");
   using Gm = Geo<KVF, D>;
   constexpr int NSUB = 16 / G;                  // row groups in the 16 MFMA columns
   constexpr int NT = NSUB < 2 ? 2 : NSUB;       // sub-tiles (16 tokens) per tile
@@ -207,7 +224,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   if (wave < ntiles) {
     // ---- query operand: lane (g, c) holds Q[h = c % G][g*QKE + 8j + e]
     f16x8 qop[NQ][Gm::kQkJ];
-    {
+    if constexpr (PM != 2) {
       // 16-byte vector loads (q rows and strides are 16-byte aligned)
       const int64_t qb = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(hq0 + my_h) * a.q_sh +
                          g * Gm::kQkElems;
@@ -635,7 +652,127 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
         }
       }
     };
-    if constexpr (NG > 1) {
+    // FP8-P scratch: spilled scores [B][Hq][sp_stride] (fp32, log2 units)
+    const int64_t sp_stride = (static_cast<int64_t>(a.max_kv_len) + 3) / 4 * 4;
+    const int64_t bh_row = static_cast<int64_t>(b) * a.Hq + hq0 + my_h;   // this lane's head
+    if constexpr (PM == 1) {
+      // ---- FP8-P pass 1: the scores of every tile, spilled to the scratch
+      // (tokens < ce only), and the running max / denominator of each row
+      float* const sp_row = a.p_scratch + bh_row * sp_stride;
+      auto spill_and_stats = [&](int tile, const float (&sc)[NACC][4]) {
+        const int tb = cs + tile * TT;
+#pragma unroll
+        for (int x = 0; x < NACC; ++x) {
+          const int t0 = tb + 16 * (x * NSUB + my_sub) + 4 * g;
+          if (t0 + 4 <= ce) {
+            *reinterpret_cast<float4*>(sp_row + t0) = make_float4(sc[x][0], sc[x][1], sc[x][2], sc[x][3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (t0 + i < ce) sp_row[t0 + i] = sc[x][i];
+          }
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < NACC; ++x)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[x][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));   // the row's max over its four lane groups
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        if (tmax > m_run) {
+          l_run *= __builtin_amdgcn_exp2f(m_run - tmax);   // 0 when m_run = -inf
+          m_run = tmax;
+        }
+        const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
+#pragma unroll
+        for (int x = 0; x < NACC; ++x)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) l_run += __builtin_amdgcn_exp2f(sc[x][i] - m_ref);
+      };
+      float sc[NACC][4];
+      if constexpr (NG > 1) {   // two K register sets: the next tile loads during this one
+        load_ktile(KA, tile_of(0));
+        for (int k = 0; k < nw; k += 2) {
+          load_ktile(KB, tile_of(k + 1));
+          __builtin_amdgcn_sched_barrier(0);
+          qk_scores(KA, tile_of(k), sc);
+          spill_and_stats(tile_of(k), sc);
+          if (k + 1 < nw) {
+            load_ktile(KA, tile_of(k + 2));
+            __builtin_amdgcn_sched_barrier(0);
+            qk_scores(KB, tile_of(k + 1), sc);
+            spill_and_stats(tile_of(k + 1), sc);
+          }
+        }
+      } else {
+        for (int k = 0; k < nw; ++k) {
+          load_ktile(KA, tile_of(k));
+          qk_scores(KA, tile_of(k), sc);
+          spill_and_stats(tile_of(k), sc);
+        }
+      }
+    } else if constexpr (PM == 2) {
+      // ---- FP8-P pass 2: P_t = exp2(sigma_t - LSE2) with LSE2 the head's
+      // log-sum-exp over all splits (log2 units), P~ = E4M3(P / prob_scale)
+      // (round to nearest even, saturating at 448); the codes' values are
+      // exact in f16 and prob_scale is applied with the output.
+      float M2 = -INFINITY;
+      for (int j = 0; j < num_splits; ++j) M2 = fmaxf(M2, a.part_lse[bh_row * num_splits + j] * kLog2e);
+      float S2 = 0.0f;
+      for (int j = 0; j < num_splits; ++j) {
+        const float l2 = a.part_lse[bh_row * num_splits + j] * kLog2e;
+        S2 += (l2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(l2 - M2);
+      }
+      const float lse2 = M2 + log2f(S2);   // this chunk has tokens, so S2 > 0
+      const float ps = a.prob_scale;
+      const float* const sp_row = a.p_scratch + bh_row * sp_stride;
+      auto probs = [&](int tile, f16x2 (&ph)[NACC][2]) {
+        const int tb = cs + tile * TT;
+#pragma unroll
+        for (int x = 0; x < NACC; ++x) {
+          const int t0 = tb + 16 * (x * NSUB + my_sub) + 4 * g;
+          float sg[4];
+          if (t0 + 4 <= ce) {
+            const float4 v4 = *reinterpret_cast<const float4*>(sp_row + t0);
+            sg[0] = v4.x; sg[1] = v4.y; sg[2] = v4.z; sg[3] = v4.w;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sg[i] = (t0 + i < ce) ? sp_row[t0 + i] : -INFINITY;
+          }
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float r0 = fminf(__builtin_amdgcn_exp2f(sg[2 * k] - lse2) / ps, 448.0f);
+            const float r1 = fminf(__builtin_amdgcn_exp2f(sg[2 * k + 1] - lse2) / ps, 448.0f);
+            ph[x][k] = fp8x2<false>(static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false)));
+          }
+        }
+      };
+      f16x2 ph[NACC][2], pl[NACC][2];
+      if constexpr (NG > 1) {   // two V register sets
+        load_vtile(VA, tile_of(0));
+        for (int k = 0; k < nw; k += 2) {
+          load_vtile(VB, tile_of(k + 1));
+          __builtin_amdgcn_sched_barrier(0);
+          probs(tile_of(k), ph);
+          mask_vtile(VA, tile_of(k));
+          pv_tile(VA, ph, pl);
+          if (k + 1 < nw) {
+            load_vtile(VA, tile_of(k + 2));
+            __builtin_amdgcn_sched_barrier(0);
+            probs(tile_of(k + 1), ph);
+            mask_vtile(VB, tile_of(k + 1));
+            pv_tile(VB, ph, pl);
+          }
+        }
+      } else {
+        for (int k = 0; k < nw; ++k) {
+          load_vtile(VA, tile_of(k));
+          probs(tile_of(k), ph);
+          mask_vtile(VA, tile_of(k));
+          pv_tile(VA, ph, pl);
+        }
+      }
+    } else if constexpr (NG > 1) {
       load_ktile(KA, tile_of(0));
       int k0 = 0;
       for (; k0 + NG <= nw; k0 += NG) group(k0, NG, std::integral_constant<bool, true>{});
@@ -662,10 +799,12 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
     lds_m[wave][c] = m_run;
     lds_l[wave][c] = l_tot;
   }
+  if constexpr (PM != 1) {
 #pragma unroll
-  for (int j = 0; j < Gm::kPvJ; ++j) {
+    for (int j = 0; j < Gm::kPvJ; ++j) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_o[wave][4 * g + i][c * Gm::kPvElems + j] = acc_o[j][i];
+      for (int i = 0; i < 4; ++i) lds_o[wave][4 * g + i][c * Gm::kPvElems + j] = acc_o[j][i];
+    }
   }
   __syncthreads();
 
@@ -675,7 +814,26 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   // with equal lane % G, and butterfly shuffles over the other lane bits
   // give the head's maximum and merged denominator.  The weights include
   // the division by that denominator.
-  if (wave == 0) {
+  if (PM == 2 && wave == 0) {
+    // FP8-P pass 2: rows hold plain sums of P~ . V (no running max), merged
+    // with weight 1; the output factor of head h is prob_scale / w_j with
+    // w_j = exp(lse_j - LSE) this split's share of the head's softmax mass
+    // (0 for an empty split, whose sum is 0 too).
+    lds_w[lane >> 4][lane & 15] = 1.0f;
+    if (lane < G) {
+      const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + lane;
+      float M2 = -INFINITY;
+      for (int j = 0; j < num_splits; ++j) M2 = fmaxf(M2, a.part_lse[bh * num_splits + j] * kLog2e);
+      float S2 = 0.0f;
+      for (int j = 0; j < num_splits; ++j) {
+        const float l2 = a.part_lse[bh * num_splits + j] * kLog2e;
+        S2 += (l2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(l2 - M2);
+      }
+      const float own = a.part_lse[bh * num_splits + split] * kLog2e;
+      const float wj = (own == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(own - (M2 + log2f(S2)));
+      lds_lse[lane] = wj > 0.0f ? a.prob_scale / wj : 0.0f;
+    }
+  } else if (wave == 0) {
     const int w = lane >> 4, r = lane & 15;
     const float mv = lds_m[w][r];
     float M = mv;
@@ -689,6 +847,13 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
     if (lane < G) lds_lse[lane] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
   }
   __syncthreads();
+  if constexpr (PM == 1) {   // pass 1 writes the split's lse only
+    if (threadIdx.x < G) {
+      const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + threadIdx.x;
+      a.part_lse[bh * num_splits + split] = lds_lse[threadIdx.x];
+    }
+    return;
+  }
   const bool direct = FUSED && num_splits == 1;   // no partials needed
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, d = idx % D;
@@ -697,7 +862,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
     for (int w = 0; w < kWaves; ++w)
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) num += lds_w[w][s * G + h] * lds_o[w][s * G + h][d];
-    const float o = num * vscale;
+    const float o = (PM == 2) ? num * vscale * lds_lse[h] : num * vscale;
     const float lse = lds_lse[h];
     const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + h;
     if (direct) {
@@ -710,7 +875,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
         if (d == 0) __hip_atomic_store(a.part_lse + po, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
         a.part_o[po * D + d] = o;
-        if (d == 0) a.part_lse[po] = lse;
+        if (PM == 0 && d == 0) a.part_lse[po] = lse;   // pass 2 keeps pass 1's lse
       }
     }
   }
@@ -743,48 +908,54 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   }
 }
 
-template <int KVF, int G, int D, bool QF32, int PSPLIT, int VL>
+template <int KVF, int G, int D, bool QF32, int PSPLIT, int VL, int PM>
 hipError_t launch_v(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
   dim3 grid(p.s, a.Hkv, a.B);
-  if (fo != nullptr)
-    hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, true, VL>), grid, dim3(kThreads), 0, st, a, p.s, *fo);
-  else
-    hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, false, VL>), grid, dim3(kThreads), 0, st, a, p.s,
-                       FusedOut{});
+  if constexpr (PM == 0) {
+    if (fo != nullptr) {
+      hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, true, VL, 0>), grid, dim3(kThreads), 0, st, a, p.s, *fo);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, false, VL, PM>), grid, dim3(kThreads), 0, st, a, p.s,
+                     FusedOut{});
   return hipGetLastError();
 }
 
-template <int KVF, int G, int D, bool QF32, int PSPLIT>
+template <int KVF, int G, int D, bool QF32, int PSPLIT, int PM>
 hipError_t launch_t(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
-  if constexpr (D == 128) {
-    if (a.v_layout == KVQ_PLANE_TOKEN4) return launch_v<KVF, G, D, QF32, PSPLIT, KVQ_PLANE_TOKEN4>(a, p, fo, st);
+  if constexpr (D == 128 && PM != 1) {   // pass 1 reads no V
+    if (a.v_layout == KVQ_PLANE_TOKEN4) return launch_v<KVF, G, D, QF32, PSPLIT, KVQ_PLANE_TOKEN4, PM>(a, p, fo, st);
   }
-  return launch_v<KVF, G, D, QF32, PSPLIT, KVQ_PLANE_ROWS>(a, p, fo, st);
+  return launch_v<KVF, G, D, QF32, PSPLIT, KVQ_PLANE_ROWS, PM>(a, p, fo, st);
 }
 
-template <int KVF, int G, int D>
+template <int KVF, int G, int D, int PM>
 hipError_t launch_q(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
-  // fp32 queries select the fp32-accuracy path (hi/lo split of Q and P)
-  if (a.q_dtype == KVQ_F32) return launch_t<KVF, G, D, true, 2>(a, p, fo, st);
-  return launch_t<KVF, G, D, false, 1>(a, p, fo, st);
+  if constexpr (PM == 2) return launch_t<KVF, G, D, false, 1, 2>(a, p, fo, st);   // reads no Q
+  // fp32 queries select the fp32-accuracy path (hi/lo split of Q, and of P
+  // when P is not quantized)
+  if (a.q_dtype == KVQ_F32) return launch_t<KVF, G, D, true, (PM == 0 ? 2 : 1), PM>(a, p, fo, st);
+  return launch_t<KVF, G, D, false, 1, PM>(a, p, fo, st);
 }
 
-template <int KVF, int D>
+template <int KVF, int D, int PM>
 hipError_t launch_g(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_q<KVF, 1, D>(a, p, fo, st);
-    case 2: return launch_q<KVF, 2, D>(a, p, fo, st);
-    case 4: return launch_q<KVF, 4, D>(a, p, fo, st);
-    case 8: return launch_q<KVF, 8, D>(a, p, fo, st);
-    case 16: return launch_q<KVF, 16, D>(a, p, fo, st);
+    case 1: return launch_q<KVF, 1, D, PM>(a, p, fo, st);
+    case 2: return launch_q<KVF, 2, D, PM>(a, p, fo, st);
+    case 4: return launch_q<KVF, 4, D, PM>(a, p, fo, st);
+    case 8: return launch_q<KVF, 8, D, PM>(a, p, fo, st);
+    case 16: return launch_q<KVF, 16, D, PM>(a, p, fo, st);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int PM>
 hipError_t dispatch(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
   if (a.kv_format == KVQ_NVFP4)
-    return a.D == 128 ? launch_g<KVQ_NVFP4, 128>(a, p, fo, st) : launch_g<KVQ_NVFP4, 64>(a, p, fo, st);
-  return a.D == 128 ? launch_g<KVQ_FP8E4M3, 128>(a, p, fo, st) : launch_g<KVQ_FP8E4M3, 64>(a, p, fo, st);
+    return a.D == 128 ? launch_g<KVQ_NVFP4, 128, PM>(a, p, fo, st) : launch_g<KVQ_NVFP4, 64, PM>(a, p, fo, st);
+  return a.D == 128 ? launch_g<KVQ_FP8E4M3, 128, PM>(a, p, fo, st) : launch_g<KVQ_FP8E4M3, 64, PM>(a, p, fo, st);
 }
 
 }  // namespace
@@ -802,13 +973,19 @@ bool gqa_supported(int kv_format, int G, int D, int q_dtype) {
 }
 
 hipError_t launch_decode_gqa(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
-  return dispatch(a, p, nullptr, st);
+  return dispatch<0>(a, p, nullptr, st);
+}
+
+hipError_t launch_decode_fp8p(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
+  hipError_t e = dispatch<1>(a, p, nullptr, st);   // scores + split lse
+  if (e == hipSuccess) e = dispatch<2>(a, p, nullptr, st);   // quantized P . V
+  return e;
 }
 
 hipError_t launch_decode_gqa_fused(const kvq_decode_args& a, const DecodePlan& p, void* out, int out_dtype,
                                    const float* out_scale, float* lse_out, int* counters, hipStream_t st) {
   FusedOut fo{out, out_dtype, out_scale, lse_out, counters};
-  return dispatch(a, p, &fo, st);
+  return dispatch<0>(a, p, &fo, st);
 }
 
 }  // namespace kvq

@@ -155,15 +155,23 @@ def gpu_pack(inp, fmt, v_layout=0):
     return kp, vp, ka, va, lens
 
 
-def gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.bfloat16, out_scale=None, with_lse=False, fused=False):
+def gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.bfloat16, out_scale=None, with_lse=False, fused=False,
+               prob_scale=None):
+    """prob_scale: None for exact probabilities, else the FP8-P path."""
     k_ = K()
     B, Hq, D = inp.B, inp.Hq, inp.D
     cap = 64
     part_o = torch.empty(B * Hq * cap * D, dtype=torch.float32, device=DEV)
     part_lse = torch.empty(B * Hq * cap, dtype=torch.float32, device=DEV)
     q = inp.q.to(DEV)
+    fp8p = {}
+    if prob_scale is not None:
+        n = k_.kvq_fp8p_scratch_floats(B, Hq, cap, inp.Lmax)
+        # NaN-filled: a score read that pass 1 did not write would show up
+        fp8p = dict(quantize_p=True, prob_scale=prob_scale,
+                    p_scratch=torch.full((max(n, 4),), float("nan"), dtype=torch.float32, device=DEV))
     args = k_.make_decode_args(q, kp, vp, lens, max_kv_len=inp.Lmax, softmax_scale=inp.softmax_scale,
-                               num_splits=s, part_o=part_o, part_lse=part_lse)
+                               num_splits=s, part_o=part_o, part_lse=part_lse, **fp8p)
     out = torch.empty(B, Hq, D, dtype=out_dtype, device=DEV)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV) if with_lse else None
     if fused:

@@ -73,7 +73,8 @@ def test_auto_split_rejects_bad_args(K):
 
 
 def test_fp8p_scratch_size(K):
-    assert K.kvq_fp8p_scratch_floats(2, 4, 3, 100) == 2 * 4 * (100 + 6 + 2)
+    assert K.kvq_fp8p_scratch_floats(2, 4, 3, 100) == 2 * 4 * 100
+    assert K.kvq_fp8p_scratch_floats(2, 4, 3, 101) == 2 * 4 * 104
     assert K.kvq_fp8p_scratch_floats(0, 4, 3, 100) == 0
 
 
