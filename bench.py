@@ -49,9 +49,11 @@ def parse():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
-    ap.add_argument("--workload", choices=["gqa32k", "mla"], default="gqa32k",
+    ap.add_argument("--workload", choices=["gqa32k", "mla", "fp8"], default="gqa32k",
                     help="gqa32k: the metric's configuration (default); mla: DeepSeek-V2 per-rank MLA, "
-                         "B=32, 16 heads, NVFP4 latent 512 + bf16 rope 64, kv 8192")
+                         "B=32, 16 heads, NVFP4 latent 512 + bf16 rope 64, kv 8192; fp8: per-tensor FP8 KV, "
+                         "B=64, Hq=32, Hkv=8, D=128, ragged kv_len ~ U{512..4096}, with and without FP8 "
+                         "probabilities")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of the cache's size (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -237,6 +239,95 @@ def run_mla(args):
     print(json.dumps(res), flush=True)
 
 
+FP8_B, FP8_LO, FP8_HI = 64, 512, 4096
+FP8_BYTES_PER_TOKEN_HEAD = 2 * D   # K and V E4M3 codes
+
+
+def run_fp8(args):
+    """FP8 KV decode over ragged requests: one step = attn_decode_splitkv +
+    combine (K rows, V TOKEN4), timed with exact probabilities, with FP8
+    probabilities (prob_scale 1/448: two split passes + combine) and with
+    FP8 output.  Rotation of >= 1 GiB of cache copies."""
+    import torch
+    import kvq_synth
+    import quantized_kv_cache_nvfp4_amd as K
+
+    K._lib.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating FP8 ragged inputs")
+    inp = kvq_synth.fp8_ragged(B=FP8_B, lo=FP8_LO, hi=FP8_HI)
+    lens = torch.from_numpy(inp.kv_lens).to(dev)
+    k, v = inp.k.to(dev), inp.v.to(dev)
+    ka, va = K.kvq_amax(k, lens), K.kvq_amax(v, lens)
+    kp0 = K.kvq_pack_fp8(k, ka)
+    vp0 = K.kvq_pack_fp8(v, va, layout=K.KVQ_PLANE_TOKEN4)
+    del k, v
+    q = inp.q.to(dev)
+    per_copy = kp0.codes.numel() + vp0.codes.numel()
+    n_copies = max(2, math.ceil(args.rotate_gib * (1 << 30) / per_copy))
+    log(f"rotation: {n_copies} cache copies x {per_copy / 1e6:.1f} MB (allocated at kv {FP8_HI})")
+    copies = [(kp0, vp0)] + [(K.FP8Plane(kp0.codes.clone(), kp0.scale.clone(), kp0.layout),
+                              K.FP8Plane(vp0.codes.clone(), vp0.scale.clone(), vp0.layout))
+                             for _ in range(n_copies - 1)]
+    Hq, Hkv = inp.Hq, inp.Hkv
+    s = args.splits if args.splits > 0 else K.kvq_auto_num_splits(K.kvq_device_cu_count(), FP8_B, Hkv, FP8_HI, D, Hq)
+    part_o = torch.empty(FP8_B * Hq * s * D, dtype=torch.float32, device=dev)
+    part_lse = torch.empty(FP8_B * Hq * s, dtype=torch.float32, device=dev)
+    scratch = torch.empty(K.kvq_fp8p_scratch_floats(FP8_B, Hq, s, FP8_HI), dtype=torch.float32, device=dev)
+    out = torch.empty(FP8_B, Hq, D, dtype=torch.bfloat16, device=dev)
+    out8 = torch.empty(FP8_B, Hq, D, dtype=torch.uint8, device=dev)
+    out_scale = torch.full((1,), 4.0 / 448.0, dtype=torch.float32, device=dev)   # a given fp32 output scale
+
+    def mk(kc, vc, fp8p):
+        extra = dict(quantize_p=True, prob_scale=float(1.0 / 448.0), p_scratch=scratch) if fp8p else {}
+        return K.make_decode_args(q, kc, vc, lens, max_kv_len=FP8_HI, softmax_scale=inp.softmax_scale,
+                                  num_splits=s, part_o=part_o, part_lse=part_lse, **extra)
+
+    dargs = [mk(kc, vc, False) for kc, vc in copies]
+    pargs = [mk(kc, vc, True) for kc, vc in copies]
+
+    def step(i, a, o):
+        used = K.attn_decode_splitkv(a[i])
+        K.attn_decode_combine(part_o, part_lse, FP8_B, Hq, D, used, o, out_scale=out_scale)
+
+    for i in range(max(args.warmup, n_copies)):
+        step(i % n_copies, dargs, out)
+        step(i % n_copies, pargs, out)
+    torch.cuda.synchronize()
+    capture, timed, steps = graph_timer(torch, n_copies, args.steps)
+    ms = {"decode": timed(capture(lambda i: step(i, dargs, out))),
+          "decode_fp8_out": timed(capture(lambda i: step(i, dargs, out8))),
+          "decode_fp8p": timed(capture(lambda i: step(i, pargs, out))),
+          "split_kernel": timed(capture(lambda i: K.attn_decode_splitkv(dargs[i]))),
+          "fp8p_passes": timed(capture(lambda i: K.attn_decode_splitkv(pargs[i])))}
+    assert torch.isfinite(out.float()).all()
+    tokens = int(inp.kv_lens.astype("int64").sum())
+    algo = tokens * Hkv * FP8_BYTES_PER_TOKEN_HEAD
+    algo_p = algo + tokens * Hq * 4 * 2   # + the spilled scores, written once and read once
+    kernel_us = ms["split_kernel"] * 1e3
+    achieved = algo / (kernel_us * 1e-6) / 1e9
+    res = {
+        "metric": "us/decode step + achieved HBM GB/s, FP8-KV split-KV decode B=64 GQA4:1 ragged 512..4096",
+        "value": round(ms["decode"] * 1e3, 3), "unit": "us/step", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms["decode"], 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16 MFMA, fp32 accumulate (FP8 E4M3 KV)",
+        "data": "synthetic",
+        "config": {"workload": "FP8 per-tensor KV decode, Llama-3-8B attention shape, ragged", "B": FP8_B,
+                   "Hq": Hq, "Hkv": Hkv, "head_dim": D, "kv_len": f"U{{{FP8_LO}..{FP8_HI}}}",
+                   "tokens": tokens, "splits": s, "out_dtype": "bf16", "v_layout": "token4",
+                   "prob_scale": "1/448", "rotation_copies": n_copies},
+        "hbm_gbps_step": round(algo / (ms["decode"] * 1e-3) / 1e9, 1),
+        "step_us": {k_: round(v_ * 1e3, 3) for k_, v_ in ms.items()},
+        "fp8p_hbm_gbps": round(algo_p / (ms["fp8p_passes"] * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "k_decode_gqa<FP8,G=4,D=128> (split kernel, partials)",
+                     "kernel_us_mean": round(kernel_us, 3), "algorithmic_bytes": algo},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -248,6 +339,9 @@ def main():
         return
     if args.workload == "mla":
         run_mla(args)
+        return
+    if args.workload == "fp8":
+        run_fp8(args)
         return
     import numpy as np
     import torch

@@ -202,11 +202,14 @@ int kvq_auto_num_splits(int32_t num_cus, int32_t B, int32_t programs_per_req, in
   const int64_t by_len = (static_cast<int64_t>(max_kv_len) + 255) / 256;
   if (s > by_len) s = by_len;
   // 3) the partials (written and read once: 8 bytes per element) stay under
-  //    a sixth of the packed KV bytes (about 9/8 * Dv bytes per token and
-  //    program for NVFP4 K and V)
+  //    a third of the packed KV bytes (about 9/8 * Dv bytes per token and
+  //    program for NVFP4 K and V).  Only the wide-head single-program case
+  //    (the MLA latent, 16 heads x 512 per request) comes near this bound;
+  //    on MI355X its decode step measured fastest at two work-groups per
+  //    compute unit, where the partials are about a third of the KV bytes.
   const double kv_bytes = static_cast<double>(base) * max_kv_len * (9.0 * Dv / 8.0);
   const double per_split = static_cast<double>(B) * Hq * (Dv + 1) * 8.0;
-  const int64_t by_traffic = static_cast<int64_t>(kv_bytes / (6.0 * per_split));
+  const int64_t by_traffic = static_cast<int64_t>(kv_bytes / (3.0 * per_split));
   if (s > by_traffic) s = by_traffic;
   if (s > 64) s = 64;
   if (s < 1) s = 1;

@@ -196,7 +196,26 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
+  const int hq0 = kvh * G;
+  const int my_h = c % G;
+  const int my_sub = c / G;
 
+  // ---- prologue loads, issued together so that they cost one memory round
+  // trip: the query words of this lane (vector), the request's length and
+  // the two tensor scales (scalar).  The first tile's loads need the length.
+  constexpr int kQRaw = QF32 ? 2 * Gm::kQkJ : Gm::kQkJ;   // 16-byte query words per lane
+  uint4 qraw[kQRaw];
+  if constexpr (PM != 2) {
+    // lane (g, c) holds Q[h = c % G][g*QKE + 8j + e] (q rows and strides are 16-byte aligned)
+    const int64_t qb = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(hq0 + my_h) * a.q_sh +
+                       g * Gm::kQkElems;
+    const uint4* qp = QF32 ? reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + qb)
+                           : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qb);
+#pragma unroll
+    for (int j = 0; j < kQRaw; ++j) qraw[j] = qp[j];
+  }
+  const float kscale = *a.k_scale;
+  const float vscale = *a.v_scale;
   int L = a.kv_lens[b];
   L = L < a.max_kv_len ? L : a.max_kv_len;
   L = L > 0 ? L : 0;
@@ -205,12 +224,6 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   const int cs = split * chunk;
   const int ce = (cs + chunk < L) ? cs + chunk : L;
 
-  const int hq0 = kvh * G;
-  const int my_h = c % G;
-  const int my_sub = c / G;
-
-  const float kscale = *a.k_scale;
-  const float vscale = *a.v_scale;
   const float qk_scale = a.softmax_scale * kscale * kLog2e;
 
   float m_run = -INFINITY;  // running max of row c (log2 domain)
@@ -221,24 +234,21 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
 
   const int ntiles = cs < ce ? (ce - cs + TT - 1) / TT : 0;
 
-  if (wave < ntiles) {
+  {   // (waves without a tile run through with empty loads and no loop iterations)
     // ---- query operand: lane (g, c) holds Q[h = c % G][g*QKE + 8j + e]
     f16x8 qop[NQ][Gm::kQkJ];
     if constexpr (PM != 2) {
-      // 16-byte vector loads (q rows and strides are 16-byte aligned)
-      const int64_t qb = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(hq0 + my_h) * a.q_sh +
-                         g * Gm::kQkElems;
 #pragma unroll
       for (int j = 0; j < Gm::kQkJ; ++j) {
         float x[8];
         if constexpr (QF32) {
-          const float* qp = static_cast<const float*>(a.q) + qb + 8 * j;
-          const float4 x0 = *reinterpret_cast<const float4*>(qp);
-          const float4 x1 = *reinterpret_cast<const float4*>(qp + 4);
-          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-          x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+          const uint4 w0 = qraw[2 * j], w1 = qraw[2 * j + 1];
+          x[0] = __uint_as_float(w0.x); x[1] = __uint_as_float(w0.y);
+          x[2] = __uint_as_float(w0.z); x[3] = __uint_as_float(w0.w);
+          x[4] = __uint_as_float(w1.x); x[5] = __uint_as_float(w1.y);
+          x[6] = __uint_as_float(w1.z); x[7] = __uint_as_float(w1.w);
         } else {
-          const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qb + 8 * j);
+          const uint4 w = qraw[j];
           const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {   // bf16 pair -> two fp32 (exact)
