@@ -266,8 +266,11 @@ typedef struct {
  * contiguous chunk of one (request, kv head), dequantizes in registers,
  * computes the scores, keeps an online softmax (running max and
  * denominator) and accumulates P.V; it writes per-split partials.
- * Chunking: c = ceil(L_b / s) rounded up to the kernel tile; split j covers
- * [j c, min((j+1) c, L_b)).
+ * Chunking: c = ceil(max_kv_len / s) rounded up to the kernel tile; split j
+ * covers [j c, min((j+1) c, L_b)) (empty when j c >= L_b).  The chunk
+ * depends on kernel arguments only, so the first tile is requested together
+ * with L_b; rows of the planes up to max_kv_len may be read, and tokens at
+ * or past L_b never contribute.
  * With quantize_p = 1 (GQA only; vLLM PR #15734 "[Quantization][FP8] Add
  * support for FP8 models with input_scale for output projection and QK
  * quantization", item 2) the probabilities are the normalized softmax over

@@ -200,9 +200,17 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   const int my_h = c % G;
   const int my_sub = c / G;
 
+  // ---- chunking: c = ceil(max_kv_len / s) rounded up to the tile; split j
+  // covers [j c, min((j+1) c, L)).  It depends on kernel arguments only, so
+  // the tile addresses are known before the request length is read.
+  int chunk = (a.max_kv_len + num_splits - 1) / num_splits;
+  chunk = (chunk + TT - 1) / TT * TT;
+  const int cs = split * chunk;
+  int ce_ld = (cs + chunk < a.max_kv_len) ? cs + chunk : a.max_kv_len;   // load bound (rows present)
+
   // ---- prologue loads, issued together so that they cost one memory round
-  // trip: the query words of this lane (vector), the request's length and
-  // the two tensor scales (scalar).  The first tile's loads need the length.
+  // trip: the query words of this lane (vector), the first K tile, the
+  // request's length and the two tensor scales (scalar).
   constexpr int kQRaw = QF32 ? 2 * Gm::kQkJ : Gm::kQkJ;   // 16-byte query words per lane
   uint4 qraw[kQRaw];
   if constexpr (PM != 2) {
@@ -214,15 +222,79 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
 #pragma unroll
     for (int j = 0; j < kQRaw; ++j) qraw[j] = qp[j];
   }
+  // per-(request, kv head) plane bases
+  const int64_t head_row = static_cast<int64_t>(b) * a.kv_sb + static_cast<int64_t>(kvh) * a.kv_sh;
+  const uint8_t* kc = a.k_codes + head_row * Gm::kRowBytes;
+  const uint8_t* vc = a.v_codes + head_row * Gm::kRowBytes;
+  const uint8_t* ksc = (KVF == KVQ_NVFP4) ? a.k_scales + head_row * Gm::kScaleBytes : kc;
+  const uint8_t* vsc = (KVF == KVQ_NVFP4) ? a.v_scales + head_row * Gm::kScaleBytes : vc;
+  // token stride in rows (always 1 with a TOKEN4 V plane, K and V share it)
+  const int st = (VL == KVQ_PLANE_TOKEN4) ? 1 : static_cast<int>(a.kv_st);
+  constexpr int RB = Gm::kRowBytes;
+  constexpr int SB = Gm::kScaleBytes;
+
+  // Every load goes through a buffer resource whose base is the tile's
+  // first token and whose size ends at the chunk end ce (for the first K
+  // tile, issued before the request length is known, at the end of the
+  // chunk's rows in the plane): lanes whose token is at or past that end
+  // read zeros (hardware range check, nothing is fetched), and the
+  // prefetch past a wave's last tile touches no memory.
+  // Lane offsets are fixed for the whole chunk, so the loop does no
+  // address arithmetic.  (All byte offsets stay below 2^31.)
+  const int lk = c * st * RB + g * (Gm::kKWords * 4);          // K codes: token c, quarter g
+  const int lks = c * st * SB + (D == 128 ? 2 * g : g);          // K scales of that quarter
+  const int lv = 4 * g * st * RB + c * Gm::kVBytes;              // V codes (row layout)
+  const int lvs = 4 * g * st * SB + (c * Gm::kPvElems) / 16;     // V scales (row layout)
+  constexpr int GB = 4 * RB;                // TOKEN4: bytes per 4-token group (codes)
+  constexpr int GS = 4 * SB;                //         bytes per 4-token group (scales)
+  constexpr int CB = 4 * Gm::kVBytes;       //         this lane's run inside a group
+  const int lvt = g * GB + c * CB;
+  const int lvts = g * GS + (c / 2) * 4;
+
+  // (the lane offsets are re-materialized per call, so that the constant
+  // parts fold into the loads' immediate offsets instead of occupying
+  // loop-invariant registers)
+  auto opaque = [](int x) { asm volatile("" : "+v"(x)); return x; };
+  auto load_ktile = [&](KT& R, int tile) {
+    const int tb = cs + tile * TT;
+    const int lk_ = opaque(lk), lks_ = opaque(lks);
+    const int nv = ce_ld - tb;
+    const int64_t base = static_cast<int64_t>(tb) * st;
+    const Rsrc rk = make_rsrc(kc + base * RB, nv * st * RB);
+    const Rsrc rks = make_rsrc(ksc + base * SB, nv * st * SB);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int o = lk_ + u * 16 * st * RB;
+      if constexpr (Gm::kKWords == 8) {
+        const u32x4 x0 = ld128(rk, o), x1 = ld128(rk, o + 16);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) { R.k[u][w] = x0[w]; R.k[u][4 + w] = x1[w]; }
+      } else if constexpr (Gm::kKWords == 4) {
+        const u32x4 x0 = ld128(rk, o);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) R.k[u][w] = x0[w];
+      } else {
+        const u32x2 x0 = ld64(rk, o);
+        R.k[u][0] = x0[0]; R.k[u][1] = x0[1];
+      }
+      if constexpr (KVF == KVQ_NVFP4) {
+        const int os = lks_ + u * 16 * st * SB;
+        R.ks[u] = (D == 128) ? ld16(rks, os) : ld8(rks, os);
+      }
+    }
+  };
+  // the first K tile of this wave, loaded before the request length arrives
+  // (scores of tokens at or past the request's end are masked to -inf)
+  KT KA, KB;
+  if constexpr (PM != 2 && NG > 1) load_ktile(KA, wave);
+
   const float kscale = *a.k_scale;
   const float vscale = *a.v_scale;
   int L = a.kv_lens[b];
   L = L < a.max_kv_len ? L : a.max_kv_len;
   L = L > 0 ? L : 0;
-  int chunk = (L + num_splits - 1) / num_splits;
-  chunk = (chunk + TT - 1) / TT * TT;
-  const int cs = split * chunk;
   const int ce = (cs + chunk < L) ? cs + chunk : L;
+  ce_ld = ce;   // every later load stops at the request's end
 
   const float qk_scale = a.softmax_scale * kscale * kLog2e;
 
@@ -269,65 +341,6 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
       }
     }
 
-    // per-(request, kv head) plane bases
-    const int64_t head_row = static_cast<int64_t>(b) * a.kv_sb + static_cast<int64_t>(kvh) * a.kv_sh;
-    const uint8_t* kc = a.k_codes + head_row * Gm::kRowBytes;
-    const uint8_t* vc = a.v_codes + head_row * Gm::kRowBytes;
-    const uint8_t* ksc = (KVF == KVQ_NVFP4) ? a.k_scales + head_row * Gm::kScaleBytes : kc;
-    const uint8_t* vsc = (KVF == KVQ_NVFP4) ? a.v_scales + head_row * Gm::kScaleBytes : vc;
-    // token stride in rows (always 1 with a TOKEN4 V plane, K and V share it)
-    const int st = (VL == KVQ_PLANE_TOKEN4) ? 1 : static_cast<int>(a.kv_st);
-    constexpr int RB = Gm::kRowBytes;
-    constexpr int SB = Gm::kScaleBytes;
-
-    // Every load goes through a buffer resource whose base is the tile's
-    // first token and whose size ends at the chunk end ce: lanes whose token
-    // is at or past ce read zeros (hardware range check, nothing is
-    // fetched), and the prefetch past a wave's last tile touches no memory.
-    // Lane offsets are fixed for the whole chunk, so the loop does no
-    // address arithmetic.  (All byte offsets stay below 2^31.)
-    const int lk = c * st * RB + g * (Gm::kKWords * 4);          // K codes: token c, quarter g
-    const int lks = c * st * SB + (D == 128 ? 2 * g : g);          // K scales of that quarter
-    const int lv = 4 * g * st * RB + c * Gm::kVBytes;              // V codes (row layout)
-    const int lvs = 4 * g * st * SB + (c * Gm::kPvElems) / 16;     // V scales (row layout)
-    constexpr int GB = 4 * RB;                // TOKEN4: bytes per 4-token group (codes)
-    constexpr int GS = 4 * SB;                //         bytes per 4-token group (scales)
-    constexpr int CB = 4 * Gm::kVBytes;       //         this lane's run inside a group
-    const int lvt = g * GB + c * CB;
-    const int lvts = g * GS + (c / 2) * 4;
-
-    // (the lane offsets are re-materialized per call, so that the constant
-    // parts fold into the loads' immediate offsets instead of occupying
-    // loop-invariant registers)
-    auto opaque = [](int x) { asm volatile("" : "+v"(x)); return x; };
-    auto load_ktile = [&](KT& R, int tile) {
-      const int tb = cs + tile * TT;
-      const int lk_ = opaque(lk), lks_ = opaque(lks);
-      const int nv = ce - tb;
-      const int64_t base = static_cast<int64_t>(tb) * st;
-      const Rsrc rk = make_rsrc(kc + base * RB, nv * st * RB);
-      const Rsrc rks = make_rsrc(ksc + base * SB, nv * st * SB);
-#pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        const int o = lk_ + u * 16 * st * RB;
-        if constexpr (Gm::kKWords == 8) {
-          const u32x4 x0 = ld128(rk, o), x1 = ld128(rk, o + 16);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) { R.k[u][w] = x0[w]; R.k[u][4 + w] = x1[w]; }
-        } else if constexpr (Gm::kKWords == 4) {
-          const u32x4 x0 = ld128(rk, o);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) R.k[u][w] = x0[w];
-        } else {
-          const u32x2 x0 = ld64(rk, o);
-          R.k[u][0] = x0[0]; R.k[u][1] = x0[1];
-        }
-        if constexpr (KVF == KVQ_NVFP4) {
-          const int os = lks_ + u * 16 * st * SB;
-          R.ks[u] = (D == 128) ? ld16(rks, os) : ld8(rks, os);
-        }
-      }
-    };
     auto load_vtile = [&](VT& R, int tile) {
       const int tb = cs + tile * TT;
       const int lvt_ = opaque(lvt), lvts_ = opaque(lvts), lv_ = opaque(lv), lvs_ = opaque(lvs);
@@ -635,7 +648,6 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
     // boundaries.  Loads past the wave's last tile are empty.
     const int nw = (ntiles - wave + kWaves - 1) / kWaves;   // this wave's tiles
     auto tile_of = [&](int k) { return wave + k * kWaves; };
-    KT KA, KB;
     VT VA, VB;
     auto group = [&](int k0, int n, auto full) {
       constexpr bool kFull = decltype(full)::value;
@@ -700,8 +712,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
           for (int i = 0; i < 4; ++i) l_run += __builtin_amdgcn_exp2f(sc[x][i] - m_ref);
       };
       float sc[NACC][4];
-      if constexpr (NG > 1) {   // two K register sets: the next tile loads during this one
-        load_ktile(KA, tile_of(0));
+      if constexpr (NG > 1) {   // two K register sets: the next tile loads during this one (KA: tile 0, loaded above)
         for (int k = 0; k < nw; k += 2) {
           load_ktile(KB, tile_of(k + 1));
           __builtin_amdgcn_sched_barrier(0);
@@ -782,8 +793,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
           pv_tile(VA, ph, pl);
         }
       }
-    } else if constexpr (NG > 1) {
-      load_ktile(KA, tile_of(0));
+    } else if constexpr (NG > 1) {   // (KA holds tile 0, loaded above)
       int k0 = 0;
       for (; k0 + NG <= nw; k0 += NG) group(k0, NG, std::integral_constant<bool, true>{});
       if (k0 < nw) group(k0, nw - k0, std::integral_constant<bool, false>{});

@@ -80,41 +80,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
   const int split = blockIdx.x;
   const int b = blockIdx.y;
 
-  int L = a.kv_lens[b];
-  L = L < a.max_kv_len ? L : a.max_kv_len;
-  L = L > 0 ? L : 0;
-  int chunk = (L + num_splits - 1) / num_splits;
+  // chunking from kernel arguments only: c = ceil(max_kv_len / s) rounded
+  // up to the tile, split j covers [j c, min((j+1) c, L)); the first tiles'
+  // addresses are known before the request length is read
+  int chunk = (a.max_kv_len + num_splits - 1) / num_splits;
   chunk = (chunk + kT - 1) / kT * kT;
   const int cs = split * chunk;
-  const int ce = (cs + chunk < L) ? cs + chunk : L;
-  const int ntiles = cs < ce ? (ce - cs + kT - 1) / kT : 0;
-
-  const float s_t = *a.k_scale;
-  const float sc_lat = a.softmax_scale * s_t * kLog2e;   // latent scores carry the tensor scale
-  const float sc_rope = a.softmax_scale * kLog2e;
-
-  // ---- query operands, lane (g, c) = head c:
-  //   latent MFMA j (0..7): dims 256 dh + 64 g + 8 j + e; rope: 32 dh + 8 g + e
-  f16x8 qop[8];
-  bf16x8 qr;
-  {
-    const uint16_t* qc = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * a.q_sb +
-                         static_cast<int64_t>(c) * a.q_sh + 256 * dh + 64 * g;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint4 w = *reinterpret_cast<const uint4*>(qc + 8 * j);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      f16x2 h[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)   // bf16 pair -> fp32 (exact) -> f16 (exact in f16's normal range)
-        h[k] = f16x2{static_cast<_Float16>(__uint_as_float(ws[k] << 16)),
-                     static_cast<_Float16>(__uint_as_float(ws[k] & 0xFFFF0000u))};
-      qop[j] = cat4(h[0], h[1], h[2], h[3]);
-    }
-    const uint16_t* qrp = static_cast<const uint16_t*>(a.q_rope) + static_cast<int64_t>(b) * a.qr_sb +
-                          static_cast<int64_t>(c) * a.qr_sh + 32 * dh + 8 * g;
-    qr = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrp));
-  }
+  int ce_ld = (cs + chunk < a.max_kv_len) ? cs + chunk : a.max_kv_len;   // load bound (rows present)
 
   // per-request plane bases (rows of the latent, scale and rope planes)
   const int64_t row0 = static_cast<int64_t>(b) * a.kv_sb;
@@ -123,22 +95,16 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
   const uint8_t* csc = a.k_scales + row0 * kSRow;
   const uint8_t* cr = static_cast<const uint8_t*>(a.k_rope) + row0 * (kDr * 2);
 
-  float m_run = -INFINITY;   // running max of head c (log2 domain), the same in every wave
-  float l_run = 0.0f;        // this lane's share of head c's denominator (its 8 tokens per tile)
-  f32x4 acc_o[8];            // O^T rows d = 128*wave + 16*jj + 4g + i, column head c
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) acc_o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   // loads of one tile: token c; latent bytes [128 dh + 32 g, +32), scale
   // bytes [16 dh + 4 g, +4), rope bytes [64 dh + 16 g, +16).  Tokens at or
-  // past the chunk end read zeros; a tile past the chunk reads nothing.
+  // past the load bound ce_ld read zeros; a tile past it reads nothing.
   struct Raw {
     u32x4 cw0, cw1, rw;
     uint32_t sw;
   };
   auto load_tile = [&](Raw& R, int tile) {
     const int t0 = cs + tile * kT + 16 * th;
-    const int nv = ce - t0;
+    const int nv = ce_ld - t0;
     const Rsrc rc_ = make_rsrc(cc + static_cast<int64_t>(t0) * st * kRow, nv * st * kRow);
     const Rsrc rs_ = make_rsrc(csc + static_cast<int64_t>(t0) * st * kSRow, nv * st * kSRow);
     const Rsrc rr_ = make_rsrc(cr + static_cast<int64_t>(t0) * st * (kDr * 2), nv * st * (kDr * 2));
@@ -147,10 +113,73 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     R.sw = ld32(rs_, c * st * kSRow + 16 * dh + 4 * g);
     R.rw = ld128(rr_, c * st * (kDr * 2) + 64 * dh + 16 * g);
   };
+  // ---- query words, lane (g, c) = head c:
+  //   latent MFMA j (0..7): dims 256 dh + 64 g + 8 j + e; rope: 32 dh + 8 g + e
+  uint4 qraw[8], qrraw;
+  {
+    const uint16_t* qc = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * a.q_sb +
+                         static_cast<int64_t>(c) * a.q_sh + 256 * dh + 64 * g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qraw[j] = *reinterpret_cast<const uint4*>(qc + 8 * j);
+    const uint16_t* qrp = static_cast<const uint16_t*>(a.q_rope) + static_cast<int64_t>(b) * a.qr_sb +
+                          static_cast<int64_t>(c) * a.qr_sh + 32 * dh + 8 * g;
+    qrraw = *reinterpret_cast<const uint4*>(qrp);
+  }
+
+  // the first kAhead tiles, requested with the query and the request length
+  // (one memory round trip); kAhead tiles are in flight while one computes:
+  // buffer (tile mod kAhead+1) holds tile's data.  Tiles past the chunk load
+  // nothing.
+  Raw buf[kAhead + 1];
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {
+    load_tile(buf[k], k);
+    __builtin_amdgcn_sched_barrier(0);   // issue order = tile order, so a wait for one tile spares the later ones
+  }
+
+  int L = a.kv_lens[b];
+  L = L < a.max_kv_len ? L : a.max_kv_len;
+  L = L > 0 ? L : 0;
+  const int ce = (cs + chunk < L) ? cs + chunk : L;
+  ce_ld = ce;   // later loads stop at the request's end
+  const int ntiles = cs < ce ? (ce - cs + kT - 1) / kT : 0;
+
+  const float s_t = *a.k_scale;
+  const float sc_lat = a.softmax_scale * s_t * kLog2e;   // latent scores carry the tensor scale
+  const float sc_rope = a.softmax_scale * kLog2e;
+
+  f16x8 qop[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t ws[4] = {qraw[j].x, qraw[j].y, qraw[j].z, qraw[j].w};
+    f16x2 h[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)   // bf16 pair -> fp32 (exact) -> f16 (exact in f16's normal range)
+      h[k] = f16x2{static_cast<_Float16>(__uint_as_float(ws[k] << 16)),
+                   static_cast<_Float16>(__uint_as_float(ws[k] & 0xFFFF0000u))};
+    qop[j] = cat4(h[0], h[1], h[2], h[3]);
+  }
+  const bf16x8 qr = __builtin_bit_cast(bf16x8, qrraw);
+
+  float m_run = -INFINITY;   // running max of head c (log2 domain), the same in every wave
+  float l_run = 0.0f;        // this lane's share of head c's denominator (its 8 tokens per tile)
+  f32x4 acc_o[8];            // O^T rows d = 128*wave + 16*jj + 4g + i, column head c
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) acc_o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   auto process = [&](const Raw& cur, int tile) {
     const int tb = cs + tile * kT;
-    const u32x4 cw0 = cur.cw0, cw1 = cur.cw1, rw = cur.rw;
-    const uint32_t sw = cur.sw;
+    u32x4 cw0 = cur.cw0, cw1 = cur.cw1, rw = cur.rw;
+    uint32_t sw = cur.sw;
+    // the chunk's last tile: rows of tokens at or past the request's end
+    // (read before the length was known) become zeros, so that the staged
+    // latent of masked tokens is 0 (their probability is 0)
+    if (tb + kT > ce && tb + 16 * th + c >= ce) {
+      cw0 = u32x4{0u, 0u, 0u, 0u};
+      cw1 = cw0;
+      rw = cw0;
+      sw = 0u;
+    }
 
     // ---- partial scores S^T[token][head] over this wave's halves; stage the f16 rows
     f32x4 acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
@@ -236,15 +265,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     __syncthreads();   // the tile's LDS may be overwritten
   };
 
-  // kAhead tiles are in flight while one computes: buffer (tile mod
-  // kAhead+1) holds tile's data; the loop is unrolled over the buffers so
-  // that each has fixed registers.  Tiles past the chunk load nothing.
-  Raw buf[kAhead + 1];
-#pragma unroll
-  for (int k = 0; k < kAhead; ++k) {
-    load_tile(buf[k], k);
-    __builtin_amdgcn_sched_barrier(0);   // issue order = tile order, so a wait for one tile spares the later ones
-  }
+  // the loop is unrolled over the buffers so that each has fixed registers
   for (int t0 = 0; t0 < ntiles; t0 += kAhead + 1) {
 #pragma unroll
     for (int u = 0; u <= kAhead; ++u) {
