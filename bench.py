@@ -133,6 +133,20 @@ def cpu_baseline(inp, reps):
                       f"attention; median {t:.2f} s/step; numpy elementwise single-threaded, BLAS threads {threads}"}
 
 
+def eager_timer(torch, fn, reps=5):
+    """Average time of fn() over `reps` back-to-back calls (HIP events on the
+    current stream, after one warm-up call), in microseconds."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
 def graph_timer(torch, n_copies, steps_wanted):
     """Capture fn(i) for every cache copy i into one HIP graph and time its
     replays with HIP events on the replay stream (ms per captured step)."""
@@ -262,6 +276,11 @@ def run_fp8(args):
     ka, va = K.kvq_amax(k, lens), K.kvq_amax(v, lens)
     kp0 = K.kvq_pack_fp8(k, ka)
     vp0 = K.kvq_pack_fp8(v, va, layout=K.KVQ_PLANE_TOKEN4)
+    elems = k.numel()
+    prep_us = {"amax_k": eager_timer(torch, lambda: K.kvq_amax(k, lens, out=ka)),
+               "pack_k_fp8_rows": eager_timer(torch, lambda: K.kvq_pack_fp8(k, ka, out=kp0)),
+               "pack_v_fp8_token4": eager_timer(torch, lambda: K.kvq_pack_fp8(v, va, out=vp0))}
+    prep_bytes = {"amax_k": elems * 2, "pack_k_fp8_rows": elems * 3, "pack_v_fp8_token4": elems * 3}
     del k, v
     q = inp.q.to(dev)
     per_copy = kp0.codes.numel() + vp0.codes.numel()
@@ -320,6 +339,8 @@ def run_fp8(args):
         "hbm_gbps_step": round(algo / (ms["decode"] * 1e-3) / 1e9, 1),
         "step_us": {k_: round(v_ * 1e3, 3) for k_, v_ in ms.items()},
         "fp8p_hbm_gbps": round(algo_p / (ms["fp8p_passes"] * 1e-3) / 1e9, 1),
+        "calibrate_pack": {k_: {"us": round(t, 2), "GB/s": round(prep_bytes[k_] / (t * 1e-6) / 1e9, 1)}
+                           for k_, t in prep_us.items()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "k_decode_gqa<FP8,G=4,D=128> (split kernel, partials)",
@@ -357,8 +378,17 @@ def main():
     q = inp.q.to(dev)
     k = inp.k.to(dev)
     v = inp.v.to(dev)
-    # calibration + bulk pack (untimed)
+    # calibration + bulk pack (outside the decode step; timed on their own)
     k_amax, v_amax = K.kvq_amax(k, kv_lens), K.kvq_amax(v, kv_lens)
+    kp_t = K.kvq_pack_nvfp4(k, k_amax)
+    vp_t = K.kvq_pack_nvfp4(v, v_amax, layout=K.KVQ_PLANE_TOKEN4)
+    elems = k.numel()
+    prep_us = {"amax_k": eager_timer(torch, lambda: K.kvq_amax(k, kv_lens, out=k_amax)),
+               "pack_k_nvfp4_rows": eager_timer(torch, lambda: K.kvq_pack_nvfp4(k, k_amax, out=kp_t)),
+               "pack_v_nvfp4_token4": eager_timer(torch, lambda: K.kvq_pack_nvfp4(v, v_amax, out=vp_t))}
+    prep_bytes = {"amax_k": elems * 2, "pack_k_nvfp4_rows": elems * 2 + elems * 9 // 16,
+                  "pack_v_nvfp4_token4": elems * 2 + elems * 9 // 16}
+    del kp_t, vp_t
     # K planes row-major; V planes in the TOKEN4 layout (per group of four
     # tokens, element-major with the four tokens' codes side by side)
     kp0 = K.kvq_pack_nvfp4(k, k_amax)
@@ -478,6 +508,8 @@ def main():
                    "v_layout": "token4", "rotation_copies": n_copies, "step_path": best},
         "hbm_gbps_step": round(algo_bytes / (step_us * 1e-6) / 1e9, 1),
         "step_us": {k: round(v * 1e3, 3) for k, v in ms.items()},
+        "calibrate_pack": {k_: {"us": round(t, 2), "GB/s": round(prep_bytes[k_] / (t * 1e-6) / 1e9, 1)}
+                           for k_, t in prep_us.items()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                      "kernel": "k_decode_gqa<NVFP4,G=4,D=128> (split kernel, partials)",

@@ -53,6 +53,58 @@ __device__ inline int64_t group_row(const Rows& r, int64_t i0, int64_t i1, int64
   return i0 * r.s0 + i1 * r.s1 + t0;  // row index of the group's first token
 }
 
+
+// ---------------------------------------------------------------- loads
+// n (<= N) consecutive elements starting at element offset off of x, as
+// fp32 (0 past n); 16-byte vector loads when the run is whole and aligned.
+template <int N>
+__device__ inline void load_run(const void* x, int dt, int64_t off, int n, float (&v)[N]) {
+  if (dt == KVQ_F32) {
+    const float* p = static_cast<const float*>(x) + off;
+    if (n == N && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+#pragma unroll
+      for (int q = 0; q < N / 4; ++q) {
+        const float4 w = reinterpret_cast<const float4*>(p)[q];
+        v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = i < n ? p[i] : 0.0f;
+  } else {
+    const uint16_t* p = static_cast<const uint16_t*>(x) + off;
+    if (N % 8 == 0 && n == N && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+#pragma unroll
+      for (int q = 0; q < N / 8; ++q) {
+        const uint4 w = reinterpret_cast<const uint4*>(p)[q];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {   // bf16 pair -> two fp32 (exact)
+          v[8 * q + 2 * k] = __uint_as_float(ws[k] << 16);
+          v[8 * q + 2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
+        }
+      }
+      return;
+    }
+    if (N == 4 && n == 4 && (reinterpret_cast<uintptr_t>(p) & 7u) == 0) {
+      const uint2 w = *reinterpret_cast<const uint2*>(p);
+      v[0] = __uint_as_float(w.x << 16);
+      v[1] = __uint_as_float(w.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(w.y << 16);
+      v[3] = __uint_as_float(w.y & 0xFFFF0000u);
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = i < n ? __uint_as_float(static_cast<uint32_t>(p[i]) << 16) : 0.0f;
+  }
+}
+
+// Work layout of the row kernels: blockIdx.y walks the (i0, i1) heads of a
+// Rows set, blockIdx.x with the threads the items (row, run) of one head, so
+// no per-item 64-bit index arithmetic on the flat row index is needed.
+__device__ inline int64_t head_items_stride() { return static_cast<int64_t>(gridDim.x) * kThreads; }
+__device__ inline int64_t head_items_start() { return blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; }
+
 // ---------------------------------------------------------------- codecs
 // E4M3 (FN) code of the round-to-nearest-even of a non-negative double q,
 // saturating at 448.
@@ -106,7 +158,12 @@ __device__ inline float fp8_tensor_scale(float amax) {
 
 // NVFP4 encoding of one 16-element block with tensor scale s_t: returns the
 // E4M3 scale code and writes the 16 E2M1 codes (sign in bit 3); a block whose
-// scale rounds to 0 gets all-zero codes.
+// scale rounds to 0 gets all-zero codes.  The E2M1 decision for |x| / D
+// (D = s_hat * s_t) is taken by comparing |x| with the seven midpoints of the
+// E2M1 magnitudes times D: each product has at most 31 significant bits, so
+// it is exact in float64 and every comparison is the exact real one.  Ties
+// go to the even code: strictly above 0.25, 1.25, 2.5 and 5, at or above
+// 0.75, 1.75 and 3.5.  (The same decisions as rounding the quotient.)
 __device__ inline uint32_t encode_nvfp4_block(const float* v, float s_t, uint32_t* c) {
   float bamax = 0.0f;
 #pragma unroll
@@ -117,69 +174,137 @@ __device__ inline uint32_t encode_nvfp4_block(const float* v, float s_t, uint32_
     for (int i = 0; i < 16; ++i) c[i] = 0;
     return 0;
   }
-  const double denom = e4m3_value(sc) * static_cast<double>(s_t);  // exact
+  const double den = e4m3_value(sc) * static_cast<double>(s_t);  // exact
+  const double t0 = 0.25 * den, t1 = 0.75 * den, t2 = 1.25 * den, t3 = 1.75 * den;
+  const double t4 = 2.5 * den, t5 = 3.5 * den, t6 = 5.0 * den;
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    c[i] = e2m1_rne_code(fabs(static_cast<double>(v[i])) / denom) | ((__float_as_uint(v[i]) >> 28) & 8u);
+  for (int i = 0; i < 16; ++i) {
+    const double ax = fabs(static_cast<double>(v[i]));
+    uint32_t q = static_cast<uint32_t>(ax > t0) + static_cast<uint32_t>(ax >= t1) + static_cast<uint32_t>(ax > t2) +
+                 static_cast<uint32_t>(ax >= t3) + static_cast<uint32_t>(ax > t4) + static_cast<uint32_t>(ax >= t5) +
+                 static_cast<uint32_t>(ax > t6);
+    q = (ax != ax) ? 7u : q;   // NaN: as the quotient path (not below 6 -> saturate)
+    c[i] = q | ((__float_as_uint(v[i]) >> 28) & 8u);
+  }
   return sc;
 }
 
-__device__ inline uint32_t encode_fp8(float v, double dscale) {
-  return e4m3_rne_code(fabs(static_cast<double>(v)) / dscale) | ((__float_as_uint(v) >> 24) & 0x80u);
+// 2^k as a double (k in the normal range)
+__device__ inline double pow2d(int k) { return __hiloint2double((k + 1023) << 20, 0); }
+
+// Exact check of an E4M3 candidate code c for the real quotient ax / scale
+// (c the exact code or a neighbour): compare ax with the two midpoints
+// around value(c), scaled exactly in float64 (5 x 24 significant bits), ties
+// to the even code.
+__device__ inline uint32_t e4m3_fixup(uint32_t c, float ax, double dscale) {
+  const int e = static_cast<int>(c >> 3), m = static_cast<int>(c & 7u);
+  const int ue = (e == 0) ? -9 : e - 10;                       // value = mant * 2^ue
+  const double val = static_cast<double>(e == 0 ? m : 8 + m) * pow2d(ue);
+  const double half = pow2d(ue - 1);
+  const double mid_hi = (val + half) * dscale;                           // between c and c + 1
+  const double mid_lo = (val - ((m == 0 && e >= 2) ? 0.5 * half : half)) * dscale;   // between c - 1 and c
+  const double axd = static_cast<double>(ax);
+  const bool up = c < 0x7Eu && (axd > mid_hi || (axd == mid_hi && ((c + 1u) & 1u) == 0u));
+  const bool dn = c > 0u && (axd < mid_lo || (axd == mid_lo && ((c - 1u) & 1u) == 0u));
+  return c + (up ? 1u : 0u) - (dn ? 1u : 0u);
+}
+
+// FP8 code of v / scale: the round-to-nearest-even E4M3 code of |v| / scale
+// (exact decision, saturating at 448), sign of v.  The candidate is the
+// hardware conversion of the float32 quotient |v| * (1 / scale), whose
+// relative error is below 2^-22; it is the exact code unless that quotient
+// lies within 2^-20 (relative) of one of the two midpoints around the
+// candidate's value, and only then is it checked exactly (e4m3_fixup).
+__device__ inline uint32_t encode_fp8(float v, float inv, double dscale) {
+  const float ax = fabsf(v);
+  const float qa = fminf(ax * inv, 448.0f);   // NaN and inf -> 448
+  uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(qa, 0.0f, 0, false)) & 0x7Fu;
+  // values of c - 1, c, c + 1 (the neighbours only where they exist)
+  const uint32_t trio = ((c > 0u ? c - 1u : 0u)) | (c << 8) | ((c < 0x7Eu ? c + 1u : c) << 16);
+  const float vp = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(trio), 0);
+  const float vc = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(trio), 1);
+  const float vn = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(trio), 2);
+  const float mh = 0.5f * (vc + vn), ml = 0.5f * (vc + vp);   // exact in float32
+  const bool near = (c < 0x7Eu && fabsf(qa - mh) <= mh * 0x1p-20f) || (c > 0u && fabsf(qa - ml) <= ml * 0x1p-20f);
+  if (near) c = e4m3_fixup(c, ax, dscale);
+  return c | ((__float_as_uint(v) >> 24) & 0x80u);
 }
 
 // ---------------------------------------------------------------- amax
 __global__ void k_zero_scalar(float* p) { *p = 0.0f; }
 
+// max |x| over the rows (tokens at or past kv_lens[i0] excluded); runs of 8
+// elements per item, a wave and then a work-group reduction, one atomic per
+// work-group (non-negative floats order as their bit patterns, so an
+// unsigned max on the bits is a float max).  The grid is kept to about four
+// work-groups per compute unit: atomics on one address serialize.
 __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, int dt, Rows r, int d,
                                                    const int32_t* __restrict__ kv_lens, float* __restrict__ out) {
-  const int64_t n_rows = r.n0 * r.n1 * r.n2;
-  const int64_t total = n_rows * d;
+  const uint32_t nrun = static_cast<uint32_t>((d + 7) / 8);
   float m = 0.0f;
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * kThreads) {
-    int64_t row = i / d;
-    int col = static_cast<int>(i - row * d);
-    int64_t i0, i1, i2;
-    unravel(row, r, i0, i1, i2);
-    if (kv_lens != nullptr && i2 >= kv_lens[i0]) continue;
-    m = fmaxf(m, fabsf(load_elem(x, dt, row_off(r, i0, i1, i2) + col)));
+  const int64_t nh = r.n0 * r.n1;
+  for (int64_t h = blockIdx.y; h < nh; h += gridDim.y) {
+    const int64_t i0 = h / r.n1, i1 = h - i0 * r.n1;
+    int64_t n2 = r.n2;
+    if (kv_lens != nullptr) {
+      const int64_t len = kv_lens[i0];
+      n2 = len < n2 ? (len > 0 ? len : 0) : n2;
+    }
+    const int64_t items = n2 * nrun;
+    const int64_t base = i0 * r.s0 + i1 * r.s1;
+    for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
+      const int64_t t = it / nrun;
+      const int run = static_cast<int>(it - t * nrun);
+      float v[8];
+      load_run<8>(x, dt, base + t * r.s2 + 8 * run, d - 8 * run < 8 ? d - 8 * run : 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
   }
-  // wave64 reduction, then one atomic per wave (non-negative floats order as
-  // their bit patterns, so an unsigned max on the bits is a float max)
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+  __shared__ float wmax[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, wmax[w]);
+    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(b));
+  }
 }
 
 // ---------------------------------------------------------------- NVFP4 pack
-// ROWS layout: one thread per 16-element block -> 8 code bytes, 1 scale byte
-__device__ inline void pack_nvfp4_rows(const PackJob& J, float s_t, int64_t gid, int64_t stride) {
+// ROWS layout: one item per (row, 16-element block) -> 8 code bytes (one
+// 64-bit store), 1 scale byte
+__device__ inline void pack_nvfp4_rows(const PackJob& J, float s_t) {
   const int d = J.d;
-  const int nb = d / 16;
+  const uint32_t nb = static_cast<uint32_t>(d / 16);
   const Rows xr = J.xr, dr = J.dr;
-  const int64_t total = xr.n0 * xr.n1 * xr.n2 * nb;
-  for (; gid < total; gid += stride) {
-    int64_t row = gid / nb;
-    int blk = static_cast<int>(gid - row * nb);
-    int64_t i0, i1, i2;
-    unravel(row, xr, i0, i1, i2);
-    const int64_t di2 = i2 + (J.dst_pos != nullptr ? J.dst_pos[i0] : 0);
-    if (di2 < 0 || di2 >= dr.n2) continue;  // outside the destination plane
-    const int64_t xo = row_off(xr, i0, i1, i2) + blk * 16;
-    float v[16];
+  const int64_t nh = xr.n0 * xr.n1;
+  for (int64_t h = blockIdx.y; h < nh; h += gridDim.y) {
+    const int64_t i0 = h / xr.n1, i1 = h - i0 * xr.n1;
+    const int64_t pos = J.dst_pos != nullptr ? J.dst_pos[i0] : 0;
+    const int64_t xbase = i0 * xr.s0 + i1 * xr.s1, dbase = i0 * dr.s0 + i1 * dr.s1;
+    const int64_t items = xr.n2 * nb;
+    for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
+      const int64_t t = it / nb;
+      const int blk = static_cast<int>(it - t * nb);
+      const int64_t dt_ = t + pos;
+      if (dt_ < 0 || dt_ >= dr.n2) continue;  // outside the destination plane
+      float v[16];
+      load_run<16>(J.x, J.dt, xbase + t * xr.s2 + blk * 16, 16, v);
+      uint32_t c[16];
+      const uint32_t sc = encode_nvfp4_block(v, s_t, c);
+      uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = load_elem(J.x, J.dt, xo + i);
-    uint32_t c[16];
-    const uint32_t sc = encode_nvfp4_block(v, s_t, c);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      lo |= c[i] << (4 * i);
-      hi |= c[8 + i] << (4 * i);
+      for (int i = 0; i < 8; ++i) {
+        lo |= c[i] << (4 * i);
+        hi |= c[8 + i] << (4 * i);
+      }
+      const int64_t drow = dbase + dt_ * dr.s2;
+      *reinterpret_cast<uint2*>(J.codes + drow * (d / 2) + blk * 8) = make_uint2(lo, hi);
+      J.scales[drow * nb + blk] = static_cast<uint8_t>(sc);
     }
-    const int64_t drow = row_off(dr, i0, i1, di2);
-    *reinterpret_cast<uint2*>(J.codes + drow * (d / 2) + blk * 8) = make_uint2(lo, hi);
-    J.scales[drow * nb + blk] = static_cast<uint8_t>(sc);
   }
 }
 
@@ -206,125 +331,144 @@ __device__ inline bool t4_group(const Rows& xr, const Rows& dr, const int32_t* d
   return any;
 }
 
-// TOKEN4 layout: one thread per (4-token group, 16-element block): 32 code
-// bytes (two 16-byte stores) and one 4-byte scale word; tokens of the group
-// that this call does not write keep their bytes.
-__device__ inline void pack_nvfp4_t4(const PackJob& J, float s_t, int64_t gid, int64_t stride) {
+// TOKEN4 layout: one item per (4-token group slot, 16-element block): 32
+// code bytes (two 16-byte stores) and one 4-byte scale word; tokens of the
+// group that this call does not write keep their bytes.
+__device__ inline void pack_nvfp4_t4(const PackJob& J, float s_t) {
   const int d = J.d;
-  const int nb = d / 16;
+  const uint32_t nb = static_cast<uint32_t>(d / 16);
   const Rows xr = J.xr, dr = J.dr;
   const int64_t slots = t4_slots(xr.n2);
-  const int64_t total = xr.n0 * xr.n1 * slots * nb;
-  for (; gid < total; gid += stride) {
-    const int blk = static_cast<int>(gid % nb);
-    int64_t rest = gid / nb;
-    const int64_t gl = rest % slots;
-    rest /= slots;
-    const int64_t i1 = rest % xr.n1, i0 = rest / xr.n1;
-    int64_t t0, src[4];
-    if (!t4_group(xr, dr, J.dst_pos, i0, gl, t0, src)) continue;
-    const int64_t grow = group_row(dr, i0, i1, t0);
-    uint4* cp = reinterpret_cast<uint4*>(J.codes + grow * (d / 2) + blk * 32);
-    uint32_t* sp = reinterpret_cast<uint32_t*>(J.scales + grow * nb + blk * 4);
-    const bool partial = src[0] < 0 || src[1] < 0 || src[2] < 0 || src[3] < 0;
-    uint4 w0 = partial ? cp[0] : make_uint4(0, 0, 0, 0);
-    uint4 w1 = partial ? cp[1] : make_uint4(0, 0, 0, 0);
-    uint32_t sw = partial ? *sp : 0u;
-    uint32_t* wd[8] = {&w0.x, &w0.y, &w0.z, &w0.w, &w1.x, &w1.y, &w1.z, &w1.w};
+  const int64_t nh = xr.n0 * xr.n1;
+  for (int64_t h = blockIdx.y; h < nh; h += gridDim.y) {
+    const int64_t i0 = h / xr.n1, i1 = h - i0 * xr.n1;
+    const int64_t xbase = i0 * xr.s0 + i1 * xr.s1;
+    const int64_t items = slots * nb;
+    for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
+      const int64_t gl = it / nb;
+      const int blk = static_cast<int>(it - gl * nb);
+      int64_t t0, src[4];
+      if (!t4_group(xr, dr, J.dst_pos, i0, gl, t0, src)) continue;
+      const int64_t grow = group_row(dr, i0, i1, t0);
+      uint4* cp = reinterpret_cast<uint4*>(J.codes + grow * (d / 2) + blk * 32);
+      uint32_t* sp = reinterpret_cast<uint32_t*>(J.scales + grow * nb + blk * 4);
+      const bool partial = src[0] < 0 || src[1] < 0 || src[2] < 0 || src[3] < 0;
+      uint4 w0 = partial ? cp[0] : make_uint4(0, 0, 0, 0);
+      uint4 w1 = partial ? cp[1] : make_uint4(0, 0, 0, 0);
+      uint32_t sw = partial ? *sp : 0u;
+      uint32_t* wd[8] = {&w0.x, &w0.y, &w0.z, &w0.w, &w1.x, &w1.y, &w1.z, &w1.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (src[j] < 0) continue;
-      const int64_t xo = row_off(xr, i0, i1, src[j]) + blk * 16;
-      float v[16];
+      for (int j = 0; j < 4; ++j) {
+        if (src[j] < 0) continue;
+        float v[16];
+        load_run<16>(J.x, J.dt, xbase + src[j] * xr.s2 + blk * 16, 16, v);
+        uint32_t c[16];
+        const uint32_t sc = encode_nvfp4_block(v, s_t, c);
+        sw = (sw & ~(0xFFu << (8 * j))) | (sc << (8 * j));
+        // element i: byte 2i + (j >> 1), nibble j & 1 -> dword i / 2, bit 16 (i & 1) + 8 (j >> 1) + 4 (j & 1)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = load_elem(J.x, J.dt, xo + i);
-      uint32_t c[16];
-      const uint32_t sc = encode_nvfp4_block(v, s_t, c);
-      sw = (sw & ~(0xFFu << (8 * j))) | (sc << (8 * j));
-      // element i: byte 2i + (j >> 1), nibble j & 1 -> dword i / 2, bit 16 (i & 1) + 8 (j >> 1) + 4 (j & 1)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int sh = 16 * (i & 1) + 8 * (j >> 1) + 4 * (j & 1);
-        *wd[i >> 1] = (*wd[i >> 1] & ~(0xFu << sh)) | (c[i] << sh);
+        for (int i = 0; i < 16; ++i) {
+          const int sh = 16 * (i & 1) + 8 * (j >> 1) + 4 * (j & 1);
+          *wd[i >> 1] = (*wd[i >> 1] & ~(0xFu << sh)) | (c[i] << sh);
+        }
       }
+      cp[0] = w0;
+      cp[1] = w1;
+      *sp = sw;
     }
-    cp[0] = w0;
-    cp[1] = w1;
-    *sp = sw;
   }
 }
 
+// grid: (items of one head, heads, jobs)
 __global__ void __launch_bounds__(kThreads) k_pack_nvfp4(PackJobs P) {
-  const PackJob& J = P.j[blockIdx.y];
+  const PackJob& J = P.j[blockIdx.z];
   const float s_t = nvfp4_tensor_scale(*J.amax);
-  const int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
-  if (gid == 0 && J.sout != nullptr) *J.sout = s_t;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  if (J.layout == KVQ_PLANE_TOKEN4) pack_nvfp4_t4(J, s_t, gid, stride);
-  else pack_nvfp4_rows(J, s_t, gid, stride);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && J.sout != nullptr) *J.sout = s_t;
+  if (J.layout == KVQ_PLANE_TOKEN4) pack_nvfp4_t4(J, s_t);
+  else pack_nvfp4_rows(J, s_t);
 }
 
 // ---------------------------------------------------------------- FP8 pack
-// ROWS layout: one thread per 4 elements (one 32-bit code word)
-__device__ inline void pack_fp8_rows(const PackJob& J, double dscale, int64_t gid, int64_t stride) {
+// ROWS layout: one item per (row, 16-element run): 16 code bytes (one
+// 16-byte store; d % 16 != 0 leaves a shorter last run, stored per word)
+__device__ inline void pack_fp8_rows(const PackJob& J, double dscale, float inv) {
   const int d = J.d;
-  const int nw = d / 4;
+  const uint32_t nr = static_cast<uint32_t>((d + 15) / 16);
   const Rows xr = J.xr, dr = J.dr;
-  const int64_t total = xr.n0 * xr.n1 * xr.n2 * nw;
-  for (; gid < total; gid += stride) {
-    int64_t row = gid / nw;
-    int w = static_cast<int>(gid - row * nw);
-    int64_t i0, i1, i2;
-    unravel(row, xr, i0, i1, i2);
-    const int64_t di2 = i2 + (J.dst_pos != nullptr ? J.dst_pos[i0] : 0);
-    if (di2 < 0 || di2 >= dr.n2) continue;  // outside the destination plane
-    const int64_t xo = row_off(xr, i0, i1, i2) + w * 4;
-    uint32_t word = 0;
+  const int64_t nh = xr.n0 * xr.n1;
+  for (int64_t h = blockIdx.y; h < nh; h += gridDim.y) {
+    const int64_t i0 = h / xr.n1, i1 = h - i0 * xr.n1;
+    const int64_t pos = J.dst_pos != nullptr ? J.dst_pos[i0] : 0;
+    const int64_t xbase = i0 * xr.s0 + i1 * xr.s1, dbase = i0 * dr.s0 + i1 * dr.s1;
+    const int64_t items = xr.n2 * nr;
+    for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
+      const int64_t t = it / nr;
+      const int run = static_cast<int>(it - t * nr);
+      const int64_t dt_ = t + pos;
+      if (dt_ < 0 || dt_ >= dr.n2) continue;  // outside the destination plane
+      const int n = d - 16 * run < 16 ? d - 16 * run : 16;   // a multiple of 4
+      float v[16];
+      load_run<16>(J.x, J.dt, xbase + t * xr.s2 + 16 * run, n, v);
+      uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) word |= encode_fp8(load_elem(J.x, J.dt, xo + i), dscale) << (8 * i);
-    *reinterpret_cast<uint32_t*>(J.codes + row_off(dr, i0, i1, di2) * d + w * 4) = word;
+      for (int q = 0; q < 4; ++q) {
+        w[q] = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[q] |= encode_fp8(v[4 * q + i], inv, dscale) << (8 * i);
+      }
+      uint8_t* dst = J.codes + (dbase + dt_ * dr.s2) * d + 16 * run;
+      if (n == 16 && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (4 * q < n) reinterpret_cast<uint32_t*>(dst)[q] = w[q];
+      }
+    }
   }
 }
 
-// TOKEN4 layout: one thread per (4-token group, 4 elements): 16 code bytes
-__device__ inline void pack_fp8_t4(const PackJob& J, double dscale, int64_t gid, int64_t stride) {
+// TOKEN4 layout: one item per (4-token group slot, 4 elements): 16 code bytes
+__device__ inline void pack_fp8_t4(const PackJob& J, double dscale, float inv) {
   const int d = J.d;
-  const int nw = d / 4;
+  const uint32_t nw = static_cast<uint32_t>(d / 4);
   const Rows xr = J.xr, dr = J.dr;
   const int64_t slots = t4_slots(xr.n2);
-  const int64_t total = xr.n0 * xr.n1 * slots * nw;
-  for (; gid < total; gid += stride) {
-    const int w = static_cast<int>(gid % nw);
-    int64_t rest = gid / nw;
-    const int64_t gl = rest % slots;
-    rest /= slots;
-    const int64_t i1 = rest % xr.n1, i0 = rest / xr.n1;
-    int64_t t0, src[4];
-    if (!t4_group(xr, dr, J.dst_pos, i0, gl, t0, src)) continue;
-    uint4* cp = reinterpret_cast<uint4*>(J.codes + group_row(dr, i0, i1, t0) * d + w * 16);
-    const bool partial = src[0] < 0 || src[1] < 0 || src[2] < 0 || src[3] < 0;
-    uint4 wv = partial ? *cp : make_uint4(0, 0, 0, 0);
-    uint32_t* wd[4] = {&wv.x, &wv.y, &wv.z, &wv.w};
+  const int64_t nh = xr.n0 * xr.n1;
+  for (int64_t h = blockIdx.y; h < nh; h += gridDim.y) {
+    const int64_t i0 = h / xr.n1, i1 = h - i0 * xr.n1;
+    const int64_t xbase = i0 * xr.s0 + i1 * xr.s1;
+    const int64_t items = slots * nw;
+    for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
+      const int64_t gl = it / nw;
+      const int w = static_cast<int>(it - gl * nw);
+      int64_t t0, src[4];
+      if (!t4_group(xr, dr, J.dst_pos, i0, gl, t0, src)) continue;
+      uint4* cp = reinterpret_cast<uint4*>(J.codes + group_row(dr, i0, i1, t0) * d + w * 16);
+      const bool partial = src[0] < 0 || src[1] < 0 || src[2] < 0 || src[3] < 0;
+      uint4 wv = partial ? *cp : make_uint4(0, 0, 0, 0);
+      uint32_t* wd[4] = {&wv.x, &wv.y, &wv.z, &wv.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (src[j] < 0) continue;
-      const int64_t xo = row_off(xr, i0, i1, src[j]) + w * 4;
+      for (int j = 0; j < 4; ++j) {
+        if (src[j] < 0) continue;
+        float v[4];
+        load_run<4>(J.x, J.dt, xbase + src[j] * xr.s2 + w * 4, 4, v);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)  // element 4w + i of token j: byte 4 (4w + i) + j
-        *wd[i] = (*wd[i] & ~(0xFFu << (8 * j))) | (encode_fp8(load_elem(J.x, J.dt, xo + i), dscale) << (8 * j));
+        for (int i = 0; i < 4; ++i)  // element 4w + i of token j: byte 4 (4w + i) + j
+          *wd[i] = (*wd[i] & ~(0xFFu << (8 * j))) | (encode_fp8(v[i], inv, dscale) << (8 * j));
+      }
+      *cp = wv;
     }
-    *cp = wv;
   }
 }
 
 __global__ void __launch_bounds__(kThreads) k_pack_fp8(PackJobs P) {
-  const PackJob& J = P.j[blockIdx.y];
+  const PackJob& J = P.j[blockIdx.z];
   const float scale = fp8_tensor_scale(*J.amax);
-  const int64_t gid = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x;
-  if (gid == 0 && J.sout != nullptr) *J.sout = scale;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  if (J.layout == KVQ_PLANE_TOKEN4) pack_fp8_t4(J, static_cast<double>(scale), gid, stride);
-  else pack_fp8_rows(J, static_cast<double>(scale), gid, stride);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && J.sout != nullptr) *J.sout = scale;
+  const float inv = 1.0f / scale;   // candidate quotients only; decisions are exact
+  if (J.layout == KVQ_PLANE_TOKEN4) pack_fp8_t4(J, static_cast<double>(scale), inv);
+  else pack_fp8_rows(J, static_cast<double>(scale), inv);
 }
 
 // ---------------------------------------------------------------- unpack
@@ -393,29 +537,43 @@ int grid_for(int64_t items) {
 
 }  // namespace
 
+// grid of the row kernels: y = heads (at most 65535, the kernels stride over
+// the rest), x = enough blocks for the items of one head, about 8192 blocks
+// in all
+static dim3 head_grid(int64_t heads, int64_t items_per_head, int z, int64_t budget = 8192) {
+  int64_t y = heads < 1 ? 1 : (heads > 65535 ? 65535 : heads);
+  int64_t x = (items_per_head + kThreads - 1) / kThreads;
+  const int64_t xmax = budget / y > 1 ? budget / y : 1;
+  x = x < 1 ? 1 : (x > xmax ? xmax : x);
+  return dim3(static_cast<unsigned>(x), static_cast<unsigned>(y), static_cast<unsigned>(z));
+}
+
 hipError_t launch_amax(const void* x, int x_dtype, Rows rows, int d, const int32_t* kv_lens, float* amax_out,
                        bool accumulate, hipStream_t st) {
   if (!accumulate) hipLaunchKernelGGL(k_zero_scalar, dim3(1), dim3(1), 0, st, amax_out);
-  const int64_t items = rows.n0 * rows.n1 * rows.n2 * d;
-  if (items > 0) hipLaunchKernelGGL(k_amax, dim3(grid_for(items)), dim3(kThreads), 0, st, x, x_dtype, rows, d, kv_lens, amax_out);
+  const int64_t heads = rows.n0 * rows.n1;
+  if (heads > 0 && rows.n2 > 0)
+    hipLaunchKernelGGL(k_amax, head_grid(heads, rows.n2 * ((d + 7) / 8), 1, 1024), dim3(kThreads), 0, st, x, x_dtype,
+                       rows, d, kv_lens, amax_out);
   return hipGetLastError();
 }
 
-// work items of one job: one per (row, 16-block) / (row, 4 elements), or
-// per (4-token group slot, ...) for TOKEN4 destinations
-static int64_t pack_items(const PackJob& J, bool fp4) {
-  const int64_t per = fp4 ? J.d / 16 : J.d / 4;
-  const int64_t rows = J.layout == KVQ_PLANE_TOKEN4 ? J.xr.n0 * J.xr.n1 * (J.xr.n2 / 4 + 2) : J.xr.n0 * J.xr.n1 * J.xr.n2;
-  return rows * per;
+// items of one head of one job: (row, 16-block) / (row, 16-element run), or
+// (4-token group slot, 16-block / 4 elements) for TOKEN4 destinations
+static int64_t pack_items_per_head(const PackJob& J, bool fp4) {
+  const bool t4 = J.layout == KVQ_PLANE_TOKEN4;
+  const int64_t per = fp4 ? J.d / 16 : (t4 ? J.d / 4 : (J.d + 15) / 16);
+  return (t4 ? J.xr.n2 / 4 + 2 : J.xr.n2) * per;
 }
 
 static hipError_t launch_pack(const PackJobs& P, bool fp4, hipStream_t st) {
-  int64_t items = 0;
+  int64_t items = 0, heads = 0;
   for (int i = 0; i < P.n; ++i) {
-    const int64_t n = pack_items(P.j[i], fp4);
+    const int64_t n = pack_items_per_head(P.j[i], fp4), h = P.j[i].xr.n0 * P.j[i].xr.n1;
     items = n > items ? n : items;
+    heads = h > heads ? h : heads;
   }
-  const dim3 grid(grid_for(items), P.n);
+  const dim3 grid = head_grid(heads, items, P.n);
   if (fp4) hipLaunchKernelGGL(k_pack_nvfp4, grid, dim3(kThreads), 0, st, P);
   else hipLaunchKernelGGL(k_pack_fp8, grid, dim3(kThreads), 0, st, P);
   return hipGetLastError();

@@ -139,6 +139,30 @@ def test_fp8_pack_bit_exact(dt):
     assert np.array_equal(_np(u).astype(np.float64), OF.fp32_round(OQ.fp8_unpack(c, sc)))
 
 
+@pytest.mark.parametrize("amax_val", [448.0, 224.0, 672.0, 0.3])
+def test_fp8_pack_adversarial(amax_val):
+    """Every E4M3 rounding midpoint (times the scale amax/448) and its two
+    float32 neighbours, plus saturation, zeros and -0: exact ties go to the
+    even code; the GPU codes equal the oracle's bit for bit."""
+    announce(f"pack fp8 adversarial amax={amax_val}")
+    scale = np.float32(np.float32(amax_val) / np.float32(448.0))
+    pos = OF.e4m3_decode(np.arange(0x7F))
+    vals = [0.0, -0.0, 448.0 * scale, 500.0 * scale, 1e30]
+    for a, b in zip(pos[:-1], pos[1:]):
+        m = np.float32((a + b) / 2 * np.float64(scale))
+        vals += [m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1e9))]
+    v = np.asarray(vals, np.float32)
+    v = np.concatenate([v, -v])
+    v = np.concatenate([v, np.zeros((-len(v)) % 16, np.float32)]).reshape(-1, 16)
+    x = torch.from_numpy(v)
+    amax = torch.tensor([np.float32(amax_val)], device=DEV)
+    p = K().kvq_pack_fp8(x.to(DEV), amax)
+    c, sc = OQ.fp8_pack(kvq_synth.f64(x), np.float32(amax_val))
+    torch.cuda.synchronize()
+    assert float(p.scale.item()) == sc
+    assert np.array_equal(_np(p.codes), c)
+
+
 def test_append_with_dst_pos():
     announce("pack append dst_pos")
     B, H, Lmax, D = 3, 2, 40, 128
