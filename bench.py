@@ -63,21 +63,27 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_decode_gqa_nvfp4_b2_hq32_hkv8_d128_kv32k_traffic.txt")
-DECODE_SRC = os.path.join(ROOT, "quantized_kv_cache_nvfp4_amd", "csrc", "decode_gqa.hip")
+CSRC = os.path.join(ROOT, "quantized_kv_cache_nvfp4_amd", "csrc")
+TRAFFIC = {   # committed counter summaries and the kernel source they were taken from
+    "gqa": (os.path.join(ROOT, "profiles", "k_decode_gqa_nvfp4_b2_hq32_hkv8_d128_kv32k_traffic.txt"),
+            os.path.join(CSRC, "decode_gqa.hip")),
+    "mla": (os.path.join(ROOT, "profiles", "k_decode_mla_nvfp4_b32_h16_c512_r64_kv8k_traffic.txt"),
+            os.path.join(CSRC, "decode_mla.hip")),
+}
 
 
-def measured_traffic():
+def measured_traffic(which="gqa"):
     """HBM bytes per launch of the split kernel from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size),
     or None when the kernel source changed since the counters were taken."""
     import hashlib
+    path, src_path = TRAFFIC[which]
     try:
-        kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE).read().splitlines() if ":" in line)
+        kv = dict(line.split(":", 1) for line in open(path).read().splitlines() if ":" in line)
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+    src = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
     if kv.get("kernel_source_sha256") != src:
         return None
     try:
@@ -246,7 +252,7 @@ def run_mla(args):
         "hbm_gbps_step": round(algo / (ms_step * 1e-3) / 1e9, 1),
         "step_us": {"decode_two_launch": round(ms_step * 1e3, 3), "split_kernel": round(kernel_us, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("mla"),
                      "kernel": "k_decode_mla (split kernel, partials)", "kernel_us_mean": round(kernel_us, 3),
                      "algorithmic_bytes": algo},
     }
