@@ -139,6 +139,70 @@ def cpu_baseline(inp, reps):
                       f"attention; median {t:.2f} s/step; numpy elementwise single-threaded, BLAS threads {threads}"}
 
 
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
+    except Exception:
+        return 1
+
+
+def cpu_baseline_mla(inp, reps, n_req=4):
+    """The oracle timed on this host for the MLA step, on a bounded sample:
+    `n_req` of the B requests (fp64 dequantize of their latent + exact MLA
+    attention), scaled to the whole batch by the request count."""
+    import numpy as np
+    import kvq_synth
+    from oracle import attention as OA
+    from oracle import quant as OQ
+    B = inp.q_c.shape[0]
+    cf = kvq_synth.f64(inp.c[:n_req])
+    amax = OQ.amax(cf[:, None], inp.kv_lens[:n_req])   # the sample's own scale (timing only; untimed)
+    codes, scales, st = OQ.nvfp4_pack(cf, amax)
+    q_c, q_r, k_r = (kvq_synth.f64(t[:n_req]) for t in (inp.q_c, inp.q_r, inp.k_r))
+    times = []
+    for r in range(reps):
+        t0 = time.perf_counter()
+        chat = OQ.nvfp4_unpack(codes, scales, st)
+        OA.decode_mla(q_c, q_r, chat, k_r, inp.kv_lens[:n_req], inp.softmax_scale)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times)) * B / n_req
+    return {"value": t * 1e6, "unit": "us/step", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"{n_req} of {B} requests x {reps} reps (fp64 dequantize of their latent + exact MLA "
+                      f"attention), median scaled by {B}/{n_req}"}
+
+
+def cpu_baseline_fp8(inp, reps, n_req=3, prob_scale=None):
+    """The oracle timed on this host for the FP8 ragged step, on a bounded
+    sample: the first `n_req` requests (fp64 dequantize of their K/V + exact
+    attention, or FP8-P attention), scaled to the batch by token count."""
+    import numpy as np
+    import kvq_synth
+    from oracle import attention as OA
+    from oracle import quant as OQ
+    lens = inp.kv_lens
+    kf, vf = kvq_synth.f64(inp.k[:n_req]), kvq_synth.f64(inp.v[:n_req])
+    ka, va = OQ.amax(kf, lens[:n_req]), OQ.amax(vf, lens[:n_req])   # the sample's own scales (timing only; untimed)
+    kc, ks = OQ.fp8_pack(kf, ka)
+    vc, vs = OQ.fp8_pack(vf, va)
+    q = kvq_synth.f64(inp.q[:n_req])
+    times = []
+    for r in range(reps):
+        t0 = time.perf_counter()
+        khat, vhat = OQ.fp8_unpack(kc, ks), OQ.fp8_unpack(vc, vs)
+        if prob_scale is None:
+            OA.decode_gqa(q, khat, vhat, lens[:n_req], inp.softmax_scale)
+        else:
+            OA.decode_gqa_fp8p(q, khat, vhat, lens[:n_req], inp.softmax_scale, prob_scale)
+        times.append(time.perf_counter() - t0)
+    scale = float(lens.sum()) / float(lens[:n_req].sum())
+    t = float(np.median(times)) * scale
+    return {"value": t * 1e6, "unit": "us/step", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"first {n_req} of {len(lens)} requests x {reps} reps (fp64 dequantize + exact attention"
+                      f"{'' if prob_scale is None else ' with FP8 probabilities'}), median scaled by the token "
+                      f"count ratio {scale:.2f}"}
+
+
 def eager_timer(torch, fn, reps=5):
     """Average time of fn() over `reps` back-to-back calls (HIP events on the
     current stream, after one warm-up call), in microseconds."""
@@ -218,14 +282,16 @@ def run_mla(args):
     copies = [(plane0, kr0)] + [(K.NVFP4Plane(plane0.codes.clone(), plane0.scales.clone(),
                                               plane0.tensor_scale.clone(), plane0.layout), kr0.clone())
                                 for _ in range(n_copies - 1)]
-    s = args.splits if args.splits > 0 else K.kvq_auto_num_splits(K.kvq_device_cu_count(), MLA_B, 1, MLA_L,
-                                                                   MLA_DC, MLA_H)
-    part_o = torch.empty(MLA_B * MLA_H * s * MLA_DC, dtype=torch.float32, device=dev)
-    part_lse = torch.empty(MLA_B * MLA_H * s, dtype=torch.float32, device=dev)
+    # the library picks the split count when --splits is not given (the
+    # partial buffers are sized for its upper bound, 64)
+    cap = args.splits if args.splits > 0 else 64
+    part_o = torch.empty(MLA_B * MLA_H * cap * MLA_DC, dtype=torch.float32, device=dev)
+    part_lse = torch.empty(MLA_B * MLA_H * cap, dtype=torch.float32, device=dev)
     out = torch.empty(MLA_B, MLA_H, MLA_DC, dtype=torch.bfloat16, device=dev)
     dargs = [K.make_decode_args(q_c, pl, None, lens, max_kv_len=MLA_L, softmax_scale=inp.softmax_scale,
-                                num_splits=s, part_o=part_o, part_lse=part_lse, q_rope=q_r, k_rope=kr)
+                                num_splits=args.splits, part_o=part_o, part_lse=part_lse, q_rope=q_r, k_rope=kr)
              for pl, kr in copies]
+    s = K.attn_decode_splitkv(dargs[0])   # splits used
 
     def step(i):
         used = K.attn_decode_splitkv(dargs[i])
@@ -256,6 +322,9 @@ def run_mla(args):
                      "kernel": "k_decode_mla (split kernel, partials)", "kernel_us_mean": round(kernel_us, 3),
                      "algorithmic_bytes": algo},
     }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline_mla(inp, args.cpu_reps)
     print(json.dumps(res), flush=True)
 
 
@@ -352,6 +421,10 @@ def run_fp8(args):
                      "kernel": "k_decode_gqa<FP8,G=4,D=128> (split kernel, partials)",
                      "kernel_us_mean": round(kernel_us, 3), "algorithmic_bytes": algo},
     }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline_fp8(inp, args.cpu_reps)
+        res["cpu_baseline_fp8p"] = cpu_baseline_fp8(inp, args.cpu_reps, prob_scale=float(1.0 / 448.0))
     print(json.dumps(res), flush=True)
 
 
