@@ -68,7 +68,7 @@ __device__ inline float wave_split_weight(const float* lse, int s, float& inv, f
 // change the result.  Four accumulators (j mod 4).  (For N = 64 one column
 // per pass.)
 template <bool COHERENT, int N>
-__device__ inline void combine_head_n(const float* lse, const float* po, int s, int Dv, int d_lo, int d_hi, void* out,
+__device__ __attribute__((always_inline)) inline void combine_head_n(const float* lse, const float* po, int s, int Dv, int d_lo, int d_hi, void* out,
                                       int dt, int64_t oidx, float osc, float* lse_out) {
   constexpr int C = N <= 32 ? 2 : 1;   // columns per lane per pass (at most 64 loads in flight)
   const int lane = threadIdx.x & 63;
@@ -98,8 +98,10 @@ __device__ inline void combine_head_n(const float* lse, const float* po, int s, 
   if (lane == 0 && lse_out != nullptr) *lse_out = lse_m;
 }
 
+// (always inlined: called as a function from the fused decode kernel it
+// would run on a stack in scratch memory)
 template <bool COHERENT>
-__device__ inline void combine_head(const float* lse, const float* po, int s, int Dv, int d_lo, int d_hi, void* out,
+__device__ __attribute__((always_inline)) inline void combine_head(const float* lse, const float* po, int s, int Dv, int d_lo, int d_hi, void* out,
                                     int dt, int64_t oidx, float osc, float* lse_out) {
   if (s <= 16) combine_head_n<COHERENT, 16>(lse, po, s, Dv, d_lo, d_hi, out, dt, oidx, osc, lse_out);
   else if (s <= 32) combine_head_n<COHERENT, 32>(lse, po, s, Dv, d_lo, d_hi, out, dt, oidx, osc, lse_out);
