@@ -324,8 +324,11 @@ int attn_decode(const kvq_decode_args* args, void* out, int32_t out_dtype, const
  * kvq_auto_num_splits - split count when the caller passes num_splits <= 0
  * (Model-Optimizer PR #1832, Testing section: the built-in heuristic picks s
  * from the compute-unit count and batch x heads).  Host-only, no device
- * access.  Rule: s = ceil(2 num_cus / (B programs_per_req)) (two
- * work-groups per compute unit), capped at ceil(max_kv_len / 256), at
+ * access.  Rule: s = ceil(w num_cus / (B programs_per_req)), w = 1
+ * work-group per compute unit when Hq >= 4 programs_per_req and Dv <= 256
+ * (query groups of 4+ heads: the grouped-tile GQA kernel) and w = 2
+ * otherwise (query groups of 1-2 heads, the MLA latent), capped at
+ * ceil(max_kv_len / 256), at
  * floor(KV bytes / (3 x partial bytes)) with KV bytes = B programs_per_req
  * max_kv_len (9/8) Dv and partial bytes = B Hq (Dv + 1) 8 per split, and at
  * 64; at least 1.

@@ -24,8 +24,10 @@
 //    filled with (sub-tile, head) pairs: sub-tile u of 16 tokens only
 //    meets the Q columns of its own row group (block-diagonal B operand), so
 //    one 16x16 score tile holds 16*16/G tokens x G heads with no padding.
-//    Each of the 16 rows keeps its own online-softmax state; rows of the same
-//    head are merged at the end of the chunk.
+//    Each of the 16 rows keeps its own denominator and accumulators; the rows
+//    of one head share one running maximum (the maxima are taken over all of
+//    the head's rows), so at the end of the chunk they add up unweighted and
+//    only the 4 waves' states are merged, with weights.
 //  * Q.K^T contracts over head_dim, and the order of that contraction is
 //    free: lane group g owns a contiguous quarter of head_dim, so each lane
 //    reads its K codes with one 128-bit load per token.  P.V contracts over
@@ -66,7 +68,10 @@ namespace {
 
 using namespace dec;
 
-constexpr int kWaves = 4;
+#ifndef KVQ_GQA_WAVES
+#define KVQ_GQA_WAVES 4
+#endif
+constexpr int kWaves = KVQ_GQA_WAVES;   // waves per work-group
 constexpr int kThreads = 64 * kWaves;
 
 // ------------------------------------------------------------------ traits
@@ -127,6 +132,25 @@ __device__ inline void v_pairs(uint32_t vw0, uint32_t vw1, uint32_t vs, f16x2* o
   }
 }
 
+// Rows of one head.  Lane column c of a 16-lane row is MFMA row c = sub * G
+// + h; the rows of head h are the 16 / G columns with c mod G = h.  A DPP
+// rotation by N inside each 16-lane row; the max / sum over the head's rows
+// is an all-reduce by rotations of 8, 4, .. G lanes (every lane of the head
+// receives the same value: each step adds or maxes a pair symmetrically).
+template <int N>
+__device__ inline float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+template <int G, bool SUM>
+__device__ inline float head_rows_reduce(float x) {
+  auto op = [](float u, float v) { return SUM ? u + v : fmaxf(u, v); };
+  if constexpr (G <= 8) x = op(x, row_ror<8>(x));
+  if constexpr (G <= 4) x = op(x, row_ror<4>(x));
+  if constexpr (G <= 2) x = op(x, row_ror<2>(x));
+  if constexpr (G <= 1) x = op(x, row_ror<1>(x));
+  return x;
+}
+
 // ------------------------------------------------------------------ tiles
 // Registers holding one tile's packed K (codes + block scales) and V, as
 // loaded from HBM.  K and V are separate so that the next tile's K can be in
@@ -160,12 +184,11 @@ struct FusedOut {
 // QF32 fp32 queries (hi/lo split), PSPLIT 2 = P carried as f16 hi + lo,
 // FUSED: the last work-group of each (request, kv head) merges the partials
 // and writes the final output (one launch per decode step).
-// Work-groups per CU the register allocation is sized for: 4 (16 waves per
-// CU) where the tile state fits in 128 VGPRs, fewer for the wide-tile
-// (G <= 2) and fp32-query variants.
+// Work-groups per CU the register allocation is sized for: 8 waves per CU
+// (2 per SIMD, up to 256 VGPRs each).
 template <int KVF, int G, bool QF32, int VL>
 constexpr int decode_min_blocks() {
-  return (16 / G > 4) ? 2 : ((QF32 || KVF != KVQ_NVFP4) ? 2 : 2);
+  return 8 / kWaves;
 }
 
 // PM: 0 attention, 1 FP8-P pass 1 (scores), 2 FP8-P pass 2 (quantized P . V).
@@ -183,10 +206,9 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   using VT = VTile<KVF, D, NT>;
 
   __shared__ float lds_o[kWaves][16][D];
-  __shared__ float lds_m[kWaves][16];
-  __shared__ float lds_l[kWaves][16];
-  __shared__ float lds_w[kWaves][16];   // merge weights
-  __shared__ float lds_lse[16];         // merged lse per head
+  __shared__ float lds_m[kWaves][16];   // per wave and head: running max (log2 units)
+  __shared__ float lds_l[kWaves][16];   //                    denominator
+  __shared__ float lds_lse[16];         // FP8-P pass 2: output factor per head
   __shared__ int lds_last;
 
   const int lane = threadIdx.x & 63;
@@ -298,7 +320,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
 
   const float qk_scale = a.softmax_scale * kscale * kLog2e;
 
-  float m_run = -INFINITY;  // running max of row c (log2 domain)
+  float m_run = -INFINITY;  // running max of row c's head (log2 domain; the same for all its rows)
   float l_run = 0.0f;       // this lane's share of row c's denominator
   f32x4 acc_o[Gm::kPvJ];
 #pragma unroll
@@ -472,6 +494,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
             for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[t][x][i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = head_rows_reduce<G, false>(tmax);   // one maximum per head: its rows add up unweighted
       const bool bump = tmax > m_run;
       if (__any(bump)) {
         const float m_new = bump ? tmax : m_run;
@@ -701,6 +724,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
           for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[x][i]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16));   // the row's max over its four lane groups
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = head_rows_reduce<G, false>(tmax);     // and over the head's rows
         if (tmax > m_run) {
           l_run *= __builtin_amdgcn_exp2f(m_run - tmax);   // 0 when m_run = -inf
           m_run = tmax;
@@ -812,12 +836,15 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
     }
   }
 
-  // ---------------- per-wave state -> LDS
+  // ---------------- per-wave state -> LDS.  The rows of one head share
+  // the running maximum, so within a wave they add up unweighted; each wave
+  // leaves one maximum and one denominator per head.
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (g == 0) {
-    lds_m[wave][c] = m_run;
-    lds_l[wave][c] = l_tot;
+  l_tot = head_rows_reduce<G, true>(l_tot);
+  if (lane < G) {   // lane c = h of lane group 0
+    lds_m[wave][lane] = m_run;
+    lds_l[wave][lane] = l_tot;
   }
   if constexpr (PM != 1) {
 #pragma unroll
@@ -826,76 +853,103 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
       for (int i = 0; i < 4; ++i) lds_o[wave][4 * g + i][c * Gm::kPvElems + j] = acc_o[j][i];
     }
   }
-  __syncthreads();
-
-  // ---------------- merge rows (wave, sub) of each head.  Wave 0 turns
-  // the 64 (wave, row) maxima into merge weights, one lane per row: row r
-  // of wave w belongs to head r % G, so the lanes of one head are those
-  // with equal lane % G, and butterfly shuffles over the other lane bits
-  // give the head's maximum and merged denominator.  The weights include
-  // the division by that denominator.
-  if (PM == 2 && wave == 0) {
+  if (PM == 2 && wave == 0 && lane < G) {
     // FP8-P pass 2: rows hold plain sums of P~ . V (no running max), merged
     // with weight 1; the output factor of head h is prob_scale / w_j with
     // w_j = exp(lse_j - LSE) this split's share of the head's softmax mass
     // (0 for an empty split, whose sum is 0 too).
-    lds_w[lane >> 4][lane & 15] = 1.0f;
-    if (lane < G) {
-      const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + lane;
-      float M2 = -INFINITY;
-      for (int j = 0; j < num_splits; ++j) M2 = fmaxf(M2, a.part_lse[bh * num_splits + j] * kLog2e);
-      float S2 = 0.0f;
-      for (int j = 0; j < num_splits; ++j) {
-        const float l2 = a.part_lse[bh * num_splits + j] * kLog2e;
-        S2 += (l2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(l2 - M2);
-      }
-      const float own = a.part_lse[bh * num_splits + split] * kLog2e;
-      const float wj = (own == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(own - (M2 + log2f(S2)));
-      lds_lse[lane] = wj > 0.0f ? a.prob_scale / wj : 0.0f;
+    const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + lane;
+    float M2 = -INFINITY;
+    for (int j = 0; j < num_splits; ++j) M2 = fmaxf(M2, a.part_lse[bh * num_splits + j] * kLog2e);
+    float S2 = 0.0f;
+    for (int j = 0; j < num_splits; ++j) {
+      const float l2 = a.part_lse[bh * num_splits + j] * kLog2e;
+      S2 += (l2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(l2 - M2);
     }
-  } else if (wave == 0) {
-    const int w = lane >> 4, r = lane & 15;
-    const float mv = lds_m[w][r];
-    float M = mv;
-#pragma unroll
-    for (int x = G; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
-    const float f = (mv == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-    float den = f * lds_l[w][r];
-#pragma unroll
-    for (int x = G; x < 64; x <<= 1) den += __shfl_xor(den, x);
-    lds_w[w][r] = den > 0.0f ? f / den : 0.0f;
-    if (lane < G) lds_lse[lane] = den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+    const float own = a.part_lse[bh * num_splits + split] * kLog2e;
+    const float wj = (own == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(own - (M2 + log2f(S2)));
+    lds_lse[lane] = wj > 0.0f ? a.prob_scale / wj : 0.0f;
   }
   __syncthreads();
+
+  // ---------------- merge of the waves, head h: M = max_w m_w, weights
+  // f_w = exp2(m_w - M) / sum_w f_w l_w (every thread computes those of its
+  // own head from the LDS state: no second barrier), lse = (M + log2 den) ln 2
+  auto wave_weights = [&](int h, float (&wt)[kWaves]) -> float {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_m[w][h]);
+    float den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mv = lds_m[w][h];
+      wt[w] = (mv == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+      den += wt[w] * lds_l[w][h];
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) wt[w] *= inv;
+    return den > 0.0f ? (M + log2f(den)) * kLn2 : -INFINITY;
+  };
   if constexpr (PM == 1) {   // pass 1 writes the split's lse only
     if (threadIdx.x < G) {
+      float wt[kWaves];
       const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + threadIdx.x;
-      a.part_lse[bh * num_splits + split] = lds_lse[threadIdx.x];
+      a.part_lse[bh * num_splits + split] = wave_weights(threadIdx.x, wt);
     }
     return;
   }
   const bool direct = FUSED && num_splits == 1;   // no partials needed
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int h = idx / D, d = idx % D;
-    float num = 0.0f;
+  // items (head h, 64-column block kb) spread over the waves; columns
+  // d = 64 kb + lane; the LDS reads do not wait for the weights
+  constexpr int kBlk = (D + 63) / 64;
+  // blocks per item: as many as spread the G * kBlk blocks over the waves, within one head
+  constexpr int kPer = (G * kBlk / kWaves >= kBlk) ? kBlk : ((G * kBlk >= kWaves) ? G * kBlk / kWaves : 1);
+  for (int it = wave; it * kPer < G * kBlk; it += kWaves) {
+    const int h = (it * kPer) / kBlk;
+    const int kb0 = (it * kPer) % kBlk;
+    float wt[kWaves];
+    float lse = 0.0f;
+    if constexpr (PM == 2) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) num += lds_w[w][s * G + h] * lds_o[w][s * G + h][d];
-    const float o = (PM == 2) ? num * vscale * lds_lse[h] : num * vscale;
-    const float lse = lds_lse[h];
-    const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + h;
-    if (direct) {
-      store_out(fo.out, fo.out_dtype, bh * D + d, o, fo.out_dtype == KVQ_FP8E4M3 ? *fo.out_scale : 1.0f);
-      if (d == 0 && fo.lse_out != nullptr) fo.lse_out[bh] = lse;
+      for (int w = 0; w < kWaves; ++w) wt[w] = 1.0f;
     } else {
-      const int64_t po = bh * num_splits + split;
-      if constexpr (FUSED) {   // device-scope stores: read back by another work-group
-        __hip_atomic_store(a.part_o + po * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (d == 0) __hip_atomic_store(a.part_lse + po, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lse = wave_weights(h, wt);
+    }
+    const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + h;
+    constexpr int kCols = kPer;
+    float sw[kCols][kWaves];
+#pragma unroll
+    for (int k = 0; k < kCols; ++k) {
+      const int d = lane + 64 * (kb0 + k);
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        float x = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) x += (d < D) ? lds_o[w][s * G + h][d] : 0.0f;
+        sw[k][w] = x;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kCols; ++k) {
+      const int d = lane + 64 * (kb0 + k);
+      if (d >= D) continue;
+      float num = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) num += wt[w] * sw[k][w];
+      const float o = (PM == 2) ? num * vscale * lds_lse[h] : num * vscale;
+      if (direct) {
+        store_out(fo.out, fo.out_dtype, bh * D + d, o, fo.out_dtype == KVQ_FP8E4M3 ? *fo.out_scale : 1.0f);
+        if (d == 0 && fo.lse_out != nullptr) fo.lse_out[bh] = lse;
       } else {
-        a.part_o[po * D + d] = o;
-        if (PM == 0 && d == 0) a.part_lse[po] = lse;   // pass 2 keeps pass 1's lse
+        const int64_t po = bh * num_splits + split;
+        if constexpr (FUSED) {   // device-scope stores: read back by another work-group
+          __hip_atomic_store(a.part_o + po * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (d == 0) __hip_atomic_store(a.part_lse + po, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          a.part_o[po * D + d] = o;
+          if (PM == 0 && d == 0) a.part_lse[po] = lse;   // pass 2 keeps pass 1's lse
+        }
       }
     }
   }

@@ -42,8 +42,11 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_auto_split_worked_values(K):
-    # 256 CUs (MI355X): GQA 4:1, B=2, 8 kv heads, 32K -> 32 splits
-    assert K.kvq_auto_num_splits(256, 2, 8, 32768, 128, 32) == 32
+    # 256 CUs (MI355X): GQA 4:1, B=2, 8 kv heads, 32K -> one work-group per
+    # CU (query group of 4): 256 / 16 = 16 splits
+    assert K.kvq_auto_num_splits(256, 2, 8, 32768, 128, 32) == 16
+    # the same shape as MHA (query group of 1): two per CU, 2*256/16 = 32
+    assert K.kvq_auto_num_splits(256, 2, 8, 32768, 128, 8) == 32
     # short context caps at ceil(L / 256)
     assert K.kvq_auto_num_splits(256, 2, 8, 1024, 128, 32) == 4
     # MHA B=1 H=32 32K: 2*256/32 = 16
