@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "../../include/kvq.h"
+#include "wave_reduce.h"
 
 namespace kvq {
 
@@ -46,13 +47,9 @@ template <bool COHERENT>
 __device__ inline float wave_split_weight(const float* lse, int s, float& inv, float& lse_m) {
   const int lane = threadIdx.x & 63;
   const float lj = lane < s ? ld_part<COHERENT>(lse + lane) : -INFINITY;
-  float M = lj;
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x));
+  const float M = lanes::wave_all<lanes::Max>(lj);
   const float wj = (M == -INFINITY || lj == -INFINITY) ? 0.0f : __expf(lj - M);
-  float sum = wj;
-#pragma unroll
-  for (int x = 1; x < 64; x <<= 1) sum += __shfl_xor(sum, x);
+  const float sum = lanes::wave_all<lanes::Sum>(wj);
   inv = sum > 0.0f ? 1.0f / sum : 0.0f;
   lse_m = sum > 0.0f ? M + __logf(sum) : -INFINITY;
   return wj;

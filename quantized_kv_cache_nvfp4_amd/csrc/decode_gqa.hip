@@ -62,6 +62,7 @@
 #include "combine_impl.h"
 #include "decode_common.h"
 #include "kvq_internal.h"
+#include "wave_reduce.h"
 
 namespace kvq {
 namespace {
@@ -133,21 +134,17 @@ __device__ inline void v_pairs(uint32_t vw0, uint32_t vw1, uint32_t vs, f16x2* o
 }
 
 // Rows of one head.  Lane column c of a 16-lane row is MFMA row c = sub * G
-// + h; the rows of head h are the 16 / G columns with c mod G = h.  A DPP
-// rotation by N inside each 16-lane row; the max / sum over the head's rows
-// is an all-reduce by rotations of 8, 4, .. G lanes (every lane of the head
-// receives the same value: each step adds or maxes a pair symmetrically).
-template <int N>
-__device__ inline float row_ror(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
-}
+// + h; the rows of head h are the 16 / G columns with c mod G = h.  The max /
+// sum over the head's rows is an all-reduce by DPP rotations of 8, 4, .. G
+// lanes inside the row (every lane of the head receives the same value:
+// each step adds or maxes a pair symmetrically).
 template <int G, bool SUM>
 __device__ inline float head_rows_reduce(float x) {
   auto op = [](float u, float v) { return SUM ? u + v : fmaxf(u, v); };
-  if constexpr (G <= 8) x = op(x, row_ror<8>(x));
-  if constexpr (G <= 4) x = op(x, row_ror<4>(x));
-  if constexpr (G <= 2) x = op(x, row_ror<2>(x));
-  if constexpr (G <= 1) x = op(x, row_ror<1>(x));
+  if constexpr (G <= 8) x = op(x, lanes::row_ror<8>(x));
+  if constexpr (G <= 4) x = op(x, lanes::row_ror<4>(x));
+  if constexpr (G <= 2) x = op(x, lanes::row_ror<2>(x));
+  if constexpr (G <= 1) x = op(x, lanes::row_ror<1>(x));
   return x;
 }
 
@@ -492,9 +489,8 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
           for (int x = 0; x < NACC; ++x)
 #pragma unroll
             for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[t][x][i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      tmax = head_rows_reduce<G, false>(tmax);   // one maximum per head: its rows add up unweighted
+      tmax = lanes::across_rows<lanes::Max>(tmax);   // the row's max over its four lane groups
+      tmax = head_rows_reduce<G, false>(tmax);        // one maximum per head: its rows add up unweighted
       const bool bump = tmax > m_run;
       if (__any(bump)) {
         const float m_new = bump ? tmax : m_run;
@@ -722,9 +718,8 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
         for (int x = 0; x < NACC; ++x)
 #pragma unroll
           for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sc[x][i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));   // the row's max over its four lane groups
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        tmax = head_rows_reduce<G, false>(tmax);     // and over the head's rows
+        tmax = lanes::across_rows<lanes::Max>(tmax);   // the row's max over its four lane groups
+        tmax = head_rows_reduce<G, false>(tmax);        // and over the head's rows
         if (tmax > m_run) {
           l_run *= __builtin_amdgcn_exp2f(m_run - tmax);   // 0 when m_run = -inf
           m_run = tmax;
@@ -839,8 +834,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   // ---------------- per-wave state -> LDS.  The rows of one head share
   // the running maximum, so within a wave they add up unweighted; each wave
   // leaves one maximum and one denominator per head.
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  float l_tot = lanes::across_rows<lanes::Sum>(l_run);
   l_tot = head_rows_reduce<G, true>(l_tot);
   if (lane < G) {   // lane c = h of lane group 0
     lds_m[wave][lane] = m_run;

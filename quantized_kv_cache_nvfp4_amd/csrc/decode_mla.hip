@@ -33,6 +33,7 @@
 
 #include "decode_common.h"
 #include "kvq_internal.h"
+#include "wave_reduce.h"
 
 #ifndef KVQ_MLA_AHEAD
 #define KVQ_MLA_AHEAD 1
@@ -182,7 +183,8 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     }
 
     // ---- partial scores S^T[token][head] over this wave's halves; stage the f16 rows
-    f32x4 acc_l = {0.f, 0.f, 0.f, 0.f}, acc_r = {0.f, 0.f, 0.f, 0.f};
+    // (two latent accumulators, even and odd steps: half the dependent MFMA chain)
+    f32x4 acc_l[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, acc_r = {0.f, 0.f, 0.f, 0.f};
     // token row 16 th + c, dims 256 dh + 64 g ..; 16-byte chunk k of the row is stored at k ^ swz(row)
     uint8_t* stage = lds_c + (16 * th + c) * kPitch + 512 * dh + 128 * g;
     uint8_t* const stage_even = stage + 16 * swz_w;   // chunks with even k move by +16 bytes when swz = 1
@@ -194,13 +196,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
       const _Float16 sv = (j < 4) ? ((j < 2) ? sp0[0] : sp0[1]) : ((j < 6) ? sp1[0] : sp1[1]);   // block j/2
       const f16x2 s2 = {sv, sv};
       const f16x8 kop = cat4(fp4x2<0>(w) * s2, fp4x2<1>(w) * s2, fp4x2<2>(w) * s2, fp4x2<3>(w) * s2);
-      acc_l = mfma(kop, qop[j], acc_l);
+      acc_l[j & 1] = mfma(kop, qop[j], acc_l[j & 1]);
       *reinterpret_cast<f16x8*>(((j & 1) ? stage_odd : stage_even) + 16 * j) = kop;
     }
     acc_r = mfma_bf16(__builtin_bit_cast(bf16x8, rw), qr, acc_r);
     f32x4 ps;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ps[i] = acc_l[i] * sc_lat + acc_r[i] * sc_rope;
+    for (int i = 0; i < 4; ++i) ps[i] = (acc_l[0][i] + acc_l[1][i]) * sc_lat + acc_r[i] * sc_rope;
     lds_s[wave][lane] = ps;
     __syncthreads();   // staged rows and partial scores visible
 
@@ -221,8 +223,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     }
     float tm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    tm = lanes::across_rows<lanes::Max>(tm);   // head c's max over the four lane groups
     if (__any(tm > m_run)) {   // the same decision for column c in every wave
       const bool bump = tm > m_run;
       const float fac = bump ? __builtin_amdgcn_exp2f(m_run - tm) : 1.0f;   // 0 when m_run = -inf
@@ -277,8 +278,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
   }
 
   // ---- partials: o = acc * s_t / l, lse = (m + log2 l) ln 2 (l is the same in every wave)
-  float lt = l_run + __shfl_xor(l_run, 16);
-  lt += __shfl_xor(lt, 32);
+  const float lt = lanes::across_rows<lanes::Sum>(l_run);
   const float f = lt > 0.0f ? s_t / lt : 0.0f;
   const int64_t po = (static_cast<int64_t>(b) * a.Hq + c) * num_splits + split;
   float* op = a.part_o + po * kD + 128 * wave + 4 * g;
