@@ -168,19 +168,24 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc_o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](const Raw& cur, int tile) {
+  auto process = [&](Raw& cur, int tile) {
     const int tb = cs + tile * kT;
-    u32x4 cw0 = cur.cw0, cw1 = cur.cw1, rw = cur.rw;
-    uint32_t sw = cur.sw;
     // the chunk's last tile: rows of tokens at or past the request's end
     // (read before the length was known) become zeros, so that the staged
-    // latent of masked tokens is 0 (their probability is 0)
-    if (tb + kT > ce && tb + 16 * th + c >= ce) {
-      cw0 = u32x4{0u, 0u, 0u, 0u};
-      cw1 = cw0;
-      rw = cw0;
-      sw = 0u;
+    // latent of masked tokens is 0 (their probability is 0).  (The empty asm
+    // keeps this a branch taken once per chunk instead of selects on every
+    // tile.)
+    if (tb + kT > ce) {
+      asm volatile("");
+      if (tb + 16 * th + c >= ce) {
+        cur.cw0 = u32x4{0u, 0u, 0u, 0u};
+        cur.cw1 = cur.cw0;
+        cur.rw = cur.cw0;
+        cur.sw = 0u;
+      }
     }
+    const u32x4 cw0 = cur.cw0, cw1 = cur.cw1, rw = cur.rw;
+    const uint32_t sw = cur.sw;
 
     // ---- partial scores S^T[token][head] over this wave's halves; stage the f16 rows
     // (two latent accumulators, even and odd steps: half the dependent MFMA chain)
@@ -215,6 +220,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
       for (int i = 0; i < 4; ++i) sc[x][i] = p0[i] + p1[i];
     }
     if (tb + kT > ce) {   // the chunk's last tile (uniform branch)
+      asm volatile("");
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
