@@ -252,6 +252,54 @@ __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, i
     }
     const int64_t items = n2 * nrun;
     const int64_t base = i0 * r.s0 + i1 * r.s1;
+    const size_t esz = (dt == KVQ_F32) ? 4 : 2;
+    if (r.s2 == d && d % 8 == 0 && (reinterpret_cast<uintptr_t>(static_cast<const uint8_t*>(x) + base * esz) & 15u) == 0) {
+      // contiguous rows: the head is one flat run of n2 * d elements, read
+      // as 16-byte vectors with no per-load branches, eight loads in flight
+      // per thread (the grid is kept small so that the per-work-group
+      // atomics stay few)
+      constexpr int U = 8;
+      const int64_t stride = head_items_stride();
+      const int64_t start = head_items_start();
+      if (dt == KVQ_F32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + base);
+        int64_t it = start;
+        for (; it + (U - 1) * stride < items; it += U * stride) {
+          float4 w[U][2];
+#pragma unroll
+          for (int u = 0; u < U; ++u) { w[u][0] = p[2 * (it + u * stride)]; w[u][1] = p[2 * (it + u * stride) + 1]; }
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+              m = fmaxf(m, fmaxf(fmaxf(fabsf(w[u][k].x), fabsf(w[u][k].y)), fmaxf(fabsf(w[u][k].z), fabsf(w[u][k].w))));
+        }
+        for (; it < items; it += stride) {
+          const float4 a = p[2 * it], b2 = p[2 * it + 1];
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(b2.x), fabsf(b2.y)), fmaxf(fabsf(b2.z), fabsf(b2.w))));
+        }
+      } else {
+        // bf16: |x| of a pair = the two halves with the sign bits cleared
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + base);
+        auto fold = [&](const uint4 w) {
+          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            m = fmaxf(m, fmaxf(__uint_as_float((ws[k] << 16) & 0x7FFF0000u), __uint_as_float(ws[k] & 0x7FFF0000u)));
+        };
+        int64_t it = start;
+        for (; it + (U - 1) * stride < items; it += U * stride) {
+          uint4 w[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) w[u] = p[it + u * stride];
+#pragma unroll
+          for (int u = 0; u < U; ++u) fold(w[u]);
+        }
+        for (; it < items; it += stride) fold(p[it]);
+      }
+      continue;
+    }
     for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
       const int64_t t = it / nrun;
       const int run = static_cast<int>(it - t * nrun);
