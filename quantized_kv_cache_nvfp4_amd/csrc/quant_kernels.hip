@@ -164,6 +164,16 @@ __device__ inline float fp8_tensor_scale(float amax) {
 // it is exact in float64 and every comparison is the exact real one.  Ties
 // go to the even code: strictly above 0.25, 1.25, 2.5 and 5, at or above
 // 0.75, 1.75 and 3.5.  (The same decisions as rounding the quotient.)
+// float32 neighbours of a positive double t: round down / round up
+__device__ inline float f32_rd(double t) {
+  const float f = static_cast<float>(t);
+  return static_cast<double>(f) > t ? __uint_as_float(__float_as_uint(f) - 1u) : f;
+}
+__device__ inline float f32_ru(double t) {
+  const float f = static_cast<float>(t);
+  return static_cast<double>(f) < t ? __uint_as_float(__float_as_uint(f) + 1u) : f;
+}
+
 __device__ inline uint32_t encode_nvfp4_block(const float* v, float s_t, uint32_t* c) {
   float bamax = 0.0f;
 #pragma unroll
@@ -174,15 +184,23 @@ __device__ inline uint32_t encode_nvfp4_block(const float* v, float s_t, uint32_
     for (int i = 0; i < 16; ++i) c[i] = 0;
     return 0;
   }
+  // The seven thresholds t_k = midpoint_k * D (exact in float64), compared
+  // with the float32 |x| through float32 neighbours: for a float32 a,
+  // a > t <=> a > RD(t) and a >= t <=> a >= RU(t) (no float32 lies between
+  // RD(t) and RU(t)), so every comparison below is the exact real one.  The
+  // code is the number of thresholds passed, found by a three-level binary
+  // search (levels 1 and 2 use the "at or above" thresholds 1.75, 0.75 /
+  // 3.5, level 3 the "above" ones 0.25 / 1.25 / 2.5 / 5).
   const double den = e4m3_value(sc) * static_cast<double>(s_t);  // exact
-  const double t0 = 0.25 * den, t1 = 0.75 * den, t2 = 1.25 * den, t3 = 1.75 * den;
-  const double t4 = 2.5 * den, t5 = 3.5 * den, t6 = 5.0 * den;
+  const float t0 = f32_rd(0.25 * den), t1 = f32_ru(0.75 * den), t2 = f32_rd(1.25 * den), t3 = f32_ru(1.75 * den);
+  const float t4 = f32_rd(2.5 * den), t5 = f32_ru(3.5 * den), t6 = f32_rd(5.0 * den);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const double ax = fabs(static_cast<double>(v[i]));
-    uint32_t q = static_cast<uint32_t>(ax > t0) + static_cast<uint32_t>(ax >= t1) + static_cast<uint32_t>(ax > t2) +
-                 static_cast<uint32_t>(ax >= t3) + static_cast<uint32_t>(ax > t4) + static_cast<uint32_t>(ax >= t5) +
-                 static_cast<uint32_t>(ax > t6);
+    const float ax = fabsf(v[i]);
+    const bool b1 = ax >= t3;
+    const bool b2 = ax >= (b1 ? t5 : t1);
+    const bool b3 = ax > (b1 ? (b2 ? t6 : t4) : (b2 ? t2 : t0));
+    uint32_t q = (b1 ? 4u : 0u) | (b2 ? 2u : 0u) | (b3 ? 1u : 0u);
     q = (ax != ax) ? 7u : q;   // NaN: as the quotient path (not below 6 -> saturate)
     c[i] = q | ((__float_as_uint(v[i]) >> 28) & 8u);
   }
