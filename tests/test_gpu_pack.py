@@ -54,6 +54,42 @@ def test_amax_masks_ragged_padding():
     assert float(out.item()) == 1e6
 
 
+@pytest.mark.parametrize("case", ["f32_flat", "bf16_strided", "bf16_misaligned", "bf16_d20"])
+def test_amax_layouts(case):
+    """amax over rows read as one flat run (contiguous, 16-byte aligned, d %
+    8 == 0) and through the general row walk (strided rows, an unaligned
+    base, d not a multiple of 8), with ragged lengths; exact against the
+    oracle's max."""
+    announce(f"amax layout {case}")
+    g = torch.Generator().manual_seed(11)
+    B, H, L = 3, 2, 37
+    lens_np = np.array([37, 5, 0], dtype=np.int32)
+    if case == "f32_flat":
+        x = torch.randn(B, H, L, 64, generator=g, dtype=torch.float32) * 3
+    elif case == "bf16_strided":
+        x = (torch.randn(B, H, L, 80, generator=g) * 3).to(torch.bfloat16)[..., 8:72]
+    elif case == "bf16_misaligned":
+        flat = (torch.randn(B * H * L * 64 + 1, generator=g) * 3).to(torch.bfloat16)
+        x = flat[1:].view(B, H, L, 64)
+    else:
+        x = (torch.randn(B, H, L, 20, generator=g) * 3).to(torch.bfloat16)
+    x[0, 1, 36, 3] = -50.0                   # the maximum of a full-length request
+    x[1, 0, 20, 2] = 1e4                     # past request 1's length: excluded
+    xd = x.to(DEV)
+    if case == "bf16_strided":
+        xd = torch.empty(B, H, L, 80, dtype=torch.bfloat16, device=DEV)[..., 8:72]
+        xd.copy_(x)
+    elif case == "bf16_misaligned":
+        fd = torch.empty(B * H * L * 64 + 1, dtype=torch.bfloat16, device=DEV)
+        xd = fd[1:].view(B, H, L, 64)
+        xd.copy_(x)
+    lens = torch.from_numpy(lens_np).to(DEV)
+    got = float(K().kvq_amax(xd, lens).item())
+    assert got == OQ.amax(kvq_synth.f64(x), lens_np) == 50.0
+    big = float(x[1, 0, 20, 2].abs())
+    assert float(K().kvq_amax(xd).item()) == OQ.amax(kvq_synth.f64(x)) == big
+
+
 def _adversarial_rows():
     """Rows that sit on every E2M1 / E4M3 decision boundary, plus zeros, -0,
     subnormal block scales and saturation; one 2688-scaled anchor fixes s_t."""
