@@ -13,17 +13,19 @@
 //  * one work-group = 4 waves = one chunk of one request; all 16 query
 //    heads share every latent row, so they are the 16 MFMA rows and no
 //    query-group packing is needed.
-//  * tiles of 32 tokens.  Scores: wave w covers token half (w & 1) of the
-//    tile over latent half (w >> 1) (256 dims) and rope half (32 dims): 8
-//    MFMA 16x16x32 f16 steps over the dequantized latent plus one bf16 step
-//    over the rope; the two latent halves' partial scores meet in LDS.  The
-//    dequantized latent rows (f16) are staged in LDS.
-//  * P.V: wave w owns output columns 128w .. 128w+127 for all 32 tokens;
-//    its A operand (latent, token-contiguous per column) comes from the
-//    staged rows through the LDS transpose read ds_read_b64_tr_b16, so the
-//    latent is dequantized once and used by both contractions, and its B
-//    operand (P) is already in the right lanes (the token order of the P.V
-//    contraction is chosen to match the score layout).
+//  * tiles of 64 tokens (4 sub-tiles of 16).  Scores: wave w covers the
+//    sub-tiles u = (w & 1) + 2q of the tile over latent half (w >> 1) (256
+//    dims) and rope half (32 dims): per sub-tile 8 MFMA 16x16x32 f16 steps
+//    over the dequantized latent plus one bf16 step over the rope; the two
+//    latent halves' partial scores meet in LDS.  The dequantized latent rows
+//    (f16) are staged in LDS.  Two barriers per tile.
+//  * P.V: wave w owns output columns 128w .. 128w+127 for all 64 tokens (two
+//    32-token steps); its A operand (latent, token-contiguous per column)
+//    comes from the staged rows through the LDS transpose read
+//    ds_read_b64_tr_b16, so the latent is dequantized once and used by both
+//    contractions, and its B operand (P) is already in the right lanes (the
+//    token order of the P.V contraction is chosen to match the score
+//    layout).
 //  * every wave computes the softmax of the whole tile (8 scores per lane),
 //    so the four waves share one reference maximum and one denominator.
 //  * loads use buffer resources sized to the chunk (tokens past its end read
@@ -38,6 +40,9 @@
 #ifndef KVQ_MLA_AHEAD
 #define KVQ_MLA_AHEAD 1
 #endif
+#ifndef KVQ_MLA_TILE
+#define KVQ_MLA_TILE 64
+#endif
 
 namespace kvq {
 namespace {
@@ -50,7 +55,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kW = 4;                      // waves per work-group
 constexpr int kThreads = 64 * kW;
-constexpr int kT = 32;                     // tokens per tile
+constexpr int kT = KVQ_MLA_TILE;           // tokens per tile (32 or 64)
+constexpr int kQ = kT / 32;                // 16-token sub-tiles per wave: u = th + 2 q, q < kQ
 constexpr int kH = 16;                     // query heads (MFMA rows)
 constexpr int kD = 512;                    // latent rank
 constexpr int kDr = 64;                    // rope dims
@@ -65,7 +71,7 @@ __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, int num_splits) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_c[kT * kPitch];   // staged latent rows (f16)
-  __shared__ __attribute__((aligned(16))) f32x4 lds_s[kW][64];          // partial scores per wave / lane
+  __shared__ __attribute__((aligned(16))) f32x4 lds_s[kW][kQ][64];      // partial scores per wave, sub-tile, lane
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -96,23 +102,27 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
   const uint8_t* csc = a.k_scales + row0 * kSRow;
   const uint8_t* cr = static_cast<const uint8_t*>(a.k_rope) + row0 * (kDr * 2);
 
-  // loads of one tile: token c; latent bytes [128 dh + 32 g, +32), scale
-  // bytes [16 dh + 4 g, +4), rope bytes [64 dh + 16 g, +16).  Tokens at or
-  // past the load bound ce_ld read zeros; a tile past it reads nothing.
+  // loads of one tile: for each of the wave's sub-tiles u = th + 2 q, token
+  // 16 u + c; latent bytes [128 dh + 32 g, +32), scale bytes [16 dh + 4 g,
+  // +4), rope bytes [64 dh + 16 g, +16).  Tokens at or past the load bound
+  // ce_ld read zeros; a tile past it reads nothing.
   struct Raw {
-    u32x4 cw0, cw1, rw;
-    uint32_t sw;
+    u32x4 cw0[kQ], cw1[kQ], rw[kQ];
+    uint32_t sw[kQ];
   };
   auto load_tile = [&](Raw& R, int tile) {
-    const int t0 = cs + tile * kT + 16 * th;
-    const int nv = ce_ld - t0;
-    const Rsrc rc_ = make_rsrc(cc + static_cast<int64_t>(t0) * st * kRow, nv * st * kRow);
-    const Rsrc rs_ = make_rsrc(csc + static_cast<int64_t>(t0) * st * kSRow, nv * st * kSRow);
-    const Rsrc rr_ = make_rsrc(cr + static_cast<int64_t>(t0) * st * (kDr * 2), nv * st * (kDr * 2));
-    R.cw0 = ld128(rc_, c * st * kRow + 128 * dh + 32 * g);
-    R.cw1 = ld128(rc_, c * st * kRow + 128 * dh + 32 * g + 16);
-    R.sw = ld32(rs_, c * st * kSRow + 16 * dh + 4 * g);
-    R.rw = ld128(rr_, c * st * (kDr * 2) + 64 * dh + 16 * g);
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int t0 = cs + tile * kT + 16 * (th + 2 * q);
+      const int nv = ce_ld - t0;
+      const Rsrc rc_ = make_rsrc(cc + static_cast<int64_t>(t0) * st * kRow, nv * st * kRow);
+      const Rsrc rs_ = make_rsrc(csc + static_cast<int64_t>(t0) * st * kSRow, nv * st * kSRow);
+      const Rsrc rr_ = make_rsrc(cr + static_cast<int64_t>(t0) * st * (kDr * 2), nv * st * (kDr * 2));
+      R.cw0[q] = ld128(rc_, c * st * kRow + 128 * dh + 32 * g);
+      R.cw1[q] = ld128(rc_, c * st * kRow + 128 * dh + 32 * g + 16);
+      R.sw[q] = ld32(rs_, c * st * kSRow + 16 * dh + 4 * g);
+      R.rw[q] = ld128(rr_, c * st * (kDr * 2) + 64 * dh + 16 * g);
+    }
   };
   // ---- query words, lane (g, c) = head c:
   //   latent MFMA j (0..7): dims 256 dh + 64 g + 8 j + e; rope: 32 dh + 8 g + e
@@ -177,58 +187,70 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     // tile.)
     if (tb + kT > ce) {
       asm volatile("");
-      if (tb + 16 * th + c >= ce) {
-        cur.cw0 = u32x4{0u, 0u, 0u, 0u};
-        cur.cw1 = cur.cw0;
-        cur.rw = cur.cw0;
-        cur.sw = 0u;
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        if (tb + 16 * (th + 2 * q) + c >= ce) {
+          cur.cw0[q] = u32x4{0u, 0u, 0u, 0u};
+          cur.cw1[q] = cur.cw0[q];
+          cur.rw[q] = cur.cw0[q];
+          cur.sw[q] = 0u;
+        }
       }
     }
-    const u32x4 cw0 = cur.cw0, cw1 = cur.cw1, rw = cur.rw;
-    const uint32_t sw = cur.sw;
 
-    // ---- partial scores S^T[token][head] over this wave's halves; stage the f16 rows
-    // (two latent accumulators, even and odd steps: half the dependent MFMA chain)
-    f32x4 acc_l[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, acc_r = {0.f, 0.f, 0.f, 0.f};
-    // token row 16 th + c, dims 256 dh + 64 g ..; 16-byte chunk k of the row is stored at k ^ swz(row)
-    uint8_t* stage = lds_c + (16 * th + c) * kPitch + 512 * dh + 128 * g;
-    uint8_t* const stage_even = stage + 16 * swz_w;   // chunks with even k move by +16 bytes when swz = 1
-    uint8_t* const stage_odd = stage - 16 * swz_w;    // odd k by -16
-    const f16x2 sp0 = fp8x2<false>(sw), sp1 = fp8x2<true>(sw);             // scales of the lane's 4 blocks
+    // ---- partial scores S^T[token][head] of the wave's sub-tiles over its
+    // latent / rope halves; stage the f16 rows.  (Two latent accumulators,
+    // even and odd steps: half the dependent MFMA chain.)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w = (j < 4) ? cw0[j] : cw1[j - 4];
-      const _Float16 sv = (j < 4) ? ((j < 2) ? sp0[0] : sp0[1]) : ((j < 6) ? sp1[0] : sp1[1]);   // block j/2
-      const f16x2 s2 = {sv, sv};
-      const f16x8 kop = cat4(fp4x2<0>(w) * s2, fp4x2<1>(w) * s2, fp4x2<2>(w) * s2, fp4x2<3>(w) * s2);
-      acc_l[j & 1] = mfma(kop, qop[j], acc_l[j & 1]);
-      *reinterpret_cast<f16x8*>(((j & 1) ? stage_odd : stage_even) + 16 * j) = kop;
+    for (int q = 0; q < kQ; ++q) {
+      const u32x4 cw0 = cur.cw0[q], cw1 = cur.cw1[q], rw = cur.rw[q];
+      const uint32_t sw = cur.sw[q];
+      f32x4 acc_l[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, acc_r = {0.f, 0.f, 0.f, 0.f};
+      // token row 16 u + c (u = th + 2 q), dims 256 dh + 64 g ..; 16-byte
+      // chunk k of the row is stored at k ^ swz(row) (swz uses row bits 2
+      // and 3, those of c)
+      uint8_t* stage = lds_c + (16 * (th + 2 * q) + c) * kPitch + 512 * dh + 128 * g;
+      uint8_t* const stage_even = stage + 16 * swz_w;   // chunks with even k move by +16 bytes when swz = 1
+      uint8_t* const stage_odd = stage - 16 * swz_w;    // odd k by -16
+      const f16x2 sp0 = fp8x2<false>(sw), sp1 = fp8x2<true>(sw);             // scales of the lane's 4 blocks
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t w = (j < 4) ? cw0[j] : cw1[j - 4];
+        const _Float16 sv = (j < 4) ? ((j < 2) ? sp0[0] : sp0[1]) : ((j < 6) ? sp1[0] : sp1[1]);   // block j/2
+        const f16x2 s2 = {sv, sv};
+        const f16x8 kop = cat4(fp4x2<0>(w) * s2, fp4x2<1>(w) * s2, fp4x2<2>(w) * s2, fp4x2<3>(w) * s2);
+        acc_l[j & 1] = mfma(kop, qop[j], acc_l[j & 1]);
+        *reinterpret_cast<f16x8*>(((j & 1) ? stage_odd : stage_even) + 16 * j) = kop;
+      }
+      acc_r = mfma_bf16(__builtin_bit_cast(bf16x8, rw), qr, acc_r);
+      f32x4 ps;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps[i] = (acc_l[0][i] + acc_l[1][i]) * sc_lat + acc_r[i] * sc_rope;
+      lds_s[wave][q][lane] = ps;
     }
-    acc_r = mfma_bf16(__builtin_bit_cast(bf16x8, rw), qr, acc_r);
-    f32x4 ps;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ps[i] = (acc_l[0][i] + acc_l[1][i]) * sc_lat + acc_r[i] * sc_rope;
-    lds_s[wave][lane] = ps;
     __syncthreads();   // staged rows and partial scores visible
 
-    // ---- the whole tile's scores for this lane: tokens 4g+i of half 0 (x = 0) and half 1 (x = 1)
-    float sc[2][4];
+    // ---- the whole tile's scores for this lane: tokens 16 u + 4 g + i of
+    // every sub-tile u (latent halves: waves (u & 1) and 2 + (u & 1))
+    float sc[2 * kQ][4];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const f32x4 p0 = lds_s[x][lane], p1 = lds_s[2 + x][lane];   // latent halves 0 and 1
+    for (int u = 0; u < 2 * kQ; ++u) {
+      const f32x4 p0 = lds_s[u & 1][u >> 1][lane], p1 = lds_s[2 + (u & 1)][u >> 1][lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[x][i] = p0[i] + p1[i];
+      for (int i = 0; i < 4; ++i) sc[u][i] = p0[i] + p1[i];
     }
     if (tb + kT > ce) {   // the chunk's last tile (uniform branch)
       asm volatile("");
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int u = 0; u < 2 * kQ; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (tb + 16 * x + 4 * g + i >= ce) sc[x][i] = -INFINITY;
+          if (tb + 16 * u + 4 * g + i >= ce) sc[u][i] = -INFINITY;
     }
-    float tm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    float tm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2 * kQ; ++u)
+      tm = fmaxf(tm, fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
     tm = lanes::across_rows<lanes::Max>(tm);   // head c's max over the four lane groups
     if (__any(tm > m_run)) {   // the same decision for column c in every wave
       const bool bump = tm > m_run;
@@ -241,33 +263,42 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
       m_run = bump ? tm : m_run;
     }
     const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
-    // B operand of P.V (k = 8g + e): e < 4 -> token 4g+e of half 0, e >= 4 -> token 4g+e-4 of half 1
-    f16x2 ph[4];
+    // B operand of P.V step ks (k = 8g + e): e < 4 -> token 4g+e of sub-tile
+    // 2 ks, e >= 4 -> token 4g+e-4 of sub-tile 2 ks + 1
+    f16x8 pb[kQ];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int ks = 0; ks < kQ; ++ks) {
+      f16x2 ph[4];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const float p0 = __builtin_amdgcn_exp2f(sc[x][2 * k] - m_ref);   // masked: exp2(-inf) = 0
-        const float p1 = __builtin_amdgcn_exp2f(sc[x][2 * k + 1] - m_ref);
-        l_run += p0 + p1;
-        ph[2 * x + k] = f16x2{static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
-      }
-    const f16x8 pb = cat4(ph[0], ph[1], ph[2], ph[3]);
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float p0 = __builtin_amdgcn_exp2f(sc[2 * ks + x][2 * k] - m_ref);   // masked: exp2(-inf) = 0
+          const float p1 = __builtin_amdgcn_exp2f(sc[2 * ks + x][2 * k + 1] - m_ref);
+          l_run += p0 + p1;
+          ph[2 * x + k] = f16x2{static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
+        }
+      pb[ks] = cat4(ph[0], ph[1], ph[2], ph[3]);
+    }
 
-    // ---- P.V for this wave's 128 output columns over the 32 tokens.  A =
-    // latent^T rows d, k = the tokens above: two transposed reads of 4
-    // token rows; lane m of the 16-lane group points at row r + m/4, columns
-    // d0 + 4(m%4) .. +3, and receives column d0 + m of the 4 rows.
-    const int rlo = 4 * g + (c >> 2), rhi = 16 + 4 * g + (c >> 2);   // both have swz = swz_r
+    // ---- P.V for this wave's 128 output columns over the tile's tokens,
+    // 32 per step.  A = latent^T rows d, k = the tokens above: two
+    // transposed reads of 4 token rows; lane m of the 16-lane group points
+    // at row r + m/4, columns d0 + 4(m%4) .. +3, and receives column d0 + m
+    // of the 4 rows.
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int col = 256 * wave + 32 * jj + 16 * (((c >> 1) & 1) ^ swz_r) + 8 * (c & 1);
-      const f16x4 lo = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(lds_c + rlo * kPitch + col)));
-      const f16x4 hi = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(lds_c + rhi * kPitch + col)));
-      const f16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc_o[jj] = mfma(av, pb, acc_o[jj]);
+    for (int ks = 0; ks < kQ; ++ks) {
+      const int rlo = 32 * ks + 4 * g + (c >> 2), rhi = 32 * ks + 16 + 4 * g + (c >> 2);   // both have swz = swz_r
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int col = 256 * wave + 32 * jj + 16 * (((c >> 1) & 1) ^ swz_r) + 8 * (c & 1);
+        const f16x4 lo = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(lds_c + rlo * kPitch + col)));
+        const f16x4 hi = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(lds_c + rhi * kPitch + col)));
+        const f16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc_o[jj] = mfma(av, pb[ks], acc_o[jj]);
+      }
     }
     __syncthreads();   // the tile's LDS may be overwritten
   };
