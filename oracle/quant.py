@@ -27,6 +27,14 @@ Definitions followed
   code = E4M3(x / scale); amax == 0 gives scale 1 (Model-Optimizer PR #673:
   a missing KV scale is served as 1).
 
+* FP8 per kv head (compressed-tensors PR #436, "Changes": the ``attn_head``
+  strategy of ``_flatten_attention``; "Testing": ``strategy="attn_head"``,
+  symmetric, ``static_minmax`` observer, the KV-FP8-Head rows of the GSM8K
+  table).  Reading taken: the K (or V) tensor is split along the kv-head
+  axis and each head's slice is quantized exactly as a per-tensor FP8 tensor
+  of its own: amax_h over the head's valid tokens of every request, scale_h =
+  amax_h / 448.
+
 Why float64 decides exactly: x has at most 24 significant bits; a threshold
 (E2M1 midpoint * s_hat * s_t, or E4M3 midpoint * 6 * s_t) has at most 32.  Two
 such dyadic numbers that differ do so by at least 2^-32 relative, far above
@@ -128,3 +136,38 @@ def fp8_pack(x, amax_value):
 def fp8_unpack(codes, scale):
     """Exact float64 dequantization E4M3(code) * scale."""
     return F.e4m3_decode(np.asarray(codes, dtype=np.uint8)) * np.float64(scale)
+
+
+def amax_heads(x, kv_lens=None, head_axis=1, token_axis=-2):
+    """Per-kv-head max |x| over valid tokens: one float per index of
+    ``head_axis`` (the ``attn_head`` observer), each an element of x."""
+    x = np.asarray(x, dtype=np.float64)
+    ha = head_axis % x.ndim
+    return np.array([amax(np.take(x, h, axis=ha), kv_lens, token_axis=token_axis if token_axis < 0 else token_axis - (token_axis > ha))
+                     for h in range(x.shape[ha])], dtype=np.float64)
+
+
+def fp8_pack_heads(x, amax_values, head_axis=1):
+    """FP8 E4M3 with one scale per kv head: head h's slice is quantized as a
+    per-tensor FP8 tensor with amax_values[h].  Returns (codes uint8, same
+    shape as x; scales float64 [H])."""
+    x = np.asarray(x, dtype=np.float64)
+    ha = head_axis % x.ndim
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[ha], dtype=np.float64)
+    for h in range(x.shape[ha]):
+        c, sc = fp8_pack(np.take(x, h, axis=ha), amax_values[h])
+        idx = [slice(None)] * x.ndim
+        idx[ha] = h
+        codes[tuple(idx)] = c
+        scales[h] = sc
+    return codes, scales
+
+
+def fp8_unpack_heads(codes, scales, head_axis=1):
+    """Exact float64 dequantization with one scale per kv head."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    ha = head_axis % codes.ndim
+    shape = [1] * codes.ndim
+    shape[ha] = codes.shape[ha]
+    return F.e4m3_decode(codes) * np.asarray(scales, dtype=np.float64).reshape(shape)

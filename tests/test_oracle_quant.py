@@ -281,3 +281,47 @@ def test_amax_masks_padding():
     y[1, 5, 0] = 3.0
     y[0, 2, 7] = -2.0
     assert Q.amax(y, kv_lens=[6, 5], token_axis=1) == 2.0
+
+
+# ------------------------------------------------------------ FP8 per kv head
+def test_fp8_heads_worked_example():
+    """Hand-worked: head 0 has amax 448 (scale 1), head 1 amax 3.5 (scale
+    2^-7, exact).  0.78125 sits on an E4M3 midpoint in both heads: in head 0
+    between 0.75 and 0.8125 -> 0.75 (even mantissa, code 0x34); in head 1
+    0.78125 / 2^-7 = 100 lies between 96 and 104 -> 96 (code 0x6C).  Each
+    head's max maps to 448 (0x7E); a negative value keeps the sign bit."""
+    x = np.zeros((1, 2, 2, 4))
+    x[0, 0, 0, 0], x[0, 1, 1, 3] = 448.0, -3.5
+    x[0, 0, 1, 2] = x[0, 1, 0, 1] = 0.78125
+    a = Q.amax_heads(x)
+    assert list(a) == [448.0, 3.5]
+    codes, scales = Q.fp8_pack_heads(x, a)
+    assert list(scales) == [1.0, 2.0 ** -7]
+    assert codes[0, 0, 1, 2] == 0x34 and codes[0, 1, 0, 1] == 0x6C
+    assert codes[0, 0, 0, 0] == 0x7E and codes[0, 1, 1, 3] == 0xFE
+    # per tensor the same value in head 1 would use scale 1
+    pt, _ = Q.fp8_pack(x, Q.amax(x))
+    assert pt[0, 1, 0, 1] == 0x34
+    back = Q.fp8_unpack_heads(codes, scales)
+    assert back[0, 1, 0, 1] == 96 * 2.0 ** -7 and back[0, 1, 1, 3] == -3.5
+
+
+def test_fp8_heads_reduce_to_per_tensor():
+    """Invariants: the largest head amax is the tensor amax; with every head
+    given the tensor amax, per-head packing equals per-tensor packing; each
+    head's codes equal the per-tensor packing of that head alone."""
+    rng = np.random.default_rng(5)
+    x = kvq_synth.f64(torch.from_numpy(rng.standard_normal((3, 4, 33, 16)) * rng.uniform(0.1, 30, (1, 4, 1, 1))).to(torch.bfloat16))
+    lens = np.array([33, 7, 1], dtype=np.int32)
+    a = Q.amax_heads(x, lens)
+    assert a.max() == Q.amax(x, lens)
+    for h in range(4):
+        assert a[h] == Q.amax(x[:, h], lens)
+    full = np.full(4, Q.amax(x, lens))
+    c_all, s_all = Q.fp8_pack_heads(x, full)
+    c_pt, s_pt = Q.fp8_pack(x, Q.amax(x, lens))
+    assert np.array_equal(c_all, c_pt) and np.all(s_all == s_pt)
+    c_h, s_h = Q.fp8_pack_heads(x, a)
+    for h in range(4):
+        c1, s1 = Q.fp8_pack(x[:, h], a[h])
+        assert np.array_equal(c_h[:, h], c1) and s_h[h] == s1
