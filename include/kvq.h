@@ -135,6 +135,16 @@ int kvq_amax(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const i
              float* amax_out, int32_t accumulate, void* stream);
 
 /*
+ * kvq_amax_heads - one max |x| per kv head (the attn_head strategy:
+ * compressed-tensors PR #436, Changes, "attn_head" in _flatten_attention;
+ * Testing, strategy="attn_head" with the static_minmax observer): amax_out[h]
+ * is the max over the rows with i1 == h (all i0, i2 < kv_lens[i0]).
+ * Arguments as kvq_amax; amax_out is device float[x_rows.n1].
+ */
+int kvq_amax_heads(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const int32_t* kv_lens,
+                   float* amax_out, int32_t accumulate, void* stream);
+
+/*
  * kvq_pack_nvfp4 - quantize rows to NVFP4 (Model-Optimizer PR #714, Testing
  * section quantizer dump).
  *   x            device, KVQ_F32 or KVQ_BF16, rows per x_rows, d elements each.
@@ -166,6 +176,17 @@ int kvq_pack_fp8(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, con
                  float* scale_out, void* stream);
 
 /*
+ * kvq_pack_fp8_heads - FP8 E4M3 with one scale per kv head (the attn_head
+ * strategy, compressed-tensors PR #436): the rows with i1 == h are quantized
+ * with scale_h = amax[h] / 448 (1 if amax[h] == 0), exactly as kvq_pack_fp8
+ * quantizes a whole tensor.  Arguments as kvq_pack_fp8, except amax (device
+ * float[x_rows.n1]) and scale_out (device float[x_rows.n1] or NULL).
+ */
+int kvq_pack_fp8_heads(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax,
+                       uint8_t* codes, kvq_rows dst_rows, int32_t dst_layout, const int32_t* dst_pos,
+                       float* scale_out, void* stream);
+
+/*
  * Batched packing: several planes (for instance the K and the V rows of the
  * new tokens of one decode step) quantized in ONE launch.  Each job carries
  * exactly the arguments of one kvq_pack_nvfp4 / kvq_pack_fp8 call (scales
@@ -188,6 +209,8 @@ typedef struct {
   int32_t dst_layout;
   const int32_t* dst_pos;
   float* scale_out;
+  int32_t scale_per_head;   /* FP8 only: 1 = amax and scale_out hold one
+                               value per i1 (kvq_pack_fp8_heads), 0 = one */
 } kvq_pack_job;
 
 int kvq_pack_nvfp4_batch(const kvq_pack_job* jobs, int32_t n_jobs, void* stream);
@@ -237,7 +260,8 @@ typedef struct {
   int64_t qr_sb, qr_sh;
   const uint8_t* k_codes;   /* device plane (NVFP4: d/2 B rows; FP8: d B rows) */
   const uint8_t* k_scales;  /* device NVFP4 scale plane (d/16 B rows); NULL for FP8 */
-  const float* k_scale;     /* device float[1]: s_t (NVFP4) or scale (FP8)  */
+  const float* k_scale;     /* device float[1]: s_t (NVFP4) or scale (FP8);
+                               float[Hkv] with kv_scale_per_head            */
   const uint8_t* v_codes;
   const uint8_t* v_scales;
   const float* v_scale;
@@ -258,6 +282,10 @@ typedef struct {
                                splits; s must not exceed it                */
   float* p_scratch;         /* quantize_p only: device float32 buffer of
                                kvq_fp8p_scratch_floats(...) floats; else NULL */
+  int32_t kv_scale_per_head;  /* FP8, GQA layout: 1 = k_scale and v_scale are
+                               device float[Hkv], kv head h dequantized with
+                               its own scale (kvq_pack_fp8_heads); 0 = one
+                               per-tensor scale each */
 } kvq_decode_args;
 
 /*

@@ -49,7 +49,8 @@ class NVFP4Plane:
 
 @dataclass
 class FP8Plane:
-    """A per-tensor FP8 E4M3 tensor: codes [..., D], scale [1], layout."""
+    """An FP8 E4M3 tensor: codes [..., D], scale [1] (per tensor) or [Hkv]
+    (one per kv head, the attn_head strategy), layout."""
     codes: torch.Tensor
     scale: torch.Tensor
     layout: int = KVQ_PLANE_ROWS
@@ -98,13 +99,15 @@ def kvq_version() -> int:
 
 
 def kvq_amax(x: torch.Tensor, kv_lens: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-             accumulate: bool = False, stream=None) -> torch.Tensor:
-    """Per-tensor max |x| over rows [..., d]; rows with i2 >= kv_lens[i0]
-    skipped.  Returns a float32 [1] device tensor."""
+             accumulate: bool = False, per_head: bool = False, stream=None) -> torch.Tensor:
+    """Max |x| over rows [..., d]; rows with i2 >= kv_lens[i0] skipped.
+    Returns a float32 [1] device tensor, or with per_head one value per
+    index of the second-to-last-but-one dim (the kv heads of [B, Hkv, L, d])."""
+    rows = _rows(x)
     if out is None:
-        out = torch.zeros(1, dtype=torch.float32, device=x.device)
-    check(_lib.lib().kvq_amax(_ptr(x), _DT[x.dtype], _rows(x), x.shape[-1], _ptr(kv_lens), _ptr(out),
-                              int(accumulate), _stream(stream)))
+        out = torch.zeros(rows.n1 if per_head else 1, dtype=torch.float32, device=x.device)
+    fn = _lib.lib().kvq_amax_heads if per_head else _lib.lib().kvq_amax
+    check(fn(_ptr(x), _DT[x.dtype], rows, x.shape[-1], _ptr(kv_lens), _ptr(out), int(accumulate), _stream(stream)))
     return out
 
 
@@ -132,15 +135,20 @@ def kvq_pack_nvfp4(x: torch.Tensor, amax: torch.Tensor, out: Optional[NVFP4Plane
 
 def kvq_pack_fp8(x: torch.Tensor, amax: torch.Tensor, out: Optional[FP8Plane] = None,
                  dst_pos: Optional[torch.Tensor] = None, layout: int = KVQ_PLANE_ROWS, stream=None) -> FP8Plane:
-    """Pack rows of x ([..., D]) to per-tensor FP8 E4M3."""
+    """Pack rows of x ([..., D]) to FP8 E4M3: one scale per tensor, or one per
+    kv head when amax holds one value per head (kvq_amax(..., per_head=True))."""
     d = x.shape[-1]
+    xr = _rows(x)
+    per_head = amax.numel() > 1
+    if per_head and amax.numel() != xr.n1:
+        raise ValueError(f"per-head amax must have {xr.n1} entries (got {amax.numel()})")
     if out is None:
         out = FP8Plane(torch.empty(tuple(x.shape), dtype=torch.uint8, device=x.device),
-                       torch.empty(1, dtype=torch.float32, device=x.device), layout)
+                       torch.empty(amax.numel(), dtype=torch.float32, device=x.device), layout)
     dst = _rows(out.codes, d)
-    xr = _rows(x)
-    check(_lib.lib().kvq_pack_fp8(_ptr(x), _DT[x.dtype], xr, d, _ptr(amax), _ptr(out.codes), dst, out.layout,
-                                  _ptr(dst_pos), _ptr(out.scale), _stream(stream)))
+    fn = _lib.lib().kvq_pack_fp8_heads if per_head else _lib.lib().kvq_pack_fp8
+    check(fn(_ptr(x), _DT[x.dtype], xr, d, _ptr(amax), _ptr(out.codes), dst, out.layout, _ptr(dst_pos),
+             _ptr(out.scale), _stream(stream)))
     return out
 
 
@@ -165,8 +173,9 @@ def kvq_pack_batch(jobs, stream=None):
             scales, sout = _ptr(plane.scales), _ptr(plane.tensor_scale)
         else:
             dst, scales, sout = _rows(plane.codes, d), ctypes.c_void_p(0), _ptr(plane.scale)
+        per_head = (not fp4) and amax.numel() > 1   # FP8 with one scale per kv head
         arr[i] = _lib.KvqPackJob(_ptr(x), _DT[x.dtype], _rows(x), d, _ptr(amax), _ptr(plane.codes), scales, dst,
-                                 plane.layout, _ptr(dst_pos), sout)
+                                 plane.layout, _ptr(dst_pos), sout, int(per_head))
     fn = _lib.lib().kvq_pack_nvfp4_batch if fp4 else _lib.lib().kvq_pack_fp8_batch
     check(fn(arr, len(jobs), _stream(stream)))
 
@@ -254,6 +263,10 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
     else:
         a.k_codes, a.k_scale = _ptr(k.codes), _ptr(k.scale)
         a.v_codes, a.v_scale = _ptr(v.codes), _ptr(v.scale)
+        per_head = k.scale.numel() > 1 or v.scale.numel() > 1   # the attn_head strategy
+        if per_head and not (k.scale.numel() == v.scale.numel() == a.Hkv):
+            raise ValueError(f"per-head FP8 scales must have Hkv = {a.Hkv} entries for K and V")
+        a.kv_scale_per_head = int(per_head)
     a.kv_lens = _ptr(kv_lens)
     a.softmax_scale = float(softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(D))
     a.num_splits = int(num_splits)

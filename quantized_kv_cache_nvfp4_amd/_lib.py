@@ -26,7 +26,7 @@ class KvqPackJob(ctypes.Structure):
     _fields_ = [("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int32), ("x_rows", KvqRows), ("d", ctypes.c_int32),
                 ("amax", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("dst_rows", KvqRows), ("dst_layout", ctypes.c_int32), ("dst_pos", ctypes.c_void_p),
-                ("scale_out", ctypes.c_void_p)]
+                ("scale_out", ctypes.c_void_p), ("scale_per_head", ctypes.c_int32)]
 
 
 KVQ_MAX_PACK_JOBS = 8
@@ -53,6 +53,7 @@ class KvqDecodeArgs(ctypes.Structure):
         ("part_o", ctypes.c_void_p), ("part_lse", ctypes.c_void_p),
         ("part_capacity", ctypes.c_int32),
         ("p_scratch", ctypes.c_void_p),
+        ("kv_scale_per_head", ctypes.c_int32),
     ]
 
 
@@ -62,8 +63,10 @@ _PROTOS = {
     "kvq_version": (_I32, []),
     "kvq_decode_args_size": (ctypes.c_size_t, []),
     "kvq_amax": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, _I32, _VP]),
+    "kvq_amax_heads": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, _I32, _VP]),
     "kvq_pack_nvfp4": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, _VP, KvqRows, _I32, _VP, _VP, _VP]),
     "kvq_pack_fp8": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, KvqRows, _I32, _VP, _VP, _VP]),
+    "kvq_pack_fp8_heads": (ctypes.c_int, [_VP, _I32, KvqRows, _I32, _VP, _VP, KvqRows, _I32, _VP, _VP, _VP]),
     "kvq_pack_nvfp4_batch": (ctypes.c_int, [ctypes.POINTER(KvqPackJob), _I32, _VP]),
     "kvq_pack_fp8_batch": (ctypes.c_int, [ctypes.POINTER(KvqPackJob), _I32, _VP]),
     "kvq_unpack_nvfp4": (ctypes.c_int, [_VP, _VP, KvqRows, _I32, _I32, _VP, _VP, KvqRows, _VP]),

@@ -86,6 +86,8 @@ int check_pack_job(const kvq_pack_job& j, bool fp4) {
       return fail(KVQ_ERR_ARG, "d must be a positive multiple of 4, <= 4096 (got %d)", j.d);
     if (j.amax == nullptr || j.codes == nullptr) return fail(KVQ_ERR_ARG, "amax and codes must be non-null");
   }
+  if (j.scale_per_head != 0 && (fp4 || j.scale_per_head != 1))
+    return fail(KVQ_ERR_ARG, "scale_per_head must be 0 or 1, and 1 only for FP8");
   if (!fits_dst(j.x_rows, j.dst_rows))
     return fail(KVQ_ERR_ARG, "dst_rows must match x_rows in n0, n1 and be at least as long in n2");
   if (!aligned(j.codes, fp4 ? 8 : 4)) return fail(KVQ_ERR_ALIGN, "codes plane must be %d-byte aligned", fp4 ? 8 : 4);
@@ -103,7 +105,7 @@ int pack_batch(const kvq_pack_job* jobs, int32_t n_jobs, bool fp4, const char* w
     if (rc != KVQ_OK) return rc;
     if (n_rows(j.x_rows) == 0) continue;
     P.j[P.n++] = kvq::PackJob{j.x, j.x_dtype, kvq::to_rows(j.x_rows), j.d, j.amax, j.codes, j.scales,
-                              kvq::to_rows(j.dst_rows), j.dst_layout, j.dst_pos, j.scale_out};
+                              kvq::to_rows(j.dst_rows), j.dst_layout, j.dst_pos, j.scale_out, j.scale_per_head};
   }
   if (P.n == 0) return ok();
   const hipError_t e = fp4 ? kvq::launch_pack_nvfp4(P, as_stream(stream)) : kvq::launch_pack_fp8(P, as_stream(stream));
@@ -120,30 +122,49 @@ int32_t kvq_version(void) { return 100; }  // 0.1.0
 
 size_t kvq_decode_args_size(void) { return sizeof(kvq_decode_args); }
 
-int kvq_amax(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const int32_t* kv_lens, float* amax_out,
-             int32_t accumulate, void* stream) {
+namespace {
+int amax_call(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const int32_t* kv_lens, float* amax_out,
+              int32_t accumulate, bool per_head, void* stream) {
   int rc;
   if ((rc = check_float_input(x, x_dtype, "x")) != KVQ_OK) return rc;
   if ((rc = check_rows(x_rows, "x_rows")) != KVQ_OK) return rc;
   if (d <= 0) return fail(KVQ_ERR_ARG, "d must be > 0 (got %d)", d);
   if (amax_out == nullptr) return fail(KVQ_ERR_ARG, "amax_out is null");
   if (!aligned(amax_out, 4)) return fail(KVQ_ERR_ALIGN, "amax_out is not 4-byte aligned");
-  return hip_status(kvq::launch_amax(x, x_dtype, kvq::to_rows(x_rows), d, kv_lens, amax_out, accumulate != 0,
+  if (per_head && x_rows.n1 > (1 << 16)) return fail(KVQ_ERR_ARG, "at most 65536 heads (got %lld)", (long long)x_rows.n1);
+  return hip_status(kvq::launch_amax(x, x_dtype, kvq::to_rows(x_rows), d, kv_lens, amax_out, accumulate != 0, per_head,
                                      as_stream(stream)),
-                    "kvq_amax launch");
+                    per_head ? "kvq_amax_heads launch" : "kvq_amax launch");
+}
+}  // namespace
+
+int kvq_amax(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const int32_t* kv_lens, float* amax_out,
+             int32_t accumulate, void* stream) {
+  return amax_call(x, x_dtype, x_rows, d, kv_lens, amax_out, accumulate, false, stream);
+}
+
+int kvq_amax_heads(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const int32_t* kv_lens,
+                   float* amax_out, int32_t accumulate, void* stream) {
+  return amax_call(x, x_dtype, x_rows, d, kv_lens, amax_out, accumulate, true, stream);
 }
 
 int kvq_pack_nvfp4(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax, uint8_t* codes,
                    uint8_t* scales, kvq_rows dst_rows, int32_t dst_layout, const int32_t* dst_pos,
                    float* tensor_scale_out, void* stream) {
-  const kvq_pack_job j{x, x_dtype, x_rows, d, amax, codes, scales, dst_rows, dst_layout, dst_pos, tensor_scale_out};
+  const kvq_pack_job j{x, x_dtype, x_rows, d, amax, codes, scales, dst_rows, dst_layout, dst_pos, tensor_scale_out, 0};
   return pack_batch(&j, 1, true, "kvq_pack_nvfp4", stream);
 }
 
 int kvq_pack_fp8(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax, uint8_t* codes,
                  kvq_rows dst_rows, int32_t dst_layout, const int32_t* dst_pos, float* scale_out, void* stream) {
-  const kvq_pack_job j{x, x_dtype, x_rows, d, amax, codes, nullptr, dst_rows, dst_layout, dst_pos, scale_out};
+  const kvq_pack_job j{x, x_dtype, x_rows, d, amax, codes, nullptr, dst_rows, dst_layout, dst_pos, scale_out, 0};
   return pack_batch(&j, 1, false, "kvq_pack_fp8", stream);
+}
+
+int kvq_pack_fp8_heads(const void* x, int32_t x_dtype, kvq_rows x_rows, int32_t d, const float* amax, uint8_t* codes,
+                       kvq_rows dst_rows, int32_t dst_layout, const int32_t* dst_pos, float* scale_out, void* stream) {
+  const kvq_pack_job j{x, x_dtype, x_rows, d, amax, codes, nullptr, dst_rows, dst_layout, dst_pos, scale_out, 1};
+  return pack_batch(&j, 1, false, "kvq_pack_fp8_heads", stream);
 }
 
 int kvq_pack_nvfp4_batch(const kvq_pack_job* jobs, int32_t n_jobs, void* stream) {
@@ -261,6 +282,9 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
   if (a->q == nullptr || a->k_codes == nullptr || a->k_scale == nullptr || a->kv_lens == nullptr)
     return fail(KVQ_ERR_ARG, "q, k_codes, k_scale and kv_lens must be non-null");
   if (a->kv_format == KVQ_NVFP4 && a->k_scales == nullptr) return fail(KVQ_ERR_ARG, "NVFP4 needs k_scales");
+  if (a->kv_scale_per_head != 0 &&
+      (a->kv_scale_per_head != 1 || a->kv_format != KVQ_FP8E4M3 || a->layout != KVQ_LAYOUT_GQA))
+    return fail(KVQ_ERR_UNSUPPORTED, "kv_scale_per_head must be 0 or 1, and 1 only for FP8 with the GQA layout");
   if (a->q_dtype != KVQ_BF16 && a->q_dtype != KVQ_F32) return fail(KVQ_ERR_UNSUPPORTED, "q_dtype must be BF16 or F32");
   if (!(a->softmax_scale > 0.0f) || a->softmax_scale != a->softmax_scale || a->softmax_scale > 3.0e38f)
     return fail(KVQ_ERR_ARG, "softmax_scale must be a positive finite number");

@@ -307,8 +307,10 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   KT KA, KB;
   if constexpr (PM != 2 && NG > 1) load_ktile(KA, wave);
 
-  const float kscale = *a.k_scale;
-  const float vscale = *a.v_scale;
+  // per-tensor scales, or one per kv head (FP8 with the attn_head strategy)
+  const int sh = a.kv_scale_per_head ? kvh : 0;
+  const float kscale = a.k_scale[sh];
+  const float vscale = a.v_scale[sh];
   int L = a.kv_lens[b];
   L = L < a.max_kv_len ? L : a.max_kv_len;
   L = L > 0 ? L : 0;

@@ -30,6 +30,7 @@ struct PackJob {
   int layout;
   const int32_t* dst_pos;
   float* sout;
+  int per_head;   // FP8: amax / sout hold one value per i1
 };
 constexpr int kMaxPackJobs = KVQ_MAX_PACK_JOBS;
 struct PackJobs {
@@ -39,7 +40,7 @@ struct PackJobs {
 
 // ---- quantization kernels (quant_kernels.hip) ----
 hipError_t launch_amax(const void* x, int x_dtype, Rows rows, int d, const int32_t* kv_lens, float* amax_out,
-                       bool accumulate, hipStream_t st);
+                       bool accumulate, bool per_head, hipStream_t st);
 // every job of one call in one launch (blockIdx.y = job)
 hipError_t launch_pack_nvfp4(const PackJobs& jobs, hipStream_t st);
 hipError_t launch_pack_fp8(const PackJobs& jobs, hipStream_t st);

@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include "kvq_internal.h"
+#include "wave_reduce.h"
 
 namespace kvq {
 namespace {
@@ -249,20 +250,43 @@ __device__ inline uint32_t encode_fp8(float v, float inv, double dscale) {
 }
 
 // ---------------------------------------------------------------- amax
-__global__ void k_zero_scalar(float* p) { *p = 0.0f; }
+__global__ void k_zero_n(float* p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = 0.0f;
+}
 
 // max |x| over the rows (tokens at or past kv_lens[i0] excluded); runs of 8
 // elements per item, a wave and then a work-group reduction, one atomic per
 // work-group (non-negative floats order as their bit patterns, so an
 // unsigned max on the bits is a float max).  The grid is kept to about four
 // work-groups per compute unit: atomics on one address serialize.
+// Work-group max of m, merged into *dst with one atomic (non-negative
+// floats order as their bit patterns).  Called by the whole work-group.
+__device__ inline void wg_max_atomic(float m, float* dst) {
+  __shared__ float wmax[kThreads / 64];
+  m = lanes::wave_all<lanes::Max>(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, wmax[w]);
+    atomicMax(reinterpret_cast<unsigned int*>(dst), __float_as_uint(b));
+  }
+  __syncthreads();   // wmax may be reused
+}
+
+// per_head: out[i1] receives the max over the rows of head i1 (one atomic
+// per work-group and head), else out[0] the max over everything
 __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, int dt, Rows r, int d,
-                                                   const int32_t* __restrict__ kv_lens, float* __restrict__ out) {
+                                                   const int32_t* __restrict__ kv_lens, float* __restrict__ out,
+                                                   int per_head) {
   const uint32_t nrun = static_cast<uint32_t>((d + 7) / 8);
   float m = 0.0f;
   const int64_t nh = r.n0 * r.n1;
   for (int64_t h = blockIdx.y; h < nh; h += gridDim.y) {
     const int64_t i0 = h / r.n1, i1 = h - i0 * r.n1;
+    if (per_head) m = 0.0f;
     int64_t n2 = r.n2;
     if (kv_lens != nullptr) {
       const int64_t len = kv_lens[i0];
@@ -316,27 +340,19 @@ __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, i
         }
         for (; it < items; it += stride) fold(p[it]);
       }
-      continue;
-    }
-    for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
-      const int64_t t = it / nrun;
-      const int run = static_cast<int>(it - t * nrun);
-      float v[8];
-      load_run<8>(x, dt, base + t * r.s2 + 8 * run, d - 8 * run < 8 ? d - 8 * run : 8, v);
+    } else {
+      for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
+        const int64_t t = it / nrun;
+        const int run = static_cast<int>(it - t * nrun);
+        float v[8];
+        load_run<8>(x, dt, base + t * r.s2 + 8 * run, d - 8 * run < 8 ? d - 8 * run : 8, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+      }
     }
+    if (per_head) wg_max_atomic(m, out + i1);   // (the head loop is uniform over the work-group)
   }
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  __shared__ float wmax[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float b = wmax[0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, wmax[w]);
-    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(b));
-  }
+  if (!per_head) wg_max_atomic(m, out);
 }
 
 // ---------------------------------------------------------------- NVFP4 pack
@@ -457,13 +473,26 @@ __global__ void __launch_bounds__(kThreads) k_pack_nvfp4(PackJobs P) {
 // ---------------------------------------------------------------- FP8 pack
 // ROWS layout: one item per (row, 16-element run): 16 code bytes (one
 // 16-byte store; d % 16 != 0 leaves a shorter last run, stored per word)
-__device__ inline void pack_fp8_rows(const PackJob& J, double dscale, float inv) {
+// The scale of head i1: one per tensor, or amax[i1] / 448 with one scale
+// per kv head (written to sout[i1] by one work-group).
+__device__ inline void fp8_head_scale(const PackJob& J, int64_t i0, int64_t i1, double& dscale, float& inv) {
+  if (!J.per_head) return;
+  const float scale = fp8_tensor_scale(J.amax[i1]);
+  if (i0 == 0 && blockIdx.x == 0 && threadIdx.x == 0 && J.sout != nullptr) J.sout[i1] = scale;
+  dscale = static_cast<double>(scale);
+  inv = 1.0f / scale;
+}
+
+__device__ inline void pack_fp8_rows(const PackJob& J, double dscale0, float inv0) {
   const int d = J.d;
   const uint32_t nr = static_cast<uint32_t>((d + 15) / 16);
   const Rows xr = J.xr, dr = J.dr;
   const int64_t nh = xr.n0 * xr.n1;
   for (int64_t h = blockIdx.y; h < nh; h += gridDim.y) {
     const int64_t i0 = h / xr.n1, i1 = h - i0 * xr.n1;
+    double dscale = dscale0;
+    float inv = inv0;
+    fp8_head_scale(J, i0, i1, dscale, inv);
     const int64_t pos = J.dst_pos != nullptr ? J.dst_pos[i0] : 0;
     const int64_t xbase = i0 * xr.s0 + i1 * xr.s1, dbase = i0 * dr.s0 + i1 * dr.s1;
     const int64_t items = xr.n2 * nr;
@@ -495,7 +524,7 @@ __device__ inline void pack_fp8_rows(const PackJob& J, double dscale, float inv)
 }
 
 // TOKEN4 layout: one item per (4-token group slot, 4 elements): 16 code bytes
-__device__ inline void pack_fp8_t4(const PackJob& J, double dscale, float inv) {
+__device__ inline void pack_fp8_t4(const PackJob& J, double dscale0, float inv0) {
   const int d = J.d;
   const uint32_t nw = static_cast<uint32_t>(d / 4);
   const Rows xr = J.xr, dr = J.dr;
@@ -503,6 +532,9 @@ __device__ inline void pack_fp8_t4(const PackJob& J, double dscale, float inv) {
   const int64_t nh = xr.n0 * xr.n1;
   for (int64_t h = blockIdx.y; h < nh; h += gridDim.y) {
     const int64_t i0 = h / xr.n1, i1 = h - i0 * xr.n1;
+    double dscale = dscale0;
+    float inv = inv0;
+    fp8_head_scale(J, i0, i1, dscale, inv);
     const int64_t xbase = i0 * xr.s0 + i1 * xr.s1;
     const int64_t items = slots * nw;
     for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
@@ -530,8 +562,8 @@ __device__ inline void pack_fp8_t4(const PackJob& J, double dscale, float inv) {
 
 __global__ void __launch_bounds__(kThreads) k_pack_fp8(PackJobs P) {
   const PackJob& J = P.j[blockIdx.z];
-  const float scale = fp8_tensor_scale(*J.amax);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && J.sout != nullptr) *J.sout = scale;
+  const float scale = fp8_tensor_scale(*J.amax);   // (per head: replaced per head)
+  if (!J.per_head && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && J.sout != nullptr) *J.sout = scale;
   const float inv = 1.0f / scale;   // candidate quotients only; decisions are exact
   if (J.layout == KVQ_PLANE_TOKEN4) pack_fp8_t4(J, static_cast<double>(scale), inv);
   else pack_fp8_rows(J, static_cast<double>(scale), inv);
@@ -615,12 +647,15 @@ static dim3 head_grid(int64_t heads, int64_t items_per_head, int z, int64_t budg
 }
 
 hipError_t launch_amax(const void* x, int x_dtype, Rows rows, int d, const int32_t* kv_lens, float* amax_out,
-                       bool accumulate, hipStream_t st) {
-  if (!accumulate) hipLaunchKernelGGL(k_zero_scalar, dim3(1), dim3(1), 0, st, amax_out);
+                       bool accumulate, bool per_head, hipStream_t st) {
+  const int64_t nout = per_head ? rows.n1 : 1;
+  if (!accumulate && nout > 0)
+    hipLaunchKernelGGL(k_zero_n, dim3(static_cast<unsigned>((nout + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
+                       amax_out, nout);
   const int64_t heads = rows.n0 * rows.n1;
   if (heads > 0 && rows.n2 > 0)
     hipLaunchKernelGGL(k_amax, head_grid(heads, rows.n2 * ((d + 7) / 8), 1, 1024), dim3(kThreads), 0, st, x, x_dtype,
-                       rows, d, kv_lens, amax_out);
+                       rows, d, kv_lens, amax_out, per_head ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -170,6 +170,10 @@ def test_decode_validation(L, K):
     assert _decode_rc(L, a) == 3
     a = _good_args(K); a.v_layout = 5
     assert _decode_rc(L, a) == 1
+    a = _good_args(K); a.kv_scale_per_head = 1
+    assert _decode_rc(L, a) == 2                     # per-head scales: FP8 only
+    a = _good_args(K); a.kv_format = K.KVQ_FP8E4M3; a.k_scales = a.v_scales = None; a.kv_scale_per_head = 2
+    assert _decode_rc(L, a) == 2
     assert L.attn_decode_splitkv(None, None, None) == 1
 
 
@@ -199,6 +203,13 @@ def test_pack_batch_validation(L, K):
     odd = _lib.KvqPackJob(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE_ODD, FAKE, r16, R, None, None)
     arr3 = (_lib.KvqPackJob * 2)(good, odd)
     assert L.kvq_pack_nvfp4_batch(arr3, 2, None) == 3
+    # one scale per kv head is an FP8 option
+    ph = _lib.KvqPackJob(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE, FAKE, r16, R, None, None, 1)
+    assert L.kvq_pack_nvfp4_batch((_lib.KvqPackJob * 1)(ph), 1, None) == 1
+    ph2 = _lib.KvqPackJob(FAKE, K.KVQ_BF16, r16, 16, FAKE, FAKE, FAKE, r16, R, None, None, 3)
+    assert L.kvq_pack_fp8_batch((_lib.KvqPackJob * 1)(ph2), 1, None) == 1
+    assert L.kvq_amax_heads(None, K.KVQ_F32, r16, 16, None, FAKE, 0, None) == 1
+    assert L.kvq_pack_fp8_heads(FAKE, K.KVQ_F32, r16, 6, FAKE, FAKE, r16, R, None, None, None) == 1
     # empty jobs are skipped without a launch
     r0 = _rows(1, 1, 0, 0, 0, 16)
     empty = _lib.KvqPackJob(FAKE, K.KVQ_BF16, r0, 16, FAKE, FAKE, FAKE, r16, R, None, None)
