@@ -351,11 +351,19 @@ def run_fp8(args):
     ka, va = K.kvq_amax(k, lens), K.kvq_amax(v, lens)
     kp0 = K.kvq_pack_fp8(k, ka)
     vp0 = K.kvq_pack_fp8(v, va, layout=K.KVQ_PLANE_TOKEN4)
+    # the same cache with one scale per kv head (the attn_head strategy)
+    kah, vah = K.kvq_amax(k, lens, per_head=True), K.kvq_amax(v, lens, per_head=True)
+    kph = K.kvq_pack_fp8(k, kah)
+    vph = K.kvq_pack_fp8(v, vah, layout=K.KVQ_PLANE_TOKEN4)
     elems = k.numel()
     prep_us = {"amax_k": eager_timer(torch, lambda: K.kvq_amax(k, lens, out=ka)),
                "pack_k_fp8_rows": eager_timer(torch, lambda: K.kvq_pack_fp8(k, ka, out=kp0)),
-               "pack_v_fp8_token4": eager_timer(torch, lambda: K.kvq_pack_fp8(v, va, out=vp0))}
-    prep_bytes = {"amax_k": elems * 2, "pack_k_fp8_rows": elems * 3, "pack_v_fp8_token4": elems * 3}
+               "pack_v_fp8_token4": eager_timer(torch, lambda: K.kvq_pack_fp8(v, va, out=vp0)),
+               "amax_k_per_head": eager_timer(torch, lambda: K.kvq_amax(k, lens, out=kah, per_head=True)),
+               "pack_k_fp8_rows_per_head": eager_timer(torch, lambda: K.kvq_pack_fp8(k, kah, out=kph))}
+    valid = int(inp.kv_lens.astype("int64").sum()) * inp.Hkv * D   # amax reads the valid rows only
+    prep_bytes = {"amax_k": valid * 2, "pack_k_fp8_rows": elems * 3, "pack_v_fp8_token4": elems * 3,
+                  "amax_k_per_head": valid * 2, "pack_k_fp8_rows_per_head": elems * 3}
     del k, v
     q = inp.q.to(dev)
     per_copy = kp0.codes.numel() + vp0.codes.numel()
@@ -380,6 +388,11 @@ def run_fp8(args):
 
     dargs = [mk(kc, vc, False) for kc, vc in copies]
     pargs = [mk(kc, vc, True) for kc, vc in copies]
+    # per-head scales: the same code bytes read through one copy per step
+    hcopies = [(kph, vph)] + [(K.FP8Plane(kph.codes.clone(), kph.scale.clone(), kph.layout),
+                               K.FP8Plane(vph.codes.clone(), vph.scale.clone(), vph.layout))
+                              for _ in range(n_copies - 1)]
+    hargs = [mk(kc, vc, False) for kc, vc in hcopies]
 
     def step(i, a, o):
         used = K.attn_decode_splitkv(a[i])
@@ -393,6 +406,7 @@ def run_fp8(args):
     ms = {"decode": timed(capture(lambda i: step(i, dargs, out))),
           "decode_fp8_out": timed(capture(lambda i: step(i, dargs, out8))),
           "decode_fp8p": timed(capture(lambda i: step(i, pargs, out))),
+          "decode_per_head_scales": timed(capture(lambda i: step(i, hargs, out))),
           "split_kernel": timed(capture(lambda i: K.attn_decode_splitkv(dargs[i]))),
           "fp8p_passes": timed(capture(lambda i: K.attn_decode_splitkv(pargs[i])))}
     assert torch.isfinite(out.float()).all()

@@ -231,9 +231,14 @@ __device__ inline uint32_t e4m3_fixup(uint32_t c, float ax, double dscale) {
 // FP8 code of v / scale: the round-to-nearest-even E4M3 code of |v| / scale
 // (exact decision, saturating at 448), sign of v.  The candidate is the
 // hardware conversion of the float32 quotient |v| * (1 / scale), whose
-// relative error is below 2^-22; it is the exact code unless that quotient
+// relative error is below 2^-22: it is the exact code unless that quotient
 // lies within 2^-20 (relative) of one of the two midpoints around the
-// candidate's value, and only then is it checked exactly (e4m3_fixup).
+// candidate's value.  Only then is it checked exactly: m * scale - |v| is
+// formed by one fused multiply-add, rounded once, so its sign (and whether
+// it is zero) is that of the exact difference (a midpoint has at most 5
+// significant bits; a nonzero exact difference is at least the smallest
+// float32 subnormal); ties go to the even code.  Scales below 2^-100, where
+// m * scale could underflow, take the float64 check of e4m3_fixup.
 __device__ inline uint32_t encode_fp8(float v, float inv, double dscale) {
   const float ax = fabsf(v);
   const float qa = fminf(ax * inv, 448.0f);   // NaN and inf -> 448
@@ -245,7 +250,18 @@ __device__ inline uint32_t encode_fp8(float v, float inv, double dscale) {
   const float vn = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(trio), 2);
   const float mh = 0.5f * (vc + vn), ml = 0.5f * (vc + vp);   // exact in float32
   const bool near = (c < 0x7Eu && fabsf(qa - mh) <= mh * 0x1p-20f) || (c > 0u && fabsf(qa - ml) <= ml * 0x1p-20f);
-  if (near) c = e4m3_fixup(c, ax, dscale);
+  if (near) {
+    const float scale = static_cast<float>(dscale);
+    if (scale >= 0x1p-100f) {
+      const float dh = __builtin_fmaf(mh, scale, -ax);   // sign of mh * scale - |v|
+      const float dl = __builtin_fmaf(ml, scale, -ax);
+      const bool up = c < 0x7Eu && (dh < 0.0f || (dh == 0.0f && ((c + 1u) & 1u) == 0u));
+      const bool dn = c > 0u && (dl > 0.0f || (dl == 0.0f && ((c - 1u) & 1u) == 0u));
+      c = c + (up ? 1u : 0u) - (dn ? 1u : 0u);
+    } else {
+      c = e4m3_fixup(c, ax, dscale);
+    }
+  }
   return c | ((__float_as_uint(v) >> 24) & 0x80u);
 }
 
