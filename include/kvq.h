@@ -286,7 +286,29 @@ typedef struct {
                                device float[Hkv], kv head h dequantized with
                                its own scale (kvq_pack_fp8_heads); 0 = one
                                per-tensor scale each */
+  /* Paged cache (GQA layout, exact probabilities; vLLM's block tables, the
+     serving setting of Model-Optimizer PR #1832 "Purpose" and "Testing").
+     NULL block_table: the planes are addressed by kv_sb / kv_sh / kv_st as
+     above.  Otherwise token t of request b, kv head h is plane row
+       block_table[b * bt_stride + t / block_size] * kv_sblk
+         + h * kv_sh + (t % block_size) * kv_st
+     (kv_sb unused; for planes [num_blocks][Hkv][block_size][row]:
+     kv_sblk = Hkv * block_size, kv_sh = block_size, kv_st = 1).  Entries
+     are read for t < max_kv_len; only those of tokens t < kv_lens[b] are
+     used as block indices (they must be valid there).
+     block_size: a positive multiple of the decode tile (attn_decode_tile_tokens). */
+  const int32_t* block_table;
+  int32_t block_size;
+  int64_t bt_stride;
+  int64_t kv_sblk;
 } kvq_decode_args;
+
+/*
+ * attn_decode_tile_tokens - tokens per tile of the GQA decode kernel for
+ * query groups of G = Hq / Hkv heads (32 to 256): paged caches need a block
+ * size that is a multiple of it.  0 if G is unsupported.
+ */
+int32_t attn_decode_tile_tokens(int32_t Hq, int32_t Hkv);
 
 /*
  * attn_decode_splitkv - split-KV flash decode over the packed cache

@@ -216,10 +216,13 @@ def kvq_fp8p_scratch_floats(B: int, Hq: int, s: int, max_kv_len: int) -> int:
 
 def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_splits=0, part_o, part_lse,
                      q_rope=None, k_rope=None, quantize_p=False, prob_scale=1.0 / 448.0,
-                     p_scratch=None) -> KvqDecodeArgs:
+                     p_scratch=None, block_table=None) -> KvqDecodeArgs:
     """Fill the C decode-argument struct from tensors (no device work).
 
-    GQA: q [B, Hq, D]; k, v NVFP4Plane / FP8Plane with codes [B, Hkv, Lmax, .].
+    GQA: q [B, Hq, D]; k, v NVFP4Plane / FP8Plane with codes [B, Hkv, Lmax, .],
+    or, with block_table (int32 [B, max_blocks]), paged planes with codes
+    [num_blocks, Hkv, block_size, .] (token t of request b in block
+    block_table[b, t // block_size]).
     MLA: q = q_c [B, H, Dc]; k = NVFP4Plane of the latent [B, Lmax, .];
     v = None; q_rope [B, H, Dr] and k_rope [B, Lmax, Dr] bf16.
     """
@@ -252,6 +255,11 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
         a.kv_sb, a.kv_sh, a.kv_st = kr.s0, kr.s1, kr.s2
         a.Drope = 0
         a.v_layout = v.layout
+        if block_table is not None:   # paged planes [num_blocks, Hkv, block_size, .]
+            if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+                raise ValueError("block_table must be an int32 [B, max_blocks] tensor with contiguous rows")
+            a.block_table, a.block_size = _ptr(block_table), int(k.codes.shape[2])
+            a.bt_stride, a.kv_sblk, a.kv_sb = block_table.stride(0), kr.s0, 0
     a.max_kv_len = int(max_kv_len)
     a.q, a.q_dtype, a.q_sb, a.q_sh = _ptr(q), _DT[q.dtype], q.stride(0), q.stride(1)
     if fmt == KVQ_NVFP4:
@@ -275,6 +283,11 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
     a.part_capacity = part_o.numel() // (B * Hq * D) if part_o is not None else 0
     a.p_scratch = _ptr(p_scratch)
     return a
+
+
+def attn_decode_tile_tokens(Hq: int, Hkv: int) -> int:
+    """Tokens per tile of the GQA decode kernel (paged block sizes must be a multiple)."""
+    return _lib.lib().attn_decode_tile_tokens(Hq, Hkv)
 
 
 def attn_decode_splitkv(args: KvqDecodeArgs, stream=None) -> int:

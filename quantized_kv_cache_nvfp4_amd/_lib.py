@@ -54,6 +54,8 @@ class KvqDecodeArgs(ctypes.Structure):
         ("part_capacity", ctypes.c_int32),
         ("p_scratch", ctypes.c_void_p),
         ("kv_scale_per_head", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+        ("bt_stride", ctypes.c_int64), ("kv_sblk", ctypes.c_int64),
     ]
 
 
@@ -77,6 +79,7 @@ _PROTOS = {
     "kvq_auto_num_splits": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_I32)]),
     "kvq_device_cu_count": (ctypes.c_int, [ctypes.POINTER(_I32)]),
     "kvq_fp8p_scratch_floats": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
+    "attn_decode_tile_tokens": (_I32, [_I32, _I32]),
 }
 
 _lib = None

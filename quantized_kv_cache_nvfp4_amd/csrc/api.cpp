@@ -246,6 +246,11 @@ int kvq_auto_num_splits(int32_t num_cus, int32_t B, int32_t programs_per_req, in
   return ok();
 }
 
+int32_t attn_decode_tile_tokens(int32_t Hq, int32_t Hkv) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return 0;
+  return kvq::gqa_tile_tokens(Hq / Hkv);
+}
+
 int kvq_device_cu_count(int32_t* num_cus_out) {
   if (num_cus_out == nullptr) return fail(KVQ_ERR_ARG, "num_cus_out is null");
   int dev = 0, n = 0;
@@ -338,7 +343,25 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
     const int G = a->Hq / a->Hkv;
     if (!kvq::gqa_supported(a->kv_format, G, a->D, a->q_dtype))
       return fail(KVQ_ERR_UNSUPPORTED, "GQA decode: G=%d, D=%d not supported (G in 1,2,4,8,16; D in 64,128)", G, a->D);
+    if (a->block_table != nullptr) {   // paged cache
+      const int tile = kvq::gqa_tile_tokens(G);
+      if (a->quantize_p) return fail(KVQ_ERR_UNSUPPORTED, "paged caches are decoded with exact probabilities only");
+      if (a->block_size <= 0 || a->block_size % tile != 0)
+        return fail(KVQ_ERR_ARG, "block_size must be a positive multiple of the decode tile (%d tokens for G=%d)", tile, G);
+      const int64_t need = (static_cast<int64_t>(a->max_kv_len) + a->block_size - 1) / a->block_size;
+      if (a->bt_stride < need) return fail(KVQ_ERR_ARG, "bt_stride must cover ceil(max_kv_len / block_size) blocks");
+      if (a->kv_sblk < 0) return fail(KVQ_ERR_ARG, "kv_sblk must be >= 0");
+      if (!aligned(a->block_table, 4)) return fail(KVQ_ERR_ALIGN, "block_table must be 4-byte aligned");
+      if (a->v_layout == KVQ_PLANE_TOKEN4 && (a->kv_sblk % 4 != 0 || a->block_size % 4 != 0))
+        return fail(KVQ_ERR_ALIGN, "TOKEN4 V planes need kv_sblk and block_size multiples of 4");
+      int64_t chunk = (static_cast<int64_t>(a->max_kv_len) + s - 1) / s;
+      chunk = (chunk + tile - 1) / tile * tile;
+      if (chunk / a->block_size + 2 > kvq::kPagedMaxChunkBlocks)
+        return fail(KVQ_ERR_ARG, "a split spans more than %d blocks: use more splits or larger blocks",
+                    kvq::kPagedMaxChunkBlocks - 2);
+    }
   } else {
+    if (a->block_table != nullptr) return fail(KVQ_ERR_UNSUPPORTED, "paged caches are decoded for the GQA layout only");
     if (a->kv_format != KVQ_NVFP4) return fail(KVQ_ERR_UNSUPPORTED, "MLA layout supports NVFP4 only");
     if (a->Hkv != 1) return fail(KVQ_ERR_ARG, "MLA layout needs Hkv == 1");
     if (a->k_scales == nullptr || a->q_rope == nullptr || a->k_rope == nullptr)

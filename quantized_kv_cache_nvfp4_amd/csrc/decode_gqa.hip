@@ -188,10 +188,17 @@ constexpr int decode_min_blocks() {
   return 8 / kWaves;
 }
 
+// Block-table entries a work-group of a paged cache keeps in LDS (the
+// blocks its chunk touches).
+constexpr int kMaxChunkBlocks = kPagedMaxChunkBlocks;
+
 // PM: 0 attention, 1 FP8-P pass 1 (scores), 2 FP8-P pass 2 (quantized P . V).
-template <int KVF, int G, int D, bool QF32, int PSPLIT, bool FUSED, int VL, int PM>
+// PAGED: the planes are paged (block table; block size a multiple of the
+// tile, so every tile lies in one block).
+template <int KVF, int G, int D, bool QF32, int PSPLIT, bool FUSED, int VL, int PM, bool PAGED>
 __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>())) k_decode_gqa(kvq_decode_args a, int num_splits, FusedOut fo) {
   static_assert(PM == 0 || (!FUSED && PSPLIT == 1), "the FP8-P passes write partials only");
+  static_assert(!PAGED || PM == 0, "paged caches use exact probabilities");
   using Gm = Geo<KVF, D>;
   constexpr int NSUB = 16 / G;                  // row groups in the 16 MFMA columns
   constexpr int NT = NSUB < 2 ? 2 : NSUB;       // sub-tiles (16 tokens) per tile
@@ -207,6 +214,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   __shared__ float lds_l[kWaves][16];   //                    denominator
   __shared__ float lds_lse[16];         // FP8-P pass 2: output factor per head
   __shared__ int lds_last;
+  __shared__ int lds_bt[PAGED ? kMaxChunkBlocks : 1];   // paged: block-table entries of the chunk
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -241,8 +249,9 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
 #pragma unroll
     for (int j = 0; j < kQRaw; ++j) qraw[j] = qp[j];
   }
-  // per-(request, kv head) plane bases
-  const int64_t head_row = static_cast<int64_t>(b) * a.kv_sb + static_cast<int64_t>(kvh) * a.kv_sh;
+  // per-(request, kv head) plane bases (paged: the kv head's offset inside
+  // a block; the block comes from the table per tile)
+  const int64_t head_row = (PAGED ? 0 : static_cast<int64_t>(b) * a.kv_sb) + static_cast<int64_t>(kvh) * a.kv_sh;
   const uint8_t* kc = a.k_codes + head_row * Gm::kRowBytes;
   const uint8_t* vc = a.v_codes + head_row * Gm::kRowBytes;
   const uint8_t* ksc = (KVF == KVQ_NVFP4) ? a.k_scales + head_row * Gm::kScaleBytes : kc;
@@ -251,6 +260,29 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   const int st = (VL == KVQ_PLANE_TOKEN4) ? 1 : static_cast<int>(a.kv_st);
   constexpr int RB = Gm::kRowBytes;
   constexpr int SB = Gm::kScaleBytes;
+
+  // Paged cache: the block-table entries of the chunk's blocks go to LDS
+  // once; tile tb then lies in block tb / bs (the block size is a multiple
+  // of the tile) at row (tb mod bs) of that block.
+  const int bs = PAGED ? a.block_size : 1;
+  const int blk0 = PAGED ? cs / bs : 0;
+  if constexpr (PAGED) {
+    const int nblk = ce_ld > cs ? (ce_ld - 1) / bs - blk0 + 1 : 0;   // blocks holding rows [cs, ce_ld)
+    const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride + blk0;
+    for (int i = threadIdx.x; i < nblk; i += kThreads) lds_bt[i] = bt[i];
+    __syncthreads();
+  }
+  // plane row (relative to the kv head's base) of token tb's tile, and the
+  // rows available from there (a paged tile ends at its block's end)
+  auto tile_row = [&](int tb) -> int64_t {
+    if constexpr (PAGED) {
+      const int i = tb / bs - blk0;
+      return (tb < ce_ld ? static_cast<int64_t>(lds_bt[i]) * a.kv_sblk : 0) + static_cast<int64_t>(tb % bs) * st;
+    } else {
+      return static_cast<int64_t>(tb) * st;
+    }
+  };
+  auto tile_rows = [&](int nv) { return PAGED ? (nv < TT ? nv : TT) : nv; };
 
   // Every load goes through a buffer resource whose base is the tile's
   // first token and whose size ends at the chunk end ce (for the first K
@@ -277,8 +309,8 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   auto load_ktile = [&](KT& R, int tile) {
     const int tb = cs + tile * TT;
     const int lk_ = opaque(lk), lks_ = opaque(lks);
-    const int nv = ce_ld - tb;
-    const int64_t base = static_cast<int64_t>(tb) * st;
+    const int nv = tile_rows(ce_ld - tb);
+    const int64_t base = tile_row(tb);
     const Rsrc rk = make_rsrc(kc + base * RB, nv * st * RB);
     const Rsrc rks = make_rsrc(ksc + base * SB, nv * st * SB);
 #pragma unroll
@@ -305,7 +337,9 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   // the first K tile of this wave, loaded before the request length arrives
   // (scores of tokens at or past the request's end are masked to -inf)
   KT KA, KB;
-  if constexpr (PM != 2 && NG > 1) load_ktile(KA, wave);
+  // (paged: after the request length, so that only the table entries of
+  // tokens below it are used)
+  if constexpr (PM != 2 && NG > 1 && !PAGED) load_ktile(KA, wave);
 
   // per-tensor scales, or one per kv head (FP8 with the attn_head strategy)
   const int sh = a.kv_scale_per_head ? kvh : 0;
@@ -316,6 +350,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   L = L > 0 ? L : 0;
   const int ce = (cs + chunk < L) ? cs + chunk : L;
   ce_ld = ce;   // every later load stops at the request's end
+  if constexpr (PAGED && NG > 1) load_ktile(KA, wave);
 
   const float qk_scale = a.softmax_scale * kscale * kLog2e;
 
@@ -365,7 +400,8 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
     auto load_vtile = [&](VT& R, int tile) {
       const int tb = cs + tile * TT;
       const int lvt_ = opaque(lvt), lvts_ = opaque(lvts), lv_ = opaque(lv), lvs_ = opaque(lvs);
-      const int nv = ce - tb;
+      const int nv = tile_rows(ce - tb);
+      const int64_t vbase = tile_row(tb);   // TOKEN4: st = 1
       if constexpr (VL == KVQ_PLANE_TOKEN4) {
         // Group 4u+g of the tile (lane group g): for this lane's elements
         // [8c, 8c+8) the 4 tokens' codes are one contiguous run (16 bytes
@@ -373,8 +409,8 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
         // group that straddles ce is read whole; pv_tile clears its tokens
         // past ce.
         const int ng = nv > 0 ? (nv + 3) / 4 : 0;
-        const Rsrc rv = make_rsrc(vc + static_cast<int64_t>(tb) * RB, ng * GB);
-        const Rsrc rvs = make_rsrc(vsc + static_cast<int64_t>(tb) * SB, ng * GS);
+        const Rsrc rv = make_rsrc(vc + vbase * RB, ng * GB);
+        const Rsrc rvs = make_rsrc(vsc + vbase * SB, ng * GS);
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
           const int o = lvt_ + u * 4 * GB;
@@ -389,9 +425,8 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
           if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] = ld32(rvs, lvts_ + u * 4 * GS);
         }
       } else {
-        const int64_t base = static_cast<int64_t>(tb) * st;
-        const Rsrc rv = make_rsrc(vc + base * RB, nv * st * RB);
-        const Rsrc rvs = make_rsrc(vsc + base * SB, nv * st * SB);
+        const Rsrc rv = make_rsrc(vc + vbase * RB, nv * st * RB);
+        const Rsrc rvs = make_rsrc(vsc + vbase * SB, nv * st * SB);
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
 #pragma unroll
@@ -978,18 +1013,27 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   }
 }
 
-template <int KVF, int G, int D, bool QF32, int PSPLIT, int VL, int PM>
-hipError_t launch_v(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
+template <int KVF, int G, int D, bool QF32, int PSPLIT, int VL, int PM, bool PAGED>
+hipError_t launch_p(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
   dim3 grid(p.s, a.Hkv, a.B);
   if constexpr (PM == 0) {
     if (fo != nullptr) {
-      hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, true, VL, 0>), grid, dim3(kThreads), 0, st, a, p.s, *fo);
+      hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, true, VL, 0, PAGED>), grid, dim3(kThreads), 0, st, a,
+                         p.s, *fo);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, false, VL, PM>), grid, dim3(kThreads), 0, st, a, p.s,
-                     FusedOut{});
+  hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, false, VL, PM, PAGED>), grid, dim3(kThreads), 0, st, a,
+                     p.s, FusedOut{});
   return hipGetLastError();
+}
+
+template <int KVF, int G, int D, bool QF32, int PSPLIT, int VL, int PM>
+hipError_t launch_v(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
+  if constexpr (PM == 0) {
+    if (a.block_table != nullptr) return launch_p<KVF, G, D, QF32, PSPLIT, VL, 0, true>(a, p, fo, st);
+  }
+  return launch_p<KVF, G, D, QF32, PSPLIT, VL, PM, false>(a, p, fo, st);
 }
 
 template <int KVF, int G, int D, bool QF32, int PSPLIT, int PM>
@@ -1031,6 +1075,7 @@ hipError_t dispatch(const kvq_decode_args& a, const DecodePlan& p, const FusedOu
 }  // namespace
 
 int gqa_tile_tokens(int G) {
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return 0;
   const int nsub = 16 / G;
   return 16 * (nsub < 2 ? 2 : nsub);
 }
