@@ -522,6 +522,33 @@ def main():
     def split_only(i):
         K.attn_decode_splitkv(dargs[i])
 
+    # the same caches paged: blocks of 64 tokens at permuted physical blocks
+    # (one table per copy), decoded through the block table
+    PB = 64
+    nb = L // PB
+    rng = torch.Generator().manual_seed(3)
+
+    def to_paged(plane, perm):
+        def pg(t):
+            blocks = t.view(B, HKV, nb, PB, t.shape[-1]).permute(0, 2, 1, 3, 4).reshape(B * nb, HKV, PB, t.shape[-1])
+            out_ = torch.empty_like(blocks)
+            out_[perm] = blocks
+            return out_
+        return K.NVFP4Plane(pg(plane.codes), pg(plane.scales), plane.tensor_scale, plane.layout)
+
+    pdargs = []   # (decode args, paged K plane, paged V plane, block table): the tensors stay referenced
+    for kc, vc in copies:
+        perm = torch.randperm(B * nb, generator=rng).to(dev)
+        bt = perm.view(B, nb).to(torch.int32).contiguous()
+        pk, pv = to_paged(kc, perm), to_paged(vc, perm)
+        pdargs.append((K.make_decode_args(q, pk, pv, kv_lens, max_kv_len=L, softmax_scale=inp.softmax_scale,
+                                          num_splits=s, part_o=part_o, part_lse=part_lse, block_table=bt),
+                       pk, pv, bt))
+    torch.cuda.synchronize()
+
+    def paged_step(i):
+        K.attn_decode(pdargs[i][0], out, counters=counters)
+
     # warm-up (eager), then capture graphs over all copies
     for i in range(max(args.warmup, n_copies)):
         step(i % n_copies)
@@ -550,6 +577,8 @@ def main():
         "decode_fused": capture(lambda i: step(i, False, True)),
         "decode_two_launch": capture(lambda i: step(i, False, False)),
         "split_kernel": capture(split_only),
+        "decode_fused_paged64": capture(paged_step),
+        "split_kernel_paged64": capture(lambda i: K.attn_decode_splitkv(pdargs[i][0])),
     }
     reps = max(1, math.ceil(args.steps / n_copies))
     steps = reps * n_copies

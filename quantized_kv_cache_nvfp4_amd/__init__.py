@@ -282,6 +282,10 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
     a.part_o, a.part_lse = _ptr(part_o), _ptr(part_lse)
     a.part_capacity = part_o.numel() // (B * Hq * D) if part_o is not None else 0
     a.p_scratch = _ptr(p_scratch)
+    # the struct holds raw device pointers: keep the tensors they point into
+    # alive for as long as the struct is (a plane built inline for the call
+    # would otherwise be freed, and its memory may be returned to the driver)
+    a._keep = (q, k, v, kv_lens, q_rope, k_rope, part_o, part_lse, p_scratch, block_table)
     return a
 
 

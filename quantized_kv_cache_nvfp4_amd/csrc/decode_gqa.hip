@@ -263,14 +263,23 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
 
   // Paged cache: the block-table entries of the chunk's blocks go to LDS
   // once; tile tb then lies in block tb / bs (the block size is a multiple
-  // of the tile) at row (tb mod bs) of that block.
+  // of the tile) at row (tb mod bs) of that block.  The request length and
+  // the entry of this wave's first tile are read beside them (scalar
+  // loads), so that the first K tile can be requested before the barrier
+  // that publishes the LDS copy.  An entry is used only for tokens below
+  // the request length; every entry read lies inside the table row
+  // (ce_ld <= max_kv_len <= bt_stride * bs).
   const int bs = PAGED ? a.block_size : 1;
   const int blk0 = PAGED ? cs / bs : 0;
+  int len_pg = 0;     // paged: the request length
+  int first_blk = 0;  //        the table entry of this wave's first tile
   if constexpr (PAGED) {
-    const int nblk = ce_ld > cs ? (ce_ld - 1) / bs - blk0 + 1 : 0;   // blocks holding rows [cs, ce_ld)
     const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride + blk0;
+    len_pg = a.kv_lens[b];
+    const int ft = cs + wave * TT;
+    first_blk = ft < ce_ld ? bt[ft / bs - blk0] : 0;
+    const int nblk = ce_ld > cs ? (ce_ld - 1) / bs - blk0 + 1 : 0;   // blocks holding rows [cs, ce_ld)
     for (int i = threadIdx.x; i < nblk; i += kThreads) lds_bt[i] = bt[i];
-    __syncthreads();
   }
   // plane row (relative to the kv head's base) of token tb's tile, and the
   // rows available from there (a paged tile ends at its block's end)
@@ -306,11 +315,12 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   // parts fold into the loads' immediate offsets instead of occupying
   // loop-invariant registers)
   auto opaque = [](int x) { asm volatile("" : "+v"(x)); return x; };
-  auto load_ktile = [&](KT& R, int tile) {
+  // (first_base >= 0: the tile's plane row, given by the caller)
+  auto load_ktile = [&](KT& R, int tile, int64_t first_base = -1) {
     const int tb = cs + tile * TT;
     const int lk_ = opaque(lk), lks_ = opaque(lks);
     const int nv = tile_rows(ce_ld - tb);
-    const int64_t base = tile_row(tb);
+    const int64_t base = first_base >= 0 ? first_base : tile_row(tb);
     const Rsrc rk = make_rsrc(kc + base * RB, nv * st * RB);
     const Rsrc rks = make_rsrc(ksc + base * SB, nv * st * SB);
 #pragma unroll
@@ -345,12 +355,19 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   const int sh = a.kv_scale_per_head ? kvh : 0;
   const float kscale = a.k_scale[sh];
   const float vscale = a.v_scale[sh];
-  int L = a.kv_lens[b];
+  int L = PAGED ? len_pg : a.kv_lens[b];
   L = L < a.max_kv_len ? L : a.max_kv_len;
   L = L > 0 ? L : 0;
   const int ce = (cs + chunk < L) ? cs + chunk : L;
   ce_ld = ce;   // every later load stops at the request's end
-  if constexpr (PAGED && NG > 1) load_ktile(KA, wave);
+  if constexpr (PAGED) {
+    if constexpr (NG > 1) {
+      const int ft = cs + wave * TT;
+      load_ktile(KA, wave, ft < ce ? static_cast<int64_t>(first_blk) * a.kv_sblk + static_cast<int64_t>(ft % bs) * st
+                                   : 0);
+    }
+    __syncthreads();   // the chunk's table entries are in LDS
+  }
 
   const float qk_scale = a.softmax_scale * kscale * kLog2e;
 

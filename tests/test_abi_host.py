@@ -249,3 +249,32 @@ def test_mla_validation(L, K):
     assert _decode_rc(L, a) == 3
     a = _mla_args(K); a.kv_st = 0
     assert _decode_rc(L, a) == 1
+
+
+def test_decode_args_keep_their_tensors(K):
+    """The decode-argument struct holds raw pointers: the tensors behind them
+    (planes built inline for the call included) must live as long as it does,
+    or a later kernel reads memory the allocator may have handed back."""
+    import gc
+    import weakref
+    import torch
+    B, Hkv, Hq, D, bs, nb = 1, 2, 8, 128, 64, 3
+    q = torch.zeros(B, Hq, D, dtype=torch.bfloat16)
+    lens = torch.full((B,), bs * nb, dtype=torch.int32)
+
+    def plane():
+        return K.NVFP4Plane(torch.zeros(B * nb, Hkv, bs, D // 2, dtype=torch.uint8),
+                            torch.zeros(B * nb, Hkv, bs, D // 16, dtype=torch.uint8),
+                            torch.ones(1), K.KVQ_PLANE_ROWS)
+
+    part_o = torch.empty(B * Hq * 4 * D)
+    part_lse = torch.empty(B * Hq * 4)
+    bt = torch.arange(B * nb, dtype=torch.int32).view(B, nb)
+    a = K.make_decode_args(q, plane(), plane(), lens, max_kv_len=bs * nb, num_splits=1, part_o=part_o,
+                           part_lse=part_lse, block_table=bt)
+    kc = weakref.ref(a._keep[1].codes)
+    gc.collect()
+    assert kc() is not None and kc().data_ptr() == a.k_codes
+    del a
+    gc.collect()
+    assert kc() is None
