@@ -296,7 +296,8 @@ typedef struct {
      kv_sblk = Hkv * block_size, kv_sh = block_size, kv_st = 1).  Entries
      are read for t < max_kv_len; only those of tokens t < kv_lens[b] are
      used as block indices (they must be valid there).
-     block_size: a positive multiple of the decode tile (attn_decode_tile_tokens). */
+     block_size: a power of two and a multiple of the decode tile
+     (attn_decode_tile_tokens). */
   const int32_t* block_table;
   int32_t block_size;
   int64_t bt_stride;

@@ -346,8 +346,9 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
     if (a->block_table != nullptr) {   // paged cache
       const int tile = kvq::gqa_tile_tokens(G);
       if (a->quantize_p) return fail(KVQ_ERR_UNSUPPORTED, "paged caches are decoded with exact probabilities only");
-      if (a->block_size <= 0 || a->block_size % tile != 0)
-        return fail(KVQ_ERR_ARG, "block_size must be a positive multiple of the decode tile (%d tokens for G=%d)", tile, G);
+      if (a->block_size <= 0 || a->block_size % tile != 0 || (a->block_size & (a->block_size - 1)) != 0)
+        return fail(KVQ_ERR_ARG, "block_size must be a power of two and a multiple of the decode tile (%d tokens for G=%d)",
+                    tile, G);
       const int64_t need = (static_cast<int64_t>(a->max_kv_len) + a->block_size - 1) / a->block_size;
       if (a->bt_stride < need) return fail(KVQ_ERR_ARG, "bt_stride must cover ceil(max_kv_len / block_size) blocks");
       if (a->kv_sblk < 0) return fail(KVQ_ERR_ARG, "kv_sblk must be >= 0");

@@ -269,25 +269,51 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   // that publishes the LDS copy.  An entry is used only for tokens below
   // the request length; every entry read lies inside the table row
   // (ce_ld <= max_kv_len <= bt_stride * bs).
+  // The block size is a power of two: block tb >> bsh, row tb & (bs - 1).
   const int bs = PAGED ? a.block_size : 1;
-  const int blk0 = PAGED ? cs / bs : 0;
+  const int bsh = PAGED ? __builtin_ctz(static_cast<unsigned>(bs)) : 0;
+  const int blk0 = cs >> bsh;
   int len_pg = 0;     // paged: the request length
   int first_blk = 0;  //        the table entry of this wave's first tile
   if constexpr (PAGED) {
     const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride + blk0;
     len_pg = a.kv_lens[b];
     const int ft = cs + wave * TT;
-    first_blk = ft < ce_ld ? bt[ft / bs - blk0] : 0;
-    const int nblk = ce_ld > cs ? (ce_ld - 1) / bs - blk0 + 1 : 0;   // blocks holding rows [cs, ce_ld)
+    first_blk = ft < ce_ld ? bt[(ft >> bsh) - blk0] : 0;
+    const int nblk = ce_ld > cs ? ((ce_ld - 1) >> bsh) - blk0 + 1 : 0;   // blocks holding rows [cs, ce_ld)
     for (int i = threadIdx.x; i < nblk; i += kThreads) lds_bt[i] = bt[i];
   }
-  // plane row (relative to the kv head's base) of token tb's tile, and the
-  // rows available from there (a paged tile ends at its block's end)
-  auto tile_row = [&](int tb) -> int64_t {
+  // Paged: the plane rows of a wave's tiles sit in registers, lane j of a
+  // window holding the row of the wave's tile 64 w + j (tokens at or past
+  // ce_ld get 0); a window is refilled from the LDS table when a load
+  // reaches the next 64 tiles.  K and V loads keep one window each (the V
+  // loads trail the K loads).
+  struct RowWin {
+    int w;          // window index (wave-uniform)
+    uint32_t lo, hi;
+  };
+  RowWin win_k{-1, 0u, 0u}, win_v{-1, 0u, 0u};
+  auto refill = [&](RowWin& rw, int w) {
+    const int tb = cs + (wave + (64 * w + lane) * kWaves) * TT;
+    int64_t row = 0;
+    if (tb < ce_ld)
+      row = static_cast<int64_t>(lds_bt[(tb >> bsh) - blk0]) * a.kv_sblk + static_cast<int64_t>(tb & (bs - 1)) * st;
+    rw.w = w;
+    rw.lo = static_cast<uint32_t>(row);
+    rw.hi = static_cast<uint32_t>(static_cast<uint64_t>(row) >> 32);
+  };
+  // plane row (relative to the kv head's base) of token tb's tile (a tile
+  // of this wave), and the rows available from there (a paged tile ends at
+  // its block's end)
+  auto tile_row = [&](RowWin& rw, int tb) -> int64_t {
     if constexpr (PAGED) {
-      const int i = tb / bs - blk0;
-      return (tb < ce_ld ? static_cast<int64_t>(lds_bt[i]) * a.kv_sblk : 0) + static_cast<int64_t>(tb % bs) * st;
+      const int k = ((tb - cs) / TT - wave) / kWaves;   // the wave's k-th tile
+      if ((k >> 6) != rw.w) refill(rw, k >> 6);
+      const uint32_t lo = __builtin_amdgcn_readlane(rw.lo, k & 63);
+      const uint32_t hi = __builtin_amdgcn_readlane(rw.hi, k & 63);
+      return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
     } else {
+      (void)rw;
       return static_cast<int64_t>(tb) * st;
     }
   };
@@ -320,7 +346,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
     const int tb = cs + tile * TT;
     const int lk_ = opaque(lk), lks_ = opaque(lks);
     const int nv = tile_rows(ce_ld - tb);
-    const int64_t base = first_base >= 0 ? first_base : tile_row(tb);
+    const int64_t base = first_base >= 0 ? first_base : tile_row(win_k, tb);
     const Rsrc rk = make_rsrc(kc + base * RB, nv * st * RB);
     const Rsrc rks = make_rsrc(ksc + base * SB, nv * st * SB);
 #pragma unroll
@@ -367,6 +393,8 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
                                    : 0);
     }
     __syncthreads();   // the chunk's table entries are in LDS
+    refill(win_k, 0);
+    win_v = win_k;
   }
 
   const float qk_scale = a.softmax_scale * kscale * kLog2e;
@@ -418,7 +446,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
       const int tb = cs + tile * TT;
       const int lvt_ = opaque(lvt), lvts_ = opaque(lvts), lv_ = opaque(lv), lvs_ = opaque(lvs);
       const int nv = tile_rows(ce - tb);
-      const int64_t vbase = tile_row(tb);   // TOKEN4: st = 1
+      const int64_t vbase = tile_row(win_v, tb);   // TOKEN4: st = 1
       if constexpr (VL == KVQ_PLANE_TOKEN4) {
         // Group 4u+g of the tile (lane group g): for this lane's elements
         // [8c, 8c+8) the 4 tokens' codes are one contiguous run (16 bytes

@@ -278,3 +278,28 @@ def test_decode_args_keep_their_tensors(K):
     del a
     gc.collect()
     assert kc() is None
+
+
+def test_paged_decode_validation(L, K):
+    """Paged caches: block sizes must be powers of two and multiples of the
+    decode tile (64 tokens at G = 4); the table must cover max_kv_len."""
+    def paged(bs=64, stride=16):
+        a = _good_args(K)
+        a.block_table, a.block_size, a.bt_stride, a.kv_sblk, a.kv_sb = FAKE, bs, stride, 8 * bs, 0
+        a.kv_sh = bs
+        return a
+    assert K.attn_decode_tile_tokens(32, 8) == 64
+    assert _decode_rc(L, paged(bs=32, stride=32)) == 1       # below the tile
+    assert _decode_rc(L, paged(bs=192, stride=6)) == 1       # a multiple of the tile, not a power of two
+    assert _decode_rc(L, paged(bs=0)) == 1
+    assert _decode_rc(L, paged(stride=15)) == 1              # table row shorter than ceil(1024 / 64)
+    a = paged(); a.kv_sblk = -1
+    assert _decode_rc(L, a) == 1
+    a = paged(); a.block_table = FAKE_ODD
+    assert _decode_rc(L, a) == 3
+    a = paged(); a.quantize_p, a.prob_scale, a.p_scratch = 1, 1.0 / 448.0, FAKE
+    assert _decode_rc(L, a) == 2                             # exact probabilities only
+    a = paged(); a.layout = K.KVQ_LAYOUT_MLA; a.Hkv = 1; a.Hq = 16
+    assert _decode_rc(L, a) == 2                             # GQA layout only
+    a = paged(); a.v_layout = K.KVQ_PLANE_TOKEN4; a.kv_sblk = 8 * 64 + 2
+    assert _decode_rc(L, a) == 3

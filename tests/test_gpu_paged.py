@@ -64,6 +64,10 @@ CASES = [
     (("fp8", "fp8", 64), 1, 64, 1, False),
     (("nvfp4", "mha", 1024, 2, 16), 0, 256, 2, False),                        # G = 1: tile 256
     (("nvfp4", "custom", 2, 16, 2, 128, (300, 77), "bf16"), 0, 32, 4, False),  # G = 8: tile 32
+    # one split over long requests: more than 64 tiles per wave, so the
+    # register windows of tile rows are refilled from the LDS table
+    (("nvfp4", "custom", 2, 8, 1, 128, (9000, 8300), "bf16"), 0, 32, 1, False),   # G = 8: 71 tiles per wave
+    (("nvfp4", "custom", 1, 32, 8, 128, (20000,), "bf16"), 1, 64, 1, True),       # G = 4: 79 tiles per wave
 ]
 
 
