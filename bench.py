@@ -381,9 +381,18 @@ def run_fp8(args):
     out8 = torch.empty(FP8_B, Hq, D, dtype=torch.uint8, device=dev)
     out_scale = torch.full((1,), 4.0 / 448.0, dtype=torch.float32, device=dev)   # a given fp32 output scale
 
-    def mk(kc, vc, fp8p):
+    # FP8 query (the QKV-FP8 schemes): the query batch calibrated and packed
+    # per tensor by the same kernels, viewed as [B, Hq, 1, D]
+    q4 = q.contiguous().view(FP8_B, inp.Hq, 1, D)
+    qa = K.kvq_amax(q4)
+    qp8 = K.kvq_pack_fp8(q4, qa)
+    q8 = qp8.codes.view(FP8_B, inp.Hq, D)
+
+    def mk(kc, vc, fp8p, fp8q=False):
         extra = dict(quantize_p=True, prob_scale=float(1.0 / 448.0), p_scratch=scratch) if fp8p else {}
-        return K.make_decode_args(q, kc, vc, lens, max_kv_len=FP8_HI, softmax_scale=inp.softmax_scale,
+        if fp8q:
+            extra["q_scale"] = qp8.scale
+        return K.make_decode_args(q8 if fp8q else q, kc, vc, lens, max_kv_len=FP8_HI, softmax_scale=inp.softmax_scale,
                                   num_splits=s, part_o=part_o, part_lse=part_lse, **extra)
 
     dargs = [mk(kc, vc, False) for kc, vc in copies]
@@ -393,6 +402,7 @@ def run_fp8(args):
                                K.FP8Plane(vph.codes.clone(), vph.scale.clone(), vph.layout))
                               for _ in range(n_copies - 1)]
     hargs = [mk(kc, vc, False) for kc, vc in hcopies]
+    qargs = [mk(kc, vc, False, fp8q=True) for kc, vc in copies]
 
     def step(i, a, o):
         used = K.attn_decode_splitkv(a[i])
@@ -407,6 +417,9 @@ def run_fp8(args):
           "decode_fp8_out": timed(capture(lambda i: step(i, dargs, out8))),
           "decode_fp8p": timed(capture(lambda i: step(i, pargs, out))),
           "decode_per_head_scales": timed(capture(lambda i: step(i, hargs, out))),
+          "decode_fp8_query": timed(capture(lambda i: step(i, qargs, out))),
+          # the query's calibration + pack (two kernels and the amax clear), per step
+          "quantize_query_fp8": timed(capture(lambda i: (K.kvq_amax(q4, out=qa), K.kvq_pack_fp8(q4, qa, out=qp8)))),
           "split_kernel": timed(capture(lambda i: K.attn_decode_splitkv(dargs[i]))),
           "fp8p_passes": timed(capture(lambda i: K.attn_decode_splitkv(pargs[i])))}
     assert torch.isfinite(out.float()).all()

@@ -254,7 +254,7 @@ typedef struct {
   int32_t D, Dv, Drope;
   int32_t max_kv_len;  /* upper bound on kv_lens and rows allocated per request */
   const void* q;       /* device, q_dtype, [B][Hq][D] with element strides: */
-  int32_t q_dtype;     /* KVQ_BF16 or KVQ_F32                              */
+  int32_t q_dtype;     /* KVQ_BF16, KVQ_F32, or (GQA layout) KVQ_FP8E4M3:  */
   int64_t q_sb, q_sh;  /*   q + b*q_sb + h*q_sh                            */
   const void* q_rope;  /* MLA: device bf16 [B][Hq][Drope], element strides */
   int64_t qr_sb, qr_sh;
@@ -302,6 +302,18 @@ typedef struct {
   int32_t block_size;
   int64_t bt_stride;
   int64_t kv_sblk;
+  /* FP8 query (GQA layout; the QKV-FP8 schemes of compressed-tensors PR #436,
+     "Changes" and "Testing": the attention's input activations quantized to
+     FP8 E4M3 per tensor or per head).  With q_dtype = KVQ_FP8E4M3, q holds
+     E4M3 codes (q 8-byte aligned, q_sb and q_sh multiples of 8) — e.g. from
+     kvq_pack_fp8 / kvq_pack_fp8_heads of the query viewed as [B][Hq][1][D] —
+     and q_scale their scale: device float[1], or float[Hq] with
+     q_scale_per_head = 1 (query head h dequantized with q_scale[h]).  The
+     codes enter the score contraction exactly; the scale multiplies the
+     score (beside the K tensor scale and softmax_scale).  Exact
+     probabilities only (quantize_p = 0).  Unused otherwise. */
+  const float* q_scale;
+  int32_t q_scale_per_head;
 } kvq_decode_args;
 
 /*

@@ -35,6 +35,15 @@ Definitions followed
   of its own: amax_h over the head's valid tokens of every request, scale_h =
   amax_h / 448.
 
+* FP8 query (compressed-tensors PR #436, "Changes": an ``attention`` scheme
+  whose ``input_activations`` are 8-bit float with ``strategy tensor``;
+  "Testing": the QKV-FP8-Tensor and QKV-FP8-Head rows of the GSM8K table).
+  Reading taken: the decode step's query [B, Hq, D] is quantized exactly
+  like a KV tensor — per tensor (amax over every element of the query
+  batch) or per attention head (amax over that head's elements), scale =
+  amax / 448, code = E4M3(q / scale) — and the attention then uses the
+  dequantized query code * scale.
+
 Why float64 decides exactly: x has at most 24 significant bits; a threshold
 (E2M1 midpoint * s_hat * s_t, or E4M3 midpoint * 6 * s_t) has at most 32.  Two
 such dyadic numbers that differ do so by at least 2^-32 relative, far above
@@ -171,3 +180,15 @@ def fp8_unpack_heads(codes, scales, head_axis=1):
     shape = [1] * codes.ndim
     shape[ha] = codes.shape[ha]
     return F.e4m3_decode(codes) * np.asarray(scales, dtype=np.float64).reshape(shape)
+
+
+def fp8_quantize_query(q, per_head=False):
+    """FP8 E4M3 query [B, Hq, D], per tensor or per attention head (axis 1).
+    Returns (codes uint8 [B, Hq, D], scales float64 [1] or [Hq], dequantized
+    query float64)."""
+    q = np.asarray(q, dtype=np.float64)
+    if per_head:
+        codes, scales = fp8_pack_heads(q, amax_heads(q, None, head_axis=1), head_axis=1)
+        return codes, scales, fp8_unpack_heads(codes, scales, head_axis=1)
+    codes, scale = fp8_pack(q, amax(q))
+    return codes, np.array([scale], dtype=np.float64), fp8_unpack(codes, scale)

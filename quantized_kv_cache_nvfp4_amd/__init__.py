@@ -216,7 +216,7 @@ def kvq_fp8p_scratch_floats(B: int, Hq: int, s: int, max_kv_len: int) -> int:
 
 def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_splits=0, part_o, part_lse,
                      q_rope=None, k_rope=None, quantize_p=False, prob_scale=1.0 / 448.0,
-                     p_scratch=None, block_table=None) -> KvqDecodeArgs:
+                     p_scratch=None, block_table=None, q_scale=None) -> KvqDecodeArgs:
     """Fill the C decode-argument struct from tensors (no device work).
 
     GQA: q [B, Hq, D]; k, v NVFP4Plane / FP8Plane with codes [B, Hkv, Lmax, .],
@@ -225,6 +225,8 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
     block_table[b, t // block_size]).
     MLA: q = q_c [B, H, Dc]; k = NVFP4Plane of the latent [B, Lmax, .];
     v = None; q_rope [B, H, Dr] and k_rope [B, Lmax, Dr] bf16.
+    FP8 query (GQA): q uint8 E4M3 codes [B, Hq, D] with q_scale, a device
+    float tensor of 1 (per tensor) or Hq (per query head) entries.
     """
     a = KvqDecodeArgs()
     mla = v is None
@@ -261,7 +263,15 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
             a.block_table, a.block_size = _ptr(block_table), int(k.codes.shape[2])
             a.bt_stride, a.kv_sblk, a.kv_sb = block_table.stride(0), kr.s0, 0
     a.max_kv_len = int(max_kv_len)
-    a.q, a.q_dtype, a.q_sb, a.q_sh = _ptr(q), _DT[q.dtype], q.stride(0), q.stride(1)
+    if q.dtype == torch.uint8:   # FP8 query codes
+        if q_scale is None:
+            raise ValueError("an FP8 query needs q_scale")
+        if q_scale.numel() not in (1, Hq):
+            raise ValueError(f"q_scale must have 1 or Hq = {Hq} entries")
+        a.q_dtype, a.q_scale, a.q_scale_per_head = KVQ_FP8E4M3, _ptr(q_scale), int(q_scale.numel() > 1)
+    else:
+        a.q_dtype = _DT[q.dtype]
+    a.q, a.q_sb, a.q_sh = _ptr(q), q.stride(0), q.stride(1)
     if fmt == KVQ_NVFP4:
         a.k_codes, a.k_scales, a.k_scale = _ptr(k.codes), _ptr(k.scales), _ptr(k.tensor_scale)
         if not mla:
@@ -285,7 +295,7 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
     # the struct holds raw device pointers: keep the tensors they point into
     # alive for as long as the struct is (a plane built inline for the call
     # would otherwise be freed, and its memory may be returned to the driver)
-    a._keep = (q, k, v, kv_lens, q_rope, k_rope, part_o, part_lse, p_scratch, block_table)
+    a._keep = (q, k, v, kv_lens, q_rope, k_rope, part_o, part_lse, p_scratch, block_table, q_scale)
     return a
 
 

@@ -56,6 +56,7 @@ class KvqDecodeArgs(ctypes.Structure):
         ("kv_scale_per_head", ctypes.c_int32),
         ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
         ("bt_stride", ctypes.c_int64), ("kv_sblk", ctypes.c_int64),
+        ("q_scale", ctypes.c_void_p), ("q_scale_per_head", ctypes.c_int32),
     ]
 
 

@@ -290,12 +290,23 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
   if (a->kv_scale_per_head != 0 &&
       (a->kv_scale_per_head != 1 || a->kv_format != KVQ_FP8E4M3 || a->layout != KVQ_LAYOUT_GQA))
     return fail(KVQ_ERR_UNSUPPORTED, "kv_scale_per_head must be 0 or 1, and 1 only for FP8 with the GQA layout");
-  if (a->q_dtype != KVQ_BF16 && a->q_dtype != KVQ_F32) return fail(KVQ_ERR_UNSUPPORTED, "q_dtype must be BF16 or F32");
+  if (a->q_dtype == KVQ_FP8E4M3) {   // FP8 query codes with their scale
+    if (a->layout != KVQ_LAYOUT_GQA) return fail(KVQ_ERR_UNSUPPORTED, "FP8 queries are decoded for the GQA layout only");
+    if (a->q_scale == nullptr) return fail(KVQ_ERR_ARG, "an FP8 query needs q_scale");
+    if (a->quantize_p) return fail(KVQ_ERR_UNSUPPORTED, "FP8 queries are decoded with exact probabilities only");
+    if (a->q_scale_per_head != 0 && a->q_scale_per_head != 1) return fail(KVQ_ERR_ARG, "q_scale_per_head must be 0 or 1");
+    if (!aligned(a->q_scale, 4)) return fail(KVQ_ERR_ALIGN, "q_scale must be 4-byte aligned");
+    if (!aligned(a->q, 8) || a->q_sb % 8 != 0 || a->q_sh % 8 != 0)
+      return fail(KVQ_ERR_ALIGN, "FP8 query rows must be 8-byte aligned (q, q_sb, q_sh)");
+  } else if (a->q_dtype != KVQ_BF16 && a->q_dtype != KVQ_F32) {
+    return fail(KVQ_ERR_UNSUPPORTED, "q_dtype must be BF16, F32 or (GQA) FP8E4M3");
+  }
   if (!(a->softmax_scale > 0.0f) || a->softmax_scale != a->softmax_scale || a->softmax_scale > 3.0e38f)
     return fail(KVQ_ERR_ARG, "softmax_scale must be a positive finite number");
   if (!aligned(a->k_codes, 16)) return fail(KVQ_ERR_ALIGN, "k_codes must be 16-byte aligned");
   if (a->k_scales != nullptr && !aligned(a->k_scales, 4)) return fail(KVQ_ERR_ALIGN, "k_scales must be 4-byte aligned");
-  if (a->q_dtype == KVQ_F32 ? !aligned(a->q, 4) : !aligned(a->q, 2)) return fail(KVQ_ERR_ALIGN, "q misaligned");
+  if (a->q_dtype == KVQ_F32 ? !aligned(a->q, 4) : a->q_dtype == KVQ_BF16 ? !aligned(a->q, 2) : false)
+    return fail(KVQ_ERR_ALIGN, "q misaligned");
   if (a->kv_st < 0 || a->kv_sb < 0 || a->kv_sh < 0) return fail(KVQ_ERR_ARG, "cache strides must be >= 0");
   // token offsets inside one (request, kv head) are computed in 32 bits
   const int64_t row_bytes = a->kv_format == KVQ_NVFP4 ? a->D / 2 : a->D;

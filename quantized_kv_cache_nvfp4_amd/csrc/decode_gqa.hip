@@ -178,12 +178,14 @@ struct FusedOut {
 
 // ------------------------------------------------------------------ kernel
 // Template: KVF cache format, G query heads per kv head, D head_dim,
-// QF32 fp32 queries (hi/lo split), PSPLIT 2 = P carried as f16 hi + lo,
+// QT query type (kQBf16; kQF32: fp32 queries, hi/lo split; kQFp8: E4M3
+// codes with a scale), PSPLIT 2 = P carried as f16 hi + lo,
 // FUSED: the last work-group of each (request, kv head) merges the partials
 // and writes the final output (one launch per decode step).
 // Work-groups per CU the register allocation is sized for: 8 waves per CU
 // (2 per SIMD, up to 256 VGPRs each).
-template <int KVF, int G, bool QF32, int VL>
+constexpr int kQBf16 = 0, kQF32 = 1, kQFp8 = 2;
+template <int KVF, int G, int QT, int VL>
 constexpr int decode_min_blocks() {
   return 8 / kWaves;
 }
@@ -195,8 +197,10 @@ constexpr int kMaxChunkBlocks = kPagedMaxChunkBlocks;
 // PM: 0 attention, 1 FP8-P pass 1 (scores), 2 FP8-P pass 2 (quantized P . V).
 // PAGED: the planes are paged (block table; block size a multiple of the
 // tile, so every tile lies in one block).
-template <int KVF, int G, int D, bool QF32, int PSPLIT, bool FUSED, int VL, int PM, bool PAGED>
-__global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>())) k_decode_gqa(kvq_decode_args a, int num_splits, FusedOut fo) {
+template <int KVF, int G, int D, int QT, int PSPLIT, bool FUSED, int VL, int PM, bool PAGED>
+__global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>())) k_decode_gqa(kvq_decode_args a, int num_splits, FusedOut fo) {
+  constexpr bool QF32 = QT == kQF32;
+  constexpr bool q8 = QT == kQFp8;   // FP8 query codes: 8 bytes per query word instead of 16
   static_assert(PM == 0 || (!FUSED && PSPLIT == 1), "the FP8-P passes write partials only");
   static_assert(!PAGED || PM == 0, "paged caches use exact probabilities");
   using Gm = Geo<KVF, D>;
@@ -241,13 +245,23 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   constexpr int kQRaw = QF32 ? 2 * Gm::kQkJ : Gm::kQkJ;   // 16-byte query words per lane
   uint4 qraw[kQRaw];
   if constexpr (PM != 2) {
-    // lane (g, c) holds Q[h = c % G][g*QKE + 8j + e] (q rows and strides are 16-byte aligned)
+    // lane (g, c) holds Q[h = c % G][g*QKE + 8j + e] (q rows and strides are 16-byte aligned,
+    // 8-byte aligned for FP8 codes)
     const int64_t qb = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(hq0 + my_h) * a.q_sh +
                        g * Gm::kQkElems;
-    const uint4* qp = QF32 ? reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + qb)
-                           : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qb);
+    if constexpr (q8) {
+      const uint2* qp = reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(a.q) + qb);
 #pragma unroll
-    for (int j = 0; j < kQRaw; ++j) qraw[j] = qp[j];
+      for (int j = 0; j < kQRaw; ++j) {
+        const uint2 w = qp[j];
+        qraw[j] = make_uint4(w.x, w.y, 0u, 0u);
+      }
+    } else {
+      const uint4* qp = QF32 ? reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + qb)
+                             : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qb);
+#pragma unroll
+      for (int j = 0; j < kQRaw; ++j) qraw[j] = qp[j];
+    }
   }
   // per-(request, kv head) plane bases (paged: the kv head's offset inside
   // a block; the block comes from the table per tile)
@@ -397,7 +411,9 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
     win_v = win_k;
   }
 
-  const float qk_scale = a.softmax_scale * kscale * kLog2e;
+  float qk_scale = a.softmax_scale * kscale * kLog2e;
+  // FP8 query: its scale (per tensor, or this lane's query head) joins the score factor
+  if constexpr (q8) qk_scale *= a.q_scale[a.q_scale_per_head ? hq0 + my_h : 0];
 
   float m_run = -INFINITY;  // running max of row c's head (log2 domain; the same for all its rows)
   float l_run = 0.0f;       // this lane's share of row c's denominator
@@ -413,6 +429,11 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
     if constexpr (PM != 2) {
 #pragma unroll
       for (int j = 0; j < Gm::kQkJ; ++j) {
+        if constexpr (q8) {   // E4M3 codes -> f16, exact
+          const uint4 w = qraw[j];
+          qop[0][j] = cat4(fp8x2<false>(w.x), fp8x2<true>(w.x), fp8x2<false>(w.y), fp8x2<true>(w.y));
+          continue;
+        }
         float x[8];
         if constexpr (QF32) {
           const uint4 w0 = qraw[2 * j], w1 = qraw[2 * j + 1];
@@ -1058,44 +1079,48 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QF32, VL>
   }
 }
 
-template <int KVF, int G, int D, bool QF32, int PSPLIT, int VL, int PM, bool PAGED>
+template <int KVF, int G, int D, int QT, int PSPLIT, int VL, int PM, bool PAGED>
 hipError_t launch_p(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
   dim3 grid(p.s, a.Hkv, a.B);
   if constexpr (PM == 0) {
     if (fo != nullptr) {
-      hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, true, VL, 0, PAGED>), grid, dim3(kThreads), 0, st, a,
+      hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QT, PSPLIT, true, VL, 0, PAGED>), grid, dim3(kThreads), 0, st, a,
                          p.s, *fo);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QF32, PSPLIT, false, VL, PM, PAGED>), grid, dim3(kThreads), 0, st, a,
+  hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QT, PSPLIT, false, VL, PM, PAGED>), grid, dim3(kThreads), 0, st, a,
                      p.s, FusedOut{});
   return hipGetLastError();
 }
 
-template <int KVF, int G, int D, bool QF32, int PSPLIT, int VL, int PM>
+template <int KVF, int G, int D, int QT, int PSPLIT, int VL, int PM>
 hipError_t launch_v(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
   if constexpr (PM == 0) {
-    if (a.block_table != nullptr) return launch_p<KVF, G, D, QF32, PSPLIT, VL, 0, true>(a, p, fo, st);
+    if (a.block_table != nullptr) return launch_p<KVF, G, D, QT, PSPLIT, VL, 0, true>(a, p, fo, st);
   }
-  return launch_p<KVF, G, D, QF32, PSPLIT, VL, PM, false>(a, p, fo, st);
+  return launch_p<KVF, G, D, QT, PSPLIT, VL, PM, false>(a, p, fo, st);
 }
 
-template <int KVF, int G, int D, bool QF32, int PSPLIT, int PM>
+template <int KVF, int G, int D, int QT, int PSPLIT, int PM>
 hipError_t launch_t(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
   if constexpr (D == 128 && PM != 1) {   // pass 1 reads no V
-    if (a.v_layout == KVQ_PLANE_TOKEN4) return launch_v<KVF, G, D, QF32, PSPLIT, KVQ_PLANE_TOKEN4, PM>(a, p, fo, st);
+    if (a.v_layout == KVQ_PLANE_TOKEN4) return launch_v<KVF, G, D, QT, PSPLIT, KVQ_PLANE_TOKEN4, PM>(a, p, fo, st);
   }
-  return launch_v<KVF, G, D, QF32, PSPLIT, KVQ_PLANE_ROWS, PM>(a, p, fo, st);
+  return launch_v<KVF, G, D, QT, PSPLIT, KVQ_PLANE_ROWS, PM>(a, p, fo, st);
 }
 
 template <int KVF, int G, int D, int PM>
 hipError_t launch_q(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
-  if constexpr (PM == 2) return launch_t<KVF, G, D, false, 1, 2>(a, p, fo, st);   // reads no Q
+  if constexpr (PM == 2) return launch_t<KVF, G, D, kQBf16, 1, 2>(a, p, fo, st);   // reads no Q
   // fp32 queries select the fp32-accuracy path (hi/lo split of Q, and of P
   // when P is not quantized)
-  if (a.q_dtype == KVQ_F32) return launch_t<KVF, G, D, true, (PM == 0 ? 2 : 1), PM>(a, p, fo, st);
-  return launch_t<KVF, G, D, false, 1, PM>(a, p, fo, st);
+  if (a.q_dtype == KVQ_F32) return launch_t<KVF, G, D, kQF32, (PM == 0 ? 2 : 1), PM>(a, p, fo, st);
+  if (a.q_dtype == KVQ_FP8E4M3) {   // exact probabilities only
+    if constexpr (PM == 0) return launch_t<KVF, G, D, kQFp8, 1, 0>(a, p, fo, st);
+    return hipErrorInvalidValue;
+  }
+  return launch_t<KVF, G, D, kQBf16, 1, PM>(a, p, fo, st);
 }
 
 template <int KVF, int D, int PM>
@@ -1129,7 +1154,7 @@ bool gqa_supported(int kv_format, int G, int D, int q_dtype) {
   if (kv_format != KVQ_NVFP4 && kv_format != KVQ_FP8E4M3) return false;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return false;
   if (D != 64 && D != 128) return false;
-  return q_dtype == KVQ_BF16 || q_dtype == KVQ_F32;
+  return q_dtype == KVQ_BF16 || q_dtype == KVQ_F32 || q_dtype == KVQ_FP8E4M3;
 }
 
 hipError_t launch_decode_gqa(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {

@@ -303,3 +303,27 @@ def test_paged_decode_validation(L, K):
     assert _decode_rc(L, a) == 2                             # GQA layout only
     a = paged(); a.v_layout = K.KVQ_PLANE_TOKEN4; a.kv_sblk = 8 * 64 + 2
     assert _decode_rc(L, a) == 3
+
+
+def test_fp8_query_validation(L, K):
+    """FP8 queries: GQA layout only, a scale pointer, 8-byte aligned rows."""
+    def q8():
+        a = _good_args(K)
+        a.q_dtype, a.q_scale = K.KVQ_FP8E4M3, FAKE
+        return a
+    a = q8(); a.q_scale = None
+    assert _decode_rc(L, a) == 1
+    a = q8(); a.q_scale_per_head = 2
+    assert _decode_rc(L, a) == 1
+    a = q8(); a.q_scale = FAKE_ODD
+    assert _decode_rc(L, a) == 3
+    a = q8(); a.q = ctypes.c_void_p(0x10004)
+    assert _decode_rc(L, a) == 3
+    a = q8(); a.q_sh = 12
+    assert _decode_rc(L, a) == 3
+    a = q8(); a.layout = K.KVQ_LAYOUT_MLA; a.Hkv = 1; a.Hq = 16
+    assert _decode_rc(L, a) == 2
+    a = q8(); a.quantize_p, a.prob_scale, a.p_scratch = 1, 1.0 / 448.0, FAKE
+    assert _decode_rc(L, a) == 2
+    a = _good_args(K); a.q_dtype = K.KVQ_F16
+    assert _decode_rc(L, a) == 2

@@ -1,0 +1,75 @@
+"""GPU parity for FP8 queries (the QKV-FP8 schemes): the query batch is
+calibrated and packed by the same kernels as the KV planes (viewed as
+[B, Hq, 1, D]), bit-exact against the oracle, and the decode over FP8
+query codes (scale per tensor or per query head) is checked against the
+oracle's attention with the dequantized query, within the same output gates
+as the bf16-query path."""
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth
+from gpu_helpers import DEV, K, announce, assert_bf16_output, gpu_pack, make_inputs, oracle_gqa
+from oracle import attention as OA
+from oracle import quant as OQ
+
+pytestmark = pytest.mark.gpu
+
+
+def _quantize_query(q, per_head):
+    k_ = K()
+    B, Hq, D = q.shape
+    q4 = q.contiguous().view(B, Hq, 1, D)
+    amax = k_.kvq_amax(q4, per_head=per_head)
+    qp = k_.kvq_pack_fp8(q4, amax)
+    return qp.codes.view(B, Hq, D), qp.scale
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+@pytest.mark.parametrize("key", [("nvfp4", "gqa", 1024), ("nvfp4", "custom", 2, 16, 2, 128, (300, 77), "bf16")])
+def test_query_pack_bit_exact(key, per_head):
+    announce(f"fp8 query pack {key} per_head={per_head}")
+    inp = make_inputs(key)
+    codes, scale = _quantize_query(inp.q.to(DEV), per_head)
+    torch.cuda.synchronize()
+    oc, osc, _ = OQ.fp8_quantize_query(kvq_synth.f64(inp.q), per_head)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scale.cpu().numpy().astype(np.float64), osc)
+
+
+CASES = [
+    # (key, kv format, v_layout, splits, fused, per_head)
+    (("nvfp4", "gqa", 1024), "nvfp4", 1, 3, False, False),
+    (("nvfp4", "gqa", 1024), "nvfp4", 1, 0, True, True),
+    (("fp8", "fp8", 64), "fp8", 0, 2, False, False),
+    (("fp8", "fp8", 64), "fp8", 1, 0, True, True),
+    (("nvfp4", "mha", 1024, 2, 16), "nvfp4", 0, 2, False, True),                       # G = 1
+    (("nvfp4", "custom", 2, 16, 2, 128, (300, 77), "bf16"), "nvfp4", 0, 4, False, True),  # G = 8
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0][0]}-{c[0][1]}-v{c[2]}-s{c[3]}-f{int(c[4])}-h{int(c[5])}")
+def test_decode_fp8_query(case):
+    key, fmt, v_layout, s, fused, per_head = case
+    announce(f"fp8 query decode {case}")
+    k_ = K()
+    inp = make_inputs(key)
+    kp, vp, _, _, lens = gpu_pack(inp, fmt, v_layout)
+    q8, q_scale = _quantize_query(inp.q.to(DEV), per_head)
+    B, Hq, D = inp.B, inp.Hq, inp.D
+    part_o = torch.empty(B * Hq * 64 * D, dtype=torch.float32, device=DEV)
+    part_lse = torch.empty(B * Hq * 64, dtype=torch.float32, device=DEV)
+    args = k_.make_decode_args(q8, kp, vp, lens, max_kv_len=inp.Lmax, softmax_scale=inp.softmax_scale,
+                               num_splits=s, part_o=part_o, part_lse=part_lse, q_scale=q_scale)
+    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=DEV)
+    if fused:
+        counters = torch.zeros(B * inp.Hkv, dtype=torch.int32, device=DEV)
+        k_.attn_decode(args, out, counters=counters)
+    else:
+        used = k_.attn_decode_splitkv(args)
+        k_.attn_decode_combine(part_o, part_lse, B, Hq, D, used, out)
+    torch.cuda.synchronize()
+    _, _, qhat = OQ.fp8_quantize_query(kvq_synth.f64(inp.q), per_head)
+    _, _, _, khat, vhat = oracle_gqa(key)
+    o_ref, _ = OA.decode_gqa(qhat, khat, vhat, inp.kv_lens, inp.softmax_scale)
+    assert_bf16_output(out, o_ref, f"fp8 query {case}")

@@ -325,3 +325,44 @@ def test_fp8_heads_reduce_to_per_tensor():
     for h in range(4):
         c1, s1 = Q.fp8_pack(x[:, h], a[h])
         assert np.array_equal(c_h[:, h], c1) and s_h[h] == s1
+
+
+def test_fp8_query_worked_example():
+    """FP8 query, hand-worked E4M3 codes (bias 7, 3 mantissa bits, ties to
+    even).  Per tensor: amax 448 gives scale 1; 448 = 1.75 * 2^8 -> 0x7E,
+    1.0625 (midway 1.0 / 1.125) -> 1.0 = 0x38, 1.1875 (midway 1.125 / 1.25)
+    -> 1.25 = 0x3A, -3 = -1.5 * 2^1 -> 0xC4, 224 = 1.75 * 2^7 -> 0x76,
+    0.5 -> 0x30.  Per head: head 1 has amax 224, scale 0.5, so 224 -> 0x7E
+    and 0.5 -> 1.0 = 0x38, dequantized back to 224 and 0.5."""
+    q = np.zeros((1, 2, 16))
+    q[0, 0, :5] = [448.0, 1.0625, 1.1875, -3.0, 0.0]
+    q[0, 1, :2] = [224.0, 0.5]
+    codes, scales, qhat = Q.fp8_quantize_query(q)
+    assert scales.tolist() == [1.0]
+    assert codes[0, 0, :5].tolist() == [0x7E, 0x38, 0x3A, 0xC4, 0x00]
+    assert codes[0, 1, :2].tolist() == [0x76, 0x30]
+    assert qhat[0, 0, :4].tolist() == [448.0, 1.0, 1.25, -3.0]
+    codes, scales, qhat = Q.fp8_quantize_query(q, per_head=True)
+    assert scales.tolist() == [1.0, 0.5]
+    assert codes[0, 1, :2].tolist() == [0x7E, 0x38]
+    assert qhat[0, 1, :2].tolist() == [224.0, 0.5]
+    assert codes[0, 0, :5].tolist() == [0x7E, 0x38, 0x3A, 0xC4, 0x00]
+
+
+def test_fp8_query_properties():
+    """Values already on the E4M3 grid times the scale come back unchanged;
+    per head equals per tensor when every head has the same amax; the
+    per-tensor error is at most half a code step (relative 2^-4) above the
+    E4M3 subnormal range."""
+    rng = np.random.default_rng(11)
+    grid = F.e4m3_decode(np.arange(0x08, 0x7F, dtype=np.uint8))   # positive normal E4M3 values
+    q = rng.choice(grid, size=(2, 4, 32)) * rng.choice([-1.0, 1.0], size=(2, 4, 32))
+    q[:, :, 0] = 448.0   # every head's amax is 448: scale 1
+    codes, scales, qhat = Q.fp8_quantize_query(q)
+    assert scales.tolist() == [1.0] and np.array_equal(qhat, q)
+    c2, s2, qh2 = Q.fp8_quantize_query(q, per_head=True)
+    assert np.array_equal(c2, codes) and np.array_equal(qh2, qhat) and s2.tolist() == [1.0] * 4
+    x = rng.standard_normal((2, 4, 64))
+    _, sc, xh = Q.fp8_quantize_query(x)
+    big = np.abs(x) / sc[0] >= 2.0 ** -6
+    assert np.all(np.abs(xh - x)[big] <= 2.0 ** -4 * np.abs(x)[big] * (1 + 1e-12))
