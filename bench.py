@@ -10,9 +10,11 @@ the whole cache and the combine of the partials, either fused (attn_decode:
 the last work-group of each (request, kv head) merges the partials) or in two
 launches (attn_decode_splitkv + attn_decode_combine); both are timed and
 `value` is the faster.  The quantize-on-append of the new token's K and V
-rows (one kvq_pack_nvfp4_batch launch with the calibrated amax) is timed
-beside it, alone and together with the decode ("fused" / "two_launch" in
-step_us).  Calibration (kvq_amax) and the bulk packing of the cache run once
+rows is timed beside it: as its own kvq_pack_nvfp4_batch launch, alone and
+followed by the decode ("append", "fused" / "two_launch" in step_us), and
+folded into the decode launch itself ("fused_append_in_decode",
+"two_launch_append_in_split"); the same decode over 64-token paged copies of
+the cache is timed too ("*_paged64").  Calibration (kvq_amax) and the bulk packing of the cache run once
 before the timed region.  The roofline entry is the split kernel alone:
 its average duration per launch from a graph of back-to-back launches.
 
@@ -515,8 +517,8 @@ def main():
 
     cus = K.kvq_device_cu_count()
     s = args.splits if args.splits > 0 else K.kvq_auto_num_splits(cus, B, HKV, L, D, HQ)
-    part_o = torch.empty(B * HQ * s * D, dtype=torch.float32, device=dev)
-    part_lse = torch.empty(B * HQ * s, dtype=torch.float32, device=dev)
+    part_o = torch.empty(B * HQ * (s + 1) * D, dtype=torch.float32, device=dev)   # (+1: the fused append's partial)
+    part_lse = torch.empty(B * HQ * (s + 1), dtype=torch.float32, device=dev)
     out = torch.empty(B, HQ, D, dtype=torch.bfloat16, device=dev)
     counters = torch.zeros(B * HKV, dtype=torch.int32, device=dev)
     dargs = [K.make_decode_args(q, kc, vc, kv_lens, max_kv_len=L, softmax_scale=inp.softmax_scale,
@@ -534,6 +536,16 @@ def main():
 
     def split_only(i):
         K.attn_decode_splitkv(dargs[i])
+
+    # the decode step with the new token's append fused in (the decode packs
+    # row L - 1 itself and attends to it from its fresh codes)
+    new_k3, new_v3 = new_k.view(B, HKV, D), new_v.view(B, HKV, D)
+    aargs = [K.make_decode_args(q, kc, vc, kv_lens, max_kv_len=L, softmax_scale=inp.softmax_scale, num_splits=s,
+                                part_o=part_o, part_lse=part_lse, new_k=new_k3, new_v=new_v3) for kc, vc in copies]
+
+    def append_two_launch(i):
+        used = K.attn_decode_splitkv(aargs[i])
+        K.attn_decode_combine(part_o, part_lse, B, HQ, D, used, out)
 
     # the same caches paged: blocks of 64 tokens at permuted physical blocks
     # (one table per copy), decoded through the block table
@@ -590,6 +602,8 @@ def main():
         "decode_fused": capture(lambda i: step(i, False, True)),
         "decode_two_launch": capture(lambda i: step(i, False, False)),
         "split_kernel": capture(split_only),
+        "fused_append_in_decode": capture(lambda i: K.attn_decode(aargs[i], out, counters=counters)),
+        "two_launch_append_in_split": capture(append_two_launch),
         "decode_fused_paged64": capture(paged_step),
         "split_kernel_paged64": capture(lambda i: K.attn_decode_splitkv(pdargs[i][0])),
     }

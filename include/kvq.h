@@ -314,6 +314,23 @@ typedef struct {
      probabilities only (quantize_p = 0).  Unused otherwise. */
   const float* q_scale;
   int32_t q_scale_per_head;
+  /* Quantize-on-append fused into the decode step (GQA layout, bf16
+     queries, exact probabilities; the cache grows by one token per step as the model
+     serves, Model-Optimizer PR #714 "Usage").  new_k, new_v: device rows
+     [B][Hkv][D] (contiguous, new_dtype KVQ_BF16, KVQ_F16 or KVQ_F32) of the
+     step's new token, or NULL for none.  The token is request b's last, at
+     position kv_lens[b] - 1 (kv_lens counts it; clamped to max_kv_len).  It
+     is packed with the planes' own scales (k_scale, v_scale; per kv head
+     with kv_scale_per_head) into that row of the K and V planes — the bytes
+     kvq_pack_*_batch writes with the amax those scales came from — and is
+     attended from its fresh codes: the splits cover [0, kv_lens[b] - 1) and
+     one more work-group per (request, kv head) writes the token's
+     contribution as partial number s, so splits_used reports s + 1
+     (s <= 63) and part_capacity must be at least s + 1.  The planes are
+     written although declared const. */
+  const void* new_k;
+  const void* new_v;
+  int32_t new_dtype;
 } kvq_decode_args;
 
 /*

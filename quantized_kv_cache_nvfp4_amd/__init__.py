@@ -216,7 +216,7 @@ def kvq_fp8p_scratch_floats(B: int, Hq: int, s: int, max_kv_len: int) -> int:
 
 def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_splits=0, part_o, part_lse,
                      q_rope=None, k_rope=None, quantize_p=False, prob_scale=1.0 / 448.0,
-                     p_scratch=None, block_table=None, q_scale=None) -> KvqDecodeArgs:
+                     p_scratch=None, block_table=None, q_scale=None, new_k=None, new_v=None) -> KvqDecodeArgs:
     """Fill the C decode-argument struct from tensors (no device work).
 
     GQA: q [B, Hq, D]; k, v NVFP4Plane / FP8Plane with codes [B, Hkv, Lmax, .],
@@ -227,6 +227,10 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
     v = None; q_rope [B, H, Dr] and k_rope [B, Lmax, Dr] bf16.
     FP8 query (GQA): q uint8 E4M3 codes [B, Hq, D] with q_scale, a device
     float tensor of 1 (per tensor) or Hq (per query head) entries.
+    Fused append (GQA): new_k, new_v [B, Hkv, D] (contiguous bf16 / f16 /
+    f32) are the step's new token, packed into row kv_lens[b] - 1 of the
+    planes by the decode itself and attended from its fresh codes; the
+    split launch then reports one more partial per head.
     """
     a = KvqDecodeArgs()
     mla = v is None
@@ -286,6 +290,14 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
             raise ValueError(f"per-head FP8 scales must have Hkv = {a.Hkv} entries for K and V")
         a.kv_scale_per_head = int(per_head)
     a.kv_lens = _ptr(kv_lens)
+    if (new_k is None) != (new_v is None):
+        raise ValueError("new_k and new_v go together")
+    if new_k is not None:
+        Hkv = a.Hkv
+        for t in (new_k, new_v):
+            if tuple(t.shape) != (B, Hkv, D) or not t.is_contiguous() or t.dtype != new_k.dtype:
+                raise ValueError(f"new_k / new_v must be contiguous [{B}, {Hkv}, {D}] tensors of one dtype")
+        a.new_k, a.new_v, a.new_dtype = _ptr(new_k), _ptr(new_v), _DT[new_k.dtype]
     a.softmax_scale = float(softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(D))
     a.num_splits = int(num_splits)
     a.quantize_p, a.prob_scale = int(bool(quantize_p)), float(prob_scale)
@@ -295,7 +307,7 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
     # the struct holds raw device pointers: keep the tensors they point into
     # alive for as long as the struct is (a plane built inline for the call
     # would otherwise be freed, and its memory may be returned to the driver)
-    a._keep = (q, k, v, kv_lens, q_rope, k_rope, part_o, part_lse, p_scratch, block_table, q_scale)
+    a._keep = (q, k, v, kv_lens, q_rope, k_rope, part_o, part_lse, p_scratch, block_table, q_scale, new_k, new_v)
     return a
 
 

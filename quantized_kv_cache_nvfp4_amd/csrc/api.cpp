@@ -323,13 +323,32 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
     if (rc != KVQ_OK) return rc;
   }
   if (s > 64) return fail(KVQ_ERR_ARG, "num_splits %d exceeds 64", s);
+  // fused append of the new token: one more partial per head
+  const bool append = a->new_k != nullptr || a->new_v != nullptr;
+  if (append) {
+    if (a->new_k == nullptr || a->new_v == nullptr) return fail(KVQ_ERR_ARG, "new_k and new_v must both be given");
+    if (a->layout != KVQ_LAYOUT_GQA) return fail(KVQ_ERR_UNSUPPORTED, "the fused append is implemented for the GQA layout only");
+    if (a->quantize_p) return fail(KVQ_ERR_UNSUPPORTED, "the fused append decodes with exact probabilities only");
+    if (a->q_dtype != KVQ_BF16) return fail(KVQ_ERR_UNSUPPORTED, "the fused append is implemented for bf16 queries");
+    if (a->new_dtype != KVQ_BF16 && a->new_dtype != KVQ_F16 && a->new_dtype != KVQ_F32)
+      return fail(KVQ_ERR_UNSUPPORTED, "new_dtype must be BF16, F16 or F32");
+    if (!aligned(a->new_k, a->new_dtype == KVQ_F32 ? 4 : 2) || !aligned(a->new_v, a->new_dtype == KVQ_F32 ? 4 : 2))
+      return fail(KVQ_ERR_ALIGN, "new_k / new_v misaligned");
+    if (a->D > 128) return fail(KVQ_ERR_UNSUPPORTED, "the fused append supports D <= 128");
+    if (s == 64) {
+      if (a->num_splits > 0) return fail(KVQ_ERR_ARG, "with a fused append num_splits must be <= 63");
+      s = 63;
+    }
+    if (a->B + (a->B + s - 1) / s > 65535) return fail(KVQ_ERR_ARG, "B too large for the fused append's grid");
+  }
+  const int np = s + (append ? 1 : 0);   // partials per head
   // the FP8-probability passes always go through the partials
-  const bool need_partials = a->quantize_p || !(fused && s == 1);
+  const bool need_partials = a->quantize_p || !(fused && np == 1);
   if (need_partials) {
     if (a->part_o == nullptr || a->part_lse == nullptr) return fail(KVQ_ERR_ARG, "part_o and part_lse must be non-null");
     if (!aligned(a->part_o, 4) || !aligned(a->part_lse, 4)) return fail(KVQ_ERR_ALIGN, "partials must be 4-byte aligned");
-    if (s > a->part_capacity)
-      return fail(KVQ_ERR_WORKSPACE, "num_splits %d exceeds part_capacity %d", s, a->part_capacity);
+    if (np > a->part_capacity)
+      return fail(KVQ_ERR_WORKSPACE, "%d partials per head exceed part_capacity %d", np, a->part_capacity);
   }
   if (a->quantize_p) {
     if (a->layout != KVQ_LAYOUT_GQA) return fail(KVQ_ERR_UNSUPPORTED, "quantize_p is implemented for the GQA layout only");
@@ -411,7 +430,7 @@ int attn_decode_splitkv(const kvq_decode_args* a, int32_t* splits_used, void* st
   int32_t s = 0;
   int rc = validate_decode(a, &s, false);
   if (rc != KVQ_OK) return rc;
-  if (splits_used) *splits_used = s;
+  if (splits_used) *splits_used = s + (a->new_k != nullptr ? 1 : 0);   // partials written per head
   kvq::DecodePlan plan{s, 0};
   if (a->layout == KVQ_LAYOUT_MLA)
     return hip_status(kvq::launch_decode_mla(*a, plan, as_stream(stream)), "attn_decode_splitkv launch");
@@ -438,8 +457,9 @@ int attn_decode(const kvq_decode_args* a, void* out, int32_t out_dtype, const fl
                               as_stream(stream));
     return hip_status(e, "attn_decode launch");
   }
-  if (s > 1 && counters == nullptr) return fail(KVQ_ERR_ARG, "counters must be non-null when num_splits > 1");
-  if (splits_used) *splits_used = s;
+  const int np = s + (a->new_k != nullptr ? 1 : 0);
+  if (np > 1 && counters == nullptr) return fail(KVQ_ERR_ARG, "counters must be non-null when more than one partial is merged");
+  if (splits_used) *splits_used = np;
   kvq::DecodePlan plan{s, 0};
   return hip_status(kvq::launch_decode_gqa_fused(*a, plan, out, out_dtype, out_scale, lse_out, counters,
                                                  as_stream(stream)),

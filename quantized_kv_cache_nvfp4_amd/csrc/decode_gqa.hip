@@ -62,6 +62,7 @@
 #include "combine_impl.h"
 #include "decode_common.h"
 #include "kvq_internal.h"
+#include "pack_codec.h"
 #include "wave_reduce.h"
 
 namespace kvq {
@@ -190,6 +191,162 @@ constexpr int decode_min_blocks() {
   return 8 / kWaves;
 }
 
+// element i of a new K / V row ([B][Hkv][D], dt BF16 / F16 / F32)
+__device__ inline float load_new(const void* p, int dt, int64_t i) {
+  if (dt == KVQ_F32) return static_cast<const float*>(p)[i];
+  const uint16_t u = static_cast<const uint16_t*>(p)[i];
+  if (dt == KVQ_BF16) return __uint_as_float(static_cast<uint32_t>(u) << 16);
+  return static_cast<float>(__builtin_bit_cast(_Float16, u));
+}
+
+// Quantize-on-append, run by the extra work-group (split index num_splits)
+// of a (request, kv head): packs the new token's K and V rows with the
+// planes' own scales into row pos = min(kv_lens[b], max_kv_len) - 1 of the
+// planes (the bytes the pack kernels write: same encoders), then writes the
+// token's contribution as partial s_idx of each of the G heads: with one
+// token the softmax weight is 1, so the partial output is the dequantized V
+// row and its log-sum-exp the token's score.  The other work-groups stream
+// [0, pos) and never read row pos, so nothing in this launch waits for the
+// write.  (TOKEN4 V: the token's nibbles / bytes of its 4-token group are
+// replaced, the other tokens' kept.)
+template <int KVF, int G, int D, int QT, int VL, bool PAGED, bool FUSED>
+__device__ void append_token(const kvq_decode_args& a, int b, int kvh, int np, int s_idx, float (*lds_new)[128]) {
+  using Gm = Geo<KVF, D>;
+  constexpr int RB = Gm::kRowBytes;
+  constexpr int SB = Gm::kScaleBytes;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int Lr = a.kv_lens[b];
+  Lr = Lr < a.max_kv_len ? Lr : a.max_kv_len;
+  const int pos = (Lr > 0 ? Lr : 0) - 1;   // the new token (none below 0)
+  const int sh = a.kv_scale_per_head ? kvh : 0;
+  const float kscale = a.k_scale[sh];
+  const float vscale = a.v_scale[sh];
+  // the query elements this lane needs for the scores, requested up front
+  constexpr int kHw = (G + kWaves - 1) / kWaves;   // heads per wave
+  constexpr int kDl = (D + 63) / 64;              // elements per lane and head
+  float qv[kHw][kDl];
+#pragma unroll
+  for (int k = 0; k < kHw; ++k) {
+    const int h = wave + k * kWaves;
+    const int64_t qb = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(kvh * G + (h < G ? h : 0)) * a.q_sh;
+#pragma unroll
+    for (int e = 0; e < kDl; ++e) {
+      const int d = lane + 64 * e;
+      float x = 0.0f;
+      if (h < G && d < D) {
+        if constexpr (QT == kQF32) x = static_cast<const float*>(a.q)[qb + d];
+        else if constexpr (QT == kQFp8) x = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(static_cast<const uint8_t*>(a.q)[qb + d]), 0);
+        else x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(a.q)[qb + d]) << 16);
+      }
+      qv[k][e] = x;
+    }
+  }
+  if (pos >= 0 && t < 128) {
+    int64_t base;   // plane row of token 0 of pos's block (paged) or of the request
+    int tin;        // pos inside it
+    if constexpr (PAGED) {
+      const int bsh = __builtin_ctz(static_cast<unsigned>(a.block_size));
+      const int blk = a.block_table[static_cast<int64_t>(b) * a.bt_stride + (pos >> bsh)];
+      base = static_cast<int64_t>(blk) * a.kv_sblk + static_cast<int64_t>(kvh) * a.kv_sh;
+      tin = pos & (a.block_size - 1);
+    } else {
+      base = static_cast<int64_t>(b) * a.kv_sb + static_cast<int64_t>(kvh) * a.kv_sh;
+      tin = pos;
+    }
+    const int64_t st = (VL == KVQ_PLANE_TOKEN4) ? 1 : a.kv_st;
+    const int64_t row = base + tin * st;       // K row, V row (row layout)
+    const int64_t grow = base + (tin & ~3);    // first row of the TOKEN4 group
+    const int j = tin & 3;                     // the token's slot in the group
+    const bool isv = t >= 64;                  // wave 0: K, wave 1: V
+    const bool t4 = isv && VL == KVQ_PLANE_TOKEN4;
+    const void* src = isv ? a.new_v : a.new_k;
+    const int64_t off = (static_cast<int64_t>(b) * a.Hkv + kvh) * D;
+    uint8_t* codes = const_cast<uint8_t*>(isv ? a.v_codes : a.k_codes);
+    const float scl = isv ? vscale : kscale;   // s_t (NVFP4) or the FP8 scale
+    if constexpr (KVF == KVQ_NVFP4) {
+      uint8_t* scales = const_cast<uint8_t*>(isv ? a.v_scales : a.k_scales);
+      if (lane < D / 16) {   // block `lane` of the row
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = load_new(src, a.new_dtype, off + 16 * lane + i);
+        uint32_t c[16];
+        const uint32_t sc = codec::encode_nvfp4_block(v, scl, c);
+        const float sv = static_cast<float>(codec::e4m3_value(sc));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lds_new[isv][16 * lane + i] = codec::e2m1_value(c[i]) * sv;   // exact
+        if (!t4) {
+          uint32_t lo = 0, hi = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            lo |= c[i] << (4 * i);
+            hi |= c[8 + i] << (4 * i);
+          }
+          *reinterpret_cast<uint2*>(codes + row * RB + 8 * lane) = make_uint2(lo, hi);
+          scales[row * SB + lane] = static_cast<uint8_t>(sc);
+        } else {
+          // element x of token j: nibble (j & 1) of byte 2x + (j >> 1) of the
+          // group, so block `lane` lives in the group's bytes [32 lane, 32 lane
+          // + 32): one read of that span, the token's 16 nibbles replaced in
+          // registers, one write (the other tokens' nibbles written back as read)
+          uint4* span = reinterpret_cast<uint4*>(codes + grow * RB + 32 * lane);
+          uint4 w0 = span[0], w1 = span[1];
+          uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+          const int sh = 4 * (j & 1) + 8 * (j >> 1);   // bit offset of the token's nibble in a 2-byte pair
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {   // element 16 lane + i: byte pair i of the span
+            const int bit = 16 * (i & 1) + sh;
+            wd[i >> 1] = (wd[i >> 1] & ~(0xFu << bit)) | (c[i] << bit);
+          }
+          span[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+          span[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+          scales[grow * SB + 4 * lane + j] = static_cast<uint8_t>(sc);   // block `lane` of token j
+        }
+      }
+    } else {
+      const double dscale = static_cast<double>(scl);
+      const float inv = 1.0f / scl;
+      for (int x = lane; x < D; x += 64) {
+        const uint32_t cde = codec::encode_fp8(load_new(src, a.new_dtype, off + x), inv, dscale);
+        lds_new[isv][x] = static_cast<float>(codec::e4m3_value(cde));
+        if (!t4) codes[row * RB + x] = static_cast<uint8_t>(cde);
+        else codes[grow * RB + 4 * x + j] = static_cast<uint8_t>(cde);   // element x of token j
+      }
+    }
+  }
+  __syncthreads();
+  // the token's score per head (fp32) and the partial
+#pragma unroll
+  for (int k = 0; k < kHw; ++k) {
+    const int h = wave + k * kWaves;
+    if (h >= G) break;
+    const int hq = kvh * G + h;
+    const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq;
+    float lse = -INFINITY;
+    if (pos >= 0) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kDl; ++e) {
+        const int d = lane + 64 * e;
+        if (d < D) dot += qv[k][e] * lds_new[0][d];
+      }
+      dot = lanes::wave_all<lanes::Sum>(dot);
+      float qk_scale = a.softmax_scale * kscale * kLog2e;
+      if constexpr (QT == kQFp8) qk_scale *= a.q_scale[a.q_scale_per_head ? hq : 0];
+      lse = dot * qk_scale * kLn2;
+    }
+    const int64_t po = bh * np + s_idx;
+    for (int d = lane; d < D; d += 64) {
+      const float o = pos >= 0 ? lds_new[1][d] * vscale : 0.0f;
+      if constexpr (FUSED) __hip_atomic_store(a.part_o + po * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else a.part_o[po * D + d] = o;
+    }
+    if (lane == 0) {
+      if constexpr (FUSED) __hip_atomic_store(a.part_lse + po, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else a.part_lse[po] = lse;
+    }
+  }
+}
+
 // Block-table entries a work-group of a paged cache keeps in LDS (the
 // blocks its chunk touches).
 constexpr int kMaxChunkBlocks = kPagedMaxChunkBlocks;
@@ -197,8 +354,9 @@ constexpr int kMaxChunkBlocks = kPagedMaxChunkBlocks;
 // PM: 0 attention, 1 FP8-P pass 1 (scores), 2 FP8-P pass 2 (quantized P . V).
 // PAGED: the planes are paged (block table; block size a multiple of the
 // tile, so every tile lies in one block).
-template <int KVF, int G, int D, int QT, int PSPLIT, bool FUSED, int VL, int PM, bool PAGED>
+template <int KVF, int G, int D, int QT, int PSPLIT, bool FUSED, int VL, int PM, bool PAGED, bool APP>
 __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>())) k_decode_gqa(kvq_decode_args a, int num_splits, FusedOut fo) {
+  static_assert(!APP || (PM == 0 && QT == kQBf16), "the fused append: exact probabilities, bf16 queries");
   constexpr bool QF32 = QT == kQF32;
   constexpr bool q8 = QT == kQFp8;   // FP8 query codes: 8 bytes per query word instead of 16
   static_assert(PM == 0 || (!FUSED && PSPLIT == 1), "the FP8-P passes write partials only");
@@ -230,6 +388,49 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
   const int hq0 = kvh * G;
   const int my_h = c % G;
   const int my_sub = c / G;
+  // fused append of the new token: one more work-group per (request, kv
+  // head) writes it and its partial (index num_splits).  Those work-groups
+  // form extra z planes after the B request planes (request (z - B) *
+  // num_splits + x), so that they are dispatched after the streaming
+  // work-groups and share a compute unit with one only briefly.
+  constexpr bool app = APP;
+  const int np = num_splits + (app ? 1 : 0);   // partials per head
+
+  // ---------------- fused combine: the last work-group of (b, kv head) to
+  // finish merges the np partials of its G heads.  The partials were stored
+  // at device scope; waiting for those stores to complete before the
+  // counter increment orders them before it (no cache write-back fence is
+  // needed), and the last work-group reads them at device scope.
+  auto fused_tail = [&](int b) {
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int* ctr = fo.counters + static_cast<int64_t>(b) * a.Hkv + kvh;
+      const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = (prev == np - 1);
+      if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
+      lds_last = last;
+    }
+    __syncthreads();
+    if (!lds_last) return;
+    const float osc = (fo.out_dtype == KVQ_FP8E4M3) ? *fo.out_scale : 1.0f;
+    // one head per wave (the routine of the standalone combine kernel)
+    for (int h = wave; h < G; h += kWaves) {
+      const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + h;
+      combine_head<true>(a.part_lse + bh * np, a.part_o + bh * np * D, np, D, 0, D, fo.out, fo.out_dtype, bh * D,
+                         osc, fo.lse_out != nullptr ? fo.lse_out + bh : nullptr);
+    }
+  };
+  if constexpr (APP) {
+    if (b >= a.B) {
+      const int ba = (b - a.B) * num_splits + split;   // the request of this append work-group
+      if (ba >= a.B) return;
+      __shared__ float lds_new[2][128];
+      append_token<KVF, G, D, QT, VL, PAGED, FUSED>(a, ba, kvh, np, num_splits, lds_new);
+      if constexpr (FUSED) fused_tail(ba);
+      return;
+    }
+  }
 
   // ---- chunking: c = ceil(max_kv_len / s) rounded up to the tile; split j
   // covers [j c, min((j+1) c, L)).  It depends on kernel arguments only, so
@@ -398,6 +599,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
   int L = PAGED ? len_pg : a.kv_lens[b];
   L = L < a.max_kv_len ? L : a.max_kv_len;
   L = L > 0 ? L : 0;
+  if constexpr (APP) L = L > 0 ? L - 1 : 0;   // the new token is the append work-group's
   const int ce = (cs + chunk < L) ? cs + chunk : L;
   ce_ld = ce;   // every later load stops at the request's end
   if constexpr (PAGED) {
@@ -996,7 +1198,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
     }
     return;
   }
-  const bool direct = FUSED && num_splits == 1;   // no partials needed
+  const bool direct = FUSED && np == 1;   // no partials needed
   // items (head h, 64-column block kb) spread over the waves; columns
   // d = 64 kb + lane; the LDS reads do not wait for the weights
   constexpr int kBlk = (D + 63) / 64;
@@ -1039,7 +1241,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
         store_out(fo.out, fo.out_dtype, bh * D + d, o, fo.out_dtype == KVQ_FP8E4M3 ? *fo.out_scale : 1.0f);
         if (d == 0 && fo.lse_out != nullptr) fo.lse_out[bh] = lse;
       } else {
-        const int64_t po = bh * num_splits + split;
+        const int64_t po = bh * np + split;
         if constexpr (FUSED) {   // device-scope stores: read back by another work-group
           __hip_atomic_store(a.part_o + po * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (d == 0) __hip_atomic_store(a.part_lse + po, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1052,54 +1254,40 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
   }
   if constexpr (!FUSED) return;
   if (direct) return;
-
-  // ---------------- fused combine: the last work-group of (b, kv head) to
-  // finish merges the num_splits partials of its G heads.  The partials
-  // were stored at device scope; waiting for those stores to complete
-  // before the counter increment orders them before it (no cache
-  // write-back fence is needed), and the last work-group reads them at
-  // device scope.
-  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int* ctr = fo.counters + static_cast<int64_t>(b) * a.Hkv + kvh;
-    const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = (prev == num_splits - 1);
-    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
-    lds_last = last;
-  }
-  __syncthreads();
-  if (!lds_last) return;
-  const float osc = (fo.out_dtype == KVQ_FP8E4M3) ? *fo.out_scale : 1.0f;
-  // one head per wave (the routine of the standalone combine kernel)
-  for (int h = wave; h < G; h += kWaves) {
-    const int64_t bh = static_cast<int64_t>(b) * a.Hq + hq0 + h;
-    combine_head<true>(a.part_lse + bh * num_splits, a.part_o + bh * num_splits * D, num_splits, D, 0, D, fo.out,
-                       fo.out_dtype, bh * D, osc, fo.lse_out != nullptr ? fo.lse_out + bh : nullptr);
-  }
+  fused_tail(b);
 }
 
-template <int KVF, int G, int D, int QT, int PSPLIT, int VL, int PM, bool PAGED>
+template <int KVF, int G, int D, int QT, int PSPLIT, int VL, int PM, bool PAGED, bool APP>
 hipError_t launch_p(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
-  dim3 grid(p.s, a.Hkv, a.B);
+  // (a fused append adds ceil(B / s) z planes: one work-group per (request, kv head))
+  const int zapp = APP ? (a.B + p.s - 1) / p.s : 0;
+  dim3 grid(p.s, a.Hkv, a.B + zapp);
   if constexpr (PM == 0) {
     if (fo != nullptr) {
-      hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QT, PSPLIT, true, VL, 0, PAGED>), grid, dim3(kThreads), 0, st, a,
-                         p.s, *fo);
+      hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QT, PSPLIT, true, VL, 0, PAGED, APP>), grid, dim3(kThreads), 0, st,
+                         a, p.s, *fo);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QT, PSPLIT, false, VL, PM, PAGED>), grid, dim3(kThreads), 0, st, a,
+  hipLaunchKernelGGL((k_decode_gqa<KVF, G, D, QT, PSPLIT, false, VL, PM, PAGED, APP>), grid, dim3(kThreads), 0, st, a,
                      p.s, FusedOut{});
   return hipGetLastError();
+}
+
+template <int KVF, int G, int D, int QT, int PSPLIT, int VL, int PM, bool PAGED>
+hipError_t launch_a(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
+  if constexpr (PM == 0 && QT == kQBf16) {
+    if (a.new_k != nullptr) return launch_p<KVF, G, D, QT, PSPLIT, VL, 0, PAGED, true>(a, p, fo, st);
+  }
+  return launch_p<KVF, G, D, QT, PSPLIT, VL, PM, PAGED, false>(a, p, fo, st);
 }
 
 template <int KVF, int G, int D, int QT, int PSPLIT, int VL, int PM>
 hipError_t launch_v(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
   if constexpr (PM == 0) {
-    if (a.block_table != nullptr) return launch_p<KVF, G, D, QT, PSPLIT, VL, 0, true>(a, p, fo, st);
+    if (a.block_table != nullptr) return launch_a<KVF, G, D, QT, PSPLIT, VL, 0, true>(a, p, fo, st);
   }
-  return launch_p<KVF, G, D, QT, PSPLIT, VL, PM, false>(a, p, fo, st);
+  return launch_a<KVF, G, D, QT, PSPLIT, VL, PM, false>(a, p, fo, st);
 }
 
 template <int KVF, int G, int D, int QT, int PSPLIT, int PM>

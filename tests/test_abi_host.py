@@ -327,3 +327,30 @@ def test_fp8_query_validation(L, K):
     assert _decode_rc(L, a) == 2
     a = _good_args(K); a.q_dtype = K.KVQ_F16
     assert _decode_rc(L, a) == 2
+
+
+def test_fused_append_validation(L, K):
+    """Fused append: both rows, GQA layout, exact probabilities, a known row
+    dtype, one more partial per head than splits (at most 64)."""
+    def app():
+        a = _good_args(K)
+        a.new_k = a.new_v = FAKE
+        a.new_dtype = K.KVQ_BF16
+        a.num_splits, a.part_capacity = 3, 4
+        return a
+    a = app(); a.new_v = None
+    assert _decode_rc(L, a) == 1
+    a = app(); a.new_dtype = K.KVQ_FP8E4M3
+    assert _decode_rc(L, a) == 2
+    a = app(); a.num_splits = 4
+    assert _decode_rc(L, a) == 4                     # 5 partials, capacity 4
+    a = app(); a.num_splits, a.part_capacity = 64, 100
+    assert _decode_rc(L, a) == 1
+    a = app(); a.quantize_p, a.prob_scale, a.p_scratch = 1, 1.0 / 448.0, FAKE
+    assert _decode_rc(L, a) == 2
+    a = app(); a.new_k = FAKE_ODD
+    assert _decode_rc(L, a) == 3
+    a = app(); a.layout = K.KVQ_LAYOUT_MLA; a.Hkv = 1; a.Hq = 16
+    assert _decode_rc(L, a) == 2
+    a = app(); a.q_dtype = K.KVQ_F32
+    assert _decode_rc(L, a) == 2                     # bf16 queries only
