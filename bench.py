@@ -299,12 +299,45 @@ def run_mla(args):
         used = K.attn_decode_splitkv(dargs[i])
         K.attn_decode_combine(part_o, part_lse, MLA_B, MLA_H, MLA_DC, used, out)
 
+    # the same latent caches paged: blocks of 64 tokens at permuted physical
+    # blocks (one table per copy; latent codes, scales and rope share it)
+    PB = 64
+    nb = MLA_L // PB
+    rng = torch.Generator().manual_seed(5)
+
+    def pg(t, perm):
+        out_ = torch.empty_like(t).view(MLA_B * nb, PB, t.shape[-1])
+        out_[perm] = t.view(MLA_B * nb, PB, t.shape[-1])
+        return out_
+
+    pdargs = []   # (decode args, tensors it points into)
+    for pl, kr in copies:
+        perm = torch.randperm(MLA_B * nb, generator=rng).to(dev)
+        bt = perm.view(MLA_B, nb).to(torch.int32).contiguous()
+        ppl = K.NVFP4Plane(pg(pl.codes, perm), pg(pl.scales, perm), pl.tensor_scale, pl.layout)
+        pkr = pg(kr, perm)
+        pdargs.append((K.make_decode_args(q_c, ppl, None, lens, max_kv_len=MLA_L, softmax_scale=inp.softmax_scale,
+                                          num_splits=s, part_o=part_o, part_lse=part_lse, q_rope=q_r, k_rope=pkr,
+                                          block_table=bt), ppl, pkr, bt))
+    torch.cuda.synchronize()
+
+    def paged_step(i):
+        used = K.attn_decode_splitkv(pdargs[i][0])
+        K.attn_decode_combine(part_o, part_lse, MLA_B, MLA_H, MLA_DC, used, out)
+
+    for i in range(max(args.warmup, n_copies)):
+        paged_step(i % n_copies)
+    torch.cuda.synchronize()
+    out_paged = out.clone()
     for i in range(max(args.warmup, n_copies)):
         step(i % n_copies)
     torch.cuda.synchronize()
+    assert torch.equal(out, out_paged), "paged and contiguous MLA decode differ"
     capture, timed, steps = graph_timer(torch, n_copies, args.steps)
     ms_step = timed(capture(step))
     ms_split = timed(capture(lambda i: K.attn_decode_splitkv(dargs[i])))
+    ms_step_pg = timed(capture(paged_step))
+    ms_split_pg = timed(capture(lambda i: K.attn_decode_splitkv(pdargs[i][0])))
     assert torch.isfinite(out.float()).all()
     algo = MLA_B * MLA_L * MLA_BYTES_PER_TOKEN
     kernel_us = ms_split * 1e3
@@ -318,7 +351,9 @@ def run_mla(args):
                    "latent": MLA_DC, "rope": MLA_DR, "kv_len": MLA_L, "splits": s, "out_dtype": "bf16",
                    "rotation_copies": n_copies},
         "hbm_gbps_step": round(algo / (ms_step * 1e-3) / 1e9, 1),
-        "step_us": {"decode_two_launch": round(ms_step * 1e3, 3), "split_kernel": round(kernel_us, 3)},
+        "step_us": {"decode_two_launch": round(ms_step * 1e3, 3), "split_kernel": round(kernel_us, 3),
+                    "decode_two_launch_paged64": round(ms_step_pg * 1e3, 3),
+                    "split_kernel_paged64": round(ms_split_pg * 1e3, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("mla"),
                      "kernel": "k_decode_mla (split kernel, partials)", "kernel_us_mean": round(kernel_us, 3),

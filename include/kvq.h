@@ -286,18 +286,25 @@ typedef struct {
                                device float[Hkv], kv head h dequantized with
                                its own scale (kvq_pack_fp8_heads); 0 = one
                                per-tensor scale each */
-  /* Paged cache (GQA layout, exact probabilities; vLLM's block tables, the
-     serving setting of Model-Optimizer PR #1832 "Purpose" and "Testing").
+  /* Paged cache (GQA and MLA layouts, exact probabilities; vLLM's block
+     tables, the serving setting of Model-Optimizer PR #1832 "Purpose" and
+     "Testing").
      NULL block_table: the planes are addressed by kv_sb / kv_sh / kv_st as
      above.  Otherwise token t of request b, kv head h is plane row
        block_table[b * bt_stride + t / block_size] * kv_sblk
          + h * kv_sh + (t % block_size) * kv_st
      (kv_sb unused; for planes [num_blocks][Hkv][block_size][row]:
-     kv_sblk = Hkv * block_size, kv_sh = block_size, kv_st = 1).  Entries
-     are read for t < max_kv_len; only those of tokens t < kv_lens[b] are
-     used as block indices (they must be valid there).
-     block_size: a power of two and a multiple of the decode tile
-     (attn_decode_tile_tokens). */
+     kv_sblk = Hkv * block_size, kv_sh = block_size, kv_st = 1).
+     GQA: entries are read for t < max_kv_len; only those of tokens
+     t < kv_lens[b] are used as block indices (they must be valid there);
+     block_size is a power of two and a multiple of the decode tile
+     (attn_decode_tile_tokens).
+     MLA (latent, scale and rope planes [num_blocks][block_size][row], one
+     table for all three; h = 0): only entries of tokens t < kv_lens[b] are
+     read; block_size is a power of two and a multiple of 64 (the MLA
+     kernel's tile), and one split may span at most 510 blocks.
+     Errors: KVQ_ERR_ARG for a block size, bt_stride or kv_sblk out of
+     these bounds; KVQ_ERR_UNSUPPORTED with quantize_p (GQA). */
   const int32_t* block_table;
   int32_t block_size;
   int64_t bt_stride;

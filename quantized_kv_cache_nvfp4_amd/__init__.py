@@ -224,7 +224,8 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
     [num_blocks, Hkv, block_size, .] (token t of request b in block
     block_table[b, t // block_size]).
     MLA: q = q_c [B, H, Dc]; k = NVFP4Plane of the latent [B, Lmax, .];
-    v = None; q_rope [B, H, Dr] and k_rope [B, Lmax, Dr] bf16.
+    v = None; q_rope [B, H, Dr] and k_rope [B, Lmax, Dr] bf16; with
+    block_table, the latent and rope planes are [num_blocks, block_size, .].
     FP8 query (GQA): q uint8 E4M3 codes [B, Hq, D] with q_scale, a device
     float tensor of 1 (per tensor) or Hq (per query head) entries.
     Fused append (GQA): new_k, new_v [B, Hkv, D] (contiguous bf16 / f16 /
@@ -247,6 +248,11 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
             rr = _rows(k_rope, k_rope.shape[-1])
             if (rr.s1, rr.s2) != (kr.s1, kr.s2):
                 raise ValueError("k_rope must share the latent plane's row layout")
+        if block_table is not None:   # paged latent planes [num_blocks, block_size, .]
+            if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+                raise ValueError("block_table must be an int32 [B, max_blocks] tensor with contiguous rows")
+            a.block_table, a.block_size = _ptr(block_table), int(k.codes.shape[1])
+            a.bt_stride, a.kv_sblk, a.kv_sb = block_table.stride(0), kr.s1, 0
         a.q_rope, a.k_rope = _ptr(q_rope), _ptr(k_rope)
         if q_rope is not None:
             a.qr_sb, a.qr_sh = q_rope.stride(0), q_rope.stride(1)

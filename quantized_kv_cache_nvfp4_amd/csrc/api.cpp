@@ -392,8 +392,22 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
                     kvq::kPagedMaxChunkBlocks - 2);
     }
   } else {
-    if (a->block_table != nullptr) return fail(KVQ_ERR_UNSUPPORTED, "paged caches are decoded for the GQA layout only");
     if (a->kv_format != KVQ_NVFP4) return fail(KVQ_ERR_UNSUPPORTED, "MLA layout supports NVFP4 only");
+    if (a->block_table != nullptr) {   // paged latent cache
+      const int tile = kvq::mla_tile_tokens();
+      if (a->block_size <= 0 || a->block_size % tile != 0 || (a->block_size & (a->block_size - 1)) != 0)
+        return fail(KVQ_ERR_ARG, "block_size must be a power of two and a multiple of the MLA decode tile (%d tokens)",
+                    tile);
+      const int64_t need = (static_cast<int64_t>(a->max_kv_len) + a->block_size - 1) / a->block_size;
+      if (a->bt_stride < need) return fail(KVQ_ERR_ARG, "bt_stride must cover ceil(max_kv_len / block_size) blocks");
+      if (a->kv_sblk < 0) return fail(KVQ_ERR_ARG, "kv_sblk must be >= 0");
+      if (!aligned(a->block_table, 4)) return fail(KVQ_ERR_ALIGN, "block_table must be 4-byte aligned");
+      int64_t chunk = (static_cast<int64_t>(a->max_kv_len) + s - 1) / s;
+      chunk = (chunk + tile - 1) / tile * tile;
+      if (chunk / a->block_size + 2 > kvq::kMlaPagedMaxChunkBlocks)
+        return fail(KVQ_ERR_ARG, "a split spans more than %d blocks: use more splits or larger blocks",
+                    kvq::kMlaPagedMaxChunkBlocks - 2);
+    }
     if (a->Hkv != 1) return fail(KVQ_ERR_ARG, "MLA layout needs Hkv == 1");
     if (a->k_scales == nullptr || a->q_rope == nullptr || a->k_rope == nullptr)
       return fail(KVQ_ERR_ARG, "MLA needs k_scales, q_rope and k_rope");

@@ -30,6 +30,11 @@
 //    so the four waves share one reference maximum and one denominator.
 //  * loads use buffer resources sized to the chunk (tokens past its end read
 //    zeros), as in the GQA kernel.
+//  * paged caches (vLLM-style block tables): the block size is a power of
+//    two and a multiple of the tile, so every 64-token tile lies in one
+//    block; a work-group copies its chunk's table entries into LDS once and
+//    addresses each tile through them (the first tile through an entry read
+//    directly, so that its loads need not wait for the copy).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -69,9 +74,11 @@ __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+template <bool PAGED>
 __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, int num_splits) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_c[kT * kPitch];   // staged latent rows (f16)
   __shared__ __attribute__((aligned(16))) f32x4 lds_s[kW][kQ][64];      // partial scores per wave, sub-tile, lane
+  __shared__ int lds_bt[PAGED ? kMlaPagedMaxChunkBlocks : 1];          // paged: the chunk's block-table entries
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -95,12 +102,47 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
   const int cs = split * chunk;
   int ce_ld = (cs + chunk < a.max_kv_len) ? cs + chunk : a.max_kv_len;   // load bound (rows present)
 
-  // per-request plane bases (rows of the latent, scale and rope planes)
-  const int64_t row0 = static_cast<int64_t>(b) * a.kv_sb;
+  // per-request plane bases (rows of the latent, scale and rope planes);
+  // paged planes are addressed from the plane start through the table
+  const int64_t row0 = PAGED ? 0 : static_cast<int64_t>(b) * a.kv_sb;
   const int st = static_cast<int>(a.kv_st);
   const uint8_t* cc = a.k_codes + row0 * kRow;
   const uint8_t* csc = a.k_scales + row0 * kSRow;
   const uint8_t* cr = static_cast<const uint8_t*>(a.k_rope) + row0 * (kDr * 2);
+
+  // paged: block tb >> bsh holds token tb at row tb & (bs - 1); entries are
+  // kept for the blocks of rows [cs, ce) only, so the request length is
+  // read before the first loads (an entry past the request's end need not
+  // be a valid block)
+  const int bs = PAGED ? a.block_size : 1;
+  const int bsh = PAGED ? __builtin_ctz(static_cast<unsigned>(bs)) : 0;
+  const int blk0 = cs >> bsh;
+  int L = 0, ce = 0;
+  int64_t first_row = 0;   // paged: plane row of the chunk's first token
+  if constexpr (PAGED) {
+    L = a.kv_lens[b];
+    L = L < a.max_kv_len ? L : a.max_kv_len;
+    L = L > 0 ? L : 0;
+    ce = (cs + chunk < L) ? cs + chunk : L;
+    ce_ld = ce;
+    const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride + blk0;
+    if (cs < ce) first_row = static_cast<int64_t>(bt[0]) * a.kv_sblk + static_cast<int64_t>(cs & (bs - 1)) * st;
+    const int nblk = ce > cs ? ((ce - 1) >> bsh) - blk0 + 1 : 0;
+    for (int i = threadIdx.x; i < nblk; i += kThreads) lds_bt[i] = bt[i];
+  }
+  // plane row of tile's first token (relative to the request's base when
+  // the cache is contiguous); tiles past the chunk's end get 0 (they load
+  // nothing).  Paged tiles after the first read the LDS copy of the table.
+  auto tile_row = [&](int tile) -> int64_t {
+    const int tb = cs + tile * kT;
+    if constexpr (PAGED) {
+      if (tile == 0) return first_row;
+      if (tb >= ce_ld) return 0;
+      return static_cast<int64_t>(lds_bt[(tb >> bsh) - blk0]) * a.kv_sblk + static_cast<int64_t>(tb & (bs - 1)) * st;
+    } else {
+      return static_cast<int64_t>(tb) * st;
+    }
+  };
 
   // loads of one tile: for each of the wave's sub-tiles u = th + 2 q, token
   // 16 u + c; latent bytes [128 dh + 32 g, +32), scale bytes [16 dh + 4 g,
@@ -111,13 +153,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     uint32_t sw[kQ];
   };
   auto load_tile = [&](Raw& R, int tile) {
+    const int64_t trow = tile_row(tile);
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       const int t0 = cs + tile * kT + 16 * (th + 2 * q);
       const int nv = ce_ld - t0;
-      const Rsrc rc_ = make_rsrc(cc + static_cast<int64_t>(t0) * st * kRow, nv * st * kRow);
-      const Rsrc rs_ = make_rsrc(csc + static_cast<int64_t>(t0) * st * kSRow, nv * st * kSRow);
-      const Rsrc rr_ = make_rsrc(cr + static_cast<int64_t>(t0) * st * (kDr * 2), nv * st * (kDr * 2));
+      const int64_t r0 = trow + static_cast<int64_t>(16 * (th + 2 * q)) * st;
+      const Rsrc rc_ = make_rsrc(cc + r0 * kRow, nv * st * kRow);
+      const Rsrc rs_ = make_rsrc(csc + r0 * kSRow, nv * st * kSRow);
+      const Rsrc rr_ = make_rsrc(cr + r0 * (kDr * 2), nv * st * (kDr * 2));
       R.cw0[q] = ld128(rc_, c * st * kRow + 128 * dh + 32 * g);
       R.cw1[q] = ld128(rc_, c * st * kRow + 128 * dh + 32 * g + 16);
       R.sw[q] = ld32(rs_, c * st * kSRow + 16 * dh + 4 * g);
@@ -148,11 +192,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     __builtin_amdgcn_sched_barrier(0);   // issue order = tile order, so a wait for one tile spares the later ones
   }
 
-  int L = a.kv_lens[b];
-  L = L < a.max_kv_len ? L : a.max_kv_len;
-  L = L > 0 ? L : 0;
-  const int ce = (cs + chunk < L) ? cs + chunk : L;
-  ce_ld = ce;   // later loads stop at the request's end
+  if constexpr (PAGED) {
+    __syncthreads();   // the LDS table copy is visible to the later tiles' loads
+  } else {
+    L = a.kv_lens[b];
+    L = L < a.max_kv_len ? L : a.max_kv_len;
+    L = L > 0 ? L : 0;
+    ce = (cs + chunk < L) ? cs + chunk : L;
+    ce_ld = ce;   // later loads stop at the request's end
+  }
   const int ntiles = cs < ce ? (ce - cs + kT - 1) / kT : 0;
 
   const float s_t = *a.k_scale;
@@ -336,7 +384,10 @@ bool mla_supported(const kvq_decode_args& a) {
 }
 
 hipError_t launch_decode_mla(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
-  hipLaunchKernelGGL(k_decode_mla, dim3(p.s, a.B), dim3(kThreads), 0, st, a, p.s);
+  if (a.block_table != nullptr)
+    hipLaunchKernelGGL(k_decode_mla<true>, dim3(p.s, a.B), dim3(kThreads), 0, st, a, p.s);
+  else
+    hipLaunchKernelGGL(k_decode_mla<false>, dim3(p.s, a.B), dim3(kThreads), 0, st, a, p.s);
   return hipGetLastError();
 }
 

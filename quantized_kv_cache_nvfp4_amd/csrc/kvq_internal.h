@@ -67,6 +67,7 @@ hipError_t launch_combine(const float* part_o, const float* part_lse, int B, int
 int gqa_tile_tokens(int G);
 int mla_tile_tokens();
 constexpr int kPagedMaxChunkBlocks = 2048;   // block-table entries one work-group keeps (LDS)
+constexpr int kMlaPagedMaxChunkBlocks = 512;  // the same for the MLA kernel (two work-groups per CU share the LDS)
 // is (format, G, D, q dtype) implemented by the GQA kernel
 bool gqa_supported(int kv_format, int G, int D, int q_dtype);
 // is the MLA configuration implemented (NVFP4 latent 512 + rope 64, 16 heads, bf16 queries)

@@ -128,3 +128,113 @@ def test_mla_full_config_sampled():
         o, _ = OA.decode_mla(kvq_synth.f64(inp.q_c[b:b + 1]), kvq_synth.f64(inp.q_r[b:b + 1]), chat,
                              kvq_synth.f64(inp.k_r[b:b + 1]), inp.kv_lens[b:b + 1], inp.softmax_scale)
         assert_bf16_output(out[b:b + 1], o, f"mla full b={b}")
+
+
+# ------------------------------------------------------------ paged latent cache
+def _page_mla(t, lens, bs, perm_seed):
+    """Paged copy of a contiguous per-request plane t [B, Lp, .] (latent codes,
+    scales or rope): blocks of bs tokens at physical blocks given by a seeded
+    permutation of B * nb + 3 slots.  Blocks that lie wholly at or past a
+    request's length point at the spare slots, which (like every unused
+    slot) hold 0xFF bytes: NaN E4M3 scales and NaN bf16 rope values, so a
+    read through such an entry shows in the output.  Returns (paged plane
+    [nphys, bs, .], block table int32 [B, nb])."""
+    B, Lp = t.shape[:2]
+    nb = (Lp + bs - 1) // bs
+    nphys = B * nb + 3
+    perm = np.random.default_rng(perm_seed).permutation(nphys)
+    table = perm[: B * nb].reshape(B, nb).astype(np.int32)
+    spare = perm[B * nb:]
+    for b in range(B):
+        first_unused = (int(lens[b]) + bs - 1) // bs
+        table[b, first_unused:] = spare[np.arange(nb - first_unused) % len(spare)]
+    row_shape = tuple(t.shape[2:])
+    raw = t.contiguous().view(torch.uint8).reshape(B, Lp, -1)
+    out = torch.full((nphys, bs, raw.shape[-1]), 0xFF, dtype=torch.uint8, device=DEV)
+    for b in range(B):
+        for j in range((int(lens[b]) + bs - 1) // bs):
+            n = min(bs, Lp - j * bs)
+            out[int(table[b, j]), :n] = raw[b, j * bs: j * bs + n]
+    return out.view(t.dtype).reshape((nphys, bs) + row_shape), torch.from_numpy(table).to(DEV)
+
+
+def _gpu_paged(inp, plane, s, bs, out_dtype=torch.float32, fused=False, perm_seed=7):
+    k_ = K()
+    lens_np = inp.kv_lens
+    lens = torch.from_numpy(lens_np).to(DEV)
+    codes, bt = _page_mla(plane.codes, lens_np, bs, perm_seed)
+    scales, bt2 = _page_mla(plane.scales, lens_np, bs, perm_seed)
+    k_r, bt3 = _page_mla(inp.k_r.to(DEV), lens_np, bs, perm_seed)
+    assert torch.equal(bt, bt2) and torch.equal(bt, bt3)
+    paged = k_.NVFP4Plane(codes, scales, plane.tensor_scale, plane.layout)
+    q_c, q_r = inp.q_c.to(DEV), inp.q_r.to(DEV)
+    B, H, D = q_c.shape
+    cap = 64
+    part_o = torch.empty(B * H * cap * D, dtype=torch.float32, device=DEV)
+    part_lse = torch.empty(B * H * cap, dtype=torch.float32, device=DEV)
+    args = k_.make_decode_args(q_c, paged, None, lens, max_kv_len=int(inp.c.shape[1]),
+                               softmax_scale=inp.softmax_scale, num_splits=s, part_o=part_o, part_lse=part_lse,
+                               q_rope=q_r, k_rope=k_r, block_table=bt)
+    out = torch.empty(B, H, D, dtype=out_dtype, device=DEV)
+    lse = torch.empty(B, H, dtype=torch.float32, device=DEV)
+    if fused:
+        used = k_.attn_decode(args, out, lse_out=lse)
+    else:
+        used = k_.attn_decode_splitkv(args)
+        k_.attn_decode_combine(part_o, part_lse, B, H, D, used, out, lse_out=lse)
+    torch.cuda.synchronize()
+    return out, lse, used
+
+
+# (B, lens, s, block size): chunks that start inside a block (s = 4 over 2048
+# tokens with 1024-token blocks), one-block requests, auto splits, a
+# one-token request, more than one block per chunk
+MLA_PAGED_CASES = [
+    (2, (300, 77), 1, 64), (2, (300, 77), 3, 128), (3, (1000, 64, 65), 0, 256),
+    (4, (2048, 2000, 1500, 129), 4, 1024), (2, (513, 1), 8, 64), (4, (2048, 2000, 1500, 129), 2, 64),
+]
+
+
+@pytest.mark.parametrize("B,lens,s,bs", MLA_PAGED_CASES, ids=lambda v: str(v))
+def test_mla_paged_matches_contiguous(B, lens, s, bs):
+    """The latent, scale and rope planes in permuted blocks decode to outputs
+    and lse bit-identical to the contiguous planes (same chunking, same
+    arithmetic), and within the oracle's fp32 gate."""
+    announce(f"mla paged B={B} lens={lens} s={s} bs={bs}")
+    inp, _, o_ref, _, o_abs = _case(B, lens, 1)
+    plane, _, out_c, lse_c, used_c = _gpu(inp, s, torch.float32)
+    out_p, lse_p, used_p = _gpu_paged(inp, plane, s, bs)
+    assert used_p == used_c
+    assert torch.equal(out_p, out_c) and torch.equal(lse_p, lse_c)
+    _check_fp32(out_p, o_ref, o_abs, f"mla paged s={used_p} bs={bs}")
+
+
+def test_mla_paged_fused_bf16():
+    announce("mla paged fused bf16")
+    inp, _, o_ref, _, _ = _case(2, (700, 450), 2)
+    plane, _, out_c, _, _ = _gpu(inp, 5, torch.bfloat16, fused=True)
+    out_p, _, _ = _gpu_paged(inp, plane, 5, 128, out_dtype=torch.bfloat16, fused=True)
+    assert torch.equal(out_p, out_c)
+    assert_bf16_output(out_p, o_ref, "mla paged fused")
+
+
+def test_mla_paged_full_config_sampled():
+    """B = 32, kv 8192, auto splits, 64-token blocks: bit-identical to the
+    contiguous planes over every request."""
+    announce("mla paged full config")
+    inp = kvq_synth.mla()
+    plane, _, out_c, lse_c, used = _gpu(inp, 0, torch.bfloat16)
+    out_p, lse_p, used_p = _gpu_paged(inp, plane, 0, 64, out_dtype=torch.bfloat16)
+    assert used_p == used
+    assert torch.equal(out_p, out_c) and torch.equal(lse_p, lse_c)
+
+
+def test_mla_paged_rejects_bad_blocks():
+    """Block sizes that are not a power of two or not a multiple of the MLA
+    tile (64 tokens) are refused before any launch."""
+    k_ = K()
+    inp, _, _, _, _ = _case(2, (300, 77), 1)
+    plane, _, _, _, _ = _gpu(inp, 1, torch.float32)
+    for bs in (32, 96):
+        with pytest.raises(k_.KvqError):
+            _gpu_paged(inp, plane, 2, bs)
