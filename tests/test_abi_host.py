@@ -234,6 +234,28 @@ def _mla_args(K):
     return a
 
 
+def test_mla_paged_validation(L, K):
+    """Paged latent planes: power-of-two block sizes that are multiples of the
+    MLA tile (64 tokens), a table row covering max_kv_len, kv_sblk >= 0, a
+    4-byte aligned table, at most 510 blocks per split."""
+    def paged(bs=64, stride=16):
+        a = _mla_args(K)
+        a.block_table, a.block_size, a.bt_stride, a.kv_sblk, a.kv_sb = FAKE, bs, stride, bs, 0
+        return a
+    assert _decode_rc(L, paged(bs=32, stride=32)) == 1       # below the tile
+    assert _decode_rc(L, paged(bs=192, stride=6)) == 1       # a multiple of the tile, not a power of two
+    assert _decode_rc(L, paged(bs=0)) == 1
+    assert _decode_rc(L, paged(stride=15)) == 1              # table row shorter than ceil(1024 / 64)
+    a = paged(); a.kv_sblk = -1
+    assert _decode_rc(L, a) == 1
+    a = paged(); a.block_table = FAKE_ODD
+    assert _decode_rc(L, a) == 3
+    a = paged(stride=600); a.max_kv_len = 600 * 64; a.num_splits = 1
+    assert _decode_rc(L, a) == 1                             # one split over 600 blocks
+    a = paged(); a.kv_format = K.KVQ_FP8E4M3
+    assert _decode_rc(L, a) == 2                             # NVFP4 latent only
+
+
 def test_mla_validation(L, K):
     a = _mla_args(K); a.Hq = 8
     assert _decode_rc(L, a) == 2                     # 16 heads only
@@ -299,8 +321,6 @@ def test_paged_decode_validation(L, K):
     assert _decode_rc(L, a) == 3
     a = paged(); a.quantize_p, a.prob_scale, a.p_scratch = 1, 1.0 / 448.0, FAKE
     assert _decode_rc(L, a) == 2                             # exact probabilities only
-    a = paged(); a.layout = K.KVQ_LAYOUT_MLA; a.Hkv = 1; a.Hq = 16
-    assert _decode_rc(L, a) == 2                             # GQA layout only
     a = paged(); a.v_layout = K.KVQ_PLANE_TOKEN4; a.kv_sblk = 8 * 64 + 2
     assert _decode_rc(L, a) == 3
 
