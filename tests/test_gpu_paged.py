@@ -68,6 +68,10 @@ CASES = [
     # register windows of tile rows are refilled from the LDS table
     (("nvfp4", "custom", 2, 8, 1, 128, (9000, 8300), "bf16"), 0, 32, 1, False),   # G = 8: 71 tiles per wave
     (("nvfp4", "custom", 1, 32, 8, 128, (20000,), "bf16"), 1, 64, 1, True),       # G = 4: 79 tiles per wave
+    # the GQA 4:1 32K cache in the launch configuration bench.py times
+    # (auto splits, TOKEN4 V, 64-token blocks), two launches and fused
+    (("nvfp4", "gqa", 32768), 1, 64, 0, False),
+    (("nvfp4", "gqa", 32768), 1, 64, 0, True),
 ]
 
 
