@@ -286,9 +286,9 @@ typedef struct {
                                device float[Hkv], kv head h dequantized with
                                its own scale (kvq_pack_fp8_heads); 0 = one
                                per-tensor scale each */
-  /* Paged cache (GQA and MLA layouts, exact probabilities; vLLM's block
-     tables, the serving setting of Model-Optimizer PR #1832 "Purpose" and
-     "Testing").
+  /* Paged cache (GQA and MLA layouts; vLLM's block tables, the serving
+     setting of Model-Optimizer PR #1832 "Purpose" and "Testing").  GQA
+     paged caches are decoded with exact or FP8-quantized probabilities.
      NULL block_table: the planes are addressed by kv_sb / kv_sh / kv_st as
      above.  Otherwise token t of request b, kv head h is plane row
        block_table[b * bt_stride + t / block_size] * kv_sblk
@@ -304,7 +304,7 @@ typedef struct {
      read; block_size is a power of two and a multiple of 64 (the MLA
      kernel's tile), and one split may span at most 510 blocks.
      Errors: KVQ_ERR_ARG for a block size, bt_stride or kv_sblk out of
-     these bounds; KVQ_ERR_UNSUPPORTED with quantize_p (GQA). */
+     these bounds. */
   const int32_t* block_table;
   int32_t block_size;
   int64_t bt_stride;

@@ -375,7 +375,6 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
       return fail(KVQ_ERR_UNSUPPORTED, "GQA decode: G=%d, D=%d not supported (G in 1,2,4,8,16; D in 64,128)", G, a->D);
     if (a->block_table != nullptr) {   // paged cache
       const int tile = kvq::gqa_tile_tokens(G);
-      if (a->quantize_p) return fail(KVQ_ERR_UNSUPPORTED, "paged caches are decoded with exact probabilities only");
       if (a->block_size <= 0 || a->block_size % tile != 0 || (a->block_size & (a->block_size - 1)) != 0)
         return fail(KVQ_ERR_ARG, "block_size must be a power of two and a multiple of the decode tile (%d tokens for G=%d)",
                     tile, G);

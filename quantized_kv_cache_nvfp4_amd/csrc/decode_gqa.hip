@@ -360,7 +360,6 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
   constexpr bool QF32 = QT == kQF32;
   constexpr bool q8 = QT == kQFp8;   // FP8 query codes: 8 bytes per query word instead of 16
   static_assert(PM == 0 || (!FUSED && PSPLIT == 1), "the FP8-P passes write partials only");
-  static_assert(!PAGED || PM == 0, "paged caches use exact probabilities");
   using Gm = Geo<KVF, D>;
   constexpr int NSUB = 16 / G;                  // row groups in the 16 MFMA columns
   constexpr int NT = NSUB < 2 ? 2 : NSUB;       // sub-tiles (16 tokens) per tile
@@ -603,7 +602,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
   const int ce = (cs + chunk < L) ? cs + chunk : L;
   ce_ld = ce;   // every later load stops at the request's end
   if constexpr (PAGED) {
-    if constexpr (NG > 1) {
+    if constexpr (PM != 2 && NG > 1) {   // (pass 2 reads no K)
       const int ft = cs + wave * TT;
       load_ktile(KA, wave, ft < ce ? static_cast<int64_t>(first_blk) * a.kv_sblk + static_cast<int64_t>(ft % bs) * st
                                    : 0);
@@ -1284,9 +1283,7 @@ hipError_t launch_a(const kvq_decode_args& a, const DecodePlan& p, const FusedOu
 
 template <int KVF, int G, int D, int QT, int PSPLIT, int VL, int PM>
 hipError_t launch_v(const kvq_decode_args& a, const DecodePlan& p, const FusedOut* fo, hipStream_t st) {
-  if constexpr (PM == 0) {
-    if (a.block_table != nullptr) return launch_a<KVF, G, D, QT, PSPLIT, VL, 0, true>(a, p, fo, st);
-  }
+  if (a.block_table != nullptr) return launch_a<KVF, G, D, QT, PSPLIT, VL, PM, true>(a, p, fo, st);
   return launch_a<KVF, G, D, QT, PSPLIT, VL, PM, false>(a, p, fo, st);
 }
 

@@ -156,8 +156,9 @@ def gpu_pack(inp, fmt, v_layout=0):
 
 
 def gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.bfloat16, out_scale=None, with_lse=False, fused=False,
-               prob_scale=None):
-    """prob_scale: None for exact probabilities, else the FP8-P path."""
+               prob_scale=None, block_table=None):
+    """prob_scale: None for exact probabilities, else the FP8-P path;
+    block_table: paged planes kp / vp (None: contiguous)."""
     k_ = K()
     B, Hq, D = inp.B, inp.Hq, inp.D
     cap = 64
@@ -171,7 +172,7 @@ def gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.bfloat16, out_scale=None, w
         fp8p = dict(quantize_p=True, prob_scale=prob_scale,
                     p_scratch=torch.full((max(n, 4),), float("nan"), dtype=torch.float32, device=DEV))
     args = k_.make_decode_args(q, kp, vp, lens, max_kv_len=inp.Lmax, softmax_scale=inp.softmax_scale,
-                               num_splits=s, part_o=part_o, part_lse=part_lse, **fp8p)
+                               num_splits=s, part_o=part_o, part_lse=part_lse, block_table=block_table, **fp8p)
     out = torch.empty(B, Hq, D, dtype=out_dtype, device=DEV)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV) if with_lse else None
     if fused:

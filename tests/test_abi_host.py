@@ -319,8 +319,8 @@ def test_paged_decode_validation(L, K):
     assert _decode_rc(L, a) == 1
     a = paged(); a.block_table = FAKE_ODD
     assert _decode_rc(L, a) == 3
-    a = paged(); a.quantize_p, a.prob_scale, a.p_scratch = 1, 1.0 / 448.0, FAKE
-    assert _decode_rc(L, a) == 2                             # exact probabilities only
+    a = paged(); a.quantize_p, a.prob_scale, a.p_scratch = 1, 1.0 / 448.0, FAKE; a.block_size = 32
+    assert _decode_rc(L, a) == 1                             # FP8-P: the same block-size rule
     a = paged(); a.v_layout = K.KVQ_PLANE_TOKEN4; a.kv_sblk = 8 * 64 + 2
     assert _decode_rc(L, a) == 3
 

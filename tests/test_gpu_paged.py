@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import DEV, K, announce, assert_bf16_output, gpu_pack, make_inputs, oracle_gqa
+from gpu_helpers import DEV, K, announce, assert_bf16_output, gpu_decode, gpu_pack, make_inputs, oracle_gqa
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +103,36 @@ def test_paged_rejects_small_blocks():
     vpp, _ = _page(vp, 32, 2)
     with pytest.raises(k_.KvqError):
         _decode(inp, kpp, vpp, lens, 2, block_table=bt)
+
+
+FP8P_CASES = [
+    # (key, v_layout, block_size, splits, fused)
+    (("nvfp4", "gqa", 1024), 1, 64, 3, False),
+    (("nvfp4", "gqa", 1024), 0, 128, 0, True),
+    (("fp8", "fp8", 64), 1, 64, 2, False),
+    (("nvfp4", "custom", 2, 16, 2, 128, (300, 77), "bf16"), 0, 32, 4, False),   # G = 8: tile 32
+    (("nvfp4", "custom", 2, 8, 1, 128, (9000, 8300), "bf16"), 0, 32, 1, False),   # windows refilled
+]
+
+
+@pytest.mark.parametrize("case", FP8P_CASES, ids=lambda c: f"{c[0][0]}-{c[0][1]}-v{c[1]}-bs{c[2]}-s{c[3]}-f{int(c[4])}")
+def test_paged_fp8p_matches_contiguous(case):
+    """FP8-quantized probabilities over paged planes: both passes address the
+    blocks through the table, so output and lse are bit-identical to the
+    contiguous planes' FP8-P decode (itself checked against the oracle)."""
+    key, v_layout, bs, s, fused = case
+    fmt = key[0]
+    announce(f"paged fp8p {case}")
+    inp = make_inputs(key)
+    kp, vp, _, _, lens = gpu_pack(inp, fmt, v_layout)
+    ps = float(np.float32(1.0 / 448.0))
+    ref, used, ref_lse = gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.float32, with_lse=True, fused=fused,
+                                    prob_scale=ps)
+    kpp, bt = _page(kp, bs, 4)
+    vpp, bt2 = _page(vp, bs, 4)
+    assert torch.equal(bt, bt2)
+    got, used_p, lse = gpu_decode(inp, kpp, vpp, lens, s, out_dtype=torch.float32, with_lse=True, fused=fused,
+                                  prob_scale=ps, block_table=bt)
+    assert used_p == used
+    assert torch.isfinite(got).all()
+    assert torch.equal(got, ref) and torch.equal(lse, ref_lse), "paged FP8-P must match the contiguous planes"
