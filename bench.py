@@ -71,6 +71,8 @@ TRAFFIC = {   # committed counter summaries and the kernel source they were take
             os.path.join(CSRC, "decode_gqa.hip")),
     "mla": (os.path.join(ROOT, "profiles", "k_decode_mla_nvfp4_b32_h16_c512_r64_kv8k_traffic.txt"),
             os.path.join(CSRC, "decode_mla.hip")),
+    "fp8": (os.path.join(ROOT, "profiles", "k_decode_gqa_fp8_b64_hq32_hkv8_d128_ragged_traffic.txt"),
+            os.path.join(CSRC, "decode_gqa.hip")),
 }
 
 
@@ -481,7 +483,7 @@ def run_fp8(args):
         "calibrate_pack": {k_: {"us": round(t, 2), "GB/s": round(prep_bytes[k_] / (t * 1e-6) / 1e9, 1)}
                            for k_, t in prep_us.items()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic("fp8"),
                      "kernel": "k_decode_gqa<FP8,G=4,D=128> (split kernel, partials)",
                      "kernel_us_mean": round(kernel_us, 3), "algorithmic_bytes": algo},
     }
