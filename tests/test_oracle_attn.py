@@ -164,3 +164,78 @@ def test_fp8_output_codes():
     assert list(codes) == [0x38, 0xC4, 0x7E, 0x00]
     codes = A.fp8_output(np.array([0.5]), 0.25)
     assert int(codes[0]) == int(F.e4m3_encode(2.0))
+
+
+# ---- FP8 probabilities at query groups of more than one head --------------
+# gqa_probs and decode_gqa_fp8p are pinned here with G = 4 query heads per kv
+# head, kv heads that differ, nonzero scores and softmax_scale != 1, so that a
+# wrong head mapping (h % G instead of h // G) or a dropped softmax_scale fails.
+
+def _gqa_case():
+    B, Hq, Hkv, D, L = 2, 8, 2, 16, 23
+    q = _rand((B, Hq, D), 60) * 2.0
+    k = _rand((B, Hkv, L, D), 61)
+    k[:, 1] *= 3.0   # kv heads see clearly different score ranges
+    v = _rand((B, Hkv, L, D), 62)
+    return q, k, v, [L, 14], 0.37
+
+
+def test_gqa_probs_match_torch_sdpa_on_identity_values():
+    # SDPA with V = the identity matrix returns the probability rows
+    # themselves (library routine; keys repeat-interleaved by G)
+    q, k, _, lens, alpha = _gqa_case()
+    P = A.gqa_probs(q, k, lens, alpha)
+    G = q.shape[1] // k.shape[1]
+    kt = torch.from_numpy(k).repeat_interleave(G, dim=1)
+    for b, Lb in enumerate(lens):
+        eye = torch.eye(Lb, dtype=torch.float64).expand(1, q.shape[1], Lb, Lb)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[b:b + 1, :, None, :]), kt[b:b + 1, :, :Lb], eye, scale=alpha)[0, :, 0].numpy()
+        np.testing.assert_allclose(P[b, :, :Lb], ref, rtol=1e-12, atol=1e-15)
+        assert np.all(P[b, :, Lb:] == 0)
+        np.testing.assert_allclose(P[b, :, :Lb].sum(-1), 1.0, rtol=1e-14)
+
+
+def test_gqa_probs_weight_values_like_decode_gqa():
+    # sum_t P_t V_t reproduces decode_gqa's output (itself pinned by SDPA and
+    # mpmath above); P_t = exp(sigma_t - lse) with decode_gqa's lse, where
+    # sigma_t comes from the single-token case (L = 1: lse = sigma_0)
+    q, k, v, lens, alpha = _gqa_case()
+    P = A.gqa_probs(q, k, lens, alpha)
+    o, lse = A.decode_gqa(q, k, v, lens, alpha)
+    G = q.shape[1] // k.shape[1]
+    for b, Lb in enumerate(lens):
+        for h in range(q.shape[1]):
+            np.testing.assert_allclose(P[b, h, :Lb] @ v[b, h // G, :Lb], o[b, h], rtol=1e-12, atol=1e-14)
+            for t in (0, Lb // 2, Lb - 1):
+                kt = k[b:b + 1, :, t:t + 1]
+                _, sig = A.decode_gqa(q[b:b + 1], kt, v[b:b + 1, :, t:t + 1], [1], alpha)
+                assert P[b, h, t] == pytest.approx(math.exp(sig[0, h] - lse[b, h]), rel=1e-12)
+
+
+def test_fp8_probabilities_closed_form_four_heads_per_kv_head():
+    # Hkv = 2, G = 4, L = 3, softmax_scale 0.5, D = 4.
+    #  kv head 0: three equal keys -> P = 1/3 for every query head of the
+    #    group; 448/3 = 149.33 -> E4M3 144, so o = (144/448) (V0 + V1 + V2).
+    #  kv head 1: keys (0, 2 ln 4, -2000) on channel 0.  Query head 4 has
+    #    q = e_0: alpha * dscore = ln 4 -> P = (1/5, 4/5, 0); 448/5 = 89.6 ->
+    #    88 and 4*448/5 = 358.4 -> 352.  Query head 5 has q = 2 e_0:
+    #    P = (1/17, 16/17, 0); 26.35 -> 26 and 421.65 -> 416.  Heads 6 and 7
+    #    have q = 0: P = 1/3 each -> 144 each.
+    alpha, ps = 0.5, 1.0 / 448.0
+    k = np.zeros((1, 2, 3, 4))
+    k[0, 0, :, :] = [0.7, -1.2, 0.3, 2.0]
+    k[0, 1, :, 0] = [0.0, 2.0 * math.log(4.0), -2000.0]
+    q = np.zeros((1, 8, 4))
+    q[0, 0:4] = _rand((4, 4), 63)
+    q[0, 4, 0] = 1.0
+    q[0, 5, 0] = 2.0
+    v = _rand((1, 2, 3, 4), 64)
+    o = A.decode_gqa_fp8p(q, k, v, [3], alpha, ps)
+    V0, V1 = v[0, 0], v[0, 1]
+    for h in range(4):
+        np.testing.assert_allclose(o[0, h], (144.0 / 448.0) * V0.sum(0), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(o[0, 4], (88.0 * V1[0] + 352.0 * V1[1]) / 448.0, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(o[0, 5], (26.0 * V1[0] + 416.0 * V1[1]) / 448.0, rtol=1e-14, atol=1e-15)
+    for h in (6, 7):
+        np.testing.assert_allclose(o[0, h], (144.0 / 448.0) * V1.sum(0), rtol=1e-14, atol=1e-15)
