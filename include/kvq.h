@@ -218,7 +218,10 @@ int kvq_pack_fp8_batch(const kvq_pack_job* jobs, int32_t n_jobs, void* stream);
 
 /*
  * kvq_unpack_nvfp4 - dequantize NVFP4 rows to float32: out = fp32(E2M1(c) *
- * s_hat * s_t) (one rounding; e * s_hat is exact).  Test / inspection path.
+ * s_hat * s_t) (one rounding; e * s_hat is exact).  This is the fake-quant
+ * value of Model-Optimizer PR #714, Testing section (the quantizer dump's
+ * "fake" mode returns the dequantized tensor): the value the decode kernels
+ * reconstruct in registers.  Test / inspection path.
  *   codes, scales  device planes per src_rows and src_layout (KVQ_PLANE_*);
  *                  tensor_scale device float[1];
  *   out            device float32 rows per out_rows (extents == src_rows').
@@ -226,7 +229,12 @@ int kvq_pack_fp8_batch(const kvq_pack_job* jobs, int32_t n_jobs, void* stream);
 int kvq_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, kvq_rows src_rows, int32_t src_layout,
                      int32_t d, const float* tensor_scale, float* out, kvq_rows out_rows, void* stream);
 
-/* kvq_unpack_fp8 - out = fp32(E4M3(c) * scale); as kvq_unpack_nvfp4. */
+/*
+ * kvq_unpack_fp8 - out = fp32(E4M3(c) * scale): the dequantized value of the
+ * per-tensor FP8 kv_cache_scheme (compressed-tensors PR #436, Changes;
+ * symmetric, so no zero point).  Arguments and errors as kvq_unpack_nvfp4;
+ * scale is device float[1].
+ */
 int kvq_unpack_fp8(const uint8_t* codes, kvq_rows src_rows, int32_t src_layout, int32_t d, const float* scale,
                    float* out, kvq_rows out_rows, void* stream);
 
@@ -375,8 +383,10 @@ int32_t attn_decode_tile_tokens(int32_t Hq, int32_t Hkv);
 int attn_decode_splitkv(const kvq_decode_args* args, int32_t* splits_used, void* stream);
 
 /*
- * attn_decode_combine - merge the s partials (Model-Optimizer PR #1832,
- * Testing section: "a small combine kernel merges the s partials"):
+ * attn_decode_combine - merge the s split partials into one output per
+ * (request, head) (Model-Optimizer PR #1832, Testing section: the split-KV
+ * description ends with a small separate kernel that merges the per-split
+ * results):
  * LSE = log sum_j exp(lse_j), o = sum_j exp(lse_j - LSE) o_j; empty splits
  * (lse_j = -inf) are skipped; a request with no tokens gives o = 0, lse =
  * -inf.
@@ -428,12 +438,34 @@ int attn_decode(const kvq_decode_args* args, void* out, int32_t out_dtype, const
 int kvq_auto_num_splits(int32_t num_cus, int32_t B, int32_t programs_per_req, int32_t max_kv_len,
                         int32_t Dv, int32_t Hq, int32_t* s_out);
 
-/* Compute units of the current HIP device (host call; needs a GPU). */
+/*
+ * kvq_device_cu_count - compute units of the current HIP device, the first
+ * input of the automatic split count (Model-Optimizer PR #1832, Testing
+ * section: the heuristic sizes num_kv_splits from the GPU's compute-unit
+ * count and batch x heads).  Host call; needs a GPU.  num_cus_out: host
+ * int32*.  Errors: KVQ_ERR_ARG (null), KVQ_ERR_HIP (no device).
+ */
 int kvq_device_cu_count(int32_t* num_cus_out);
 
 /*
+ * kvq_decode_workspace_bytes - bytes of the split partials for s splits:
+ * part_o [B][Hq][s][Dv] plus part_lse [B][Hq][s], float32, i.e.
+ * B * Hq * s * (Dv + 1) * 4 (Model-Optimizer PR #1832, Testing section: each
+ * split writes its partial output and log-sum-exp for the combine).  A
+ * caller that passes num_splits <= 0 sizes for kvq_auto_num_splits' result
+ * (or for 64, its maximum); with a fused append pass s + 1.  Host-only;
+ * returns 0 for a non-positive argument.  The caller allocates: the library
+ * never does.
+ */
+size_t kvq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Dv, int32_t s);
+
+/*
  * kvq_fp8p_scratch_floats - float32 elements of p_scratch needed by the
- * FP8-probability path (quantize_p = 1): the spilled scores, one row of
+ * FP8-probability path (quantize_p = 1; vLLM PR #15734 "[Quantization][FP8]
+ * Add support for FP8 models with input_scale for output projection and QK
+ * quantization", item 2: the softmax probabilities quantized to FP8, which
+ * with normalized probabilities needs the scores of the whole sequence
+ * before P is formed): the spilled scores, one row of
  * roundup(max_kv_len, 4) floats per (request, query head); s is accepted for
  * interface stability and does not change the size.  Host-only.
  */

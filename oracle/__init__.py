@@ -22,7 +22,7 @@ written from the format and method descriptions on these pages:
 * Model-Optimizer PR #1832 ("Add quant+sparse attention for vLLM serving"),
   Testing section: the split-KV decode description (s contiguous chunks per
   (request, head), partial softmax with running max, denominator and
-  weighted V; a small combine kernel merges the partials).
+  weighted V; the per-split results are merged by a separate step).
 
 Modules:
   formats    E2M1 / E4M3 / bf16 / fp32 encoders and decoders

@@ -24,7 +24,7 @@ from ._lib import (KVQ_BF16, KVQ_F16, KVQ_F32, KVQ_FP8E4M3, KVQ_LAYOUT_GQA, KVQ_
 __all__ = [
     "kvq_amax", "kvq_pack_nvfp4", "kvq_pack_fp8", "kvq_unpack_nvfp4", "kvq_unpack_fp8",
     "attn_decode_splitkv", "attn_decode_combine", "attn_decode", "kvq_auto_num_splits", "kvq_device_cu_count",
-    "kvq_fp8p_scratch_floats", "kvq_last_error", "kvq_version", "NVFP4Plane", "FP8Plane", "KvqError",
+    "kvq_fp8p_scratch_floats", "kvq_decode_workspace_bytes", "decode_workspace", "kvq_last_error", "kvq_version", "NVFP4Plane", "FP8Plane", "KvqError",
     "KVQ_F32", "KVQ_BF16", "KVQ_F16", "KVQ_FP8E4M3", "KVQ_NVFP4", "KVQ_LAYOUT_GQA", "KVQ_LAYOUT_MLA",
     "KVQ_PLANE_ROWS", "KVQ_PLANE_TOKEN4", "make_decode_args",
 ]
@@ -214,6 +214,23 @@ def kvq_fp8p_scratch_floats(B: int, Hq: int, s: int, max_kv_len: int) -> int:
     return _lib.lib().kvq_fp8p_scratch_floats(B, Hq, s, max_kv_len)
 
 
+def kvq_decode_workspace_bytes(B: int, Hq: int, Dv: int, s: int) -> int:
+    """Bytes of the split partials (part_o plus part_lse) for s splits."""
+    return _lib.lib().kvq_decode_workspace_bytes(B, Hq, Dv, s)
+
+
+def decode_workspace(B: int, Hq: int, Dv: int, s: int, device) -> tuple:
+    """(part_o [B*Hq*s*Dv], part_lse [B*Hq*s]) float32 views of one buffer of
+    kvq_decode_workspace_bytes(B, Hq, Dv, s) bytes: part_o first, part_lse
+    right after it (both 4-byte aligned)."""
+    nbytes = kvq_decode_workspace_bytes(B, Hq, Dv, s)
+    if nbytes == 0:
+        raise ValueError("B, Hq, Dv and s must be positive")
+    buf = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+    n_o = B * Hq * s * Dv
+    return buf[:n_o], buf[n_o:]
+
+
 def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_splits=0, part_o, part_lse,
                      q_rope=None, k_rope=None, quantize_p=False, prob_scale=1.0 / 448.0,
                      p_scratch=None, block_table=None, q_scale=None, new_k=None, new_v=None) -> KvqDecodeArgs:
@@ -235,12 +252,18 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
     """
     a = KvqDecodeArgs()
     mla = v is None
+    if q.dim() != 3 or (q.shape[-1] > 1 and q.stride(-1) != 1):
+        raise ValueError("q must be [B, Hq, D] with a contiguous last dim")
+    if q_rope is not None and (q_rope.dim() != 3 or (q_rope.shape[-1] > 1 and q_rope.stride(-1) != 1)):
+        raise ValueError("q_rope must be [B, Hq, Drope] with a contiguous last dim")
     fmt = KVQ_NVFP4 if isinstance(k, NVFP4Plane) else KVQ_FP8E4M3
     B, Hq, D = q.shape
     a.kv_format, a.layout = fmt, (KVQ_LAYOUT_MLA if mla else KVQ_LAYOUT_GQA)
     a.B, a.Hq, a.D, a.Dv = B, Hq, D, D
     row_elems = D // 2 if fmt == KVQ_NVFP4 else D
     if mla:
+        if k.layout != KVQ_PLANE_ROWS:
+            raise ValueError("the MLA latent plane is read in the row layout")
         a.Hkv, a.Drope = 1, (q_rope.shape[-1] if q_rope is not None else 0)
         kr = _rows(k.codes, row_elems)  # [B, Lmax, .] -> n0=1, n1=B, n2=Lmax
         a.kv_sb, a.kv_sh, a.kv_st = kr.s1, 0, kr.s2

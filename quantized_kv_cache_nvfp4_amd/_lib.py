@@ -81,6 +81,7 @@ _PROTOS = {
     "kvq_auto_num_splits": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_I32)]),
     "kvq_device_cu_count": (ctypes.c_int, [ctypes.POINTER(_I32)]),
     "kvq_fp8p_scratch_floats": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
+    "kvq_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "attn_decode_tile_tokens": (_I32, [_I32, _I32]),
 }
 

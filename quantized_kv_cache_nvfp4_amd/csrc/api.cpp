@@ -261,6 +261,12 @@ int kvq_device_cu_count(int32_t* num_cus_out) {
   return ok();
 }
 
+size_t kvq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Dv, int32_t s) {
+  if (B <= 0 || Hq <= 0 || Dv <= 0 || s <= 0) return 0;
+  // part_o [B][Hq][s][Dv] and part_lse [B][Hq][s], float32
+  return static_cast<size_t>(B) * Hq * s * (static_cast<size_t>(Dv) + 1) * sizeof(float);
+}
+
 size_t kvq_fp8p_scratch_floats(int32_t B, int32_t Hq, int32_t s, int32_t max_kv_len) {
   if (B <= 0 || Hq <= 0 || s <= 0 || max_kv_len < 0) return 0;
   // the spilled scores: one row of roundup(max_kv_len, 4) floats per (request, head)
@@ -305,8 +311,14 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
     return fail(KVQ_ERR_ARG, "softmax_scale must be a positive finite number");
   if (!aligned(a->k_codes, 16)) return fail(KVQ_ERR_ALIGN, "k_codes must be 16-byte aligned");
   if (a->k_scales != nullptr && !aligned(a->k_scales, 4)) return fail(KVQ_ERR_ALIGN, "k_scales must be 4-byte aligned");
-  if (a->q_dtype == KVQ_F32 ? !aligned(a->q, 4) : a->q_dtype == KVQ_BF16 ? !aligned(a->q, 2) : false)
-    return fail(KVQ_ERR_ALIGN, "q misaligned");
+  if (a->q_dtype == KVQ_F32 || a->q_dtype == KVQ_BF16) {
+    // query rows are read with 16-byte loads: the base 16-byte aligned and
+    // the strides whole 16-byte units (8 bf16 or 4 fp32 elements)
+    const int64_t unit = a->q_dtype == KVQ_F32 ? 4 : 8;
+    if (!aligned(a->q, 16) || a->q_sb % unit != 0 || a->q_sh % unit != 0)
+      return fail(KVQ_ERR_ALIGN, "q must be 16-byte aligned with q_sb and q_sh multiples of %d elements",
+                  static_cast<int>(unit));
+  }
   if (a->kv_st < 0 || a->kv_sb < 0 || a->kv_sh < 0) return fail(KVQ_ERR_ARG, "cache strides must be >= 0");
   // token offsets inside one (request, kv head) are computed in 32 bits
   const int64_t row_bytes = a->kv_format == KVQ_NVFP4 ? a->D / 2 : a->D;
@@ -342,8 +354,9 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
     if (a->B + (a->B + s - 1) / s > 65535) return fail(KVQ_ERR_ARG, "B too large for the fused append's grid");
   }
   const int np = s + (append ? 1 : 0);   // partials per head
-  // the FP8-probability passes always go through the partials
-  const bool need_partials = a->quantize_p || !(fused && np == 1);
+  // the FP8-probability passes and the MLA kernel always go through the
+  // partials (the latter followed by the combine launch)
+  const bool need_partials = a->quantize_p || a->layout == KVQ_LAYOUT_MLA || !(fused && np == 1);
   if (need_partials) {
     if (a->part_o == nullptr || a->part_lse == nullptr) return fail(KVQ_ERR_ARG, "part_o and part_lse must be non-null");
     if (!aligned(a->part_o, 4) || !aligned(a->part_lse, 4)) return fail(KVQ_ERR_ALIGN, "partials must be 4-byte aligned");

@@ -1,6 +1,6 @@
 // Combine of split-KV partials (Model-Optimizer PR #1832 "Add quant+sparse
-// attention for vLLM serving", Testing section: a small combine kernel
-// merges the s partials of each (request, head)), with the output written as
+// attention for vLLM serving", Testing section: the per-split results of
+// each (request, head) are merged by a separate small kernel), with the output written as
 // fp32, bf16 (round to nearest even) or FP8 E4M3 with an output scale (vLLM
 // PR #15734, item 1: the attention output kept in FP8 for the next layer).
 //

@@ -5,7 +5,7 @@
 // serving", Testing section: the KV sequence of one (request, head) is cut
 // into s contiguous chunks; each program keeps a running max and denominator
 // of the softmax over its chunk and accumulates the probability-weighted V,
-// and a combine step merges the s partials.  Cache formats: Model-Optimizer
+// and a separate step merges the per-split results.  Cache formats: Model-Optimizer
 // PR #714 Testing section (NVFP4: E2M1 codes, E4M3 scale per 16 elements
 // along head_dim, per-tensor fp32 scale) and compressed-tensors PR #436
 // kv_cache_scheme (per-tensor FP8 E4M3).
@@ -396,22 +396,25 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
   const int np = num_splits + (app ? 1 : 0);   // partials per head
 
   // ---------------- fused combine: the last work-group of (b, kv head) to
-  // finish merges the np partials of its G heads.  The partials were stored
-  // at device scope; waiting for those stores to complete before the
-  // counter increment orders them before it (no cache write-back fence is
-  // needed), and the last work-group reads them at device scope.
+  // finish merges the np partials of its G heads.  Publication follows the
+  // HIP memory model: every thread issues an agent-scope release fence after
+  // its partial stores, the barrier orders all of them before thread 0's
+  // counter increment (acquire-release, agent scope), and the work-group
+  // that sees the last count takes an agent-scope acquire fence before it
+  // reads the partials (the reads are device-scope loads as well).
   auto fused_tail = [&](int b) {
-    __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (threadIdx.x == 0) {
       int* ctr = fo.counters + static_cast<int64_t>(b) * a.Hkv + kvh;
-      const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
       const int last = (prev == np - 1);
       if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // ready for the next call
       lds_last = last;
     }
     __syncthreads();
     if (!lds_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const float osc = (fo.out_dtype == KVQ_FP8E4M3) ? *fo.out_scale : 1.0f;
     // one head per wave (the routine of the standalone combine kernel)
     for (int h = wave; h < G; h += kWaves) {

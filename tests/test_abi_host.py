@@ -374,3 +374,72 @@ def test_fused_append_validation(L, K):
     assert _decode_rc(L, a) == 2
     a = app(); a.q_dtype = K.KVQ_F32
     assert _decode_rc(L, a) == 2                     # bf16 queries only
+
+
+def test_query_alignment_validation(L, K):
+    """bf16 / fp32 query rows are read with 16-byte loads: the base must be
+    16-byte aligned and q_sb, q_sh whole 16-byte units (8 bf16, 4 fp32)."""
+    a = _good_args(K); a.q = ctypes.c_void_p(0x10002)         # offset by one bf16 element
+    assert _decode_rc(L, a) == 3 and "16-byte" in K.kvq_last_error()
+    a = _good_args(K); a.q_sh = 129
+    assert _decode_rc(L, a) == 3
+    a = _good_args(K); a.q_sb = 4
+    assert _decode_rc(L, a) == 3
+    a = _good_args(K); a.q_dtype = K.KVQ_F32; a.q_sh = 4; a.q_sb = 4 * 32
+    a.num_splits = 65; a.part_capacity = 100                 # passes the query checks, fails on s
+    assert _decode_rc(L, a) == 1 and "num_splits" in K.kvq_last_error()
+    a = _good_args(K); a.q_dtype = K.KVQ_F32; a.q_sh = 6
+    assert _decode_rc(L, a) == 3
+
+
+def test_mla_single_split_still_needs_partials(L, K):
+    """The MLA path always writes partials and runs the combine, also through
+    attn_decode with one split."""
+    a = _mla_args(K); a.num_splits = 1; a.part_o = None
+    s = ctypes.c_int32(0)
+    rc = L.attn_decode(ctypes.byref(a), FAKE, K.KVQ_BF16, None, None, None, ctypes.byref(s), None)
+    assert rc == 1 and "part_o" in K.kvq_last_error()
+    a = _mla_args(K); a.num_splits = 1; a.part_capacity = 0
+    rc = L.attn_decode(ctypes.byref(a), FAKE, K.KVQ_BF16, None, None, None, ctypes.byref(s), None)
+    assert rc == 4
+    a = _mla_args(K); a.num_splits = 1; a.part_lse = FAKE_ODD
+    rc = L.attn_decode(ctypes.byref(a), FAKE, K.KVQ_BF16, None, None, None, ctypes.byref(s), None)
+    assert rc == 3
+
+
+def test_decode_workspace_bytes(K):
+    # part_o [B][Hq][s][Dv] + part_lse [B][Hq][s], float32
+    assert K.kvq_decode_workspace_bytes(2, 32, 128, 16) == 2 * 32 * 16 * 129 * 4
+    assert K.kvq_decode_workspace_bytes(32, 16, 512, 16) == 32 * 16 * 16 * 513 * 4
+    assert K.kvq_decode_workspace_bytes(0, 32, 128, 16) == 0
+    assert K.kvq_decode_workspace_bytes(2, 32, 128, 0) == 0
+    import torch
+    po, pl = K.decode_workspace(2, 4, 8, 3, "cpu")
+    assert po.numel() == 2 * 4 * 3 * 8 and pl.numel() == 2 * 4 * 3
+    assert pl.data_ptr() == po.data_ptr() + po.numel() * 4
+
+
+def test_binding_rejects_unreadable_views(K):
+    """The binding refuses query views whose last dim is strided and MLA
+    latent planes that are not in the row layout (the kernels read neither)."""
+    import torch
+    B, H, Dc, Dr, Lm = 1, 16, 512, 64, 64
+    lens = torch.full((B,), Lm, dtype=torch.int32)
+    lat = K.NVFP4Plane(torch.zeros(B, Lm, Dc // 2, dtype=torch.uint8), torch.zeros(B, Lm, Dc // 16, dtype=torch.uint8),
+                       torch.ones(1), K.KVQ_PLANE_ROWS)
+    q_c = torch.zeros(B, H, Dc, dtype=torch.bfloat16)
+    q_r = torch.zeros(B, H, Dr, dtype=torch.bfloat16)
+    k_r = torch.zeros(B, Lm, Dr, dtype=torch.bfloat16)
+    po, pl = K.decode_workspace(B, H, Dc, 4, "cpu")
+    K.make_decode_args(q_c, lat, None, lens, max_kv_len=Lm, num_splits=4, part_o=po, part_lse=pl, q_rope=q_r,
+                       k_rope=k_r)
+    with pytest.raises(ValueError):
+        K.make_decode_args(torch.zeros(B, Dc, H, dtype=torch.bfloat16).transpose(1, 2), lat, None, lens,
+                           max_kv_len=Lm, num_splits=4, part_o=po, part_lse=pl, q_rope=q_r, k_rope=k_r)
+    with pytest.raises(ValueError):
+        K.make_decode_args(q_c, lat, None, lens, max_kv_len=Lm, num_splits=4, part_o=po, part_lse=pl,
+                           q_rope=torch.zeros(B, Dr, H, dtype=torch.bfloat16).transpose(1, 2), k_rope=k_r)
+    lat4 = K.NVFP4Plane(lat.codes, lat.scales, lat.tensor_scale, K.KVQ_PLANE_TOKEN4)
+    with pytest.raises(ValueError):
+        K.make_decode_args(q_c, lat4, None, lens, max_kv_len=Lm, num_splits=4, part_o=po, part_lse=pl, q_rope=q_r,
+                           k_rope=k_r)
