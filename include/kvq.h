@@ -273,10 +273,15 @@ typedef struct {
   const uint8_t* v_codes;
   const uint8_t* v_scales;
   const float* v_scale;
-  int32_t v_layout;         /* KVQ_PLANE_ROWS or KVQ_PLANE_TOKEN4 (D = 128,
-                               kv_st = 1, kv_sb and kv_sh multiples of 4,
-                               the V planes at least roundup(max_kv_len, 4)
-                               tokens long); K planes are always ROWS     */
+  int32_t v_layout;         /* GQA: KVQ_PLANE_TOKEN4 at D = 128 (kv_st = 1,
+                               kv_sb and kv_sh multiples of 4, the V planes
+                               at least roundup(max_kv_len, 4) tokens
+                               long), KVQ_PLANE_ROWS at D = 64; other
+                               pairings: KVQ_ERR_UNSUPPORTED.  K planes are
+                               always ROWS.  At D = 64 the planes are
+                               contiguous (no block table), there is no
+                               fused append and queries are bf16 or fp32;
+                               fp32 queries need contiguous planes.       */
   const void* k_rope;       /* MLA: device bf16 rope-key rows              */
   int64_t kv_sb, kv_sh, kv_st;
   const int32_t* kv_lens;   /* device int32[B]                             */

@@ -16,7 +16,11 @@ ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "quant_kernels.hip", "decode_gqa.hip", "decode_mla.hip", "combine.hip"]
+SOURCES = ["api.cpp", "quant_kernels.hip", "decode_gqa.hip", "decode_gqa_nvfp4_d128.hip", "decode_gqa_nvfp4_d64.hip",
+           "decode_gqa_fp8_d128.hip", "decode_gqa_fp8_d64.hip", "decode_mla.hip", "combine.hip"]
+# the benchmark's streaming-read probe: its own small library, not part of the C ABI
+PROBE_SOURCE = "probe_read.hip"
+PROBE_LIB_PATH = os.path.join(HERE, "libkvq_probe.so")
 
 ARCH = "gfx950"
 
@@ -52,17 +56,22 @@ def _compile(src, verbose):
 def build(verbose=False) -> str:
     """Compile every HIP source for gfx950 and link libkvq.so; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SOURCE]))
+    _link(objs[:-1], LIB_PATH, verbose)
+    _link(objs[-1:], PROBE_LIB_PATH, verbose)
+    return LIB_PATH
+
+
+def _link(objs, path, verbose):
+    tmp = path + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, path)
 
 
 if __name__ == "__main__":

@@ -384,8 +384,8 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
         return fail(KVQ_ERR_ALIGN, "TOKEN4 V planes need kv_st == 1 and kv_sb, kv_sh multiples of 4");
     }
     const int G = a->Hq / a->Hkv;
-    if (!kvq::gqa_supported(a->kv_format, G, a->D, a->q_dtype))
-      return fail(KVQ_ERR_UNSUPPORTED, "GQA decode: G=%d, D=%d not supported (G in 1,2,4,8,16; D in 64,128)", G, a->D);
+    if (const char* why = kvq::gqa_unsupported(*a))
+      return fail(KVQ_ERR_UNSUPPORTED, "GQA decode (G=%d, D=%d): %s", G, a->D, why);
     if (a->block_table != nullptr) {   // paged cache
       const int tile = kvq::gqa_tile_tokens(G);
       if (a->block_size <= 0 || a->block_size % tile != 0 || (a->block_size & (a->block_size - 1)) != 0)

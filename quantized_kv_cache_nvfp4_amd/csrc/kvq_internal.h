@@ -68,8 +68,10 @@ int gqa_tile_tokens(int G);
 int mla_tile_tokens();
 constexpr int kPagedMaxChunkBlocks = 2048;   // block-table entries one work-group keeps (LDS)
 constexpr int kMlaPagedMaxChunkBlocks = 512;  // the same for the MLA kernel (two work-groups per CU share the LDS)
-// is (format, G, D, q dtype) implemented by the GQA kernel
-bool gqa_supported(int kv_format, int G, int D, int q_dtype);
+// null if the GQA kernel implements this combination of format, query
+// group, head_dim, query type, V layout, paging and fused append; otherwise
+// the reason it does not
+const char* gqa_unsupported(const kvq_decode_args& a);
 // is the MLA configuration implemented (NVFP4 latent 512 + rope 64, 16 heads, bf16 queries)
 bool mla_supported(const kvq_decode_args& a);
 

@@ -133,10 +133,13 @@ def empty_plane(fmt, shape_lead, D, layout, fill=0xFF):
                        torch.empty(1, dtype=torch.float32, device=DEV), layout)
 
 
-def gpu_pack(inp, fmt, v_layout=0):
-    """K in the row layout; V in v_layout (TOKEN4 planes are padded to a
-    multiple of 4 tokens and the padding holds 0xFF bytes)."""
+def gpu_pack(inp, fmt, v_layout=None, fill=0xFF):
+    """K in the row layout; V in v_layout, by default the one the decode
+    kernel reads at this head_dim (TOKEN4 at 128, rows at 64; TOKEN4 planes
+    are padded to a multiple of 4 tokens and the padding holds 0xFF bytes)."""
     k_ = K()
+    if v_layout is None:
+        v_layout = k_.KVQ_PLANE_TOKEN4 if inp.D == 128 else k_.KVQ_PLANE_ROWS
     k, v = inp.k.to(DEV), inp.v.to(DEV)
     lens = torch.from_numpy(inp.kv_lens).to(DEV)
     ka, va = k_.kvq_amax(k, lens), k_.kvq_amax(v, lens)
@@ -148,11 +151,47 @@ def gpu_pack(inp, fmt, v_layout=0):
         # both planes padded to a multiple of 4 tokens (shared strides)
         B, H, L, D = v.shape
         Lp = (L + 3) // 4 * 4
-        kp = empty_plane(fmt, (B, H, Lp), D, k_.KVQ_PLANE_ROWS)
+        kp = empty_plane(fmt, (B, H, Lp), D, k_.KVQ_PLANE_ROWS, fill)
         pack(k, ka, out=kp)
-        vp = empty_plane(fmt, (B, H, Lp), D, v_layout)
+        vp = empty_plane(fmt, (B, H, Lp), D, v_layout, fill)
         pack(v, va, out=vp)
     return kp, vp, ka, va, lens
+
+
+def page_plane(plane, bs, perm_seed, lens=None):
+    """Paged copy of a contiguous plane [B, H, Lp, .] (codes and, for NVFP4,
+    scales): blocks of bs tokens at physical blocks given by a seeded
+    permutation of B * nb + 3 slots; returns (paged plane, block table).
+    With lens (host ints [B]) the table entries of blocks that lie wholly at
+    or past a request's length point at the spare slots, which hold 0xFF
+    bytes (NaN E4M3 scales): the decode may read those entries but must not
+    use them, and a read through one would show in the output."""
+    k_ = K()
+    B, H, Lp = plane.codes.shape[:3]
+    nb = (Lp + bs - 1) // bs
+    nphys = B * nb + 3
+    full = np.random.default_rng(perm_seed).permutation(nphys)
+    perm = full[: B * nb].reshape(B, nb).astype(np.int32)
+    used = [nb] * B
+    if lens is not None:
+        spare = full[B * nb:]
+        for b in range(B):
+            used[b] = (int(lens[b]) + bs - 1) // bs
+            perm[b, used[b]:] = spare[np.arange(nb - used[b]) % len(spare)]
+
+    def pg(t):
+        out = torch.full((nphys, H, bs) + tuple(t.shape[3:]), 0xFF, dtype=t.dtype, device=DEV)
+        for b in range(B):
+            for j in range(used[b]):
+                n = min(bs, Lp - j * bs)
+                out[int(perm[b, j]), :, :n] = t[b, :, j * bs: j * bs + n]
+        return out
+
+    if isinstance(plane, k_.NVFP4Plane):
+        paged = k_.NVFP4Plane(pg(plane.codes), pg(plane.scales), plane.tensor_scale, plane.layout)
+    else:
+        paged = k_.FP8Plane(pg(plane.codes), plane.scale, plane.layout)
+    return paged, torch.from_numpy(perm).to(DEV)
 
 
 def gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.bfloat16, out_scale=None, with_lse=False, fused=False,

@@ -129,6 +129,7 @@ def _good_args(K):
     a.v_codes = a.v_scales = a.v_scale = FAKE
     a.kv_lens = FAKE
     a.kv_sb, a.kv_sh, a.kv_st = 8 * 1024, 1024, 1
+    a.v_layout = K.KVQ_PLANE_TOKEN4
     a.softmax_scale = 0.088
     a.num_splits = 4
     a.part_o = a.part_lse = FAKE
@@ -166,6 +167,14 @@ def test_decode_validation(L, K):
     assert _decode_rc(L, a) == 1
     a = _good_args(K); a.v_layout = K.KVQ_PLANE_TOKEN4; a.D = a.Dv = 64
     assert _decode_rc(L, a) == 2                     # TOKEN4 V needs D = 128
+    a = _good_args(K); a.v_layout = K.KVQ_PLANE_ROWS
+    assert _decode_rc(L, a) == 2 and "TOKEN4" in K.kvq_last_error()   # D = 128 V is TOKEN4
+    a = _good_args(K); a.v_layout = K.KVQ_PLANE_ROWS; a.D = a.Dv = 64
+    a.block_table, a.block_size, a.bt_stride, a.kv_sblk = FAKE, 64, 16, 512
+    assert _decode_rc(L, a) == 2 and "paged" in K.kvq_last_error()    # D = 64: contiguous planes only
+    a = _good_args(K); a.q_dtype = K.KVQ_F32
+    a.block_table, a.block_size, a.bt_stride, a.kv_sblk = FAKE, 64, 16, 512
+    assert _decode_rc(L, a) == 2 and "fp32" in K.kvq_last_error()     # fp32 queries: contiguous planes
     a = _good_args(K); a.v_layout = K.KVQ_PLANE_TOKEN4; a.kv_st = 2
     assert _decode_rc(L, a) == 3
     a = _good_args(K); a.v_layout = 5

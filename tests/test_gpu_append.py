@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import DEV, K, announce, assert_bf16_output, gpu_pack, make_inputs, oracle_gqa
+from gpu_helpers import DEV, K, announce, assert_bf16_output, gpu_pack, make_inputs, oracle_gqa, page_plane
 
 pytestmark = pytest.mark.gpu
 
@@ -27,42 +27,20 @@ def _clone(p):
     return k_.FP8Plane(p.codes.clone(), p.scale.clone(), p.layout)
 
 
-def _page(plane, bs, seed):
-    """Paged copy [B * nb + 2, H, bs, .] of a contiguous plane and its table."""
-    k_ = K()
-    B, H, Lp = plane.codes.shape[:3]
-    nb = (Lp + bs - 1) // bs
-    nphys = B * nb + 2
-    perm = np.random.default_rng(seed).permutation(nphys)[: B * nb].reshape(B, nb).astype(np.int32)
-
-    def pg(t):
-        out = torch.zeros((nphys, H, bs) + tuple(t.shape[3:]), dtype=t.dtype, device=DEV)
-        for b in range(B):
-            for j in range(nb):
-                n = min(bs, Lp - j * bs)
-                out[int(perm[b, j]), :, :n] = t[b, :, j * bs: j * bs + n]
-        return out
-
-    if isinstance(plane, k_.NVFP4Plane):
-        return k_.NVFP4Plane(pg(plane.codes), pg(plane.scales), plane.tensor_scale, plane.layout), \
-            torch.from_numpy(perm).to(DEV)
-    return k_.FP8Plane(pg(plane.codes), plane.scale, plane.layout), torch.from_numpy(perm).to(DEV)
-
-
 FP8_KEY = ("fp8", "custom", 3, 32, 8, 128, (200, 513, 64), "bf16")   # ragged, FP8 planes
 
 CASES = [
     # (key, format, v_layout, splits, fused, paged block size or 0, per-head FP8 scales)
     (("nvfp4", "gqa", 1024), "nvfp4", 1, 3, False, 0, False),
     (("nvfp4", "gqa", 1024), "nvfp4", 1, 0, True, 0, False),
-    (("nvfp4", "gqa", 1024), "nvfp4", 0, 4, True, 0, False),
+    (("nvfp4", "gqa", 1024), "nvfp4", 1, 4, True, 0, False),
     (("nvfp4", "gqa", 1024), "nvfp4", 1, 2, True, 64, False),
     (FP8_KEY, "fp8", 1, 2, False, 0, False),
-    (FP8_KEY, "fp8", 0, 0, True, 0, True),
+    (FP8_KEY, "fp8", 1, 0, True, 0, True),
     (FP8_KEY, "fp8", 1, 1, True, 64, True),
-    (("nvfp4", "mha", 1024, 2, 16), "nvfp4", 0, 2, False, 0, False),                        # G = 1
+    (("nvfp4", "mha", 1024, 2, 16), "nvfp4", 1, 2, False, 0, False),                        # G = 1
     (("nvfp4", "custom", 2, 16, 2, 128, (1, 130), "bf16"), "nvfp4", 1, 2, True, 0, False),  # G = 8, a 1-token request
-    (("nvfp4", "custom", 2, 16, 2, 128, (1, 130), "bf16"), "nvfp4", 0, 1, False, 0, False),
+    (("nvfp4", "custom", 2, 16, 2, 128, (1, 130), "bf16"), "nvfp4", 1, 1, False, 64, False),
 ]
 
 
@@ -103,10 +81,10 @@ def test_decode_with_fused_append(case):
     new_v = torch.stack([v[b, :, lens_np[b] - 1] for b in range(B)]).contiguous()
     bt = None
     if bs:
-        st_k, bt = _page(st_k, bs, 5)
-        st_v, _ = _page(st_v, bs, 5)
-        ref_k, _ = _page(ref_k, bs, 5)
-        ref_v, _ = _page(ref_v, bs, 5)
+        st_k, bt = page_plane(st_k, bs, 5, lens_np)
+        st_v, _ = page_plane(st_v, bs, 5, lens_np)
+        ref_k, _ = page_plane(ref_k, bs, 5, lens_np)
+        ref_v, _ = page_plane(ref_v, bs, 5, lens_np)
     part_o = torch.empty(B * Hq * 64 * D, dtype=torch.float32, device=DEV)
     part_lse = torch.empty(B * Hq * 64, dtype=torch.float32, device=DEV)
     args = k_.make_decode_args(inp.q.to(DEV), st_k, st_v, lens, max_kv_len=inp.Lmax, softmax_scale=inp.softmax_scale,

@@ -7,34 +7,10 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import DEV, K, announce, assert_bf16_output, gpu_decode, gpu_pack, make_inputs, oracle_gqa
+from gpu_helpers import (DEV, K, announce, assert_bf16_output, gpu_decode, gpu_pack, make_inputs, oracle_gqa,
+                         page_plane as _page)
 
 pytestmark = pytest.mark.gpu
-
-
-def _page(plane, bs, perm_seed):
-    """Paged copy of a contiguous plane [B, H, Lp, .] (codes and, for NVFP4,
-    scales): blocks of bs tokens at physical blocks given by a seeded
-    permutation of B * nb + 3 slots; returns (paged plane, block table)."""
-    k_ = K()
-    B, H, Lp = plane.codes.shape[:3]
-    nb = (Lp + bs - 1) // bs
-    nphys = B * nb + 3
-    perm = np.random.default_rng(perm_seed).permutation(nphys)[: B * nb].reshape(B, nb).astype(np.int32)
-
-    def pg(t):
-        out = torch.full((nphys, H, bs) + tuple(t.shape[3:]), 0xFF, dtype=t.dtype, device=DEV)
-        for b in range(B):
-            for j in range(nb):
-                n = min(bs, Lp - j * bs)
-                out[int(perm[b, j]), :, :n] = t[b, :, j * bs: j * bs + n]
-        return out
-
-    if isinstance(plane, k_.NVFP4Plane):
-        paged = k_.NVFP4Plane(pg(plane.codes), pg(plane.scales), plane.tensor_scale, plane.layout)
-    else:
-        paged = k_.FP8Plane(pg(plane.codes), plane.scale, plane.layout)
-    return paged, torch.from_numpy(perm).to(DEV)
 
 
 def _decode(inp, kp, vp, lens, s, block_table=None, fused=False, out_dtype=torch.bfloat16):
@@ -59,14 +35,14 @@ CASES = [
     # (key, v_layout, block_size, splits, fused)
     (("nvfp4", "gqa", 1024), 1, 64, 3, False),
     (("nvfp4", "gqa", 1024), 1, 256, 0, False),
-    (("nvfp4", "gqa", 1024), 0, 128, 1, True),
+    (("nvfp4", "gqa", 1024), 1, 128, 1, True),
     (("nvfp4", "gqa", 1024), 1, 64, 5, True),
     (("fp8", "fp8", 64), 1, 64, 1, False),
-    (("nvfp4", "mha", 1024, 2, 16), 0, 256, 2, False),                        # G = 1: tile 256
-    (("nvfp4", "custom", 2, 16, 2, 128, (300, 77), "bf16"), 0, 32, 4, False),  # G = 8: tile 32
+    (("nvfp4", "mha", 1024, 2, 16), 1, 256, 2, False),                        # G = 1: tile 256
+    (("nvfp4", "custom", 2, 16, 2, 128, (300, 77), "bf16"), 1, 32, 4, False),  # G = 8: tile 32
     # one split over long requests: more than 64 tiles per wave, so the
     # register windows of tile rows are refilled from the LDS table
-    (("nvfp4", "custom", 2, 8, 1, 128, (9000, 8300), "bf16"), 0, 32, 1, False),   # G = 8: 71 tiles per wave
+    (("nvfp4", "custom", 2, 8, 1, 128, (9000, 8300), "bf16"), 1, 32, 1, False),   # G = 8: 71 tiles per wave
     (("nvfp4", "custom", 1, 32, 8, 128, (20000,), "bf16"), 1, 64, 1, True),       # G = 4: 79 tiles per wave
     # the GQA 4:1 32K cache in the launch configuration bench.py times
     # (auto splits, TOKEN4 V, 64-token blocks), two launches and fused
@@ -83,8 +59,8 @@ def test_paged_matches_contiguous(case):
     inp = make_inputs(key)
     kp, vp, _, _, lens = gpu_pack(inp, fmt, v_layout)
     ref = _decode(inp, kp, vp, lens, s, fused=fused)
-    kpp, bt = _page(kp, bs, 1)
-    vpp, bt2 = _page(vp, bs, 1)
+    kpp, bt = _page(kp, bs, 1, inp.kv_lens)
+    vpp, bt2 = _page(vp, bs, 1, inp.kv_lens)
     assert torch.equal(bt, bt2)
     got = _decode(inp, kpp, vpp, lens, s, block_table=bt, fused=fused)
     assert torch.equal(got, ref), "paged and contiguous planes must decode to identical bits"
@@ -108,10 +84,10 @@ def test_paged_rejects_small_blocks():
 FP8P_CASES = [
     # (key, v_layout, block_size, splits, fused)
     (("nvfp4", "gqa", 1024), 1, 64, 3, False),
-    (("nvfp4", "gqa", 1024), 0, 128, 0, True),
+    (("nvfp4", "gqa", 1024), 1, 128, 0, True),
     (("fp8", "fp8", 64), 1, 64, 2, False),
-    (("nvfp4", "custom", 2, 16, 2, 128, (300, 77), "bf16"), 0, 32, 4, False),   # G = 8: tile 32
-    (("nvfp4", "custom", 2, 8, 1, 128, (9000, 8300), "bf16"), 0, 32, 1, False),   # windows refilled
+    (("nvfp4", "custom", 2, 16, 2, 128, (300, 77), "bf16"), 1, 32, 4, False),   # G = 8: tile 32
+    (("nvfp4", "custom", 2, 8, 1, 128, (9000, 8300), "bf16"), 1, 32, 1, False),   # windows refilled
 ]
 
 
@@ -128,8 +104,8 @@ def test_paged_fp8p_matches_contiguous(case):
     ps = float(np.float32(1.0 / 448.0))
     ref, used, ref_lse = gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.float32, with_lse=True, fused=fused,
                                     prob_scale=ps)
-    kpp, bt = _page(kp, bs, 4)
-    vpp, bt2 = _page(vp, bs, 4)
+    kpp, bt = _page(kp, bs, 4, inp.kv_lens)
+    vpp, bt2 = _page(vp, bs, 4, inp.kv_lens)
     assert torch.equal(bt, bt2)
     got, used_p, lse = gpu_decode(inp, kpp, vpp, lens, s, out_dtype=torch.float32, with_lse=True, fused=fused,
                                   prob_scale=ps, block_table=bt)

@@ -41,10 +41,10 @@ CASES = [
     # (key, kv format, v_layout, splits, fused, per_head)
     (("nvfp4", "gqa", 1024), "nvfp4", 1, 3, False, False),
     (("nvfp4", "gqa", 1024), "nvfp4", 1, 0, True, True),
-    (("fp8", "fp8", 64), "fp8", 0, 2, False, False),
+    (("fp8", "fp8", 64), "fp8", 1, 2, False, False),
     (("fp8", "fp8", 64), "fp8", 1, 0, True, True),
-    (("nvfp4", "mha", 1024, 2, 16), "nvfp4", 0, 2, False, True),                       # G = 1
-    (("nvfp4", "custom", 2, 16, 2, 128, (300, 77), "bf16"), "nvfp4", 0, 4, False, True),  # G = 8
+    (("nvfp4", "mha", 1024, 2, 16), "nvfp4", 1, 2, False, True),                       # G = 1
+    (("nvfp4", "custom", 2, 16, 2, 128, (300, 77), "bf16"), "nvfp4", 1, 4, False, True),  # G = 8
 ]
 
 
