@@ -47,7 +47,7 @@ def test_tiny_fp32_path(s):
     assert np.abs(lse.cpu().double().numpy() - lse_ref).max() <= 1e-5
 
 
-GQA_CASES = [(L, s) for L in (1024, 8192) for s in (1, 2, 4, 8, 0)] + [(32768, s) for s in (1, 8, 0)]
+GQA_CASES = [(L, s) for L in (1024, 8192, 32768) for s in (1, 2, 4, 8, 0)]
 
 
 @pytest.mark.parametrize("L,s", GQA_CASES, ids=lambda v: str(v))
@@ -64,7 +64,8 @@ def test_gqa_nvfp4(L, s):
     announce(f"  s={used}: max abs {mae:.2e} max rel {mre:.2e} cos {cos:.6f}")
 
 
-MHA_CASES = [(L, 2, 16, s) for L in (1024, 8192) for s in (1, 4, 0)] + [(32768, 2, 16, 0), (32768, 1, 32, 0)]
+MHA_CASES = ([(L, 2, 16, s) for L in (1024, 8192) for s in (1, 2, 4, 8, 0)] +
+             [(32768, B, H, s) for (B, H) in ((2, 16), (1, 32)) for s in (1, 8, 0)])
 
 
 @pytest.mark.parametrize("L,B,H,s", MHA_CASES, ids=lambda v: str(v))

@@ -111,17 +111,24 @@ def test_mla_empty_request():
     _check_fp32(out[1:], o_ref[1:], o_abs[1:], "mla neighbour of empty")
 
 
-def test_mla_full_config_sampled():
-    """DeepSeek-V2 per-rank shape, B = 32, kv 8192, auto splits: the GPU output
-    of 3 requests checked against the oracle run on those requests alone."""
-    announce("mla full config")
+@functools.lru_cache(maxsize=1)
+def _full_inputs():
     inp = kvq_synth.mla()   # B=32, L=8192
-    plane, amax_g, out, _, used = _gpu(inp, 0, torch.bfloat16)
-    assert used >= 1
     cf = kvq_synth.f64(inp.c)
-    amax = OQ.amax(cf[:, None], inp.kv_lens)
+    return inp, cf, OQ.amax(cf[:, None], inp.kv_lens)
+
+
+@pytest.mark.parametrize("s", [0, 1, 4, 8])
+def test_mla_full_config_sampled(s):
+    """DeepSeek-V2 per-rank shape, B = 32, kv 8192, explicit and auto splits:
+    the GPU output of 8 requests checked against the oracle run on those
+    requests alone."""
+    announce(f"mla full config s={s}")
+    inp, cf, amax = _full_inputs()
+    plane, amax_g, out, _, used = _gpu(inp, s, torch.bfloat16)
+    assert used >= 1 and (s == 0 or used == s)
     assert float(amax_g.item()) == amax
-    for b in (0, 17, 31):
+    for b in range(0, 32, 4) if s else (0, 7, 17, 22, 31):
         codes, scales, st = OQ.nvfp4_pack(cf[b:b + 1], amax)
         assert np.array_equal(_np(plane.codes)[b:b + 1], codes)
         chat = OQ.nvfp4_unpack(codes, scales, st)
