@@ -423,6 +423,29 @@ int attn_decode(const kvq_decode_args* args, void* out, int32_t out_dtype, const
                 int32_t* counters, int32_t* splits_used, void* stream);
 
 /*
+ * attn_decode_noalloc - attn_decode for callers that cannot allocate memory
+ * or pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the split partials and the merge
+ * counters live in a static device array of the library, one per GPU, of
+ * KVQ_NOALLOC_SCRATCH_BYTES (held until the process ends).  The call
+ * allocates nothing.  Arguments and results as attn_decode (same kernels,
+ * same bits); args->part_o, part_lse, part_capacity and p_scratch are
+ * ignored.  Limits: the partials, B * Hq * s' * (Dv + 1) * 4 bytes with s'
+ * = s (s + 1 with a fused append), must fit in KVQ_NOALLOC_SCRATCH_BYTES -
+ * 64 KiB, and B * Hkv <= 16384: otherwise KVQ_ERR_WORKSPACE, nothing
+ * launched.  FP8 probabilities (quantize_p) need a score scratch of the
+ * sequence's size and are refused (KVQ_ERR_UNSUPPORTED).  The first call on
+ * a device looks the array up (hipGetSymbolAddress) and clears its counters
+ * with a kernel on `stream`; every completed call leaves them zero.  All
+ * calls on one GPU share its array, which keeps the last call's partials:
+ * calls that overlap on a GPU (other streams or threads) race; calls on one
+ * stream are ordered and safe.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (24u << 20)
+int attn_decode_noalloc(const kvq_decode_args* args, void* out, int32_t out_dtype, const float* out_scale,
+                        float* lse_out, int32_t* splits_used, void* stream);
+
+/*
  * kvq_auto_num_splits - split count when the caller passes num_splits <= 0
  * (Model-Optimizer PR #1832, Testing section: the built-in heuristic picks s
  * from the compute-unit count and batch x heads).  Host-only, no device

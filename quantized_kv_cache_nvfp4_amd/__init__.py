@@ -23,7 +23,7 @@ from ._lib import (KVQ_BF16, KVQ_F16, KVQ_F32, KVQ_FP8E4M3, KVQ_LAYOUT_GQA, KVQ_
 
 __all__ = [
     "kvq_amax", "kvq_pack_nvfp4", "kvq_pack_fp8", "kvq_unpack_nvfp4", "kvq_unpack_fp8",
-    "attn_decode_splitkv", "attn_decode_combine", "attn_decode", "kvq_auto_num_splits", "kvq_device_cu_count",
+    "attn_decode_splitkv", "attn_decode_combine", "attn_decode", "attn_decode_noalloc", "kvq_auto_num_splits", "kvq_device_cu_count",
     "kvq_fp8p_scratch_floats", "kvq_decode_workspace_bytes", "decode_workspace", "kvq_last_error", "kvq_version", "NVFP4Plane", "FP8Plane", "KvqError",
     "KVQ_F32", "KVQ_BF16", "KVQ_F16", "KVQ_FP8E4M3", "KVQ_NVFP4", "KVQ_LAYOUT_GQA", "KVQ_LAYOUT_MLA",
     "KVQ_PLANE_ROWS", "KVQ_PLANE_TOKEN4", "make_decode_args",
@@ -369,4 +369,16 @@ def attn_decode(args: KvqDecodeArgs, out, out_scale=None, lse_out=None, counters
     s = ctypes.c_int32(0)
     check(_lib.lib().attn_decode(ctypes.byref(args), _ptr(out), odt, _ptr(out_scale), _ptr(lse_out), _ptr(counters),
                                  ctypes.byref(s), _stream(stream)))
+    return s.value
+
+
+def attn_decode_noalloc(args: KvqDecodeArgs, out, out_scale=None, lse_out=None, stream=None) -> int:
+    """attn_decode with the partials and merge counters in the library's
+    static per-GPU scratch (no allocation, no workspace: the part_o /
+    part_lse fields of args are ignored).  Calls that overlap on one GPU
+    race.  Returns the number of partials merged per head."""
+    odt = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16, torch.uint8: KVQ_FP8E4M3}[out.dtype]
+    s = ctypes.c_int32(0)
+    check(_lib.lib().attn_decode_noalloc(ctypes.byref(args), _ptr(out), odt, _ptr(out_scale), _ptr(lse_out),
+                                         ctypes.byref(s), _stream(stream)))
     return s.value

@@ -30,6 +30,7 @@ class KvqPackJob(ctypes.Structure):
 
 
 KVQ_MAX_PACK_JOBS = 8
+KVQ_NOALLOC_SCRATCH_BYTES = 24 << 20
 
 
 class KvqDecodeArgs(ctypes.Structure):
@@ -78,6 +79,7 @@ _PROTOS = {
     "attn_decode_splitkv": (ctypes.c_int, [ctypes.POINTER(KvqDecodeArgs), ctypes.POINTER(_I32), _VP]),
     "attn_decode_combine": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _I32, _VP, _VP, _VP]),
     "attn_decode": (ctypes.c_int, [ctypes.POINTER(KvqDecodeArgs), _VP, _I32, _VP, _VP, _VP, ctypes.POINTER(_I32), _VP]),
+    "attn_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(KvqDecodeArgs), _VP, _I32, _VP, _VP, ctypes.POINTER(_I32), _VP]),
     "kvq_auto_num_splits": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_I32)]),
     "kvq_device_cu_count": (ctypes.c_int, [ctypes.POINTER(_I32)]),
     "kvq_fp8p_scratch_floats": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),

@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "kvq_internal.h"
@@ -507,3 +508,83 @@ int attn_decode_combine(const float* part_o, const float* part_lse, int32_t B, i
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ no-allocation entry
+// For callers that cannot allocate or pass a workspace: the partials and the
+// merge counters of attn_decode live in a static device array of this file,
+// one copy per GPU (each device gets its own instance of the code object's
+// globals), looked up once per device with hipGetSymbolAddress.  Layout:
+// [0, 64 KiB) counters of the fused merge (zero at load, cleared once more by
+// a kernel at the first call on a device, and left zero by every completed
+// call), then part_o and part_lse.
+namespace {
+
+constexpr size_t kScratchBytes = KVQ_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void k_zero_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the device address of this GPU's scratch array (set up on first use)
+int scratch_of_current_device(void** out, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "attn_decode_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "attn_decode_noalloc: device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(KVQ_ERR_HIP, "attn_decode_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    constexpr int n = static_cast<int>(kCounterBytes / 4);
+    hipLaunchKernelGGL(k_zero_words, dim3((n + 255) / 256), dim3(256), 0, st, static_cast<uint32_t*>(ptr), n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "attn_decode_noalloc: counter clear: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_decode_noalloc(const kvq_decode_args* args, void* out, int32_t out_dtype, const float* out_scale,
+                                   float* lse_out, int32_t* splits_used, void* stream) {
+  if (args == nullptr) return fail(KVQ_ERR_ARG, "args is null");
+  if (args->quantize_p)
+    return fail(KVQ_ERR_UNSUPPORTED,
+                "attn_decode_noalloc: FP8 probabilities need a score scratch of B*Hq*max_kv_len floats; use attn_decode");
+  void* base = nullptr;
+  int rc = scratch_of_current_device(&base, as_stream(stream));
+  if (rc != KVQ_OK) return rc;
+  uint8_t* const part_base = static_cast<uint8_t*>(base) + kCounterBytes;
+  kvq_decode_args a = *args;
+  a.part_o = reinterpret_cast<float*>(part_base);   // provisional, to resolve the split count
+  a.part_lse = a.part_o;
+  a.part_capacity = 64;
+  a.p_scratch = nullptr;
+  int32_t s = 0;
+  if ((rc = validate_decode(&a, &s, true)) != KVQ_OK) return rc;
+  const size_t np = static_cast<size_t>(s) + (a.new_k != nullptr ? 1 : 0);
+  const size_t n_o = static_cast<size_t>(a.B) * a.Hq * np * a.Dv;
+  const size_t lse_off = (n_o * sizeof(float) + 255) / 256 * 256;
+  const size_t need = lse_off + static_cast<size_t>(a.B) * a.Hq * np * sizeof(float);
+  if (need > kScratchBytes - kCounterBytes)
+    return fail(KVQ_ERR_WORKSPACE,
+                "attn_decode_noalloc: %zu partials per head need %zu bytes, the scratch holds %zu; use fewer splits or "
+                "attn_decode with a workspace", np, need, kScratchBytes - kCounterBytes);
+  if (static_cast<size_t>(a.B) * a.Hkv * sizeof(int32_t) > kCounterBytes)
+    return fail(KVQ_ERR_WORKSPACE, "attn_decode_noalloc: B * Hkv must be <= %zu", kCounterBytes / sizeof(int32_t));
+  a.part_o = reinterpret_cast<float*>(part_base);
+  a.part_lse = reinterpret_cast<float*>(part_base + lse_off);
+  a.part_capacity = static_cast<int32_t>(np);
+  return attn_decode(&a, out, out_dtype, out_scale, lse_out, static_cast<int32_t*>(base), splits_used, stream);
+}
