@@ -182,3 +182,31 @@ def decode_gqa_fp8p(q, k, v, kv_lens, softmax_scale, prob_scale):
 def fp8_output(o, out_scale):
     """E4M3 codes of o / out_scale (saturating, RNE)."""
     return F.e4m3_encode(np.asarray(o, np.float64) / np.float64(out_scale))
+
+
+def prefill_gqa(q, k, v, kv_lens, softmax_scale):
+    """Chunked prefill over the (dequantized) cache: the Sq query tokens of
+    request b are its last Sq positions, p_i = kv_lens[b] - Sq + i, and query
+    i attends causally to the cached tokens t <= p_i (the chunk's own tokens
+    are in the cache already).  A query with p_i < 0 sees nothing: o = 0,
+    lse = -inf.  GQA head mapping as decode_gqa.
+
+    q: [B, Sq, Hq, D]; k: [B, Hkv, Lmax, D]; v: [B, Hkv, Lmax, Dv] (float64).
+    Returns (o [B, Sq, Hq, Dv], lse [B, Sq, Hq])."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, Sq, Hq, _ = q.shape
+    G = Hq // k.shape[1]
+    o = np.zeros((B, Sq, Hq, v.shape[-1]))
+    lse = np.full((B, Sq, Hq), -math.inf)
+    for b in range(B):
+        for i in range(Sq):
+            n = int(kv_lens[b]) - Sq + i + 1   # keys 0 .. p_i
+            if n <= 0:
+                continue
+            for h in range(Hq):
+                s = softmax_scale * (k[b, h // G, :n] @ q[b, i, h])
+                p, lse[b, i, h] = _softmax_stats(s)
+                o[b, i, h] = p @ v[b, h // G, :n]
+    return o, lse

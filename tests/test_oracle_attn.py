@@ -239,3 +239,54 @@ def test_fp8_probabilities_closed_form_four_heads_per_kv_head():
     np.testing.assert_allclose(o[0, 5], (26.0 * V1[0] + 416.0 * V1[1]) / 448.0, rtol=1e-14, atol=1e-15)
     for h in (6, 7):
         np.testing.assert_allclose(o[0, h], (144.0 / 448.0) * V1.sum(0), rtol=1e-14, atol=1e-15)
+
+
+# ---- chunked prefill -------------------------------------------------------
+def test_prefill_matches_torch_sdpa_with_causal_offset_mask():
+    # library routine: SDPA in float64 with an explicit boolean mask in which
+    # query i of the chunk sees keys t <= L - Sq + i (keys repeat-interleaved by G)
+    B, Sq, Hq, Hkv, D = 2, 5, 8, 2, 16
+    q = _rand((B, Sq, Hq, D), 70)
+    k = _rand((B, Hkv, 23, D), 71)
+    v = _rand((B, Hkv, 23, D), 72)
+    lens = [23, 9]
+    alpha = 0.21
+    o, lse = A.prefill_gqa(q, k, v, lens, alpha)
+    G = Hq // Hkv
+    for b, L in enumerate(lens):
+        kt = torch.from_numpy(k[b:b + 1, :, :L]).repeat_interleave(G, dim=1)
+        vt = torch.from_numpy(v[b:b + 1, :, :L]).repeat_interleave(G, dim=1)
+        qt = torch.from_numpy(q[b:b + 1]).transpose(1, 2)   # [1, Hq, Sq, D]
+        mask = torch.arange(L)[None, :] <= (L - Sq + torch.arange(Sq))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=alpha)
+        np.testing.assert_allclose(o[b], ref[0].transpose(0, 1).numpy(), rtol=1e-12, atol=1e-13)
+    assert np.all(np.isfinite(lse))
+
+
+def test_prefill_full_causal_is_sdpa_is_causal():
+    # Sq = L: ordinary causal self-attention (torch's is_causal)
+    B, Sq, H, D = 1, 12, 4, 8
+    q = _rand((B, Sq, H, D), 73)
+    k = _rand((B, H, Sq, D), 74)
+    v = _rand((B, H, Sq, D), 75)
+    o, _ = A.prefill_gqa(q, k, v, [Sq], 0.4)
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q).transpose(1, 2), torch.from_numpy(k),
+                                                           torch.from_numpy(v), is_causal=True, scale=0.4)
+    np.testing.assert_allclose(o, ref.transpose(1, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_rows_reduce_to_decode():
+    # query i is the decode of the cache truncated to p_i + 1 tokens (decode_gqa
+    # is pinned above); the first query of a chunk longer than the cache sees nothing
+    B, Sq, Hq, Hkv, D = 1, 4, 4, 1, 8
+    q = _rand((B, Sq, Hq, D), 76)
+    k = _rand((B, Hkv, 6, D), 77)
+    v = _rand((B, Hkv, 6, D), 78)
+    o, lse = A.prefill_gqa(q, k, v, [6], 0.3)
+    for i in range(Sq):
+        od, ld = A.decode_gqa(q[:, i], k, v, [6 - Sq + i + 1], 0.3)
+        np.testing.assert_array_equal(o[:, i], od)
+        np.testing.assert_array_equal(lse[:, i], ld)
+    o2, l2 = A.prefill_gqa(q, k, v, [2], 0.3)   # p_i = 2 - 4 + i: queries 0, 1 see nothing
+    assert np.all(o2[:, :2] == 0) and np.all(np.isneginf(l2[:, :2]))
+    np.testing.assert_allclose(o2[0, 2], np.repeat(v[0, :, 0], 4, axis=0), rtol=0, atol=0)   # one key: o = v_0
