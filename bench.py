@@ -83,20 +83,20 @@ def log(msg):
 
 # ------------------------------------------------------------------ traffic
 CSRC = os.path.join(ROOT, "quantized_kv_cache_nvfp4_amd", "csrc")
-TRAFFIC = {   # committed counter summaries and the kernel source they were taken from
+TRAFFIC = {   # committed counter summaries and the kernel sources they were taken from (launch + instantiation)
     "gqa": (os.path.join(ROOT, "profiles", "k_decode_gqa_nvfp4_b2_hq32_hkv8_d128_kv32k_traffic.txt"),
-            os.path.join(CSRC, "decode_gqa.hip")),
+            (os.path.join(CSRC, "decode_gqa.hip"), os.path.join(CSRC, "decode_gqa_nvfp4_d128.hip"))),
     "mla": (os.path.join(ROOT, "profiles", "k_decode_mla_nvfp4_b32_h16_c512_r64_kv8k_traffic.txt"),
-            os.path.join(CSRC, "decode_mla.hip")),
+            (os.path.join(CSRC, "decode_mla.hip"),)),
     "fp8": (os.path.join(ROOT, "profiles", "k_decode_gqa_fp8_b64_hq32_hkv8_d128_ragged_traffic.txt"),
-            os.path.join(CSRC, "decode_gqa.hip")),
+            (os.path.join(CSRC, "decode_gqa.hip"), os.path.join(CSRC, "decode_gqa_fp8_d128.hip"))),
 }
 
 
-def source_closure(path):
-    """The kernel source and every file it includes with #include "..."
+def source_closure(paths):
+    """The kernel sources and every file they include with #include "..."
     (recursively), sorted: what the compiled kernel depends on here."""
-    seen, todo = set(), [os.path.abspath(path)]
+    seen, todo = set(), [os.path.abspath(p) for p in paths]
     while todo:
         p = todo.pop()
         if p in seen or not os.path.exists(p):
