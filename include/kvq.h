@@ -499,6 +499,76 @@ size_t kvq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Dv, int32_t s);
  */
 size_t kvq_fp8p_scratch_floats(int32_t B, int32_t Hq, int32_t s, int32_t max_kv_len);
 
+/*
+ * Chunked prefill over the packed cache (Model-Optimizer PR #1832 "Add
+ * quant+sparse attention for vLLM serving", Testing section: the prefill
+ * path timed in the "prefill" column of both decode-latency tables, the
+ * triton_fa.py entry of the coverage report).  A chunk of Sq new query
+ * tokens per request attends to the quantized cache, which already holds
+ * the chunk's own K/V rows (they were packed with kvq_pack_* first): query
+ * i of request b sits at position p_i = kv_lens[b] - Sq + i and sees the
+ * cached tokens t <= p_i (causal); a query with p_i < 0 sees nothing and
+ * gets output 0 and lse -inf.  Scores and dequantization as in decode
+ * (scores softmax_scale * (q . K_t), K_t and V_t dequantized; the tensor
+ * scales in fp32), GQA head mapping h -> h / (Hq / Hkv).
+ *
+ * Layout: q [B][Sq][Hq][D] bf16 with element strides q_sb, q_st, q_sh;
+ * out [B][Sq][Hq][D] with element strides o_sb, o_st, o_sh; lse_out
+ * contiguous [B][Sq][Hq] float32 or NULL.  K planes in the row layout, V
+ * planes in KVQ_PLANE_TOKEN4 (the decode layout at D = 128), plane rows
+ * indexed (request, kv head, token) with strides kv_sb, kv_sh and token
+ * stride 1, at least roundup(max_kv_len, 4) rows per (request, kv head);
+ * or paged (block_table non-NULL; same addressing as kvq_decode_args,
+ * block_size a power of two >= 64; entries are read for the tokens a query
+ * sees, t < kv_lens[b], and must be valid there).  The caller owns every
+ * buffer; the call allocates nothing and keeps no state.
+ */
+typedef struct {
+  int32_t kv_format;         /* KVQ_NVFP4 or KVQ_FP8E4M3                     */
+  int32_t B, Hq, Hkv, D;     /* D = 128; Hq / Hkv in {1, 2, 4, 8}            */
+  int32_t Sq;                /* query tokens per request (>= 0)             */
+  int32_t max_kv_len;        /* upper bound on kv_lens; rows per request    */
+  const void* q;             /* device bf16, 16-byte aligned                */
+  int32_t q_dtype;           /* KVQ_BF16                                    */
+  int64_t q_sb, q_st, q_sh;  /* element strides, multiples of 8             */
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;   /* NVFP4 only                                  */
+  const float* k_scale;      /* device float[1] (float[Hkv] with kv_scale_per_head) */
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  const float* v_scale;
+  int32_t v_layout;          /* KVQ_PLANE_TOKEN4                            */
+  int32_t kv_scale_per_head; /* FP8: 1 = one scale per kv head              */
+  int64_t kv_sb, kv_sh;      /* plane-row strides (multiples of 4)          */
+  const int32_t* kv_lens;    /* device int32[B], cache length incl. the chunk */
+  float softmax_scale;       /* > 0                                         */
+  const int32_t* block_table;/* NULL: contiguous planes                     */
+  int32_t block_size;
+  int64_t bt_stride, kv_sblk;
+  void* out;                 /* device, out_dtype                           */
+  int32_t out_dtype;         /* KVQ_F32 (16-byte aligned) or KVQ_BF16 (8-byte) */
+  int64_t o_sb, o_st, o_sh;  /* element strides, multiples of 4             */
+  float* lse_out;            /* device float[B][Sq][Hq] or NULL             */
+} kvq_prefill_args;
+
+/* sizeof(kvq_prefill_args) as compiled into the library (binding check). */
+size_t kvq_prefill_args_size(void);
+
+/*
+ * attn_prefill - the chunked prefill above, one launch, no workspace.
+ * Both contractions (Q.K^T over head_dim, P.V over tokens) run on the
+ * matrix cores; the softmax is online over 64-token tiles; each query row
+ * sees its keys in one pass (no split, no partials).  Every row of the
+ * planes that a query sees is read; rows at or past kv_lens[b] (at most
+ * max_kv_len) are never used.
+ * Errors (nothing launched): KVQ_ERR_ARG (null pointers, negative sizes,
+ * softmax_scale <= 0, kv_lens bound, block-table geometry),
+ * KVQ_ERR_UNSUPPORTED (D != 128, group width outside {1, 2, 4, 8}, query
+ * dtype, V layout, output dtype), KVQ_ERR_ALIGN (bases or strides off the
+ * alignment above), KVQ_ERR_HIP (launch).
+ */
+int attn_prefill(const kvq_prefill_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

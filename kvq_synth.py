@@ -29,7 +29,7 @@ import torch
 
 BASE_SEED = 20261202
 
-CONFIG_IDS = {"tiny": 1, "gqa": 2, "mha": 3, "fp8": 4, "mla": 5}
+CONFIG_IDS = {"tiny": 1, "gqa": 2, "mha": 3, "fp8": 4, "mla": 5, "prefill": 6}
 
 
 def _streams(config_id, salt=0):
@@ -161,6 +161,60 @@ def mla(L=8192, B=32, H=16, Dc=512, Dr=64, salt=0, kv_lens=None) -> MLAInputs:
                      k_r=_to_dtype(k_r, bf), kv_lens=kv_lens,
                      softmax_scale=float(np.float32(1.0 / np.sqrt(192.0))),
                      name=f"mla_B{B}_H{H}_L{Lmax}")
+
+
+@dataclass
+class PrefillInputs:
+    """Chunked-prefill inputs: a chunk of Sq query tokens per request over a
+    cache whose last Sq rows are the chunk's own keys and values."""
+    q: torch.Tensor            # [B, Sq, Hq, D]
+    k: torch.Tensor            # [B, Hkv, Lmax, D]
+    v: torch.Tensor            # [B, Hkv, Lmax, D]
+    kv_lens: np.ndarray        # [B] int32, cache length including the chunk
+    softmax_scale: float
+    name: str = ""
+
+    @property
+    def B(self):
+        return self.q.shape[0]
+
+    @property
+    def Sq(self):
+        return self.q.shape[1]
+
+    @property
+    def Hq(self):
+        return self.q.shape[2]
+
+    @property
+    def Hkv(self):
+        return self.k.shape[1]
+
+    @property
+    def D(self):
+        return self.q.shape[3]
+
+    @property
+    def Lmax(self):
+        return self.k.shape[2]
+
+
+def prefill_queries(B, Sq, Hq, D, salt=0, dtype=torch.bfloat16) -> torch.Tensor:
+    """A chunk of Sq query tokens per request, N(0, 1) rounded to dtype
+    (the prefill config's own stream)."""
+    rq = _streams(CONFIG_IDS["prefill"], salt)[0]
+    return _to_dtype(rq.standard_normal((B, Sq, Hq, D), dtype=np.float32), dtype)
+
+
+def prefill(B, Hq, Hkv, D, kv_lens, Sq, *, salt=0, outliers=False, Lmax=None) -> PrefillInputs:
+    """Gaussian chunked-prefill inputs (bf16): cache K/V drawn as
+    gqa_inputs draws them (optionally with the 4 x20 outlier channels per kv
+    head) from the prefill config's streams, queries [B, Sq, Hq, D]."""
+    cache = gqa_inputs(B, Hq, Hkv, D, None, kv_lens=kv_lens, config="prefill", salt=salt, outliers=outliers,
+                       Lmax=Lmax)
+    q = prefill_queries(B, Sq, Hq, D, salt=salt + 1000)
+    return PrefillInputs(q=q, k=cache.k, v=cache.v, kv_lens=cache.kv_lens, softmax_scale=cache.softmax_scale,
+                         name=f"prefill_B{B}_Sq{Sq}_Hq{Hq}_Hkv{Hkv}_D{D}_L{cache.Lmax}")
 
 
 def f64(t: torch.Tensor) -> np.ndarray:

@@ -18,15 +18,17 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (KVQ_BF16, KVQ_F16, KVQ_F32, KVQ_FP8E4M3, KVQ_LAYOUT_GQA, KVQ_LAYOUT_MLA, KVQ_NVFP4,
-                   KVQ_PLANE_ROWS, KVQ_PLANE_TOKEN4, KvqError, KvqDecodeArgs, KvqRows, check)
+from ._lib import (KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP,
+                   KVQ_BF16, KVQ_F16, KVQ_F32, KVQ_FP8E4M3, KVQ_LAYOUT_GQA, KVQ_LAYOUT_MLA, KVQ_NVFP4,
+                   KVQ_PLANE_ROWS, KVQ_PLANE_TOKEN4, KvqError, KvqDecodeArgs, KvqPrefillArgs, KvqRows, check)
 
 __all__ = [
     "kvq_amax", "kvq_pack_nvfp4", "kvq_pack_fp8", "kvq_unpack_nvfp4", "kvq_unpack_fp8",
     "attn_decode_splitkv", "attn_decode_combine", "attn_decode", "attn_decode_noalloc", "kvq_auto_num_splits", "kvq_device_cu_count",
     "kvq_fp8p_scratch_floats", "kvq_decode_workspace_bytes", "decode_workspace", "kvq_last_error", "kvq_version", "NVFP4Plane", "FP8Plane", "KvqError",
     "KVQ_F32", "KVQ_BF16", "KVQ_F16", "KVQ_FP8E4M3", "KVQ_NVFP4", "KVQ_LAYOUT_GQA", "KVQ_LAYOUT_MLA",
-    "KVQ_PLANE_ROWS", "KVQ_PLANE_TOKEN4", "make_decode_args",
+    "KVQ_PLANE_ROWS", "KVQ_PLANE_TOKEN4", "make_decode_args", "make_prefill_args", "attn_prefill",
+    "KVQ_OK", "KVQ_ERR_ARG", "KVQ_ERR_UNSUPPORTED", "KVQ_ERR_ALIGN", "KVQ_ERR_WORKSPACE", "KVQ_ERR_HIP",
 ]
 
 _DT = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16, torch.float16: KVQ_F16}
@@ -382,3 +384,70 @@ def attn_decode_noalloc(args: KvqDecodeArgs, out, out_scale=None, lse_out=None, 
     check(_lib.lib().attn_decode_noalloc(ctypes.byref(args), _ptr(out), odt, _ptr(out_scale), _ptr(lse_out),
                                          ctypes.byref(s), _stream(stream)))
     return s.value
+
+
+def make_prefill_args(q, k, v, kv_lens, out, *, max_kv_len, softmax_scale=None, lse_out=None,
+                      block_table=None) -> KvqPrefillArgs:
+    """Fill the C prefill-argument struct from tensors (no device work).
+
+    q [B, Sq, Hq, D] bfloat16 (the chunk's queries; last dim contiguous);
+    k, v NVFP4Plane / FP8Plane with codes [B, Hkv, Lmax, .] (K rows, V
+    TOKEN4), or, with block_table (int32 [B, max_blocks]), paged planes
+    [num_blocks, Hkv, block_size, .]; kv_lens int32 [B] (cache length
+    including the chunk); out [B, Sq, Hq, D] float32 or bfloat16; lse_out
+    float32 [B, Sq, Hq] contiguous or None.
+    """
+    if q.dim() != 4 or (q.shape[-1] > 1 and q.stride(-1) != 1):
+        raise ValueError("q must be [B, Sq, Hq, D] with a contiguous last dim")
+    if out.dim() != 4 or tuple(out.shape) != tuple(q.shape) or (out.shape[-1] > 1 and out.stride(-1) != 1):
+        raise ValueError("out must be [B, Sq, Hq, D] like q, with a contiguous last dim")
+    if q.dtype != torch.bfloat16:
+        raise ValueError("q must be bfloat16")
+    if lse_out is not None and (tuple(lse_out.shape) != tuple(q.shape[:3]) or not lse_out.is_contiguous()
+                                or lse_out.dtype != torch.float32):
+        raise ValueError("lse_out must be a contiguous float32 [B, Sq, Hq] tensor")
+    if k.layout != KVQ_PLANE_ROWS:
+        raise ValueError("K planes are read in the row layout")
+    a = KvqPrefillArgs()
+    fmt = KVQ_NVFP4 if isinstance(k, NVFP4Plane) else KVQ_FP8E4M3
+    B, Sq, Hq, D = q.shape
+    a.kv_format, a.B, a.Hq, a.D, a.Sq = fmt, B, Hq, D, Sq
+    a.Hkv = k.codes.shape[1]
+    row_elems = D // 2 if fmt == KVQ_NVFP4 else D
+    kr, vr = _rows(k.codes, row_elems), _rows(v.codes, row_elems)
+    if (kr.s0, kr.s1, kr.s2) != (vr.s0, vr.s1, vr.s2):
+        raise ValueError("K and V planes must share their row strides")
+    if kr.s2 != 1 and kr.n2 > 1:
+        raise ValueError("planes must have token stride 1")
+    a.kv_sb, a.kv_sh = kr.s0, kr.s1
+    a.v_layout = v.layout
+    if block_table is not None:   # paged planes [num_blocks, Hkv, block_size, .]
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise ValueError("block_table must be an int32 [B, max_blocks] tensor with contiguous rows")
+        a.block_table, a.block_size = _ptr(block_table), int(k.codes.shape[2])
+        a.bt_stride, a.kv_sblk, a.kv_sb = block_table.stride(0), kr.s0, 0
+    a.max_kv_len = int(max_kv_len)
+    a.q, a.q_dtype = _ptr(q), KVQ_BF16
+    a.q_sb, a.q_st, a.q_sh = q.stride(0), q.stride(1), q.stride(2)
+    if fmt == KVQ_NVFP4:
+        a.k_codes, a.k_scales, a.k_scale = _ptr(k.codes), _ptr(k.scales), _ptr(k.tensor_scale)
+        a.v_codes, a.v_scales, a.v_scale = _ptr(v.codes), _ptr(v.scales), _ptr(v.tensor_scale)
+    else:
+        a.k_codes, a.k_scale = _ptr(k.codes), _ptr(k.scale)
+        a.v_codes, a.v_scale = _ptr(v.codes), _ptr(v.scale)
+        per_head = k.scale.numel() > 1 or v.scale.numel() > 1
+        if per_head and not (k.scale.numel() == v.scale.numel() == a.Hkv):
+            raise ValueError(f"per-head FP8 scales must have Hkv = {a.Hkv} entries for K and V")
+        a.kv_scale_per_head = int(per_head)
+    a.kv_lens = _ptr(kv_lens)
+    a.softmax_scale = float(softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(D))
+    a.out, a.out_dtype = _ptr(out), {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}[out.dtype]
+    a.o_sb, a.o_st, a.o_sh = out.stride(0), out.stride(1), out.stride(2)
+    a.lse_out = _ptr(lse_out)
+    a._keep = (q, k, v, kv_lens, out, lse_out, block_table)
+    return a
+
+
+def attn_prefill(args: KvqPrefillArgs, stream=None):
+    """Chunked prefill over the packed cache for prepared args (one launch)."""
+    check(_lib.lib().attn_prefill(ctypes.byref(args), _stream(stream)))

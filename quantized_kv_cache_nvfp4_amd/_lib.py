@@ -62,6 +62,27 @@ class KvqDecodeArgs(ctypes.Structure):
     ]
 
 
+class KvqPrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("kv_format", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("Sq", ctypes.c_int32), ("max_kv_len", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("q_dtype", ctypes.c_int32),
+        ("q_sb", ctypes.c_int64), ("q_st", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("v_layout", ctypes.c_int32), ("kv_scale_per_head", ctypes.c_int32),
+        ("kv_sb", ctypes.c_int64), ("kv_sh", ctypes.c_int64),
+        ("kv_lens", ctypes.c_void_p),
+        ("softmax_scale", ctypes.c_float),
+        ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+        ("bt_stride", ctypes.c_int64), ("kv_sblk", ctypes.c_int64),
+        ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int32),
+        ("o_sb", ctypes.c_int64), ("o_st", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+        ("lse_out", ctypes.c_void_p),
+    ]
+
+
 _VP, _I32, _I64, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 _PROTOS = {
     "kvq_last_error": (ctypes.c_char_p, []),
@@ -85,6 +106,8 @@ _PROTOS = {
     "kvq_fp8p_scratch_floats": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "kvq_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32]),
     "attn_decode_tile_tokens": (_I32, [_I32, _I32]),
+    "kvq_prefill_args_size": (ctypes.c_size_t, []),
+    "attn_prefill": (ctypes.c_int, [ctypes.POINTER(KvqPrefillArgs), _VP]),
 }
 
 _lib = None
@@ -113,6 +136,8 @@ def lib():
             fn.argtypes = args
         if L.kvq_decode_args_size() != ctypes.sizeof(KvqDecodeArgs):
             raise RuntimeError("libkvq.so and this binding disagree on kvq_decode_args; rebuild the library")
+        if L.kvq_prefill_args_size() != ctypes.sizeof(KvqPrefillArgs):
+            raise RuntimeError("libkvq.so and this binding disagree on kvq_prefill_args; rebuild the library")
         _lib = L
     return _lib
 

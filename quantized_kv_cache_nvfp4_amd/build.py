@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(HERE, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "quant_kernels.hip", "decode_gqa.hip", "decode_gqa_nvfp4_d128.hip", "decode_gqa_nvfp4_d64.hip",
-           "decode_gqa_fp8_d128.hip", "decode_gqa_fp8_d64.hip", "decode_mla.hip", "combine.hip"]
+           "decode_gqa_fp8_d128.hip", "decode_gqa_fp8_d64.hip", "decode_mla.hip", "combine.hip",
+           "prefill_gqa.hip"]
 # the benchmark's streaming-read probe: its own small library, not part of the C ABI
 PROBE_SOURCE = "probe_read.hip"
 PROBE_LIB_PATH = os.path.join(HERE, "libkvq_probe.so")

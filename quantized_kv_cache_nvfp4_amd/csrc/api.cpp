@@ -507,6 +507,77 @@ int attn_decode_combine(const float* part_o, const float* part_lse, int32_t B, i
                     "attn_decode_combine launch");
 }
 
+size_t kvq_prefill_args_size(void) { return sizeof(kvq_prefill_args); }
+
+int attn_prefill(const kvq_prefill_args* a, void* stream) {
+  if (a == nullptr) return fail(KVQ_ERR_ARG, "args is null");
+  if (a->kv_format != KVQ_NVFP4 && a->kv_format != KVQ_FP8E4M3)
+    return fail(KVQ_ERR_UNSUPPORTED, "kv_format %d not supported (NVFP4, FP8E4M3)", a->kv_format);
+  if (a->B <= 0 || a->Hq <= 0 || a->Hkv <= 0) return fail(KVQ_ERR_ARG, "B, Hq and Hkv must be positive");
+  if (a->B > 65535 || a->Hkv > 65535) return fail(KVQ_ERR_ARG, "B and Hkv must be <= 65535");
+  if (a->Hq % a->Hkv != 0) return fail(KVQ_ERR_ARG, "Hq (%d) must be a multiple of Hkv (%d)", a->Hq, a->Hkv);
+  const int G = a->Hq / a->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(KVQ_ERR_UNSUPPORTED, "query groups of %d heads are not implemented (1, 2, 4, 8)", G);
+  if (a->D != 128) return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d not implemented (128)", a->D);
+  if (a->Sq < 0 || a->Sq > (1 << 24)) return fail(KVQ_ERR_ARG, "Sq must be in [0, 2^24]");
+  if (a->max_kv_len < 0) return fail(KVQ_ERR_ARG, "max_kv_len must be >= 0");
+  if (a->k_codes == nullptr || a->v_codes == nullptr || a->k_scale == nullptr || a->v_scale == nullptr ||
+      a->kv_lens == nullptr || (a->Sq > 0 && (a->q == nullptr || a->out == nullptr)))
+    return fail(KVQ_ERR_ARG, "q, k_codes, v_codes, k_scale, v_scale, kv_lens and out must be non-null");
+  if (a->kv_format == KVQ_NVFP4 && (a->k_scales == nullptr || a->v_scales == nullptr))
+    return fail(KVQ_ERR_ARG, "NVFP4 needs k_scales and v_scales");
+  if (a->q_dtype != KVQ_BF16) return fail(KVQ_ERR_UNSUPPORTED, "q_dtype must be BF16");
+  if (a->v_layout != KVQ_PLANE_TOKEN4) return fail(KVQ_ERR_UNSUPPORTED, "V planes must be in the TOKEN4 layout");
+  if (a->kv_scale_per_head != 0 && (a->kv_scale_per_head != 1 || a->kv_format != KVQ_FP8E4M3))
+    return fail(KVQ_ERR_UNSUPPORTED, "kv_scale_per_head must be 0 or 1, and 1 only for FP8");
+  if (!(a->softmax_scale > 0.0f) || a->softmax_scale != a->softmax_scale || a->softmax_scale > 3.0e38f)
+    return fail(KVQ_ERR_ARG, "softmax_scale must be a positive finite number");
+  if (a->out_dtype != KVQ_F32 && a->out_dtype != KVQ_BF16)
+    return fail(KVQ_ERR_UNSUPPORTED, "out_dtype must be F32 or BF16");
+  if (!aligned(a->q, 16) || a->q_sb % 8 != 0 || a->q_st % 8 != 0 || a->q_sh % 8 != 0)
+    return fail(KVQ_ERR_ALIGN, "q must be 16-byte aligned with q_sb, q_st and q_sh multiples of 8 elements");
+  if (!aligned(a->k_codes, 16) || !aligned(a->v_codes, 16))
+    return fail(KVQ_ERR_ALIGN, "k_codes and v_codes must be 16-byte aligned");
+  if ((a->k_scales != nullptr && !aligned(a->k_scales, 4)) || (a->v_scales != nullptr && !aligned(a->v_scales, 4)))
+    return fail(KVQ_ERR_ALIGN, "k_scales and v_scales must be 4-byte aligned");
+  if (!aligned(a->k_scale, 4) || !aligned(a->v_scale, 4) || !aligned(a->kv_lens, 4))
+    return fail(KVQ_ERR_ALIGN, "k_scale, v_scale and kv_lens must be 4-byte aligned");
+  if (!aligned(a->out, a->out_dtype == KVQ_F32 ? 16 : 8) || a->o_sb % 4 != 0 || a->o_st % 4 != 0 || a->o_sh % 4 != 0)
+    return fail(KVQ_ERR_ALIGN, "out must be %d-byte aligned with o_sb, o_st and o_sh multiples of 4 elements",
+                a->out_dtype == KVQ_F32 ? 16 : 8);
+  if (a->lse_out != nullptr && !aligned(a->lse_out, 4)) return fail(KVQ_ERR_ALIGN, "lse_out must be 4-byte aligned");
+  if (a->kv_sb < 0 || a->kv_sh < 0) return fail(KVQ_ERR_ARG, "cache strides must be >= 0");
+  if (a->kv_sh % 4 != 0 || (a->block_table == nullptr && a->kv_sb % 4 != 0))
+    return fail(KVQ_ERR_ALIGN, "TOKEN4 V planes need kv_sb and kv_sh multiples of 4");
+  int log2_bs = 0;
+  if (a->block_table != nullptr) {
+    if (a->block_size < 64 || (a->block_size & (a->block_size - 1)) != 0)
+      return fail(KVQ_ERR_ARG, "block_size must be a power of two >= 64 (the prefill tile)");
+    const int64_t need = (static_cast<int64_t>(a->max_kv_len) + a->block_size - 1) / a->block_size;
+    if (a->bt_stride < need) return fail(KVQ_ERR_ARG, "bt_stride must cover ceil(max_kv_len / block_size) blocks");
+    if (a->kv_sblk < 0) return fail(KVQ_ERR_ARG, "kv_sblk must be >= 0");
+    if (a->kv_sblk % 4 != 0) return fail(KVQ_ERR_ALIGN, "TOKEN4 V planes need kv_sblk to be a multiple of 4");
+    while ((1 << log2_bs) < a->block_size) ++log2_bs;
+  }
+  if (a->Sq == 0) return ok();
+
+  kvq::PrefillParams p{};
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.q_sb = a->q_sb; p.q_st = a->q_st; p.q_sh = a->q_sh;
+  p.k_codes = a->k_codes; p.k_scales = a->k_scales; p.v_codes = a->v_codes; p.v_scales = a->v_scales;
+  p.k_scale = a->k_scale; p.v_scale = a->v_scale; p.per_head = a->kv_scale_per_head;
+  p.kv_lens = a->kv_lens; p.max_kv_len = a->max_kv_len;
+  p.kv_sb = a->kv_sb; p.kv_sh = a->kv_sh;
+  p.block_table = a->block_table; p.log2_bs = log2_bs; p.bt_stride = a->bt_stride; p.kv_sblk = a->kv_sblk;
+  p.B = a->B; p.Hq = a->Hq; p.Hkv = a->Hkv; p.Sq = a->Sq;
+  p.softmax_scale = a->softmax_scale;
+  p.out = a->out; p.out_dtype = a->out_dtype;
+  p.o_sb = a->o_sb; p.o_st = a->o_st; p.o_sh = a->o_sh;
+  p.lse = a->lse_out;
+  return hip_status(kvq::launch_prefill_gqa(p, a->kv_format, G, as_stream(stream)), "attn_prefill launch");
+}
+
 }  // extern "C"
 
 // ------------------------------------------------------------ no-allocation entry

@@ -75,4 +75,33 @@ const char* gqa_unsupported(const kvq_decode_args& a);
 // is the MLA configuration implemented (NVFP4 latent 512 + rope 64, 16 heads, bf16 queries)
 bool mla_supported(const kvq_decode_args& a);
 
+
+// ---- chunked prefill (prefill_gqa.hip) ----
+// Kernel parameters, from a validated kvq_prefill_args (contiguous or paged
+// planes, K rows, V TOKEN4, head_dim 128, bf16 queries).
+struct PrefillParams {
+  const uint16_t* q;
+  int64_t q_sb, q_st, q_sh;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  const float* k_scale;
+  const float* v_scale;
+  int per_head;
+  const int32_t* kv_lens;
+  int max_kv_len;
+  int64_t kv_sb, kv_sh;
+  const int32_t* block_table;   // null: contiguous planes
+  int log2_bs;
+  int64_t bt_stride, kv_sblk;
+  int B, Hq, Hkv, Sq;
+  float softmax_scale;
+  void* out;
+  int out_dtype;
+  int64_t o_sb, o_st, o_sh;
+  float* lse;
+};
+hipError_t launch_prefill_gqa(const PrefillParams& p, int kv_format, int G, hipStream_t st);
+
 }  // namespace kvq

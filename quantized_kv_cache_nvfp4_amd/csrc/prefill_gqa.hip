@@ -1,0 +1,395 @@
+// Chunked prefill over an NVFP4 or FP8 E4M3 KV cache, GQA / MHA layout, for
+// gfx950 (wave64, MFMA 16x16x32 f16).
+//
+// What it computes: the prefill path the pages time beside their split-KV
+// decode (Model-Optimizer PR #1832 "Add quant+sparse attention for vLLM
+// serving", Testing section: the "prefill" column of both decode-latency
+// tables, and triton_fa.py in the coverage report): attention of a chunk of
+// Sq new query tokens per request over the quantized cache, which already
+// holds the chunk's own K/V rows.  Query i of request b sits at position
+// p_i = kv_len[b] - Sq + i and attends causally to the cached tokens
+// t <= p_i; a query with p_i < 0 sees nothing (output 0, lse -inf).  Cache
+// formats as the decode kernels (Model-Optimizer PR #714 Testing section:
+// NVFP4 = E2M1 codes, E4M3 scale per 16 elements, fp32 tensor scale;
+// compressed-tensors PR #436 kv_cache_scheme: per-tensor FP8 E4M3).
+//
+// Design for CDNA4.  The chunk gives many query rows per kv head, so both
+// contractions are dense and run on MFMA (the decode kernels fill the MFMA
+// columns with tokens because there one query row meets each kv head):
+//  * a work-group of 4 waves owns 128 query rows of one (request, kv head):
+//    128 / G consecutive query tokens x the G heads of the group (row r ->
+//    token r / G, head r % G); each wave owns 32 rows as two 16-row blocks.
+//  * per 64-token KV tile the 256 threads dequantize K and V once into LDS
+//    as f16 (E2M1 or E4M3 -> f16 with the hardware convert, exact; times the
+//    E4M3 block scale, an exact f16 product), two stages so that one
+//    barrier per tile suffices; the raw bytes of the next tile are loaded
+//    into registers before the current tile is computed.
+//  * S^T = K . Q^T: the K tile is the A operand (16 tokens x 32 dims from
+//    LDS), the query rows the B operand (registers, loaded once).  A lane
+//    then holds 4 tokens of one query row, so the row maximum is a local
+//    max and two lane swaps (no LDS), and the same registers, converted to
+//    f16, are the B operand of O^T = V^T . P^T: the order in which the
+//    contraction meets the tokens is free, and V^T is stored in LDS with
+//    its token slots permuted to match.  A lane's output column is again
+//    its query row, so the softmax rescale is a per-lane scalar.
+//  * LDS: K rows of 256 B with a 16-byte-chunk XOR swizzle, V^T rows of
+//    64 token slots padded to 144 B; both conflict-free for the MFMA reads
+//    and the staging writes.  2 x 34 KB per work-group, two work-groups per
+//    CU.
+//  * the per-tensor scales are applied in fp32: s_t,K inside the score
+//    scale, s_t,V at the end.  P enters the second MFMA as f16.
+//  * query blocks are dispatched longest first (the last block of the chunk
+//    sees the most tokens).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "decode_common.h"
+#include "kvq_internal.h"
+#include "wave_reduce.h"
+
+namespace kvq {
+namespace pf {
+
+using namespace dec;
+
+constexpr int kThreads = 256;
+constexpr int kRows = 128;                    // query rows per work-group
+constexpr int kTile = 64;                     // KV tokens per tile
+constexpr int kD = 128;                       // head_dim
+constexpr int kKRow = kD * 2;                 // f16 K row in LDS (bytes)
+constexpr int kKBytes = kTile * kKRow;        // 16 KB
+constexpr int kVtRow = kTile * 2 + 16;        // f16 V^T row of 64 token slots + 16 B of padding
+constexpr int kVtBytes = kD * kVtRow;         // 18 KB
+constexpr int kStage = kKBytes + kVtBytes;
+constexpr int kLdsBytes = 2 * kStage;         // 69,632 B
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// token slot of tile token t in a V^T row: tokens 16u + 4g + e (u = 0..3,
+// g = 0..3, e = 0..3) go to 32 (u / 2) + 8 g + 4 (u % 2) + e, so that the 8
+// tokens a lane of group g holds for 32-token chunk kc (sub-tiles 2kc and
+// 2kc + 1) are the contiguous slots 32 kc + 8 g .. + 7
+__device__ inline int vt_slot(int t) {
+  const int u = t >> 4, g = (t >> 2) & 3, e = t & 3;
+  return 32 * (u >> 1) + 8 * g + 4 * (u & 1) + e;
+}
+
+__device__ inline uint16_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <class T>
+__device__ inline T lds_ld(const uint8_t* p) {
+  return *reinterpret_cast<const T*>(p);
+}
+template <class T>
+__device__ inline void lds_st(uint8_t* p, T v) {
+  *reinterpret_cast<T*>(p) = v;
+}
+
+// One tile's raw bytes in registers (the thread's share).
+template <int KVF>
+struct Raw {
+  static constexpr bool kFp4 = KVF == KVQ_NVFP4;
+  u32x4 k[kFp4 ? 1 : 2];   // K: 32 elements of one token
+  u32x4 v[kFp4 ? 1 : 2];   // V: 8 elements of a 4-token group
+  uint32_t ks;             // NVFP4: the 2 block scales of the K elements
+  uint32_t vs;             // NVFP4: block scale of the V elements, 4 tokens
+};
+
+template <int KVF, int G, bool PAGED>
+__global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
+  constexpr bool kFp4 = KVF == KVQ_NVFP4;
+  constexpr int RB = kFp4 ? kD / 2 : kD;   // code bytes per row
+  constexpr int SB = kD / 16;              // NVFP4 scale bytes per row
+  constexpr int QB = kRows / G;            // query tokens per work-group
+
+  __shared__ __align__(16) uint8_t lds[kLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
+  const int qb = static_cast<int>(gridDim.x) - 1 - static_cast<int>(blockIdx.x);   // longest first
+  const int hk = blockIdx.y, b = blockIdx.z;
+  const int i0 = qb * QB;
+
+  int L = P.kv_lens[b];
+  L = L < 0 ? 0 : (L > P.max_kv_len ? P.max_kv_len : L);
+  const int pos0 = L - P.Sq;                                  // position of query token 0
+  const int i_last = (i0 + QB < P.Sq ? i0 + QB : P.Sq) - 1;   // last query token of the block
+  int n_end = pos0 + i_last + 1;                              // keys [0, n_end) are seen by some row
+  n_end = n_end < 0 ? 0 : (n_end > L ? L : n_end);
+  const int p_min = pos0 + i0;                                // position of the block's first row
+  const int ntiles = (n_end + kTile - 1) / kTile;
+
+  const float ksc = P.k_scale[P.per_head ? hk : 0];
+  const float vsc = P.v_scale[P.per_head ? hk : 0];
+  const float c2 = P.softmax_scale * ksc * kLog2e;   // raw score -> log2 units
+
+  // ---- this lane's query rows: B operand of S^T = K . Q^T, lane (g, c)
+  // holds row c of each block, elements 32 kk + 8 g .. + 7
+  f16x8 qop[2][4];
+  int prow[2];   // key positions <= prow are visible to the lane's row
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = 32 * w + 16 * rb + c;
+    const int qi = i0 + r / G, h = hk * G + r % G;
+    prow[rb] = pos0 + qi;
+    const bool valid = qi < P.Sq;
+    const uint16_t* qp = P.q + b * P.q_sb + static_cast<int64_t>(qi) * P.q_st + h * P.q_sh + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 wv = valid ? *reinterpret_cast<const uint4*>(qp + 32 * kk) : uint4{0, 0, 0, 0};
+      const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+      f16x8 o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {   // bf16 pair -> f16 pair through fp32 (RNE)
+        o[2 * k] = static_cast<_Float16>(__uint_as_float(ws[k] << 16));
+        o[2 * k + 1] = static_cast<_Float16>(__uint_as_float(ws[k] & 0xFFFF0000u));
+      }
+      qop[rb][kk] = o;
+    }
+  }
+
+  // ---- staging roles: K token kt, elements 32 kq .. + 31; V group vq (tokens
+  // 4 vq .. + 3), elements 8 vr .. + 7
+  const int kt = tid >> 2, kq = tid & 3;
+  const int vr = tid >> 4, vq = tid & 15;
+  const int kst_off = kt * kKRow;
+  const int vst_off = (8 * vr) * kVtRow + 2 * vt_slot(4 * vq);
+
+  auto tile_row = [&](int t0) -> int64_t {   // plane row of tile token 0
+    if constexpr (PAGED) {
+      const int blk = P.block_table[b * P.bt_stride + (t0 >> P.log2_bs)];
+      return static_cast<int64_t>(blk) * P.kv_sblk + hk * P.kv_sh + (t0 & ((1 << P.log2_bs) - 1));
+    } else {
+      return b * P.kv_sb + hk * P.kv_sh + t0;
+    }
+  };
+
+  Raw<KVF> raw;
+  auto load = [&](int n) {
+    const int t0 = n * kTile;
+    const int nv = n_end - t0 < kTile ? n_end - t0 : kTile;
+    const int ng = (nv + 3) >> 2;
+    const int64_t row = tile_row(t0);
+    const Rsrc rk = make_rsrc(P.k_codes + row * RB, nv * RB);
+    const Rsrc rv = make_rsrc(P.v_codes + row * RB, ng * 4 * RB);
+    if constexpr (kFp4) {
+      raw.k[0] = ld128(rk, kt * RB + 16 * kq);
+      raw.v[0] = ld128(rv, vq * 4 * RB + 16 * vr);
+      const Rsrc rks = make_rsrc(P.k_scales + row * SB, nv * SB);
+      const Rsrc rvs = make_rsrc(P.v_scales + row * SB, ng * 4 * SB);
+      raw.ks = ld16(rks, kt * SB + 2 * kq);
+      raw.vs = ld32(rvs, vq * 4 * SB + 4 * (vr >> 1));
+    } else {
+      raw.k[0] = ld128(rk, kt * RB + 32 * kq);
+      raw.k[1] = ld128(rk, kt * RB + 32 * kq + 16);
+      raw.v[0] = ld128(rv, vq * 4 * RB + 32 * vr);
+      raw.v[1] = ld128(rv, vq * 4 * RB + 32 * vr + 16);
+    }
+  };
+
+  auto stage = [&](int n, uint8_t* st) {
+    const int nv = n_end - n * kTile;
+    uint8_t* ks_ = st;
+    uint8_t* vs_ = st + kKBytes;
+    // K: 4 chunks of 8 elements, chunk j of row kt at 16 (j ^ (kt & 15))
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f16x8 x;
+      if constexpr (kFp4) {
+        const uint32_t wd = raw.k[0][j];
+        x = cat4(fp4x2<0>(wd), fp4x2<1>(wd), fp4x2<2>(wd), fp4x2<3>(wd));
+        const f16x2 s2 = fp8x2<false>(raw.ks);
+        const _Float16 s = j < 2 ? s2[0] : s2[1];
+        x = x * s;
+      } else {
+        const uint32_t w0 = raw.k[j >> 1][2 * (j & 1)], w1 = raw.k[j >> 1][2 * (j & 1) + 1];
+        x = cat4(fp8x2<false>(w0), fp8x2<true>(w0), fp8x2<false>(w1), fp8x2<true>(w1));
+      }
+      lds_st<f16x8>(ks_ + kst_off + 16 * ((4 * kq + j) ^ (kt & 15)), x);
+    }
+    // V: for each of the 8 elements, the 4 tokens' values (8 bytes) at their
+    // slots in row 8 vr + x; tokens at or past nv are cleared (a group that
+    // straddles the end of the seen keys may hold stale or NaN bytes there)
+    uint32_t m01 = 0xFFFFFFFFu, m23 = 0xFFFFFFFFu;
+    if (4 * vq + 4 > nv) {
+      const int t = 4 * vq;
+      m01 = (t + 0 < nv ? 0x0000FFFFu : 0u) | (t + 1 < nv ? 0xFFFF0000u : 0u);
+      m23 = (t + 2 < nv ? 0x0000FFFFu : 0u) | (t + 3 < nv ? 0xFFFF0000u : 0u);
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      f16x2 lo, hi;   // tokens (0, 1) and (2, 3) of element 8 vr + x
+      if constexpr (kFp4) {
+        const uint32_t wd = raw.v[0][x >> 1];
+        const f16x2 s01 = fp8x2<false>(raw.vs), s23 = fp8x2<true>(raw.vs);
+        if (x & 1) {
+          lo = fp4x2<2>(wd) * s01;
+          hi = fp4x2<3>(wd) * s23;
+        } else {
+          lo = fp4x2<0>(wd) * s01;
+          hi = fp4x2<1>(wd) * s23;
+        }
+      } else {
+        const uint32_t wd = raw.v[x >> 2][x & 3];
+        lo = fp8x2<false>(wd);
+        hi = fp8x2<true>(wd);
+      }
+      const u32x2 pr = {as_u32(lo) & m01, as_u32(hi) & m23};
+      lds_st<u32x2>(vs_ + vst_off + x * kVtRow, pr);
+    }
+  };
+
+  // ---- running state per row block: max (log2 units), partial denominator
+  // (this lane's tokens), O^T accumulators (lane (g, c): row c, elements
+  // 16 db + 4 g .. + 3)
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (ntiles > 0) load(0);
+  for (int n = 0; n < ntiles; ++n) {
+    uint8_t* st = lds + (n & 1) * kStage;
+    stage(n, st);
+    if (n + 1 < ntiles) load(n + 1);
+    __syncthreads();
+
+    const uint8_t* ks_ = st;
+    const uint8_t* vs_ = st + kKBytes;
+    const int t0 = n * kTile;
+
+    // S^T = K . Q^T: s[rb][u][e] = score of token t0 + 16 u + 4 g + e, row c
+    f32x4 s[2][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s[0][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[1][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const f16x8 ka = lds_ld<f16x8>(ks_ + (16 * u + c) * kKRow + 16 * ((4 * kk + g) ^ c));
+        s[0][u] = mfma(ka, qop[0][kk], s[0][u]);
+        s[1][u] = mfma(ka, qop[1][kk], s[1][u]);
+      }
+    }
+
+    const bool masked = t0 + kTile - 1 > p_min;
+    f16x8 pb[2][2];
+    bool rescale = false;
+    float alpha[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      if (masked) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (t0 + 16 * u + 4 * g + e > prow[rb]) s[rb][u][e] = -INFINITY;
+      }
+      float mx = s[rb][0][0];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[rb][u][e]);
+      mx = lanes::across_rows<lanes::Max>(mx) * c2;
+      const float m_new = fmaxf(m[rb], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      alpha[rb] = __builtin_amdgcn_exp2f(m[rb] - m_use);
+      rescale |= m_new != m[rb];
+      m[rb] = m_new;
+      float sum = 0.f;
+      float p[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[u][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][u][e], c2, -m_use));
+          sum += p[u][e];
+        }
+      l[rb] = l[rb] * alpha[rb] + sum;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        f16x8 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = static_cast<_Float16>(p[2 * kc][e]);
+          v[4 + e] = static_cast<_Float16>(p[2 * kc + 1][e]);
+        }
+        pb[rb][kc] = v;
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[rb][db] *= alpha[rb];
+    }
+
+    // O^T += V^T . P^T: A = V^T (16 elements x 32 token slots), B = P^T
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const f16x8 va = lds_ld<f16x8>(vs_ + (16 * db + c) * kVtRow + 2 * (32 * kc + 8 * g));
+        acc[0][db] = mfma(va, pb[0][kc], acc[0][db]);
+        acc[1][db] = mfma(va, pb[1][kc], acc[1][db]);
+      }
+  }
+
+  // ---- epilogue: o = acc / l * s_t,V, lse = ln 2 (m + log2 l)
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float lt = lanes::across_rows<lanes::Sum>(l[rb]);
+    const int r = 32 * w + 16 * rb + c;
+    const int qi = i0 + r / G, h = hk * G + r % G;
+    if (qi >= P.Sq) continue;
+    const float inv = lt > 0.f ? vsc / lt : 0.f;
+    const int64_t ob = b * P.o_sb + static_cast<int64_t>(qi) * P.o_st + h * P.o_sh + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const f32x4 o = acc[rb][db] * inv;
+      if (P.out_dtype == KVQ_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(P.out) + ob + 16 * db) = o;
+      } else {
+        const u32x2 pk = {static_cast<uint32_t>(bf16_rne(o[0])) | (static_cast<uint32_t>(bf16_rne(o[1])) << 16),
+                          static_cast<uint32_t>(bf16_rne(o[2])) | (static_cast<uint32_t>(bf16_rne(o[3])) << 16)};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(P.out) + ob + 16 * db) = pk;
+      }
+    }
+    if (P.lse != nullptr && g == 0)
+      P.lse[(static_cast<int64_t>(b) * P.Sq + qi) * P.Hq + h] = lt > 0.f ? kLn2 * (m[rb] + __log2f(lt)) : -INFINITY;
+  }
+}
+
+template <int KVF, int G>
+hipError_t launch_g(const PrefillParams& p, hipStream_t st) {
+  const dim3 grid((p.Sq * G + kRows - 1) / kRows, p.Hkv, p.B);
+  if (p.block_table != nullptr)
+    hipLaunchKernelGGL((k_prefill_gqa<KVF, G, true>), grid, dim3(kThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_prefill_gqa<KVF, G, false>), grid, dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int KVF>
+hipError_t launch_fmt(const PrefillParams& p, int G, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_g<KVF, 1>(p, st);
+    case 2: return launch_g<KVF, 2>(p, st);
+    case 4: return launch_g<KVF, 4>(p, st);
+    default: return launch_g<KVF, 8>(p, st);
+  }
+}
+
+}  // namespace pf
+
+hipError_t launch_prefill_gqa(const PrefillParams& p, int kv_format, int G, hipStream_t st) {
+  return kv_format == KVQ_NVFP4 ? pf::launch_fmt<KVQ_NVFP4>(p, G, st) : pf::launch_fmt<KVQ_FP8E4M3>(p, G, st);
+}
+
+}  // namespace kvq

@@ -452,3 +452,77 @@ def test_binding_rejects_unreadable_views(K):
     with pytest.raises(ValueError):
         K.make_decode_args(q_c, lat4, None, lens, max_kv_len=Lm, num_splits=4, part_o=po, part_lse=pl, q_rope=q_r,
                            k_rope=k_r)
+
+
+def test_prefill_struct_size_matches_binding(L):
+    from quantized_kv_cache_nvfp4_amd import _lib
+    assert L.kvq_prefill_args_size() == ctypes.sizeof(_lib.KvqPrefillArgs)
+    assert "attn_prefill" in _lib.header_functions()
+
+
+def _prefill_args(K):
+    a = K.KvqPrefillArgs()
+    a.kv_format = K.KVQ_NVFP4
+    a.B, a.Hq, a.Hkv, a.D, a.Sq = 2, 32, 8, 128, 64
+    a.max_kv_len = 1024
+    a.q, a.q_dtype = FAKE, K.KVQ_BF16
+    a.q_sb, a.q_st, a.q_sh = 64 * 32 * 128, 32 * 128, 128
+    a.k_codes = a.k_scales = a.k_scale = FAKE
+    a.v_codes = a.v_scales = a.v_scale = FAKE
+    a.v_layout = K.KVQ_PLANE_TOKEN4
+    a.kv_sb, a.kv_sh = 8 * 1024, 1024
+    a.kv_lens = FAKE
+    a.softmax_scale = 0.088
+    a.out, a.out_dtype = FAKE, K.KVQ_BF16
+    a.o_sb, a.o_st, a.o_sh = 64 * 32 * 128, 32 * 128, 128
+    return a
+
+
+def test_prefill_validation(L, K):
+    """Every case breaks one rule and must be refused before any launch."""
+    rc = lambda a: L.attn_prefill(ctypes.byref(a), None)   # noqa: E731
+    cases = [
+        (lambda a: setattr(a, "kv_format", 7), K.KVQ_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "Hq", 30), K.KVQ_ERR_ARG),                      # Hq % Hkv
+        (lambda a: (setattr(a, "Hq", 128)), K.KVQ_ERR_UNSUPPORTED),           # G = 16
+        (lambda a: (setattr(a, "Hq", 24)), K.KVQ_ERR_UNSUPPORTED),            # G = 3
+        (lambda a: setattr(a, "D", 64), K.KVQ_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "Sq", -1), K.KVQ_ERR_ARG),
+        (lambda a: setattr(a, "max_kv_len", -1), K.KVQ_ERR_ARG),
+        (lambda a: setattr(a, "q", None), K.KVQ_ERR_ARG),
+        (lambda a: setattr(a, "v_codes", None), K.KVQ_ERR_ARG),
+        (lambda a: setattr(a, "kv_lens", None), K.KVQ_ERR_ARG),
+        (lambda a: setattr(a, "out", None), K.KVQ_ERR_ARG),
+        (lambda a: setattr(a, "v_scales", None), K.KVQ_ERR_ARG),               # NVFP4 needs scales
+        (lambda a: setattr(a, "q_dtype", K.KVQ_F32), K.KVQ_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "v_layout", K.KVQ_PLANE_ROWS), K.KVQ_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "kv_scale_per_head", 1), K.KVQ_ERR_UNSUPPORTED),  # NVFP4
+        (lambda a: setattr(a, "softmax_scale", 0.0), K.KVQ_ERR_ARG),
+        (lambda a: setattr(a, "softmax_scale", float("inf")), K.KVQ_ERR_ARG),
+        (lambda a: setattr(a, "out_dtype", K.KVQ_FP8E4M3), K.KVQ_ERR_UNSUPPORTED),
+        (lambda a: setattr(a, "q", FAKE_ODD), K.KVQ_ERR_ALIGN),
+        (lambda a: setattr(a, "q_st", 100), K.KVQ_ERR_ALIGN),
+        (lambda a: setattr(a, "k_codes", FAKE_ODD), K.KVQ_ERR_ALIGN),
+        (lambda a: setattr(a, "o_sh", 130), K.KVQ_ERR_ALIGN),
+        (lambda a: setattr(a, "kv_sh", 1022), K.KVQ_ERR_ALIGN),                 # TOKEN4 groups
+        (lambda a: setattr(a, "kv_sb", -4), K.KVQ_ERR_ARG),
+        (lambda a: (setattr(a, "block_table", FAKE), setattr(a, "block_size", 32), setattr(a, "bt_stride", 64)),
+         K.KVQ_ERR_ARG),                                                         # below the 64-token tile
+        (lambda a: (setattr(a, "block_table", FAKE), setattr(a, "block_size", 96), setattr(a, "bt_stride", 64)),
+         K.KVQ_ERR_ARG),                                                         # not a power of two
+        (lambda a: (setattr(a, "block_table", FAKE), setattr(a, "block_size", 64), setattr(a, "bt_stride", 8)),
+         K.KVQ_ERR_ARG),                                                         # table too short
+        (lambda a: (setattr(a, "block_table", FAKE), setattr(a, "block_size", 64), setattr(a, "bt_stride", 16),
+                    setattr(a, "kv_sblk", 6)), K.KVQ_ERR_ALIGN),
+    ]
+    for i, (mutate, want) in enumerate(cases):
+        a = _prefill_args(K)
+        mutate(a)
+        got = rc(a)
+        assert got == want, f"case {i}: got {got}, want {want} ({L.kvq_last_error().decode()})"
+        assert L.kvq_last_error().decode() != ""
+    assert L.attn_prefill(None, None) == K.KVQ_ERR_ARG
+    # an empty chunk is valid and launches nothing
+    a = _prefill_args(K)
+    a.Sq = 0
+    assert rc(a) == K.KVQ_OK

@@ -1,0 +1,250 @@
+"""GPU parity for the chunked prefill over the packed cache (attn_prefill,
+through the C ABI) against the oracle's prefill_gqa on the oracle's own
+dequantized cache: query i of an Sq-token chunk sits at position
+kv_len - Sq + i and attends causally to the cached tokens up to it.
+
+Cases span several 128-row query blocks and 64-token KV tiles with ragged
+tails, every implemented query-group width (1, 2, 4, 8), chunks longer than
+the cache (queries that see nothing: output 0, lse -inf), a chunk that is the
+whole sequence, one-token chunks, both cache formats, per-head FP8 scales,
+paged planes (bit-identical to contiguous), both output dtypes, and the
+bench workload's shape (GQA 4:1, 32K cache, 1024-token chunk) on sampled
+query rows.  Planes are padded with 0xFF bytes (NaN E4M3 scales), so a read
+of a row past a request's length would show."""
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth
+from gpu_helpers import DEV, K, announce, err_report, gpu_pack, page_plane
+from oracle import formats as OF
+from oracle import attention as OA
+from oracle import quant as OQ
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_cache(inp, fmt, per_head=False):
+    """Oracle packing + dequantization of the cache (fp64)."""
+    kf, vf = kvq_synth.f64(inp.k), kvq_synth.f64(inp.v)
+    if fmt == "nvfp4":
+        kc, ks, kst = OQ.nvfp4_pack(kf, OQ.amax(kf, inp.kv_lens))
+        vc, vs, vst = OQ.nvfp4_pack(vf, OQ.amax(vf, inp.kv_lens))
+        return OQ.nvfp4_unpack(kc, ks, kst), OQ.nvfp4_unpack(vc, vs, vst)
+    if per_head:
+        kc, ks = OQ.fp8_pack_heads(kf, OQ.amax_heads(kf, inp.kv_lens))
+        vc, vs = OQ.fp8_pack_heads(vf, OQ.amax_heads(vf, inp.kv_lens))
+        return OQ.fp8_unpack_heads(kc, ks), OQ.fp8_unpack_heads(vc, vs)
+    kc, kst = OQ.fp8_pack(kf, OQ.amax(kf, inp.kv_lens))
+    vc, vst = OQ.fp8_pack(vf, OQ.amax(vf, inp.kv_lens))
+    return OQ.fp8_unpack(kc, kst), OQ.fp8_unpack(vc, vst)
+
+
+def _gpu_planes(inp, fmt, per_head=False):
+    """K rows + V TOKEN4 planes, padded to whole 4-token groups with 0xFF."""
+    k_ = K()
+    if not per_head:
+        kp, vp, _, _, lens = gpu_pack(inp, fmt)
+        return kp, vp, lens
+    k, v = inp.k.to(DEV), inp.v.to(DEV)
+    lens = torch.from_numpy(inp.kv_lens).to(DEV)
+    B, H, L, D = inp.k.shape
+    Lp = (L + 3) // 4 * 4
+
+    def plane(x, layout):   # one E4M3 scale per kv head (the amax tensor has H entries)
+        p = k_.FP8Plane(torch.full((B, H, Lp, D), 0xFF, dtype=torch.uint8, device=DEV),
+                        torch.empty(H, dtype=torch.float32, device=DEV), layout)
+        k_.kvq_pack_fp8(x, k_.kvq_amax(x, lens, per_head=True), out=p)
+        return p
+    return plane(k, k_.KVQ_PLANE_ROWS), plane(v, k_.KVQ_PLANE_TOKEN4), lens
+
+
+def gpu_prefill(inp, kp, vp, lens, out_dtype=torch.bfloat16, block_table=None, q=None):
+    k_ = K()
+    q = inp.q.to(DEV) if q is None else q
+    out = torch.full(tuple(q.shape), float("nan"), dtype=out_dtype, device=DEV)
+    lse = torch.full(tuple(q.shape[:3]), float("nan"), dtype=torch.float32, device=DEV)
+    args = k_.make_prefill_args(q, kp, vp, lens, out, max_kv_len=inp.Lmax, softmax_scale=inp.softmax_scale,
+                                lse_out=lse, block_table=block_table)
+    k_.attn_prefill(args)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _check(out, lse, o_ref, lse_ref, label, pv_abs):
+    """Output: |o - o_ref| <= 2^-11 sum_t P_t |V_t| (P enters the P.V
+    contraction as f16: one rounding, <= 2^-11 relative, per probability)
+    plus 1e-5 (1 + |o|) of fp32 arithmetic for fp32 output, or plus
+    max(2e-3, 1 bf16 ulp(o_ref)) for bf16 output (its RNE rounding), and
+    cosine >= 0.9999.  lse: 1e-5 (1 + |lse|), and exactly -inf where the
+    oracle has -inf (queries that see nothing, whose output is 0)."""
+    o = out.float().cpu().double().numpy()
+    p_round = 2.0 ** -11 * pv_abs
+    if out.dtype == torch.bfloat16:
+        bound = np.maximum(2e-3, OF.bf16_ulp(o_ref)) + p_round
+    else:
+        bound = 1e-5 * (1.0 + np.abs(o_ref)) + p_round
+    bad = np.abs(o - o_ref) > bound
+    assert not bad.any(), f"{label}: {bad.sum()} elements out of the bound; max abs {np.abs(o - o_ref).max():.3g}"
+    if np.abs(o_ref).max() > 0:
+        _, _, cos = err_report(o, o_ref)
+        assert cos >= 0.9999, f"{label}: cosine {cos}"
+    g = lse.cpu().double().numpy()
+    ninf = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(g), ninf), f"{label}: -inf lse pattern differs"
+    assert np.all(o[ninf] == 0.0), f"{label}: queries that see nothing must output 0"
+    fin = ~ninf
+    assert np.all(np.abs(g[fin] - lse_ref[fin]) <= 1e-5 * (1.0 + np.abs(lse_ref[fin]))), f"{label}: lse"
+
+
+CASES = [
+    # (name, fmt, B, Hq, Hkv, kv_lens, Sq)
+    ("gqa4_ragged", "nvfp4", 2, 8, 2, (300, 1000), 200),
+    ("mha", "nvfp4", 1, 4, 4, (777,), 300),
+    ("gqa8_chunk_longer_than_cache", "nvfp4", 2, 16, 2, (130, 64), 100),
+    ("gqa2_whole_sequence", "nvfp4", 1, 8, 4, (513,), 513),
+    ("gqa4_one_token", "nvfp4", 3, 8, 2, (1, 65, 700), 1),
+    ("fp8_gqa4", "fp8", 2, 8, 2, (700, 69), 96),
+    ("fp8_mha_whole", "fp8", 1, 2, 2, (200,), 200),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_matches_oracle(case):
+    name, fmt, B, Hq, Hkv, lens, Sq = case
+    announce(f"prefill {case}")
+    inp = kvq_synth.prefill(B, Hq, Hkv, 128, list(lens), Sq, outliers=True)
+    khat, vhat = _oracle_cache(inp, fmt)
+    o_ref, lse_ref = OA.prefill_gqa(kvq_synth.f64(inp.q), khat, vhat, inp.kv_lens, inp.softmax_scale)
+    kp, vp, klens = _gpu_planes(inp, fmt)
+    pv_abs, _ = OA.prefill_gqa(kvq_synth.f64(inp.q), khat, np.abs(vhat), inp.kv_lens, inp.softmax_scale)
+    out, lse = gpu_prefill(inp, kp, vp, klens)
+    _check(out, lse, o_ref, lse_ref, f"prefill {name} bf16", pv_abs)
+    out32, lse32 = gpu_prefill(inp, kp, vp, klens, out_dtype=torch.float32)
+    _check(out32, lse32, o_ref, lse_ref, f"prefill {name} f32", pv_abs)
+    # the bf16 output is the RNE rounding of the fp32 one (same kernel arithmetic)
+    assert torch.equal(out32.to(torch.bfloat16), out)
+    assert torch.equal(lse32, lse)
+
+
+def test_prefill_fp8_per_head_scales():
+    announce("prefill fp8 per-head scales")
+    inp = kvq_synth.prefill(2, 8, 2, 128, [400, 150], 128, outliers=True)
+    khat, vhat = _oracle_cache(inp, "fp8", per_head=True)
+    o_ref, lse_ref = OA.prefill_gqa(kvq_synth.f64(inp.q), khat, vhat, inp.kv_lens, inp.softmax_scale)
+    pv_abs, _ = OA.prefill_gqa(kvq_synth.f64(inp.q), khat, np.abs(vhat), inp.kv_lens, inp.softmax_scale)
+    kp, vp, lens = _gpu_planes(inp, "fp8", per_head=True)
+    assert kp.scale.numel() == 2
+    out, lse = gpu_prefill(inp, kp, vp, lens)
+    _check(out, lse, o_ref, lse_ref, "prefill fp8 per-head", pv_abs)
+
+
+@pytest.mark.parametrize("fmt,bs", [("nvfp4", 64), ("nvfp4", 256), ("fp8", 128)])
+def test_prefill_paged_matches_contiguous(fmt, bs):
+    """Paged planes (permuted blocks, table entries past a request's length
+    pointing at 0xFF blocks) give bit-identical outputs."""
+    announce(f"prefill paged {fmt} bs={bs}")
+    inp = kvq_synth.prefill(2, 8, 2, 128, [900, 333], 160, outliers=True)
+    kp, vp, lens = _gpu_planes(inp, fmt)
+    ref, ref_lse = gpu_prefill(inp, kp, vp, lens)
+    kpp, bt = page_plane(kp, bs, 11, inp.kv_lens)
+    vpp, bt2 = page_plane(vp, bs, 11, inp.kv_lens)
+    assert torch.equal(bt, bt2)
+    got, lse = gpu_prefill(inp, kpp, vpp, lens, block_table=bt)
+    assert torch.equal(got, ref) and torch.equal(lse, ref_lse)
+
+
+def test_prefill_strided_views():
+    """q and out as strided views ([B, Hq, Sq, D] storage seen as
+    [B, Sq, Hq, D]): the strides go through the ABI unchanged."""
+    announce("prefill strided views")
+    inp = kvq_synth.prefill(2, 8, 2, 128, [250, 300], 70)
+    kp, vp, lens = _gpu_planes(inp, "nvfp4")
+    ref, ref_lse = gpu_prefill(inp, kp, vp, lens)
+    q_t = inp.q.to(DEV).transpose(1, 2).contiguous().transpose(1, 2)   # [B, Sq, Hq, D] view of [B, Hq, Sq, D]
+    k_ = K()
+    out_t = torch.zeros(2, 8, 70, 128, dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+    lse = torch.empty(2, 70, 8, dtype=torch.float32, device=DEV)
+    args = k_.make_prefill_args(q_t, kp, vp, lens, out_t, max_kv_len=inp.Lmax, softmax_scale=inp.softmax_scale,
+                                lse_out=lse)
+    k_.attn_prefill(args)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t, ref) and torch.equal(lse, ref_lse)
+
+
+def test_prefill_one_token_chunk_equals_decode():
+    """A one-token chunk is a decode step at position kv_len - 1: the output
+    matches attn_decode's within the two kernels' rounding (both are gated
+    against the oracle elsewhere; here the two HIP paths agree to 2 bf16 ulp)."""
+    announce("prefill one-token chunk vs decode")
+    k_ = K()
+    inp = kvq_synth.prefill(2, 32, 8, 128, [1024, 777], 1)
+    kp, vp, lens = _gpu_planes(inp, "nvfp4")
+    out, lse = gpu_prefill(inp, kp, vp, lens, out_dtype=torch.float32)
+    q = inp.q[:, 0].to(DEV).contiguous()
+    part_o = torch.empty(2 * 32 * 64 * 128, dtype=torch.float32, device=DEV)
+    part_lse = torch.empty(2 * 32 * 64, dtype=torch.float32, device=DEV)
+    args = k_.make_decode_args(q, kp, vp, lens, max_kv_len=inp.Lmax, softmax_scale=inp.softmax_scale, num_splits=1,
+                               part_o=part_o, part_lse=part_lse)
+    dec = torch.empty(2, 32, 128, dtype=torch.float32, device=DEV)
+    dlse = torch.empty(2, 32, dtype=torch.float32, device=DEV)
+    used = k_.attn_decode_splitkv(args)
+    k_.attn_decode_combine(part_o, part_lse, 2, 32, 128, used, dec, lse_out=dlse)
+    torch.cuda.synchronize()
+    assert torch.allclose(out[:, 0], dec, rtol=2e-3, atol=2e-3)
+    assert torch.allclose(lse[:, 0], dlse, rtol=1e-5, atol=1e-5)
+
+
+def test_prefill_empty_and_zero_length():
+    """Sq = 0 launches nothing; requests with kv_len = 0 give 0 and -inf."""
+    announce("prefill empty chunk / empty request")
+    k_ = K()
+    inp = kvq_synth.prefill(2, 8, 2, 128, [0, 100], 40)
+    khat, vhat = _oracle_cache(inp, "nvfp4")
+    o_ref, lse_ref = OA.prefill_gqa(kvq_synth.f64(inp.q), khat, vhat, inp.kv_lens, inp.softmax_scale)
+    pv_abs, _ = OA.prefill_gqa(kvq_synth.f64(inp.q), khat, np.abs(vhat), inp.kv_lens, inp.softmax_scale)
+    kp, vp, lens = _gpu_planes(inp, "nvfp4")
+    out, lse = gpu_prefill(inp, kp, vp, lens)
+    _check(out, lse, o_ref, lse_ref, "prefill kv_len 0", pv_abs)
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    q0 = torch.empty(2, 0, 8, 128, dtype=torch.bfloat16, device=DEV)
+    o0 = torch.empty(2, 0, 8, 128, dtype=torch.bfloat16, device=DEV)
+    k_.attn_prefill(k_.make_prefill_args(q0, kp, vp, lens, o0, max_kv_len=inp.Lmax))
+
+
+# ---------------------------------------------------------------- full size
+BENCH_B, BENCH_HQ, BENCH_HKV, BENCH_L, BENCH_SQ = 2, 32, 8, 32768, 1024
+
+
+def test_prefill_bench_shape_sampled():
+    """The bench workload: GQA 4:1 NVFP4 32K cache (the decode metric's
+    cache, kvq_synth.gqa(32768)), a 1024-token chunk per request, in the
+    launch bench.py times; 48 sampled (request, query, head) rows against the
+    oracle, each as decode of the cache truncated at the query's position
+    (the reduction the oracle's prefill is pinned to)."""
+    announce("prefill bench shape, sampled rows")
+    from gpu_helpers import oracle_gqa
+    cache = kvq_synth.gqa(BENCH_L)
+    q = kvq_synth.prefill_queries(BENCH_B, BENCH_SQ, BENCH_HQ, 128)
+    inp = kvq_synth.PrefillInputs(q=q, k=cache.k, v=cache.v, kv_lens=cache.kv_lens,
+                                  softmax_scale=cache.softmax_scale)
+    kp, vp, _, _, lens = gpu_pack(cache, "nvfp4")
+    out, lse = gpu_prefill(inp, kp, vp, lens, out_dtype=torch.float32)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    _, _, _, khat, vhat = oracle_gqa(("nvfp4", "gqa", BENCH_L))
+    rng = np.random.default_rng(5)
+    G = BENCH_HQ // BENCH_HKV
+    for n in range(48):
+        b = int(rng.integers(BENCH_B))
+        i = int(rng.integers(BENCH_SQ)) if n % 4 else (0 if n % 8 == 0 else BENCH_SQ - 1)
+        h = int(rng.integers(BENCH_HQ))
+        pos = BENCH_L - BENCH_SQ + i
+        qv = kvq_synth.f64(q[b, i, h])[None, None, None]
+        o1, l1 = OA.prefill_gqa(qv, khat[b:b + 1, h // G:h // G + 1], vhat[b:b + 1, h // G:h // G + 1],
+                                np.array([pos + 1]), inp.softmax_scale)
+        pv, _ = OA.prefill_gqa(qv, khat[b:b + 1, h // G:h // G + 1], np.abs(vhat[b:b + 1, h // G:h // G + 1]),
+                               np.array([pos + 1]), inp.softmax_scale)
+        got = out[b, i, h].cpu().double().numpy()
+        bound = 1e-5 * (1.0 + np.abs(o1[0, 0, 0])) + 2.0 ** -11 * pv[0, 0, 0]
+        assert np.all(np.abs(got - o1[0, 0, 0]) <= bound), f"row (b={b}, i={i}, h={h})"
+        assert abs(float(lse[b, i, h]) - l1[0, 0, 0]) <= 1e-5 * (1 + abs(l1[0, 0, 0])), f"lse (b={b}, i={i}, h={h})"
