@@ -47,6 +47,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/decode step + achieved HBM GB/s, NVFP4-KV split-KV decode B=2 GQA4:1 32K"
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0                     # MI355X dense f16 / bf16 matrix peak (no sparsity)
 B, HQ, HKV, D, L = 2, 32, 8, 128, 32768
 BYTES_PER_TOKEN_HEAD = 2 * (D // 2 + D // 16)   # K and V: codes + E4M3 scales = 144 B
 SPIN_CYCLES = 4_000_000                          # device spin before a timed replay (~1-2 ms)
@@ -61,11 +62,13 @@ def parse():
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
-    ap.add_argument("--workload", choices=["gqa32k", "mha", "mla", "fp8"], default="gqa32k",
+    ap.add_argument("--workload", choices=["gqa32k", "mha", "mla", "fp8", "prefill"], default="gqa32k",
                     help="gqa32k: the metric's configuration (default); mha: B=2, Hq=Hkv=16, D=128, kv 32768 "
                          "(plus the split-starved B=1, H=32 case); mla: DeepSeek-V2 per-rank MLA, B=32, 16 heads, "
                          "NVFP4 latent 512 + bf16 rope 64, kv 8192; fp8: per-tensor FP8 KV, B=64, Hq=32, Hkv=8, "
-                         "D=128, ragged kv_len ~ U{512..4096}, with and without FP8 probabilities")
+                         "D=128, ragged kv_len ~ U{512..4096}, with and without FP8 probabilities; prefill: "
+                         "chunked prefill of a 1024-token chunk per request over the GQA 4:1 B=2 32K cache "
+                         "(MFMA-bound)")
     ap.add_argument("--sweep", action="store_true",
                     help="decode step over split counts x kv lengths for GQA 4:1 and MHA (table + JSON)")
     ap.add_argument("--read-probe", action="store_true",
@@ -868,6 +871,113 @@ def run_fp8(args):
     print(json.dumps(res), flush=True)
 
 
+PREFILL_SQ = 1024
+
+
+def prefill_flops(kv_lens, Sq, Hq, Dh):
+    """Algorithmic flops of a chunked prefill: query i of request b sees
+    n = kv_len - Sq + i + 1 keys (causal, clamped at 0); each seen key costs
+    2 Dh flops in Q.K^T and 2 Dh in P.V per query head."""
+    tot = 0
+    for Lb in kv_lens:
+        for i in range(Sq):
+            tot += max(0, int(Lb) - Sq + i + 1)
+    return 4 * Dh * Hq * tot
+
+
+def cpu_baseline_prefill(inp, q, reps, n_rows=64):
+    """The oracle, untouched, timed on this host: per prefill step it
+    dequantizes the packed cache and runs exact fp64 causal attention for
+    every query row.  Sample: the dequantization of one kv head's K and V
+    plus the attention of `n_rows` query tokens (all their heads sharing
+    that kv head) at the end of request 0's chunk, scaled to the whole step
+    (kv heads x requests for the dequantization, query tokens x kv heads x
+    requests for the attention; the sampled tokens see the most keys, so the
+    scaling over-estimates by at most Sq / (2 L) = 1.6 %); the oracle's
+    one-off packing is not timed."""
+    import numpy as np
+    import kvq_synth
+    from oracle import attention as OA
+    from oracle import quant as OQ
+    G = inp.Hq // inp.Hkv
+    log("oracle: packing one kv head once (untimed)")
+    kf, vf = kvq_synth.f64(inp.k[:1, :1]), kvq_synth.f64(inp.v[:1, :1])
+    kc, ks, kst = OQ.nvfp4_pack(kf, OQ.amax(kf))
+    vc, vs, vst = OQ.nvfp4_pack(vf, OQ.amax(vf))
+    Sq = q.shape[1]
+    qs = kvq_synth.f64(q[:1, Sq - n_rows:, :G])
+    times = []
+    for r in range(reps):
+        log(f"oracle prefill sample {r + 1}/{reps}")
+        t0 = time.perf_counter()
+        khat, vhat = OQ.nvfp4_unpack(kc, ks, kst), OQ.nvfp4_unpack(vc, vs, vst)
+        t1 = time.perf_counter()
+        OA.prefill_gqa(qs, khat, vhat, inp.kv_lens[:1], inp.softmax_scale)
+        t2 = time.perf_counter()
+        times.append((t1 - t0) * inp.B * inp.Hkv + (t2 - t1) * (Sq / n_rows) * inp.Hkv * inp.B)
+    t = float(np.median(times))
+    return _cpu_entry(t, f"{reps} samples: dequantize 1 of {inp.B * inp.Hkv} (request, kv head) caches and "
+                         f"attend {n_rows} of {Sq} query tokens x {G} heads of request 0 over {inp.Lmax} keys "
+                         f"(fp64), median scaled to B={inp.B}, Hkv={inp.Hkv}, Sq={Sq}; numpy elementwise "
+                         f"single-threaded, BLAS threads {_blas_threads()}")
+
+
+def run_prefill(args):
+    """Chunked prefill over the GQA 4:1 B=2 32K NVFP4 cache (the decode
+    metric's cache): the last 1024 tokens of each request are the chunk, so
+    query i sits at position 32768 - 1024 + i.  Both contractions run on
+    MFMA (f16 inputs, fp32 accumulate); the roofline is the dense f16 matrix
+    peak.  Also timed: the same chunk over the FP8 E4M3 copy of the cache."""
+    import torch
+    import kvq_synth
+    import quantized_kv_cache_nvfp4_amd as K
+    K._lib.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("prefill: GQA 4:1 B=2 32K cache, 1024-token chunk")
+    inp = kvq_synth.gqa(L)
+    q = kvq_synth.prefill_queries(B, PREFILL_SQ, HQ, D)
+    _, kv_lens, k_amax, v_amax, kp0, vp0, k, v = _setup_gqa(K, torch, inp, dev)
+    kf0 = K.kvq_pack_fp8(k, k_amax)
+    vf0 = K.kvq_pack_fp8(v, v_amax, layout=K.KVQ_PLANE_TOKEN4)
+    del k, v
+    copies = _rotation(K, kp0, vp0, 2)
+    qd = q.to(dev)
+    out = torch.empty(B, PREFILL_SQ, HQ, D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, PREFILL_SQ, HQ, dtype=torch.float32, device=dev)
+    args_n = [K.make_prefill_args(qd, kc, vc, kv_lens, out, max_kv_len=L, softmax_scale=inp.softmax_scale,
+                                  lse_out=lse) for kc, vc in copies]
+    args_f = [K.make_prefill_args(qd, kf0, vf0, kv_lens, out, max_kv_len=L, softmax_scale=inp.softmax_scale,
+                                  lse_out=lse)]
+    for i in range(args.warmup):
+        K.attn_prefill(args_n[i % 2])
+        K.attn_prefill(args_f[0])
+    torch.cuda.synchronize()
+    tm = Timer(torch, 2, args.steps)
+    ms = {"prefill_nvfp4": tm.run(lambda i: K.attn_prefill(args_n[i]))}
+    assert torch.isfinite(out.float()).all()
+    tm1 = Timer(torch, 1, args.steps)
+    ms["prefill_fp8"] = tm1.run(lambda i: K.attn_prefill(args_f[0]))
+    flops = prefill_flops(inp.kv_lens, PREFILL_SQ, HQ, D)
+    step_us = ms["prefill_nvfp4"] * 1e3
+    res = base_record("us/prefill step + achieved TFLOP/s, NVFP4-KV chunked prefill B=2 GQA4:1 32K cache, "
+                      "1024-token chunk", step_us, args.steps, args.warmup, "f16 MFMA, fp32 accumulate (NVFP4 KV)",
+                      {"workload": "NVFP4-KV chunked prefill, GQA 4:1", "B": B, "Hq": HQ, "Hkv": HKV, "head_dim": D,
+                       "kv_len": L, "chunk": PREFILL_SQ, "out_dtype": "bf16", "v_layout": "token4",
+                       "rotation_copies": 2})
+    res["step_us"] = {k_: round(v_ * 1e3, 3) for k_, v_ in ms.items()}
+    achieved = flops / (step_us * 1e-6) / 1e12
+    res["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                       "kernel": "k_prefill_gqa<NVFP4,G=4> (one launch per step)", "kernel_us_mean": round(step_us, 3),
+                       "algorithmic_flops": flops}
+    res["fp8_cache_tflops"] = round(flops / (ms["prefill_fp8"] * 1e-3) / 1e12, 1)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline_prefill(inp, q, args.cpu_reps)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.source_hash:
@@ -892,6 +1002,8 @@ def main():
         run_mla(args)
     elif args.workload == "fp8":
         run_fp8(args)
+    elif args.workload == "prefill":
+        run_prefill(args)
     else:
         run_gqa(args)
 

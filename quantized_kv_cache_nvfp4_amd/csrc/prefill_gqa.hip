@@ -43,6 +43,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "decode_common.h"
 #include "kvq_internal.h"
 #include "wave_reduce.h"
@@ -62,6 +64,10 @@ constexpr int kVtRow = kTile * 2 + 16;        // f16 V^T row of 64 token slots +
 constexpr int kVtBytes = kD * kVtRow;         // 18 KB
 constexpr int kStage = kKBytes + kVtBytes;
 constexpr int kLdsBytes = 2 * kStage;         // 69,632 B
+#ifndef KVQ_PF_SCHED
+#define KVQ_PF_SCHED 0
+#endif
+constexpr bool kSchedGroups = KVQ_PF_SCHED;
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
@@ -77,6 +83,15 @@ __device__ inline int vt_slot(int t) {
 __device__ inline uint16_t bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Work-group barrier that orders LDS only: the fences cover the local
+// address space, so global loads still in flight (the next tile's raw
+// bytes) are not waited for, as they would be at __syncthreads().
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 template <class T>
@@ -160,41 +175,53 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
 
   auto tile_row = [&](int t0) -> int64_t {   // plane row of tile token 0
     if constexpr (PAGED) {
-      const int blk = P.block_table[b * P.bt_stride + (t0 >> P.log2_bs)];
+      // tiles past the seen keys are loaded with empty ranges: their table
+      // entry is never used, so read the entry of the last seen key instead
+      const int tc = t0 < n_end ? t0 : (n_end > 0 ? n_end - 1 : 0);
+      const int blk = P.block_table[b * P.bt_stride + (tc >> P.log2_bs)];
       return static_cast<int64_t>(blk) * P.kv_sblk + hk * P.kv_sh + (t0 & ((1 << P.log2_bs) - 1));
     } else {
       return b * P.kv_sb + hk * P.kv_sh + t0;
     }
   };
+  // keys of tile n that some row sees (<= 0 past the last tile: the range-
+  // checked loads of such a tile read nothing and return zeros)
+  auto tile_keys = [&](int n) { return n_end - n * kTile < kTile ? n_end - n * kTile : kTile; };
 
   Raw<KVF> raw;
-  auto load = [&](int n) {
-    const int t0 = n * kTile;
-    const int nv = n_end - t0 < kTile ? n_end - t0 : kTile;
-    const int ng = (nv + 3) >> 2;
-    const int64_t row = tile_row(t0);
+  auto load_k = [&](int n) {
+    const int nv = tile_keys(n);
+    const int64_t row = tile_row(n * kTile);
     const Rsrc rk = make_rsrc(P.k_codes + row * RB, nv * RB);
-    const Rsrc rv = make_rsrc(P.v_codes + row * RB, ng * 4 * RB);
     if constexpr (kFp4) {
       raw.k[0] = ld128(rk, kt * RB + 16 * kq);
-      raw.v[0] = ld128(rv, vq * 4 * RB + 16 * vr);
       const Rsrc rks = make_rsrc(P.k_scales + row * SB, nv * SB);
-      const Rsrc rvs = make_rsrc(P.v_scales + row * SB, ng * 4 * SB);
       raw.ks = ld16(rks, kt * SB + 2 * kq);
-      raw.vs = ld32(rvs, vq * 4 * SB + 4 * (vr >> 1));
     } else {
       raw.k[0] = ld128(rk, kt * RB + 32 * kq);
       raw.k[1] = ld128(rk, kt * RB + 32 * kq + 16);
+    }
+  };
+  auto load_v = [&](int n) {
+    const int nv = tile_keys(n);
+    const int ng = nv > 0 ? (nv + 3) >> 2 : 0;
+    const int64_t row = tile_row(n * kTile);
+    const Rsrc rv = make_rsrc(P.v_codes + row * RB, ng * 4 * RB);
+    if constexpr (kFp4) {
+      raw.v[0] = ld128(rv, vq * 4 * RB + 16 * vr);
+      const Rsrc rvs = make_rsrc(P.v_scales + row * SB, ng * 4 * SB);
+      raw.vs = ld32(rvs, vq * 4 * SB + 4 * (vr >> 1));
+    } else {
       raw.v[0] = ld128(rv, vq * 4 * RB + 32 * vr);
       raw.v[1] = ld128(rv, vq * 4 * RB + 32 * vr + 16);
     }
   };
 
-  auto stage = [&](int n, uint8_t* st) {
-    const int nv = n_end - n * kTile;
-    uint8_t* ks_ = st;
-    uint8_t* vs_ = st + kKBytes;
-    // K: 4 chunks of 8 elements, chunk j of row kt at 16 (j ^ (kt & 15))
+  // K: 4 chunks of 8 elements, chunk j of row kt at 16 (j ^ (kt & 15))
+  int kst[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kst[j] = kst_off + 16 * ((4 * kq + j) ^ (kt & 15));
+  auto stage_k = [&](uint8_t* kb) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f16x8 x;
@@ -202,49 +229,96 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
         const uint32_t wd = raw.k[0][j];
         x = cat4(fp4x2<0>(wd), fp4x2<1>(wd), fp4x2<2>(wd), fp4x2<3>(wd));
         const f16x2 s2 = fp8x2<false>(raw.ks);
-        const _Float16 s = j < 2 ? s2[0] : s2[1];
-        x = x * s;
+        const _Float16 sc = j < 2 ? s2[0] : s2[1];
+        x = x * sc;
       } else {
         const uint32_t w0 = raw.k[j >> 1][2 * (j & 1)], w1 = raw.k[j >> 1][2 * (j & 1) + 1];
         x = cat4(fp8x2<false>(w0), fp8x2<true>(w0), fp8x2<false>(w1), fp8x2<true>(w1));
       }
-      lds_st<f16x8>(ks_ + kst_off + 16 * ((4 * kq + j) ^ (kt & 15)), x);
+      lds_st<f16x8>(kb + kst[j], x);
     }
-    // V: for each of the 8 elements, the 4 tokens' values (8 bytes) at their
-    // slots in row 8 vr + x; tokens at or past nv are cleared (a group that
-    // straddles the end of the seen keys may hold stale or NaN bytes there)
+  };
+  // V: for each of the 8 elements, the 4 tokens' values (8 bytes) at their
+  // slots in row 8 vr + x; tokens at or past the tile's seen keys are
+  // cleared (a group that straddles them may hold stale or NaN bytes there)
+  auto stage_v = [&](auto partial_tag, uint8_t* vb, int nv) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;   // the tile holds fewer than kTile seen keys
     uint32_t m01 = 0xFFFFFFFFu, m23 = 0xFFFFFFFFu;
-    if (4 * vq + 4 > nv) {
+    const bool straddle = PARTIAL && 4 * vq + 4 > nv;
+    if (straddle) {
       const int t = 4 * vq;
       m01 = (t + 0 < nv ? 0x0000FFFFu : 0u) | (t + 1 < nv ? 0xFFFF0000u : 0u);
       m23 = (t + 2 < nv ? 0x0000FFFFu : 0u) | (t + 3 < nv ? 0xFFFF0000u : 0u);
     }
+    f16x2 lo[8], hi[8];   // tokens (0, 1) and (2, 3) of element 8 vr + x
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      f16x2 lo, hi;   // tokens (0, 1) and (2, 3) of element 8 vr + x
       if constexpr (kFp4) {
         const uint32_t wd = raw.v[0][x >> 1];
         const f16x2 s01 = fp8x2<false>(raw.vs), s23 = fp8x2<true>(raw.vs);
         if (x & 1) {
-          lo = fp4x2<2>(wd) * s01;
-          hi = fp4x2<3>(wd) * s23;
+          lo[x] = fp4x2<2>(wd) * s01;
+          hi[x] = fp4x2<3>(wd) * s23;
         } else {
-          lo = fp4x2<0>(wd) * s01;
-          hi = fp4x2<1>(wd) * s23;
+          lo[x] = fp4x2<0>(wd) * s01;
+          hi[x] = fp4x2<1>(wd) * s23;
         }
       } else {
         const uint32_t wd = raw.v[x >> 2][x & 3];
-        lo = fp8x2<false>(wd);
-        hi = fp8x2<true>(wd);
+        lo[x] = fp8x2<false>(wd);
+        hi[x] = fp8x2<true>(wd);
       }
-      const u32x2 pr = {as_u32(lo) & m01, as_u32(hi) & m23};
-      lds_st<u32x2>(vs_ + vst_off + x * kVtRow, pr);
+    }
+    if constexpr (PARTIAL) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        lo[x] = as_h2(as_u32(lo[x]) & m01);
+        hi[x] = as_h2(as_u32(hi[x]) & m23);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) lds_st<u32x2>(vb + vst_off + x * kVtRow, u32x2{as_u32(lo[x]), as_u32(hi[x])});
+  };
+
+  // ---- MFMA operand addresses (bytes inside a stage)
+  int kld[4];   // K row 16 u + c, chunk 4 kk + g (swizzled); + 16 u rows per sub-tile
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) kld[kk] = c * kKRow + 16 * ((4 * kk + g) ^ c);
+  const int vld = c * kVtRow + 16 * g;   // V^T row 16 db + c, slots 32 kc + 8 g
+
+  // S^T = K . Q^T: s[rb][u][e] = score of tile token 16 u + 4 g + e, row c.
+  // The K operands of sub-tile u + 1 are read from LDS while the MFMAs of
+  // sub-tile u run (the scheduling fences keep that order).
+  auto qk = [&](const uint8_t* kb, f32x4 (&sc)[2][4]) {
+    f16x8 ka[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) ka[0][kk] = lds_ld<f16x8>(kb + kld[kk]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u < 3) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[(u + 1) & 1][kk] = lds_ld<f16x8>(kb + kld[kk] + (u + 1) * 16 * kKRow);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      sc[0][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sc[1][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        sc[0][u] = mfma(ka[u & 1][kk], qop[0][kk], sc[0][u]);
+        sc[1][u] = mfma(ka[u & 1][kk], qop[1][kk], sc[1][u]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- running state per row block: max (log2 units), partial denominator
-  // (this lane's tokens), O^T accumulators (lane (g, c): row c, elements
-  // 16 db + 4 g .. + 3)
+  // ---- running state per row block: reference maximum (log2 units),
+  // partial denominator (this lane's tokens), O^T accumulators (lane (g, c):
+  // row c, elements 16 db + 4 g .. + 3).  The reference is raised only when
+  // a tile's maximum exceeds it by more than kLazy (then the accumulators are
+  // rescaled); otherwise probabilities up to 2^kLazy are formed against the
+  // old reference, which is exact in real arithmetic and keeps f16's relative
+  // precision for P.
+  constexpr float kLazy = 8.f;
   float m[2] = {-INFINITY, -INFINITY};
   float l[2] = {0.f, 0.f};
   f32x4 acc[2][8];
@@ -253,62 +327,49 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (ntiles > 0) load(0);
-  for (int n = 0; n < ntiles; ++n) {
-    uint8_t* st = lds + (n & 1) * kStage;
-    stage(n, st);
-    if (n + 1 < ntiles) load(n + 1);
-    __syncthreads();
-
-    const uint8_t* ks_ = st;
-    const uint8_t* vs_ = st + kKBytes;
+  // The softmax of tile n in two parts.  tile_max: (MASK: clear the scores
+  // of keys past each row's position,) take the tile's row maxima and move
+  // the reference maxima, giving the factors alpha by which l and the
+  // accumulators are rescaled (any != 1 in the wave: `rescale`).  probs:
+  // P = exp2(score * c2 - m) as the f16 P^T operands, l = l alpha + sum P.
+  float alpha[2] = {1.f, 1.f};
+  bool rescale = false;
+  auto tile_max = [&](auto mask_tag, f32x4 (&sc)[2][4], int n) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int t0 = n * kTile;
-
-    // S^T = K . Q^T: s[rb][u][e] = score of token t0 + 16 u + 4 g + e, row c
-    f32x4 s[2][4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      s[0][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      s[1][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const f16x8 ka = lds_ld<f16x8>(ks_ + (16 * u + c) * kKRow + 16 * ((4 * kk + g) ^ c));
-        s[0][u] = mfma(ka, qop[0][kk], s[0][u]);
-        s[1][u] = mfma(ka, qop[1][kk], s[1][u]);
-      }
-    }
-
-    const bool masked = t0 + kTile - 1 > p_min;
-    f16x8 pb[2][2];
-    bool rescale = false;
-    float alpha[2];
+    rescale = false;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      if (masked) {
+      if constexpr (MASK) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (t0 + 16 * u + 4 * g + e > prow[rb]) s[rb][u][e] = -INFINITY;
+            if (t0 + 16 * u + 4 * g + e > prow[rb]) sc[rb][u][e] = -INFINITY;
       }
-      float mx = s[rb][0][0];
+      float mx = sc[rb][0][0];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[rb][u][e]);
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[rb][u][e]);
       mx = lanes::across_rows<lanes::Max>(mx) * c2;
-      const float m_new = fmaxf(m[rb], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      alpha[rb] = __builtin_amdgcn_exp2f(m[rb] - m_use);
-      rescale |= m_new != m[rb];
-      m[rb] = m_new;
+      const bool up = mx > m[rb] + kLazy;   // false when mx = -inf
+      alpha[rb] = up ? __builtin_amdgcn_exp2f(m[rb] - mx) : 1.f;   // 0 when m = -inf
+      m[rb] = up ? mx : m[rb];
+      rescale |= up;
+    }
+  };
+  auto probs = [&](const f32x4 (&sc)[2][4], f16x8 (&pb)[2][2]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float m_use = m[rb] == -INFINITY ? 0.f : m[rb];
       float sum = 0.f;
       float p[4][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[u][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][u][e], c2, -m_use));
+          p[u][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rb][u][e], c2, -m_use));
           sum += p[u][e];
         }
       l[rb] = l[rb] * alpha[rb] + sum;
@@ -323,23 +384,74 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
         pb[rb][kc] = v;
       }
     }
+  };
+  auto rescale_acc = [&]() {
     if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int db = 0; db < 8; ++db) acc[rb][db] *= alpha[rb];
     }
+  };
 
-    // O^T += V^T . P^T: A = V^T (16 elements x 32 token slots), B = P^T
+  // O^T += V^T . P^T: A = V^T (16 elements x 32 token slots), B = P^T;
+  // element block db + 1's operands are read while block db's MFMAs run
+  auto pv = [&](const uint8_t* vb, const f16x8 (&pb)[2][2]) {
+    f16x8 va[2][2];
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int kc = 0; kc < 2; ++kc) va[0][kc] = lds_ld<f16x8>(vb + vld + kc * 64);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      if (db < 7) {
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) va[(db + 1) & 1][kc] = lds_ld<f16x8>(vb + vld + (db + 1) * 16 * kVtRow + kc * 64);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        const f16x8 va = lds_ld<f16x8>(vs_ + (16 * db + c) * kVtRow + 2 * (32 * kc + 8 * g));
-        acc[0][db] = mfma(va, pb[0][kc], acc[0][db]);
-        acc[1][db] = mfma(va, pb[1][kc], acc[1][db]);
+        acc[0][db] = mfma(va[db & 1][kc], pb[0][kc], acc[0][db]);
+        acc[1][db] = mfma(va[db & 1][kc], pb[1][kc], acc[1][db]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- the tile loop.  Two LDS stages (K and V^T of one tile each); tile
+  // n is staged into stage n % 2, which tile n - 2 used before the previous
+  // barrier, while the raw bytes of tile n + 1 load into registers: one
+  // barrier per tile.  The two work-groups a compute unit holds overlap each
+  // other's MFMA and VALU phases.
+  uint8_t* const kbuf = lds;
+  uint8_t* const vbuf = lds + 2 * kKBytes;
+  // tiles whose keys every row sees (no causal mask needed)
+  int n_open = p_min >= kTile - 1 ? (p_min - (kTile - 1)) / kTile + 1 : 0;
+  n_open = n_open < ntiles ? n_open : ntiles;
+  if (ntiles > 0) {
+    load_k(0);
+    load_v(0);
   }
+  auto step = [&](auto mask_tag, int n) {
+    f32x4 sc[2][4];
+    f16x8 pb[2][2];
+    uint8_t* const kb = kbuf + (n & 1) * kKBytes;
+    uint8_t* const vb = vbuf + (n & 1) * kVtBytes;
+    stage_k(kb);
+    if (tile_keys(n) < kTile)
+      stage_v(std::true_type{}, vb, tile_keys(n));
+    else
+      stage_v(std::false_type{}, vb, kTile);
+    load_k(n + 1);
+    load_v(n + 1);
+    lds_barrier();
+    qk(kb, sc);
+    tile_max(mask_tag, sc, n);
+    rescale_acc();
+    probs(sc, pb);
+    pv(vb, pb);
+  };
+  int n = 0;
+  for (; n < n_open; ++n) step(std::false_type{}, n);
+  for (; n < ntiles; ++n) step(std::true_type{}, n);
 
   // ---- epilogue: o = acc / l * s_t,V, lse = ln 2 (m + log2 l)
 #pragma unroll
