@@ -730,11 +730,34 @@ def run_mla(args):
     torch.cuda.synchronize()
     if args.warmup > 0:
         assert torch.equal(out, out_paged), "paged and contiguous MLA decode differ"
+    # the latent query quantized to NVFP4 (per-tensor amax over the batch's
+    # queries), decoded from its codes; timed beside: the query's calibration
+    # and packing (two launches per step)
+    qplane = K.kvq_pack_nvfp4(q_c, K.kvq_amax(q_c.unsqueeze(1)))
+    qdargs = [K.make_decode_args(qplane, pl, None, lens, max_kv_len=MLA_L, softmax_scale=inp.softmax_scale,
+                                 num_splits=s, part_o=part_o, part_lse=part_lse, q_rope=q_r, k_rope=kr)
+              for pl, kr in copies]
+    q_amax = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def qnv_step(i):
+        used = K.attn_decode_splitkv(qdargs[i])
+        K.attn_decode_combine(part_o, part_lse, MLA_B, MLA_H, MLA_DC, used, out)
+
+    def quantize_query(i):
+        K.kvq_amax(q_c.unsqueeze(1), out=q_amax)
+        K.kvq_pack_nvfp4(q_c, q_amax, out=qplane)
+
+    for i in range(args.warmup):
+        qnv_step(i % n_copies)
+        quantize_query(i)
+    torch.cuda.synchronize()
     tm = Timer(torch, n_copies, args.steps)
     ms_step = tm.run(step)
     ms_split = tm.run(lambda i: K.attn_decode_splitkv(dargs[i]))
     ms_step_pg = tm.run(paged_step)
     ms_split_pg = tm.run(lambda i: K.attn_decode_splitkv(pdargs[i]))
+    ms_step_qnv = tm.run(qnv_step)
+    ms_qquant = tm.run(quantize_query)
     assert torch.isfinite(out.float()).all()
     algo = MLA_B * MLA_L * MLA_BYTES_PER_TOKEN
     res = base_record("us/decode step + achieved HBM GB/s, NVFP4-latent MLA split-KV decode B=32 H=16 8K",
@@ -745,7 +768,9 @@ def run_mla(args):
     res["hbm_gbps_step"] = round(algo / (ms_step * 1e-3) / 1e9, 1)
     res["step_us"] = {"decode_two_launch": round(ms_step * 1e3, 3), "split_kernel": round(ms_split * 1e3, 3),
                       "decode_two_launch_paged64": round(ms_step_pg * 1e3, 3),
-                      "split_kernel_paged64": round(ms_split_pg * 1e3, 3)}
+                      "split_kernel_paged64": round(ms_split_pg * 1e3, 3),
+                      "decode_two_launch_nvfp4_query": round(ms_step_qnv * 1e3, 3),
+                      "quantize_query_nvfp4": round(ms_qquant * 1e3, 3)}
     res["roofline"] = roofline(algo, ms_split * 1e3, "k_decode_mla (split kernel, partials)", measured_traffic("mla"))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")

@@ -351,6 +351,18 @@ typedef struct {
   const void* new_k;
   const void* new_v;
   int32_t new_dtype;
+  /* NVFP4 latent query (MLA layout; the q_bmm_quantizer of Model-Optimizer
+     PR #714 "Testing" — present in QuantMLAAttention beside the latent's
+     kv_c_bmm_quantizer and shown disabled there — read as the same NVFP4
+     quantizer applied to the absorbed query q_c): with q_dtype =
+     KVQ_NVFP4, q holds the E2M1 codes of q_c (rows of D/2 bytes, element
+     2j in the low nibble), q_block_scales the E4M3 block scales (rows of
+     D/16 bytes) and q_scale its fp32 tensor scale (device float[1]); q_sb
+     and q_sh then count query rows (a row = D/2 code bytes and D/16 scale
+     bytes).  The dequantized query enters the latent contraction exactly;
+     the tensor scale multiplies the latent score.  The rope query q_r stays
+     bf16.  q 16-byte and q_block_scales 4-byte aligned.  NULL otherwise. */
+  const uint8_t* q_block_scales;
 } kvq_decode_args;
 
 /*

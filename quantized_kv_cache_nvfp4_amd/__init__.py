@@ -254,12 +254,24 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
     """
     a = KvqDecodeArgs()
     mla = v is None
+    q_nv = None
+    if isinstance(q, NVFP4Plane):   # NVFP4 latent query (MLA): codes [B, Hq, D/2], scales [B, Hq, D/16]
+        if not mla:
+            raise ValueError("NVFP4 queries are decoded for the MLA layout only")
+        q_nv, q = q, q.codes
+        if q.dim() != 3 or q_nv.scales.dim() != 3:
+            raise ValueError("an NVFP4 query must be [B, Hq, D/2] codes with [B, Hq, D/16] scales")
+        qr_c, qr_s = _rows(q, q.shape[-1]), _rows(q_nv.scales, q_nv.scales.shape[-1])
+        if (qr_c.s1, qr_c.s2) != (qr_s.s1, qr_s.s2):
+            raise ValueError("the NVFP4 query's codes and scales must share their row strides")
     if q.dim() != 3 or (q.shape[-1] > 1 and q.stride(-1) != 1):
         raise ValueError("q must be [B, Hq, D] with a contiguous last dim")
     if q_rope is not None and (q_rope.dim() != 3 or (q_rope.shape[-1] > 1 and q_rope.stride(-1) != 1)):
         raise ValueError("q_rope must be [B, Hq, Drope] with a contiguous last dim")
     fmt = KVQ_NVFP4 if isinstance(k, NVFP4Plane) else KVQ_FP8E4M3
     B, Hq, D = q.shape
+    if q_nv is not None:
+        D = q_nv.d
     a.kv_format, a.layout = fmt, (KVQ_LAYOUT_MLA if mla else KVQ_LAYOUT_GQA)
     a.B, a.Hq, a.D, a.Dv = B, Hq, D, D
     row_elems = D // 2 if fmt == KVQ_NVFP4 else D
@@ -298,7 +310,11 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
             a.block_table, a.block_size = _ptr(block_table), int(k.codes.shape[2])
             a.bt_stride, a.kv_sblk, a.kv_sb = block_table.stride(0), kr.s0, 0
     a.max_kv_len = int(max_kv_len)
-    if q.dtype == torch.uint8:   # FP8 query codes
+    if q_nv is not None:
+        qr_c = _rows(q, q.shape[-1])   # query rows: the struct counts them for NVFP4 queries
+        a.q_dtype, a.q_scale, a.q_block_scales = KVQ_NVFP4, _ptr(q_nv.tensor_scale), _ptr(q_nv.scales)
+        a.q, a.q_sb, a.q_sh = _ptr(q), qr_c.s1, qr_c.s2
+    elif q.dtype == torch.uint8:   # FP8 query codes
         if q_scale is None:
             raise ValueError("an FP8 query needs q_scale")
         if q_scale.numel() not in (1, Hq):
@@ -306,7 +322,8 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
         a.q_dtype, a.q_scale, a.q_scale_per_head = KVQ_FP8E4M3, _ptr(q_scale), int(q_scale.numel() > 1)
     else:
         a.q_dtype = _DT[q.dtype]
-    a.q, a.q_sb, a.q_sh = _ptr(q), q.stride(0), q.stride(1)
+    if q_nv is None:
+        a.q, a.q_sb, a.q_sh = _ptr(q), q.stride(0), q.stride(1)
     if fmt == KVQ_NVFP4:
         a.k_codes, a.k_scales, a.k_scale = _ptr(k.codes), _ptr(k.scales), _ptr(k.tensor_scale)
         if not mla:
@@ -338,7 +355,8 @@ def make_decode_args(q, k, v, kv_lens, *, max_kv_len, softmax_scale=None, num_sp
     # the struct holds raw device pointers: keep the tensors they point into
     # alive for as long as the struct is (a plane built inline for the call
     # would otherwise be freed, and its memory may be returned to the driver)
-    a._keep = (q, k, v, kv_lens, q_rope, k_rope, part_o, part_lse, p_scratch, block_table, q_scale, new_k, new_v)
+    a._keep = (q, k, v, kv_lens, q_rope, k_rope, part_o, part_lse, p_scratch, block_table, q_scale, new_k, new_v,
+               q_nv)
     return a
 
 

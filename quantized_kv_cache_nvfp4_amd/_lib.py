@@ -59,6 +59,7 @@ class KvqDecodeArgs(ctypes.Structure):
         ("bt_stride", ctypes.c_int64), ("kv_sblk", ctypes.c_int64),
         ("q_scale", ctypes.c_void_p), ("q_scale_per_head", ctypes.c_int32),
         ("new_k", ctypes.c_void_p), ("new_v", ctypes.c_void_p), ("new_dtype", ctypes.c_int32),
+        ("q_block_scales", ctypes.c_void_p),
     ]
 
 

@@ -305,8 +305,15 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
     if (!aligned(a->q_scale, 4)) return fail(KVQ_ERR_ALIGN, "q_scale must be 4-byte aligned");
     if (!aligned(a->q, 8) || a->q_sb % 8 != 0 || a->q_sh % 8 != 0)
       return fail(KVQ_ERR_ALIGN, "FP8 query rows must be 8-byte aligned (q, q_sb, q_sh)");
+  } else if (a->q_dtype == KVQ_NVFP4) {   // NVFP4 latent query (MLA)
+    if (a->layout != KVQ_LAYOUT_MLA) return fail(KVQ_ERR_UNSUPPORTED, "NVFP4 queries are decoded for the MLA layout only");
+    if (a->q_block_scales == nullptr || a->q_scale == nullptr)
+      return fail(KVQ_ERR_ARG, "an NVFP4 query needs q_block_scales and q_scale");
+    if (!aligned(a->q, 16) || !aligned(a->q_block_scales, 4) || !aligned(a->q_scale, 4))
+      return fail(KVQ_ERR_ALIGN, "NVFP4 query codes must be 16-byte, its scales 4-byte aligned");
+    if (a->q_sb < 0 || a->q_sh < 0) return fail(KVQ_ERR_ARG, "query row strides must be >= 0");
   } else if (a->q_dtype != KVQ_BF16 && a->q_dtype != KVQ_F32) {
-    return fail(KVQ_ERR_UNSUPPORTED, "q_dtype must be BF16, F32 or (GQA) FP8E4M3");
+    return fail(KVQ_ERR_UNSUPPORTED, "q_dtype must be BF16, F32, (GQA) FP8E4M3 or (MLA) NVFP4");
   }
   if (!(a->softmax_scale > 0.0f) || a->softmax_scale != a->softmax_scale || a->softmax_scale > 3.0e38f)
     return fail(KVQ_ERR_ARG, "softmax_scale must be a positive finite number");
@@ -426,10 +433,10 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
       return fail(KVQ_ERR_ARG, "MLA needs k_scales, q_rope and k_rope");
     if (!kvq::mla_supported(*a))
       return fail(KVQ_ERR_UNSUPPORTED,
-                  "MLA decode: implemented for Hq = 16, D = Dv = 512, Drope = 64, bf16 queries (got Hq=%d D=%d Dv=%d "
-                  "Drope=%d)", a->Hq, a->D, a->Dv, a->Drope);
-    if (!aligned(a->q, 16) || a->q_sh % 8 != 0 || a->q_sb % 8 != 0 || !aligned(a->q_rope, 16) ||
-        a->qr_sh % 8 != 0 || a->qr_sb % 8 != 0)
+                  "MLA decode: implemented for Hq = 16, D = Dv = 512, Drope = 64, bf16 or NVFP4 latent queries (got "
+                  "Hq=%d D=%d Dv=%d Drope=%d)", a->Hq, a->D, a->Dv, a->Drope);
+    if (!aligned(a->q, 16) || (a->q_dtype == KVQ_BF16 && (a->q_sh % 8 != 0 || a->q_sb % 8 != 0)) ||
+        !aligned(a->q_rope, 16) || a->qr_sh % 8 != 0 || a->qr_sb % 8 != 0)
       return fail(KVQ_ERR_ALIGN, "MLA queries must be 16-byte aligned with strides multiple of 8 elements");
     if (!aligned(a->k_scales, 8) || !aligned(a->k_rope, 16))
       return fail(KVQ_ERR_ALIGN, "MLA k_scales must be 8-byte and k_rope 16-byte aligned");

@@ -74,7 +74,9 @@ __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <bool PAGED>
+// QNV: the latent query q_c arrives as NVFP4 codes + block scales + tensor
+// scale (dequantized exactly to f16 in the prologue) instead of bf16
+template <bool PAGED, bool QNV>
 __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, int num_splits) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_c[kT * kPitch];   // staged latent rows (f16)
   __shared__ __attribute__((aligned(16))) f32x4 lds_s[kW][kQ][64];      // partial scores per wave, sub-tile, lane
@@ -170,12 +172,23 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
   };
   // ---- query words, lane (g, c) = head c:
   //   latent MFMA j (0..7): dims 256 dh + 64 g + 8 j + e; rope: 32 dh + 8 g + e
+  //   (NVFP4 latent query: the same 64 elements are code bytes [128 dh +
+  //   32 g, +32) and scale bytes [16 dh + 4 g, +4) of head c's row)
   uint4 qraw[8], qrraw;
+  uint32_t qsw = 0;
   {
-    const uint16_t* qc = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * a.q_sb +
-                         static_cast<int64_t>(c) * a.q_sh + 256 * dh + 64 * g;
+    if constexpr (QNV) {
+      const int64_t qrow = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(c) * a.q_sh;
+      const uint8_t* qc = static_cast<const uint8_t*>(a.q) + qrow * (kD / 2) + 128 * dh + 32 * g;
+      qraw[0] = *reinterpret_cast<const uint4*>(qc);
+      qraw[1] = *reinterpret_cast<const uint4*>(qc + 16);
+      qsw = *reinterpret_cast<const uint32_t*>(a.q_block_scales + qrow * (kD / 16) + 16 * dh + 4 * g);
+    } else {
+      const uint16_t* qc = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * a.q_sb +
+                           static_cast<int64_t>(c) * a.q_sh + 256 * dh + 64 * g;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qraw[j] = *reinterpret_cast<const uint4*>(qc + 8 * j);
+      for (int j = 0; j < 8; ++j) qraw[j] = *reinterpret_cast<const uint4*>(qc + 8 * j);
+    }
     const uint16_t* qrp = static_cast<const uint16_t*>(a.q_rope) + static_cast<int64_t>(b) * a.qr_sb +
                           static_cast<int64_t>(c) * a.qr_sh + 32 * dh + 8 * g;
     qrraw = *reinterpret_cast<const uint4*>(qrp);
@@ -204,12 +217,24 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
   const int ntiles = cs < ce ? (ce - cs + kT - 1) / kT : 0;
 
   const float s_t = *a.k_scale;
-  const float sc_lat = a.softmax_scale * s_t * kLog2e;   // latent scores carry the tensor scale
+  // latent scores carry the tensor scale of the latent (and of an NVFP4 query)
+  const float sc_lat = a.softmax_scale * s_t * (QNV ? *a.q_scale : 1.0f) * kLog2e;
   const float sc_rope = a.softmax_scale * kLog2e;
 
   f16x8 qop[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
+    if constexpr (QNV) {
+      // elements 8j..8j+7 of the lane's 64: code dword j, block j / 2
+      // (E2M1 x E4M3 is exact in f16)
+      const uint4& qw = j < 4 ? qraw[0] : qraw[1];
+      const uint32_t w = (j & 3) == 0 ? qw.x : ((j & 3) == 1 ? qw.y : ((j & 3) == 2 ? qw.z : qw.w));
+      const f16x2 s2 = fp8x2<false>(qsw >> (16 * ((j >> 1) >> 1)));
+      const _Float16 sv = ((j >> 1) & 1) ? s2[1] : s2[0];
+      const f16x2 sp = f16x2{sv, sv};
+      qop[j] = cat4(fp4x2<0>(w) * sp, fp4x2<1>(w) * sp, fp4x2<2>(w) * sp, fp4x2<3>(w) * sp);
+      continue;
+    }
     const uint32_t ws[4] = {qraw[j].x, qraw[j].y, qraw[j].z, qraw[j].w};
     f16x2 h[4];
 #pragma unroll
@@ -380,14 +405,23 @@ int mla_tile_tokens() { return kT; }
 
 bool mla_supported(const kvq_decode_args& a) {
   return a.kv_format == KVQ_NVFP4 && a.Hq == kH && a.Hkv == 1 && a.D == kD && a.Dv == kD && a.Drope == kDr &&
-         a.q_dtype == KVQ_BF16;
+         (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_NVFP4);
 }
 
 hipError_t launch_decode_mla(const kvq_decode_args& a, const DecodePlan& p, hipStream_t st) {
-  if (a.block_table != nullptr)
-    hipLaunchKernelGGL(k_decode_mla<true>, dim3(p.s, a.B), dim3(kThreads), 0, st, a, p.s);
-  else
-    hipLaunchKernelGGL(k_decode_mla<false>, dim3(p.s, a.B), dim3(kThreads), 0, st, a, p.s);
+  const dim3 grid(p.s, a.B);
+  const bool qnv = a.q_dtype == KVQ_NVFP4;
+  if (a.block_table != nullptr) {
+    if (qnv)
+      hipLaunchKernelGGL((k_decode_mla<true, true>), grid, dim3(kThreads), 0, st, a, p.s);
+    else
+      hipLaunchKernelGGL((k_decode_mla<true, false>), grid, dim3(kThreads), 0, st, a, p.s);
+  } else {
+    if (qnv)
+      hipLaunchKernelGGL((k_decode_mla<false, true>), grid, dim3(kThreads), 0, st, a, p.s);
+    else
+      hipLaunchKernelGGL((k_decode_mla<false, false>), grid, dim3(kThreads), 0, st, a, p.s);
+  }
   return hipGetLastError();
 }
 

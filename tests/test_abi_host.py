@@ -282,6 +282,27 @@ def test_mla_validation(L, K):
     assert _decode_rc(L, a) == 1
 
 
+def test_nvfp4_query_validation(L, K):
+    """NVFP4 latent queries: MLA layout only, with block scales and a tensor
+    scale, 16-byte aligned codes and 4-byte aligned scales; the rows of a
+    query count query rows (no element-stride rule)."""
+    def nv(**kw):
+        a = _mla_args(K)
+        a.q_dtype, a.q_block_scales, a.q_scale, a.q_sb, a.q_sh = K.KVQ_NVFP4, FAKE, FAKE, 16, 1
+        for k_, v_ in kw.items():
+            setattr(a, k_, v_)
+        return a
+    assert _decode_rc(L, nv(q_block_scales=None)) == 1
+    assert _decode_rc(L, nv(q_scale=None)) == 1
+    assert _decode_rc(L, nv(q=FAKE_ODD)) == 3
+    assert _decode_rc(L, nv(q_block_scales=FAKE_ODD)) == 3
+    assert _decode_rc(L, nv(q_sb=-1)) == 1
+    a = _good_args(K)
+    a.q_dtype, a.q_block_scales, a.q_scale = K.KVQ_NVFP4, FAKE, FAKE
+    assert _decode_rc(L, a) == 2                     # GQA layout: not implemented
+    assert L.kvq_decode_args_size() == ctypes.sizeof(K.KvqDecodeArgs)
+
+
 def test_decode_args_keep_their_tensors(K):
     """The decode-argument struct holds raw pointers: the tensors behind them
     (planes built inline for the call included) must live as long as it does,

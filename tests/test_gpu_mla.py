@@ -245,3 +245,61 @@ def test_mla_paged_rejects_bad_blocks():
     for bs in (32, 96):
         with pytest.raises(k_.KvqError):
             _gpu_paged(inp, plane, 2, bs)
+
+
+# ---------------------------------------------------------------- NVFP4 latent query
+QNV_CASES = [(2, (300, 77), 1, False), (3, (1000, 64, 65), 0, False), (2, (513, 1), 8, True)]
+
+
+@pytest.mark.parametrize("B,lens,s,paged", QNV_CASES, ids=lambda v: str(v))
+def test_mla_nvfp4_query(B, lens, s, paged):
+    """The latent query q_c quantized to NVFP4 (per-tensor amax over the
+    batch's queries, the same quantizer as the latent cache) and decoded from
+    its codes: the query codes are bit-exact against the oracle's packing,
+    and the output is within the fp32 gate of the oracle's MLA attention with
+    the dequantized query (q_r stays bf16).  Paged: the same through a block
+    table of 64-token blocks."""
+    announce(f"mla nvfp4 query B={B} lens={lens} s={s} paged={paged}")
+    k_ = K()
+    inp, (codes, scales, st, _), _, _, _ = _case(B, lens, 2)
+    # oracle: quantize q_c with its own packing, attention with the dequantized query
+    qf = kvq_synth.f64(inp.q_c)
+    q_amax = OQ.amax(qf[:, None])                        # [B, 1, H, 512]: every query element counts
+    q_codes, q_scales, q_st = OQ.nvfp4_pack(qf, q_amax)
+    q_hat = OQ.nvfp4_unpack(q_codes, q_scales, q_st)
+    chat = OQ.nvfp4_unpack(codes, scales, st)
+    q_r, k_r = kvq_synth.f64(inp.q_r), kvq_synth.f64(inp.k_r)
+    o_ref, lse_ref = OA.decode_mla(q_hat, q_r, chat, k_r, inp.kv_lens, inp.softmax_scale)
+    o_abs, _ = OA.decode_mla(q_hat, q_r, np.abs(chat), k_r, inp.kv_lens, inp.softmax_scale)
+    # GPU: the same two kernels quantize the query
+    c = inp.c.to(DEV)
+    lens_d = torch.from_numpy(inp.kv_lens).to(DEV)
+    plane = k_.kvq_pack_nvfp4(c, k_.kvq_amax(c.unsqueeze(1), lens_d))
+    qc = inp.q_c.to(DEV)
+    qplane = k_.kvq_pack_nvfp4(qc, k_.kvq_amax(qc.unsqueeze(1)))   # codes [B, H, 256], scales [B, H, 32]
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(qplane.codes), q_codes)
+    assert np.array_equal(_np(qplane.scales), q_scales)
+    assert float(qplane.tensor_scale.item()) == np.float32(q_st)
+    bt, k_r_d = None, inp.k_r.to(DEV)
+    if paged:   # 64-token blocks at permuted physical blocks, 0xFF spares past each request
+        codes_p, bt = _page_mla(plane.codes, inp.kv_lens, 64, 5)
+        scales_p, bt2 = _page_mla(plane.scales, inp.kv_lens, 64, 5)
+        k_r_d, bt3 = _page_mla(k_r_d, inp.kv_lens, 64, 5)
+        assert torch.equal(bt, bt2) and torch.equal(bt, bt3)
+        plane = k_.NVFP4Plane(codes_p, scales_p, plane.tensor_scale, plane.layout)
+    H, D = 16, 512
+    cap = 64
+    part_o = torch.empty(B * H * cap * D, dtype=torch.float32, device=DEV)
+    part_lse = torch.empty(B * H * cap, dtype=torch.float32, device=DEV)
+    args = k_.make_decode_args(qplane, plane, None, lens_d, max_kv_len=int(inp.c.shape[1]),
+                               softmax_scale=inp.softmax_scale, num_splits=s, part_o=part_o, part_lse=part_lse,
+                               q_rope=inp.q_r.to(DEV), k_rope=k_r_d, block_table=bt)
+    out = torch.empty(B, H, D, dtype=torch.float32, device=DEV)
+    lse = torch.empty(B, H, dtype=torch.float32, device=DEV)
+    used = k_.attn_decode_splitkv(args)
+    k_.attn_decode_combine(part_o, part_lse, B, H, D, used, out, lse_out=lse)
+    torch.cuda.synchronize()
+    _check_fp32(out, o_ref, o_abs, f"mla nvfp4 query B={B} lens={lens}")
+    fin = np.isfinite(lse_ref)
+    assert np.all(np.abs(_np(lse).astype(np.float64)[fin] - lse_ref[fin]) <= 1e-5 * (1 + np.abs(lse_ref[fin])))
