@@ -952,7 +952,9 @@ def run_prefill(args):
     metric's cache): the last 1024 tokens of each request are the chunk, so
     query i sits at position 32768 - 1024 + i.  Both contractions run on
     MFMA (f16 inputs, fp32 accumulate); the roofline is the dense f16 matrix
-    peak.  Also timed: the same chunk over the FP8 E4M3 copy of the cache."""
+    peak.  Also timed: the same chunk over the FP8 E4M3 copy of the cache,
+    and the chunk's queries as FP8 codes (one scale) over both caches (over
+    the FP8 cache Q.K^T runs on the FP8 matrix cores)."""
     import torch
     import kvq_synth
     import quantized_kv_cache_nvfp4_amd as K
@@ -974,15 +976,27 @@ def run_prefill(args):
                                   lse_out=lse) for kc, vc in copies]
     args_f = [K.make_prefill_args(qd, kf0, vf0, kv_lens, out, max_kv_len=L, softmax_scale=inp.softmax_scale,
                                   lse_out=lse)]
+    q4 = qd.view(B * PREFILL_SQ, HQ, 1, D)
+    qp = K.kvq_pack_fp8(q4, K.kvq_amax(q4))
+    q8 = qp.codes.view(B, PREFILL_SQ, HQ, D)
+    args_q8 = [K.make_prefill_args(q8, kf0, vf0, kv_lens, out, max_kv_len=L, softmax_scale=inp.softmax_scale,
+                                   lse_out=lse, q_scale=qp.scale),
+               K.make_prefill_args(q8, copies[0][0], copies[0][1], kv_lens, out, max_kv_len=L,
+                                   softmax_scale=inp.softmax_scale, lse_out=lse, q_scale=qp.scale)]
     for i in range(args.warmup):
         K.attn_prefill(args_n[i % 2])
         K.attn_prefill(args_f[0])
+        K.attn_prefill(args_q8[0])
+        K.attn_prefill(args_q8[1])
     torch.cuda.synchronize()
     tm = Timer(torch, 2, args.steps)
     ms = {"prefill_nvfp4": tm.run(lambda i: K.attn_prefill(args_n[i]))}
     assert torch.isfinite(out.float()).all()
     tm1 = Timer(torch, 1, args.steps)
     ms["prefill_fp8"] = tm1.run(lambda i: K.attn_prefill(args_f[0]))
+    ms["prefill_fp8_query_fp8"] = tm1.run(lambda i: K.attn_prefill(args_q8[0]))
+    ms["prefill_fp8_query_nvfp4"] = tm1.run(lambda i: K.attn_prefill(args_q8[1]))
+    assert torch.isfinite(out.float()).all()
     flops = prefill_flops(inp.kv_lens, PREFILL_SQ, HQ, D)
     step_us = ms["prefill_nvfp4"] * 1e3
     res = base_record("us/prefill step + achieved TFLOP/s, NVFP4-KV chunked prefill B=2 GQA4:1 32K cache, "
@@ -997,6 +1011,7 @@ def run_prefill(args):
                        "kernel": "k_prefill_gqa<NVFP4,G=4> (one launch per step)", "kernel_us_mean": round(step_us, 3),
                        "algorithmic_flops": flops}
     res["fp8_cache_tflops"] = round(flops / (ms["prefill_fp8"] * 1e-3) / 1e12, 1)
+    res["fp8_query_fp8_cache_tflops"] = round(flops / (ms["prefill_fp8_query_fp8"] * 1e-3) / 1e12, 1)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         res["cpu_baseline"] = cpu_baseline_prefill(inp, q, args.cpu_reps)

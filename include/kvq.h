@@ -524,7 +524,8 @@ size_t kvq_fp8p_scratch_floats(int32_t B, int32_t Hq, int32_t s, int32_t max_kv_
  * (scores softmax_scale * (q . K_t), K_t and V_t dequantized; the tensor
  * scales in fp32), GQA head mapping h -> h / (Hq / Hkv).
  *
- * Layout: q [B][Sq][Hq][D] bf16 with element strides q_sb, q_st, q_sh;
+ * Layout: q [B][Sq][Hq][D] bf16 with element strides q_sb, q_st, q_sh
+ * (or FP8 codes, below);
  * out [B][Sq][Hq][D] with element strides o_sb, o_st, o_sh; lse_out
  * contiguous [B][Sq][Hq] float32 or NULL.  K planes in the row layout, V
  * planes in KVQ_PLANE_TOKEN4 (the decode layout at D = 128), plane rows
@@ -540,8 +541,8 @@ typedef struct {
   int32_t B, Hq, Hkv, D;     /* D = 128; Hq / Hkv in {1, 2, 4, 8}            */
   int32_t Sq;                /* query tokens per request (>= 0)             */
   int32_t max_kv_len;        /* upper bound on kv_lens; rows per request    */
-  const void* q;             /* device bf16, 16-byte aligned                */
-  int32_t q_dtype;           /* KVQ_BF16                                    */
+  const void* q;             /* device bf16 16-byte aligned, or FP8 codes   */
+  int32_t q_dtype;           /* KVQ_BF16 or KVQ_FP8E4M3                     */
   int64_t q_sb, q_st, q_sh;  /* element strides, multiples of 8             */
   const uint8_t* k_codes;
   const uint8_t* k_scales;   /* NVFP4 only                                  */
@@ -561,6 +562,19 @@ typedef struct {
   int32_t out_dtype;         /* KVQ_F32 (16-byte aligned) or KVQ_BF16 (8-byte) */
   int64_t o_sb, o_st, o_sh;  /* element strides, multiples of 4             */
   float* lse_out;            /* device float[B][Sq][Hq] or NULL             */
+  /* FP8 queries (the QKV-FP8 schemes of compressed-tensors PR #436,
+     "Changes" and "Testing": the attention's query activations quantized
+     to FP8 E4M3 per tensor or per head).  With q_dtype = KVQ_FP8E4M3, q
+     holds E4M3 codes, one byte an element (q 8-byte aligned, strides as
+     above) — e.g. kvq_pack_fp8 / kvq_pack_fp8_heads of the chunk viewed as
+     [B * Sq][Hq][1][D] — and q_scale their scale: device float[1], or
+     float[Hq] with q_scale_per_head = 1.  The codes enter the score
+     contraction exactly (over an FP8 cache both operands are E4M3 codes
+     on the FP8 matrix cores, products exact, sums in fp32); the scale
+     multiplies the score beside the K tensor scale and softmax_scale.
+     Unused for bf16 queries. */
+  const float* q_scale;
+  int32_t q_scale_per_head;
 } kvq_prefill_args;
 
 /* sizeof(kvq_prefill_args) as compiled into the library (binding check). */

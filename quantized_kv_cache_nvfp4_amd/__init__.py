@@ -405,7 +405,7 @@ def attn_decode_noalloc(args: KvqDecodeArgs, out, out_scale=None, lse_out=None, 
 
 
 def make_prefill_args(q, k, v, kv_lens, out, *, max_kv_len, softmax_scale=None, lse_out=None,
-                      block_table=None) -> KvqPrefillArgs:
+                      block_table=None, q_scale=None) -> KvqPrefillArgs:
     """Fill the C prefill-argument struct from tensors (no device work).
 
     q [B, Sq, Hq, D] bfloat16 (the chunk's queries; last dim contiguous);
@@ -413,14 +413,21 @@ def make_prefill_args(q, k, v, kv_lens, out, *, max_kv_len, softmax_scale=None, 
     TOKEN4), or, with block_table (int32 [B, max_blocks]), paged planes
     [num_blocks, Hkv, block_size, .]; kv_lens int32 [B] (cache length
     including the chunk); out [B, Sq, Hq, D] float32 or bfloat16; lse_out
-    float32 [B, Sq, Hq] contiguous or None.
+    float32 [B, Sq, Hq] contiguous or None.  FP8 queries: q uint8 E4M3
+    codes [B, Sq, Hq, D] with q_scale, a device float tensor of 1 (per
+    tensor) or Hq (per query head) entries.
     """
     if q.dim() != 4 or (q.shape[-1] > 1 and q.stride(-1) != 1):
         raise ValueError("q must be [B, Sq, Hq, D] with a contiguous last dim")
     if out.dim() != 4 or tuple(out.shape) != tuple(q.shape) or (out.shape[-1] > 1 and out.stride(-1) != 1):
         raise ValueError("out must be [B, Sq, Hq, D] like q, with a contiguous last dim")
-    if q.dtype != torch.bfloat16:
-        raise ValueError("q must be bfloat16")
+    q8 = q.dtype == torch.uint8
+    if q.dtype != torch.bfloat16 and not q8:
+        raise ValueError("q must be bfloat16 or uint8 E4M3 codes")
+    if q8 != (q_scale is not None):
+        raise ValueError("q_scale goes with FP8 (uint8) queries and only with them")
+    if q8 and q_scale.numel() not in (1, q.shape[2]):
+        raise ValueError(f"q_scale must have 1 or Hq = {q.shape[2]} entries")
     if lse_out is not None and (tuple(lse_out.shape) != tuple(q.shape[:3]) or not lse_out.is_contiguous()
                                 or lse_out.dtype != torch.float32):
         raise ValueError("lse_out must be a contiguous float32 [B, Sq, Hq] tensor")
@@ -445,8 +452,10 @@ def make_prefill_args(q, k, v, kv_lens, out, *, max_kv_len, softmax_scale=None, 
         a.block_table, a.block_size = _ptr(block_table), int(k.codes.shape[2])
         a.bt_stride, a.kv_sblk, a.kv_sb = block_table.stride(0), kr.s0, 0
     a.max_kv_len = int(max_kv_len)
-    a.q, a.q_dtype = _ptr(q), KVQ_BF16
+    a.q, a.q_dtype = _ptr(q), (KVQ_FP8E4M3 if q8 else KVQ_BF16)
     a.q_sb, a.q_st, a.q_sh = q.stride(0), q.stride(1), q.stride(2)
+    if q8:
+        a.q_scale, a.q_scale_per_head = _ptr(q_scale), int(q_scale.numel() > 1)
     if fmt == KVQ_NVFP4:
         a.k_codes, a.k_scales, a.k_scale = _ptr(k.codes), _ptr(k.scales), _ptr(k.tensor_scale)
         a.v_codes, a.v_scales, a.v_scale = _ptr(v.codes), _ptr(v.scales), _ptr(v.tensor_scale)
@@ -462,7 +471,7 @@ def make_prefill_args(q, k, v, kv_lens, out, *, max_kv_len, softmax_scale=None, 
     a.out, a.out_dtype = _ptr(out), {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}[out.dtype]
     a.o_sb, a.o_st, a.o_sh = out.stride(0), out.stride(1), out.stride(2)
     a.lse_out = _ptr(lse_out)
-    a._keep = (q, k, v, kv_lens, out, lse_out, block_table)
+    a._keep = (q, k, v, kv_lens, out, lse_out, block_table, q_scale)
     return a
 
 

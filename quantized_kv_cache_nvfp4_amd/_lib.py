@@ -81,6 +81,7 @@ class KvqPrefillArgs(ctypes.Structure):
         ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int32),
         ("o_sb", ctypes.c_int64), ("o_st", ctypes.c_int64), ("o_sh", ctypes.c_int64),
         ("lse_out", ctypes.c_void_p),
+        ("q_scale", ctypes.c_void_p), ("q_scale_per_head", ctypes.c_int32),
     ]
 
 

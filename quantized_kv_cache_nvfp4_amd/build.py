@@ -19,8 +19,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["api.cpp", "quant_kernels.hip", "decode_gqa.hip", "decode_gqa_nvfp4_d128.hip", "decode_gqa_nvfp4_d64.hip",
            "decode_gqa_fp8_d128.hip", "decode_gqa_fp8_d64.hip", "decode_mla.hip", "combine.hip",
            "prefill_gqa.hip"]
-# the benchmark's streaming-read probe: its own small library, not part of the C ABI
-PROBE_SOURCE = "probe_read.hip"
+# measurement probes (the benchmark's streaming-read ceiling, the FP8 matrix
+# core's accumulation error): their own small library, not part of the C ABI
+PROBE_SOURCES = ["probe_read.hip", "probe_mfma8.hip"]
 PROBE_LIB_PATH = os.path.join(HERE, "libkvq_probe.so")
 
 ARCH = "gfx950"
@@ -64,9 +65,9 @@ def build(verbose=False) -> str:
     """Compile every HIP source for gfx950 and link libkvq.so; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=8) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + [PROBE_SOURCE]))
-    _link(objs[:-1], LIB_PATH, verbose)
-    _link(objs[-1:], PROBE_LIB_PATH, verbose)
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB_PATH, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 

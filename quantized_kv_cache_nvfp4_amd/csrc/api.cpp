@@ -534,7 +534,12 @@ int attn_prefill(const kvq_prefill_args* a, void* stream) {
     return fail(KVQ_ERR_ARG, "q, k_codes, v_codes, k_scale, v_scale, kv_lens and out must be non-null");
   if (a->kv_format == KVQ_NVFP4 && (a->k_scales == nullptr || a->v_scales == nullptr))
     return fail(KVQ_ERR_ARG, "NVFP4 needs k_scales and v_scales");
-  if (a->q_dtype != KVQ_BF16) return fail(KVQ_ERR_UNSUPPORTED, "q_dtype must be BF16");
+  if (a->q_dtype != KVQ_BF16 && a->q_dtype != KVQ_FP8E4M3)
+    return fail(KVQ_ERR_UNSUPPORTED, "q_dtype must be BF16 or FP8E4M3");
+  const bool q8 = a->q_dtype == KVQ_FP8E4M3;
+  if (q8 && a->q_scale == nullptr) return fail(KVQ_ERR_ARG, "FP8 queries need q_scale");
+  if (q8 && a->q_scale_per_head != 0 && a->q_scale_per_head != 1)
+    return fail(KVQ_ERR_ARG, "q_scale_per_head must be 0 or 1");
   if (a->v_layout != KVQ_PLANE_TOKEN4) return fail(KVQ_ERR_UNSUPPORTED, "V planes must be in the TOKEN4 layout");
   if (a->kv_scale_per_head != 0 && (a->kv_scale_per_head != 1 || a->kv_format != KVQ_FP8E4M3))
     return fail(KVQ_ERR_UNSUPPORTED, "kv_scale_per_head must be 0 or 1, and 1 only for FP8");
@@ -542,8 +547,10 @@ int attn_prefill(const kvq_prefill_args* a, void* stream) {
     return fail(KVQ_ERR_ARG, "softmax_scale must be a positive finite number");
   if (a->out_dtype != KVQ_F32 && a->out_dtype != KVQ_BF16)
     return fail(KVQ_ERR_UNSUPPORTED, "out_dtype must be F32 or BF16");
-  if (!aligned(a->q, 16) || a->q_sb % 8 != 0 || a->q_st % 8 != 0 || a->q_sh % 8 != 0)
-    return fail(KVQ_ERR_ALIGN, "q must be 16-byte aligned with q_sb, q_st and q_sh multiples of 8 elements");
+  if (!aligned(a->q, q8 ? 8 : 16) || a->q_sb % 8 != 0 || a->q_st % 8 != 0 || a->q_sh % 8 != 0)
+    return fail(KVQ_ERR_ALIGN, "q must be %d-byte aligned with q_sb, q_st and q_sh multiples of 8 elements",
+                q8 ? 8 : 16);
+  if (q8 && !aligned(a->q_scale, 4)) return fail(KVQ_ERR_ALIGN, "q_scale must be 4-byte aligned");
   if (!aligned(a->k_codes, 16) || !aligned(a->v_codes, 16))
     return fail(KVQ_ERR_ALIGN, "k_codes and v_codes must be 16-byte aligned");
   if ((a->k_scales != nullptr && !aligned(a->k_scales, 4)) || (a->v_scales != nullptr && !aligned(a->v_scales, 4)))
@@ -571,6 +578,7 @@ int attn_prefill(const kvq_prefill_args* a, void* stream) {
 
   kvq::PrefillParams p{};
   p.q = static_cast<const uint16_t*>(a->q);
+  p.q_dtype = a->q_dtype; p.q_scale = a->q_scale; p.q_scale_per_head = q8 ? a->q_scale_per_head : 0;
   p.q_sb = a->q_sb; p.q_st = a->q_st; p.q_sh = a->q_sh;
   p.k_codes = a->k_codes; p.k_scales = a->k_scales; p.v_codes = a->v_codes; p.v_scales = a->v_scales;
   p.k_scale = a->k_scale; p.v_scale = a->v_scale; p.per_head = a->kv_scale_per_head;

@@ -80,7 +80,10 @@ bool mla_supported(const kvq_decode_args& a);
 // Kernel parameters, from a validated kvq_prefill_args (contiguous or paged
 // planes, K rows, V TOKEN4, head_dim 128, bf16 queries).
 struct PrefillParams {
-  const uint16_t* q;
+  const uint16_t* q;              // bf16 elements, or (q_dtype FP8) E4M3 code bytes
+  int q_dtype;
+  const float* q_scale;           // FP8 queries: float[1] or float[Hq]
+  int q_scale_per_head;
   int64_t q_sb, q_st, q_sh;
   const uint8_t* k_codes;
   const uint8_t* k_scales;

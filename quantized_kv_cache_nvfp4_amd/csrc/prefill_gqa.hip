@@ -113,9 +113,20 @@ struct Raw {
   uint32_t vs;             // NVFP4: block scale of the V elements, 4 tokens
 };
 
-template <int KVF, int G, bool PAGED>
+// Q8: the queries are FP8 E4M3 codes with a scale (the QKV-FP8 schemes).
+// Over an FP8 cache (K8) both operands of Q.K^T are E4M3 codes and the
+// contraction runs on the FP8 matrix cores, K staged in LDS as its raw bytes
+// (no conversion); over an NVFP4 cache the codes are converted to f16
+// (exact) and the f16 path runs.
+typedef long i64x1;
+__device__ inline f32x4 mfma_fp8(i64x1 a, i64x1 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+template <int KVF, int G, bool PAGED, bool Q8>
 __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
   constexpr bool kFp4 = KVF == KVQ_NVFP4;
+  constexpr bool K8 = Q8 && KVF == KVQ_FP8E4M3;   // Q.K^T on FP8 MFMA
   constexpr int RB = kFp4 ? kD / 2 : kD;   // code bytes per row
   constexpr int SB = kD / 16;              // NVFP4 scale bytes per row
   constexpr int QB = kRows / G;            // query tokens per work-group
@@ -139,11 +150,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
 
   const float ksc = P.k_scale[P.per_head ? hk : 0];
   const float vsc = P.v_scale[P.per_head ? hk : 0];
-  const float c2 = P.softmax_scale * ksc * kLog2e;   // raw score -> log2 units
+  // raw score -> log2 units, per row block (an FP8 query's scale may be per head)
+  float c2r[2];
 
   // ---- this lane's query rows: B operand of S^T = K . Q^T, lane (g, c)
   // holds row c of each block, elements 32 kk + 8 g .. + 7
   f16x8 qop[2][4];
+  i64x1 qop8[2][4];   // K8: the E4M3 codes themselves
   int prow[2];   // key positions <= prow are visible to the lane's row
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -151,6 +164,22 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
     const int qi = i0 + r / G, h = hk * G + r % G;
     prow[rb] = pos0 + qi;
     const bool valid = qi < P.Sq;
+    const float qs = Q8 ? P.q_scale[P.q_scale_per_head ? h : 0] : 1.0f;
+    c2r[rb] = P.softmax_scale * ksc * qs * kLog2e;
+    if constexpr (Q8) {
+      const uint8_t* qp8 = reinterpret_cast<const uint8_t*>(P.q) + b * P.q_sb + static_cast<int64_t>(qi) * P.q_st +
+                           h * P.q_sh + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint2 wv = valid ? *reinterpret_cast<const uint2*>(qp8 + 32 * kk) : uint2{0, 0};
+        if constexpr (K8) {
+          qop8[rb][kk] = static_cast<i64x1>((static_cast<uint64_t>(wv.y) << 32) | wv.x);
+        } else {   // E4M3 -> f16, exact
+          qop[rb][kk] = cat4(fp8x2<false>(wv.x), fp8x2<true>(wv.x), fp8x2<false>(wv.y), fp8x2<true>(wv.y));
+        }
+      }
+      continue;
+    }
     const uint16_t* qp = P.q + b * P.q_sb + static_cast<int64_t>(qi) * P.q_st + h * P.q_sh + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -222,6 +251,16 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) kst[j] = kst_off + 16 * ((4 * kq + j) ^ (kt & 15));
   auto stage_k = [&](uint8_t* kb) {
+    if constexpr (K8) {
+      // the token's 32 code bytes as 4 chunks of 8 (elements 32 kq + 8 j ..),
+      // chunk j of row kt at 8 ((4 kq + j) ^ (kt & 14)) of a 128-byte row
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 x = {raw.k[j >> 1][2 * (j & 1)], raw.k[j >> 1][2 * (j & 1) + 1]};
+        lds_st<u32x2>(kb + kt * kD + 8 * ((4 * kq + j) ^ (kt & 14)), x);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f16x8 x;
@@ -290,6 +329,32 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
   // The K operands of sub-tile u + 1 are read from LDS while the MFMAs of
   // sub-tile u run (the scheduling fences keep that order).
   auto qk = [&](const uint8_t* kb, f32x4 (&sc)[2][4]) {
+    if constexpr (K8) {
+      // A = K codes (16 tokens x 32 elements, 8 bytes a lane), B = Q^T codes
+      int kl8[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kl8[kk] = c * kD + 8 * ((4 * kk + g) ^ (c & 14));
+      i64x1 ka8[2][4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) ka8[0][kk] = lds_ld<i64x1>(kb + kl8[kk]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u < 3) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) ka8[(u + 1) & 1][kk] = lds_ld<i64x1>(kb + kl8[kk] + (u + 1) * 16 * kD);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sc[0][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sc[1][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          sc[0][u] = mfma_fp8(ka8[u & 1][kk], qop8[0][kk], sc[0][u]);
+          sc[1][u] = mfma_fp8(ka8[u & 1][kk], qop8[1][kk], sc[1][u]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
     f16x8 ka[2][4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) ka[0][kk] = lds_ld<f16x8>(kb + kld[kk]);
@@ -352,7 +417,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[rb][u][e]);
-      mx = lanes::across_rows<lanes::Max>(mx) * c2;
+      mx = lanes::across_rows<lanes::Max>(mx) * c2r[rb];
       const bool up = mx > m[rb] + kLazy;   // false when mx = -inf
       alpha[rb] = up ? __builtin_amdgcn_exp2f(m[rb] - mx) : 1.f;   // 0 when m = -inf
       m[rb] = up ? mx : m[rb];
@@ -369,7 +434,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[u][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rb][u][e], c2, -m_use));
+          p[u][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rb][u][e], c2r[rb], -m_use));
           sum += p[u][e];
         }
       l[rb] = l[rb] * alpha[rb] + sum;
@@ -481,10 +546,18 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
 template <int KVF, int G>
 hipError_t launch_g(const PrefillParams& p, hipStream_t st) {
   const dim3 grid((p.Sq * G + kRows - 1) / kRows, p.Hkv, p.B);
-  if (p.block_table != nullptr)
-    hipLaunchKernelGGL((k_prefill_gqa<KVF, G, true>), grid, dim3(kThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL((k_prefill_gqa<KVF, G, false>), grid, dim3(kThreads), 0, st, p);
+  const bool q8 = p.q_dtype == KVQ_FP8E4M3;
+  if (p.block_table != nullptr) {
+    if (q8)
+      hipLaunchKernelGGL((k_prefill_gqa<KVF, G, true, true>), grid, dim3(kThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((k_prefill_gqa<KVF, G, true, false>), grid, dim3(kThreads), 0, st, p);
+  } else {
+    if (q8)
+      hipLaunchKernelGGL((k_prefill_gqa<KVF, G, false, true>), grid, dim3(kThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((k_prefill_gqa<KVF, G, false, false>), grid, dim3(kThreads), 0, st, p);
+  }
   return hipGetLastError();
 }
 

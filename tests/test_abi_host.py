@@ -535,6 +535,15 @@ def test_prefill_validation(L, K):
          K.KVQ_ERR_ARG),                                                         # table too short
         (lambda a: (setattr(a, "block_table", FAKE), setattr(a, "block_size", 64), setattr(a, "bt_stride", 16),
                     setattr(a, "kv_sblk", 6)), K.KVQ_ERR_ALIGN),
+        # FP8 queries: a scale is required, per-head flag 0/1, 8-byte codes, aligned scale
+        (lambda a: setattr(a, "q_dtype", K.KVQ_FP8E4M3), K.KVQ_ERR_ARG),
+        (lambda a: (setattr(a, "q_dtype", K.KVQ_FP8E4M3), setattr(a, "q_scale", FAKE),
+                    setattr(a, "q_scale_per_head", 2)), K.KVQ_ERR_ARG),
+        (lambda a: (setattr(a, "q_dtype", K.KVQ_FP8E4M3), setattr(a, "q_scale", FAKE),
+                    setattr(a, "q", FAKE_ODD)), K.KVQ_ERR_ALIGN),
+        (lambda a: (setattr(a, "q_dtype", K.KVQ_FP8E4M3), setattr(a, "q_scale", FAKE_ODD)), K.KVQ_ERR_ALIGN),
+        (lambda a: (setattr(a, "q_dtype", K.KVQ_FP8E4M3), setattr(a, "q_scale", FAKE),
+                    setattr(a, "q_sh", 12)), K.KVQ_ERR_ALIGN),
     ]
     for i, (mutate, want) in enumerate(cases):
         a = _prefill_args(K)

@@ -71,15 +71,20 @@ def gpu_prefill(inp, kp, vp, lens, out_dtype=torch.bfloat16, block_table=None, q
     return out, lse
 
 
-def _check(out, lse, o_ref, lse_ref, label, pv_abs):
+def _check(out, lse, o_ref, lse_ref, label, pv_abs, eps=None):
     """Output: |o - o_ref| <= 2^-11 sum_t P_t |V_t| (P enters the P.V
     contraction as f16: one rounding, <= 2^-11 relative, per probability)
     plus 1e-5 (1 + |o|) of fp32 arithmetic for fp32 output, or plus
     max(2e-3, 1 bf16 ulp(o_ref)) for bf16 output (its RNE rounding), and
     cosine >= 0.9999.  lse: 1e-5 (1 + |lse|), and exactly -inf where the
-    oracle has -inf (queries that see nothing, whose output is 0)."""
+    oracle has -inf (queries that see nothing, whose output is 0).
+    eps [B, Sq, Hq]: a bound on every score's error in the row (FP8 matrix
+    cores, _fp8_score_eps); scores off by at most eps move each probability
+    by a factor within exp(+-2 eps), so the output by at most
+    (exp(2 eps) - 1) sum_t P_t |V_t|, and lse by at most eps."""
     o = out.float().cpu().double().numpy()
-    p_round = 2.0 ** -11 * pv_abs
+    eps = np.zeros(lse_ref.shape) if eps is None else eps
+    p_round = (2.0 ** -11 + np.expm1(2.0 * eps)[..., None]) * pv_abs
     if out.dtype == torch.bfloat16:
         bound = np.maximum(2e-3, OF.bf16_ulp(o_ref)) + p_round
     else:
@@ -94,7 +99,7 @@ def _check(out, lse, o_ref, lse_ref, label, pv_abs):
     assert np.array_equal(np.isneginf(g), ninf), f"{label}: -inf lse pattern differs"
     assert np.all(o[ninf] == 0.0), f"{label}: queries that see nothing must output 0"
     fin = ~ninf
-    assert np.all(np.abs(g[fin] - lse_ref[fin]) <= 1e-5 * (1.0 + np.abs(lse_ref[fin]))), f"{label}: lse"
+    assert np.all(np.abs(g[fin] - lse_ref[fin]) <= 1e-5 * (1.0 + np.abs(lse_ref[fin])) + eps[fin]), f"{label}: lse"
 
 
 CASES = [
@@ -248,3 +253,142 @@ def test_prefill_bench_shape_sampled():
         bound = 1e-5 * (1.0 + np.abs(o1[0, 0, 0])) + 2.0 ** -11 * pv[0, 0, 0]
         assert np.all(np.abs(got - o1[0, 0, 0]) <= bound), f"row (b={b}, i={i}, h={h})"
         assert abs(float(lse[b, i, h]) - l1[0, 0, 0]) <= 1e-5 * (1 + abs(l1[0, 0, 0])), f"lse (b={b}, i={i}, h={h})"
+
+
+# ---------------------------------------------------------------- FP8 queries
+def _quantize_chunk(q, per_head):
+    """The chunk's queries packed by the library's FP8 packer, viewed as
+    [B * Sq, Hq, 1, D] (one scale, or one per query head)."""
+    k_ = K()
+    B, Sq, Hq, D = q.shape
+    q4 = q.contiguous().view(B * Sq, Hq, 1, D)
+    qp = k_.kvq_pack_fp8(q4, k_.kvq_amax(q4, per_head=per_head))
+    return qp.codes.view(B, Sq, Hq, D), qp.scale
+
+
+def _oracle_query(q, per_head):
+    """Oracle FP8 quantization of the chunk (codes, scales, dequantized)."""
+    B, Sq, Hq, D = q.shape
+    codes, scales, qhat = OQ.fp8_quantize_query(kvq_synth.f64(q).reshape(B * Sq, Hq, D), per_head)
+    return codes.reshape(B, Sq, Hq, D), scales, qhat.reshape(B, Sq, Hq, D)
+
+
+# the FP8 matrix core's accumulation error per score, as a fraction of
+# sum_k |q_k k_k| (measured on the device by test_gpu_fp8_mfma.py)
+EPS_FP8_DOT = 2.0 ** -10
+
+
+def _fp8_score_eps(qhat, khat, kv_lens, softmax_scale):
+    """Per query row (b, i, h): EPS_FP8_DOT * softmax_scale * the largest
+    sum_k |q_k| |K_tk| over the keys the row sees (natural-log units)."""
+    B, Sq, Hq, _ = qhat.shape
+    G = Hq // khat.shape[1]
+    eps = np.zeros((B, Sq, Hq))
+    for b in range(B):
+        L = int(kv_lens[b])
+        if L == 0:
+            continue
+        pos = L - Sq + np.arange(Sq)
+        for h in range(Hq):
+            m = np.abs(qhat[b, :, h]) @ np.abs(khat[b, h // G, :L]).T          # [Sq, L]
+            m = np.where(np.arange(L)[None, :] <= pos[:, None], m, 0.0)
+            eps[b, :, h] = EPS_FP8_DOT * softmax_scale * m.max(axis=1)
+    return eps
+
+
+def gpu_prefill_q8(inp, kp, vp, lens, q8, q_scale, out_dtype=torch.float32, block_table=None):
+    k_ = K()
+    out = torch.full(tuple(q8.shape), float("nan"), dtype=out_dtype, device=DEV)
+    lse = torch.full(tuple(q8.shape[:3]), float("nan"), dtype=torch.float32, device=DEV)
+    args = k_.make_prefill_args(q8, kp, vp, lens, out, max_kv_len=inp.Lmax, softmax_scale=inp.softmax_scale,
+                                lse_out=lse, block_table=block_table, q_scale=q_scale)
+    k_.attn_prefill(args)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+Q8_CASES = [
+    # (name, kv fmt, B, Hq, Hkv, kv_lens, Sq, per-head query scale, per-head kv scale)
+    ("fp8cache_gqa4", "fp8", 2, 8, 2, (700, 69), 96, False, False),
+    ("fp8cache_gqa8_perhead", "fp8", 2, 16, 2, (300, 1000), 200, True, True),
+    ("fp8cache_mha_whole", "fp8", 1, 2, 2, (200,), 200, True, False),
+    ("fp8cache_gqa4_longer_than_cache", "fp8", 2, 8, 2, (130, 64), 100, False, True),
+    ("nvfp4cache_gqa4", "nvfp4", 2, 8, 2, (300, 1000), 200, False, False),
+    ("nvfp4cache_gqa2_whole_perhead", "nvfp4", 1, 8, 4, (513,), 513, True, False),
+]
+
+
+@pytest.mark.parametrize("case", Q8_CASES, ids=[c[0] for c in Q8_CASES])
+def test_prefill_fp8_query_matches_oracle(case):
+    """FP8 query codes and scales bit-exact against the oracle's packing;
+    the prefill over them against the oracle's prefill with the dequantized
+    query.  NVFP4 cache: the codes are converted to f16 (exact) and the
+    bf16-query gates hold as they are.  FP8 cache: Q.K^T runs on the FP8
+    matrix cores, and the gates add the effect of their accumulation error
+    (at most EPS_FP8_DOT sum_k |q_k k_k| per score)."""
+    name, fmt, B, Hq, Hkv, lens, Sq, qh, kvh = case
+    announce(f"prefill fp8 query {case}")
+    inp = kvq_synth.prefill(B, Hq, Hkv, 128, list(lens), Sq, outliers=True)
+    q8, q_scale = _quantize_chunk(inp.q.to(DEV), qh)
+    oc, osc, qhat = _oracle_query(inp.q, qh)
+    torch.cuda.synchronize()
+    assert np.array_equal(q8.cpu().numpy(), oc)
+    assert np.array_equal(q_scale.cpu().numpy().astype(np.float64), osc)
+    khat, vhat = _oracle_cache(inp, fmt, per_head=kvh)
+    o_ref, lse_ref = OA.prefill_gqa(qhat, khat, vhat, inp.kv_lens, inp.softmax_scale)
+    pv_abs, _ = OA.prefill_gqa(qhat, khat, np.abs(vhat), inp.kv_lens, inp.softmax_scale)
+    kp, vp, klens = _gpu_planes(inp, fmt, per_head=kvh)
+    eps = _fp8_score_eps(qhat, khat, inp.kv_lens, inp.softmax_scale) if fmt == "fp8" else None
+    out32, lse32 = gpu_prefill_q8(inp, kp, vp, klens, q8, q_scale)
+    _check(out32, lse32, o_ref, lse_ref, f"prefill fp8 query {name} f32", pv_abs, eps)
+    out, lse = gpu_prefill_q8(inp, kp, vp, klens, q8, q_scale, out_dtype=torch.bfloat16)
+    _check(out, lse, o_ref, lse_ref, f"prefill fp8 query {name} bf16", pv_abs, eps)
+    assert torch.equal(out32.to(torch.bfloat16), out)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_prefill_fp8_query_paged_matches_contiguous(fmt):
+    announce(f"prefill fp8 query paged {fmt}")
+    inp = kvq_synth.prefill(2, 8, 2, 128, [900, 333], 160, outliers=True)
+    kp, vp, lens = _gpu_planes(inp, fmt)
+    q8, q_scale = _quantize_chunk(inp.q.to(DEV), True)
+    ref, ref_lse = gpu_prefill_q8(inp, kp, vp, lens, q8, q_scale)
+    kpp, bt = page_plane(kp, 128, 11, inp.kv_lens)
+    vpp, _ = page_plane(vp, 128, 11, inp.kv_lens)
+    got, lse = gpu_prefill_q8(inp, kpp, vpp, lens, q8, q_scale, block_table=bt)
+    assert torch.equal(got, ref) and torch.equal(lse, ref_lse)
+
+
+def test_prefill_fp8_query_bench_shape_sampled():
+    """The FP8 variant of the bench workload (the 32K GQA 4:1 cache packed in
+    FP8, the 1024-token chunk as FP8 codes with one scale): 24 sampled rows
+    against the oracle, each as the truncated-cache reduction, with the FP8
+    matrix cores' score-error term."""
+    announce("prefill fp8 query bench shape, sampled rows")
+    cache = kvq_synth.gqa(BENCH_L)
+    q = kvq_synth.prefill_queries(BENCH_B, BENCH_SQ, BENCH_HQ, 128)
+    inp = kvq_synth.PrefillInputs(q=q, k=cache.k, v=cache.v, kv_lens=cache.kv_lens,
+                                  softmax_scale=cache.softmax_scale)
+    kp, vp, _, _, lens = gpu_pack(cache, "fp8")
+    q8, q_scale = _quantize_chunk(q.to(DEV), False)
+    out, lse = gpu_prefill_q8(inp, kp, vp, lens, q8, q_scale)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    oc, _, qhat = _oracle_query(q, False)
+    assert np.array_equal(q8.cpu().numpy(), oc)
+    from gpu_helpers import oracle_gqa
+    _, _, _, khat, vhat = oracle_gqa(("fp8", "gqa", BENCH_L))
+    rng = np.random.default_rng(9)
+    G = BENCH_HQ // BENCH_HKV
+    for n in range(24):
+        b, i, h = int(rng.integers(BENCH_B)), int(rng.integers(BENCH_SQ)), int(rng.integers(BENCH_HQ))
+        pos = BENCH_L - BENCH_SQ + i
+        qv = qhat[b, i, h][None, None, None]
+        kh, vh = khat[b:b + 1, h // G:h // G + 1], vhat[b:b + 1, h // G:h // G + 1]
+        o1, l1 = OA.prefill_gqa(qv, kh, vh, np.array([pos + 1]), inp.softmax_scale)
+        pv, _ = OA.prefill_gqa(qv, kh, np.abs(vh), np.array([pos + 1]), inp.softmax_scale)
+        eps = EPS_FP8_DOT * inp.softmax_scale * float((np.abs(kh[0, 0, :pos + 1]) @ np.abs(qhat[b, i, h])).max())
+        got = out[b, i, h].cpu().double().numpy()
+        bound = 1e-5 * (1.0 + np.abs(o1[0, 0, 0])) + (2.0 ** -11 + np.expm1(2 * eps)) * pv[0, 0, 0]
+        assert np.all(np.abs(got - o1[0, 0, 0]) <= bound), f"row (b={b}, i={i}, h={h})"
+        assert abs(float(lse[b, i, h]) - l1[0, 0, 0]) <= 1e-5 * (1 + abs(l1[0, 0, 0])) + eps, \
+            f"lse (b={b}, i={i}, h={h})"
