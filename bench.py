@@ -369,11 +369,28 @@ def read_probe(args):
         log(f"read probe grid {grid}: {us:.3f} us/launch, {n / us / 1e3:.1f} GB/s")
     best = min(res, key=res.get)
     us = res[best]
+    # the decode kernels' launch shape: one 256-thread work-group per CU, each
+    # reading one contiguous chunk (as the split-KV work-groups do), with the
+    # chunk streamed as 1, 2 or 4 side-by-side parts
+    lib.kvq_probe_read_chunks.restype = ctypes.c_int
+    lib.kvq_probe_read_chunks.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    chunks = {}
+    for grid, fronts in ((256, 1), (256, 2), (256, 4), (512, 1)):
+        def fc(i, grid=grid, fronts=fronts):
+            rc = lib.kvq_probe_read_chunks(ctypes.c_void_p(bufs[i].data_ptr()), n, grid, fronts,
+                                           ctypes.c_void_p(sink.data_ptr()),
+                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"kvq_probe_read_chunks failed ({rc})")
+        cu = tm.run(fc) * 1e3
+        chunks[f"grid{grid}_fronts{fronts}"] = round(cu, 3)
+        log(f"chunked read grid {grid} fronts {fronts}: {cu:.3f} us/launch, {n / cu / 1e3:.1f} GB/s")
     out = {"metric": "streaming-read ceiling (plain 16-byte-load read, graph of back-to-back launches)",
            "value": round(us, 3), "unit": "us/launch", "bytes_per_launch": n, "steps": args.steps,
            "GB/s": round(n / us / 1e3, 1), "frac_of_8TBs": round(n / us / 1e3 / HBM_PEAK_GBPS, 4),
            "best_grid": best, "threads": 256, "per_grid_us": {str(k): round(v, 3) for k, v in res.items()},
-           "rotation_copies": n_copies}
+           "chunked_us": chunks, "rotation_copies": n_copies}
     print(json.dumps(out), flush=True)
 
 
@@ -757,6 +774,7 @@ def run_mla(args):
     ms_step_pg = tm.run(paged_step)
     ms_split_pg = tm.run(lambda i: K.attn_decode_splitkv(pdargs[i]))
     ms_step_qnv = tm.run(qnv_step)
+    ms_split_qnv = tm.run(lambda i: K.attn_decode_splitkv(qdargs[i]))
     ms_qquant = tm.run(quantize_query)
     assert torch.isfinite(out.float()).all()
     algo = MLA_B * MLA_L * MLA_BYTES_PER_TOKEN
@@ -770,6 +788,7 @@ def run_mla(args):
                       "decode_two_launch_paged64": round(ms_step_pg * 1e3, 3),
                       "split_kernel_paged64": round(ms_split_pg * 1e3, 3),
                       "decode_two_launch_nvfp4_query": round(ms_step_qnv * 1e3, 3),
+                      "split_kernel_nvfp4_query": round(ms_split_qnv * 1e3, 3),
                       "quantize_query_nvfp4": round(ms_qquant * 1e3, 3)}
     res["roofline"] = roofline(algo, ms_split * 1e3, "k_decode_mla (split kernel, partials)", measured_traffic("mla"))
     if not args.no_cpu_baseline:

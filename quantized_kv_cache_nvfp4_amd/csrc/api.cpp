@@ -218,15 +218,15 @@ int kvq_auto_num_splits(int32_t num_cus, int32_t B, int32_t programs_per_req, in
   if (num_cus <= 0 || B <= 0 || programs_per_req <= 0 || Dv <= 0 || Hq <= 0 || max_kv_len < 0)
     return fail(KVQ_ERR_ARG, "kvq_auto_num_splits: non-positive argument");
   // 1) enough work-groups for every compute unit: one each where the query
-  //    group has 4 or more heads of at most 256 columns (the GQA kernel then
-  //    runs its grouped tiles, which keep two tiles of loads in flight per
-  //    wave; fewer partials make the combine cheaper), two each otherwise
-  //    (the single-register-set tiles of query groups of 1 or 2 and the MLA
-  //    kernel's per-tile chain need a second work-group per CU to cover their
-  //    load latency).  Measured on MI355X: GQA 4:1 B=2 at 8K and 32K fastest
-  //    at 16 splits, MHA B=1/2 at 32K at 2 work-groups per CU.
+  //    group has 4 or more heads (the GQA kernel then runs its grouped
+  //    tiles, which keep two tiles of loads in flight per wave, and the MLA
+  //    kernel's work-groups are 8 waves, two per SIMD; fewer partials make
+  //    the combine cheaper), two each otherwise (the single-register-set
+  //    tiles of query groups of 1 or 2 need a second work-group per CU to
+  //    cover their load latency).  Measured on MI355X: GQA 4:1 B=2 at 8K and
+  //    32K fastest at 16 splits, MHA B=1/2 at 32K at 2 work-groups per CU.
   const int64_t base = static_cast<int64_t>(B) * programs_per_req;
-  const int64_t per_cu = (static_cast<int64_t>(Hq) >= 4LL * programs_per_req && Dv <= 256) ? 1 : 2;
+  const int64_t per_cu = static_cast<int64_t>(Hq) >= 4LL * programs_per_req ? 1 : 2;
   int64_t s = (per_cu * num_cus + base - 1) / base;
   // 2) no split shorter than 256 tokens
   const int64_t by_len = (static_cast<int64_t>(max_kv_len) + 255) / 256;

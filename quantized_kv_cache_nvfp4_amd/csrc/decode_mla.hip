@@ -10,44 +10,48 @@
 // attention for vLLM serving", Testing section.
 //
 // Design for CDNA4:
-//  * one work-group = 4 waves = one chunk of one request; all 16 query
-//    heads share every latent row, so they are the 16 MFMA rows and no
-//    query-group packing is needed.
-//  * tiles of 64 tokens (4 sub-tiles of 16).  Scores: wave w covers the
-//    sub-tiles u = (w & 1) + 2q of the tile over latent half (w >> 1) (256
-//    dims) and rope half (32 dims): per sub-tile 8 MFMA 16x16x32 f16 steps
-//    over the dequantized latent plus one bf16 step over the rope; the two
-//    latent halves' partial scores meet in LDS.  The dequantized latent rows
-//    (f16) are staged in LDS.  Two barriers per tile.
+//  * one work-group = 8 waves = one chunk of one request, as two groups of
+//    4 waves that take alternate tiles of the chunk and merge their states
+//    at the end (half the partials of two 4-wave work-groups per compute
+//    unit, at the same two waves per SIMD); all 16 query heads share every
+//    latent row, so they are the 16 MFMA columns and no query-group packing
+//    is needed.
+//  * tiles of 64 tokens; wave w owns sub-tile w (16 tokens) whole: its
+//    scores over the full latent (16 MFMA 16x16x32 f16 steps over the
+//    dequantized rows) plus the rope (2 bf16 steps), its softmax, and the
+//    staging of its 16 dequantized rows (f16) into LDS.  Nothing of the
+//    scores crosses waves; the probabilities do, through LDS (fp32), with
+//    the reference each wave used.
+//  * one reference maximum per head, shared by the four waves and raised
+//    lazily: a wave whose tile maximum exceeds it by more than 2^8 (in P)
+//    uses its own and says so; after the barrier every wave takes the
+//    largest reference of the tile, rescales its accumulators when that
+//    moved, and scales the probabilities of waves that used a smaller one
+//    (exact fp32 products, then one rounding to f16).  Most tiles need no
+//    rescale and no correction (wave-uniform branches).
 //  * P.V: wave w owns output columns 128w .. 128w+127 for all 64 tokens (two
 //    32-token steps); its A operand (latent, token-contiguous per column)
 //    comes from the staged rows through the LDS transpose read
 //    ds_read_b64_tr_b16, so the latent is dequantized once and used by both
-//    contractions, and its B operand (P) is already in the right lanes (the
-//    token order of the P.V contraction is chosen to match the score
-//    layout).
-//  * every wave computes the softmax of the whole tile (8 scores per lane),
-//    so the four waves share one reference maximum and one denominator.
+//    contractions, and its B operand (P) is read from LDS in the token order
+//    of that contraction.  Two barriers per tile.
+//  * the head_dim order of Q.K^T is free: lane group g of load instruction
+//    k reads bytes [64 k + 16 g, +16) of its token's latent codes (each
+//    instruction covers 64 contiguous bytes of every row), i.e. latent dims
+//    128 k + 32 g .. + 31, and the query operand follows the same order.
 //  * loads use buffer resources sized to the chunk (tokens past its end read
 //    zeros), as in the GQA kernel.
 //  * paged caches (vLLM-style block tables): the block size is a power of
 //    two and a multiple of the tile, so every 64-token tile lies in one
 //    block; a work-group copies its chunk's table entries into LDS once and
-//    addresses each tile through them (the first tile through an entry read
-//    directly, so that its loads need not wait for the copy).
+//    addresses each tile through them (each group's first tile through an
+//    entry read directly, so that its loads need not wait for the copy).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "decode_common.h"
 #include "kvq_internal.h"
 #include "wave_reduce.h"
-
-#ifndef KVQ_MLA_AHEAD
-#define KVQ_MLA_AHEAD 1
-#endif
-#ifndef KVQ_MLA_TILE
-#define KVQ_MLA_TILE 64
-#endif
 
 namespace kvq {
 namespace {
@@ -58,17 +62,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kW = 4;                      // waves per work-group
-constexpr int kThreads = 64 * kW;
-constexpr int kT = KVQ_MLA_TILE;           // tokens per tile (32 or 64)
-constexpr int kQ = kT / 32;                // 16-token sub-tiles per wave: u = th + 2 q, q < kQ
-constexpr int kH = 16;                     // query heads (MFMA rows)
+constexpr int kW = 4;                      // waves per group
+constexpr int kGrp = 2;                    // groups per work-group (alternate tiles)
+constexpr int kThreads = 64 * kW * kGrp;
+constexpr int kT = 16 * kW;                // tokens per tile: wave w owns tokens 16 w .. 16 w + 15
+constexpr int kH = 16;                     // query heads (MFMA columns)
 constexpr int kD = 512;                    // latent rank
 constexpr int kDr = 64;                    // rope dims
 constexpr int kRow = kD / 2;               // latent code bytes per token
 constexpr int kSRow = kD / 16;             // latent scale bytes per token
 constexpr int kPitch = kD * 2 + 32;        // staged f16 row pitch in LDS (bytes; +32 spreads banks)
-constexpr int kAhead = KVQ_MLA_AHEAD;      // tiles loaded ahead of the one being computed
+constexpr int kPPitch = kT + 4;            // P^T row pitch in LDS (floats, one row per head)
+constexpr float kLazy = 8.0f;              // a wave's own reference only past P = 2^8
 
 __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -77,22 +82,28 @@ __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 // QNV: the latent query q_c arrives as NVFP4 codes + block scales + tensor
 // scale (dequantized exactly to f16 in the prologue) instead of bf16
 template <bool PAGED, bool QNV>
-__global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, int num_splits) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_c[kT * kPitch];   // staged latent rows (f16)
-  __shared__ __attribute__((aligned(16))) f32x4 lds_s[kW][kQ][64];      // partial scores per wave, sub-tile, lane
-  __shared__ int lds_bt[PAGED ? kMlaPagedMaxChunkBlocks : 1];          // paged: the chunk's block-table entries
+__global__ void __launch_bounds__(kThreads, 1) k_decode_mla(kvq_decode_args a, int num_splits) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_c_[kGrp][kT * kPitch];   // staged latent rows (f16)
+  __shared__ __attribute__((aligned(16))) float lds_p_[kGrp][kH * kPPitch];    // the tile's P^T (fp32), head rows
+  __shared__ __attribute__((aligned(16))) float lds_r_[kGrp][kH][kW];          // each wave's reference per head
+  __shared__ int lds_bt[PAGED ? kMlaPagedMaxChunkBlocks : 1];                  // paged: the chunk's block-table entries
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 15;   // MFMA row / column index of this lane
+  const int w8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = w8 >> 2;   // this wave's group: tiles grp, grp + 2, grp + 4, ...
+  const int wave = w8 & 3;   // its role in the group: sub-tile, output columns
+  uint8_t* const lds_c = lds_c_[grp];
+  float* const lds_p = lds_p_[grp];
+  float (*const lds_r)[kW] = lds_r_[grp];
+  const int c = lane & 15;   // MFMA row (token) / column (head) index of this lane
   const int g = lane >> 4;   // lane group (k-slice of the MFMA operands)
-  const int th = wave & 1;   // token half of the tile this wave scores
-  const int dh = wave >> 1;  // latent / rope half this wave scores
   // LDS bank spreading of the staged rows: chunk k (16 bytes) of row r sits at
   // k ^ swz(r), swz(r) = bit 2 of r xor bit 3 of r, which makes both the
   // row-wise 16-byte stores and the transposed 8-byte reads conflict-free.
-  const int swz_w = ((c >> 2) ^ (c >> 3)) & 1;   // rows 16 th + c (stores)
+  const int swz_w = ((c >> 2) ^ (c >> 3)) & 1;   // rows 16 w + c (stores)
   const int swz_r = (g ^ (g >> 1)) & 1;          // rows 4 g + m/4 and 16 + 4 g + m/4 (transposed reads)
+  // the two scale bytes of this lane's blocks 8 k + 2 g, + 1 out of a pair of scale dwords
+  const uint32_t ssel = static_cast<uint32_t>(2 * g) | (static_cast<uint32_t>(2 * g + 1) << 8);
   const int split = blockIdx.x;
   const int b = blockIdx.y;
 
@@ -120,7 +131,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
   const int bsh = PAGED ? __builtin_ctz(static_cast<unsigned>(bs)) : 0;
   const int blk0 = cs >> bsh;
   int L = 0, ce = 0;
-  int64_t first_row = 0;   // paged: plane row of the chunk's first token
+  int64_t first_row = 0;   // paged: plane row of the group's first tile (tile grp)
   if constexpr (PAGED) {
     L = a.kv_lens[b];
     L = L < a.max_kv_len ? L : a.max_kv_len;
@@ -128,17 +139,20 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     ce = (cs + chunk < L) ? cs + chunk : L;
     ce_ld = ce;
     const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.bt_stride + blk0;
-    if (cs < ce) first_row = static_cast<int64_t>(bt[0]) * a.kv_sblk + static_cast<int64_t>(cs & (bs - 1)) * st;
+    const int ft = cs + grp * kT;
+    if (ft < ce)
+      first_row = static_cast<int64_t>(bt[(ft >> bsh) - blk0]) * a.kv_sblk + static_cast<int64_t>(ft & (bs - 1)) * st;
     const int nblk = ce > cs ? ((ce - 1) >> bsh) - blk0 + 1 : 0;
     for (int i = threadIdx.x; i < nblk; i += kThreads) lds_bt[i] = bt[i];
   }
   // plane row of tile's first token (relative to the request's base when
   // the cache is contiguous); tiles past the chunk's end get 0 (they load
-  // nothing).  Paged tiles after the first read the LDS copy of the table.
+  // nothing).  Paged tiles after the group's first read the LDS copy of the
+  // table.
   auto tile_row = [&](int tile) -> int64_t {
     const int tb = cs + tile * kT;
     if constexpr (PAGED) {
-      if (tile == 0) return first_row;
+      if (tile == grp) return first_row;
       if (tb >= ce_ld) return 0;
       return static_cast<int64_t>(lds_bt[(tb >> bsh) - blk0]) * a.kv_sblk + static_cast<int64_t>(tb & (bs - 1)) * st;
     } else {
@@ -146,68 +160,107 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     }
   };
 
-  // loads of one tile: for each of the wave's sub-tiles u = th + 2 q, token
-  // 16 u + c; latent bytes [128 dh + 32 g, +32), scale bytes [16 dh + 4 g,
-  // +4), rope bytes [64 dh + 16 g, +16).  Tokens at or past the load bound
+  // loads of one tile for this wave's sub-tile: token 16 w + c; latent code
+  // bytes [64 k + 16 g, +16) for k < 4, the token's 32 scale bytes, rope
+  // bytes [64 k + 16 g, +16) for k < 2.  Tokens at or past the load bound
   // ce_ld read zeros; a tile past it reads nothing.
   struct Raw {
-    u32x4 cw0[kQ], cw1[kQ], rw[kQ];
-    uint32_t sw[kQ];
+    u32x4 cw[4], sw[2], rw[2];
   };
   auto load_tile = [&](Raw& R, int tile) {
     const int64_t trow = tile_row(tile);
+    const int nv = ce_ld - (cs + tile * kT + 16 * wave);
+    const int64_t r0 = trow + static_cast<int64_t>(16 * wave) * st;
+    const Rsrc rc_ = make_rsrc(cc + r0 * kRow, nv * st * kRow);
+    const Rsrc rs_ = make_rsrc(csc + r0 * kSRow, nv * st * kSRow);
+    const Rsrc rr_ = make_rsrc(cr + r0 * (kDr * 2), nv * st * (kDr * 2));
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const int t0 = cs + tile * kT + 16 * (th + 2 * q);
-      const int nv = ce_ld - t0;
-      const int64_t r0 = trow + static_cast<int64_t>(16 * (th + 2 * q)) * st;
-      const Rsrc rc_ = make_rsrc(cc + r0 * kRow, nv * st * kRow);
-      const Rsrc rs_ = make_rsrc(csc + r0 * kSRow, nv * st * kSRow);
-      const Rsrc rr_ = make_rsrc(cr + r0 * (kDr * 2), nv * st * (kDr * 2));
-      R.cw0[q] = ld128(rc_, c * st * kRow + 128 * dh + 32 * g);
-      R.cw1[q] = ld128(rc_, c * st * kRow + 128 * dh + 32 * g + 16);
-      R.sw[q] = ld32(rs_, c * st * kSRow + 16 * dh + 4 * g);
-      R.rw[q] = ld128(rr_, c * st * (kDr * 2) + 64 * dh + 16 * g);
-    }
+    for (int k = 0; k < 4; ++k) R.cw[k] = ld128(rc_, c * st * kRow + 64 * k + 16 * g);
+    R.sw[0] = ld128(rs_, c * st * kSRow);
+    R.sw[1] = ld128(rs_, c * st * kSRow + 16);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) R.rw[k] = ld128(rr_, c * st * (kDr * 2) + 64 * k + 16 * g);
   };
-  // ---- query words, lane (g, c) = head c:
-  //   latent MFMA j (0..7): dims 256 dh + 64 g + 8 j + e; rope: 32 dh + 8 g + e
-  //   (NVFP4 latent query: the same 64 elements are code bytes [128 dh +
-  //   32 g, +32) and scale bytes [16 dh + 4 g, +4) of head c's row)
-  uint4 qraw[8], qrraw;
-  uint32_t qsw = 0;
-  {
-    if constexpr (QNV) {
-      const int64_t qrow = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(c) * a.q_sh;
-      const uint8_t* qc = static_cast<const uint8_t*>(a.q) + qrow * (kD / 2) + 128 * dh + 32 * g;
-      qraw[0] = *reinterpret_cast<const uint4*>(qc);
-      qraw[1] = *reinterpret_cast<const uint4*>(qc + 16);
-      qsw = *reinterpret_cast<const uint32_t*>(a.q_block_scales + qrow * (kD / 16) + 16 * dh + 4 * g);
-    } else {
-      const uint16_t* qc = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * a.q_sb +
-                           static_cast<int64_t>(c) * a.q_sh + 256 * dh + 64 * g;
+  // scale dwords 2 k, 2 k + 1 of a 32-byte scale row -> f16 scales of blocks 8 k + 2 g, + 1
+  auto block_scales = [&](const u32x4 (&sw)[2], int k) -> f16x2 {
+    const u32x4 v = sw[k >> 1];
+    const uint32_t lo = (k & 1) ? v[2] : v[0], hi = (k & 1) ? v[3] : v[1];
+    return fp8x2<false>(__builtin_amdgcn_perm(hi, lo, ssel));
+  };
+
+  // ---- the request's query, read once per work-group with coalesced
+  // 16-byte loads (thread t: chunks t, t + 512) and staged in the second
+  // group's row area, which is free until its first tile: latent rows of
+  // kQRow bytes per head, then rope rows of kRRow bytes (each padded by 16
+  // bytes, so that the operand reads below are conflict-free).
+  constexpr int kQRow = (QNV ? kD / 2 : kD * 2) + 16;   // latent query row pitch (bytes)
+  constexpr int kQsOff = kH * kQRow;                     // NVFP4: the scale rows (32 bytes + 16)
+  constexpr int kQrOff = kQsOff + (QNV ? kH * 48 : 0);   // the rope rows (128 bytes + 16)
+  constexpr int kQLat = kH * (QNV ? kD / 32 : kD / 8);   // 16-byte chunks of the latent query
+  constexpr int kQSc = QNV ? kH * 2 : 0;                 //   of its scales
+  constexpr int kQChunks = kQLat + kQSc + kH * 8;        //   in all
+  uint8_t* const lds_q = lds_c_[1];
+  uint4 qstage[(kQChunks + kThreads - 1) / kThreads];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qraw[j] = *reinterpret_cast<const uint4*>(qc + 8 * j);
+  for (int r = 0; r < (kQChunks + kThreads - 1) / kThreads; ++r) {
+    const int i = static_cast<int>(threadIdx.x) + r * kThreads;
+    if (i < kQLat) {
+      constexpr int per = QNV ? kD / 32 : kD / 8;   // chunks per head row
+      const int h = i / per, k = i % per;
+      const int64_t qrow = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(h) * a.q_sh;
+      qstage[r] = QNV ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) + qrow * (kD / 2) + 16 * k)
+                      : *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qrow + 8 * k);
+    } else if (i < kQLat + kQSc) {
+      const int u = i - kQLat, h = u >> 1;
+      const int64_t qrow = static_cast<int64_t>(b) * a.q_sb + static_cast<int64_t>(h) * a.q_sh;
+      qstage[r] = *reinterpret_cast<const uint4*>(a.q_block_scales + qrow * (kD / 16) + 16 * (u & 1));
+    } else if (i < kQChunks) {
+      const int u = i - kQLat - kQSc, h = u >> 3;
+      qstage[r] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q_rope) +
+                                                  static_cast<int64_t>(b) * a.qr_sb +
+                                                  static_cast<int64_t>(h) * a.qr_sh + 8 * (u & 7));
     }
-    const uint16_t* qrp = static_cast<const uint16_t*>(a.q_rope) + static_cast<int64_t>(b) * a.qr_sb +
-                          static_cast<int64_t>(c) * a.qr_sh + 32 * dh + 8 * g;
-    qrraw = *reinterpret_cast<const uint4*>(qrp);
   }
 
-  // the first kAhead tiles, requested with the query and the request length
-  // (one memory round trip); kAhead tiles are in flight while one computes:
-  // buffer (tile mod kAhead+1) holds tile's data.  Tiles past the chunk load
-  // nothing.
-  Raw buf[kAhead + 1];
+  // the group's first tile, requested with the query and the request length
+  // (one memory round trip); one tile is in flight while one computes
+  Raw buf[2];
+  load_tile(buf[0], grp);
+  __builtin_amdgcn_sched_barrier(0);
+
 #pragma unroll
-  for (int k = 0; k < kAhead; ++k) {
-    load_tile(buf[k], k);
-    __builtin_amdgcn_sched_barrier(0);   // issue order = tile order, so a wait for one tile spares the later ones
+  for (int r = 0; r < (kQChunks + kThreads - 1) / kThreads; ++r) {
+    const int i = static_cast<int>(threadIdx.x) + r * kThreads;
+    int off = -1;
+    if (i < kQLat) {
+      constexpr int per = QNV ? kD / 32 : kD / 8;
+      off = (i / per) * kQRow + 16 * (i % per);
+    } else if (i < kQLat + kQSc) {
+      const int u = i - kQLat;
+      off = kQsOff + (u >> 1) * 48 + 16 * (u & 1);
+    } else if (i < kQChunks) {
+      const int u = i - kQLat - kQSc;
+      off = kQrOff + (u >> 3) * 144 + 16 * (u & 7);
+    }
+    if (off < 0) continue;
+    if (!QNV && i < kQLat) {   // bf16 pair -> fp32 (exact) -> f16 (exact in f16's normal range)
+      const uint4 w = qstage[r];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      f16x2 h[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        h[k] = f16x2{static_cast<_Float16>(__uint_as_float(ws[k] << 16)),
+                     static_cast<_Float16>(__uint_as_float(ws[k] & 0xFFFF0000u))};
+      *reinterpret_cast<f16x8*>(lds_q + off) = cat4(h[0], h[1], h[2], h[3]);
+    } else {
+      *reinterpret_cast<uint4*>(lds_q + off) = qstage[r];
+    }
   }
 
-  if constexpr (PAGED) {
-    __syncthreads();   // the LDS table copy is visible to the later tiles' loads
-  } else {
+  __syncthreads();   // the staged query (and, paged, the LDS table copy) are visible
+
+
+  if constexpr (!PAGED) {
     L = a.kv_lens[b];
     L = L < a.max_kv_len ? L : a.max_kv_len;
     L = L > 0 ? L : 0;
@@ -215,143 +268,150 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     ce_ld = ce;   // later loads stop at the request's end
   }
   const int ntiles = cs < ce ? (ce - cs + kT - 1) / kT : 0;
+  // both groups run the same number of steps (their barriers are the
+  // work-group's): with an odd tile count the second group's last step is
+  // a tile past the chunk, which loads nothing and has every token masked
+  const int nsteps = (ntiles + 1) / 2;
 
   const float s_t = *a.k_scale;
   // latent scores carry the tensor scale of the latent (and of an NVFP4 query)
   const float sc_lat = a.softmax_scale * s_t * (QNV ? *a.q_scale : 1.0f) * kLog2e;
   const float sc_rope = a.softmax_scale * kLog2e;
 
-  f16x8 qop[8];
+  // ---- query operand, lane (g, c) = head c: latent MFMA J = 4 k + jj
+  //   (0..15) takes dims 128 k + 32 g + 8 jj .. + 7 (f16: the bf16 query
+  //   converted by the staging; NVFP4: code bytes [64 k + 16 g, +16) and
+  //   the scales of head c's row, dequantized here, E2M1 x E4M3 exact in
+  //   f16); rope MFMA k (0, 1) dims 32 k + 8 g .. + 7 (bf16)
+  f16x8 qop[16];
+  if constexpr (QNV) {
+    u32x4 qsw[2];
+    qsw[0] = *reinterpret_cast<const u32x4*>(lds_q + kQsOff + c * 48);
+    qsw[1] = *reinterpret_cast<const u32x4*>(lds_q + kQsOff + c * 48 + 16);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if constexpr (QNV) {
-      // elements 8j..8j+7 of the lane's 64: code dword j, block j / 2
-      // (E2M1 x E4M3 is exact in f16)
-      const uint4& qw = j < 4 ? qraw[0] : qraw[1];
-      const uint32_t w = (j & 3) == 0 ? qw.x : ((j & 3) == 1 ? qw.y : ((j & 3) == 2 ? qw.z : qw.w));
-      const f16x2 s2 = fp8x2<false>(qsw >> (16 * ((j >> 1) >> 1)));
-      const _Float16 sv = ((j >> 1) & 1) ? s2[1] : s2[0];
-      const f16x2 sp = f16x2{sv, sv};
-      qop[j] = cat4(fp4x2<0>(w) * sp, fp4x2<1>(w) * sp, fp4x2<2>(w) * sp, fp4x2<3>(w) * sp);
-      continue;
+    for (int k = 0; k < 4; ++k) {
+      const u32x4 qw = *reinterpret_cast<const u32x4*>(lds_q + c * kQRow + 64 * k + 16 * g);
+      const f16x2 s2 = block_scales(qsw, k);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const _Float16 sv = jj < 2 ? s2[0] : s2[1];
+        const f16x2 sp = f16x2{sv, sv};
+        const uint32_t w = qw[jj];
+        qop[4 * k + jj] = cat4(fp4x2<0>(w) * sp, fp4x2<1>(w) * sp, fp4x2<2>(w) * sp, fp4x2<3>(w) * sp);
+      }
     }
-    const uint32_t ws[4] = {qraw[j].x, qraw[j].y, qraw[j].z, qraw[j].w};
-    f16x2 h[4];
+  } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)   // bf16 pair -> fp32 (exact) -> f16 (exact in f16's normal range)
-      h[k] = f16x2{static_cast<_Float16>(__uint_as_float(ws[k] << 16)),
-                   static_cast<_Float16>(__uint_as_float(ws[k] & 0xFFFF0000u))};
-    qop[j] = cat4(h[0], h[1], h[2], h[3]);
+    for (int J = 0; J < 16; ++J)
+      qop[J] = *reinterpret_cast<const f16x8*>(lds_q + c * kQRow + 256 * (J >> 2) + 64 * g + 16 * (J & 3));
   }
-  const bf16x8 qr = __builtin_bit_cast(bf16x8, qrraw);
+  const bf16x8 qr[2] = {*reinterpret_cast<const bf16x8*>(lds_q + kQrOff + c * 144 + 16 * g),
+                        *reinterpret_cast<const bf16x8*>(lds_q + kQrOff + c * 144 + 64 + 16 * g)};
+  __syncthreads();   // every wave holds its query operand: the staging area is free
 
-  float m_run = -INFINITY;   // running max of head c (log2 domain), the same in every wave
-  float l_run = 0.0f;        // this lane's share of head c's denominator (its 8 tokens per tile)
+  float m_ref = -INFINITY;   // reference maximum of head c (log2 domain), the same in every wave
+  float l_run = 0.0f;        // this lane's share of head c's denominator (its tokens, against m_ref)
   f32x4 acc_o[8];            // O^T rows d = 128*wave + 16*jj + 4g + i, column head c
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc_o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  uint8_t* const stage = lds_c + (16 * wave + c) * kPitch;   // this lane's staged row (token 16 w + c)
+
   auto process = [&](Raw& cur, int tile) {
     const int tb = cs + tile * kT;
-    // the chunk's last tile: rows of tokens at or past the request's end
-    // (read before the length was known) become zeros, so that the staged
-    // latent of masked tokens is 0 (their probability is 0).  (The empty asm
-    // keeps this a branch taken once per chunk instead of selects on every
-    // tile.)
+    // the chunk's last tile: the row of a token at or past the request's end
+    // (read before the length was known) becomes zeros, so that its staged
+    // latent is 0 (its probability is 0).  (The empty asm keeps this a
+    // branch taken once per chunk instead of selects on every tile.)
     if (tb + kT > ce) {
       asm volatile("");
+      if (tb + 16 * wave + c >= ce) {
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        if (tb + 16 * (th + 2 * q) + c >= ce) {
-          cur.cw0[q] = u32x4{0u, 0u, 0u, 0u};
-          cur.cw1[q] = cur.cw0[q];
-          cur.rw[q] = cur.cw0[q];
-          cur.sw[q] = 0u;
-        }
+        for (int k = 0; k < 4; ++k) cur.cw[k] = u32x4{0u, 0u, 0u, 0u};
+        cur.sw[0] = cur.sw[1] = cur.rw[0] = cur.rw[1] = u32x4{0u, 0u, 0u, 0u};
       }
     }
 
-    // ---- partial scores S^T[token][head] of the wave's sub-tiles over its
-    // latent / rope halves; stage the f16 rows.  (Two latent accumulators,
-    // even and odd steps: half the dependent MFMA chain.)
+    // ---- scores S^T[token 16 w + 4 g + i][head c] over the whole latent and
+    // rope; stage the f16 rows (chunk 16 k + 4 g + jj of the row, swizzled).
+    // Four latent accumulators: dependent MFMA chains of 4.
+    f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 acc_r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const u32x4 cw0 = cur.cw0[q], cw1 = cur.cw1[q], rw = cur.rw[q];
-      const uint32_t sw = cur.sw[q];
-      f32x4 acc_l[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, acc_r = {0.f, 0.f, 0.f, 0.f};
-      // token row 16 u + c (u = th + 2 q), dims 256 dh + 64 g ..; 16-byte
-      // chunk k of the row is stored at k ^ swz(row) (swz uses row bits 2
-      // and 3, those of c)
-      uint8_t* stage = lds_c + (16 * (th + 2 * q) + c) * kPitch + 512 * dh + 128 * g;
-      uint8_t* const stage_even = stage + 16 * swz_w;   // chunks with even k move by +16 bytes when swz = 1
-      uint8_t* const stage_odd = stage - 16 * swz_w;    // odd k by -16
-      const f16x2 sp0 = fp8x2<false>(sw), sp1 = fp8x2<true>(sw);             // scales of the lane's 4 blocks
+    for (int k = 0; k < 4; ++k) {
+      const f16x2 sp = block_scales(cur.sw, k);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t w = (j < 4) ? cw0[j] : cw1[j - 4];
-        const _Float16 sv = (j < 4) ? ((j < 2) ? sp0[0] : sp0[1]) : ((j < 6) ? sp1[0] : sp1[1]);   // block j/2
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t w = cur.cw[k][jj];
+        const _Float16 sv = jj < 2 ? sp[0] : sp[1];
         const f16x2 s2 = {sv, sv};
         const f16x8 kop = cat4(fp4x2<0>(w) * s2, fp4x2<1>(w) * s2, fp4x2<2>(w) * s2, fp4x2<3>(w) * s2);
-        acc_l[j & 1] = mfma(kop, qop[j], acc_l[j & 1]);
-        *reinterpret_cast<f16x8*>(((j & 1) ? stage_odd : stage_even) + 16 * j) = kop;
+        acc[jj] = mfma(kop, qop[4 * k + jj], acc[jj]);
+        *reinterpret_cast<f16x8*>(stage + 16 * ((16 * k + 4 * g + jj) ^ swz_w)) = kop;
       }
-      acc_r = mfma_bf16(__builtin_bit_cast(bf16x8, rw), qr, acc_r);
-      f32x4 ps;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ps[i] = (acc_l[0][i] + acc_l[1][i]) * sc_lat + acc_r[i] * sc_rope;
-      lds_s[wave][q][lane] = ps;
     }
-    __syncthreads();   // staged rows and partial scores visible
-
-    // ---- the whole tile's scores for this lane: tokens 16 u + 4 g + i of
-    // every sub-tile u (latent halves: waves (u & 1) and 2 + (u & 1))
-    float sc[2 * kQ][4];
 #pragma unroll
-    for (int u = 0; u < 2 * kQ; ++u) {
-      const f32x4 p0 = lds_s[u & 1][u >> 1][lane], p1 = lds_s[2 + (u & 1)][u >> 1][lane];
+    for (int k = 0; k < 2; ++k) acc_r = mfma_bf16(__builtin_bit_cast(bf16x8, cur.rw[k]), qr[k], acc_r);
+    float sc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[u][i] = p0[i] + p1[i];
-    }
+    for (int i = 0; i < 4; ++i) sc[i] = ((acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i])) * sc_lat + acc_r[i] * sc_rope;
     if (tb + kT > ce) {   // the chunk's last tile (uniform branch)
       asm volatile("");
 #pragma unroll
-      for (int u = 0; u < 2 * kQ; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tb + 16 * u + 4 * g + i >= ce) sc[u][i] = -INFINITY;
+      for (int i = 0; i < 4; ++i)
+        if (tb + 16 * wave + 4 * g + i >= ce) sc[i] = -INFINITY;
     }
-    float tm = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 2 * kQ; ++u)
-      tm = fmaxf(tm, fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
+
+    // ---- softmax of the wave's 16 tokens against the shared reference,
+    // or against the wave's own maximum when that exceeds it by more than 2^8
+    float tm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     tm = lanes::across_rows<lanes::Max>(tm);   // head c's max over the four lane groups
-    if (__any(tm > m_run)) {   // the same decision for column c in every wave
-      const bool bump = tm > m_run;
-      const float fac = bump ? __builtin_amdgcn_exp2f(m_run - tm) : 1.0f;   // 0 when m_run = -inf
+    const float r = tm > m_ref + kLazy ? tm : m_ref;
+    const float ru = r == -INFINITY ? 0.0f : r;
+    f32x4 p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - ru);   // masked: exp2(-inf) = 0
+    const float l_tile = (p[0] + p[1]) + (p[2] + p[3]);
+    *reinterpret_cast<f32x4*>(lds_p + c * kPPitch + 16 * wave + 4 * g) = p;
+    if (g == 0) lds_r[c][wave] = r;
+    __syncthreads();   // staged rows, P and the references visible
+
+    // ---- the tile's reference: the largest any wave used (>= m_ref)
+    const f32x4 rr = *reinterpret_cast<const f32x4*>(&lds_r[c][0]);
+    const float R = fmaxf(fmaxf(rr[0], rr[1]), fmaxf(rr[2], rr[3]));
+    if (__any(R > m_ref)) {   // the same decision for column c in every wave
+      const float fac = R > m_ref ? __builtin_amdgcn_exp2f(m_ref - R) : 1.0f;   // 0 when m_ref = -inf
       l_run *= fac;
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc_o[jj][i] *= fac;
-      m_run = bump ? tm : m_run;
+      m_ref = fmaxf(m_ref, R);
     }
-    const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
-    // B operand of P.V step ks (k = 8g + e): e < 4 -> token 4g+e of sub-tile
-    // 2 ks, e >= 4 -> token 4g+e-4 of sub-tile 2 ks + 1
-    f16x8 pb[kQ];
+    l_run += r == R ? l_tile : l_tile * __builtin_amdgcn_exp2f(r - R);
+
+    // ---- B operand of P.V step ks (k = 8 g + e): e < 4 -> token 32 ks + 4 g
+    // + e (wave 2 ks), e >= 4 -> token 32 ks + 16 + 4 g + e - 4 (wave 2 ks + 1);
+    // a wave that used a smaller reference has its P scaled down to R first
+    const bool fix = __any(rr[0] != R || rr[1] != R || rr[2] != R || rr[3] != R);
+    f16x8 pb[2];
 #pragma unroll
-    for (int ks = 0; ks < kQ; ++ks) {
-      f16x2 ph[4];
+    for (int ks = 0; ks < 2; ++ks) {
+      f32x4 p0 = *reinterpret_cast<const f32x4*>(lds_p + c * kPPitch + 32 * ks + 4 * g);
+      f32x4 p1 = *reinterpret_cast<const f32x4*>(lds_p + c * kPPitch + 32 * ks + 16 + 4 * g);
+      if (fix) {
+        const float r0 = rr[2 * ks], r1 = rr[2 * ks + 1];
+        const float f0 = r0 == R ? 1.0f : __builtin_amdgcn_exp2f(r0 - R);
+        const float f1 = r1 == R ? 1.0f : __builtin_amdgcn_exp2f(r1 - R);
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float p0 = __builtin_amdgcn_exp2f(sc[2 * ks + x][2 * k] - m_ref);   // masked: exp2(-inf) = 0
-          const float p1 = __builtin_amdgcn_exp2f(sc[2 * ks + x][2 * k + 1] - m_ref);
-          l_run += p0 + p1;
-          ph[2 * x + k] = f16x2{static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
+        for (int i = 0; i < 4; ++i) {
+          p0[i] *= f0;
+          p1[i] *= f1;
         }
-      pb[ks] = cat4(ph[0], ph[1], ph[2], ph[3]);
+      }
+      pb[ks] = f16x8{static_cast<_Float16>(p0[0]), static_cast<_Float16>(p0[1]), static_cast<_Float16>(p0[2]),
+                     static_cast<_Float16>(p0[3]), static_cast<_Float16>(p1[0]), static_cast<_Float16>(p1[1]),
+                     static_cast<_Float16>(p1[2]), static_cast<_Float16>(p1[3])};
     }
 
     // ---- P.V for this wave's 128 output columns over the tile's tokens,
@@ -360,7 +420,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     // at row r + m/4, columns d0 + 4(m%4) .. +3, and receives column d0 + m
     // of the 4 rows.
 #pragma unroll
-    for (int ks = 0; ks < kQ; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
       const int rlo = 32 * ks + 4 * g + (c >> 2), rhi = 32 * ks + 16 + 4 * g + (c >> 2);   // both have swz = swz_r
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
@@ -376,19 +436,55 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
     __syncthreads();   // the tile's LDS may be overwritten
   };
 
-  // the loop is unrolled over the buffers so that each has fixed registers
-  for (int t0 = 0; t0 < ntiles; t0 += kAhead + 1) {
-#pragma unroll
-    for (int u = 0; u <= kAhead; ++u) {
-      if (t0 + u >= ntiles) break;
-      load_tile(buf[(u + kAhead) % (kAhead + 1)], t0 + u + kAhead);
-      __builtin_amdgcn_sched_barrier(0);
-      process(buf[u], t0 + u);
-    }
+  // the loop is unrolled over the two buffers so that each has fixed
+  // registers; step n processes tile 2 n + grp
+  for (int n = 0; n < nsteps; n += 2) {
+    load_tile(buf[1], 2 * (n + 1) + grp);
+    __builtin_amdgcn_sched_barrier(0);
+    process(buf[0], 2 * n + grp);
+    if (n + 1 >= nsteps) break;
+    load_tile(buf[0], 2 * (n + 2) + grp);
+    __builtin_amdgcn_sched_barrier(0);
+    process(buf[1], 2 * (n + 1) + grp);
   }
 
-  // ---- partials: o = acc * s_t / l, lse = (m + log2 l) ln 2 (l is the same in every wave)
-  const float lt = lanes::across_rows<lanes::Sum>(l_run);
+  // ---- each group's denominator: l summed over the lanes of its waves
+  // (each holds its own tokens' share)
+  const float lw = lanes::across_rows<lanes::Sum>(l_run);
+  if (g == 0) lds_r[c][wave] = lw;
+  __syncthreads();
+  const f32x4 lv = *reinterpret_cast<const f32x4*>(&lds_r[c][0]);
+  float lt = (lv[0] + lv[1]) + (lv[2] + lv[3]);
+  __syncthreads();   // (the LDS below is reused)
+  // ---- the second group hands its state to the first: accumulators (the
+  // same lane layout), reference maximum and denominator per head
+  f32x4* const xacc = reinterpret_cast<f32x4*>(lds_c_[0]) + (wave * 64 + lane) * 8;
+  if (grp == 1) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) xacc[jj] = acc_o[jj];
+    if (wave == 0 && g == 0) {
+      lds_r_[1][c][0] = m_ref;
+      lds_r_[1][c][1] = lt;
+    }
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  {
+    const float m1 = lds_r_[1][c][0], l1 = lds_r_[1][c][1];
+    const float M = fmaxf(m_ref, m1);
+    const float f0 = m_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - M);
+    const float f1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const f32x4 x = xacc[jj];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc_o[jj][i] = acc_o[jj][i] * f0 + x[i] * f1;
+    }
+    lt = lt * f0 + l1 * f1;
+    m_ref = M;
+  }
+
+  // ---- partials: o = acc * s_t / l, lse = (m + log2 l) ln 2
   const float f = lt > 0.0f ? s_t / lt : 0.0f;
   const int64_t po = (static_cast<int64_t>(b) * a.Hq + c) * num_splits + split;
   float* op = a.part_o + po * kD + 128 * wave + 4 * g;
@@ -396,7 +492,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_decode_mla(kvq_decode_args a, i
   for (int jj = 0; jj < 8; ++jj)
     *reinterpret_cast<float4*>(op + 16 * jj) =
         make_float4(acc_o[jj][0] * f, acc_o[jj][1] * f, acc_o[jj][2] * f, acc_o[jj][3] * f);
-  if (wave == 0 && g == 0) a.part_lse[po] = lt > 0.0f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+  if (wave == 0 && g == 0) a.part_lse[po] = lt > 0.0f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY;
 }
 
 }  // namespace

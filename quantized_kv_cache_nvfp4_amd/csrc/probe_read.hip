@@ -12,6 +12,12 @@
 //            equals a fixed constant, so the loads cannot be dropped and
 //            the probe writes (almost surely) nothing.
 //   Returns 0, or 1 for bad arguments, 2 for a launch error.
+//
+//   kvq_probe_read_chunks(p, bytes, grid, fronts, sink, stream)
+//     the same read in the decode kernels' launch shape: work-group g of
+//     grid (256 threads) reads one contiguous chunk, bytes / grid rounded
+//     up to 16, split into `fronts` (1, 2 or 4) equal parts streamed side
+//     by side by as many thread groups.  Same arguments and returns.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,7 +44,47 @@ __global__ void __launch_bounds__(kThreads) k_read_probe(const uint4* __restrict
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+template <int F>
+__global__ void __launch_bounds__(kThreads) k_read_chunks(const uint4* __restrict__ p, uint64_t n16, uint64_t per,
+                                                          uint32_t* sink) {
+  constexpr int T = kThreads / F;   // threads per front
+  const int f = static_cast<int>(threadIdx.x) / T, t = static_cast<int>(threadIdx.x) % T;
+  const uint64_t wlo = static_cast<uint64_t>(blockIdx.x) * per;
+  const uint64_t whi = wlo + per < n16 ? wlo + per : n16;
+  const uint64_t fper = (per + F - 1) / F;
+  const uint64_t lo = wlo + f * fper;
+  const uint64_t hi = lo + fper < whi ? lo + fper : whi;
+  uint32_t acc = 0;
+  uint64_t i = lo + t;
+  for (; i + (kInFlight - 1) * T < hi; i += kInFlight * T) {
+    uint4 v[kInFlight];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) v[k] = p[i + k * T];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < hi; i += T) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 }  // namespace
+
+extern "C" int kvq_probe_read_chunks(const void* p, uint64_t bytes, int32_t grid, int32_t fronts, uint32_t* sink,
+                                     void* stream) {
+  if (p == nullptr || sink == nullptr || bytes % 16 != 0 || grid <= 0 ||
+      reinterpret_cast<uintptr_t>(p) % 16 != 0 || (fronts != 1 && fronts != 2 && fronts != 4))
+    return 1;
+  const uint64_t n16 = bytes / 16, per = (n16 + grid - 1) / grid;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const auto* q = static_cast<const uint4*>(p);
+  if (fronts == 1) hipLaunchKernelGGL(k_read_chunks<1>, dim3(grid), dim3(kThreads), 0, st, q, n16, per, sink);
+  if (fronts == 2) hipLaunchKernelGGL(k_read_chunks<2>, dim3(grid), dim3(kThreads), 0, st, q, n16, per, sink);
+  if (fronts == 4) hipLaunchKernelGGL(k_read_chunks<4>, dim3(grid), dim3(kThreads), 0, st, q, n16, per, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 extern "C" int kvq_probe_read(const void* p, uint64_t bytes, int32_t grid, uint32_t* sink, void* stream) {
   if (p == nullptr || sink == nullptr || bytes % 16 != 0 || grid <= 0 ||

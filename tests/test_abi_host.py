@@ -53,10 +53,11 @@ def test_auto_split_worked_values(K):
     assert K.kvq_auto_num_splits(256, 1, 32, 32768, 128, 32) == 16
     # large batch: already 512 programs -> 1
     assert K.kvq_auto_num_splits(256, 64, 8, 4096, 128, 32) == 1
-    # MLA B=32: 2*256/32 = 16 splits; the partial-traffic bound (a third of
-    # the KV bytes: 32*8192*576 / (3 * 32*16*513*8)) = 23 does not bind
-    assert K.kvq_auto_num_splits(256, 32, 1, 8192, 512, 16) == 16
-    # the bound binds for a wide head at B=4, kv 2048: min(2*256/4 -> 64,
+    # MLA B=32 (16 heads share the request's latent: one 8-wave work-group
+    # per CU): 256/32 = 8 splits; the partial-traffic bound (a third of the
+    # KV bytes: 32*8192*576 / (3 * 32*16*513*8)) = 23 does not bind
+    assert K.kvq_auto_num_splits(256, 32, 1, 8192, 512, 16) == 8
+    # the bound binds for a wide head at B=4, kv 2048: min(256/4 = 64,
     # 2048/256 = 8, floor(4*2048*576 / (3 * 4*16*513*8)) = 5) = 5
     assert K.kvq_auto_num_splits(256, 4, 1, 2048, 512, 16) == 5
     assert K.kvq_auto_num_splits(256, 1, 1, 0, 128, 1) == 1
