@@ -72,7 +72,8 @@ constexpr int kDr = 64;                    // rope dims
 constexpr int kRow = kD / 2;               // latent code bytes per token
 constexpr int kSRow = kD / 16;             // latent scale bytes per token
 constexpr int kPitch = kD * 2 + 32;        // staged f16 row pitch in LDS (bytes; +32 spreads banks)
-constexpr int kPPitch = kT + 4;            // P^T row pitch in LDS (floats, one row per head)
+constexpr int kPPitch = kT;                // P^T row pitch in LDS (floats, one row per head; 16-byte
+                                           // chunk k of row c at k ^ c: conflict-free writes and reads)
 constexpr float kLazy = 8.0f;              // a wave's own reference only past P = 2^8
 
 __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -372,7 +373,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_decode_mla(kvq_decode_args a, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - ru);   // masked: exp2(-inf) = 0
     const float l_tile = (p[0] + p[1]) + (p[2] + p[3]);
-    *reinterpret_cast<f32x4*>(lds_p + c * kPPitch + 16 * wave + 4 * g) = p;
+    *reinterpret_cast<f32x4*>(lds_p + c * kPPitch + 4 * ((4 * wave + g) ^ c)) = p;
     if (g == 0) lds_r[c][wave] = r;
     __syncthreads();   // staged rows, P and the references visible
 
@@ -397,8 +398,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_decode_mla(kvq_decode_args a, i
     f16x8 pb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      f32x4 p0 = *reinterpret_cast<const f32x4*>(lds_p + c * kPPitch + 32 * ks + 4 * g);
-      f32x4 p1 = *reinterpret_cast<const f32x4*>(lds_p + c * kPPitch + 32 * ks + 16 + 4 * g);
+      f32x4 p0 = *reinterpret_cast<const f32x4*>(lds_p + c * kPPitch + 4 * ((8 * ks + g) ^ c));
+      f32x4 p1 = *reinterpret_cast<const f32x4*>(lds_p + c * kPPitch + 4 * ((8 * ks + 4 + g) ^ c));
       if (fix) {
         const float r0 = rr[2 * ks], r1 = rr[2 * ks + 1];
         const float f0 = r0 == R ? 1.0f : __builtin_amdgcn_exp2f(r0 - R);
@@ -458,10 +459,11 @@ __global__ void __launch_bounds__(kThreads, 1) k_decode_mla(kvq_decode_args a, i
   __syncthreads();   // (the LDS below is reused)
   // ---- the second group hands its state to the first: accumulators (the
   // same lane layout), reference maximum and denominator per head
-  f32x4* const xacc = reinterpret_cast<f32x4*>(lds_c_[0]) + (wave * 64 + lane) * 8;
+  // (accumulator jj of every lane of the group contiguous: conflict-free)
+  f32x4* const xacc = reinterpret_cast<f32x4*>(lds_c_[0]) + wave * 64 + lane;
   if (grp == 1) {
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) xacc[jj] = acc_o[jj];
+    for (int jj = 0; jj < 8; ++jj) xacc[jj * kW * 64] = acc_o[jj];
     if (wave == 0 && g == 0) {
       lds_r_[1][c][0] = m_ref;
       lds_r_[1][c][1] = lt;
@@ -476,7 +478,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_decode_mla(kvq_decode_args a, i
     const float f1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - M);
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      const f32x4 x = xacc[jj];
+      const f32x4 x = xacc[jj * kW * 64];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc_o[jj][i] = acc_o[jj][i] * f0 + x[i] * f1;
     }

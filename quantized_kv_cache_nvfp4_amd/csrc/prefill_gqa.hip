@@ -32,10 +32,13 @@
 //    contraction meets the tokens is free, and V^T is stored in LDS with
 //    its token slots permuted to match.  A lane's output column is again
 //    its query row, so the softmax rescale is a per-lane scalar.
-//  * LDS: K rows of 256 B with a 16-byte-chunk XOR swizzle, V^T rows of
-//    64 token slots padded to 144 B; both conflict-free for the MFMA reads
-//    and the staging writes.  2 x 34 KB per work-group, two work-groups per
-//    CU.
+//  * LDS: K rows of 256 B with a 16-byte-chunk XOR swizzle (chunk j of row
+//    r at j ^ (r mod 16)), staged token-major (a 16-lane row of a wave
+//    writes 16 tokens); V^T rows of 64 token slots padded to 160 B.  Both
+//    measured free of bank conflicts on gfx950 for the MFMA reads and the
+//    staging writes (SQ_LDS_BANK_CONFLICT of a probe of each access
+//    pattern; a 144-byte V^T pitch, or four consecutive lanes per K token,
+//    is not).  2 x 36 KB per work-group, two work-groups per CU.
 //  * the per-tensor scales are applied in fp32: s_t,K inside the score
 //    scale, s_t,V at the end.  P enters the second MFMA as f16.
 //  * query blocks are dispatched longest first (the last block of the chunk
@@ -60,14 +63,10 @@ constexpr int kTile = 64;                     // KV tokens per tile
 constexpr int kD = 128;                       // head_dim
 constexpr int kKRow = kD * 2;                 // f16 K row in LDS (bytes)
 constexpr int kKBytes = kTile * kKRow;        // 16 KB
-constexpr int kVtRow = kTile * 2 + 16;        // f16 V^T row of 64 token slots + 16 B of padding
-constexpr int kVtBytes = kD * kVtRow;         // 18 KB
+constexpr int kVtRow = kTile * 2 + 32;        // f16 V^T row of 64 token slots + 32 B of padding
+constexpr int kVtBytes = kD * kVtRow;         // 20 KB
 constexpr int kStage = kKBytes + kVtBytes;
-constexpr int kLdsBytes = 2 * kStage;         // 69,632 B
-#ifndef KVQ_PF_SCHED
-#define KVQ_PF_SCHED 0
-#endif
-constexpr bool kSchedGroups = KVQ_PF_SCHED;
+constexpr int kLdsBytes = 2 * kStage;         // 73,728 B
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
@@ -197,7 +196,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
 
   // ---- staging roles: K token kt, elements 32 kq .. + 31; V group vq (tokens
   // 4 vq .. + 3), elements 8 vr .. + 7
-  const int kt = tid >> 2, kq = tid & 3;
+  // (f16 K: token-major, lane (g, c) of wave w stages token 16 w + c, quarter
+  // g, so that a 16-lane row of the wave writes 16 tokens: conflict-free
+  // under the 256-byte K rows' swizzle; FP8 K: four consecutive lanes per
+  // token, conflict-free under its 128-byte rows' swizzle.  Both read the
+  // tile's bytes with fully used 64-byte runs per token.)
+  const int kt = K8 ? tid >> 2 : 16 * (tid >> 6) + (tid & 15);
+  const int kq = K8 ? tid & 3 : (tid >> 4) & 3;
   const int vr = tid >> 4, vq = tid & 15;
   const int kst_off = kt * kKRow;
   const int vst_off = (8 * vr) * kVtRow + 2 * vt_slot(4 * vq);
@@ -253,11 +258,11 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
   auto stage_k = [&](uint8_t* kb) {
     if constexpr (K8) {
       // the token's 32 code bytes as 4 chunks of 8 (elements 32 kq + 8 j ..),
-      // chunk j of row kt at 8 ((4 kq + j) ^ (kt & 14)) of a 128-byte row
+      // chunk j of row kt at 8 ((4 kq + j) ^ (kt & 15)) of a 128-byte row
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x2 x = {raw.k[j >> 1][2 * (j & 1)], raw.k[j >> 1][2 * (j & 1) + 1]};
-        lds_st<u32x2>(kb + kt * kD + 8 * ((4 * kq + j) ^ (kt & 14)), x);
+        lds_st<u32x2>(kb + kt * kD + 8 * ((4 * kq + j) ^ (kt & 15)), x);
       }
       return;
     }
@@ -333,7 +338,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
       // A = K codes (16 tokens x 32 elements, 8 bytes a lane), B = Q^T codes
       int kl8[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kl8[kk] = c * kD + 8 * ((4 * kk + g) ^ (c & 14));
+      for (int kk = 0; kk < 4; ++kk) kl8[kk] = c * kD + 8 * ((4 * kk + g) ^ c);
       i64x1 ka8[2][4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) ka8[0][kk] = lds_ld<i64x1>(kb + kl8[kk]);
