@@ -16,14 +16,22 @@
 // Design for CDNA4.  The chunk gives many query rows per kv head, so both
 // contractions are dense and run on MFMA (the decode kernels fill the MFMA
 // columns with tokens because there one query row meets each kv head):
-//  * a work-group of 4 waves owns 128 query rows of one (request, kv head):
-//    128 / G consecutive query tokens x the G heads of the group (row r ->
+//  * a work-group of 8 waves owns 256 query rows of one (request, kv head):
+//    256 / G consecutive query tokens x the G heads of the group (row r ->
 //    token r / G, head r % G); each wave owns 32 rows as two 16-row blocks.
-//  * per 64-token KV tile the 256 threads dequantize K and V once into LDS
-//    as f16 (E2M1 or E4M3 -> f16 with the hardware convert, exact; times the
-//    E4M3 block scale, an exact f16 product), two stages so that one
-//    barrier per tile suffices; the raw bytes of the next tile are loaded
-//    into registers before the current tile is computed.
+//  * the waves form two groups of 4 (A: waves 0-3, B: waves 4-7; waves w
+//    and w + 4 share a SIMD) that run the same tile half a step apart
+//    (ping-pong): each tile takes four phases separated by barriers, and in
+//    every phase one group is in its matrix-core work while the other is in
+//    vector work, so the SIMD issues both at once:
+//        phase      1           2           3           4
+//        A          Q.K^T       softmax     P.V         stage K(n+1)
+//        B          stage V(n+1) Q.K^T      softmax     P.V
+//  * per 64-token KV tile K and V are dequantized once into LDS as f16
+//    (E2M1 or E4M3 -> f16 with the hardware convert, exact; times the E4M3
+//    block scale, an exact f16 product) for all 256 rows: group A stages K
+//    and group B stages V, each from raw bytes it loaded one tile ahead, into
+//    two stages of LDS.
 //  * S^T = K . Q^T: the K tile is the A operand (16 tokens x 32 dims from
 //    LDS), the query rows the B operand (registers, loaded once).  A lane
 //    then holds 4 tokens of one query row, so the row maximum is a local
@@ -57,8 +65,8 @@ namespace pf {
 
 using namespace dec;
 
-constexpr int kThreads = 256;
-constexpr int kRows = 128;                    // query rows per work-group
+constexpr int kThreads = 512;                 // two groups of 4 waves
+constexpr int kRows = 256;                    // query rows per work-group
 constexpr int kTile = 64;                     // KV tokens per tile
 constexpr int kD = 128;                       // head_dim
 constexpr int kKRow = kD * 2;                 // f16 K row in LDS (bytes)
@@ -123,7 +131,7 @@ __device__ inline f32x4 mfma_fp8(i64x1 a, i64x1 b, f32x4 c) {
 }
 
 template <int KVF, int G, bool PAGED, bool Q8>
-__global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
+__global__ void __launch_bounds__(kThreads, 1) k_prefill_gqa(PrefillParams P) {
   constexpr bool kFp4 = KVF == KVQ_NVFP4;
   constexpr bool K8 = Q8 && KVF == KVQ_FP8E4M3;   // Q.K^T on FP8 MFMA
   constexpr int RB = kFp4 ? kD / 2 : kD;   // code bytes per row
@@ -201,9 +209,13 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
   // under the 256-byte K rows' swizzle; FP8 K: four consecutive lanes per
   // token, conflict-free under its 128-byte rows' swizzle.  Both read the
   // tile's bytes with fully used 64-byte runs per token.)
-  const int kt = K8 ? tid >> 2 : 16 * (tid >> 6) + (tid & 15);
-  const int kq = K8 ? tid & 3 : (tid >> 4) & 3;
-  const int vr = tid >> 4, vq = tid & 15;
+  // (group A's threads stage K, group B's stage V: t8 is the thread's index
+  // in its group)
+  const int t8 = tid & 255;
+  const bool grp_a = tid < 256;   // wave-uniform
+  const int kt = K8 ? t8 >> 2 : 16 * (t8 >> 6) + (t8 & 15);
+  const int kq = K8 ? t8 & 3 : (t8 >> 4) & 3;
+  const int vr = t8 >> 4, vq = t8 & 15;
   const int kst_off = kt * kKRow;
   const int vst_off = (8 * vr) * kVtRow + 2 * vt_slot(4 * vq);
 
@@ -486,38 +498,71 @@ __global__ void __launch_bounds__(kThreads, 2) k_prefill_gqa(PrefillParams P) {
     }
   };
 
-  // ---- the tile loop.  Two LDS stages (K and V^T of one tile each); tile
-  // n is staged into stage n % 2, which tile n - 2 used before the previous
-  // barrier, while the raw bytes of tile n + 1 load into registers: one
-  // barrier per tile.  The two work-groups a compute unit holds overlap each
-  // other's MFMA and VALU phases.
+  // ---- the tile loop.  Two LDS stages (K and V^T of one tile each): tile n
+  // is read from stage n % 2 while tile n + 1 is staged into the other one,
+  // in the phase order of the header (K(n + 1) is staged after B's Q.K^T of
+  // tile n, V(n + 1) before A's P.V of tile n + 1; every stage is written
+  // only after both groups' last read of its previous tile).  The raw bytes
+  // of tile n + 2 are loaded right after tile n + 1 is staged.
   uint8_t* const kbuf = lds;
   uint8_t* const vbuf = lds + 2 * kKBytes;
   // tiles whose keys every row sees (no causal mask needed)
   int n_open = p_min >= kTile - 1 ? (p_min - (kTile - 1)) / kTile + 1 : 0;
   n_open = n_open < ntiles ? n_open : ntiles;
+  auto stage_v_tile = [&](uint8_t* vb, int n) {
+    if (tile_keys(n) < kTile)
+      stage_v(std::true_type{}, vb, tile_keys(n));
+    else
+      stage_v(std::false_type{}, vb, kTile);
+  };
   if (ntiles > 0) {
-    load_k(0);
-    load_v(0);
+    if (grp_a) {
+      load_k(0);
+      stage_k(kbuf);
+      load_k(1);
+    } else {
+      load_v(0);
+      stage_v_tile(vbuf, 0);
+      load_v(1);
+    }
   }
+  lds_barrier();
   auto step = [&](auto mask_tag, int n) {
     f32x4 sc[2][4];
     f16x8 pb[2][2];
     uint8_t* const kb = kbuf + (n & 1) * kKBytes;
     uint8_t* const vb = vbuf + (n & 1) * kVtBytes;
-    stage_k(kb);
-    if (tile_keys(n) < kTile)
-      stage_v(std::true_type{}, vb, tile_keys(n));
-    else
-      stage_v(std::false_type{}, vb, kTile);
-    load_k(n + 1);
-    load_v(n + 1);
+    uint8_t* const kb1 = kbuf + ((n + 1) & 1) * kKBytes;
+    uint8_t* const vb1 = vbuf + ((n + 1) & 1) * kVtBytes;
+    auto softmax = [&]() {
+      tile_max(mask_tag, sc, n);
+      rescale_acc();
+      probs(sc, pb);
+    };
+    if (grp_a) {   // phase 1
+      qk(kb, sc);
+    } else {
+      stage_v_tile(vb1, n + 1);
+      load_v(n + 2);
+    }
     lds_barrier();
-    qk(kb, sc);
-    tile_max(mask_tag, sc, n);
-    rescale_acc();
-    probs(sc, pb);
-    pv(vb, pb);
+    if (grp_a)     // phase 2
+      softmax();
+    else
+      qk(kb, sc);
+    lds_barrier();
+    if (grp_a)     // phase 3
+      pv(vb, pb);
+    else
+      softmax();
+    lds_barrier();
+    if (grp_a) {   // phase 4
+      stage_k(kb1);
+      load_k(n + 2);
+    } else {
+      pv(vb, pb);
+    }
+    lds_barrier();
   };
   int n = 0;
   for (; n < n_open; ++n) step(std::false_type{}, n);
