@@ -330,8 +330,9 @@ typedef struct {
      and q_scale their scale: device float[1], or float[Hq] with
      q_scale_per_head = 1 (query head h dequantized with q_scale[h]).  The
      codes enter the score contraction exactly; the scale multiplies the
-     score (beside the K tensor scale and softmax_scale).  Exact
-     probabilities only (quantize_p = 0).  Unused otherwise. */
+     score (beside the K tensor scale and softmax_scale).  Exact or
+     FP8 probabilities (quantize_p: pass 1 forms the scores from the
+     codes).  Unused otherwise. */
   const float* q_scale;
   int32_t q_scale_per_head;
   /* Quantize-on-append fused into the decode step (GQA layout, bf16

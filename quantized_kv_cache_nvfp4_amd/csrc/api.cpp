@@ -300,7 +300,6 @@ int validate_decode(const kvq_decode_args* a, int32_t* s_out, bool fused) {
   if (a->q_dtype == KVQ_FP8E4M3) {   // FP8 query codes with their scale
     if (a->layout != KVQ_LAYOUT_GQA) return fail(KVQ_ERR_UNSUPPORTED, "FP8 queries are decoded for the GQA layout only");
     if (a->q_scale == nullptr) return fail(KVQ_ERR_ARG, "an FP8 query needs q_scale");
-    if (a->quantize_p) return fail(KVQ_ERR_UNSUPPORTED, "FP8 queries are decoded with exact probabilities only");
     if (a->q_scale_per_head != 0 && a->q_scale_per_head != 1) return fail(KVQ_ERR_ARG, "q_scale_per_head must be 0 or 1");
     if (!aligned(a->q_scale, 4)) return fail(KVQ_ERR_ALIGN, "q_scale must be 4-byte aligned");
     if (!aligned(a->q, 8) || a->q_sb % 8 != 0 || a->q_sh % 8 != 0)

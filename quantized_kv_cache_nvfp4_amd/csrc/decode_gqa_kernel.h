@@ -1296,7 +1296,7 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
 //   D = 128: V planes in the TOKEN4 layout; bf16 queries (contiguous or
 //            paged planes, with or without the fused append, split or fused
 //            combine, exact or FP8 probabilities), FP8 queries (contiguous
-//            or paged, split or fused; exact probabilities), fp32 queries
+//            or paged, split or fused, exact or FP8 probabilities), fp32 queries
 //            (contiguous planes, split or fused, exact or FP8 probabilities);
 //   D = 64:  V planes in the row layout; bf16 and fp32 queries over
 //            contiguous planes (split or fused, exact or FP8 probabilities).
@@ -1347,8 +1347,8 @@ hipError_t launch_q(const kvq_decode_args& a, const DecodePlan& p, const FusedOu
   // fp32 queries select the fp32-accuracy path (hi/lo split of Q, and of P
   // when P is not quantized)
   if (a.q_dtype == KVQ_F32) return launch_layout<KVF, G, D, kQF32, (PM == 0 ? 2 : 1), PM>(a, p, fo, st);
-  if (a.q_dtype == KVQ_FP8E4M3) {   // exact probabilities, D = 128
-    if constexpr (PM == 0 && D == 128) return launch_layout<KVF, G, D, kQFp8, 1, 0>(a, p, fo, st);
+  if (a.q_dtype == KVQ_FP8E4M3) {   // D = 128; exact probabilities or FP8-P pass 1
+    if constexpr ((PM == 0 || PM == 1) && D == 128) return launch_layout<KVF, G, D, kQFp8, 1, PM>(a, p, fo, st);
     return hipErrorInvalidValue;
   }
   return launch_layout<KVF, G, D, kQBf16, 1, PM>(a, p, fo, st);

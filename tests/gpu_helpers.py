@@ -195,15 +195,16 @@ def page_plane(plane, bs, perm_seed, lens=None):
 
 
 def gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.bfloat16, out_scale=None, with_lse=False, fused=False,
-               prob_scale=None, block_table=None):
+               prob_scale=None, block_table=None, q=None, q_scale=None):
     """prob_scale: None for exact probabilities, else the FP8-P path;
-    block_table: paged planes kp / vp (None: contiguous)."""
+    block_table: paged planes kp / vp (None: contiguous); q / q_scale: a
+    query other than inp.q (e.g. FP8 codes with their scale)."""
     k_ = K()
     B, Hq, D = inp.B, inp.Hq, inp.D
     cap = 64
     part_o = torch.empty(B * Hq * cap * D, dtype=torch.float32, device=DEV)
     part_lse = torch.empty(B * Hq * cap, dtype=torch.float32, device=DEV)
-    q = inp.q.to(DEV)
+    q = inp.q.to(DEV) if q is None else q
     fp8p = {}
     if prob_scale is not None:
         n = k_.kvq_fp8p_scratch_floats(B, Hq, cap, inp.Lmax)
@@ -211,7 +212,8 @@ def gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.bfloat16, out_scale=None, w
         fp8p = dict(quantize_p=True, prob_scale=prob_scale,
                     p_scratch=torch.full((max(n, 4),), float("nan"), dtype=torch.float32, device=DEV))
     args = k_.make_decode_args(q, kp, vp, lens, max_kv_len=inp.Lmax, softmax_scale=inp.softmax_scale,
-                               num_splits=s, part_o=part_o, part_lse=part_lse, block_table=block_table, **fp8p)
+                               num_splits=s, part_o=part_o, part_lse=part_lse, block_table=block_table,
+                               q_scale=q_scale, **fp8p)
     out = torch.empty(B, Hq, D, dtype=out_dtype, device=DEV)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=DEV) if with_lse else None
     if fused:

@@ -374,8 +374,9 @@ def test_fp8_query_validation(L, K):
     assert _decode_rc(L, a) == 3
     a = q8(); a.layout = K.KVQ_LAYOUT_MLA; a.Hkv = 1; a.Hq = 16
     assert _decode_rc(L, a) == 2
-    a = q8(); a.quantize_p, a.prob_scale, a.p_scratch = 1, 1.0 / 448.0, FAKE
-    assert _decode_rc(L, a) == 2
+    # FP8 queries with FP8 probabilities pass the query checks and meet the FP8-P ones
+    a = q8(); a.quantize_p, a.prob_scale, a.p_scratch = 1, 1.0 / 448.0, None
+    assert _decode_rc(L, a) == 1
     a = _good_args(K); a.q_dtype = K.KVQ_F16
     assert _decode_rc(L, a) == 2
 

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import kvq_synth
-from gpu_helpers import DEV, K, announce, assert_bf16_output, gpu_pack, make_inputs, oracle_gqa
+from gpu_helpers import DEV, K, announce, assert_bf16_output, gpu_decode, gpu_pack, make_inputs, oracle_gqa
 from oracle import attention as OA
 from oracle import quant as OQ
 
@@ -73,3 +73,59 @@ def test_decode_fp8_query(case):
     _, _, _, khat, vhat = oracle_gqa(key)
     o_ref, _ = OA.decode_gqa(qhat, khat, vhat, inp.kv_lens, inp.softmax_scale)
     assert_bf16_output(out, o_ref, f"fp8 query {case}")
+
+
+# ---------------------------------------------------------------- FP8 queries with FP8 probabilities
+PS = float(np.float32(1.0 / 448.0))
+EPS = 2e-5
+
+
+def _fp8p_reference(qhat, khat, vhat, inp, ps):
+    """The oracle's FP8-P decode with the dequantized query, and the
+    near-boundary allowance of the FP8-P gate (tokens whose P / prob_scale
+    lies within a relative 2e-5 of an E4M3 rounding boundary may take the
+    neighbouring code: each adds |code step| * prob_scale * |V_t|)."""
+    from oracle import formats as OF
+    P = OA.gqa_probs(qhat, khat, inp.kv_lens, inp.softmax_scale)
+    o = OA.decode_gqa_fp8p(qhat, khat, vhat, inp.kv_lens, inp.softmax_scale, ps)
+    r = P / ps
+    step = np.abs(OF.e4m3_round(r * (1 + EPS)) - OF.e4m3_round(r * (1 - EPS))) * ps
+    va = np.repeat(np.abs(vhat), inp.Hq // inp.Hkv, axis=1)
+    flip = np.einsum("bht,bhtd->bhd", step, va)
+    mass = np.einsum("bht,bhtd->bhd", OF.e4m3_round(r) * ps, va)
+    return o, flip, mass
+
+
+FP8P_CASES = [
+    # (key, kv format, splits, per-head query scale)
+    (("fp8", "fp8", 64), "fp8", 3, False),
+    (("nvfp4", "custom", 3, 8, 2, 128, (0, 1, 300), "bf16"), "nvfp4", 4, True),
+    (("nvfp4", "custom", 2, 16, 1, 128, (700, 33), "bf16"), "nvfp4", 0, False),   # G = 16, auto splits
+]
+
+
+@pytest.mark.parametrize("case", FP8P_CASES, ids=lambda c: f"{c[0][0]}-{c[0][1]}-s{c[2]}-h{int(c[3])}")
+def test_decode_fp8_query_fp8_probabilities(case):
+    """FP8 query codes (per tensor or per head) with FP8-quantized
+    probabilities: pass 1 forms the scores from the codes, pass 2 the
+    quantized P . V; against the oracle's FP8-P decode with the dequantized
+    query, within the FP8-P gate (fp32 output: 1e-5 (1 + |o|) + 2^-16
+    sum_t P~_t |V_t| + the near-boundary allowance)."""
+    key, fmt, s, per_head = case
+    announce(f"fp8 query + fp8p {case}")
+    inp = make_inputs(key)
+    kp, vp, _, _, lens = gpu_pack(inp, fmt)
+    q8, q_scale = _quantize_query(inp.q.to(DEV), per_head)
+    out, used, lse = gpu_decode(inp, kp, vp, lens, s, out_dtype=torch.float32, with_lse=True, prob_scale=PS,
+                                q=q8, q_scale=q_scale)
+    _, _, qhat = OQ.fp8_quantize_query(kvq_synth.f64(inp.q), per_head)
+    _, _, _, khat, vhat = oracle_gqa(key)
+    o_ref, flip, mass = _fp8p_reference(qhat, khat, vhat, inp, PS)
+    g = out.cpu().double().numpy()
+    bad = np.abs(g - o_ref) > 1e-5 * (1 + np.abs(o_ref)) + 2.0 ** -16 * mass + flip
+    assert not bad.any(), f"{case}: {bad.sum()} outputs off; max abs {np.abs(g - o_ref).max():.3g}"
+    _, lse_ref = OA.decode_gqa(qhat, khat, vhat, inp.kv_lens, inp.softmax_scale)
+    l = lse.cpu().double().numpy()
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(l), fin)
+    assert np.all(np.abs(l[fin] - lse_ref[fin]) <= 1e-5 * (1 + np.abs(lse_ref[fin])))
