@@ -34,7 +34,8 @@
 //    comes from the staged rows through the LDS transpose read
 //    ds_read_b64_tr_b16, so the latent is dequantized once and used by both
 //    contractions, and its B operand (P) is read from LDS in the token order
-//    of that contraction.  Two barriers per tile.
+//    of that contraction.  Two barriers per tile; the two groups run half
+//    a tile apart (one scores while the other runs P.V).
 //  * the head_dim order of Q.K^T is free: lane group g of load instruction
 //    k reads bytes [64 k + 16 g, +16) of its token's latent codes (each
 //    instruction covers 64 contiguous bytes of every row), i.e. latent dims
@@ -438,7 +439,13 @@ __global__ void __launch_bounds__(kThreads, 1) k_decode_mla(kvq_decode_args a, i
   };
 
   // the loop is unrolled over the two buffers so that each has fixed
-  // registers; step n processes tile 2 n + grp
+  // registers; step n processes tile 2 n + grp.  The second group starts
+  // one barrier later and the first ends with one more, so the groups run
+  // half a tile apart: while one dequantizes and scores, the other runs
+  // P.V (the two waves of a SIMD are one of each), and their loads go out
+  // in alternate halves.  Each group's LDS is its own, and between any two
+  // of its halves lies one work-group barrier.
+  if (grp == 1) __syncthreads();
   for (int n = 0; n < nsteps; n += 2) {
     load_tile(buf[1], 2 * (n + 1) + grp);
     __builtin_amdgcn_sched_barrier(0);
@@ -448,6 +455,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_decode_mla(kvq_decode_args a, i
     __builtin_amdgcn_sched_barrier(0);
     process(buf[1], 2 * (n + 1) + grp);
   }
+  if (grp == 0) __syncthreads();
 
   // ---- each group's denominator: l summed over the lanes of its waves
   // (each holds its own tokens' share)
