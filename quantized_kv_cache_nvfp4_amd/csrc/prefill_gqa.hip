@@ -394,15 +394,20 @@ __global__ void __launch_bounds__(kThreads, 1) k_prefill_gqa(PrefillParams P) {
   };
 
   // ---- running state per row block: reference maximum (log2 units),
-  // partial denominator (this lane's tokens), O^T accumulators (lane (g, c):
-  // row c, elements 16 db + 4 g .. + 3).  The reference is raised only when
-  // a tile's maximum exceeds it by more than kLazy (then the accumulators are
-  // rescaled); otherwise probabilities up to 2^kLazy are formed against the
-  // old reference, which is exact in real arithmetic and keeps f16's relative
-  // precision for P.
+  // denominator, O^T accumulators (lane (g, c): row c, elements 16 db + 4 g
+  // .. + 3).  The denominator is one more MFMA accumulator: an all-ones A
+  // operand times the P^T operand sums the f16 probabilities of row c that
+  // P.V uses (every element of lane (g, c) holds row c's sum), so the
+  // softmax phase forms no sums and the epilogue no cross-lane reduction;
+  // numerator and denominator then carry the same rounded probabilities.
+  // The reference is raised only when a tile's maximum exceeds it by more
+  // than kLazy (then the accumulators are rescaled); otherwise probabilities
+  // up to 2^kLazy are formed against the old reference, which is exact in
+  // real arithmetic and keeps f16's relative precision for P.
   constexpr float kLazy = 8.f;
   float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
+  f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
   f32x4 acc[2][8];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
@@ -411,9 +416,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_prefill_gqa(PrefillParams P) {
 
   // The softmax of tile n in two parts.  tile_max: (MASK: clear the scores
   // of keys past each row's position,) take the tile's row maxima and move
-  // the reference maxima, giving the factors alpha by which l and the
-  // accumulators are rescaled (any != 1 in the wave: `rescale`).  probs:
-  // P = exp2(score * c2 - m) as the f16 P^T operands, l = l alpha + sum P.
+  // the reference maxima, giving the factors alpha by which the
+  // accumulators and the denominator are rescaled (any != 1 in the wave:
+  // `rescale`).  probs: P = exp2(score * c2 - m) as the f16 P^T operands.
   float alpha[2] = {1.f, 1.f};
   bool rescale = false;
   auto tile_max = [&](auto mask_tag, f32x4 (&sc)[2][4], int n) {
@@ -445,16 +450,11 @@ __global__ void __launch_bounds__(kThreads, 1) k_prefill_gqa(PrefillParams P) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const float m_use = m[rb] == -INFINITY ? 0.f : m[rb];
-      float sum = 0.f;
       float p[4][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[u][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rb][u][e], c2r[rb], -m_use));
-          sum += p[u][e];
-        }
-      l[rb] = l[rb] * alpha[rb] + sum;
+        for (int e = 0; e < 4; ++e) p[u][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[rb][u][e], c2r[rb], -m_use));
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         f16x8 v;
@@ -470,14 +470,17 @@ __global__ void __launch_bounds__(kThreads, 1) k_prefill_gqa(PrefillParams P) {
   auto rescale_acc = [&]() {
     if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) acc[rb][db] *= alpha[rb];
+        lsum[rb] *= alpha[rb];
+      }
     }
   };
 
   // O^T += V^T . P^T: A = V^T (16 elements x 32 token slots), B = P^T;
-  // element block db + 1's operands are read while block db's MFMAs run
+  // element block db + 1's operands are read while block db's MFMAs run;
+  // then the denominator: all-ones A times the same P^T
   auto pv = [&](const uint8_t* vb, const f16x8 (&pb)[2][2]) {
     f16x8 va[2][2];
 #pragma unroll
@@ -495,6 +498,11 @@ __global__ void __launch_bounds__(kThreads, 1) k_prefill_gqa(PrefillParams P) {
         acc[1][db] = mfma(va[db & 1][kc], pb[1][kc], acc[1][db]);
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      lsum[0] = mfma(ones, pb[0][kc], lsum[0]);
+      lsum[1] = mfma(ones, pb[1][kc], lsum[1]);
     }
   };
 
@@ -568,10 +576,11 @@ __global__ void __launch_bounds__(kThreads, 1) k_prefill_gqa(PrefillParams P) {
   for (; n < n_open; ++n) step(std::false_type{}, n);
   for (; n < ntiles; ++n) step(std::true_type{}, n);
 
-  // ---- epilogue: o = acc / l * s_t,V, lse = ln 2 (m + log2 l)
+  // ---- epilogue: o = acc / l * s_t,V, lse = ln 2 (m + log2 l), l = the
+  // denominator (every element of lsum holds it)
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const float lt = lanes::across_rows<lanes::Sum>(l[rb]);
+    const float lt = lsum[rb][0];
     const int r = 32 * w + 16 * rb + c;
     const int qi = i0 + r / G, h = hk * G + r % G;
     if (qi >= P.Sq) continue;

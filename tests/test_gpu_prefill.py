@@ -71,20 +71,41 @@ def gpu_prefill(inp, kp, vp, lens, out_dtype=torch.bfloat16, block_table=None, q
     return out, lse
 
 
-def _check(out, lse, o_ref, lse_ref, label, pv_abs, eps=None):
-    """Output: |o - o_ref| <= 2^-11 sum_t P_t |V_t| (P enters the P.V
-    contraction as f16: one rounding, <= 2^-11 relative, per probability)
-    plus 1e-5 (1 + |o|) of fp32 arithmetic for fp32 output, or plus
-    max(2e-3, 1 bf16 ulp(o_ref)) for bf16 output (its RNE rounding), and
-    cosine >= 0.9999.  lse: 1e-5 (1 + |lse|), and exactly -inf where the
-    oracle has -inf (queries that see nothing, whose output is 0).
-    eps [B, Sq, Hq]: a bound on every score's error in the row (FP8 matrix
-    cores, _fp8_score_eps); scores off by at most eps move each probability
-    by a factor within exp(+-2 eps), so the output by at most
-    (exp(2 eps) - 1) sum_t P_t |V_t|, and lse by at most eps."""
+# The kernel's probabilities: every P_t enters P.V as one f16 value (RNE,
+# relative error d_t <= 2^-11 in f16's normal range) and the denominator is
+# the matrix cores' fp32 sum of the same f16 values, so the denominator's
+# relative error e is a P-weighted mean of the d_t (|e| <= 2^-11) and every
+# normalized weight carries (1 + d_t) / (1 + e): relative error at most
+# W_F16 = 2^-10 (1 + 2^-10).  The log-sum-exp carries ln(1 + e), at most
+# L_F16 = 2^-11 (1 + 2^-10), plus the f16 subnormal tail: probabilities
+# below 2^-14 round with an absolute error up to 2^-25 each, against a
+# denominator of at least 1 (the largest probability of a row is >= 1), so
+# at most 2^-25 per key.  (That tail's effect on the output, at most 2^-25
+# per key times |V_t|, is left out of the output bound, as for the decode.)
+W_F16 = 2.0 ** -10 * (1.0 + 2.0 ** -10)
+L_F16 = 2.0 ** -11 * (1.0 + 2.0 ** -10)
+
+
+def _nkeys(inp):
+    """the most keys any query row of the chunk sees (its request's kv_len)"""
+    return int(np.max(inp.kv_lens)) if len(inp.kv_lens) else 0
+
+
+def _check(out, lse, o_ref, lse_ref, label, pv_abs, nkeys, eps=None):
+    """Output: |o - o_ref| <= (W_F16 e^{2 eps} + e^{2 eps} - 1) sum_t P_t
+    |V_t| (the f16 probabilities above) plus 1e-5 (1 + |o|) of fp32
+    arithmetic for fp32 output, or plus max(2e-3, 1 bf16 ulp(o_ref)) for bf16
+    output (its RNE rounding), and cosine >= 0.9999.  lse: 1e-5 (1 + |lse|)
+    + L_F16 + nkeys 2^-25 (nkeys: the most keys any row sees), and exactly
+    -inf where the oracle has -inf (queries that see nothing, whose output
+    is 0).  eps [B, Sq, Hq]: a bound on every score's error in the row (FP8
+    matrix cores, _fp8_score_eps); scores off by at most eps move each
+    probability by a factor within exp(+-2 eps), so the output by at most
+    (exp(2 eps) - 1) sum_t P_t |V_t| more, and lse by at most eps."""
     o = out.float().cpu().double().numpy()
     eps = np.zeros(lse_ref.shape) if eps is None else eps
-    p_round = (2.0 ** -11 + np.expm1(2.0 * eps)[..., None]) * pv_abs
+    e2 = np.exp(2.0 * eps)[..., None]
+    p_round = (W_F16 * e2 + (e2 - 1.0)) * pv_abs
     if out.dtype == torch.bfloat16:
         bound = np.maximum(2e-3, OF.bf16_ulp(o_ref)) + p_round
     else:
@@ -99,7 +120,8 @@ def _check(out, lse, o_ref, lse_ref, label, pv_abs, eps=None):
     assert np.array_equal(np.isneginf(g), ninf), f"{label}: -inf lse pattern differs"
     assert np.all(o[ninf] == 0.0), f"{label}: queries that see nothing must output 0"
     fin = ~ninf
-    assert np.all(np.abs(g[fin] - lse_ref[fin]) <= 1e-5 * (1.0 + np.abs(lse_ref[fin])) + eps[fin]), f"{label}: lse"
+    lse_tol = 1e-5 * (1.0 + np.abs(lse_ref[fin])) + L_F16 + nkeys * 2.0 ** -25 + eps[fin]
+    assert np.all(np.abs(g[fin] - lse_ref[fin]) <= lse_tol), f"{label}: lse"
 
 
 CASES = [
@@ -124,9 +146,9 @@ def test_prefill_matches_oracle(case):
     kp, vp, klens = _gpu_planes(inp, fmt)
     pv_abs, _ = OA.prefill_gqa(kvq_synth.f64(inp.q), khat, np.abs(vhat), inp.kv_lens, inp.softmax_scale)
     out, lse = gpu_prefill(inp, kp, vp, klens)
-    _check(out, lse, o_ref, lse_ref, f"prefill {name} bf16", pv_abs)
+    _check(out, lse, o_ref, lse_ref, f"prefill {name} bf16", pv_abs, _nkeys(inp))
     out32, lse32 = gpu_prefill(inp, kp, vp, klens, out_dtype=torch.float32)
-    _check(out32, lse32, o_ref, lse_ref, f"prefill {name} f32", pv_abs)
+    _check(out32, lse32, o_ref, lse_ref, f"prefill {name} f32", pv_abs, _nkeys(inp))
     # the bf16 output is the RNE rounding of the fp32 one (same kernel arithmetic)
     assert torch.equal(out32.to(torch.bfloat16), out)
     assert torch.equal(lse32, lse)
@@ -141,7 +163,7 @@ def test_prefill_fp8_per_head_scales():
     kp, vp, lens = _gpu_planes(inp, "fp8", per_head=True)
     assert kp.scale.numel() == 2
     out, lse = gpu_prefill(inp, kp, vp, lens)
-    _check(out, lse, o_ref, lse_ref, "prefill fp8 per-head", pv_abs)
+    _check(out, lse, o_ref, lse_ref, "prefill fp8 per-head", pv_abs, _nkeys(inp))
 
 
 @pytest.mark.parametrize("fmt,bs", [("nvfp4", 64), ("nvfp4", 256), ("fp8", 128)])
@@ -180,7 +202,9 @@ def test_prefill_strided_views():
 def test_prefill_one_token_chunk_equals_decode():
     """A one-token chunk is a decode step at position kv_len - 1: the output
     matches attn_decode's within the two kernels' rounding (both are gated
-    against the oracle elsewhere; here the two HIP paths agree to 2 bf16 ulp)."""
+    against the oracle elsewhere; here the two HIP paths agree to 2 bf16 ulp,
+    and the log-sum-exp within the prefill's f16 denominator, L_F16 plus
+    2^-25 per key)."""
     announce("prefill one-token chunk vs decode")
     k_ = K()
     inp = kvq_synth.prefill(2, 32, 8, 128, [1024, 777], 1)
@@ -197,7 +221,7 @@ def test_prefill_one_token_chunk_equals_decode():
     k_.attn_decode_combine(part_o, part_lse, 2, 32, 128, used, dec, lse_out=dlse)
     torch.cuda.synchronize()
     assert torch.allclose(out[:, 0], dec, rtol=2e-3, atol=2e-3)
-    assert torch.allclose(lse[:, 0], dlse, rtol=1e-5, atol=1e-5)
+    assert torch.allclose(lse[:, 0], dlse, rtol=1e-5, atol=1e-5 + L_F16 + 1024 * 2.0 ** -25)
 
 
 def test_prefill_empty_and_zero_length():
@@ -210,7 +234,7 @@ def test_prefill_empty_and_zero_length():
     pv_abs, _ = OA.prefill_gqa(kvq_synth.f64(inp.q), khat, np.abs(vhat), inp.kv_lens, inp.softmax_scale)
     kp, vp, lens = _gpu_planes(inp, "nvfp4")
     out, lse = gpu_prefill(inp, kp, vp, lens)
-    _check(out, lse, o_ref, lse_ref, "prefill kv_len 0", pv_abs)
+    _check(out, lse, o_ref, lse_ref, "prefill kv_len 0", pv_abs, _nkeys(inp))
     assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
     q0 = torch.empty(2, 0, 8, 128, dtype=torch.bfloat16, device=DEV)
     o0 = torch.empty(2, 0, 8, 128, dtype=torch.bfloat16, device=DEV)
@@ -250,9 +274,10 @@ def test_prefill_bench_shape_sampled():
         pv, _ = OA.prefill_gqa(qv, khat[b:b + 1, h // G:h // G + 1], np.abs(vhat[b:b + 1, h // G:h // G + 1]),
                                np.array([pos + 1]), inp.softmax_scale)
         got = out[b, i, h].cpu().double().numpy()
-        bound = 1e-5 * (1.0 + np.abs(o1[0, 0, 0])) + 2.0 ** -11 * pv[0, 0, 0]
+        bound = 1e-5 * (1.0 + np.abs(o1[0, 0, 0])) + W_F16 * pv[0, 0, 0]
         assert np.all(np.abs(got - o1[0, 0, 0]) <= bound), f"row (b={b}, i={i}, h={h})"
-        assert abs(float(lse[b, i, h]) - l1[0, 0, 0]) <= 1e-5 * (1 + abs(l1[0, 0, 0])), f"lse (b={b}, i={i}, h={h})"
+        assert abs(float(lse[b, i, h]) - l1[0, 0, 0]) <= 1e-5 * (1 + abs(l1[0, 0, 0])) + L_F16 + (pos + 1) * 2.0 ** -25, \
+            f"lse (b={b}, i={i}, h={h})"
 
 
 # ---------------------------------------------------------------- FP8 queries
@@ -340,9 +365,9 @@ def test_prefill_fp8_query_matches_oracle(case):
     kp, vp, klens = _gpu_planes(inp, fmt, per_head=kvh)
     eps = _fp8_score_eps(qhat, khat, inp.kv_lens, inp.softmax_scale) if fmt == "fp8" else None
     out32, lse32 = gpu_prefill_q8(inp, kp, vp, klens, q8, q_scale)
-    _check(out32, lse32, o_ref, lse_ref, f"prefill fp8 query {name} f32", pv_abs, eps)
+    _check(out32, lse32, o_ref, lse_ref, f"prefill fp8 query {name} f32", pv_abs, _nkeys(inp), eps)
     out, lse = gpu_prefill_q8(inp, kp, vp, klens, q8, q_scale, out_dtype=torch.bfloat16)
-    _check(out, lse, o_ref, lse_ref, f"prefill fp8 query {name} bf16", pv_abs, eps)
+    _check(out, lse, o_ref, lse_ref, f"prefill fp8 query {name} bf16", pv_abs, _nkeys(inp), eps)
     assert torch.equal(out32.to(torch.bfloat16), out)
 
 
@@ -388,7 +413,7 @@ def test_prefill_fp8_query_bench_shape_sampled():
         pv, _ = OA.prefill_gqa(qv, kh, np.abs(vh), np.array([pos + 1]), inp.softmax_scale)
         eps = EPS_FP8_DOT * inp.softmax_scale * float((np.abs(kh[0, 0, :pos + 1]) @ np.abs(qhat[b, i, h])).max())
         got = out[b, i, h].cpu().double().numpy()
-        bound = 1e-5 * (1.0 + np.abs(o1[0, 0, 0])) + (2.0 ** -11 + np.expm1(2 * eps)) * pv[0, 0, 0]
+        bound = 1e-5 * (1.0 + np.abs(o1[0, 0, 0])) + (W_F16 * np.exp(2 * eps) + np.expm1(2 * eps)) * pv[0, 0, 0]
         assert np.all(np.abs(got - o1[0, 0, 0]) <= bound), f"row (b={b}, i={i}, h={h})"
-        assert abs(float(lse[b, i, h]) - l1[0, 0, 0]) <= 1e-5 * (1 + abs(l1[0, 0, 0])) + eps, \
+        assert abs(float(lse[b, i, h]) - l1[0, 0, 0]) <= 1e-5 * (1 + abs(l1[0, 0, 0])) + L_F16 + (pos + 1) * 2.0 ** -25 + eps, \
             f"lse (b={b}, i={i}, h={h})"
