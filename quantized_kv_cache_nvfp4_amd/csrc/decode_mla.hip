@@ -444,7 +444,14 @@ __global__ void __launch_bounds__(kThreads, 1) k_decode_mla(kvq_decode_args a, i
   // half a tile apart: while one dequantizes and scores, the other runs
   // P.V (the two waves of a SIMD are one of each), and their loads go out
   // in alternate halves.  Each group's LDS is its own, and between any two
-  // of its halves lies one work-group barrier.
+  // of its halves lies one work-group barrier.  The two extra barriers sit
+  // in branches that are uniform per wave (grp is the wave's), so this is
+  // the hardware's barrier rather than the HIP model's: s_barrier releases
+  // once every wave of the work-group has reached an s_barrier, whichever
+  // instruction it is, and every wave reaches 2 nsteps + 1 of them (then
+  // the epilogue's), so the k-th barrier of one group pairs with the k-th
+  // of the other.  The GPU tests check this path bit for bit across the
+  // paged and contiguous forms and against the oracle.
   if (grp == 1) __syncthreads();
   for (int n = 0; n < nsteps; n += 2) {
     load_tile(buf[1], 2 * (n + 1) + grp);
