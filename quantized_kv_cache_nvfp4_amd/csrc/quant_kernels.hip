@@ -216,11 +216,151 @@ __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, i
 }
 
 // ---------------------------------------------------------------- NVFP4 pack
+// The pack kernels encode whole blocks with the hardware converters and take
+// encode_nvfp4_block's float64 decisions only where a converter's input lies
+// near a rounding boundary, so the bytes are the same as that routine's.
+//  * Block scale: the E4M3 code of the real quotient bamax / (6 s_t) is the
+//    hardware conversion (round to nearest even) of the float32 quotient
+//    bamax * inv6 (inv6 = 1 / (6 s_t) in float32: relative error below
+//    2^-22 for the product) unless that lies within 2^-20 (relative) of one
+//    of the two midpoints around the candidate; then e4m3_rne_code decides.
+//  * Elements: with D = value(scale code) * s_t, the float32 products
+//    x * ih and x * il, ih and il = rcp(D) (1 +- 2^-19), lie on either side
+//    of the real x / D (their errors are below 2^-21), strictly; the
+//    hardware E2M1 conversion (round to nearest even, saturating at 6, sign
+//    kept) is monotone, so where it gives both the same code, that is the
+//    code of x / D (a tie, exactly at a midpoint, always splits them).
+//    Where they differ (adjacent codes: one midpoint between them), the
+//    element is decided exactly: |x| against that midpoint times D, a
+//    product exact in float64, ties to the even code (e2m1_resolve).  With
+//    bf16 inputs and calibrated scales such elements are not rare (a few in
+//    a thousand at the synthetic GQA cache), so they are resolved one by
+//    one.  Blocks with a non-finite element, a zero scale code or D outside
+//    [2^-100, 2^100] take encode_nvfp4_block whole.
+constexpr float kSide = 0x1p-19f;
+
+__device__ inline uint32_t nvfp4_scale_code(float bamax, float s_t, float inv6) {
+  const float qa = fminf(bamax * inv6, 448.0f);
+  uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(qa, 0.0f, 0, false)) & 0x7Fu;
+  const uint32_t trio = (c > 0u ? c - 1u : 0u) | (c << 8) | ((c < 0x7Eu ? c + 1u : c) << 16);
+  const float vp = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(trio), 0);
+  const float vc = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(trio), 1);
+  const float vn = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(trio), 2);
+  const float mh = 0.5f * (vc + vn), ml = 0.5f * (vc + vp);   // exact in float32
+  const bool near = (c < 0x7Eu && fabsf(qa - mh) <= mh * 0x1p-20f) || (c > 0u && fabsf(qa - ml) <= ml * 0x1p-20f);
+  if (near) c = e4m3_rne_code(static_cast<double>(bamax) / (6.0 * static_cast<double>(s_t)));
+  return c;
+}
+
+// A block's scale code and the two multipliers; ok false: the block takes
+// encode_nvfp4_block (the element test comes on top)
+struct Nvfp4Prep {
+  uint32_t sc;
+  float ih, il;
+  bool ok;
+};
+__device__ inline Nvfp4Prep nvfp4_prep(const float (&v)[16], float s_t, float inv6) {
+  uint32_t mb = 0;   // the largest |x| as bits: equal to the float maximum when all are finite
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mb = max(mb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  const bool fin = mb < 0x7F800000u;
+  Nvfp4Prep p;
+  p.sc = fin ? nvfp4_scale_code(__uint_as_float(mb), s_t, inv6) : 0u;
+  const float D = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(p.sc), 0) * s_t;
+  const float inv = __builtin_amdgcn_rcpf(D);
+  p.ih = inv * (1.0f + kSide);
+  p.il = inv * (1.0f - kSide);
+  p.ok = fin && p.sc != 0u && D >= 0x1p-100f && D <= 0x1p100f;
+  return p;
+}
+
+// E2M1 code of x / D for an element whose two side codes ca, cb differ:
+// their magnitudes are adjacent, and the midpoint between them times D
+// (Ds = value(scale code) * s_t, exact in float64; the product too) decides
+// against |x|, ties to the even code; the sign is x's (as in ca)
+__device__ inline uint32_t e2m1_resolve(float x, uint32_t ca, uint32_t cb, double Ds) {
+  constexpr uint32_t kTwice = 0xC8643210u;   // nibble m: twice the E2M1 magnitude of code m
+  const uint32_t ma = ca & 7u, mb = cb & 7u;
+  const uint32_t hi_m = ma > mb ? ma : mb, lo_m = ma > mb ? mb : ma;
+  const uint32_t s4 = ((kTwice >> (4 * ma)) & 15u) + ((kTwice >> (4 * mb)) & 15u);   // 4 x the midpoint
+  const double md = static_cast<double>(s4) * 0.25 * Ds;
+  const double ax = static_cast<double>(fabsf(x));
+  const uint32_t m = ax > md ? hi_m : (ax < md ? lo_m : ((hi_m & 1u) == 0u ? hi_m : lo_m));
+  return m | (ca & 8u);
+}
+
+// the nibble at bit sh of w (its other side's nibble differs where d has
+// bits) decided by e2m1_resolve
+__device__ inline void resolve_nibble(uint32_t& w, uint32_t d, int sh, float x, double Ds) {
+  const uint32_t dn = (d >> sh) & 15u;
+  if (dn != 0u) {
+    const uint32_t ca = (w >> sh) & 15u;
+    w = (w & ~(15u << sh)) | (e2m1_resolve(x, ca, ca ^ dn, Ds) << sh);
+  }
+}
+
+__device__ inline double nvfp4_ds(uint32_t sc, float s_t) {
+  return static_cast<double>(__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sc), 0)) * static_cast<double>(s_t);
+}
+
+// 8 E2M1 codes of x[o .. o + 7] * m (element o + i in nibble i)
+__device__ inline uint32_t e2m1_word(const float (&x)[16], int o, float m) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[o] * m, x[o + 1] * m, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[o + 2] * m, x[o + 3] * m, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[o + 4] * m, x[o + 5] * m, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[o + 6] * m, x[o + 7] * m, 1.0f, 3);
+  return w;
+}
+
+// TOKEN4: codes of tokens (2H, 2H + 1) of a group (element i: byte 2i + H of
+// the 32, dword i / 2, byte 2 (i & 1) + H), with the multipliers of the side m
+template <int H>
+__device__ inline void t4_pair(const float (&v0)[16], const float (&v1)[16], float m0, float m1, uint32_t (&w)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    w[k] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[k], v0[2 * k] * m0, v1[2 * k] * m1, 1.0f, H);
+    w[k] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[k], v0[2 * k + 1] * m0, v1[2 * k + 1] * m1, 1.0f, 2 + H);
+  }
+}
+
+// TOKEN4: the codes of tokens (2H, 2H + 1) in w (the ih side) where the il
+// side (wl, this pair's bytes only) differs, decided exactly
+template <int H>
+__device__ inline void t4_pair_resolve(const float (&v0)[16], const float (&v1)[16], double ds0, double ds1,
+                                       const uint32_t (&wl)[8], uint32_t (&w)[8]) {
+  constexpr uint32_t kMask = 0x00FF00FFu << (8 * H);
+  uint32_t any = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) any |= (w[k] ^ wl[k]) & kMask;
+  if (any == 0u) return;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t d = (w[k] ^ wl[k]) & kMask;
+    resolve_nibble(w[k], d, 8 * H, v0[2 * k], ds0);
+    resolve_nibble(w[k], d, 8 * H + 4, v1[2 * k], ds1);
+    resolve_nibble(w[k], d, 16 + 8 * H, v0[2 * k + 1], ds0);
+    resolve_nibble(w[k], d, 16 + 8 * H + 4, v1[2 * k + 1], ds1);
+  }
+}
+
+// item it of a head -> (row or group, block); nb a power of two takes a shift
+__device__ inline void split_item(int64_t it, uint32_t nb, int nbsh, int64_t& t, int& blk) {
+  if (nbsh >= 0) {
+    t = it >> nbsh;
+    blk = static_cast<int>(it & (nb - 1u));
+  } else {
+    t = it / nb;
+    blk = static_cast<int>(it - t * nb);
+  }
+}
+
 // ROWS layout: one item per (row, 16-element block) -> 8 code bytes (one
 // 64-bit store), 1 scale byte
-__device__ inline void pack_nvfp4_rows(const PackJob& J, float s_t) {
+__device__ inline void pack_nvfp4_rows(const PackJob& J, float s_t, float inv6) {
   const int d = J.d;
   const uint32_t nb = static_cast<uint32_t>(d / 16);
+  const int nbsh = (nb & (nb - 1u)) == 0u ? __builtin_ctz(nb) : -1;
   const Rows xr = J.xr, dr = J.dr;
   const int64_t nh = xr.n0 * xr.n1;
   for (int64_t h = blockIdx.y; h < nh; h += gridDim.y) {
@@ -229,19 +369,36 @@ __device__ inline void pack_nvfp4_rows(const PackJob& J, float s_t) {
     const int64_t xbase = i0 * xr.s0 + i1 * xr.s1, dbase = i0 * dr.s0 + i1 * dr.s1;
     const int64_t items = xr.n2 * nb;
     for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
-      const int64_t t = it / nb;
-      const int blk = static_cast<int>(it - t * nb);
+      int64_t t;
+      int blk;
+      split_item(it, nb, nbsh, t, blk);
       const int64_t dt_ = t + pos;
       if (dt_ < 0 || dt_ >= dr.n2) continue;  // outside the destination plane
       float v[16];
       load_run<16>(J.x, J.dt, xbase + t * xr.s2 + blk * 16, 16, v);
-      uint32_t c[16];
-      const uint32_t sc = encode_nvfp4_block(v, s_t, c);
-      uint32_t lo = 0, hi = 0;
+      const Nvfp4Prep p = nvfp4_prep(v, s_t, inv6);
+      uint32_t sc = p.sc;
+      uint32_t lo = e2m1_word(v, 0, p.ih), hi = e2m1_word(v, 8, p.ih);
+      const uint32_t dlo = lo ^ e2m1_word(v, 0, p.il), dhi = hi ^ e2m1_word(v, 8, p.il);
+      if (p.ok) {
+        if ((dlo | dhi) != 0u) {   // elements next to a midpoint: exact decisions
+          const double ds = nvfp4_ds(sc, s_t);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        lo |= c[i] << (4 * i);
-        hi |= c[8 + i] << (4 * i);
+          for (int i = 0; i < 8; ++i) {
+            resolve_nibble(lo, dlo, 4 * i, v[i], ds);
+            resolve_nibble(hi, dhi, 4 * i, v[8 + i], ds);
+          }
+        }
+      } else {
+        uint32_t c[16];
+        sc = encode_nvfp4_block(v, s_t, c);
+        lo = 0;
+        hi = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          lo |= c[i] << (4 * i);
+          hi |= c[8 + i] << (4 * i);
+        }
       }
       const int64_t drow = dbase + dt_ * dr.s2;
       *reinterpret_cast<uint2*>(J.codes + drow * (d / 2) + blk * 8) = make_uint2(lo, hi);
@@ -276,9 +433,10 @@ __device__ inline bool t4_group(const Rows& xr, const Rows& dr, const int32_t* d
 // TOKEN4 layout: one item per (4-token group slot, 16-element block): 32
 // code bytes (two 16-byte stores) and one 4-byte scale word; tokens of the
 // group that this call does not write keep their bytes.
-__device__ inline void pack_nvfp4_t4(const PackJob& J, float s_t) {
+__device__ inline void pack_nvfp4_t4(const PackJob& J, float s_t, float inv6) {
   const int d = J.d;
   const uint32_t nb = static_cast<uint32_t>(d / 16);
+  const int nbsh = (nb & (nb - 1u)) == 0u ? __builtin_ctz(nb) : -1;
   const Rows xr = J.xr, dr = J.dr;
   const int64_t slots = t4_slots(xr.n2);
   const int64_t nh = xr.n0 * xr.n1;
@@ -287,14 +445,45 @@ __device__ inline void pack_nvfp4_t4(const PackJob& J, float s_t) {
     const int64_t xbase = i0 * xr.s0 + i1 * xr.s1;
     const int64_t items = slots * nb;
     for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
-      const int64_t gl = it / nb;
-      const int blk = static_cast<int>(it - gl * nb);
+      int64_t gl;
+      int blk;
+      split_item(it, nb, nbsh, gl, blk);
       int64_t t0, src[4];
       if (!t4_group(xr, dr, J.dst_pos, i0, gl, t0, src)) continue;
       const int64_t grow = group_row(dr, i0, i1, t0);
       uint4* cp = reinterpret_cast<uint4*>(J.codes + grow * (d / 2) + blk * 32);
       uint32_t* sp = reinterpret_cast<uint32_t*>(J.scales + grow * nb + blk * 4);
       const bool partial = src[0] < 0 || src[1] < 0 || src[2] < 0 || src[3] < 0;
+      if (!partial) {   // a whole group: tokens (0, 1), then (2, 3), two at a time
+        uint32_t wh[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        uint32_t scw = 0;
+        bool ok = true;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float v0[16], v1[16];
+          load_run<16>(J.x, J.dt, xbase + src[2 * h] * xr.s2 + blk * 16, 16, v0);
+          load_run<16>(J.x, J.dt, xbase + src[2 * h + 1] * xr.s2 + blk * 16, 16, v1);
+          const Nvfp4Prep p0 = nvfp4_prep(v0, s_t, inv6), p1 = nvfp4_prep(v1, s_t, inv6);
+          ok = ok && p0.ok && p1.ok;
+          scw |= (p0.sc | (p1.sc << 8)) << (16 * h);
+          uint32_t wl[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+          if (h == 0) {
+            t4_pair<0>(v0, v1, p0.ih, p1.ih, wh);
+            t4_pair<0>(v0, v1, p0.il, p1.il, wl);
+            if (p0.ok && p1.ok) t4_pair_resolve<0>(v0, v1, nvfp4_ds(p0.sc, s_t), nvfp4_ds(p1.sc, s_t), wl, wh);
+          } else {
+            t4_pair<1>(v0, v1, p0.ih, p1.ih, wh);
+            t4_pair<1>(v0, v1, p0.il, p1.il, wl);
+            if (p0.ok && p1.ok) t4_pair_resolve<1>(v0, v1, nvfp4_ds(p0.sc, s_t), nvfp4_ds(p1.sc, s_t), wl, wh);
+          }
+        }
+        if (ok) {
+          cp[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+          cp[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
+          *sp = scw;
+          continue;
+        }
+      }
       uint4 w0 = partial ? cp[0] : make_uint4(0, 0, 0, 0);
       uint4 w1 = partial ? cp[1] : make_uint4(0, 0, 0, 0);
       uint32_t sw = partial ? *sp : 0u;
@@ -326,8 +515,9 @@ __global__ void __launch_bounds__(kThreads) k_pack_nvfp4(PackJobs P) {
   const PackJob& J = P.j[blockIdx.z];
   const float s_t = nvfp4_tensor_scale(*J.amax);
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && J.sout != nullptr) *J.sout = s_t;
-  if (J.layout == KVQ_PLANE_TOKEN4) pack_nvfp4_t4(J, s_t);
-  else pack_nvfp4_rows(J, s_t);
+  const float inv6 = 1.0f / (6.0f * s_t);
+  if (J.layout == KVQ_PLANE_TOKEN4) pack_nvfp4_t4(J, s_t, inv6);
+  else pack_nvfp4_rows(J, s_t, inv6);
 }
 
 // ---------------------------------------------------------------- FP8 pack
