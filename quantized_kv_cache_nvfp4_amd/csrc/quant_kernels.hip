@@ -521,6 +521,68 @@ __global__ void __launch_bounds__(kThreads) k_pack_nvfp4(PackJobs P) {
 }
 
 // ---------------------------------------------------------------- FP8 pack
+// As for NVFP4, the bulk pack converts every element twice with the
+// hardware (x * ih and x * il, ih and il = (1 / scale) (1 +- 2^-19), both
+// clamped to +-448, converted two at a time into the code word): the two
+// products lie strictly on either side of x / scale (errors below 2^-21), so
+// equal codes are the code of encode_fp8, and where they differ (adjacent
+// codes) one fused multiply-add decides exactly (e4m3_resolve).  Runs with a
+// non-finite element, partial runs and scales below 2^-100 take encode_fp8.
+
+// E4M3 code of x / scale where the side codes ca, cb (bytes, with x's sign)
+// differ: |x| against the midpoint between them times scale; the midpoint
+// has at most 5 significant bits, so m * scale - |x| is formed exactly
+// inside the fused multiply-add and its rounded result has the exact sign
+// (and is 0 only for a tie), ties to the even code
+__device__ inline uint32_t e4m3_resolve(float x, uint32_t ca, uint32_t cb, float scale) {
+  const uint32_t ma = ca & 0x7Fu, mb = cb & 0x7Fu;
+  const uint32_t hi_m = ma > mb ? ma : mb, lo_m = ma > mb ? mb : ma;
+  const float vh = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(hi_m), 0);
+  const float vl = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(lo_m), 0);
+  const float dd = __builtin_fmaf(0.5f * (vh + vl), scale, -fabsf(x));
+  const uint32_t m = dd < 0.0f ? hi_m : (dd > 0.0f ? lo_m : ((hi_m & 1u) == 0u ? hi_m : lo_m));
+  return m | (ca & 0x80u);
+}
+
+// the byte at bit sh of w (its other side's byte differs where d has bits)
+// decided by e4m3_resolve
+__device__ inline void resolve_byte(uint32_t& w, uint32_t d, int sh, float x, float scale) {
+  if (((d >> sh) & 0xFFu) != 0u) {
+    const uint32_t ca = (w >> sh) & 0xFFu, cb = ca ^ ((d >> sh) & 0xFFu);
+    w = (w & ~(0xFFu << sh)) | (e4m3_resolve(x, ca, cb, scale) << sh);
+  }
+}
+
+// codes of x0 .. x3 (byte i) on the side m
+__device__ inline uint32_t e4m3_word(float x0, float x1, float x2, float x3, float m) {
+  const float a0 = __builtin_amdgcn_fmed3f(x0 * m, -448.0f, 448.0f), a1 = __builtin_amdgcn_fmed3f(x1 * m, -448.0f, 448.0f);
+  const float a2 = __builtin_amdgcn_fmed3f(x2 * m, -448.0f, 448.0f), a3 = __builtin_amdgcn_fmed3f(x3 * m, -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// the exact codes of x0 .. x3 (all finite; scale >= 2^-100)
+__device__ inline uint32_t fp8_word_fast(float x0, float x1, float x2, float x3, float ih, float il, float scale) {
+  uint32_t w = e4m3_word(x0, x1, x2, x3, ih);
+  const uint32_t d = w ^ e4m3_word(x0, x1, x2, x3, il);
+  if (d != 0u) {
+    resolve_byte(w, d, 0, x0, scale);
+    resolve_byte(w, d, 8, x1, scale);
+    resolve_byte(w, d, 16, x2, scale);
+    resolve_byte(w, d, 24, x3, scale);
+  }
+  return w;
+}
+
+template <int N>
+__device__ inline bool all_finite(const float (&v)[N]) {
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) mb = max(mb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  return mb < 0x7F800000u;
+}
+
 // ROWS layout: one item per (row, 16-element run): 16 code bytes (one
 // 16-byte store; d % 16 != 0 leaves a shorter last run, stored per word)
 // The scale of head i1: one per tensor, or amax[i1] / 448 with one scale
@@ -543,6 +605,8 @@ __device__ inline void pack_fp8_rows(const PackJob& J, double dscale0, float inv
     double dscale = dscale0;
     float inv = inv0;
     fp8_head_scale(J, i0, i1, dscale, inv);
+    const float fsc = static_cast<float>(dscale), ih = inv * (1.0f + 0x1p-19f), il = inv * (1.0f - 0x1p-19f);
+    const bool fast = fsc >= 0x1p-100f;
     const int64_t pos = J.dst_pos != nullptr ? J.dst_pos[i0] : 0;
     const int64_t xbase = i0 * xr.s0 + i1 * xr.s1, dbase = i0 * dr.s0 + i1 * dr.s1;
     const int64_t items = xr.n2 * nr;
@@ -555,11 +619,16 @@ __device__ inline void pack_fp8_rows(const PackJob& J, double dscale0, float inv
       float v[16];
       load_run<16>(J.x, J.dt, xbase + t * xr.s2 + 16 * run, n, v);
       uint32_t w[4];
+      if (fast && n == 16 && all_finite(v)) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        w[q] = 0;
+        for (int q = 0; q < 4; ++q) w[q] = fp8_word_fast(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], ih, il, fsc);
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[q] |= encode_fp8(v[4 * q + i], inv, dscale) << (8 * i);
+        for (int q = 0; q < 4; ++q) {
+          w[q] = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[q] |= encode_fp8(v[4 * q + i], inv, dscale) << (8 * i);
+        }
       }
       uint8_t* dst = J.codes + (dbase + dt_ * dr.s2) * d + 16 * run;
       if (n == 16 && (reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
@@ -585,6 +654,8 @@ __device__ inline void pack_fp8_t4(const PackJob& J, double dscale0, float inv0)
     double dscale = dscale0;
     float inv = inv0;
     fp8_head_scale(J, i0, i1, dscale, inv);
+    const float fsc = static_cast<float>(dscale), ih = inv * (1.0f + 0x1p-19f), il = inv * (1.0f - 0x1p-19f);
+    const bool fast = fsc >= 0x1p-100f;
     const int64_t xbase = i0 * xr.s0 + i1 * xr.s1;
     const int64_t items = slots * nw;
     for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
@@ -594,6 +665,18 @@ __device__ inline void pack_fp8_t4(const PackJob& J, double dscale0, float inv0)
       if (!t4_group(xr, dr, J.dst_pos, i0, gl, t0, src)) continue;
       uint4* cp = reinterpret_cast<uint4*>(J.codes + group_row(dr, i0, i1, t0) * d + w * 16);
       const bool partial = src[0] < 0 || src[1] < 0 || src[2] < 0 || src[3] < 0;
+      if (fast && !partial) {   // a whole group: dword i = element 4w + i of tokens 0 .. 3
+        float x[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) load_run<4>(J.x, J.dt, xbase + src[j] * xr.s2 + w * 4, 4, x[j]);
+        if (all_finite(x[0]) && all_finite(x[1]) && all_finite(x[2]) && all_finite(x[3])) {
+          uint32_t o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = fp8_word_fast(x[0][i], x[1][i], x[2][i], x[3][i], ih, il, fsc);
+          *cp = make_uint4(o[0], o[1], o[2], o[3]);
+          continue;
+        }
+      }
       uint4 wv = partial ? *cp : make_uint4(0, 0, 0, 0);
       uint32_t* wd[4] = {&wv.x, &wv.y, &wv.z, &wv.w};
 #pragma unroll
