@@ -642,10 +642,13 @@ __device__ inline void pack_fp8_rows(const PackJob& J, double dscale0, float inv
   }
 }
 
-// TOKEN4 layout: one item per (4-token group slot, 4 elements): 16 code bytes
+// TOKEN4 layout: one item per (4-token group slot, 16 elements): 64 code
+// bytes (4 elements and 16 bytes when d is not a multiple of 16)
 __device__ inline void pack_fp8_t4(const PackJob& J, double dscale0, float inv0) {
   const int d = J.d;
-  const uint32_t nw = static_cast<uint32_t>(d / 4);
+  const int per = d % 16 == 0 ? 4 : 1;   // 16-byte code words per item
+  const uint32_t nw = static_cast<uint32_t>(d / (4 * per));
+  const int nwsh = (nw & (nw - 1u)) == 0u ? __builtin_ctz(nw) : -1;
   const Rows xr = J.xr, dr = J.dr;
   const int64_t slots = t4_slots(xr.n2);
   const int64_t nh = xr.n0 * xr.n1;
@@ -659,36 +662,56 @@ __device__ inline void pack_fp8_t4(const PackJob& J, double dscale0, float inv0)
     const int64_t xbase = i0 * xr.s0 + i1 * xr.s1;
     const int64_t items = slots * nw;
     for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
-      const int64_t gl = it / nw;
-      const int w = static_cast<int>(it - gl * nw);
+      int64_t gl;
+      int r;
+      split_item(it, nw, nwsh, gl, r);
       int64_t t0, src[4];
       if (!t4_group(xr, dr, J.dst_pos, i0, gl, t0, src)) continue;
-      uint4* cp = reinterpret_cast<uint4*>(J.codes + group_row(dr, i0, i1, t0) * d + w * 16);
+      uint4* cp = reinterpret_cast<uint4*>(J.codes + group_row(dr, i0, i1, t0) * d + r * 16 * per);
       const bool partial = src[0] < 0 || src[1] < 0 || src[2] < 0 || src[3] < 0;
-      if (fast && !partial) {   // a whole group: dword i = element 4w + i of tokens 0 .. 3
-        float x[4][4];
+      if (fast && !partial && per == 4) {   // a whole group, 16 elements: dword e = element 16 r + e of tokens 0 .. 3
+        float x[4][16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) load_run<4>(J.x, J.dt, xbase + src[j] * xr.s2 + w * 4, 4, x[j]);
+        for (int j = 0; j < 4; ++j) load_run<16>(J.x, J.dt, xbase + src[j] * xr.s2 + r * 16, 16, x[j]);
         if (all_finite(x[0]) && all_finite(x[1]) && all_finite(x[2]) && all_finite(x[3])) {
-          uint32_t o[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = fp8_word_fast(x[0][i], x[1][i], x[2][i], x[3][i], ih, il, fsc);
-          *cp = make_uint4(o[0], o[1], o[2], o[3]);
+          for (int q = 0; q < 4; ++q) {
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              o[i] = fp8_word_fast(x[0][4 * q + i], x[1][4 * q + i], x[2][4 * q + i], x[3][4 * q + i], ih, il, fsc);
+            cp[q] = make_uint4(o[0], o[1], o[2], o[3]);
+          }
           continue;
         }
       }
-      uint4 wv = partial ? *cp : make_uint4(0, 0, 0, 0);
-      uint32_t* wd[4] = {&wv.x, &wv.y, &wv.z, &wv.w};
+      for (int q = 0; q < per; ++q) {   // 4 elements at a time: w = the word of the row
+        const int w = r * per + q;
+        if (fast && !partial) {   // a whole group: dword i = element 4w + i of tokens 0 .. 3
+          float x[4][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (src[j] < 0) continue;
-        float v[4];
-        load_run<4>(J.x, J.dt, xbase + src[j] * xr.s2 + w * 4, 4, v);
+          for (int j = 0; j < 4; ++j) load_run<4>(J.x, J.dt, xbase + src[j] * xr.s2 + w * 4, 4, x[j]);
+          if (all_finite(x[0]) && all_finite(x[1]) && all_finite(x[2]) && all_finite(x[3])) {
+            uint32_t o[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)  // element 4w + i of token j: byte 4 (4w + i) + j
-          *wd[i] = (*wd[i] & ~(0xFFu << (8 * j))) | (encode_fp8(v[i], inv, dscale) << (8 * j));
+            for (int i = 0; i < 4; ++i) o[i] = fp8_word_fast(x[0][i], x[1][i], x[2][i], x[3][i], ih, il, fsc);
+            cp[q] = make_uint4(o[0], o[1], o[2], o[3]);
+            continue;
+          }
+        }
+        uint4 wv = partial ? cp[q] : make_uint4(0, 0, 0, 0);
+        uint32_t* wd[4] = {&wv.x, &wv.y, &wv.z, &wv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (src[j] < 0) continue;
+          float v[4];
+          load_run<4>(J.x, J.dt, xbase + src[j] * xr.s2 + w * 4, 4, v);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)  // element 4w + i of token j: byte 4 (4w + i) + j
+            *wd[i] = (*wd[i] & ~(0xFFu << (8 * j))) | (encode_fp8(v[i], inv, dscale) << (8 * j));
+        }
+        cp[q] = wv;
       }
-      *cp = wv;
     }
   }
 }
@@ -793,10 +816,11 @@ hipError_t launch_amax(const void* x, int x_dtype, Rows rows, int d, const int32
 }
 
 // items of one head of one job: (row, 16-block) / (row, 16-element run), or
-// (4-token group slot, 16-block / 4 elements) for TOKEN4 destinations
+// (4-token group slot, 16-block / 16 elements, or 4 when d is not a multiple
+// of 16) for TOKEN4 destinations
 static int64_t pack_items_per_head(const PackJob& J, bool fp4) {
   const bool t4 = J.layout == KVQ_PLANE_TOKEN4;
-  const int64_t per = fp4 ? J.d / 16 : (t4 ? J.d / 4 : (J.d + 15) / 16);
+  const int64_t per = fp4 ? J.d / 16 : (t4 ? (J.d % 16 == 0 ? J.d / 16 : J.d / 4) : (J.d + 15) / 16);
   return (t4 ? J.xr.n2 / 4 + 2 : J.xr.n2) * per;
 }
 
