@@ -175,12 +175,9 @@ def test_fp8_pack_bit_exact(dt):
     assert np.array_equal(_np(u).astype(np.float64), OF.fp32_round(OQ.fp8_unpack(c, sc)))
 
 
-@pytest.mark.parametrize("amax_val", [448.0, 224.0, 672.0, 0.3])
-def test_fp8_pack_adversarial(amax_val):
+def _fp8_adversarial_values(amax_val):
     """Every E4M3 rounding midpoint (times the scale amax/448) and its two
-    float32 neighbours, plus saturation, zeros and -0: exact ties go to the
-    even code; the GPU codes equal the oracle's bit for bit."""
-    announce(f"pack fp8 adversarial amax={amax_val}")
+    float32 neighbours, plus saturation, zeros and -0, both signs."""
     scale = np.float32(np.float32(amax_val) / np.float32(448.0))
     pos = OF.e4m3_decode(np.arange(0x7F))
     vals = [0.0, -0.0, 448.0 * scale, 500.0 * scale, 1e30]
@@ -188,7 +185,15 @@ def test_fp8_pack_adversarial(amax_val):
         m = np.float32((a + b) / 2 * np.float64(scale))
         vals += [m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1e9))]
     v = np.asarray(vals, np.float32)
-    v = np.concatenate([v, -v])
+    return np.concatenate([v, -v])
+
+
+@pytest.mark.parametrize("amax_val", [448.0, 224.0, 672.0, 0.3])
+def test_fp8_pack_adversarial(amax_val):
+    """The adversarial values (every decision boundary): exact ties go to the
+    even code; the GPU codes equal the oracle's bit for bit."""
+    announce(f"pack fp8 adversarial amax={amax_val}")
+    v = _fp8_adversarial_values(amax_val)
     v = np.concatenate([v, np.zeros((-len(v)) % 16, np.float32)]).reshape(-1, 16)
     x = torch.from_numpy(v)
     amax = torch.tensor([np.float32(amax_val)], device=DEV)
@@ -197,6 +202,39 @@ def test_fp8_pack_adversarial(amax_val):
     torch.cuda.synchronize()
     assert float(p.scale.item()) == sc
     assert np.array_equal(_np(p.codes), c)
+
+
+@pytest.mark.parametrize("case", [("nvfp4", 64, torch.float32), ("nvfp4", 64, torch.bfloat16),
+                                  ("fp8", 16, torch.float32), ("fp8", 20, torch.float32), ("fp8", 16, torch.bfloat16)],
+                         ids=str)
+def test_token4_pack_adversarial(case):
+    """The adversarial rows packed into a TOKEN4 plane (whole 4-token groups:
+    the per-element decisions of the group paths; d = 20 takes the FP8
+    4-element path) equal the oracle's codes in that layout, bit for bit."""
+    fmt, d, dt = case
+    announce(f"pack {fmt} token4 adversarial d={d} {dt}")
+    if fmt == "nvfp4":
+        v, amax_val = _adversarial_rows().reshape(-1), np.float32(2688.0)
+    else:
+        v, amax_val = _fp8_adversarial_values(448.0), np.float32(448.0)
+    per = 4 * d   # four tokens of d elements
+    v = np.concatenate([v, np.zeros((-len(v)) % per, np.float32)]).reshape(1, 1, -1, d)
+    x = torch.from_numpy(v).to(dt)
+    L = x.shape[2]
+    plane = empty_plane(fmt, (1, 1, L), d, K().KVQ_PLANE_TOKEN4, fill=0)
+    amax = torch.tensor([amax_val], device=DEV)
+    xf = kvq_synth.f64(x)
+    if fmt == "nvfp4":
+        K().kvq_pack_nvfp4(x.to(DEV), amax, out=plane)
+        c, sc, _ = OQ.nvfp4_pack(xf, float(amax_val))
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(plane.scales), to_token4(sc, "scales"))
+        assert np.array_equal(_np(plane.codes), to_token4(nibbles(c), "nvfp4"))
+    else:
+        K().kvq_pack_fp8(x.to(DEV), amax, out=plane)
+        c, _ = OQ.fp8_pack(xf, float(amax_val))
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(plane.codes), to_token4(c, "fp8"))
 
 
 def test_append_with_dst_pos():
