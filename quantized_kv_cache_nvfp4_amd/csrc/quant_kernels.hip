@@ -231,8 +231,8 @@ __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, i
 //    kept) is monotone, so where it gives both the same code, that is the
 //    code of x / D (a tie, exactly at a midpoint, always splits them).
 //    Where they differ (adjacent codes: one midpoint between them), the
-//    element is decided exactly: |x| against that midpoint times D, a
-//    product exact in float64, ties to the even code (e2m1_resolve).  With
+//    element is decided exactly: the sign of (midpoint * s_hat) * s_t - |x|
+//    from one fused multiply-add, ties to the even code (e2m1_resolve).  With
 //    bf16 inputs and calibrated scales such elements are not rare (a few in
 //    a thousand at the synthetic GQA cache), so they are resolved one by
 //    one.  Blocks with a non-finite element, a zero scale code or D outside
@@ -275,33 +275,47 @@ __device__ inline Nvfp4Prep nvfp4_prep(const float (&v)[16], float s_t, float in
 }
 
 // E2M1 code of x / D for an element whose two side codes ca, cb differ:
-// their magnitudes are adjacent, and the midpoint between them times D
-// (Ds = value(scale code) * s_t, exact in float64; the product too) decides
-// against |x|, ties to the even code; the sign is x's (as in ca)
-__device__ inline uint32_t e2m1_resolve(float x, uint32_t ca, uint32_t cb, double Ds) {
+// their magnitudes are adjacent, and x is decided against the midpoint m
+// between them: m * s_hat has at most 9 significant bits (exact in float32),
+// so (m s_hat) * s_t - |x| is formed exactly inside one fused multiply-add and
+// its rounded result has the exact sign (0 only for a tie; D >= 2^-100 keeps
+// nonzero results clear of underflow); ties to the even code; the sign is
+// x's (as in ca)
+__device__ inline uint32_t e2m1_resolve(float x, uint32_t ca, uint32_t cb, float shat, float s_t) {
   constexpr uint32_t kTwice = 0xC8643210u;   // nibble m: twice the E2M1 magnitude of code m
   const uint32_t ma = ca & 7u, mb = cb & 7u;
   const uint32_t hi_m = ma > mb ? ma : mb, lo_m = ma > mb ? mb : ma;
   const uint32_t s4 = ((kTwice >> (4 * ma)) & 15u) + ((kTwice >> (4 * mb)) & 15u);   // 4 x the midpoint
-  const double md = static_cast<double>(s4) * 0.25 * Ds;
-  const double ax = static_cast<double>(fabsf(x));
-  const uint32_t m = ax > md ? hi_m : (ax < md ? lo_m : ((hi_m & 1u) == 0u ? hi_m : lo_m));
+  const float dd = __builtin_fmaf(static_cast<float>(s4) * 0.25f * shat, s_t, -fabsf(x));
+  const uint32_t m = dd < 0.0f ? hi_m : (dd > 0.0f ? lo_m : ((hi_m & 1u) == 0u ? hi_m : lo_m));
   return m | (ca & 8u);
 }
 
 // the nibble at bit sh of w (its other side's nibble differs where d has
 // bits) decided by e2m1_resolve
-__device__ inline void resolve_nibble(uint32_t& w, uint32_t d, int sh, float x, double Ds) {
+__device__ inline void resolve_nibble(uint32_t& w, uint32_t d, int sh, float x, float shat, float s_t) {
   const uint32_t dn = (d >> sh) & 15u;
   if (dn != 0u) {
     const uint32_t ca = (w >> sh) & 15u;
-    w = (w & ~(15u << sh)) | (e2m1_resolve(x, ca, ca ^ dn, Ds) << sh);
+    w = (w & ~(15u << sh)) | (e2m1_resolve(x, ca, ca ^ dn, shat, s_t) << sh);
   }
 }
 
-__device__ inline double nvfp4_ds(uint32_t sc, float s_t) {
-  return static_cast<double>(__builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sc), 0)) * static_cast<double>(s_t);
+// v[i] for a per-lane index i: a tree of bit selects on the index bits (no
+// indexed access, which would put v in scratch memory)
+__device__ inline float pick16(const float (&v)[16], int i) {
+  const uint32_t m0 = 0u - static_cast<uint32_t>(i & 1), m1 = 0u - static_cast<uint32_t>((i >> 1) & 1);
+  const uint32_t m2 = 0u - static_cast<uint32_t>((i >> 2) & 1), m3 = 0u - static_cast<uint32_t>((i >> 3) & 1);
+  uint32_t a[8], b[4];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a[k] = (__float_as_uint(v[2 * k + 1]) & m0) | (__float_as_uint(v[2 * k]) & ~m0);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) b[k] = (a[2 * k + 1] & m1) | (a[2 * k] & ~m1);
+  const uint32_t c0 = (b[1] & m2) | (b[0] & ~m2), c1 = (b[3] & m2) | (b[2] & ~m2);
+  return __uint_as_float((c1 & m3) | (c0 & ~m3));
 }
+
+__device__ inline float e4m3_val(uint32_t sc) { return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sc), 0); }
 
 // 8 E2M1 codes of x[o .. o + 7] * m (element o + i in nibble i)
 __device__ inline uint32_t e2m1_word(const float (&x)[16], int o, float m) {
@@ -327,7 +341,7 @@ __device__ inline void t4_pair(const float (&v0)[16], const float (&v1)[16], flo
 // TOKEN4: the codes of tokens (2H, 2H + 1) in w (the ih side) where the il
 // side (wl, this pair's bytes only) differs, decided exactly
 template <int H>
-__device__ inline void t4_pair_resolve(const float (&v0)[16], const float (&v1)[16], double ds0, double ds1,
+__device__ inline void t4_pair_resolve(const float (&v0)[16], const float (&v1)[16], float sh0, float sh1, float s_t,
                                        const uint32_t (&wl)[8], uint32_t (&w)[8]) {
   constexpr uint32_t kMask = 0x00FF00FFu << (8 * H);
   uint32_t any = 0;
@@ -337,10 +351,10 @@ __device__ inline void t4_pair_resolve(const float (&v0)[16], const float (&v1)[
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const uint32_t d = (w[k] ^ wl[k]) & kMask;
-    resolve_nibble(w[k], d, 8 * H, v0[2 * k], ds0);
-    resolve_nibble(w[k], d, 8 * H + 4, v1[2 * k], ds1);
-    resolve_nibble(w[k], d, 16 + 8 * H, v0[2 * k + 1], ds0);
-    resolve_nibble(w[k], d, 16 + 8 * H + 4, v1[2 * k + 1], ds1);
+    resolve_nibble(w[k], d, 8 * H, v0[2 * k], sh0, s_t);
+    resolve_nibble(w[k], d, 8 * H + 4, v1[2 * k], sh1, s_t);
+    resolve_nibble(w[k], d, 16 + 8 * H, v0[2 * k + 1], sh0, s_t);
+    resolve_nibble(w[k], d, 16 + 8 * H + 4, v1[2 * k + 1], sh1, s_t);
   }
 }
 
@@ -381,14 +395,22 @@ __device__ inline void pack_nvfp4_rows(const PackJob& J, float s_t, float inv6) 
       uint32_t lo = e2m1_word(v, 0, p.ih), hi = e2m1_word(v, 8, p.ih);
       const uint32_t dlo = lo ^ e2m1_word(v, 0, p.il), dhi = hi ^ e2m1_word(v, 8, p.il);
       if (p.ok) {
-        if ((dlo | dhi) != 0u) {   // elements next to a midpoint: exact decisions
-          const double ds = nvfp4_ds(sc, s_t);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            resolve_nibble(lo, dlo, 4 * i, v[i], ds);
-            resolve_nibble(hi, dhi, 4 * i, v[8 + i], ds);
+        // elements next to a midpoint: exact decisions, one differing nibble
+        // per lane and pass (usually one pass)
+        uint64_t dd = (static_cast<uint64_t>(dhi) << 32) | dlo;
+        uint64_t code = (static_cast<uint64_t>(hi) << 32) | lo;
+        const float shat = e4m3_val(sc);
+        while (__any(dd != 0u)) {
+          if (dd != 0u) {
+            const int sh = __builtin_ctzll(dd) & ~3;
+            const uint32_t ca = static_cast<uint32_t>(code >> sh) & 15u;
+            const uint32_t cb = ca ^ (static_cast<uint32_t>(dd >> sh) & 15u);
+            code = (code & ~(15ull << sh)) | (static_cast<uint64_t>(e2m1_resolve(pick16(v, sh >> 2), ca, cb, shat, s_t)) << sh);
+            dd &= ~(15ull << sh);
           }
         }
+        lo = static_cast<uint32_t>(code);
+        hi = static_cast<uint32_t>(code >> 32);
       } else {
         uint32_t c[16];
         sc = encode_nvfp4_block(v, s_t, c);
@@ -470,11 +492,11 @@ __device__ inline void pack_nvfp4_t4(const PackJob& J, float s_t, float inv6) {
           if (h == 0) {
             t4_pair<0>(v0, v1, p0.ih, p1.ih, wh);
             t4_pair<0>(v0, v1, p0.il, p1.il, wl);
-            if (p0.ok && p1.ok) t4_pair_resolve<0>(v0, v1, nvfp4_ds(p0.sc, s_t), nvfp4_ds(p1.sc, s_t), wl, wh);
+            if (p0.ok && p1.ok) t4_pair_resolve<0>(v0, v1, e4m3_val(p0.sc), e4m3_val(p1.sc), s_t, wl, wh);
           } else {
             t4_pair<1>(v0, v1, p0.ih, p1.ih, wh);
             t4_pair<1>(v0, v1, p0.il, p1.il, wl);
-            if (p0.ok && p1.ok) t4_pair_resolve<1>(v0, v1, nvfp4_ds(p0.sc, s_t), nvfp4_ds(p1.sc, s_t), wl, wh);
+            if (p0.ok && p1.ok) t4_pair_resolve<1>(v0, v1, e4m3_val(p0.sc), e4m3_val(p1.sc), s_t, wl, wh);
           }
         }
         if (ok) {
