@@ -29,12 +29,6 @@ using namespace codec;
 
 constexpr int kThreads = 256;
 
-__device__ inline float load_elem(const void* base, int dt, int64_t idx) {
-  if (dt == KVQ_F32) return static_cast<const float*>(base)[idx];
-  uint32_t bits = static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16;
-  return __uint_as_float(bits);
-}
-
 // unravel a flat row index into the (i0, i1, i2) of `r`
 __device__ inline void unravel(int64_t row, const Rows& r, int64_t& i0, int64_t& i1, int64_t& i2) {
   i2 = row % r.n2;
