@@ -31,8 +31,11 @@ __global__ void __launch_bounds__(kThreads) k_combine(const float* __restrict__ 
   const int sl = static_cast<int>(wv - bh * nsl);
   const int d_lo = sl * kSlice, d_hi = d_lo + kSlice < Dv ? d_lo + kSlice : Dv;
   const float osc = (out_dtype == KVQ_FP8E4M3) ? *out_scale : 1.0f;
-  combine_head<false>(part_lse + bh * s, part_o + bh * s * Dv, s, Dv, d_lo, d_hi, out, out_dtype, bh * Dv, osc,
-                      (lse_out != nullptr && sl == 0) ? lse_out + bh : nullptr);
+  float* const lo = (lse_out != nullptr && sl == 0) ? lse_out + bh : nullptr;
+  // up to 8 splits: loads of those splits only (the same sums: the extra
+  // terms of the wider forms add +0 in the same order)
+  if (s <= 8) combine_head_n<false, 8>(part_lse + bh * s, part_o + bh * s * Dv, s, Dv, d_lo, d_hi, out, out_dtype, bh * Dv, osc, lo);
+  else combine_head<false>(part_lse + bh * s, part_o + bh * s * Dv, s, Dv, d_lo, d_hi, out, out_dtype, bh * Dv, osc, lo);
 }
 
 }  // namespace
