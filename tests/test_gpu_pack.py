@@ -188,13 +188,14 @@ def _fp8_adversarial_values(amax_val):
     return np.concatenate([v, -v])
 
 
-@pytest.mark.parametrize("amax_val", [448.0, 224.0, 672.0, 0.3])
-def test_fp8_pack_adversarial(amax_val):
+@pytest.mark.parametrize("amax_val,d", [(448.0, 16), (224.0, 16), (672.0, 16), (0.3, 16), (448.0, 20)])
+def test_fp8_pack_adversarial(amax_val, d):
     """The adversarial values (every decision boundary): exact ties go to the
-    even code; the GPU codes equal the oracle's bit for bit."""
-    announce(f"pack fp8 adversarial amax={amax_val}")
+    even code; the GPU codes equal the oracle's bit for bit (d = 20: rows of a
+    whole 16-element run and a 4-element one)."""
+    announce(f"pack fp8 adversarial amax={amax_val} d={d}")
     v = _fp8_adversarial_values(amax_val)
-    v = np.concatenate([v, np.zeros((-len(v)) % 16, np.float32)]).reshape(-1, 16)
+    v = np.concatenate([v, np.zeros((-len(v)) % d, np.float32)]).reshape(-1, d)
     x = torch.from_numpy(v)
     amax = torch.tensor([np.float32(amax_val)], device=DEV)
     p = K().kvq_pack_fp8(x.to(DEV), amax)
