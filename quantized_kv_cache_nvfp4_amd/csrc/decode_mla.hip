@@ -501,14 +501,17 @@ __global__ void __launch_bounds__(kThreads, 1) k_decode_mla(kvq_decode_args a, i
     m_ref = M;
   }
 
-  // ---- partials: o = acc * s_t / l, lse = (m + log2 l) ln 2
+  // ---- partials: o = acc * s_t / l, lse = (m + log2 l) ln 2 (non-temporal
+  // stores: the partials are read once, by the merge; the end-of-kernel
+  // burst of 8.4 MB at B = 32 measured 0.9 us shorter than with cached stores)
   const float f = lt > 0.0f ? s_t / lt : 0.0f;
   const int64_t po = (static_cast<int64_t>(b) * a.Hq + c) * num_splits + split;
   float* op = a.part_o + po * kD + 128 * wave + 4 * g;
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj)
-    *reinterpret_cast<float4*>(op + 16 * jj) =
-        make_float4(acc_o[jj][0] * f, acc_o[jj][1] * f, acc_o[jj][2] * f, acc_o[jj][3] * f);
+  for (int jj = 0; jj < 8; ++jj) {
+    const f32x4 ov = {acc_o[jj][0] * f, acc_o[jj][1] * f, acc_o[jj][2] * f, acc_o[jj][3] * f};
+    __builtin_nontemporal_store(ov, reinterpret_cast<f32x4*>(op + 16 * jj));
+  }
   if (wave == 0 && g == 0) a.part_lse[po] = lt > 0.0f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY;
 }
 
