@@ -347,9 +347,14 @@ def read_probe(args):
     if not os.path.exists(kbuild.PROBE_LIB_PATH):
         raise RuntimeError(f"{kbuild.PROBE_LIB_PATH} missing: run __graft_entry__.build()")
     lib = ctypes.CDLL(kbuild.PROBE_LIB_PATH)
-    lib.kvq_probe_read.restype = ctypes.c_int
-    lib.kvq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p,
-                                   ctypes.c_void_p]
+    for name in ("kvq_probe_read", "kvq_probe_read_nt"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    for name in ("kvq_probe_read_chunks", "kvq_probe_read_chunks_nt"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     n = B * HKV * L * BYTES_PER_TOKEN_HEAD
@@ -357,40 +362,43 @@ def read_probe(args):
     bufs = [torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev) for _ in range(n_copies)]
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     tm = Timer(torch, n_copies, args.steps)
-    res = {}
-    for grid in (256, 512, 1024, 2048, 4096, 8192):
-        def fn(i, grid=grid):
-            rc = lib.kvq_probe_read(ctypes.c_void_p(bufs[i].data_ptr()), n, grid, ctypes.c_void_p(sink.data_ptr()),
-                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-            if rc != 0:
-                raise RuntimeError(f"kvq_probe_read failed ({rc})")
-        us = tm.run(fn) * 1e3
-        res[grid] = us
-        log(f"read probe grid {grid}: {us:.3f} us/launch, {n / us / 1e3:.1f} GB/s")
-    best = min(res, key=res.get)
-    us = res[best]
-    # the decode kernels' launch shape: one 256-thread work-group per CU, each
-    # reading one contiguous chunk (as the split-KV work-groups do), with the
-    # chunk streamed as 1, 2 or 4 side-by-side parts
-    lib.kvq_probe_read_chunks.restype = ctypes.c_int
-    lib.kvq_probe_read_chunks.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
-                                          ctypes.c_void_p, ctypes.c_void_p]
-    chunks = {}
-    for grid, fronts in ((256, 1), (256, 2), (256, 4), (512, 1)):
-        def fc(i, grid=grid, fronts=fronts):
-            rc = lib.kvq_probe_read_chunks(ctypes.c_void_p(bufs[i].data_ptr()), n, grid, fronts,
-                                           ctypes.c_void_p(sink.data_ptr()),
-                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-            if rc != 0:
-                raise RuntimeError(f"kvq_probe_read_chunks failed ({rc})")
-        cu = tm.run(fc) * 1e3
-        chunks[f"grid{grid}_fronts{fronts}"] = round(cu, 3)
-        log(f"chunked read grid {grid} fronts {fronts}: {cu:.3f} us/launch, {n / cu / 1e3:.1f} GB/s")
+    # plain loads and loads with the non-temporal hint (the hint the NVFP4
+    # decode planes are read with)
+    res, chunks = {"": {}, "_nt": {}}, {"": {}, "_nt": {}}
+    for sfx in ("", "_nt"):
+        fread = getattr(lib, "kvq_probe_read" + sfx)
+        for grid in (256, 512, 1024, 2048, 4096, 8192):
+            def fn(i, grid=grid, fread=fread):
+                rc = fread(ctypes.c_void_p(bufs[i].data_ptr()), n, grid, ctypes.c_void_p(sink.data_ptr()),
+                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"kvq_probe_read{sfx} failed ({rc})")
+            us = tm.run(fn) * 1e3
+            res[sfx][grid] = us
+            log(f"read probe{sfx} grid {grid}: {us:.3f} us/launch, {n / us / 1e3:.1f} GB/s")
+        # the decode kernels' launch shape: one 256-thread work-group per CU,
+        # each reading one contiguous chunk (as the split-KV work-groups do),
+        # with the chunk streamed as 1, 2 or 4 side-by-side parts
+        fchunk = getattr(lib, "kvq_probe_read_chunks" + sfx)
+        for grid, fronts in ((256, 1), (256, 2), (256, 4), (512, 1)):
+            def fc(i, grid=grid, fronts=fronts, fchunk=fchunk):
+                rc = fchunk(ctypes.c_void_p(bufs[i].data_ptr()), n, grid, fronts, ctypes.c_void_p(sink.data_ptr()),
+                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"kvq_probe_read_chunks{sfx} failed ({rc})")
+            cu = tm.run(fc) * 1e3
+            chunks[sfx][f"grid{grid}_fronts{fronts}"] = round(cu, 3)
+            log(f"chunked read{sfx} grid {grid} fronts {fronts}: {cu:.3f} us/launch, {n / cu / 1e3:.1f} GB/s")
+    # the ceiling: the fastest plain read over both load policies and every grid
+    best_sfx, best = min(((sfx, g) for sfx in res for g in res[sfx]), key=lambda k: res[k[0]][k[1]])
+    us = res[best_sfx][best]
     out = {"metric": "streaming-read ceiling (plain 16-byte-load read, graph of back-to-back launches)",
            "value": round(us, 3), "unit": "us/launch", "bytes_per_launch": n, "steps": args.steps,
            "GB/s": round(n / us / 1e3, 1), "frac_of_8TBs": round(n / us / 1e3 / HBM_PEAK_GBPS, 4),
-           "best_grid": best, "threads": 256, "per_grid_us": {str(k): round(v, 3) for k, v in res.items()},
-           "chunked_us": chunks, "rotation_copies": n_copies}
+           "best_grid": best, "best_loads": "non-temporal" if best_sfx else "plain", "threads": 256,
+           "per_grid_us": {str(k): round(v, 3) for k, v in res[""].items()},
+           "per_grid_us_nt": {str(k): round(v, 3) for k, v in res["_nt"].items()},
+           "chunked_us": chunks[""], "chunked_us_nt": chunks["_nt"], "rotation_copies": n_copies}
     print(json.dumps(out), flush=True)
 
 

@@ -18,6 +18,10 @@
 //     grid (256 threads) reads one contiguous chunk, bytes / grid rounded
 //     up to 16, split into `fronts` (1, 2 or 4) equal parts streamed side
 //     by side by as many thread groups.  Same arguments and returns.
+//
+//   kvq_probe_read_nt, kvq_probe_read_chunks_nt: the same reads with the
+//   non-temporal hint on every load (the hint the NVFP4 decode planes are
+//   read with).  Same arguments and returns.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,7 +29,20 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kInFlight = 8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// one 16-byte load, with the non-temporal hint when NT
+template <bool NT>
+__device__ inline uint4 ld(const uint4* p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *p;
+  }
+}
+
+template <bool NT>
 __global__ void __launch_bounds__(kThreads) k_read_probe(const uint4* __restrict__ p, uint64_t n16, uint32_t* sink) {
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
   uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -33,18 +50,18 @@ __global__ void __launch_bounds__(kThreads) k_read_probe(const uint4* __restrict
   for (; i + (kInFlight - 1) * stride < n16; i += kInFlight * stride) {
     uint4 v[kInFlight];
 #pragma unroll
-    for (int k = 0; k < kInFlight; ++k) v[k] = p[i + k * stride];
+    for (int k = 0; k < kInFlight; ++k) v[k] = ld<NT>(p + i + k * stride);
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
   for (; i < n16; i += stride) {
-    const uint4 v = p[i];
+    const uint4 v = ld<NT>(p + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
-template <int F>
+template <int F, bool NT>
 __global__ void __launch_bounds__(kThreads) k_read_chunks(const uint4* __restrict__ p, uint64_t n16, uint64_t per,
                                                           uint32_t* sink) {
   constexpr int T = kThreads / F;   // threads per front
@@ -59,38 +76,57 @@ __global__ void __launch_bounds__(kThreads) k_read_chunks(const uint4* __restric
   for (; i + (kInFlight - 1) * T < hi; i += kInFlight * T) {
     uint4 v[kInFlight];
 #pragma unroll
-    for (int k = 0; k < kInFlight; ++k) v[k] = p[i + k * T];
+    for (int k = 0; k < kInFlight; ++k) v[k] = ld<NT>(p + i + k * T);
 #pragma unroll
     for (int k = 0; k < kInFlight; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
   for (; i < hi; i += T) {
-    const uint4 v = p[i];
+    const uint4 v = ld<NT>(p + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
-}  // namespace
-
-extern "C" int kvq_probe_read_chunks(const void* p, uint64_t bytes, int32_t grid, int32_t fronts, uint32_t* sink,
-                                     void* stream) {
+template <bool NT>
+int read_chunks(const void* p, uint64_t bytes, int32_t grid, int32_t fronts, uint32_t* sink, void* stream) {
   if (p == nullptr || sink == nullptr || bytes % 16 != 0 || grid <= 0 ||
       reinterpret_cast<uintptr_t>(p) % 16 != 0 || (fronts != 1 && fronts != 2 && fronts != 4))
     return 1;
   const uint64_t n16 = bytes / 16, per = (n16 + grid - 1) / grid;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const auto* q = static_cast<const uint4*>(p);
-  if (fronts == 1) hipLaunchKernelGGL(k_read_chunks<1>, dim3(grid), dim3(kThreads), 0, st, q, n16, per, sink);
-  if (fronts == 2) hipLaunchKernelGGL(k_read_chunks<2>, dim3(grid), dim3(kThreads), 0, st, q, n16, per, sink);
-  if (fronts == 4) hipLaunchKernelGGL(k_read_chunks<4>, dim3(grid), dim3(kThreads), 0, st, q, n16, per, sink);
+  if (fronts == 1) hipLaunchKernelGGL((k_read_chunks<1, NT>), dim3(grid), dim3(kThreads), 0, st, q, n16, per, sink);
+  if (fronts == 2) hipLaunchKernelGGL((k_read_chunks<2, NT>), dim3(grid), dim3(kThreads), 0, st, q, n16, per, sink);
+  if (fronts == 4) hipLaunchKernelGGL((k_read_chunks<4, NT>), dim3(grid), dim3(kThreads), 0, st, q, n16, per, sink);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
-extern "C" int kvq_probe_read(const void* p, uint64_t bytes, int32_t grid, uint32_t* sink, void* stream) {
+template <bool NT>
+int read_all(const void* p, uint64_t bytes, int32_t grid, uint32_t* sink, void* stream) {
   if (p == nullptr || sink == nullptr || bytes % 16 != 0 || grid <= 0 ||
       reinterpret_cast<uintptr_t>(p) % 16 != 0)
     return 1;
-  hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+  hipLaunchKernelGGL((k_read_probe<NT>), dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(p), bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // namespace
+
+extern "C" int kvq_probe_read_chunks(const void* p, uint64_t bytes, int32_t grid, int32_t fronts, uint32_t* sink,
+                                     void* stream) {
+  return read_chunks<false>(p, bytes, grid, fronts, sink, stream);
+}
+
+extern "C" int kvq_probe_read_chunks_nt(const void* p, uint64_t bytes, int32_t grid, int32_t fronts, uint32_t* sink,
+                                        void* stream) {
+  return read_chunks<true>(p, bytes, grid, fronts, sink, stream);
+}
+
+extern "C" int kvq_probe_read(const void* p, uint64_t bytes, int32_t grid, uint32_t* sink, void* stream) {
+  return read_all<false>(p, bytes, grid, sink, stream);
+}
+
+extern "C" int kvq_probe_read_nt(const void* p, uint64_t bytes, int32_t grid, uint32_t* sink, void* stream) {
+  return read_all<true>(p, bytes, grid, sink, stream);
 }

@@ -35,7 +35,8 @@ def _probe_lib():
 
 def test_probe_library_exports():
     lib = _probe_lib()
-    assert all(hasattr(lib, n) for n in ("kvq_probe_read", "kvq_probe_read_chunks", "kvq_probe_mfma_fp8"))
+    assert all(hasattr(lib, n) for n in ("kvq_probe_read", "kvq_probe_read_chunks", "kvq_probe_read_nt",
+                                        "kvq_probe_read_chunks_nt", "kvq_probe_mfma_fp8"))
     # argument checks run on the host: nothing is launched
     assert lib.kvq_probe_mfma_fp8(None, None, 4, 4, None, None) == 1
     fake = ctypes.c_void_p(0x10000)
