@@ -223,10 +223,17 @@ int kvq_auto_num_splits(int32_t num_cus, int32_t B, int32_t programs_per_req, in
   //    kernel's work-groups are 8 waves, two per SIMD; fewer partials make
   //    the combine cheaper), two each otherwise (the single-register-set
   //    tiles of query groups of 1 or 2 need a second work-group per CU to
-  //    cover their load latency).  Measured on MI355X: GQA 4:1 B=2 at 8K and
-  //    32K fastest at 16 splits, MHA B=1/2 at 32K at 2 work-groups per CU.
+  //    cover their load latency) as long as their chunks stay 1024 tokens or
+  //    longer, else one.  Measured on MI355X: GQA 4:1 B=2 at 8K and 32K
+  //    fastest at 16 splits; MHA B=1/2 at 32K at 2 work-groups per CU (2048-
+  //    token chunks), MHA B=2 at 8K at one (2 per CU: 512-token chunks, 9 %
+  //    slower).
   const int64_t base = static_cast<int64_t>(B) * programs_per_req;
-  const int64_t per_cu = static_cast<int64_t>(Hq) >= 4LL * programs_per_req ? 1 : 2;
+  int64_t per_cu = static_cast<int64_t>(Hq) >= 4LL * programs_per_req ? 1 : 2;
+  if (per_cu == 2) {
+    const int64_t s2 = (2LL * num_cus + base - 1) / base;
+    if (static_cast<int64_t>(max_kv_len) < 1024LL * s2) per_cu = 1;
+  }
   int64_t s = (per_cu * num_cus + base - 1) / base;
   // 2) no split shorter than 256 tokens
   const int64_t by_len = (static_cast<int64_t>(max_kv_len) + 255) / 256;

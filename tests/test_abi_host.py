@@ -51,6 +51,10 @@ def test_auto_split_worked_values(K):
     assert K.kvq_auto_num_splits(256, 2, 8, 1024, 128, 32) == 4
     # MHA B=1 H=32 32K: 2*256/32 = 16
     assert K.kvq_auto_num_splits(256, 1, 32, 32768, 128, 32) == 16
+    # MHA B=2 H=16: at 32K two per CU (16 splits, 2048-token chunks); at 8K
+    # two per CU would leave 512-token chunks, so one per CU: 256/32 = 8
+    assert K.kvq_auto_num_splits(256, 2, 16, 32768, 128, 16) == 16
+    assert K.kvq_auto_num_splits(256, 2, 16, 8192, 128, 16) == 8
     # large batch: already 512 programs -> 1
     assert K.kvq_auto_num_splits(256, 64, 8, 4096, 128, 32) == 1
     # MLA B=32 (16 heads share the request's latent: one 8-wave work-group
