@@ -53,6 +53,15 @@ __device__ inline int64_t group_row(const Rows& r, int64_t i0, int64_t i1, int64
 
 
 // ---------------------------------------------------------------- loads
+// 16-byte load with the non-temporal hint, for the calibration's single
+// pass over a tensor (28.4 -> 27.2 us over 134 MB of bf16; the packs
+// measured 15-20 % slower with it and keep plain loads)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load_nt(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // n (<= N) consecutive elements starting at element offset off of x, as
 // fp32 (0 past n); 16-byte vector loads when the run is whole and aligned.
 template <int N>
@@ -188,11 +197,11 @@ __global__ void __launch_bounds__(kThreads) k_amax(const void* __restrict__ x, i
         for (; it + (U - 1) * stride < items; it += U * stride) {
           uint4 w[U];
 #pragma unroll
-          for (int u = 0; u < U; ++u) w[u] = p[it + u * stride];
+          for (int u = 0; u < U; ++u) w[u] = load_nt(p + it + u * stride);
 #pragma unroll
           for (int u = 0; u < U; ++u) fold(w[u]);
         }
-        for (; it < items; it += stride) fold(p[it]);
+        for (; it < items; it += stride) fold(load_nt(p + it));
       }
     } else {
       for (int64_t it = head_items_start(); it < items; it += head_items_stride()) {
