@@ -106,8 +106,16 @@ __global__ void __launch_bounds__(kThreads, 1) k_decode_mla(kvq_decode_args a, i
   const int swz_r = (g ^ (g >> 1)) & 1;          // rows 4 g + m/4 and 16 + 4 g + m/4 (transposed reads)
   // the two scale bytes of this lane's blocks 8 k + 2 g, + 1 out of a pair of scale dwords
   const uint32_t ssel = static_cast<uint32_t>(2 * g) | (static_cast<uint32_t>(2 * g + 1) << 8);
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
+  // XCD-aware order: work-groups are handed to the 8 XCDs in turn, so
+  // dispatch slot L goes to XCD L mod 8; slot L takes work item
+  // (L mod 8) * (N / 8) + L / 8, which gives each XCD a contiguous range of
+  // (request, split) items (whole requests at the bench shape).  A bijection
+  // of the N items, so the results do not depend on the dispatch order
+  // (B = 32, 8 splits: decode step 34.4 -> 33.6 us side by side).
+  int item = blockIdx.x + gridDim.x * blockIdx.y;
+  if (const int n_items = gridDim.x * gridDim.y; n_items % 8 == 0) item = (item % 8) * (n_items / 8) + item / 8;
+  const int split = item % gridDim.x;
+  const int b = item / gridDim.x;
 
   // chunking from kernel arguments only: c = ceil(max_kv_len / s) rounded
   // up to the tile, split j covers [j c, min((j+1) c, L)); the first tiles'
