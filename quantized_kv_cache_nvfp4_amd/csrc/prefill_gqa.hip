@@ -142,8 +142,17 @@ __global__ void __launch_bounds__(kThreads, 1) k_prefill_gqa(PrefillParams P) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, g = lane >> 4, c = lane & 15;
-  const int qb = static_cast<int>(gridDim.x) - 1 - static_cast<int>(blockIdx.x);   // longest first
-  const int hk = blockIdx.y, b = blockIdx.z;
+  // XCD-aware order: work-groups are handed to the 8 XCDs in turn (slot L
+  // to XCD L mod 8), and slot L takes work item (L mod 8) * (N / 8) + L / 8,
+  // so each XCD holds whole (request, kv head) groups, whose query blocks all
+  // read the same K and V through that XCD's L2 (a bijection of the N items:
+  // the results do not depend on the dispatch order; 1024-token chunk over
+  // the 32K cache: 1039-1054 -> 1010-1033 us side by side).  Within an XCD
+  // the query blocks still start longest first.
+  int item = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  if (const int n_items = gridDim.x * gridDim.y * gridDim.z; n_items % 8 == 0) item = (item % 8) * (n_items / 8) + item / 8;
+  const int qb = static_cast<int>(gridDim.x) - 1 - item % static_cast<int>(gridDim.x);   // longest first
+  const int hk = (item / gridDim.x) % gridDim.y, b = item / (gridDim.x * gridDim.y);
   const int i0 = qb * QB;
 
   int L = P.kv_lens[b];
