@@ -72,12 +72,17 @@ namespace gqa {
 using namespace dec;
 
 // K and V plane loads with a cache policy (the buffer loads' auxiliary
-// operand): NVFP4 planes are read with the non-temporal hint (2), FP8 planes
-// without (0).  Measured on the bench shapes: the NVFP4 GQA 32K split kernel
-// 15.9 -> 14.6 us and the MHA 32K one 29.6 -> 27.6 us with the hint, but the
-// FP8 ragged B = 64 kernel 64.1 -> 74.5 us, so FP8 keeps the plain loads.
+// operand): the non-temporal hint (2) or none (0).  Measured on the bench
+// shapes: the NVFP4 GQA 32K split kernel 15.9 -> 14.6 us and the MHA 32K one
+// 29.6 -> 27.6 us with the hint on both planes; the FP8 ragged B = 64 kernel
+// 64.1 -> 74.5 us with it on both, 64.1 -> 62.7 us on K alone (V alone
+// 66.3 us), while its FP8-P pass 1, which reads K alone, went 84.5 -> 86.5 us
+// with it.  So NVFP4 planes take the hint, FP8 K planes only in attention
+// with exact probabilities, FP8 V planes never.
+template <int KVF, int PM>
+constexpr int k_load_policy() { return (KVF == KVQ_NVFP4 || PM == 0) ? 2 : 0; }
 template <int KVF>
-constexpr int kv_load_policy() { return KVF == KVQ_NVFP4 ? 2 : 0; }
+constexpr int v_load_policy() { return KVF == KVQ_NVFP4 ? 2 : 0; }
 template <int CP>
 __device__ inline u32x4 ld128_p(Rsrc r, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP));
@@ -393,7 +398,8 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
   constexpr bool q8 = QT == kQFp8;   // FP8 query codes: 8 bytes per query word instead of 16
   static_assert(PM == 0 || (!FUSED && PSPLIT == 1), "the FP8-P passes write partials only");
   using Gm = Geo<KVF, D>;
-  constexpr int kCP = kv_load_policy<KVF>();   // cache policy of the K and V plane loads
+  constexpr int kCPK = k_load_policy<KVF, PM>();   // cache policies of the K and V plane loads
+  constexpr int kCPV = v_load_policy<KVF>();
   constexpr int NSUB = 16 / G;                  // row groups in the 16 MFMA columns
   constexpr int NT = NSUB < 2 ? 2 : NSUB;       // sub-tiles (16 tokens) per tile
   constexpr int NACC = NT / NSUB;               // score accumulators per tile
@@ -613,20 +619,20 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
     for (int u = 0; u < NT; ++u) {
       const int o = lk_ + u * 16 * st * RB;
       if constexpr (Gm::kKWords == 8) {
-        const u32x4 x0 = ld128_p<kCP>(rk, o), x1 = ld128_p<kCP>(rk, o + 16);
+        const u32x4 x0 = ld128_p<kCPK>(rk, o), x1 = ld128_p<kCPK>(rk, o + 16);
 #pragma unroll
         for (int w = 0; w < 4; ++w) { R.k[u][w] = x0[w]; R.k[u][4 + w] = x1[w]; }
       } else if constexpr (Gm::kKWords == 4) {
-        const u32x4 x0 = ld128_p<kCP>(rk, o);
+        const u32x4 x0 = ld128_p<kCPK>(rk, o);
 #pragma unroll
         for (int w = 0; w < 4; ++w) R.k[u][w] = x0[w];
       } else {
-        const u32x2 x0 = ld64_p<kCP>(rk, o);
+        const u32x2 x0 = ld64_p<kCPK>(rk, o);
         R.k[u][0] = x0[0]; R.k[u][1] = x0[1];
       }
       if constexpr (KVF == KVQ_NVFP4) {
         const int os = lks_ + u * 16 * st * SB;
-        R.ks[u] = (D == 128) ? ld16_p<kCP>(rks, os) : ld8_p<kCP>(rks, os);
+        R.ks[u] = (D == 128) ? ld16_p<kCPK>(rks, os) : ld8_p<kCPK>(rks, os);
       }
     }
   };
@@ -727,15 +733,15 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
           const int o = lvt_ + u * 4 * GB;
-          const u32x4 x0 = ld128_p<kCP>(rv, o);
+          const u32x4 x0 = ld128_p<kCPV>(rv, o);
 #pragma unroll
           for (int w = 0; w < 4; ++w) R.t4[u][w] = x0[w];
           if constexpr (CB == 32) {
-            const u32x4 x1 = ld128_p<kCP>(rv, o + 16);
+            const u32x4 x1 = ld128_p<kCPV>(rv, o + 16);
 #pragma unroll
             for (int w = 0; w < 4; ++w) R.t4[u][4 + w] = x1[w];
           }
-          if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] = ld32_p<kCP>(rvs, lvts_ + u * 4 * GS);
+          if constexpr (KVF == KVQ_NVFP4) R.vs[u][0] = ld32_p<kCPV>(rvs, lvts_ + u * 4 * GS);
         }
       } else {
         const Rsrc rv = make_rsrc(vc + vbase * RB, nv * st * RB);
@@ -746,14 +752,14 @@ __global__ void __launch_bounds__(kThreads, (decode_min_blocks<KVF, G, QT, VL>()
           for (int i = 0; i < 4; ++i) {
             const int o = lv_ + (16 * u + i) * st * RB;
             if constexpr (Gm::kVBytes == 8) {
-              const u32x2 x = ld64_p<kCP>(rv, o);
+              const u32x2 x = ld64_p<kCPV>(rv, o);
               R.v[u][i][0] = x[0]; R.v[u][i][1] = x[1];
             } else if constexpr (Gm::kVBytes == 4) {
-              R.v[u][i][0] = ld32_p<kCP>(rv, o);
+              R.v[u][i][0] = ld32_p<kCPV>(rv, o);
             } else {
-              R.v[u][i][0] = ld16_p<kCP>(rv, o);
+              R.v[u][i][0] = ld16_p<kCPV>(rv, o);
             }
-            if constexpr (KVF == KVQ_NVFP4) R.vs[u][i] = ld8_p<kCP>(rvs, lvs_ + (16 * u + i) * st * SB);
+            if constexpr (KVF == KVQ_NVFP4) R.vs[u][i] = ld8_p<kCPV>(rvs, lvs_ + (16 * u + i) * st * SB);
           }
         }
       }
